@@ -1,0 +1,333 @@
+"""CSA2 hot path, written out plainly on the CPU (test infrastructure only).
+
+Steps, in the pages' order (aiwiki "DeepSeek V4.1-Flash", section "Compressed
+Sparse Attention 2"; model card, Introduction, CSA2 paragraph):
+
+1. quantize-and-append of main K/V into the FP4 cache (E2M1 codes, one E4M3
+   scale per 16 channels) and storage of the index keys;
+2. index scoring of every causally visible candidate against the layer's index
+   query, and per-query Top-K, in Full, Reindex or Reuse mode, with the
+   decoder's candidate pool of 8-position blocks ranked by their maximum score;
+3. gather and dequantization of the selected rows;
+4. softmax attention of every query head over those rows.
+
+Cache layout (the library's, so parity compares raw bytes):
+    kv_codes  [batch][capacity][dk/2 + dv/2]  uint8: K codes then V codes;
+              channel 2i in the low nibble of byte i, 2i+1 in the high nibble
+    kv_scales [batch][capacity][dk/16 + dv/16] uint8 E4M3: K scales then V
+    idx_k     [batch][capacity][idx_heads][idx_dim]: bf16 bits (uint16) or
+              E4M3 codes (uint8)
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .formats import (bf16_value, e2m1_encode, e2m1_value, e4m3_encode, e4m3_encode_ratio,
+                      e4m3_value, fma_f32)
+
+BLOCK = 16          # channels per E4M3 scale
+POOL_BLOCK = 8      # positions per candidate-pool block
+
+
+# ---------------------------------------------------------------------------
+# Step 1: quantize-and-append
+# ---------------------------------------------------------------------------
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """[..., 2n] 4-bit codes -> [..., n] bytes; even channel in the low nibble (reading)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def quantize_rows(x_bits: np.ndarray):
+    """FP4 quantization of bf16 rows [n, d] (d a multiple of 16).
+
+    Model card, Introduction, CSA2 paragraph: E2M1 values with one E4M3 scale
+    per 16 channels.  Reading (the pages give no rule): the scale of a block is
+    the E4M3 value nearest amax/6 (amax = largest |x| in the block, 6 = largest
+    E2M1 magnitude), RNE, saturating at 448; each element takes the E2M1 code
+    nearest x/scale, RNE, saturating at 6, keeping x's sign.
+
+    Returns (packed codes [n, d/2] uint8, scale codes [n, d/16] uint8).
+    """
+    x = bf16_value(x_bits)
+    n, d = x.shape
+    blocks = x.reshape(n, d // BLOCK, BLOCK)
+    amax = np.abs(blocks).max(axis=2)
+    sc = e4m3_encode_ratio(amax, 6.0)
+    s = e4m3_value(sc)
+    codes = e2m1_encode(blocks, s[:, :, None]).reshape(n, d)
+    return pack_nibbles(codes), sc
+
+
+def dequantize_rows(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Value of FP4 rows: E2M1(code) * E4M3(scale), float64 (exact)."""
+    codes = unpack_nibbles(packed)
+    n, d = codes.shape
+    v = e2m1_value(codes).reshape(n, d // BLOCK, BLOCK) * e4m3_value(scales)[:, :, None]
+    return v.reshape(n, d)
+
+
+class OracleCache:
+    """Host copy of the FP4 main-KV cache and the index-key cache (library layout)."""
+
+    def __init__(self, batch, capacity, dk=128, dv=128, idx_heads=8, idx_dim=64, idx_k_dtype="fp8"):
+        self.batch, self.capacity = batch, capacity
+        self.dk, self.dv, self.idx_heads, self.idx_dim = dk, dv, idx_heads, idx_dim
+        self.idx_k_dtype = idx_k_dtype
+        self.kv_codes = np.zeros((batch, capacity, dk // 2 + dv // 2), np.uint8)
+        self.kv_scales = np.zeros((batch, capacity, dk // BLOCK + dv // BLOCK), np.uint8)
+        ik_t = np.uint8 if idx_k_dtype == "fp8" else np.uint16
+        self.idx_k = np.zeros((batch, capacity, idx_heads, idx_dim), ik_t)
+
+    def bytes_per_token(self) -> dict:
+        """Bytes one cached position occupies (main KV and index keys)."""
+        main = self.kv_codes.shape[2] + self.kv_scales.shape[2]
+        idx = self.idx_k.shape[2] * self.idx_k.shape[3] * self.idx_k.itemsize
+        return {"main_kv": main, "index_keys": idx}
+
+    def append(self, k_bits, v_bits, ik_bits, seq, pos):
+        """Quantize and store rows r at (seq[r], pos[r]).
+
+        Index keys are stored verbatim (bf16 cache) or cast to E4M3 with RNE,
+        saturating (fp8 cache).  The pages say index keys come from main-KV
+        entries (aiwiki, "Compressed Sparse Attention 2") without giving the map;
+        here they arrive as an input, as the learned projection needs weights.
+        """
+        seq = np.asarray(seq)
+        pos = np.asarray(pos)
+        kc, ks = quantize_rows(k_bits)
+        vc, vs = quantize_rows(v_bits)
+        self.kv_codes[seq, pos] = np.concatenate([kc, vc], axis=1)
+        self.kv_scales[seq, pos] = np.concatenate([ks, vs], axis=1)
+        if ik_bits is not None:
+            if self.idx_k_dtype == "fp8":
+                self.idx_k[seq, pos] = e4m3_encode(bf16_value(ik_bits))
+            else:
+                self.idx_k[seq, pos] = np.asarray(ik_bits, np.uint16)
+
+    def index_key_values(self, b, rows) -> np.ndarray:
+        """Decoded index keys of sequence b at `rows`, float32 [n, idx_heads, idx_dim]."""
+        raw = self.idx_k[b, rows]
+        if self.idx_k_dtype == "fp8":
+            return e4m3_value(raw).astype(np.float32)
+        return bf16_value(raw).astype(np.float32)
+
+    def kv_values(self, b, rows):
+        """Dequantized (K, V) of sequence b at `rows`, float64 [n, dk], [n, dv]."""
+        codes = self.kv_codes[b, rows]
+        scales = self.kv_scales[b, rows]
+        hk, sk = self.dk // 2, self.dk // BLOCK
+        k = dequantize_rows(codes[:, :hk], scales[:, :sk])
+        v = dequantize_rows(codes[:, hk:], scales[:, sk:])
+        return k, v
+
+
+# ---------------------------------------------------------------------------
+# Step 2: index scoring, Top-K, candidate pool, modes
+# ---------------------------------------------------------------------------
+
+def query_index_values(q_idx_bits, dtype: str) -> np.ndarray:
+    """Index query as float32 values: bf16 as given, or cast to E4M3 (RNE, saturating)."""
+    v = bf16_value(q_idx_bits)
+    if dtype == "fp8":
+        v = e4m3_value(e4m3_encode(v))
+    return v.astype(np.float32)
+
+
+def _pairwise_f32(x: np.ndarray, axis: int) -> np.ndarray:
+    """Balanced pairwise fp32 sum along `axis` (length a power of two):
+    ((x0+x1)+(x2+x3)) + ((x4+x5)+(x6+x7)) for eight terms."""
+    x = np.moveaxis(np.asarray(x, np.float32), axis, -1)
+    while x.shape[-1] > 1:
+        x = (x[..., 0::2] + x[..., 1::2]).astype(np.float32)
+    return x[..., 0]
+
+
+def index_scores(q: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Index score of every candidate: sum over indexer heads of q_h . k_h, in fp32.
+
+    Source: aiwiki "Compressed Sparse Attention 2" (Full and Reindex layers
+    score candidate positions with a new index query against the shared index
+    keys).  The pages do not give the score's form.  Reading: the plain sum over
+    heads of the head dot products, no activation or head weights, accumulated
+    in fp32 in this fixed order, so that the Top-K decision is reproducible:
+      * per head h and 16-channel block j: a chain of fp32 fused multiply-adds
+        over the block's channels in increasing order, starting from 0;
+      * per head: the four block sums added pairwise, (b0+b1)+(b2+b3);
+      * over heads: the head sums added pairwise (a balanced tree).
+
+    q: float32 [H, D]; keys: float32 [n, H, D]; returns float32 [n].
+    Parity pin: error bound against the exact dot product, and exact integer
+    cases (tests/test_oracle_scores.py); the rounding sequence itself is the
+    reading above.
+    """
+    q = np.asarray(q, np.float32)
+    keys = np.asarray(keys, np.float32)
+    n = keys.shape[0]
+    H, D = q.shape
+    nb = D // BLOCK
+    qb = q.reshape(H, nb, BLOCK)
+    kb = keys.reshape(n, H, nb, BLOCK)
+    part = np.zeros((n, H, nb), np.float32)
+    for t in range(BLOCK):
+        part = fma_f32(qb[None, :, :, t], kb[:, :, :, t], part)
+    per_head = _pairwise_f32(part, axis=2)
+    return _pairwise_f32(per_head, axis=1)
+
+
+def topk_select(scores: np.ndarray, positions: np.ndarray, k: int) -> np.ndarray:
+    """The k candidates with the largest scores, as positions in ascending order, -1 padded.
+
+    Source: model card, CSA2 paragraph and aiwiki "Compressed Sparse Attention 2"
+    (each indexing layer makes a fresh Top-K selection).  Readings: ties in
+    score go to the lower position; -0 and +0 are equal; fewer than k
+    candidates leaves -1 padding at the end.
+    """
+    s = np.asarray(scores, np.float32).astype(np.float64) + 0.0   # -0.0 -> +0.0
+    positions = np.asarray(positions, np.int64)
+    order = np.lexsort((positions, -s))             # score descending, then position ascending
+    chosen = np.sort(positions[order[:k]])
+    out = np.full(k, -1, np.int32)
+    out[:len(chosen)] = chosen
+    return out
+
+
+def build_pool(scores: np.ndarray, pool_blocks: int) -> np.ndarray:
+    """Candidate pool of the first Full layer, from scores of positions 0..n-1.
+
+    Source: aiwiki "Compressed Sparse Attention 2" (the first Full-mode decoder
+    layer scores every visible position, ranks blocks of eight positions by
+    their maximum index score and keeps a fixed number of blocks as the shared
+    pool).  Readings: blocks are aligned to position 0; a partial last block
+    uses its visible members; block ties go to the lower block; the pool lists
+    the kept positions in ascending order, -1 padded to 8 * pool_blocks.
+    """
+    s = np.asarray(scores, np.float32)
+    n = len(s)
+    nblk = (n + POOL_BLOCK - 1) // POOL_BLOCK
+    bmax = np.array([s[b * POOL_BLOCK:min(n, (b + 1) * POOL_BLOCK)].max() for b in range(nblk)],
+                    np.float32)
+    blocks = topk_select(bmax, np.arange(nblk), pool_blocks)
+    pos = [p for b in blocks if b >= 0
+           for p in range(b * POOL_BLOCK, min(n, (b + 1) * POOL_BLOCK))]
+    out = np.full(POOL_BLOCK * pool_blocks, -1, np.int32)
+    out[:len(pos)] = pos
+    return out
+
+
+def index_topk(mode: str, cache: OracleCache, seq: int, q_pos: int, q_idx: np.ndarray, top_k: int,
+               pool_in: Optional[np.ndarray] = None, pool_blocks: int = 0,
+               reuse_src: Optional[np.ndarray] = None):
+    """One query's Top-K in the given mode; returns (topk, pool or None, scores, candidates).
+
+    Source: aiwiki "Compressed Sparse Attention 2":
+      * full: score every causally visible position [0, q_pos]; optionally
+        build the candidate pool;
+      * reindex: new index query over an earlier layer's index keys, searching
+        only the pool (pool_in; entries -1 or beyond q_pos are skipped), or all
+        visible positions when no pool is given;
+      * reuse: the earlier layer's Top-K indices, unchanged.
+    q_idx: float32 [idx_heads, idx_dim] (see query_index_values).
+    """
+    if mode == "reuse":
+        return np.array(reuse_src, np.int32).copy(), None, None, None
+    if mode == "full" or pool_in is None:
+        cand = np.arange(q_pos + 1)
+    elif mode == "reindex":
+        p = np.asarray(pool_in, np.int64)
+        cand = p[(p >= 0) & (p <= q_pos)]
+    else:
+        raise ValueError(mode)
+    scores = index_scores(q_idx, cache.index_key_values(seq, cand))
+    topk = topk_select(scores, cand, top_k)
+    pool = build_pool(scores, pool_blocks) if (mode == "full" and pool_blocks > 0) else None
+    return topk, pool, scores, cand
+
+
+# ---------------------------------------------------------------------------
+# Steps 3-4: gather, dequantize, softmax attention
+# ---------------------------------------------------------------------------
+
+def sparse_attention(q_bits: np.ndarray, cache: OracleCache, seq: int, topk: np.ndarray,
+                     scale: Optional[float] = None):
+    """Softmax attention of every head over the selected rows, in float64.
+
+    Source: model card, CSA2 paragraph and aiwiki "Compressed Sparse Attention
+    2" (each layer attends over its Top-K positions of the shared FP4 main KV,
+    one KV head shared by all query heads).  For head h:
+        z_j = scale * (q_h . K_j),  o_h = sum_j softmax(z)_j V_j,
+        lse_h = ln sum_j exp(z_j),
+    over the entries j of `topk` that are >= 0 (each entry counts once).
+    Readings: no positional term, no sink, sparse rows only; scale defaults to
+    1/sqrt(dk); an empty selection gives o = 0 and lse = -inf.
+
+    q_bits: bf16 bits [heads, dk].  Returns (out [heads, dv], lse [heads]).
+    """
+    q = bf16_value(q_bits)
+    H = q.shape[0]
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(cache.dk)))
+    rows = np.asarray(topk, np.int64)
+    rows = rows[rows >= 0]
+    if len(rows) == 0:
+        return np.zeros((H, cache.dv)), np.full(H, -np.inf)
+    k, v = cache.kv_values(seq, rows)
+    z = (q @ k.T) * scale
+    m = z.max(axis=1, keepdims=True)
+    p = np.exp(z - m)
+    ell = p.sum(axis=1, keepdims=True)
+    out = (p @ v) / ell
+    lse = (m + np.log(ell))[:, 0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# A whole step over a layer stack
+# ---------------------------------------------------------------------------
+
+def run_layers(cache: OracleCache, layers: Sequence, q_seq, q_pos, queries, top_k: int,
+               q_idx_dtype: str, scale: Optional[float] = None, only=None):
+    """Index Top-K and attention for every layer of a stack, per query.
+
+    layers: objects with .mode, .pool_blocks, .pool_from, .reuse_from
+    queries: per layer, objects with .q [nq, heads, dk] and .q_idx [nq, H_I, D] bf16 bits.
+    only: optional list of query indices to compute (others are skipped).
+    Returns per layer a dict with 'topk' [nq, K], 'pool' (or None), 'out', 'lse'.
+    """
+    nq = len(q_seq)
+    sel = range(nq) if only is None else list(only)
+    results = []
+    for li, layer in enumerate(layers):
+        qd = queries[li]
+        res = {"topk": np.full((nq, top_k), -1, np.int32), "pool": None,
+               "out": np.zeros((nq, qd.q.shape[1], cache.dv)),
+               "lse": np.full((nq, qd.q.shape[1]), -np.inf)}
+        if layer.mode == "full" and layer.pool_blocks > 0:
+            res["pool"] = np.full((nq, POOL_BLOCK * layer.pool_blocks), -1, np.int32)
+        for i in sel:
+            b, p = int(q_seq[i]), int(q_pos[i])
+            pool_in = None
+            if layer.mode == "reindex" and layer.pool_from >= 0:
+                pool_in = results[layer.pool_from]["pool"][i]
+            reuse = results[layer.reuse_from]["topk"][i] if layer.mode == "reuse" else None
+            qi = query_index_values(qd.q_idx[i], q_idx_dtype)
+            topk, pool, _, _ = index_topk(layer.mode, cache, b, p, qi, top_k, pool_in=pool_in,
+                                          pool_blocks=layer.pool_blocks, reuse_src=reuse)
+            res["topk"][i] = topk
+            if pool is not None:
+                res["pool"][i] = pool
+            res["out"][i], res["lse"][i] = sparse_attention(qd.q[i], cache, b, topk, scale)
+        results.append(res)
+    return results
