@@ -1,0 +1,200 @@
+/*
+ * csa2.h -- C ABI of the CSA2 hot path on MI355X (gfx950).
+ *
+ * Compressed Sparse Attention 2 (CSA2) as the pages state the problem:
+ *   - model card "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+ *     Compression", Introduction, CSA2 paragraph: per-layer static modes Full,
+ *     Reindex and Reuse that share main KV and indexer keys across layers and
+ *     recycle Top-K sparse-attention indices; a Hierarchical Sparse Indexer in
+ *     the decoder restricting later indexers to a candidate pool built by the
+ *     first Full layer; main KV cached in FP4 (E2M1 values, one E4M3 scale per
+ *     16 channels);
+ *   - aiwiki "DeepSeek V4.1-Flash", section "Compressed Sparse Attention 2":
+ *     what each mode computes and reuses; the pool of 8-position blocks ranked
+ *     by their maximum index score; section "KV-cache formats and bounded
+ *     replay": the main global KV lives in accelerator memory in FP4.
+ *
+ * Three calls make one layer's step: csa2_kv_append (quantize-and-append new
+ * rows), csa2_index_topk (index scoring + Top-K in a mode, optionally building
+ * the pool), csa2_sparse_attn (gather + dequantize the selected rows and run
+ * softmax attention of every query head over them).
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers (hipMalloc'd or torch-owned),
+ *     except the csa2_cache descriptor itself, which is a host struct.
+ *   - The library never allocates, frees or synchronizes.  Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the null stream) and returns at once.
+ *   - Scalars and pointers are validated on the host before anything is
+ *     enqueued; a failed check returns an error and enqueues nothing.
+ *     Launch failures return CSA2_ERR_HIP.  Device-side preconditions (listed
+ *     per call) are not checked.
+ *   - Calls are reentrant; concurrent calls must not share a workspace.
+ *   - Finite inputs only: NaN or infinite inputs give unspecified results.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = 1,         /* a required pointer is NULL */
+  CSA2_ERR_SHAPE = 2,        /* a size is out of range */
+  CSA2_ERR_UNSUPPORTED = 3,  /* a dimension or dtype this build does not implement */
+  CSA2_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the query function returns */
+  CSA2_ERR_HIP = 5,          /* a HIP launch reported an error */
+  CSA2_ERR_ARG = 6           /* inconsistent arguments (e.g. mode vs. pool/reuse pointers) */
+} csa2_status;
+
+/* Layer modes (aiwiki, "Compressed Sparse Attention 2"). */
+typedef enum {
+  CSA2_FULL = 0,     /* score every causally visible position; fresh Top-K; may build the pool */
+  CSA2_REINDEX = 1,  /* new index query over earlier index keys; search the pool (or all visible) */
+  CSA2_REUSE = 2     /* recycle an earlier layer's Top-K unchanged */
+} csa2_mode;
+
+typedef enum {
+  CSA2_BF16 = 0,
+  CSA2_FP8_E4M3 = 1  /* OCP E4M3FN: bias 7, max 448, 0x7F/0xFF NaN, no infinities */
+} csa2_dtype;
+
+/*
+ * The shared global cache of one layer group: FP4 main KV plus index keys.
+ * Caller-owned device memory; byte layout (part of the ABI):
+ *   kv_codes  [batch][capacity][dk/2 + dv/2] bytes.  Bytes 0..dk/2-1 hold the
+ *             K codes, then the V codes.  Channel 2i is the low nibble of byte
+ *             i, channel 2i+1 the high nibble.  A code is E2M1 (bit 3 sign,
+ *             magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6).
+ *   kv_scales [batch][capacity][dk/16 + dv/16] bytes, E4M3 codes: the scale
+ *             of K channels 16b..16b+15 at byte b, then the V scales.
+ *   idx_k     [batch][capacity][idx_heads][idx_dim], bf16 bits or E4M3 codes
+ *             (idx_k_dtype).
+ * One cached position = dk/2 + dv/2 + dk/16 + dv/16 bytes of main KV
+ * (144 B for dk = dv = 128) plus idx_heads * idx_dim * (1 or 2) bytes.
+ * Supported: dk = dv = 128, idx_dim = 64, idx_heads in {4, 8}.
+ */
+typedef struct csa2_cache {
+  uint8_t *kv_codes;
+  uint8_t *kv_scales;
+  void *idx_k;
+  int32_t batch;
+  int32_t capacity;
+  int32_t dk;
+  int32_t dv;
+  int32_t idx_heads;
+  int32_t idx_dim;
+  int32_t idx_k_dtype; /* csa2_dtype */
+} csa2_cache;
+
+/*
+ * Quantize-and-append n new rows (model card, Introduction, CSA2 paragraph:
+ * FP4 main KV, E2M1 values with one E4M3 scale per 16 channels).
+ *   k, v       [n][dk], [n][dv] bf16 bits: the new main K and V rows.
+ *   idx_k_in   [n][idx_heads][idx_dim] bf16 bits, or NULL to leave the index
+ *              keys untouched.  Stored verbatim (bf16 cache) or cast to E4M3
+ *              (round to nearest even, saturating at +-448, sign kept).
+ *   seq, pos   [n] int32: row r goes to sequence seq[r], position pos[r].
+ * Per 16-channel block: scale = E4M3 nearest amax/6 (ties to even,
+ * saturating at 448); each element = E2M1 nearest x/scale (ties to even,
+ * saturating at 6, sign kept; a zero scale gives magnitude 0).
+ * Device preconditions: 0 <= seq[r] < batch, 0 <= pos[r] < capacity; no two
+ * rows of one call share (seq, pos).
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (n < 0), CSA2_ERR_UNSUPPORTED, CSA2_ERR_HIP.
+ * n = 0 is a no-op returning CSA2_OK.
+ */
+csa2_status csa2_kv_append(const csa2_cache *cache, const uint16_t *k, const uint16_t *v,
+                           const uint16_t *idx_k_in, const int32_t *seq, const int32_t *pos,
+                           int32_t n, void *stream);
+
+/*
+ * Bytes of workspace csa2_index_topk needs for these arguments (0 for REUSE).
+ * Returns 0 as well when the arguments are invalid; csa2_index_topk then
+ * reports the error.
+ */
+size_t csa2_index_topk_workspace(const csa2_cache *cache, csa2_mode mode, int32_t nq, int32_t top_k,
+                                 int32_t pool_len, int32_t pool_blocks);
+
+/*
+ * Index scoring and per-query Top-K (aiwiki, "Compressed Sparse Attention 2").
+ *   q_idx      [nq][idx_heads][idx_dim] bf16 bits: each query's index query.
+ *   q_dtype    precision the index query is scored in: CSA2_BF16 as given, or
+ *              CSA2_FP8_E4M3 (cast with round to nearest even, saturating).
+ *   q_seq      [nq] int32 sequence of each query.
+ *   q_pos      [nq] int32 position of each query; it sees rows [0, q_pos].
+ *   top_k      entries per query in topk_out (1 .. 65536).
+ *   FULL:      candidates are positions 0..q_pos.  If pool_blocks > 0, also
+ *              builds the candidate pool: blocks [8b, 8b+8) ranked by their
+ *              maximum score (ties to the lower block), the top pool_blocks
+ *              blocks kept; pool_out [nq][8*pool_blocks] receives their visible
+ *              positions in ascending order, -1 padded.
+ *   REINDEX:   candidates are the entries of pool_in [nq][pool_len] that lie
+ *              in [0, q_pos] (-1 = empty slot); pool_in = NULL means all visible
+ *              positions (as FULL, no pool).  Entries must be distinct.
+ *   REUSE:     topk_out = reuse_src [nq][top_k], copied unchanged; q_idx,
+ *              q_seq, q_pos may be NULL.
+ * Score of candidate j: sum over indexer heads h of q_h . k_{j,h}, in fp32 in
+ * a fixed order: per head and 16-channel block, fused multiply-adds in channel
+ * order from 0; per head the four block sums pairwise; over heads a balanced
+ * pairwise tree.  The result is bit-reproducible.
+ * topk_out [nq][top_k] int32: the min(top_k, #candidates) candidates with the
+ * largest scores (ties to the lower position, -0 == +0), in ascending
+ * position order, then -1 padding.
+ * Device preconditions: 0 <= q_seq < batch, 0 <= q_pos < capacity.
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED, CSA2_ERR_ARG
+ * (pool_out missing with pool_blocks > 0, pool arguments in the wrong mode,
+ * reuse_src missing in REUSE), CSA2_ERR_WORKSPACE, CSA2_ERR_HIP.
+ */
+csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode, const uint16_t *q_idx,
+                            csa2_dtype q_dtype, const int32_t *q_seq, const int32_t *q_pos,
+                            int32_t nq, int32_t top_k, const int32_t *pool_in, int32_t pool_len,
+                            int32_t pool_blocks, int32_t *pool_out, const int32_t *reuse_src,
+                            int32_t *topk_out, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* Bytes of workspace csa2_sparse_attn needs (0 for invalid arguments). */
+size_t csa2_sparse_attn_workspace(const csa2_cache *cache, int32_t nq, int32_t n_heads,
+                                  int32_t top_k);
+
+/*
+ * Sparse softmax attention over the selected FP4 rows (model card,
+ * Introduction, CSA2 paragraph; aiwiki "Compressed Sparse Attention 2": every
+ * layer attends over its Top-K positions of the shared FP4 main KV; all query
+ * heads share the one KV head).
+ *   q          [nq][n_heads][dk] bf16 bits.
+ *   q_seq      [nq] int32 sequence each query reads.
+ *   topk       [nq][top_k] int32 rows; entries < 0 are skipped; each entry
+ *              counts once (duplicates count twice).
+ *   softmax_scale  multiplies q.k (pass 1/sqrt(dk) for the usual scaling).
+ *   out        [nq][n_heads][dv] fp32: sum_j softmax(z)_j V_j with
+ *              z_j = softmax_scale * q_h . K_j, K and V dequantized exactly.
+ *   lse        [nq][n_heads] fp32 natural-log sum of exp(z_j), or NULL.
+ * An empty selection gives out = 0 and lse = -inf.  Accumulation is fp32 on
+ * matrix cores (bf16 q.K products, fp16 probabilities times V).
+ * Supported: n_heads a multiple of 16 up to 128; dk = dv = 128.
+ * Device preconditions: 0 <= q_seq < batch; topk entries < capacity.
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED,
+ * CSA2_ERR_WORKSPACE, CSA2_ERR_HIP.
+ */
+csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,
+                             const int32_t *q_seq, int32_t nq, const int32_t *topk, int32_t top_k,
+                             float softmax_scale, float *out, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *csa2_strerror(csa2_status status);
+
+/* CSA2_ABI_VERSION of the loaded library. */
+int csa2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,147 @@
+// C ABI of the CSA2 library: host-side validation, workspace sizing, dispatch.
+// Every check runs before anything is enqueued, so a rejected call leaves the
+// device untouched.
+#include "csa2_internal.h"
+
+using namespace csa2;
+
+namespace {
+
+csa2_status check_cache(const csa2_cache *c, bool need_idx) {
+  if (c == nullptr || c->kv_codes == nullptr || c->kv_scales == nullptr) return CSA2_ERR_NULL;
+  if (need_idx && c->idx_k == nullptr) return CSA2_ERR_NULL;
+  if (c->batch < 1 || c->capacity < 1) return CSA2_ERR_SHAPE;
+  if (c->dk != 128 || c->dv != 128 || c->idx_dim != 64) return CSA2_ERR_UNSUPPORTED;
+  if (c->idx_heads != 4 && c->idx_heads != 8) return CSA2_ERR_UNSUPPORTED;
+  if (c->idx_k_dtype != CSA2_BF16 && c->idx_k_dtype != CSA2_FP8_E4M3) return CSA2_ERR_UNSUPPORTED;
+  return CSA2_OK;
+}
+
+constexpr int32_t kMaxTopK = 1 << 16;
+
+csa2_status check_topk_args(const csa2_cache *cache, csa2_mode mode, int32_t nq, int32_t top_k,
+                            int32_t pool_len, int32_t pool_blocks) {
+  csa2_status st = check_cache(cache, mode != CSA2_REUSE);
+  if (st != CSA2_OK) return st;
+  if (mode != CSA2_FULL && mode != CSA2_REINDEX && mode != CSA2_REUSE) return CSA2_ERR_ARG;
+  if (nq < 0 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_SHAPE;
+  if (pool_len < 0 || pool_blocks < 0 || pool_blocks > kMaxTopK) return CSA2_ERR_SHAPE;
+  if (mode != CSA2_FULL && pool_blocks != 0) return CSA2_ERR_ARG;
+  if (mode != CSA2_REINDEX && pool_len != 0) return CSA2_ERR_ARG;
+  if (nq > 65535) return CSA2_ERR_SHAPE;   // one grid row per query
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *csa2_strerror(csa2_status s) {
+  switch (s) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_NULL: return "a required pointer is NULL";
+    case CSA2_ERR_SHAPE: return "a size is out of range";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported dimension or dtype";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_HIP: return "HIP launch error";
+    case CSA2_ERR_ARG: return "inconsistent arguments";
+  }
+  return "unknown status";
+}
+
+int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+csa2_status csa2_kv_append(const csa2_cache *cache, const uint16_t *k, const uint16_t *v,
+                           const uint16_t *idx_k_in, const int32_t *seq, const int32_t *pos,
+                           int32_t n, void *stream) {
+  csa2_status st = check_cache(cache, idx_k_in != nullptr);
+  if (st != CSA2_OK) return st;
+  if (n < 0) return CSA2_ERR_SHAPE;
+  if (n == 0) return CSA2_OK;
+  if (k == nullptr || v == nullptr || seq == nullptr || pos == nullptr) return CSA2_ERR_NULL;
+  if (launch_kv_append(*cache, k, v, idx_k_in, seq, pos, n, (hipStream_t)stream) != hipSuccess)
+    return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
+size_t csa2_index_topk_workspace(const csa2_cache *cache, csa2_mode mode, int32_t nq,
+                                 int32_t top_k, int32_t pool_len, int32_t pool_blocks) {
+  if (check_topk_args(cache, mode, nq, top_k, pool_len, pool_blocks) != CSA2_OK) return 0;
+  return topk_workspace_layout(*cache, mode, nq, pool_len, pool_blocks).total;
+}
+
+csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode, const uint16_t *q_idx,
+                            csa2_dtype q_dtype, const int32_t *q_seq, const int32_t *q_pos,
+                            int32_t nq, int32_t top_k, const int32_t *pool_in, int32_t pool_len,
+                            int32_t pool_blocks, int32_t *pool_out, const int32_t *reuse_src,
+                            int32_t *topk_out, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  csa2_status st = check_topk_args(cache, mode, nq, top_k, pool_len, pool_blocks);
+  if (st != CSA2_OK) return st;
+  if (topk_out == nullptr) return CSA2_ERR_NULL;
+  if (mode == CSA2_REUSE) {
+    if (reuse_src == nullptr) return CSA2_ERR_ARG;
+    if (pool_in != nullptr || pool_out != nullptr) return CSA2_ERR_ARG;
+  } else {
+    if (q_idx == nullptr || q_seq == nullptr || q_pos == nullptr) return CSA2_ERR_NULL;
+    if (q_dtype != CSA2_BF16 && q_dtype != CSA2_FP8_E4M3) return CSA2_ERR_UNSUPPORTED;
+    if (reuse_src != nullptr) return CSA2_ERR_ARG;
+    if (mode == CSA2_FULL && pool_in != nullptr) return CSA2_ERR_ARG;
+    if (mode == CSA2_FULL && pool_blocks > 0 && pool_out == nullptr) return CSA2_ERR_ARG;
+    if (mode == CSA2_FULL && pool_blocks == 0 && pool_out != nullptr) return CSA2_ERR_ARG;
+    if (mode == CSA2_REINDEX) {
+      if (pool_out != nullptr) return CSA2_ERR_ARG;
+      if ((pool_in == nullptr) != (pool_len == 0)) return CSA2_ERR_ARG;
+    }
+  }
+  if (nq == 0) return CSA2_OK;
+  IndexArgs a;
+  a.cache = cache;
+  a.mode = mode;
+  a.q_idx = q_idx;
+  a.q_fp8 = q_dtype == CSA2_FP8_E4M3;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.nq = nq;
+  a.top_k = top_k;
+  a.pool_in = pool_in;
+  a.pool_len = pool_len;
+  a.pool_blocks = pool_blocks;
+  a.pool_out = pool_out;
+  a.reuse_src = reuse_src;
+  a.topk_out = topk_out;
+  a.layout = topk_workspace_layout(*cache, mode, nq, pool_len, pool_blocks);
+  if (a.layout.total > 0 && (workspace == nullptr || workspace_bytes < a.layout.total))
+    return CSA2_ERR_WORKSPACE;
+  a.ws = static_cast<uint8_t *>(workspace);
+  if (launch_index_topk(a, (hipStream_t)stream) != hipSuccess) return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
+size_t csa2_sparse_attn_workspace(const csa2_cache *cache, int32_t nq, int32_t n_heads,
+                                  int32_t top_k) {
+  if (check_cache(cache, false) != CSA2_OK) return 0;
+  if (nq < 0 || n_heads < 16 || n_heads > 128 || n_heads % 16 != 0) return 0;
+  if (top_k < 1 || top_k > kMaxTopK) return 0;
+  return attn_workspace_layout(*cache, nq, n_heads, top_k).total;
+}
+
+csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,
+                             const int32_t *q_seq, int32_t nq, const int32_t *topk, int32_t top_k,
+                             float softmax_scale, float *out, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  csa2_status st = check_cache(cache, false);
+  if (st != CSA2_OK) return st;
+  if (n_heads < 16 || n_heads > 128 || n_heads % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  if (nq < 0 || top_k < 1 || top_k > kMaxTopK || nq > 65535) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (q == nullptr || q_seq == nullptr || topk == nullptr || out == nullptr) return CSA2_ERR_NULL;
+  const AttnWorkspace L = attn_workspace_layout(*cache, nq, n_heads, top_k);
+  if (workspace == nullptr || workspace_bytes < L.total) return CSA2_ERR_WORKSPACE;
+  if (launch_sparse_attn(*cache, q, n_heads, q_seq, nq, topk, top_k, softmax_scale, out, lse,
+                         static_cast<uint8_t *>(workspace), L, (hipStream_t)stream) != hipSuccess)
+    return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Quantize-and-append into the FP4 main-KV cache and the index-key cache.
+//
+// Model card "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression",
+// Introduction, CSA2 paragraph: the main KV is cached in FP4, E2M1 values with
+// one E4M3 scale per 16 channels.  aiwiki "DeepSeek V4.1-Flash", "KV-cache
+// formats and bounded replay": the runtime global KV stays in accelerator
+// memory.  Rounding rules (the pages give none): scale = E4M3 nearest amax/6,
+// element = E2M1 nearest x/scale, ties to even, saturating, sign kept.
+//
+// One wave per appended row.  Lanes 0..15 each own one 16-channel block
+// (8 K blocks, then 8 V blocks): 32 B of bf16 in, 8 B of codes + 1 scale byte
+// out.  All 64 lanes then move the row's index keys (bf16 copy or E4M3 cast).
+#include "csa2_internal.h"
+
+namespace csa2 {
+namespace {
+
+// E2M1 magnitude code of |x| under decoded scale s > 0: the count of midpoints
+// (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) * s below |x|; a value exactly on a
+// midpoint moves up only when the upper neighbour's code is even.  Every
+// midpoint * s is exact in fp32 (<= 3 significant bits times <= 4).
+__device__ __forceinline__ uint32_t e2m1_mag(float ax, float s) {
+  uint32_t c = 0;
+  c += (ax > 0.25f * s);
+  c += (ax >= 0.75f * s);   // tie -> code 2 (even)
+  c += (ax > 1.25f * s);
+  c += (ax >= 1.75f * s);   // tie -> code 4
+  c += (ax > 2.5f * s);
+  c += (ax >= 3.5f * s);    // tie -> code 6
+  c += (ax > 5.0f * s);
+  return c;
+}
+
+__global__ void __launch_bounds__(256) kv_append_kernel(
+    uint8_t *__restrict__ kv_codes, uint8_t *__restrict__ kv_scales, void *__restrict__ idx_k,
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ idx_in, const int32_t *__restrict__ seq,
+    const int32_t *__restrict__ pos, int32_t n, int32_t capacity, int32_t idx_elems,
+    int32_t idx_fp8) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (row >= n) return;
+  const int64_t slot = (int64_t)seq[row] * capacity + pos[row];
+
+  if (lane < 16) {
+    const bool is_v = lane >= 8;
+    const int blk = lane & 7;
+    const uint16_t *src = (is_v ? v : k) + (int64_t)row * 128 + blk * 16;
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
+    uint4 a = s4[0], b = s4[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    // amax is a bf16 value; the correctly rounded quotient never lands on an
+    // E4M3 midpoint unless the exact quotient does, so rounding it to E4M3
+    // equals rounding the exact amax/6.
+    const uint32_t sc = e4m3_from_f32_nonneg(amax / 6.0f);
+    const float s = e4m3_to_f32(sc);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t c = s > 0.0f ? e2m1_mag(fabsf(x[i]), s) : 0u;
+      c |= (__float_as_uint(x[i]) >> 28) & 8u;   // sign bit, -0 kept
+      if (i < 8) lo |= c << (4 * i);
+      else hi |= c << (4 * (i - 8));
+    }
+    uint2 *dst = reinterpret_cast<uint2 *>(kv_codes + slot * 128 + (is_v ? 64 : 0) + blk * 8);
+    *dst = make_uint2(lo, hi);
+    kv_scales[slot * 16 + (is_v ? 8 : 0) + blk] = (uint8_t)sc;
+  }
+
+  if (idx_in != nullptr) {
+    // idx_elems = idx_heads * 64 bf16 values (256 or 512): 8 per lane-step.
+    const uint16_t *src = idx_in + (int64_t)row * idx_elems;
+    for (int e = lane * 8; e < idx_elems; e += kWave * 8) {
+      uint4 a = *reinterpret_cast<const uint4 *>(src + e);
+      if (idx_fp8) {
+        uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        uint32_t out[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+          float f = __uint_as_float(h << 16);
+          uint32_t c = e4m3_from_f32_nonneg(fabsf(f)) | ((h >> 8) & 0x80u);
+          out[i >> 2] |= c << (8 * (i & 3));
+        }
+        uint8_t *dst = static_cast<uint8_t *>(idx_k) + slot * idx_elems + e;
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(out[0], out[1]);
+      } else {
+        uint16_t *dst = static_cast<uint16_t *>(idx_k) + slot * idx_elems + e;
+        *reinterpret_cast<uint4 *>(dst) = a;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const csa2_cache &c, const uint16_t *k, const uint16_t *v,
+                            const uint16_t *idx_in, const int32_t *seq, const int32_t *pos,
+                            int32_t n, hipStream_t stream) {
+  const int rows_per_block = 4;
+  dim3 grid((n + rows_per_block - 1) / rows_per_block);
+  const int32_t idx_elems = c.idx_heads * c.idx_dim;
+  hipLaunchKernelGGL(kv_append_kernel, grid, dim3(rows_per_block * kWave), 0, stream, c.kv_codes,
+                     c.kv_scales, c.idx_k, k, v, idx_in, seq, pos, n, c.capacity, idx_elems,
+                     (int32_t)(c.idx_k_dtype == CSA2_FP8_E4M3));
+  return hipGetLastError();
+}
+
+}  // namespace csa2

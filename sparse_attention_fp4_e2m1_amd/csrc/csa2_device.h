@@ -1,0 +1,87 @@
+// Device helpers shared by the CSA2 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// OCP E4M3FN code -> float (exact).  0x7F/0xFF never reach here (finite data).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  uint32_t e = (code >> 3) & 15u;
+  uint32_t m = code & 7u;
+  float mag = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (code & 0x80u) ? -mag : mag;
+}
+
+// Non-negative finite float -> E4M3 code, round to nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_from_f32_nonneg(float y) {
+  if (!(y < 448.0f)) return 0x7Eu;                     // saturate (also y == 448)
+  if (y < 0x1p-6f) {                                    // subnormal range: multiples of 2^-9
+    return (uint32_t)__builtin_rintf(y * 512.0f);      // exact scaling; rint = ties to even
+  }
+  uint32_t u = __float_as_uint(y);
+  // keep 3 mantissa bits: round the low 20 bits to nearest even (carry may bump the exponent)
+  uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;
+  uint32_t e = (r >> 3) - 120u;                         // rebias 127 -> 7
+  uint32_t code = (e << 3) | (r & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Order-preserving key of an fp32 score; -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int mask) {
+  return (uint32_t)__shfl_xor((int)v, mask, kWave);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    uint32_t t = (uint32_t)__shfl_up((int)v, d, kWave);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over the block; `scratch` holds >= blockDim/64 + 1 words.
+// Returns the exclusive prefix, writes the block total.  Contains barriers.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
+                                                         uint32_t &total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  uint32_t inc = wave_inclusive_scan(v);
+  __syncthreads();
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      uint32_t t = scratch[w];
+      scratch[w] = acc;
+      acc += t;
+    }
+    scratch[nwaves] = acc;
+  }
+  __syncthreads();
+  total = scratch[nwaves];
+  return scratch[wave] + inc - v;
+}
+
+}  // namespace csa2

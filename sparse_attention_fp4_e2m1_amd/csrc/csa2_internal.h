@@ -1,0 +1,72 @@
+// Internal launchers of the CSA2 library (host side), one translation unit each.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+#include "csa2_device.h"
+
+namespace csa2 {
+
+constexpr int kHistBins = 4096;      // first radix pass: top 12 bits of the score key
+constexpr int kPoolBlock = 8;        // positions per candidate-pool block
+
+hipError_t launch_kv_append(const csa2_cache &c, const uint16_t *k, const uint16_t *v,
+                            const uint16_t *idx_in, const int32_t *seq, const int32_t *pos,
+                            int32_t n, hipStream_t stream);
+
+// Workspace carve-up of csa2_index_topk (byte offsets, 256-B aligned).
+struct TopkWorkspace {
+  size_t keys_tok = 0;     // uint32 [nq][n_tok]  score keys of the candidates
+  size_t hist_tok = 0;     // uint32 [nq][kHistBins]
+  size_t keys_blk = 0;     // uint32 [nq][n_blk]  block-max keys (pool)
+  size_t hist_blk = 0;     // uint32 [nq][kHistBins]
+  size_t total = 0;
+  int64_t n_tok = 0;       // candidate slots per query
+  int64_t n_blk = 0;       // block slots per query (0 without pool)
+};
+
+TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t nq,
+                                    int32_t pool_len, int32_t pool_blocks);
+
+struct IndexArgs {
+  const csa2_cache *cache;
+  csa2_mode mode;
+  const uint16_t *q_idx;
+  int32_t q_fp8;
+  const int32_t *q_seq;
+  const int32_t *q_pos;
+  int32_t nq;
+  int32_t top_k;
+  const int32_t *pool_in;
+  int32_t pool_len;
+  int32_t pool_blocks;
+  int32_t *pool_out;
+  const int32_t *reuse_src;
+  int32_t *topk_out;
+  uint8_t *ws;
+  TopkWorkspace layout;
+};
+
+hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream);
+
+struct AttnWorkspace {
+  size_t part_acc = 0;     // float [nq][splits][heads][dv]
+  size_t part_ml = 0;      // float2 [nq][splits][heads]  (max, sum) of exp2-scaled scores
+  size_t total = 0;
+  int32_t splits = 0;
+};
+
+AttnWorkspace attn_workspace_layout(const csa2_cache &c, int32_t nq, int32_t n_heads,
+                                    int32_t top_k);
+
+hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_heads,
+                              const int32_t *q_seq, int32_t nq, const int32_t *topk,
+                              int32_t top_k, float softmax_scale, float *out, float *lse,
+                              uint8_t *ws, const AttnWorkspace &layout, hipStream_t stream);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace csa2

@@ -1,0 +1,66 @@
+"""One CSA2 step over a stack of layers, as a sequence of C-ABI calls.
+
+aiwiki "DeepSeek V4.1-Flash", section "Compressed Sparse Attention 2": every
+layer has a static mode.  A Full layer scores the shared index keys and makes a
+fresh Top-K (the decoder's first Full layer also builds the candidate pool); a
+Reindex layer scores the pool (or everything visible) with its own query; a
+Reuse layer recycles an earlier layer's Top-K.  Every layer then attends over
+its Top-K rows of the shared FP4 main KV.
+
+All buffers (Top-K lists, pools, outputs, workspaces) are allocated once in the
+constructor, so a step only enqueues kernels and can be captured in a graph.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import csa2 as B
+
+
+class LayerStack:
+    def __init__(self, cache: B.Cache, layers: Sequence, nq: int, heads: int, top_k: int,
+                 q_idx_dtype: str = "bf16", softmax_scale: Optional[float] = None):
+        self.cache, self.layers, self.nq, self.heads, self.top_k = cache, list(layers), nq, heads, top_k
+        self.q_idx_dtype = q_idx_dtype
+        self.softmax_scale = softmax_scale
+        d = cache.device
+        self.topk = [torch.full((nq, top_k), -1, dtype=torch.int32, device=d) for _ in self.layers]
+        self.pool = [torch.full((nq, 8 * L.pool_blocks), -1, dtype=torch.int32, device=d)
+                     if (L.mode == "full" and L.pool_blocks > 0) else None for L in self.layers]
+        self.out = [torch.zeros((nq, heads, cache.dv), dtype=torch.float32, device=d) for _ in self.layers]
+        self.lse = [torch.zeros((nq, heads), dtype=torch.float32, device=d) for _ in self.layers]
+        ws = 0
+        for L in self.layers:
+            pool_len = 8 * self.layers[L.pool_from].pool_blocks if (L.mode == "reindex" and L.pool_from >= 0) else 0
+            ws = max(ws, B.csa2_index_topk_workspace(cache, L.mode, nq, top_k, pool_len,
+                                                     L.pool_blocks if L.mode == "full" else 0))
+        self.ws_topk = torch.empty(max(ws, 256), dtype=torch.uint8, device=d)
+        self.ws_attn = torch.empty(max(B.csa2_sparse_attn_workspace(cache, nq, heads, top_k), 256),
+                                   dtype=torch.uint8, device=d)
+
+    def run(self, q: Sequence[torch.Tensor], q_idx: Sequence[torch.Tensor], q_seq: torch.Tensor,
+            q_pos: torch.Tensor, append: Optional[tuple] = None, stream=None):
+        """Enqueue one step: optional append (k, v, idx_k, seq, pos), then every layer."""
+        if append is not None:
+            k, v, ik, seq, pos = append
+            B.csa2_kv_append(self.cache, k, v, ik, seq, pos, stream=stream)
+        for li, L in enumerate(self.layers):
+            if L.mode == "reuse":
+                B.csa2_index_topk(self.cache, "reuse", None, None, None, self.top_k,
+                                  reuse_src=self.topk[L.reuse_from], topk_out=self.topk[li],
+                                  stream=stream)
+            elif L.mode == "full":
+                B.csa2_index_topk(self.cache, "full", q_idx[li], q_seq, q_pos, self.top_k,
+                                  q_dtype=self.q_idx_dtype, pool_blocks=L.pool_blocks,
+                                  topk_out=self.topk[li], pool_out=self.pool[li],
+                                  workspace=self.ws_topk, stream=stream)
+            else:
+                pool_in = self.pool[L.pool_from] if L.pool_from >= 0 else None
+                B.csa2_index_topk(self.cache, "reindex", q_idx[li], q_seq, q_pos, self.top_k,
+                                  q_dtype=self.q_idx_dtype, pool_in=pool_in,
+                                  topk_out=self.topk[li], workspace=self.ws_topk, stream=stream)
+            B.csa2_sparse_attn(self.cache, q[li], q_seq, self.topk[li],
+                               softmax_scale=self.softmax_scale, out=self.out[li],
+                               lse=self.lse[li], workspace=self.ws_attn, stream=stream)

@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every declared entry point, and validates
+its arguments on the host (no GPU needed: every call here is rejected before
+anything is enqueued, or only queries sizes)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_attention_fp4_e2m1_amd import csa2 as b
+    return b
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for want in ("csa2_kv_append", "csa2_index_topk", "csa2_sparse_attn",
+                 "csa2_index_topk_workspace", "csa2_sparse_attn_workspace",
+                 "csa2_strerror", "csa2_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert lib.LIB.csa2_abi_version() == 1
+
+
+def _cache(lib, **kw):
+    c = dict(kv_codes=1 << 20, kv_scales=1 << 21, idx_k=1 << 22, batch=2, capacity=4096, dk=128,
+             dv=128, idx_heads=8, idx_dim=64, idx_k_dtype=1)
+    c.update(kw)
+    return lib.csa2_cache(**c)
+
+
+def test_strerror_covers_all_codes(lib):
+    for s in range(7):
+        assert lib.LIB.csa2_strerror(s)
+    assert b"unknown" in lib.LIB.csa2_strerror(99)
+
+
+def test_append_validation(lib):
+    L = lib.LIB
+    P = ctypes.c_void_p
+    assert L.csa2_kv_append(None, P(1), P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_NULL
+    c = _cache(lib, dk=64)
+    assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_UNSUPPORTED
+    c = _cache(lib, idx_heads=6)
+    assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_UNSUPPORTED
+    c = _cache(lib)
+    assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), -1, None) == lib.CSA2_ERR_SHAPE
+    assert L.csa2_kv_append(ctypes.byref(c), None, P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_NULL
+    assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 0, None) == lib.CSA2_OK
+    c = _cache(lib, idx_k=None)
+    assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), P(1), P(1), P(1), 4, None) == lib.CSA2_ERR_NULL
+    c = _cache(lib, batch=0)
+    assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_SHAPE
+
+
+def test_index_topk_validation(lib):
+    L = lib.LIB
+    P = ctypes.c_void_p
+    c = ctypes.byref(_cache(lib))
+
+    def call(mode=0, nq=2, top_k=16, pool_in=None, pool_len=0, pool_blocks=0, pool_out=None,
+             reuse=None, out=P(1), q=P(1), ws=P(1), ws_bytes=1 << 40):
+        return L.csa2_index_topk(c, mode, q, 0, P(1), P(1), nq, top_k, pool_in, pool_len,
+                                 pool_blocks, pool_out, reuse, out, ws, ws_bytes, None)
+
+    assert call(top_k=0) == lib.CSA2_ERR_SHAPE
+    assert call(top_k=(1 << 16) + 1) == lib.CSA2_ERR_SHAPE
+    assert call(nq=-1) == lib.CSA2_ERR_SHAPE
+    assert call(mode=7) == lib.CSA2_ERR_ARG
+    assert call(out=None) == lib.CSA2_ERR_NULL
+    assert call(q=None) == lib.CSA2_ERR_NULL
+    assert call(pool_blocks=4) == lib.CSA2_ERR_ARG                 # pool_out missing
+    assert call(mode=0, pool_in=P(1), pool_len=8) == lib.CSA2_ERR_ARG
+    assert call(mode=1, pool_blocks=4, pool_out=P(1)) == lib.CSA2_ERR_ARG
+    assert call(mode=1, pool_in=None, pool_len=8) == lib.CSA2_ERR_ARG
+    assert call(mode=2) == lib.CSA2_ERR_ARG                         # reuse_src missing
+    assert call(mode=0, reuse=P(1)) == lib.CSA2_ERR_ARG
+    assert call(ws=None) == lib.CSA2_ERR_WORKSPACE
+    assert call(ws_bytes=16) == lib.CSA2_ERR_WORKSPACE
+    assert call(nq=0) == lib.CSA2_OK
+    assert call(mode=2, reuse=P(1), nq=0) == lib.CSA2_OK
+
+
+def test_workspace_queries(lib):
+    L = lib.LIB
+    c = ctypes.byref(_cache(lib))
+    full = L.csa2_index_topk_workspace(c, 0, 4, 256, 0, 0)
+    pool = L.csa2_index_topk_workspace(c, 0, 4, 256, 0, 64)
+    reidx = L.csa2_index_topk_workspace(c, 1, 4, 256, 512, 0)
+    assert full >= 4 * 4096 * 4 and pool > full and 0 < reidx < full
+    assert L.csa2_index_topk_workspace(c, 2, 4, 256, 0, 0) == 0
+    assert L.csa2_index_topk_workspace(c, 0, 4, 0, 0, 0) == 0      # invalid -> 0
+    attn = L.csa2_sparse_attn_workspace(c, 4, 64, 2048)
+    assert attn >= 4 * 32 * 64 * 128 * 4
+    assert L.csa2_sparse_attn_workspace(c, 4, 24, 2048) == 0
+
+
+def test_sparse_attn_validation(lib):
+    L = lib.LIB
+    P = ctypes.c_void_p
+    c = ctypes.byref(_cache(lib))
+
+    def call(n_heads=64, nq=2, top_k=64, q=P(1), ws=P(1), ws_bytes=1 << 40):
+        return L.csa2_sparse_attn(c, q, n_heads, P(1), nq, P(1), top_k, 0.1, P(1), None, ws,
+                                  ws_bytes, None)
+
+    assert call(n_heads=24) == lib.CSA2_ERR_UNSUPPORTED
+    assert call(n_heads=144) == lib.CSA2_ERR_UNSUPPORTED
+    assert call(top_k=0) == lib.CSA2_ERR_SHAPE
+    assert call(q=None) == lib.CSA2_ERR_NULL
+    assert call(ws=None) == lib.CSA2_ERR_WORKSPACE
+    assert call(ws_bytes=8) == lib.CSA2_ERR_WORKSPACE
+    assert call(nq=0) == lib.CSA2_OK

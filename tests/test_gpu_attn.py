@@ -1,0 +1,95 @@
+"""GPU parity of csa2_sparse_attn against the oracle's fp64 attention on the
+same index lists: per (query, head) max_c |delta| / max_c |o_ref| <= 2e-3 and
+|delta lse| <= 2e-3."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import csa2 as O
+from gpu_util import ATTN_TOL, DEFAULT_SCALE, DEV, announce, attn_errors, dev_i32, dev_u16, \
+    filled_caches, host, lib
+
+pytestmark = pytest.mark.gpu
+
+_CACHES = {}
+
+
+def _setup(heads):
+    if heads not in _CACHES:
+        wl = synth.workload("tiny_4k", context=3000, batch=3, heads=heads)
+        gc, oc, _ = filled_caches(wl)
+        _CACHES[heads] = (wl, gc, oc)
+    return _CACHES[heads]
+
+
+def _run(gc, q_bits, topk, scale=None):
+    m = lib()
+    nq = q_bits.shape[0]
+    out, lse = m.csa2_sparse_attn(gc, dev_u16(q_bits), dev_i32(np.arange(nq) % gc.batch),
+                                  dev_i32(topk), softmax_scale=scale)
+    torch.cuda.synchronize()
+    return host(out), host(lse)
+
+
+def _oracle(oc, q_bits, topk, scale=DEFAULT_SCALE):
+    outs, lses = [], []
+    for i in range(q_bits.shape[0]):
+        o, l = O.sparse_attention(q_bits[i], oc, i % oc.batch, topk[i], scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+@pytest.mark.parametrize("heads", [16, 64, 48])
+@pytest.mark.parametrize("top_k", [1, 64, 100, 2048])
+def test_attention_random_lists(heads, top_k):
+    announce(f"attn heads={heads} k={top_k}")
+    wl, gc, oc = _setup(heads)
+    qd = synth.gen_queries(wl, 0)
+    rng = np.random.default_rng(top_k + heads)
+    topk = rng.integers(0, 3000, (3, top_k)).astype(np.int32)
+    topk[1, rng.random(top_k) < 0.3] = -1          # holes
+    if top_k > 1:
+        topk[2, : top_k // 2] = topk[2, 0]          # duplicates
+    out, lse = _run(gc, qd.q, topk)
+    ref_o, ref_l = _oracle(oc, qd.q, topk)
+    rel, dl = attn_errors(out, lse, ref_o, ref_l)
+    assert rel.max() <= ATTN_TOL, rel.max()
+    assert dl.max() <= ATTN_TOL, dl.max()
+
+
+def test_attention_empty_and_single():
+    announce("attn empty/single")
+    wl, gc, oc = _setup(64)
+    qd = synth.gen_queries(wl, 1)
+    topk = np.full((3, 130), -1, np.int32)
+    topk[1, 77] = 1234
+    out, lse = _run(gc, qd.q, topk)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    _, v = oc.kv_values(1, np.array([1234]))
+    assert np.array_equal(out[1], np.broadcast_to(v[0], out[1].shape).astype(np.float32))
+    ref_o, ref_l = _oracle(oc, qd.q, topk)
+    rel, dl = attn_errors(out, lse, ref_o, ref_l)
+    assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL
+
+
+def test_attention_custom_scale():
+    announce("attn scale")
+    wl, gc, oc = _setup(16)
+    qd = synth.gen_queries(wl, 2)
+    topk = np.random.default_rng(3).integers(0, 3000, (3, 300)).astype(np.int32)
+    out, lse = _run(gc, qd.q, topk, scale=0.3)
+    ref_o, ref_l = _oracle(oc, qd.q, topk, scale=float(np.float32(0.3)))
+    rel, dl = attn_errors(out, lse, ref_o, ref_l)
+    assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL
+
+
+def test_attention_deterministic():
+    announce("attn determinism")
+    wl, gc, oc = _setup(64)
+    qd = synth.gen_queries(wl, 0)
+    topk = np.random.default_rng(5).integers(0, 3000, (3, 2048)).astype(np.int32)
+    a = _run(gc, qd.q, topk)
+    b = _run(gc, qd.q, topk)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

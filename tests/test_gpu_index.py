@@ -1,0 +1,169 @@
+"""GPU parity of csa2_index_topk in Full / Reindex / Reuse mode, with and
+without the candidate pool: Top-K index sets and pools bit-exact against the
+oracle (the decode scorer follows the canonical fp32 order, so the scores
+themselves are compared bit for bit too)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import csa2 as O
+from gpu_util import DEV, announce, dev_i32, dev_u16, filled_caches, host, lib
+
+pytestmark = pytest.mark.gpu
+
+CAP = 5000                       # several 2048-candidate tiles and a ragged tail
+QPOS = [0, 5, 63, 2047, 2148, 4999]
+
+
+def _score_keys(scores):
+    u = (np.asarray(scores, np.float32) + np.float32(0.0)).view(np.uint32)
+    return np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+
+
+_SETUPS = {}
+
+
+def _setup(heads, idx_dtype, seed=1):
+    key = (heads, idx_dtype, seed)
+    if key not in _SETUPS:
+        wl = synth.workload("decode_64k_b32", context=CAP, batch=len(QPOS), idx_heads=heads,
+                            idx_k_dtype=idx_dtype, seed=seed)
+        gc, oc, _ = filled_caches(wl)
+        _SETUPS[key] = (wl, gc, oc)
+    return _SETUPS[key]
+
+
+def _oracle_full(wl, oc, qd, q_dtype, top_k, pool_blocks=0, layer_q=None):
+    tk, pools, scores = [], [], []
+    for i, p in enumerate(QPOS):
+        qi = O.query_index_values(qd.q_idx[i], q_dtype)
+        t, pool, s, _ = O.index_topk("full", oc, i, p, qi, top_k, pool_blocks=pool_blocks)
+        tk.append(t)
+        pools.append(pool)
+        scores.append(s)
+    return np.stack(tk), pools, scores
+
+
+@pytest.mark.parametrize("heads,idx_dtype,q_dtype", [
+    (8, "fp8", "bf16"), (4, "bf16", "bf16"), (8, "fp8", "fp8"), (4, "fp8", "bf16"),
+    (8, "bf16", "bf16"), (4, "bf16", "fp8")])
+@pytest.mark.parametrize("top_k", [1, 37, 256, 3000])
+def test_full_topk_bit_exact(heads, idx_dtype, q_dtype, top_k):
+    announce(f"full topk heads={heads} idx={idx_dtype} q={q_dtype} k={top_k}")
+    m = lib()
+    wl, gc, oc = _setup(heads, idx_dtype)
+    qd = synth.gen_queries(wl, 0)
+    ws_bytes = m.csa2_index_topk_workspace(gc, "full", len(QPOS), top_k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    topk, _ = m.csa2_index_topk(gc, "full", dev_u16(qd.q_idx), dev_i32(np.arange(len(QPOS))),
+                                dev_i32(QPOS), top_k, q_dtype=q_dtype, workspace=ws)
+    torch.cuda.synchronize()
+    want, _, scores = _oracle_full(wl, oc, qd, q_dtype, top_k)
+    # scores: the workspace starts with the per-query score keys [nq][roundup64(capacity)]
+    n_tok = (CAP + 63) // 64 * 64
+    keys = host(ws[: len(QPOS) * n_tok * 4].view(torch.int32)).view(np.uint32).reshape(len(QPOS), n_tok)
+    for i, p in enumerate(QPOS):
+        assert np.array_equal(keys[i, :p + 1], _score_keys(scores[i])), f"scores of query {i}"
+    assert np.array_equal(host(topk), want)
+
+
+@pytest.mark.parametrize("pool_blocks", [1, 13, 300, 700])
+@pytest.mark.parametrize("heads,idx_dtype", [(8, "fp8"), (4, "bf16")])
+def test_full_pool_and_reindex_bit_exact(pool_blocks, heads, idx_dtype):
+    announce(f"pool={pool_blocks} heads={heads} idx={idx_dtype}")
+    m = lib()
+    wl, gc, oc = _setup(heads, idx_dtype)
+    top_k = 64
+    qd0 = synth.gen_queries(wl, 0)
+    qd1 = synth.gen_queries(wl, 1)
+    q_seq = dev_i32(np.arange(len(QPOS)))
+    q_pos = dev_i32(QPOS)
+    topk, pool = m.csa2_index_topk(gc, "full", dev_u16(qd0.q_idx), q_seq, q_pos, top_k,
+                                   pool_blocks=pool_blocks)
+    torch.cuda.synchronize()
+    want_tk, want_pool, _ = _oracle_full(wl, oc, qd0, "bf16", top_k, pool_blocks)
+    assert np.array_equal(host(topk), want_tk)
+    assert np.array_equal(host(pool), np.stack(want_pool))
+    # Reindex over that pool with the next layer's index query
+    rtk, _ = m.csa2_index_topk(gc, "reindex", dev_u16(qd1.q_idx), q_seq, q_pos, top_k, pool_in=pool)
+    torch.cuda.synchronize()
+    for i, p in enumerate(QPOS):
+        qi = O.query_index_values(qd1.q_idx[i], "bf16")
+        t, _, _, _ = O.index_topk("reindex", oc, i, p, qi, top_k, pool_in=want_pool[i])
+        assert np.array_equal(host(rtk)[i], t), f"reindex query {i}"
+
+
+def test_reindex_over_everything_equals_full():
+    announce("reindex over full pool == full")
+    m = lib()
+    wl, gc, oc = _setup(8, "fp8")
+    qd = synth.gen_queries(wl, 0)
+    q_seq = dev_i32(np.arange(len(QPOS)))
+    q_pos = dev_i32(QPOS)
+    pb = (CAP + 7) // 8
+    full, pool = m.csa2_index_topk(gc, "full", dev_u16(qd.q_idx), q_seq, q_pos, 100, pool_blocks=pb)
+    re, _ = m.csa2_index_topk(gc, "reindex", dev_u16(qd.q_idx), q_seq, q_pos, 100, pool_in=pool)
+    re2, _ = m.csa2_index_topk(gc, "reindex", dev_u16(qd.q_idx), q_seq, q_pos, 100)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(full), host(re))
+    assert np.array_equal(host(full), host(re2))
+
+
+def test_reindex_crafted_pool_with_holes_and_invisible_entries():
+    announce("reindex crafted pool")
+    m = lib()
+    wl, gc, oc = _setup(8, "fp8")
+    qd = synth.gen_queries(wl, 2)
+    rng = np.random.default_rng(7)
+    pool_len = 777
+    pools = np.full((len(QPOS), pool_len), -1, np.int32)
+    for i in range(len(QPOS)):
+        cnt = int(rng.integers(0, pool_len))
+        pools[i, :cnt] = np.sort(rng.choice(CAP, cnt, replace=False))   # some beyond q_pos
+    tk, _ = m.csa2_index_topk(gc, "reindex", dev_u16(qd.q_idx), dev_i32(np.arange(len(QPOS))),
+                              dev_i32(QPOS), 50, pool_in=dev_i32(pools))
+    torch.cuda.synchronize()
+    for i, p in enumerate(QPOS):
+        qi = O.query_index_values(qd.q_idx[i], "bf16")
+        t, _, _, _ = O.index_topk("reindex", oc, i, p, qi, 50, pool_in=pools[i])
+        assert np.array_equal(host(tk)[i], t), f"query {i}"
+
+
+def test_reuse_copies_source():
+    announce("reuse")
+    m = lib()
+    wl, gc, oc = _setup(8, "fp8")
+    src = np.random.default_rng(0).integers(-1, CAP, (len(QPOS), 2048)).astype(np.int32)
+    out, pool = m.csa2_index_topk(gc, "reuse", None, None, None, 2048, reuse_src=dev_i32(src))
+    torch.cuda.synchronize()
+    assert pool is None and np.array_equal(host(out), src)
+
+
+@pytest.mark.parametrize("distinct", [1, 3])
+def test_tie_heavy_keys(distinct):
+    announce(f"ties distinct={distinct}")
+    m = lib()
+    cap = 3000
+    gc = m.Cache(2, cap, idx_heads=8, idx_k_dtype="fp8")
+    oc = O.OracleCache(2, cap, idx_heads=8, idx_k_dtype="fp8")
+    rng = np.random.default_rng(distinct)
+    base = synth.f32_to_bf16_bits(rng.standard_normal((distinct, 8, 64)).astype(np.float32))
+    ik = base[rng.integers(0, distinct, cap)]
+    kv = synth.f32_to_bf16_bits(rng.standard_normal((cap, 128)).astype(np.float32))
+    for b in range(2):
+        seq, pos = np.full(cap, b, np.int32), np.arange(cap, dtype=np.int32)
+        m.csa2_kv_append(gc, dev_u16(kv), dev_u16(kv), dev_u16(ik), dev_i32(seq), dev_i32(pos))
+        oc.append(kv, kv, ik, seq, pos)
+    qi = synth.f32_to_bf16_bits(rng.standard_normal((2, 8, 64)).astype(np.float32))
+    qpos = [2999, 1234]
+    tk, pool = m.csa2_index_topk(gc, "full", dev_u16(qi), dev_i32([0, 1]), dev_i32(qpos), 500,
+                                 pool_blocks=40)
+    torch.cuda.synchronize()
+    for i in range(2):
+        t, p, _, _ = O.index_topk("full", oc, i, qpos[i], O.query_index_values(qi[i], "bf16"), 500,
+                                  pool_blocks=40)
+        assert np.array_equal(host(tk)[i], t)
+        assert np.array_equal(host(pool)[i], p)
+    if distinct == 1:
+        assert list(host(tk)[0]) == list(range(500))
