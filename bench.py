@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Throughput of one CSA2 decode step on one MI355X; prints one JSON line.
+
+A step is one pass of the whole hot path over one batch: quantize-and-append
+of every sequence's newest row into the FP4 cache, then for every layer of the
+workload the index scoring + Top-K (Full / Reindex / Reuse, with the candidate
+pool) and the sparse attention over the selected rows.  Inputs are seeded
+synthetic tensors (``synth``) resident in HBM before the timed region.
+
+Headline workload: decode_64k_b32 (batch 32, 65536-token contexts, 64 query
+heads on one FP4 KV head, indexer 8x64 E4M3 keys, Top-K 2048).  The 1M-token
+decode (decode_1m) is measured in the same run and reported under "extra".
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-extra]
+                    [--no-cpu-baseline] [--graph] [--copy-probe MIB]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "CSA2 decode queries/s and achieved HBM GB/s (% of peak), 64K and 1M context"
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode_64k_b32")
+    p.add_argument("--no-extra", action="store_true", help="skip the 1M-context line item")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true", help="replay the step as a captured graph")
+    p.add_argument("--copy-probe", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+class Hip:
+    """hipEvent helpers (the runtime torch already loaded)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        f = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+class WorkloadRun:
+    """Cache filled with every row but the step's own, inputs resident on the GPU."""
+
+    def __init__(self, wl, dev):
+        import numpy as np
+        import torch
+        import synth
+        import sparse_attention_fp4_e2m1_amd as m
+        from sparse_attention_fp4_e2m1_amd.pipeline import LayerStack
+
+        self.wl = wl
+        t0 = time.time()
+        data = synth.gen_batch(wl, threads=16)
+        self.gen_s = time.time() - t0
+        u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.int32))).to(dev)
+        self.cache = m.Cache(wl.batch, wl.context, idx_heads=wl.idx_heads, idx_k_dtype=wl.idx_k_dtype)
+        pre = wl.context - wl.appended
+        for b in range(wl.batch):
+            for lo in range(0, pre, 1 << 18):
+                hi = min(pre, lo + (1 << 18))
+                m.csa2_kv_append(self.cache, u16(data.k[b, lo:hi]), u16(data.v[b, lo:hi]),
+                                 u16(data.ik[b, lo:hi]), i32(np.full(hi - lo, b)),
+                                 i32(np.arange(lo, hi)))
+        rb = np.repeat(np.arange(wl.batch), wl.appended)
+        rp = np.tile(np.arange(pre, wl.context), wl.batch)
+        self.append = (u16(data.k[rb, rp]), u16(data.v[rb, rp]), u16(data.ik[rb, rp]), i32(rb), i32(rp))
+        del data
+        qs = [synth.gen_queries(wl, li) for li in range(len(wl.layers))]
+        self.q = [u16(x.q) for x in qs]
+        self.q_idx = [u16(x.q_idx) for x in qs]
+        self.q_seq = i32(wl.query_seq())
+        self.q_pos = i32(wl.query_pos())
+        self.stack = LayerStack(self.cache, wl.layers, wl.nq, wl.heads, wl.top_k,
+                                q_idx_dtype=wl.q_idx_dtype)
+        torch.cuda.synchronize()
+        self.setup_s = time.time() - t0
+
+    def step(self, scan_events=None):
+        self.stack.run(self.q, self.q_idx, self.q_seq, self.q_pos, append=self.append,
+                       scan_events=scan_events)
+
+    # ---- algorithmic bytes (what the method must move; scratch and re-reads excluded)
+    def scan_bytes(self) -> int:
+        """Index keys streamed by the first Full layer's scoring kernel, plus its queries."""
+        wl = self.wl
+        vis = int((wl.query_pos().astype("int64") + 1).sum())
+        return vis * wl.idx_bytes_per_token() + wl.nq * wl.idx_heads * wl.idx_dim * 2
+
+    def step_bytes(self) -> int:
+        wl = self.wl
+        nq = wl.nq
+        total = 0
+        vis = int((wl.query_pos().astype("int64") + 1).sum())
+        total += wl.batch * wl.appended * (wl.dk * 2 + wl.dv * 2 + wl.idx_heads * wl.idx_dim * 2)  # append in
+        total += wl.batch * wl.appended * (144 + wl.idx_bytes_per_token())                       # append out
+        for L in wl.layers:
+            if L.mode == "full":
+                total += vis * wl.idx_bytes_per_token()
+                total += nq * wl.idx_heads * wl.idx_dim * 2
+                total += nq * wl.top_k * 4 + (nq * 8 * L.pool_blocks * 4 if L.pool_blocks else 0)
+            elif L.mode == "reindex":
+                pool = 8 * wl.layers[L.pool_from].pool_blocks if L.pool_from >= 0 else 0
+                cand = nq * pool if pool else vis
+                total += cand * wl.idx_bytes_per_token() + nq * pool * 4
+                total += nq * wl.idx_heads * wl.idx_dim * 2 + nq * wl.top_k * 4
+            else:
+                total += 2 * nq * wl.top_k * 4
+            total += nq * wl.top_k * (144 + 4)                   # selected rows + their indices
+            total += nq * wl.heads * (wl.dk * 2 + wl.dv * 4 + 4)  # q in, out + lse out
+        return total
+
+
+def time_run(run, steps, warmup, hip, use_graph=False):
+    import torch
+    for _ in range(warmup):
+        run.step()
+    torch.cuda.synchronize()
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run.step()
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(graph):
+            run.step()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            run.step(scan_events=evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    scan_ms = None
+    if graph is None:
+        scan_ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / steps
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    return (t1 - t0), scan_ms
+
+
+def score_kernel_sha() -> str:
+    src = os.path.join(ROOT, "sparse_attention_fp4_e2m1_amd", "csrc", "csa2_index.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per scoring launch from committed rocprofv3 counter runs, if they
+    were taken on the current scoring kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", "index_scan_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    if not rec or rec.get("kernel_sha") != score_kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def measure(name, steps, warmup, hip, use_graph):
+    import torch
+    import synth
+    wl = synth.workload(name)
+    dev = torch.device("cuda:0")
+    run = WorkloadRun(wl, dev)
+    elapsed, scan_ms = time_run(run, steps, warmup, hip, use_graph)
+    ms = elapsed * 1e3 / steps
+    qps = wl.nq * steps / elapsed
+    step_gbps = run.step_bytes() / (elapsed / steps) / 1e9
+    res = {
+        "value": qps, "ms_per_step": ms,
+        "step_hbm_gbps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": run.step_bytes(),
+        "setup_s": round(run.setup_s, 1),
+    }
+    if scan_ms is not None:
+        ach = run.scan_bytes() / (scan_ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": "score_kernel (index scan, first Full layer)",
+                           "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_for(name),
+                           "bytes_per_launch": run.scan_bytes(), "avg_launch_ms": scan_ms}
+    del run
+    torch.cuda.empty_cache()
+    return wl, res
+
+
+def cpu_baseline(name, n_sample=4):
+    """The oracle (as it stands) on a bounded sample of the same step: the first
+    n_sample queries with their full contexts, one step, one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import synth
+    from oracle import csa2 as O
+    wl = synth.workload(name)
+    samp = list(range(min(n_sample, wl.nq)))
+    oc = O.OracleCache(len(samp), wl.context, idx_heads=wl.idx_heads, idx_k_dtype=wl.idx_k_dtype)
+    pre = wl.context - wl.appended
+    rows = []
+    for i, b in enumerate(samp):
+        d = synth.gen_sequence(wl, b, threads=16)
+        oc.append(d.k[:pre], d.v[:pre], d.ik[:pre], np.full(pre, i), np.arange(pre))
+        rows.append((d.k[pre:], d.v[pre:], d.ik[pre:]))
+    qs = []
+    for li in range(len(wl.layers)):
+        q = synth.gen_queries(wl, li)
+        qs.append(synth.QueryData(q.q[samp], q.q_idx[samp]))
+    qpos = wl.query_pos()[samp]
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for i in range(len(samp)):
+            k, v, ik = rows[i]
+            oc.append(k, v, ik, np.full(wl.appended, i), np.arange(pre, wl.context))
+        O.run_layers(oc, wl.layers, np.arange(len(samp)), qpos, qs, wl.top_k, wl.q_idx_dtype)
+        t = time.perf_counter() - t0
+    return {"value": len(samp) / t, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(samp)} of {wl.nq} queries of {name} (full {wl.context}-token "
+                      f"contexts), one step incl. append, numpy oracle, 1 thread; {t:.1f} s"}
+
+
+def copy_probe(mib):
+    import torch
+    n = mib << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n}), flush=True)
+
+
+def main():
+    args = _args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    hip = Hip()
+    print(f"[bench] {args.workload}: setup + {args.warmup} warmup + {args.steps} timed steps",
+          file=sys.stderr, flush=True)
+    wl, res = measure(args.workload, args.steps, args.warmup, hip, args.graph)
+    line = {
+        "metric": METRIC, "value": res["value"], "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded numpy draws, shapes of the workload)",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context,
+                   "heads": wl.heads, "idx_heads": wl.idx_heads, "idx_k_dtype": wl.idx_k_dtype,
+                   "top_k": wl.top_k, "layers": [L.mode for L in wl.layers],
+                   "graph": bool(args.graph)},
+        "step_hbm_gbps": res["step_hbm_gbps"], "step_hbm_frac": res["step_hbm_frac"],
+        "roofline": res.get("roofline"),
+    }
+    if not args.no_extra and args.workload != "decode_1m":
+        print("[bench] decode_1m line item", file=sys.stderr, flush=True)
+        wl2, res2 = measure("decode_1m", args.steps, args.warmup, hip, args.graph)
+        line["extra"] = {"decode_1m": {k: res2[k] for k in
+                                       ("value", "ms_per_step", "step_hbm_gbps", "step_hbm_frac")}
+                         | {"roofline": res2.get("roofline")}}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

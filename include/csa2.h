@@ -187,6 +187,16 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
                              float softmax_scale, float *out, float *lse, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/*
+ * Profiling hook for callers that measure the index scan against the HBM
+ * roofline.  After a call with non-NULL events (two hipEvent_t), every
+ * csa2_index_topk call made later from the same host thread records `before`
+ * and `after` on its stream immediately around its scoring kernel, the one
+ * that streams the index keys.  csa2_profile_index_scan(NULL, NULL) turns the
+ * hook off.  The events are caller-owned; the library only records them.
+ */
+void csa2_profile_index_scan(void *before, void *after);
+
 /* Static description of a status code. */
 const char *csa2_strerror(csa2_status status);
 

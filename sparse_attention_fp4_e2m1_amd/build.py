@@ -1,6 +1,8 @@
 """Builds libcsa2.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m sparse_attention_fp4_e2m1_amd.build
+    python sparse_attention_fp4_e2m1_amd/build.py
+
+(Run it as a script: importing the package loads the library it builds.)
 """
 from __future__ import annotations
 

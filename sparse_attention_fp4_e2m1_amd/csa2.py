@@ -36,7 +36,7 @@ class csa2_cache(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m sparse_attention_fp4_e2m1_amd.build`")
+                          "`python sparse_attention_fp4_e2m1_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     C = ctypes.POINTER(csa2_cache)
@@ -46,6 +46,7 @@ def _load():
         "csa2_index_topk": (I32, [C, I32, P, I32, P, P, I32, I32, P, I32, I32, P, P, P, P, SZ, P]),
         "csa2_sparse_attn_workspace": (SZ, [C, I32, I32, I32]),
         "csa2_sparse_attn": (I32, [C, P, I32, P, I32, P, I32, F32, P, P, P, SZ, P]),
+        "csa2_profile_index_scan": (None, [P, P]),
         "csa2_strerror": (ctypes.c_char_p, [I32]),
         "csa2_abi_version": (ctypes.c_int, []),
     }

@@ -51,6 +51,10 @@ const char *csa2_strerror(csa2_status s) {
 
 int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
 
+void csa2_profile_index_scan(void *before, void *after) {
+  set_index_scan_events(static_cast<hipEvent_t>(before), static_cast<hipEvent_t>(after));
+}
+
 csa2_status csa2_kv_append(const csa2_cache *cache, const uint16_t *k, const uint16_t *v,
                            const uint16_t *idx_k_in, const int32_t *seq, const int32_t *pos,
                            int32_t n, void *stream) {

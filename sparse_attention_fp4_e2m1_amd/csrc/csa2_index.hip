@@ -362,7 +362,15 @@ void launch_score_pool(const IndexArgs &a, int64_t n, bool pool, hipStream_t s) 
   else launch_score<H, kFp8, false>(a, n, s);
 }
 
+thread_local hipEvent_t g_scan_before = nullptr;
+thread_local hipEvent_t g_scan_after = nullptr;
+
 }  // namespace
+
+void set_index_scan_events(hipEvent_t before, hipEvent_t after) {
+  g_scan_before = before;
+  g_scan_after = after;
+}
 
 TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t nq,
                                     int32_t pool_len, int32_t pool_blocks) {
@@ -409,6 +417,7 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
                          reinterpret_cast<uint32_t *>(a.ws + L.hist_blk), n);
   }
   // 2. scores
+  if (g_scan_before != nullptr) (void)hipEventRecord(g_scan_before, s);
   const int64_t n_cand = reindex_pool ? (int64_t)a.pool_len : (int64_t)c.capacity;
   const bool fp8 = c.idx_k_dtype == CSA2_FP8_E4M3;
   if (c.idx_heads == 8) {
@@ -418,6 +427,7 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
     if (fp8) launch_score_pool<4, true>(a, n_cand, pool, s);
     else launch_score_pool<4, false>(a, n_cand, pool, s);
   }
+  if (g_scan_after != nullptr) (void)hipEventRecord(g_scan_after, s);
   // 3. select
   const uint32_t *keys_tok = reinterpret_cast<const uint32_t *>(a.ws + L.keys_tok);
   const uint32_t *hist_tok = reinterpret_cast<const uint32_t *>(a.ws + L.hist_tok);

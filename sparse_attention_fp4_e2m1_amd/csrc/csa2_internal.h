@@ -52,6 +52,9 @@ struct IndexArgs {
 
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream);
 
+// Events recorded around the scoring kernel (csa2_profile_index_scan); per host thread.
+void set_index_scan_events(hipEvent_t before, hipEvent_t after);
+
 struct AttnWorkspace {
   size_t part_acc = 0;     // float [nq][splits][heads][dv]
   size_t part_ml = 0;      // float2 [nq][splits][heads]  (max, sum) of exp2-scaled scores

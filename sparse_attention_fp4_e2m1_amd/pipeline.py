@@ -41,8 +41,12 @@ class LayerStack:
                                    dtype=torch.uint8, device=d)
 
     def run(self, q: Sequence[torch.Tensor], q_idx: Sequence[torch.Tensor], q_seq: torch.Tensor,
-            q_pos: torch.Tensor, append: Optional[tuple] = None, stream=None):
-        """Enqueue one step: optional append (k, v, idx_k, seq, pos), then every layer."""
+            q_pos: torch.Tensor, append: Optional[tuple] = None, stream=None,
+            scan_events: Optional[tuple] = None):
+        """Enqueue one step: optional append (k, v, idx_k, seq, pos), then every layer.
+
+        scan_events: optional (before, after) hipEvent_t handles recorded around the
+        index-scan kernel of the first Full layer (csa2_profile_index_scan)."""
         if append is not None:
             k, v, ik, seq, pos = append
             B.csa2_kv_append(self.cache, k, v, ik, seq, pos, stream=stream)
@@ -52,10 +56,17 @@ class LayerStack:
                                   reuse_src=self.topk[L.reuse_from], topk_out=self.topk[li],
                                   stream=stream)
             elif L.mode == "full":
-                B.csa2_index_topk(self.cache, "full", q_idx[li], q_seq, q_pos, self.top_k,
-                                  q_dtype=self.q_idx_dtype, pool_blocks=L.pool_blocks,
-                                  topk_out=self.topk[li], pool_out=self.pool[li],
-                                  workspace=self.ws_topk, stream=stream)
+                if scan_events is not None:
+                    B.LIB.csa2_profile_index_scan(scan_events[0], scan_events[1])
+                try:
+                    B.csa2_index_topk(self.cache, "full", q_idx[li], q_seq, q_pos, self.top_k,
+                                      q_dtype=self.q_idx_dtype, pool_blocks=L.pool_blocks,
+                                      topk_out=self.topk[li], pool_out=self.pool[li],
+                                      workspace=self.ws_topk, stream=stream)
+                finally:
+                    if scan_events is not None:
+                        B.LIB.csa2_profile_index_scan(None, None)
+                        scan_events = None
             else:
                 pool_in = self.pool[L.pool_from] if L.pool_from >= 0 else None
                 B.csa2_index_topk(self.cache, "reindex", q_idx[li], q_seq, q_pos, self.top_k,
