@@ -74,11 +74,23 @@ typedef enum {
  *             magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6).
  *   kv_scales [batch][capacity][dk/16 + dv/16] bytes, E4M3 codes: the scale
  *             of K channels 16b..16b+15 at byte b, then the V scales.
- *   idx_k     [batch][capacity][idx_heads][idx_dim], bf16 bits or E4M3 codes
- *             (idx_k_dtype).
+ *   idx_k     index keys, bf16 bits or E4M3 codes (idx_k_dtype), idx_heads x
+ *             idx_dim per position, stored TILED so that the index scan reads
+ *             every 1 KB span with one coalesced wave load and each lane gets
+ *             one head of one position.  With E = bytes per element (1 or 2),
+ *             T = 64 / idx_heads positions per tile and C = 4 * E chunks of
+ *             16 bytes per head, element (position p, head h, channel c) of
+ *             sequence s lives at byte
+ *               s * capacity * idx_heads * idx_dim * E
+ *               + (p / T) * (64 * 64 * E)                  -- tile
+ *               + ((c * E) / 16) * 1024                    -- chunk
+ *               + ((p % T) * idx_heads + h) * 16           -- lane slot
+ *               + (c * E) % 16                             -- byte in chunk.
+ *             (For 8 heads of E4M3: tiles of 8 positions, 4 KB each.)
  * One cached position = dk/2 + dv/2 + dk/16 + dv/16 bytes of main KV
  * (144 B for dk = dv = 128) plus idx_heads * idx_dim * (1 or 2) bytes.
- * Supported: dk = dv = 128, idx_dim = 64, idx_heads in {4, 8}.
+ * Supported: dk = dv = 128, idx_dim = 64, idx_heads in {4, 8}; capacity a
+ * multiple of 16.
  */
 typedef struct csa2_cache {
   uint8_t *kv_codes;

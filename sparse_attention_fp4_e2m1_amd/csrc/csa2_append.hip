@@ -77,24 +77,35 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
   }
 
   if (idx_in != nullptr) {
-    // idx_elems = idx_heads * 64 bf16 values (256 or 512): 8 per lane-step.
+    // idx_elems = H * 64 bf16 values: 8 per lane-step, stored in the tiled
+    // layout (tiles of 64/H positions; [chunk][position-in-tile][head][16 B]).
+    const int H = idx_elems / 64;
+    const int T = kWave / H;
+    const int esz = idx_fp8 ? 1 : 2;
+    const int64_t p = pos[row];
+    const int64_t seq_bytes = (int64_t)capacity * idx_elems * esz;
+    uint8_t *tile = static_cast<uint8_t *>(idx_k) + (int64_t)seq[row] * seq_bytes +
+                    (p / T) * (64 * 64 * esz);
+    const int64_t slot16 = (p % T) * H;
     const uint16_t *src = idx_in + (int64_t)row * idx_elems;
     for (int e = lane * 8; e < idx_elems; e += kWave * 8) {
-      uint4 a = *reinterpret_cast<const uint4 *>(src + e);
+      const uint4 a = *reinterpret_cast<const uint4 *>(src + e);
+      const int h = e / 64;
+      const int ch = e % 64;
+      const int byte = ch * esz;                         // byte of channel ch within the head
+      uint8_t *dst = tile + (byte / 16) * 1024 + (slot16 + h) * 16 + byte % 16;
       if (idx_fp8) {
-        uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
         uint32_t out[2] = {0, 0};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          uint32_t h = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-          float f = __uint_as_float(h << 16);
-          uint32_t c = e4m3_from_f32_nonneg(fabsf(f)) | ((h >> 8) & 0x80u);
+          const uint32_t hb = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+          const float f = __uint_as_float(hb << 16);
+          const uint32_t c = e4m3_from_f32_nonneg(fabsf(f)) | ((hb >> 8) & 0x80u);
           out[i >> 2] |= c << (8 * (i & 3));
         }
-        uint8_t *dst = static_cast<uint8_t *>(idx_k) + slot * idx_elems + e;
         *reinterpret_cast<uint2 *>(dst) = make_uint2(out[0], out[1]);
       } else {
-        uint16_t *dst = static_cast<uint16_t *>(idx_k) + slot * idx_elems + e;
         *reinterpret_cast<uint4 *>(dst) = a;
       }
     }

@@ -34,6 +34,15 @@ __device__ __forceinline__ uint32_t e4m3_from_f32_nonneg(float y) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// Byte offset, within one sequence, of the 16-B chunk `chunk` of head h of
+// position p in the tiled index-key layout: tiles of 64/H positions, each
+// tile [chunk][position-in-tile][head][16 B].  esz = bytes per element.
+template <int H, int kEsz>
+__device__ __forceinline__ int64_t idx_chunk_offset(int64_t p, int h, int chunk) {
+  constexpr int T = kWave / H;
+  return (p / T) * (64 * 64 * kEsz) + chunk * 1024 + ((p % T) * H + h) * 16;
+}
+
 // Order-preserving key of an fp32 score; -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s + 0.0f);

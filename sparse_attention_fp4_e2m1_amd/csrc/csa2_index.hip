@@ -10,18 +10,23 @@
 // indexer bounds the deeper indexers' cost by the pool size.
 //
 // Kernels, in launch order for one call:
-//   zero_hist      clear the per-query radix histograms
-//   score_kernel   stream the index keys (16-B coalesced loads), compute the
-//                  canonical fp32 score of each candidate, store its
-//                  order-preserving key, histogram the top 12 key bits in LDS
-//                  (flushed with one global atomic per non-empty bin), and for
-//                  a pool-building Full layer the 8-block maxima + their histogram
-//   select_kernel  per query: radix-select the K-th largest key (passes on bits
-//                  19..8 and 7..0 after the histogram above), then an ordered
-//                  compaction that emits the winners in ascending position
-//                  order, ties to the lower position, -1 padding; for the pool
-//                  it emits the positions of the kept blocks.
-//   reuse_copy     Reuse mode: topk_out = reuse_src.
+//   zero2_u32_kernel clear the per-query histograms
+//   score_kernel     stream the (tiled) index keys, compute the canonical fp32
+//                    score of each candidate, keep its order-preserving key
+//                    (written out per workgroup in one burst), histogram the
+//                    top 12 key bits, and for a pool-building Full layer the
+//                    8-position block maxima and their histogram.
+//   bins_kernel      per query: the bin b1 of the 12-bit histogram holding the
+//                    K-th largest key.
+//   filter_kernel    per wave and 1024 keys: keep every key whose top 12 bits
+//                    reach b1, with its index, in index order (ballot compaction)
+//   resolve_kernel   per query: the candidates (typically K plus one bin) in
+//                    LDS; radix passes on bits 19..8 and 7..0 within bin b1 give
+//                    the K-th largest key tau; an ordered compaction emits every
+//                    key > tau and the first ties == tau, ascending, -1 padded.
+//                    With more candidates than LDS holds (heavy ties) it
+//                    streams the full key array with the same logic.
+//   copy_i32_kernel  Reuse mode: topk_out = reuse_src.
 #include <algorithm>
 
 #include "csa2_internal.h"
@@ -29,13 +34,29 @@
 namespace csa2 {
 namespace {
 
-constexpr int kScoreThreads = 256;
-constexpr int kScoreChunk = 2048;      // candidates per score workgroup (multiple of 64)
 constexpr int kSelectThreads = 1024;
+constexpr int kFilterThreads = 256;
+constexpr int kFilterSub = 1024;           // keys per filter wave (one candidate slot region)
+constexpr int kResolveCap = 8192;          // candidates held in LDS by the resolve
+constexpr int kStateWords = 16;            // per query after its histogram: see SelState
+
+// Selection state of one query and one key array, in the words after its histogram.
+enum SelState { kTicket = 0, kBin = 1, kAbove = 2, kKeff = 3 };
+
+#ifndef CSA2_SCORE_UNROLL
+#define CSA2_SCORE_UNROLL 4            // 16-B loads per lane per prefetch batch
+#endif
+#ifndef CSA2_SCORE_WAVES
+#define CSA2_SCORE_WAVES 4             // waves per SIMD the register budget allows
+#endif
+
+// Score launch shapes: (threads, candidates per workgroup).
+constexpr int64_t kBigChunkMinGroups = 512;   // use 4096-candidate chunks when >= this many groups
+constexpr int64_t kSmallGridGroups = 256;     // below this, one-wave groups of 64 candidates
 
 // ---------------------------------------------------------------------------
-// cross-lane sums inside groups of 32 lanes (commutative, so every lane of a
-// butterfly pair computes the same bits)
+// cross-lane sums inside quads / half rows (commutative, so both lanes of a
+// butterfly pair compute the same bits)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float dpp_xor1(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
@@ -43,15 +64,18 @@ __device__ __forceinline__ float dpp_xor1(float v) {
 __device__ __forceinline__ float dpp_xor2(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
-template <int kXor>
-__device__ __forceinline__ float swz_xor(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (kXor << 10)));
+// lane i <-> 7 - i within each group of 8: pairs quad 0 with quad 1
+__device__ __forceinline__ float dpp_half_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
 }
 
-__global__ void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n) {
+__global__ void zero2_u32_kernel(uint32_t *__restrict__ p, uint32_t *__restrict__ p2, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (; i < n; i += step) p[i] = 0u;
+  for (; i < n; i += step) {
+    p[i] = 0u;
+    if (p2 != nullptr) p2[i] = 0u;
+  }
 }
 
 __global__ void copy_i32_kernel(int32_t *__restrict__ dst, const int32_t *__restrict__ src,
@@ -62,162 +86,17 @@ __global__ void copy_i32_kernel(int32_t *__restrict__ dst, const int32_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// score_kernel
-//
-// Lane layout: a token's index keys (H heads x 64 channels) are split into
-// H*4 lane-blocks of 16 channels; lane `sub` = 4*h + j owns head h, channels
-// 16j..16j+15.  A wave covers TPI = 64 / (4H) tokens per load, so a load of
-// consecutive tokens is one contiguous, coalesced span.  Each lane runs the
-// canonical chain of 16 fused multiply-adds for its block; the block sums
-// combine with xor-1/xor-2 butterflies ((b0+b1)+(b2+b3)), the head sums with
-// xor-4/8/16 butterflies (a balanced tree over heads).
-// ---------------------------------------------------------------------------
-template <int H, bool kFp8Keys, bool kPool>
-__global__ void __launch_bounds__(kScoreThreads) score_kernel(
-    const uint8_t *__restrict__ idx_k, int64_t capacity, const uint16_t *__restrict__ q_idx,
-    int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
-    const int32_t *__restrict__ pool_in, int32_t pool_len, uint32_t *__restrict__ keys_tok,
-    int64_t tok_stride, uint32_t *__restrict__ hist_tok, uint32_t *__restrict__ keys_blk,
-    int64_t blk_stride, uint32_t *__restrict__ hist_blk) {
-  constexpr int kEsz = kFp8Keys ? 1 : 2;
-  constexpr int L = H * 4;                // lanes per token
-  constexpr int TPI = kWave / L;          // tokens per wave load
-  constexpr int kBpt = H * 64 * kEsz;     // bytes per token
-  constexpr int kLaneBytes = 16 * kEsz;   // bytes per lane-block
-  constexpr int kNumWaves = kScoreThreads / kWave;
-
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t histb[kPool ? kHistBins : 1];
-
-  const int q = blockIdx.y;
-  const int32_t qp = q_pos[q];
-  const int64_t n = pool_in ? (int64_t)pool_len : (int64_t)qp + 1;
-  const int64_t t_begin = (int64_t)blockIdx.x * kScoreChunk;
-  if (t_begin >= n) return;
-  const int64_t t_end = min(n, t_begin + kScoreChunk);
-
-  for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
-    hist[i] = 0u;
-    if (kPool) histb[i] = 0u;
-  }
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int sub = lane % L;
-  const int tl = lane / L;
-  const int h = sub >> 2;
-  const int j = sub & 3;
-
-  // this lane's 16 query channels, as scored (bf16, or cast to E4M3)
-  float qf[16];
-  {
-    const uint16_t *qs = q_idx + ((int64_t)q * H + h) * 64 + j * 16;
-    const uint4 a = *reinterpret_cast<const uint4 *>(qs);
-    const uint4 b = *reinterpret_cast<const uint4 *>(qs + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qf[2 * i] = __uint_as_float(w[i] << 16);
-      qf[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-    if (q_fp8) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t c = e4m3_from_f32_nonneg(fabsf(qf[i])) |
-                           ((__float_as_uint(qf[i]) >> 24) & 0x80u);
-        qf[i] = e4m3_to_f32(c);
-      }
-    }
-  }
-
-  const uint8_t *base = idx_k + (int64_t)q_seq[q] * capacity * kBpt + sub * kLaneBytes;
-  __syncthreads();
-
-  for (int64_t g = t_begin + (int64_t)wave * kWave; g < t_end; g += (int64_t)kNumWaves * kWave) {
-    uint32_t mykey = 0u;
-#pragma unroll 4
-    for (int i = 0; i < L; ++i) {
-      const int64_t t = g + (int64_t)i * TPI + tl;
-      bool valid = t < t_end;
-      int64_t row = t;
-      if (pool_in) {
-        row = valid ? (int64_t)pool_in[(int64_t)q * pool_len + t] : -1;
-        valid = valid && row >= 0 && row <= qp;
-      }
-      float kf[16];
-      if (kFp8Keys) {
-        uint4 a = make_uint4(0, 0, 0, 0);
-        if (valid) a = *reinterpret_cast<const uint4 *>(base + row * kBpt);
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
-          auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
-          kf[4 * k + 0] = lo[0];
-          kf[4 * k + 1] = lo[1];
-          kf[4 * k + 2] = hi[0];
-          kf[4 * k + 3] = hi[1];
-        }
-      } else {
-        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-        if (valid) {
-          a = *reinterpret_cast<const uint4 *>(base + row * kBpt);
-          b = *reinterpret_cast<const uint4 *>(base + row * kBpt + 16);
-        }
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          kf[2 * k] = __uint_as_float(w[k] << 16);
-          kf[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-        }
-      }
-      float acc = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) acc = __builtin_fmaf(qf[c], kf[c], acc);
-      acc = acc + dpp_xor1(acc);
-      acc = acc + dpp_xor2(acc);
-      acc = acc + swz_xor<4>(acc);
-      acc = acc + swz_xor<8>(acc);
-      if (H == 8) acc = acc + swz_xor<16>(acc);
-      if (sub == i) mykey = valid ? score_key(acc) : 0u;
-    }
-    // lane owns token g + sub*TPI + tl; permute so that lane l holds token g + l
-    const uint32_t key = (uint32_t)__shfl((int)mykey, (lane % TPI) * L + lane / TPI, kWave);
-    const int64_t t = g + lane;
-    if (t < t_end) {
-      keys_tok[(int64_t)q * tok_stride + t] = key;
-      atomicAdd(&hist[key >> 20], 1u);
-    }
-    if (kPool) {
-      // block maximum over lanes 8b..8b+7 (keys of tokens past the end count as 0)
-      uint32_t m = t < t_end ? key : 0u;
-      m = max(m, shfl_xor_u(m, 1));
-      m = max(m, shfl_xor_u(m, 2));
-      m = max(m, shfl_xor_u(m, 4));
-      if ((lane & (kPoolBlock - 1)) == 0 && t < t_end) {
-        keys_blk[(int64_t)q * blk_stride + t / kPoolBlock] = m;
-        atomicAdd(&histb[m >> 20], 1u);
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
-    if (hist[i]) atomicAdd(&hist_tok[(int64_t)q * kHistBins + i], hist[i]);
-    if (kPool && histb[i]) atomicAdd(&hist_blk[(int64_t)q * kHistBins + i], histb[i]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// select_kernel: one workgroup per query.
+// Selection helpers
 // ---------------------------------------------------------------------------
 enum OutMode { kOutPositions = 0, kOutPoolIds = 1, kOutPoolBlocks = 2 };
 
 // Finds the bin holding the element of rank `want` (1-based, counted from the
-// largest key) among `nbins` LDS bins; returns the bin and the number of
-// elements in higher bins.  All threads get the answer.  Contains barriers.
+// largest key) among `nbins` LDS bins; result = {bin, elements in higher bins}.
+// All threads of the block take part and see the result.  Contains barriers.
 __device__ void select_bin(const uint32_t *bins, int nbins, uint32_t want, uint32_t *scratch,
                            uint32_t *result) {
-  const int per = (nbins + kSelectThreads - 1) / kSelectThreads;  // 4 or 1
+  const int nt = blockDim.x;
+  const int per = (nbins + nt - 1) / nt;
   const int lo = threadIdx.x * per;
   uint32_t s = 0;
   for (int b = lo; b < lo + per && b < nbins; ++b) s += bins[b];
@@ -237,52 +116,350 @@ __device__ void select_bin(const uint32_t *bins, int nbins, uint32_t want, uint3
 }
 
 template <int kMode>
-__global__ void __launch_bounds__(kSelectThreads) select_kernel(
-    const uint32_t *__restrict__ keys, int64_t stride, const uint32_t *__restrict__ hist_g,
-    const int32_t *__restrict__ q_pos, const int32_t *__restrict__ pool_in, int32_t pool_len,
-    int32_t kk, int32_t *__restrict__ out, int64_t out_stride) {
-  __shared__ uint32_t hist[kHistBins];
+__device__ __forceinline__ int64_t array_len(int32_t qp, int32_t pool_len) {
+  if (kMode == kOutPoolBlocks) return ((int64_t)qp + 1 + kPoolBlock - 1) / kPoolBlock;
+  if (kMode == kOutPoolIds) return pool_len;
+  return (int64_t)qp + 1;
+}
+
+// ---------------------------------------------------------------------------
+// score_kernel
+//
+// Lane layout: lane l owns head h = l % H of token l / H, i.e. 64 channels =
+// 64 B (E4M3) or 128 B (bf16) of the token's index keys; a wave covers
+// TPI = 64 / H tokens per step = one tile of the tiled index-key layout, so
+// each of its 16-B loads is one contiguous 1 KB span across the wave.  Each
+// lane runs the canonical fp32 chains -- per 16-channel block, fused
+// multiply-adds in channel order -- as four independent chains, adds the
+// block sums as (b0+b1)+(b2+b3), and the head sums meet in a balanced tree
+// over lanes: xor-1, xor-2 (quad permutes) and xor-4 (half-row mirror; the
+// quads are uniform by then) DPP adds.  Every lane of a token ends with the
+// same bits.
+// ---------------------------------------------------------------------------
+template <int H, bool kFp8Keys, bool kPool, bool kReindexPool, int kThreads, int kChunk>
+struct ScoreCtx {
+  static constexpr int kEsz = kFp8Keys ? 1 : 2;
+  static constexpr int TPI = kWave / H;
+  static constexpr int kLoads = 4 * kEsz;
+  static constexpr int kNumWaves = kThreads / kWave;
+  const uint8_t *seq_base;
+  const int32_t *spool;    // this chunk's pool entries, staged in LDS (Reindex)
+  int32_t qp;
+  int64_t t_begin, t_end;
+  int wave, h, tl, lane;
+
+  // Step s of this wave covers tile s * kNumWaves + wave of the chunk, so at
+  // any step the workgroup's waves read adjacent tiles (one moving window).
+  __device__ __forceinline__ int64_t tile_start(int s) const {
+    return t_begin + ((int64_t)s * kNumWaves + wave) * TPI;
+  }
+  __device__ __forceinline__ int64_t token(int s) const { return tile_start(s) + tl; }
+
+  // loads of steps s0 .. s0+U-1; lanes past the end (or on an empty pool
+  // slot) read an in-bounds row and are masked
+  template <int U>
+  __device__ __forceinline__ void issue(int s0, uint4 (&buf)[U][kLoads], bool (&val)[U]) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = token(s0 + u);
+      bool valid = t < t_end;
+      int64_t row = valid ? t : t_begin;
+      if (kReindexPool) {
+        const int32_t p = valid ? spool[t - t_begin] : -1;
+        valid = valid && p >= 0 && p <= qp;
+        row = valid ? (int64_t)p : 0;
+      }
+      val[u] = valid;
+      // Full mode: row % TPI == tl, so a wave's loads cover one tile contiguously
+      const uint8_t *src = seq_base + idx_chunk_offset<H, kEsz>(row, h, 0);
+#pragma unroll
+      for (int v = 0; v < kLoads; ++v) buf[u][v] = *reinterpret_cast<const uint4 *>(src + v * 1024);
+    }
+  }
+
+  // canonical score of steps s0 .. s0+U-1; closes a group after its last step
+  template <int U>
+  __device__ __forceinline__ void score(int s0, const uint4 (&buf)[U][kLoads], const bool (&val)[U],
+                                        const float (&qf)[64], uint32_t &mykey, uint32_t *skeys,
+                                        uint32_t *hist, uint32_t *sblk, uint32_t *histb) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float blk[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float acc = 0.0f;
+        if (kFp8Keys) {
+          const uint4 a = buf[u][j];
+          const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
+            auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
+            acc = __builtin_fmaf(qf[16 * j + 4 * k + 0], lo[0], acc);
+            acc = __builtin_fmaf(qf[16 * j + 4 * k + 1], lo[1], acc);
+            acc = __builtin_fmaf(qf[16 * j + 4 * k + 2], hi[0], acc);
+            acc = __builtin_fmaf(qf[16 * j + 4 * k + 3], hi[1], acc);
+          }
+        } else {
+#pragma unroll
+          for (int hv = 0; hv < 2; ++hv) {
+            const uint4 a = buf[u][2 * j + hv];
+            const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              acc = __builtin_fmaf(qf[16 * j + 8 * hv + 2 * k], __uint_as_float(w[k] << 16), acc);
+              acc = __builtin_fmaf(qf[16 * j + 8 * hv + 2 * k + 1],
+                                   __uint_as_float(w[k] & 0xFFFF0000u), acc);
+            }
+          }
+        }
+        blk[j] = acc;
+      }
+      float acc = (blk[0] + blk[1]) + (blk[2] + blk[3]);
+      acc = acc + dpp_xor1(acc);
+      acc = acc + dpp_xor2(acc);
+      if (H == 8) acc = acc + dpp_half_mirror(acc);
+      const uint32_t key = val[u] ? score_key(acc) : 0u;
+      const int s = s0 + u;
+      mykey = (h == s % H) ? key : mykey;
+      if (s % H == H - 1) close_group(s / H, mykey, skeys, hist, sblk, histb);
+    }
+  }
+
+  // lane (tl, h) holds the key of step grp*H + h, token tl; permute so that
+  // lane l holds step grp*H + l/TPI, token l%TPI, then stage its key in LDS,
+  // count it, and take the 8-position block maxima (8 consecutive lanes = 8
+  // positions).  Histogram bins are 16-bit halves of LDS words.
+  __device__ __forceinline__ void close_group(int grp, uint32_t mykey, uint32_t *skeys,
+                                              uint32_t *hist, uint32_t *sblk, uint32_t *histb) const {
+    const uint32_t key = (uint32_t)__shfl((int)mykey, (lane % TPI) * H + lane / TPI, kWave);
+    const int64_t t = tile_start(grp * H + lane / TPI) + lane % TPI;
+    if (t < t_end) {
+      skeys[t - t_begin] = key;
+      atomicAdd(&hist[key >> 21], 1u << ((key >> 16) & 16u));
+    }
+    if (kPool) {
+      // block maximum over lanes 8b..8b+7 (keys of tokens past the end count as 0)
+      uint32_t m = t < t_end ? key : 0u;
+      m = max(m, shfl_xor_u(m, 1));
+      m = max(m, shfl_xor_u(m, 2));
+      m = max(m, shfl_xor_u(m, 4));
+      if ((lane & (kPoolBlock - 1)) == 0 && t < t_end) {
+        sblk[(t - t_begin) / kPoolBlock] = m;
+        atomicAdd(&histb[m >> 21], 1u << ((m >> 16) & 16u));
+      }
+    }
+  }
+};
+
+template <int H, bool kFp8Keys, bool kPool, bool kReindexPool, int kThreads, int kChunk>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kThreads == 64 ? 2 : (kFp8Keys ? CSA2_SCORE_WAVES : CSA2_SCORE_WAVES - 1))))
+score_kernel(
+    const uint8_t *__restrict__ idx_k, int64_t capacity, const uint16_t *__restrict__ q_idx,
+    int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
+    const int32_t *__restrict__ pool_in, int32_t pool_len,
+    uint32_t *__restrict__ keys_tok, int64_t tok_stride, uint32_t *__restrict__ hist_tok,
+    uint32_t *__restrict__ keys_blk, int64_t blk_stride, uint32_t *__restrict__ hist_blk) {
+  constexpr int kEsz = kFp8Keys ? 1 : 2;
+  constexpr int TPI = kWave / H;
+  constexpr int kBpt = H * 64 * kEsz;     // bytes per token
+  constexpr int kLoads = 4 * kEsz;        // 16-B loads per lane per token (64 channels)
+  constexpr int kNumWaves = kThreads / kWave;
+  constexpr int kUnroll = CSA2_SCORE_UNROLL / kLoads > 0 ? CSA2_SCORE_UNROLL / kLoads : 1;
+  static_assert(kChunk % (kWave * kNumWaves) == 0, "chunk shape");
+  constexpr int kMainWords = kHistBins / 2 + kChunk;
+
+  // LDS: 16-bit histogram bins packed in pairs, the chunk's keys (written out
+  // in one burst at the end: small stores interleaved with the read stream
+  // cost HBM efficiency), block maxima, the index query.
+  __shared__ uint32_t lds_main[kMainWords];
+  __shared__ uint32_t histb[kPool ? kHistBins / 2 : 1];
+  __shared__ uint32_t sblk[kPool ? kChunk / kPoolBlock : 1];
+  __shared__ float qlds[H * 64];
+  __shared__ int32_t spool[kReindexPool ? kChunk : 1];
+  uint32_t *hist = lds_main;
+  uint32_t *skeys = lds_main + kHistBins / 2;
+
+  const int q = blockIdx.y;
+  const int32_t qp = q_pos[q];
+  const int64_t n = kReindexPool ? (int64_t)pool_len : (int64_t)qp + 1;
+  const int64_t t_begin = (int64_t)blockIdx.x * kChunk;
+  if (t_begin >= n) return;
+  const int64_t t_end = min(n, t_begin + kChunk);
+
+  for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
+    hist[i] = 0u;
+    if (kPool) histb[i] = 0u;
+  }
+  // Reindex: the chunk's pool entries, staged once (no dependent load per gather)
+  if (kReindexPool)
+    for (int64_t i = threadIdx.x; i < t_end - t_begin; i += kThreads)
+      spool[i] = pool_in[(int64_t)q * pool_len + t_begin + i];
+  // the index query as scored (bf16, or cast to E4M3), staged once through LDS
+  for (int i = threadIdx.x; i < H * 64; i += kThreads) {
+    float f = bf16_to_f32(q_idx[(int64_t)q * H * 64 + i]);
+    if (q_fp8) f = e4m3_to_f32(e4m3_from_f32_nonneg(fabsf(f)) | ((__float_as_uint(f) >> 24) & 0x80u));
+    qlds[i] = f;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int h = lane % H;
+  const int tl = lane / H;
+  float qf[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) qf[i] = qlds[h * 64 + i];
+
+  // tiled index keys: the lane slot of (position-in-tile tl, head h) is `lane`
+  const uint8_t *seq_base = idx_k + (int64_t)q_seq[q] * capacity * kBpt;
+
+  // The wave walks its steps (one tile each; H steps make a group of 64
+  // tokens) with a ping-pong prefetch: the loads of the next kUnroll steps are
+  // in flight while the current ones are scored.  Every issue is
+  // unconditional (steps past the end read a masked in-bounds tile): with no
+  // branch around a prefetch the compiler waits only for the batch being
+  // scored.
+  const int64_t ntiles = (t_end - t_begin + TPI - 1) / TPI;
+  const int64_t wave_steps = (ntiles + kNumWaves - 1) / kNumWaves;
+  const int nsteps = (int)((wave_steps + H - 1) / H * H);
+  ScoreCtx<H, kFp8Keys, kPool, kReindexPool, kThreads, kChunk> cx{
+      seq_base, spool, qp, t_begin, t_end, wave, h, tl, lane};
+  uint4 bufA[kUnroll][kLoads], bufB[kUnroll][kLoads];
+  bool valA[kUnroll], valB[kUnroll];
+  uint32_t mykey = 0u;
+  static_assert(H % (2 * kUnroll) == 0, "steps per group must be a multiple of the ping-pong");
+  if (nsteps > 0) {
+    cx.template issue<kUnroll>(0, bufA, valA);
+    for (int s0 = 0; s0 < nsteps; s0 += 2 * kUnroll) {
+      cx.template issue<kUnroll>(s0 + kUnroll, bufB, valB);
+      cx.template score<kUnroll>(s0, bufA, valA, qf, mykey, skeys, hist, sblk, histb);
+      cx.template issue<kUnroll>(s0 + 2 * kUnroll, bufA, valA);
+      cx.template score<kUnroll>(s0 + kUnroll, bufB, valB, qf, mykey, skeys, hist, sblk, histb);
+    }
+  }
+  __syncthreads();
+
+  // the chunk's keys and block maxima in one burst of coalesced stores
+  const int64_t cnt = t_end - t_begin;
+  {
+    uint32_t *dst = keys_tok + (int64_t)q * tok_stride + t_begin;
+    for (int64_t i = threadIdx.x; i < cnt; i += kThreads) dst[i] = skeys[i];
+    if (kPool) {
+      const int64_t nb = (cnt + kPoolBlock - 1) / kPoolBlock;
+      uint32_t *db = keys_blk + (int64_t)q * blk_stride + t_begin / kPoolBlock;
+      for (int64_t i = threadIdx.x; i < nb; i += kThreads) db[i] = sblk[i];
+    }
+  }
+  uint32_t *hq = hist_tok + (int64_t)q * (kHistBins + kStateWords);
+  uint32_t *hbq = kPool ? hist_blk + (int64_t)q * (kHistBins + kStateWords) : nullptr;
+  for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
+    const uint32_t w = hist[i];
+    if (w & 0xFFFFu) atomicAdd(&hq[2 * i], w & 0xFFFFu);
+    if (w >> 16) atomicAdd(&hq[2 * i + 1], w >> 16);
+    if (kPool) {
+      const uint32_t b = histb[i];
+      if (b & 0xFFFFu) atomicAdd(&hbq[2 * i], b & 0xFFFFu);
+      if (b >> 16) atomicAdd(&hbq[2 * i + 1], b >> 16);
+    }
+  }
+
+}
+
+// One workgroup per (query, key array): bin b1 of the K-th largest key from the
+// query's 12-bit histogram, written to the state words after the histogram.
+__global__ void __launch_bounds__(kSelectThreads) bins_kernel(
+    uint32_t *__restrict__ hist_tok, uint32_t *__restrict__ hist_blk, const int32_t *__restrict__ q_pos,
+    int32_t pool_len, int32_t reindex_pool, int32_t top_k, int32_t pool_blocks) {
+  __shared__ uint32_t lds[kHistBins];
   __shared__ uint32_t scratch[kSelectThreads / kWave + 1];
   __shared__ uint32_t res[2];
-
   const int q = blockIdx.x;
+  const bool blocks = blockIdx.y == 1;
   const int32_t qp = q_pos[q];
-  int64_t n;
-  if (kMode == kOutPoolBlocks) n = ((int64_t)qp + 1 + kPoolBlock - 1) / kPoolBlock;
-  else if (pool_in) n = pool_len;
-  else n = (int64_t)qp + 1;
-  const uint32_t *kq = keys + (int64_t)q * stride;
-  int32_t *oq = out + (int64_t)q * out_stride;
-  const int tid = threadIdx.x;
-
-  for (int i = tid; i < kHistBins; i += kSelectThreads) hist[i] = hist_g[(int64_t)q * kHistBins + i];
+  int64_t n = reindex_pool ? (int64_t)pool_len : (int64_t)qp + 1;
+  if (blocks) n = (n + kPoolBlock - 1) / kPoolBlock;
+  uint32_t *hq = (blocks ? hist_blk : hist_tok) + (int64_t)q * (kHistBins + kStateWords);
+  for (int i = threadIdx.x; i < kHistBins; i += kSelectThreads) lds[i] = hq[i];
   __syncthreads();
-  const int64_t n_valid = n - (int64_t)hist[0];   // key 0 marks an empty pool slot
-  const uint32_t keff = (uint32_t)min<int64_t>((int64_t)kk, n_valid);
+  const int64_t n_valid = n - (int64_t)lds[0];   // key 0 marks an empty pool slot
+  const uint32_t keff = (uint32_t)min((int64_t)(blocks ? pool_blocks : top_k), n_valid);
+  if (keff > 0) {
+    select_bin(lds, kHistBins, keff, scratch, res);
+  } else if (threadIdx.x == 0) {
+    res[0] = 0u;
+    res[1] = 0u;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    hq[kHistBins + kBin] = res[0];
+    hq[kHistBins + kAbove] = res[1];
+    hq[kHistBins + kKeff] = keff;
+  }
+}
 
+// ---------------------------------------------------------------------------
+// Selection proper
+// ---------------------------------------------------------------------------
+struct GlobalKeys {   // keys[i], index i
+  const uint32_t *k;
+  __device__ uint32_t key(int64_t i) const { return k[i]; }
+  __device__ int64_t id(int64_t i) const { return i; }
+};
+
+struct LdsCands {     // candidates gathered in index order
+  const uint32_t *k;
+  const int32_t *ids;
+  __device__ uint32_t key(int64_t i) const { return k[i]; }
+  __device__ int64_t id(int64_t i) const { return ids[i]; }
+};
+
+template <int kMode>
+struct Emit {
+  int32_t *out;          // this query's output row
+  const int32_t *pool;   // this query's pool row (kOutPoolIds)
+  int32_t qp;
+  __device__ void operator()(uint32_t o, int64_t id) const {
+    if (kMode == kOutPositions) {
+      out[o] = (int32_t)id;
+    } else if (kMode == kOutPoolIds) {
+      out[o] = pool[id];
+    } else {
+      for (int m = 0; m < kPoolBlock; ++m) {
+        const int64_t p = id * kPoolBlock + m;
+        out[(int64_t)o * kPoolBlock + m] = p <= qp ? (int32_t)p : -1;
+      }
+    }
+  }
+};
+
+// Radix passes on bits 19..8 and 7..0 among the keys of bin b1 (above1 keys
+// lie in higher bins), then the ordered compaction.  One 1024-thread block;
+// `hist` has kHistBins words of LDS.
+template <class Src, class E>
+__device__ void select_core(const Src &src, int64_t n, uint32_t keff, uint32_t b1,
+                            uint32_t above1, uint32_t *hist, uint32_t *scratch, uint32_t *res,
+                            const E &emit) {
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
   uint32_t tau = 0, c_gt = 0;
   if (keff > 0) {
-    // pass 1 (histogram from score_kernel): bits 31..20
-    select_bin(hist, kHistBins, keff, scratch, res);
-    const uint32_t b1 = res[0];
-    uint32_t above = res[1];
-    // pass 2: bits 19..8 among keys in bin b1
-    for (int i = tid; i < kHistBins; i += kSelectThreads) hist[i] = 0u;
+    uint32_t above = above1;
+    for (int i = tid; i < kHistBins; i += nt) hist[i] = 0u;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kSelectThreads) {
-      const uint32_t k = kq[i];
+    for (int64_t i = tid; i < n; i += nt) {                  // bits 19..8 within bin b1
+      const uint32_t k = src.key(i);
       if ((k >> 20) == b1) atomicAdd(&hist[(k >> 8) & 0xFFFu], 1u);
     }
     __syncthreads();
     select_bin(hist, kHistBins, keff - above, scratch, res);
-    const uint32_t b2 = res[0];
+    const uint32_t pre24 = (b1 << 12) | res[0];
     above += res[1];
-    // pass 3: bits 7..0 among keys matching the top 24 bits
-    const uint32_t pre24 = (b1 << 12) | b2;
-    for (int i = tid; i < 256; i += kSelectThreads) hist[i] = 0u;
+    for (int i = tid; i < 256; i += nt) hist[i] = 0u;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kSelectThreads) {
-      const uint32_t k = kq[i];
+    for (int64_t i = tid; i < n; i += nt) {                  // bits 7..0
+      const uint32_t k = src.key(i);
       if ((k >> 8) == pre24) atomicAdd(&hist[k & 0xFFu], 1u);
     }
     __syncthreads();
@@ -290,80 +467,254 @@ __global__ void __launch_bounds__(kSelectThreads) select_kernel(
     tau = (pre24 << 8) | res[0];
     c_gt = above + res[1];
   }
-  // keys > tau are all taken; of the keys == tau, the first (keff - c_gt) in position order
   const uint32_t ties_wanted = keff - c_gt;
-
+  // ordered compaction, 4 consecutive keys per thread per tile
   uint32_t carry_eq = 0, carry_sel = 0;
-  for (int64_t base = 0; base < n && carry_sel < keff; base += 4 * kSelectThreads) {
+  for (int64_t base = 0; base < n && carry_sel < keff; base += 4 * (int64_t)nt) {
     const int64_t i0 = base + 4 * tid;
     uint32_t k4[4];
+    bool in4[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) k4[u] = (i0 + u < n) ? kq[i0 + u] : 0u;
+    for (int u = 0; u < 4; ++u) {
+      in4[u] = i0 + u < n;
+      k4[u] = in4[u] ? src.key(i0 + u) : 0u;
+    }
     uint32_t neq = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) neq += (k4[u] == tau && i0 + u < n && keff > 0);
+    for (int u = 0; u < 4; ++u) neq += (in4[u] && k4[u] == tau);
     uint32_t tot_eq;
     uint32_t eq_rank = carry_eq + block_exclusive_scan(neq, scratch, tot_eq);
     bool sel[4];
     uint32_t nsel = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bool in = i0 + u < n && keff > 0;
-      const bool eq = in && k4[u] == tau;
-      sel[u] = in && (k4[u] > tau || (eq && eq_rank < ties_wanted));
+      const bool eq = in4[u] && k4[u] == tau;
+      sel[u] = in4[u] && (k4[u] > tau || (eq && eq_rank < ties_wanted));
       eq_rank += eq;
       nsel += sel[u];
     }
     uint32_t tot_sel;
     uint32_t o = carry_sel + block_exclusive_scan(nsel, scratch, tot_sel);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (!sel[u]) continue;
-      const int64_t id = i0 + u;
-      if (kMode == kOutPositions) {
-        oq[o] = (int32_t)id;
-      } else if (kMode == kOutPoolIds) {
-        oq[o] = pool_in[(int64_t)q * pool_len + id];
-      } else {
-        for (int m = 0; m < kPoolBlock; ++m) {
-          const int64_t p = id * kPoolBlock + m;
-          oq[(int64_t)o * kPoolBlock + m] = p <= qp ? (int32_t)p : -1;
-        }
-      }
-      ++o;
-    }
+    for (int u = 0; u < 4; ++u)
+      if (sel[u]) emit(o++, src.id(i0 + u));
     carry_eq += tot_eq;
     carry_sel += tot_sel;
+  }
+}
+
+// One wave per kFilterSub keys: keep every key whose top 12 bits reach bin b1,
+// with its index, in index order, into the wave's own slot region.
+template <int kMode>
+__global__ void __launch_bounds__(kFilterThreads) filter_kernel(
+    const uint32_t *__restrict__ keys, int64_t stride, const uint32_t *__restrict__ hist_g,
+    const int32_t *__restrict__ q_pos, int32_t pool_len, uint32_t *__restrict__ cand_key,
+    int32_t *__restrict__ cand_id, int64_t cand_stride, uint32_t *__restrict__ cnt,
+    int64_t cnt_stride) {
+  const int q = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t sub = (int64_t)blockIdx.x * (kFilterThreads / kWave) + threadIdx.x / kWave;
+  const int64_t n = array_len<kMode>(q_pos[q], pool_len);
+  const int64_t start = sub * kFilterSub;
+  if (start >= n) return;
+  const uint32_t *st = hist_g + (int64_t)q * (kHistBins + kStateWords) + kHistBins;
+  const bool none = st[kKeff] == 0u;
+  const uint32_t thr = st[kBin] << 20;
+  const uint32_t *kq = keys + (int64_t)q * stride;
+  uint32_t *ck = cand_key + (int64_t)q * cand_stride + start;
+  int32_t *ci = cand_id + (int64_t)q * cand_stride + start;
+  // 4 x 4 keys per lane; key (k, lane, e) sits at start + k*256 + lane*4 + e
+  uint32_t kv[4][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t i0 = start + k * 256 + lane * 4;
+    if (i0 + 3 < n) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(kq + i0);
+      kv[k][0] = v.x;
+      kv[k][1] = v.y;
+      kv[k][2] = v.z;
+      kv[k][3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kv[k][e] = i0 + e < n ? kq[i0 + e] : 0u;
+    }
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t written = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    bool f[4];
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = start + k * 256 + lane * 4 + e;
+      f[e] = !none && i < n && kv[k][e] >= thr;
+      const uint64_t b = __ballot(f[e]);
+      before += __popcll(b & lt);
+      total += __popcll(b);
+    }
+    uint32_t o = written + before;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (f[e]) {
+        ck[o] = kv[k][e];
+        ci[o] = (int32_t)(start + k * 256 + lane * 4 + e);
+        ++o;
+      }
+    }
+    written += total;
+  }
+  if (lane == 0) cnt[(int64_t)q * cnt_stride + sub] = written;
+}
+
+template <int kMode>
+__global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
+    const uint32_t *__restrict__ keys, int64_t stride, const uint32_t *__restrict__ hist_g,
+    const int32_t *__restrict__ q_pos, const int32_t *__restrict__ pool_in, int32_t pool_len,
+    int32_t kk, const uint32_t *__restrict__ cand_key, const int32_t *__restrict__ cand_id,
+    int64_t cand_stride, const uint32_t *__restrict__ cnt, int64_t cnt_stride,
+    int32_t *__restrict__ out, int64_t out_stride) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t scratch[kSelectThreads / kWave + 1];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t lkey[kResolveCap];
+  __shared__ int32_t lid[kResolveCap];
+  __shared__ uint32_t goff[kSelectThreads];
+
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t qp = q_pos[q];
+  const int64_t n = array_len<kMode>(qp, pool_len);
+  const uint32_t *st = hist_g + (int64_t)q * (kHistBins + kStateWords) + kHistBins;
+  const uint32_t keff = st[kKeff];
+  const uint32_t b1 = st[kBin];
+  const uint32_t above1 = st[kAbove];
+  Emit<kMode> emit{out + (int64_t)q * out_stride,
+                   pool_in ? pool_in + (int64_t)q * pool_len : nullptr, qp};
+
+  // candidate count, and their gather into LDS in index order: slot offsets by
+  // a block scan; then every thread copies candidates, finding each one's slot
+  // region by binary search over the offsets
+  const int64_t nsub = (n + kFilterSub - 1) / kFilterSub;
+  const uint32_t *cq = cnt + (int64_t)q * cnt_stride;
+  uint32_t carry = 0;
+  for (int64_t c0 = 0; c0 < nsub; c0 += kSelectThreads) {
+    const int64_t c = c0 + tid;
+    const uint32_t mine = c < nsub ? cq[c] : 0u;
+    uint32_t tot;
+    const uint32_t off = carry + block_exclusive_scan(mine, scratch, tot);
+    goff[tid] = off;
+    __syncthreads();
+    if (carry + tot <= kResolveCap) {
+      const int group = (int)min((int64_t)kSelectThreads, nsub - c0);
+      for (uint32_t j = carry + tid; j < carry + tot; j += kSelectThreads) {
+        int lo = 0, hi = group - 1;           // last region with goff <= j
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (goff[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        const int64_t src = (int64_t)q * cand_stride + (c0 + lo) * kFilterSub + (j - goff[lo]);
+        lkey[j] = cand_key[src];
+        lid[j] = cand_id[src];
+      }
+    }
+    carry += tot;
+    __syncthreads();
+  }
+  if (carry <= kResolveCap) {
+    select_core(LdsCands{lkey, lid}, (int64_t)carry, keff, b1, above1, hist, scratch, res, emit);
+  } else {
+    select_core(GlobalKeys{keys + (int64_t)q * stride}, n, keff, b1, above1, hist, scratch, res,
+                emit);
   }
   // padding
   const int64_t pad_from = (kMode == kOutPoolBlocks) ? (int64_t)keff * kPoolBlock : keff;
   const int64_t pad_to = (kMode == kOutPoolBlocks) ? (int64_t)kk * kPoolBlock : kk;
+  int32_t *oq = out + (int64_t)q * out_stride;
   for (int64_t i = pad_from + tid; i < pad_to; i += kSelectThreads) oq[i] = -1;
 }
 
-template <int H, bool kFp8, bool kPool>
-void launch_score(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <int H, bool kFp8, bool kPool, bool kReindexPool, int kThreads, int kChunk>
+void launch_score_shape(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
   const csa2_cache &c = *a.cache;
   const TopkWorkspace &L = a.layout;
-  dim3 grid((unsigned)((n_cand_max + kScoreChunk - 1) / kScoreChunk), (unsigned)a.nq);
-  const int32_t *pool = a.mode == CSA2_REINDEX ? a.pool_in : nullptr;
-  hipLaunchKernelGGL((score_kernel<H, kFp8, kPool>), grid, dim3(kScoreThreads), 0, s,
-                     static_cast<const uint8_t *>(c.idx_k), (int64_t)c.capacity, a.q_idx, a.q_fp8,
-                     a.q_seq, a.q_pos, pool, a.pool_len,
-                     reinterpret_cast<uint32_t *>(a.ws + L.keys_tok), L.n_tok,
-                     reinterpret_cast<uint32_t *>(a.ws + L.hist_tok),
-                     kPool ? reinterpret_cast<uint32_t *>(a.ws + L.keys_blk) : nullptr, L.n_blk,
-                     kPool ? reinterpret_cast<uint32_t *>(a.ws + L.hist_blk) : nullptr);
+  dim3 grid((unsigned)((n_cand_max + kChunk - 1) / kChunk), (unsigned)a.nq);
+  const int32_t *pool = kReindexPool ? a.pool_in : nullptr;
+  hipLaunchKernelGGL((score_kernel<H, kFp8, kPool, kReindexPool, kThreads, kChunk>), grid,
+                     dim3(kThreads), 0, s, static_cast<const uint8_t *>(c.idx_k),
+                     (int64_t)c.capacity, a.q_idx, a.q_fp8, a.q_seq, a.q_pos, pool, a.pool_len,
+                     reinterpret_cast<uint32_t *>(a.ws + L.tok.keys),
+                     L.tok.n, reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
+                     kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.keys) : nullptr, L.blk.n,
+                     kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr);
+}
+
+// Workgroup shape from the amount of work: long streams when there are enough
+// groups, one-wave groups for small searches (a Reindex pool) so that the
+// gathers spread over the chip.
+template <int H, bool kFp8, bool kPool, bool kReindexPool>
+void launch_score(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
+  const int64_t big = (int64_t)a.nq * ((n_cand_max + 4095) / 4096);
+  const int64_t mid = (int64_t)a.nq * ((n_cand_max + 2047) / 2048);
+  if (big >= kBigChunkMinGroups)
+    launch_score_shape<H, kFp8, kPool, kReindexPool, 256, 4096>(a, n_cand_max, s);
+  else if (mid >= kSmallGridGroups || kPool)
+    launch_score_shape<H, kFp8, kPool, kReindexPool, 256, 2048>(a, n_cand_max, s);
+  else
+    launch_score_shape<H, kFp8, false, kReindexPool, 64, 64>(a, n_cand_max, s);
 }
 
 template <int H, bool kFp8>
-void launch_score_pool(const IndexArgs &a, int64_t n, bool pool, hipStream_t s) {
-  if (pool) launch_score<H, kFp8, true>(a, n, s);
-  else launch_score<H, kFp8, false>(a, n, s);
+void launch_score_mode(const IndexArgs &a, int64_t n, bool pool, bool reindex_pool, hipStream_t s) {
+  if (pool) launch_score<H, kFp8, true, false>(a, n, s);
+  else if (reindex_pool) launch_score<H, kFp8, false, true>(a, n, s);
+  else launch_score<H, kFp8, false, false>(a, n, s);
+}
+
+template <int kMode>
+void launch_select(const IndexArgs &a, const SelectArrays &A, int32_t kk, int32_t *out,
+                   int64_t out_stride, hipStream_t s) {
+  uint8_t *w = a.ws;
+  const int32_t pool_len = kMode == kOutPoolIds ? a.pool_len : 0;
+  const int64_t waves = kFilterThreads / kWave;
+  hipLaunchKernelGGL((filter_kernel<kMode>),
+                     dim3((unsigned)((A.nsub + waves - 1) / waves), (unsigned)a.nq),
+                     dim3(kFilterThreads), 0, s, reinterpret_cast<const uint32_t *>(w + A.keys), A.n,
+                     reinterpret_cast<const uint32_t *>(w + A.hist), a.q_pos, pool_len,
+                     reinterpret_cast<uint32_t *>(w + A.cand_key),
+                     reinterpret_cast<int32_t *>(w + A.cand_id), A.cand_stride,
+                     reinterpret_cast<uint32_t *>(w + A.cnt), A.nsub);
+  hipLaunchKernelGGL((resolve_kernel<kMode>), dim3((unsigned)a.nq), dim3(kSelectThreads), 0, s,
+                     reinterpret_cast<const uint32_t *>(w + A.keys), A.n,
+                     reinterpret_cast<const uint32_t *>(w + A.hist), a.q_pos,
+                     kMode == kOutPoolIds ? a.pool_in : nullptr, pool_len, kk,
+                     reinterpret_cast<const uint32_t *>(w + A.cand_key),
+                     reinterpret_cast<const int32_t *>(w + A.cand_id), A.cand_stride,
+                     reinterpret_cast<const uint32_t *>(w + A.cnt), A.nsub, out, out_stride);
 }
 
 thread_local hipEvent_t g_scan_before = nullptr;
 thread_local hipEvent_t g_scan_after = nullptr;
+
+size_t carve(SelectArrays &A, int64_t n_slots, int32_t nq, size_t off) {
+  A.n = (n_slots + 63) / 64 * 64;
+  A.nsub = (A.n + kFilterSub - 1) / kFilterSub;
+  A.cand_stride = A.nsub * kFilterSub;
+  A.keys = off;
+  off = align256(off + (size_t)nq * A.n * 4);
+  A.hist = off;
+  off = align256(off + (size_t)nq * (kHistBins + kStateWords) * 4);
+  A.cand_key = off;
+  off = align256(off + (size_t)nq * A.cand_stride * 4);
+  A.cand_id = off;
+  off = align256(off + (size_t)nq * A.cand_stride * 4);
+  A.cnt = off;
+  off = align256(off + (size_t)nq * A.nsub * 4);
+  return off;
+}
 
 }  // namespace
 
@@ -377,20 +728,9 @@ TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t
   TopkWorkspace w;
   if (mode == CSA2_REUSE) return w;
   const bool reindex_pool = mode == CSA2_REINDEX && pool_len > 0;
-  w.n_tok = ((reindex_pool ? (int64_t)pool_len : (int64_t)c.capacity) + 63) / 64 * 64;
   const bool pool = mode == CSA2_FULL && pool_blocks > 0;
-  w.n_blk = pool ? (((int64_t)c.capacity + kPoolBlock - 1) / kPoolBlock + 63) / 64 * 64 : 0;
-  size_t off = 0;
-  w.keys_tok = off;
-  off = align256(off + (size_t)nq * w.n_tok * 4);
-  w.hist_tok = off;
-  off = align256(off + (size_t)nq * kHistBins * 4);
-  if (pool) {
-    w.keys_blk = off;
-    off = align256(off + (size_t)nq * w.n_blk * 4);
-    w.hist_blk = off;
-    off = align256(off + (size_t)nq * kHistBins * 4);
-  }
+  size_t off = carve(w.tok, reindex_pool ? (int64_t)pool_len : (int64_t)c.capacity, nq, 0);
+  if (pool) off = carve(w.blk, ((int64_t)c.capacity + kPoolBlock - 1) / kPoolBlock, nq, off);
   w.total = off;
   return w;
 }
@@ -406,44 +746,39 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
   const TopkWorkspace &L = a.layout;
   const bool pool = a.mode == CSA2_FULL && a.pool_blocks > 0;
   const bool reindex_pool = a.mode == CSA2_REINDEX && a.pool_in != nullptr;
-  // 1. clear histograms (hist_tok and, with a pool, hist_blk which follows keys_blk)
+  // 1. clear the histograms (the token and block histograms are cleared by one
+  //    launch when both exist: the block one follows the token arrays)
   {
-    const int64_t n = (int64_t)a.nq * kHistBins;
-    const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 2048);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(blocks), dim3(256), 0, s,
-                       reinterpret_cast<uint32_t *>(a.ws + L.hist_tok), n);
-    if (pool)
-      hipLaunchKernelGGL(zero_u32_kernel, dim3(blocks), dim3(256), 0, s,
-                         reinterpret_cast<uint32_t *>(a.ws + L.hist_blk), n);
+    const int64_t n_tok = (int64_t)a.nq * (kHistBins + kStateWords);
+    const unsigned blocks = (unsigned)std::min<int64_t>((n_tok + 255) / 256, 2048);
+    hipLaunchKernelGGL(zero2_u32_kernel, dim3(blocks), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
+                       pool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr, n_tok);
   }
-  // 2. scores
+  // 2. scores, first-pass histograms and bins
   if (g_scan_before != nullptr) (void)hipEventRecord(g_scan_before, s);
   const int64_t n_cand = reindex_pool ? (int64_t)a.pool_len : (int64_t)c.capacity;
   const bool fp8 = c.idx_k_dtype == CSA2_FP8_E4M3;
   if (c.idx_heads == 8) {
-    if (fp8) launch_score_pool<8, true>(a, n_cand, pool, s);
-    else launch_score_pool<8, false>(a, n_cand, pool, s);
+    if (fp8) launch_score_mode<8, true>(a, n_cand, pool, reindex_pool, s);
+    else launch_score_mode<8, false>(a, n_cand, pool, reindex_pool, s);
   } else {
-    if (fp8) launch_score_pool<4, true>(a, n_cand, pool, s);
-    else launch_score_pool<4, false>(a, n_cand, pool, s);
+    if (fp8) launch_score_mode<4, true>(a, n_cand, pool, reindex_pool, s);
+    else launch_score_mode<4, false>(a, n_cand, pool, reindex_pool, s);
   }
   if (g_scan_after != nullptr) (void)hipEventRecord(g_scan_after, s);
-  // 3. select
-  const uint32_t *keys_tok = reinterpret_cast<const uint32_t *>(a.ws + L.keys_tok);
-  const uint32_t *hist_tok = reinterpret_cast<const uint32_t *>(a.ws + L.hist_tok);
+  // 3. first-pass bins, then selection
+  hipLaunchKernelGGL(bins_kernel, dim3((unsigned)a.nq, pool ? 2u : 1u), dim3(kSelectThreads), 0, s,
+                     reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
+                     pool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr, a.q_pos,
+                     a.pool_len, (int32_t)reindex_pool, a.top_k, a.pool_blocks);
   if (reindex_pool)
-    hipLaunchKernelGGL((select_kernel<kOutPoolIds>), dim3(a.nq), dim3(kSelectThreads), 0, s,
-                       keys_tok, L.n_tok, hist_tok, a.q_pos, a.pool_in, a.pool_len, a.top_k,
-                       a.topk_out, (int64_t)a.top_k);
+    launch_select<kOutPoolIds>(a, L.tok, a.top_k, a.topk_out, a.top_k, s);
   else
-    hipLaunchKernelGGL((select_kernel<kOutPositions>), dim3(a.nq), dim3(kSelectThreads), 0, s,
-                       keys_tok, L.n_tok, hist_tok, a.q_pos, nullptr, 0, a.top_k, a.topk_out,
-                       (int64_t)a.top_k);
+    launch_select<kOutPositions>(a, L.tok, a.top_k, a.topk_out, a.top_k, s);
   if (pool)
-    hipLaunchKernelGGL((select_kernel<kOutPoolBlocks>), dim3(a.nq), dim3(kSelectThreads), 0, s,
-                       reinterpret_cast<const uint32_t *>(a.ws + L.keys_blk), L.n_blk,
-                       reinterpret_cast<const uint32_t *>(a.ws + L.hist_blk), a.q_pos, nullptr,
-                       0, a.pool_blocks, a.pool_out, (int64_t)a.pool_blocks * kPoolBlock);
+    launch_select<kOutPoolBlocks>(a, L.blk, a.pool_blocks, a.pool_out,
+                                  (int64_t)a.pool_blocks * kPoolBlock, s);
   return hipGetLastError();
 }
 

@@ -18,14 +18,21 @@ hipError_t launch_kv_append(const csa2_cache &c, const uint16_t *k, const uint16
                             int32_t n, hipStream_t stream);
 
 // Workspace carve-up of csa2_index_topk (byte offsets, 256-B aligned).
+struct SelectArrays {      // one selection problem per query (tokens, or pool blocks)
+  size_t keys = 0;         // uint32 [nq][n]      order-preserving score keys
+  size_t hist = 0;         // uint32 [nq][kHistBins + 16]  top-12-bit histogram, then state words
+  size_t cand_key = 0;     // uint32 [nq][cand_stride] filter output, one slot region per wave
+  size_t cand_id = 0;      // int32  [nq][cand_stride]
+  size_t cnt = 0;          // uint32 [nq][nsub]   candidates per slot region
+  int64_t n = 0;           // key slots per query
+  int64_t cand_stride = 0;
+  int64_t nsub = 0;
+};
+
 struct TopkWorkspace {
-  size_t keys_tok = 0;     // uint32 [nq][n_tok]  score keys of the candidates
-  size_t hist_tok = 0;     // uint32 [nq][kHistBins]
-  size_t keys_blk = 0;     // uint32 [nq][n_blk]  block-max keys (pool)
-  size_t hist_blk = 0;     // uint32 [nq][kHistBins]
+  SelectArrays tok;        // candidate positions (or pool entries)
+  SelectArrays blk;        // pool blocks (Full layer with a pool), else n = 0
   size_t total = 0;
-  int64_t n_tok = 0;       // candidate slots per query
-  int64_t n_blk = 0;       // block slots per query (0 without pool)
 };
 
 TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t nq,

@@ -54,6 +54,19 @@ def filled_caches(wl: synth.Workload, capacity=None, seqs=None):
     return gc, oc, data
 
 
+def untile_idx(raw: np.ndarray, heads: int, dtype) -> np.ndarray:
+    """Index keys from the library's tiled layout (include/csa2.h) to
+    [batch][capacity][heads][64] in `dtype` (uint8 E4M3 codes or uint16 bf16 bits)."""
+    esz = np.dtype(dtype).itemsize
+    raw = np.ascontiguousarray(raw).view(np.uint8)
+    b = raw.shape[0]
+    t = 64 // heads
+    chunks = 4 * esz
+    r = raw.reshape(b, -1, chunks, t, heads, 16)          # [b][tile][chunk][pos][head][16]
+    r = r.transpose(0, 1, 3, 4, 2, 5)                     # [b][tile][pos][head][chunk][16]
+    return np.ascontiguousarray(r).reshape(b, -1, heads, 64 * esz).view(dtype).reshape(b, -1, heads, 64)
+
+
 def attn_errors(out, lse, ref_out, ref_lse):
     """Per (query, head) row: max_c |delta| / max_c |ref|, and |delta lse|."""
     out = np.asarray(out, np.float64)

@@ -67,6 +67,8 @@ def test_append_validation(lib):
     assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), P(1), P(1), P(1), 4, None) == lib.CSA2_ERR_NULL
     c = _cache(lib, batch=0)
     assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_SHAPE
+    c = _cache(lib, capacity=1000)          # the tiled index keys need capacity % 16 == 0
+    assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_SHAPE
 
 
 def test_index_topk_validation(lib):

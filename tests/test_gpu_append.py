@@ -8,7 +8,7 @@ import torch
 import synth
 from oracle import csa2 as O
 from oracle import formats as F
-from gpu_util import DEV, announce, dev_i32, dev_u16, filled_caches, host, lib
+from gpu_util import DEV, announce, dev_i32, dev_u16, filled_caches, host, lib, untile_idx
 
 pytestmark = pytest.mark.gpu
 
@@ -21,11 +21,11 @@ def _finite_bf16_bits():
 @pytest.mark.parametrize("idx_dtype,heads", [("fp8", 8), ("bf16", 4), ("fp8", 4), ("bf16", 8)])
 def test_append_seeded_rows_bit_exact(idx_dtype, heads):
     announce(f"append seeded rows idx={idx_dtype} heads={heads}")
-    wl = synth.workload("tiny_4k", context=1000, batch=2, idx_heads=heads, idx_k_dtype=idx_dtype)
+    wl = synth.workload("tiny_4k", context=1008, batch=2, idx_heads=heads, idx_k_dtype=idx_dtype)
     gc, oc, _ = filled_caches(wl)
     assert np.array_equal(host(gc.kv_codes), oc.kv_codes)
     assert np.array_equal(host(gc.kv_scales), oc.kv_scales)
-    assert np.array_equal(host(gc.idx_k).view(oc.idx_k.dtype), oc.idx_k)
+    assert np.array_equal(untile_idx(host(gc.idx_k), heads, oc.idx_k.dtype), oc.idx_k)
 
 
 def _sweep_rows():
@@ -55,6 +55,7 @@ def _sweep_rows():
         blocks.append(blk)
     blocks = np.concatenate(blocks)
     nrow = (len(blocks) + 15) // 16
+    nrow = (nrow + 15) // 16 * 16          # capacity must be a multiple of 16
     pad = np.zeros((nrow * 16 - len(blocks), 16), np.uint16)
     blocks = np.concatenate([blocks, pad]).reshape(nrow, 16, 16)
     k = blocks[:, :8].reshape(nrow, 128)
@@ -82,7 +83,7 @@ def test_append_exhaustive_element_and_scale_sweep():
     torch.cuda.synchronize()
     assert np.array_equal(host(gc.kv_scales), oc.kv_scales)
     assert np.array_equal(host(gc.kv_codes), oc.kv_codes)
-    assert np.array_equal(host(gc.idx_k), oc.idx_k)
+    assert np.array_equal(untile_idx(host(gc.idx_k), 8, np.uint8), oc.idx_k)
     # every scale code 0..126 occurred
     assert len(np.unique(oc.kv_scales)) == 127
 

@@ -17,7 +17,7 @@ _CACHES = {}
 
 def _setup(heads):
     if heads not in _CACHES:
-        wl = synth.workload("tiny_4k", context=3000, batch=3, heads=heads)
+        wl = synth.workload("tiny_4k", context=3008, batch=3, heads=heads)
         gc, oc, _ = filled_caches(wl)
         _CACHES[heads] = (wl, gc, oc)
     return _CACHES[heads]

@@ -12,7 +12,7 @@ from gpu_util import DEV, announce, dev_i32, dev_u16, filled_caches, host, lib
 
 pytestmark = pytest.mark.gpu
 
-CAP = 5000                       # several 2048-candidate tiles and a ragged tail
+CAP = 5008                       # several 2048-candidate tiles and a ragged tail
 QPOS = [0, 5, 63, 2047, 2148, 4999]
 
 
@@ -140,11 +140,12 @@ def test_reuse_copies_source():
     assert pool is None and np.array_equal(host(out), src)
 
 
-@pytest.mark.parametrize("distinct", [1, 3])
-def test_tie_heavy_keys(distinct):
-    announce(f"ties distinct={distinct}")
+@pytest.mark.parametrize("distinct,cap", [(1, 3008), (3, 3008), (1, 20000), (2, 40000)])
+def test_tie_heavy_keys(distinct, cap):
+    # cap 20000/40000 with few distinct scores: more candidates than the LDS
+    # resolve holds, so the selection streams the full key array instead
+    announce(f"ties distinct={distinct} cap={cap}")
     m = lib()
-    cap = 3000
     gc = m.Cache(2, cap, idx_heads=8, idx_k_dtype="fp8")
     oc = O.OracleCache(2, cap, idx_heads=8, idx_k_dtype="fp8")
     rng = np.random.default_rng(distinct)
@@ -156,7 +157,7 @@ def test_tie_heavy_keys(distinct):
         m.csa2_kv_append(gc, dev_u16(kv), dev_u16(kv), dev_u16(ik), dev_i32(seq), dev_i32(pos))
         oc.append(kv, kv, ik, seq, pos)
     qi = synth.f32_to_bf16_bits(rng.standard_normal((2, 8, 64)).astype(np.float32))
-    qpos = [2999, 1234]
+    qpos = [cap - 1, 1234]
     tk, pool = m.csa2_index_topk(gc, "full", dev_u16(qi), dev_i32([0, 1]), dev_i32(qpos), 500,
                                  pool_blocks=40)
     torch.cuda.synchronize()
