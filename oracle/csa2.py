@@ -11,12 +11,12 @@ Sparse Attention 2"; model card, Introduction, CSA2 paragraph):
 3. gather and dequantization of the selected rows;
 4. softmax attention of every query head over those rows.
 
-Cache layout (the library's, so parity compares raw bytes):
+Cache layout (the library's main-KV layout, so parity compares raw bytes):
     kv_codes  [batch][capacity][dk/2 + dv/2]  uint8: K codes then V codes;
               channel 2i in the low nibble of byte i, 2i+1 in the high nibble
     kv_scales [batch][capacity][dk/16 + dv/16] uint8 E4M3: K scales then V
     idx_k     [batch][capacity][idx_heads][idx_dim]: bf16 bits (uint16) or
-              E4M3 codes (uint8)
+              E4M3 codes (uint8), in logical order (the library tiles them)
 """
 from __future__ import annotations
 
@@ -79,15 +79,46 @@ def dequantize_rows(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return v.reshape(n, d)
 
 
-class OracleCache:
-    """Host copy of the FP4 main-KV cache and the index-key cache (library layout)."""
+# E4M3 of every bf16 bit pattern and the value of every E4M3 code: the same
+# functions evaluated once per distinct input, so large caches decode fast.
+_E4M3_OF_BF16 = None
+_E4M3_VALUE = None
 
-    def __init__(self, batch, capacity, dk=128, dv=128, idx_heads=8, idx_dim=64, idx_k_dtype="fp8"):
+
+def _e4m3_tables():
+    global _E4M3_OF_BF16, _E4M3_VALUE
+    if _E4M3_OF_BF16 is None:
+        bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+        with np.errstate(invalid="ignore"):
+            vals = bf16_value(bits)
+        finite = np.isfinite(vals)
+        enc = np.zeros(1 << 16, np.uint8)
+        enc[finite] = e4m3_encode(vals[finite])
+        _E4M3_OF_BF16 = enc
+        _E4M3_VALUE = e4m3_value(np.arange(256)).astype(np.float32)
+    return _E4M3_OF_BF16, _E4M3_VALUE
+
+
+class OracleCache:
+    """Host copy of the FP4 main-KV cache and the index-key cache (logical layout).
+
+    lazy=True keeps the appended bf16 K/V rows and quantizes a row only when
+    it is read (kv_values), for contexts too long to quantize whole; the index
+    keys are always stored.
+    """
+
+    def __init__(self, batch, capacity, dk=128, dv=128, idx_heads=8, idx_dim=64, idx_k_dtype="fp8",
+                 lazy=False):
         self.batch, self.capacity = batch, capacity
         self.dk, self.dv, self.idx_heads, self.idx_dim = dk, dv, idx_heads, idx_dim
         self.idx_k_dtype = idx_k_dtype
-        self.kv_codes = np.zeros((batch, capacity, dk // 2 + dv // 2), np.uint8)
-        self.kv_scales = np.zeros((batch, capacity, dk // BLOCK + dv // BLOCK), np.uint8)
+        self.lazy = lazy
+        if lazy:
+            self.raw_k = [None] * batch     # per sequence: list of (pos, K bits, V bits)
+            self.kv_codes = self.kv_scales = None
+        else:
+            self.kv_codes = np.zeros((batch, capacity, dk // 2 + dv // 2), np.uint8)
+            self.kv_scales = np.zeros((batch, capacity, dk // BLOCK + dv // BLOCK), np.uint8)
         ik_t = np.uint8 if idx_k_dtype == "fp8" else np.uint16
         self.idx_k = np.zeros((batch, capacity, idx_heads, idx_dim), ik_t)
 
@@ -107,13 +138,19 @@ class OracleCache:
         """
         seq = np.asarray(seq)
         pos = np.asarray(pos)
-        kc, ks = quantize_rows(k_bits)
-        vc, vs = quantize_rows(v_bits)
-        self.kv_codes[seq, pos] = np.concatenate([kc, vc], axis=1)
-        self.kv_scales[seq, pos] = np.concatenate([ks, vs], axis=1)
+        if self.lazy:
+            for b in np.unique(seq):
+                m = seq == b
+                entry = (pos[m], np.asarray(k_bits)[m], np.asarray(v_bits)[m])
+                self.raw_k[b] = (self.raw_k[b] or []) + [entry]
+        else:
+            kc, ks = quantize_rows(k_bits)
+            vc, vs = quantize_rows(v_bits)
+            self.kv_codes[seq, pos] = np.concatenate([kc, vc], axis=1)
+            self.kv_scales[seq, pos] = np.concatenate([ks, vs], axis=1)
         if ik_bits is not None:
             if self.idx_k_dtype == "fp8":
-                self.idx_k[seq, pos] = e4m3_encode(bf16_value(ik_bits))
+                self.idx_k[seq, pos] = _e4m3_tables()[0][np.asarray(ik_bits, np.uint16)]
             else:
                 self.idx_k[seq, pos] = np.asarray(ik_bits, np.uint16)
 
@@ -121,11 +158,29 @@ class OracleCache:
         """Decoded index keys of sequence b at `rows`, float32 [n, idx_heads, idx_dim]."""
         raw = self.idx_k[b, rows]
         if self.idx_k_dtype == "fp8":
-            return e4m3_value(raw).astype(np.float32)
+            return _e4m3_tables()[1][raw]
         return bf16_value(raw).astype(np.float32)
+
+    def _rows_bits(self, b, rows):
+        """bf16 K and V bits of sequence b at `rows` (lazy mode; latest append wins)."""
+        k = np.zeros((len(rows), self.dk), np.uint16)
+        v = np.zeros((len(rows), self.dv), np.uint16)
+        for pos, kb, vb in self.raw_k[b] or []:
+            where = np.full(self.capacity, -1, np.int64)
+            where[pos] = np.arange(len(pos))
+            idx = where[rows]
+            hit = idx >= 0
+            k[hit] = kb[idx[hit]]
+            v[hit] = vb[idx[hit]]
+        return k, v
 
     def kv_values(self, b, rows):
         """Dequantized (K, V) of sequence b at `rows`, float64 [n, dk], [n, dv]."""
+        if self.lazy:
+            kb, vb = self._rows_bits(b, np.asarray(rows))
+            kc, ks = quantize_rows(kb)
+            vc, vs = quantize_rows(vb)
+            return dequantize_rows(kc, ks), dequantize_rows(vc, vs)
         codes = self.kv_codes[b, rows]
         scales = self.kv_scales[b, rows]
         hk, sk = self.dk // 2, self.dk // BLOCK
@@ -217,8 +272,9 @@ def build_pool(scores: np.ndarray, pool_blocks: int) -> np.ndarray:
     s = np.asarray(scores, np.float32)
     n = len(s)
     nblk = (n + POOL_BLOCK - 1) // POOL_BLOCK
-    bmax = np.array([s[b * POOL_BLOCK:min(n, (b + 1) * POOL_BLOCK)].max() for b in range(nblk)],
-                    np.float32)
+    padded = np.full(nblk * POOL_BLOCK, -np.inf, np.float32)   # absent members never win a max
+    padded[:n] = s
+    bmax = padded.reshape(nblk, POOL_BLOCK).max(axis=1)
     blocks = topk_select(bmax, np.arange(nblk), pool_blocks)
     pos = [p for b in blocks if b >= 0
            for p in range(b * POOL_BLOCK, min(n, (b + 1) * POOL_BLOCK))]
@@ -250,7 +306,10 @@ def index_topk(mode: str, cache: OracleCache, seq: int, q_pos: int, q_idx: np.nd
         cand = p[(p >= 0) & (p <= q_pos)]
     else:
         raise ValueError(mode)
-    scores = index_scores(q_idx, cache.index_key_values(seq, cand))
+    # candidates are scored independently; chunks only bound the memory
+    chunk = 1 << 16
+    scores = np.concatenate([index_scores(q_idx, cache.index_key_values(seq, cand[i:i + chunk]))
+                             for i in range(0, len(cand), chunk)] or [np.zeros(0, np.float32)])
     topk = topk_select(scores, cand, top_k)
     pool = build_pool(scores, pool_blocks) if (mode == "full" and pool_blocks > 0) else None
     return topk, pool, scores, cand

@@ -99,3 +99,29 @@ def test_append_layout_and_chunking():
     c = O.OracleCache(1, 64, idx_heads=4, idx_k_dtype="fp8")
     c.append(seq.k, seq.v, seq.ik, np.zeros(64, int), np.arange(64))
     assert np.array_equal(c.idx_k[0], F.e4m3_encode(F.bf16_value(seq.ik)))
+
+
+def test_lazy_cache_and_tables_match_direct_quantization():
+    wl = synth.workload("decode_64k_b32", context=96, batch=2)
+    data = synth.gen_batch(wl)
+    eager = O.OracleCache(2, 96)
+    lazy = O.OracleCache(2, 96, lazy=True)
+    for b in range(2):
+        seq, pos = np.full(96, b), np.arange(96)
+        eager.append(data.k[b], data.v[b], data.ik[b], seq, pos)
+        lazy.append(data.k[b], data.v[b], data.ik[b], seq, pos)
+    # index keys through the lookup table equal the encoder applied directly
+    assert np.array_equal(eager.idx_k, F.e4m3_encode(F.bf16_value(data.ik)))
+    assert np.array_equal(lazy.idx_k, eager.idx_k)
+    assert np.array_equal(eager.index_key_values(1, np.arange(96)),
+                          F.e4m3_value(eager.idx_k[1]).astype(np.float32))
+    rows = np.array([5, 0, 95, 40])
+    for b in range(2):
+        ke, ve = eager.kv_values(b, rows)
+        kl, vl = lazy.kv_values(b, rows)
+        assert np.array_equal(ke, kl) and np.array_equal(ve, vl)
+    # a later append to the same position wins in both
+    newk = data.k[0, :1].copy() ^ np.uint16(0x8000)
+    eager.append(newk, data.v[0, :1], None, [1], [40])
+    lazy.append(newk, data.v[0, :1], None, [1], [40])
+    assert np.array_equal(eager.kv_values(1, rows)[0], lazy.kv_values(1, rows)[0])
