@@ -155,6 +155,16 @@ size_t csa2_index_topk_workspace(const csa2_cache *cache, csa2_mode mode, int32_
  * a fixed order: per head and 16-channel block, fused multiply-adds in channel
  * order from 0; per head the four block sums pairwise; over heads a balanced
  * pairwise tree.  The result is bit-reproducible.
+ * Matrix-core scoring: with q_dtype = CSA2_FP8_E4M3 against E4M3 keys and
+ * every visible position a candidate (FULL without a pool, REINDEX without
+ * pool_in), all queries of the call are scored as one dense E4M3 product on
+ * matrix cores.  Each product is exact; the fp32 sums follow the hardware's
+ * order (deterministic, but not the order above), so a Top-K may differ from
+ * the fixed-order one only among candidates whose exact scores lie within
+ * fp32 rounding of the K-th score.  Queries are grouped 512 at a time in
+ * index order; a group whose queries share one sequence (a prefill chunk)
+ * runs at full rate, a group spanning several sequences makes one pass per
+ * sequence.
  * topk_out [nq][top_k] int32: the min(top_k, #candidates) candidates with the
  * largest scores (ties to the lower position, -0 == +0), in ascending
  * position order, then -1 padding.

@@ -242,6 +242,25 @@ def index_scores(q: np.ndarray, keys: np.ndarray) -> np.ndarray:
     return _pairwise_f32(per_head, axis=1)
 
 
+def index_scores_exact(q: np.ndarray, keys: np.ndarray):
+    """The index score of every candidate without rounding, and its magnitude sum.
+
+    Same sum as index_scores (every head, every channel: sum_h q_h . k_h) taken
+    in float64, with sum_h |q_h| . |k_h| beside it (the scale of the fp32
+    rounding error of any summation order: n terms in any order stay within
+    n * 2^-24 times that sum).  For E4M3 queries against E4M3 keys the result
+    is exact: an E4M3 value is a multiple of 2^-9 below 2^9, so each product is
+    a multiple of 2^-18 below 2^18 and a sum of 512 of them needs at most 45
+    bits; float64 carries 53, in any order.
+
+    q: float32 [H, D]; keys: float32 [n, H, D]; returns (float64 [n], float64 [n]).
+    Used to judge index sets of a scorer whose fp32 sums follow another order.
+    """
+    q = np.asarray(q, np.float64).reshape(-1)
+    k = np.asarray(keys, np.float64).reshape(len(keys), -1)
+    return k @ q, np.abs(k) @ np.abs(q)
+
+
 def topk_select(scores: np.ndarray, positions: np.ndarray, k: int) -> np.ndarray:
     """The k candidates with the largest scores, as positions in ascending order, -1 padded.
 

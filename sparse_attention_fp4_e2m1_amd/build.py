@@ -16,7 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
-SOURCES = ["csa2_api.hip", "csa2_append.hip", "csa2_index.hip", "csa2_attn.hip"]
+SOURCES = ["csa2_api.hip", "csa2_append.hip", "csa2_index.hip", "csa2_index_gemm.hip",
+           "csa2_attn.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -1,0 +1,618 @@
+// Index scoring on matrix cores (E4M3 index queries against E4M3 index keys)
+// and the exact Top-K of those scores.
+//
+// aiwiki "DeepSeek V4.1-Flash", section "Compressed Sparse Attention 2": a Full
+// layer, or a Reindex layer without a pool, scores every causally visible
+// position of its sequence.  When many queries of one sequence score together
+// (a prefill chunk), the scores are a dense product -- queries x positions,
+// contracted over idx_heads x 64 channels -- and run here as fp8 MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales).  Each product of two
+// E4M3 values is exact; their fp32 sum follows the matrix core, not the fixed
+// order of the streaming scorer.
+//
+// The Top-K is found without storing the queries x positions score matrix:
+//   gemm_prep_kernel    E4M3 copy of the index queries; the length of the
+//                       position ranges the product is split into.
+//   gemm_score_kernel<1> per query and block of 16 positions, the block's
+//                       largest score key (its top 16 bits), in one row per
+//                       query.
+//   gemm_kth_kernel     per query, t = the K-th largest of those block maxima.
+//                       At least K blocks reach t and each holds a score >= t,
+//                       so the K-th largest score is >= t: the whole Top-K
+//                       scores at least t.  (Fewer than K blocks: t = 0.)
+//   gemm_score_kernel<2> the same product again (same instructions, same
+//                       operand order, so the same bits) keeping every
+//                       (key >= t, position) in position order, in one slot
+//                       region per (query, position range).
+//   gemm_resolve_kernel per query, the exact selection among the candidates
+//                       (ties to the lower position, ascending output), with
+//                       the radix passes of the streaming path.
+// With continuous scores about K plus a few percent candidates survive.
+#include <algorithm>
+
+#include "csa2_select.h"
+
+namespace csa2 {
+namespace {
+
+typedef int v8i __attribute__((__vector_size__(8 * sizeof(int))));
+typedef float v4f __attribute__((__vector_size__(4 * sizeof(float))));
+
+constexpr int kGemmThreads = 512;       // 8 waves, two per SIMD
+constexpr int kGemmWaves = kGemmThreads / kWave;
+constexpr int kGemmQ = 512;             // queries per workgroup: 64 per wave, 4 column tiles of 16
+#ifndef CSA2_GEMM_STAGE
+#define CSA2_GEMM_STAGE 64
+#endif
+constexpr int kGemmStage = CSA2_GEMM_STAGE;   // positions per LDS stage (16-row tiles)
+constexpr int kGemmTargetGroups = 256;  // workgroups aimed for (one per CU)
+constexpr int kBlk = 16;                // positions per block maximum (one row tile)
+constexpr int kBlkGroup = 16;           // block maxima a lane collects before one 32-B store
+constexpr int kRangeAlign = kBlk * kBlkGroup;   // positions per range: a multiple of this
+constexpr int kKthThreads = 256;
+constexpr int kKthLdsMax = 32768;       // block maxima a gemm_kth_kernel keeps in LDS
+
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+  return e4m3_from_f32_nonneg(fabsf(f)) | ((__float_as_uint(f) >> 24) & 0x80u);
+}
+
+// E4M3 copy of q_idx (n_elems bf16 values), and plan[0] = the position-range
+// length: ceil(L / nranges) rounded up to a multiple of kRangeAlign, with
+// L = 1 + max q_pos.
+__global__ void __launch_bounds__(256) gemm_prep_kernel(
+    const uint16_t *__restrict__ q_idx, int64_t n_elems, uint8_t *__restrict__ q8,
+    const int32_t *__restrict__ q_pos, int32_t nq, int32_t nranges, uint32_t *__restrict__ plan) {
+  if (blockIdx.x == 0) {
+    __shared__ int32_t red[256 / kWave];
+    int32_t m = -1;
+    for (int i = threadIdx.x; i < nq; i += 256) m = max(m, q_pos[i]);
+    for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, kWave));
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < 256 / kWave; ++w) m = max(m, red[w]);
+      const int64_t len = (int64_t)m + 1;
+      int64_t sub = (len + nranges - 1) / nranges;
+      sub = (sub + kRangeAlign - 1) / kRangeAlign * kRangeAlign;
+      plan[0] = (uint32_t)max(sub, (int64_t)kRangeAlign);
+    }
+  }
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i0 >= n_elems) return;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lo |= e4m3_code(bf16_to_f32(q_idx[i0 + e])) << (8 * e);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hi |= e4m3_code(bf16_to_f32(q_idx[i0 + 4 + e])) << (8 * e);
+  *reinterpret_cast<uint2 *>(q8 + i0) = make_uint2(lo, hi);
+}
+
+// ---------------------------------------------------------------------------
+// gemm_score_kernel
+//
+// Grid (nranges, ceil(nq / kGemmQ)); workgroup (r, g) takes queries
+// [g*512, g*512 + 512) and positions [r*sub, (r+1)*sub) clipped to 1 + the
+// largest q_pos among them.  Each wave keeps its 64 queries' E4M3 index
+// queries in registers as MFMA B operands (4 column tiles x kSteps k-steps of
+// 32 bytes per lane); the 8 waves share the index keys, staged through LDS
+// kGemmStage positions (16-row tiles) at a time, double buffered.  With grid.x a
+// multiple of 8 all query groups of one range land on one XCD and share the
+// keys through its L2.
+//
+// MFMA operands (16x16x128, 32 bytes per lane): lane l supplies row / column
+// l % 16 and the 32 k-slots of lane group l / 16.  The k-slots are mapped to
+// channels identically in A (keys) and B (queries), so each output is the full
+// sum over heads and channels:
+//   8 heads: k-step s = channels 16s..16s+15; lane group g = heads 2g, 2g+1
+//            (the two 16-B halves; adjacent in the tiled key layout).
+//   4 heads: k-step s = channels 32s..32s+31; lane group g = head g.
+// LDS keeps, per row tile, k-step and half, the 64 lanes' 16-byte pieces in
+// lane order, so operand reads are linear (no bank conflicts).
+// The output tile's lane l holds rows (positions) 4(l/16)..4(l/16)+3 of
+// column (query) l % 16.
+// ---------------------------------------------------------------------------
+template <int H, int kPass>
+__global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
+    const uint8_t *__restrict__ idx_k, int64_t capacity, const uint8_t *__restrict__ q8,
+    const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos, int32_t nq,
+    const uint32_t *__restrict__ plan, uint16_t *__restrict__ bmax, int64_t bmax_row,
+    const uint32_t *__restrict__ thr, uint2 *__restrict__ cand, int64_t cand_stride,
+    uint32_t *__restrict__ cnt, int32_t nranges) {
+  constexpr int kPB = H * 64;                          // key bytes per position
+  constexpr int kSteps = kPB / 128;                    // MFMA k-steps
+  constexpr int kTileBytes = kBlk * kPB;               // one 16-row tile
+  constexpr int kStageBytes = kGemmStage * kPB;
+  constexpr int kPieces = kStageBytes / 16 / kGemmThreads;   // 16-B loads per thread per stage
+  static_assert(kPieces >= 1 && kStageBytes % (16 * kGemmThreads) == 0, "stage shape");
+
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageBytes];
+  __shared__ int32_t s_seq[kGemmQ];
+  __shared__ int32_t s_list[kGemmQ];
+  __shared__ uint32_t s_scr[kGemmWaves + 1];
+  __shared__ int32_t s_red[kGemmWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int sub = (int)plan[0];
+  const int r = blockIdx.x;
+  const int qbase = blockIdx.y * kGemmQ;
+  const int p_begin = r * sub;   // positions fit int32 (capacity is an int32)
+
+  // the group's sequences and furthest visible position
+  const int qt = qbase + tid;
+  const int32_t my_seq = qt < nq ? q_seq[qt] : -1;
+  int32_t m = qt < nq ? q_pos[qt] : -1;
+  s_seq[tid] = my_seq;
+  for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, kWave));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  int32_t maxqp = s_red[0];
+  for (int w = 1; w < kGemmWaves; ++w) maxqp = max(maxqp, s_red[w]);
+  if (p_begin > maxqp) return;   // uniform: no query of the group sees this range
+  const int p_end = min(p_begin + sub, maxqp + 1);
+
+  bool first = qt < nq;
+  for (int j = tid - 1; first && j >= 0; --j)
+    if (s_seq[j] == my_seq) first = false;
+  uint32_t nseq;
+  const uint32_t slot = block_exclusive_scan(first ? 1u : 0u, s_scr, nseq);
+  if (first) s_list[slot] = my_seq;
+  __syncthreads();
+
+  // this lane's four queries (one per column tile)
+  int32_t qp[4], qs[4];
+  uint32_t tq[4], run[4];
+  uint2 *cbase[4];   // pass 2: the query's slot region of this range
+  v8i qb[4][kSteps];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = qbase + wave * 64 + 16 * j + col;
+    const bool in = q < nq;
+    const int qc = in ? q : nq - 1;
+    cbase[j] = cand + (int64_t)qc * cand_stride + (int64_t)r * sub;
+    qp[j] = in ? q_pos[q] : -1;
+    qs[j] = in ? q_seq[q] : -1;
+    tq[j] = (kPass == 2 && in) ? thr[q] : 0u;
+    run[j] = 0;
+    const uint8_t *qrow = q8 + (int64_t)qc * kPB;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      uint4 a, b;
+      if (H == 8) {
+        a = *reinterpret_cast<const uint4 *>(qrow + (2 * grp) * 64 + 16 * s);
+        b = *reinterpret_cast<const uint4 *>(qrow + (2 * grp + 1) * 64 + 16 * s);
+      } else {
+        a = *reinterpret_cast<const uint4 *>(qrow + grp * 64 + 32 * s);
+        b = *reinterpret_cast<const uint4 *>(qrow + grp * 64 + 32 * s + 16);
+      }
+      qb[j][s] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    }
+  }
+
+  // stage loads: piece i of a stage -> LDS offset 16 i; its key bytes are
+  // (row tile rt, k-step s, half hf, lane l) of the operand layout above
+  int piece_off[kPieces];         // byte offset within the position's tile
+  int piece_pos[kPieces];         // position within the stage
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    const int i = tid + k * kGemmThreads;
+    const int rt = i / (kTileBytes / 16);
+    const int w = i % (kTileBytes / 16);
+    const int s = w / 128, hf = (w / 64) & 1, l = w & 63;
+    const int pl = rt * kBlk + (l & 15);
+    const int g = l >> 4;
+    const int h = H == 8 ? 2 * g + hf : g;
+    const int chunk = H == 8 ? s : 2 * s + hf;
+    piece_pos[k] = pl;
+    piece_off[k] = chunk * 1024 + h * 16;   // plus the position's tile and slot
+  }
+  constexpr int T = kWave / H;   // positions per key tile
+  auto load_stage = [&](const uint8_t *kb, int p0, uint4 *pf) {
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int p = min(p0 + piece_pos[k], (int)capacity - 1);
+      pf[k] = *reinterpret_cast<const uint4 *>(kb + (int64_t)(p / T) * 4096 + (p % T) * H * 16 +
+                                               piece_off[k]);
+    }
+  };
+  auto store_stage = [&](uint8_t *dst, const uint4 *pf) {
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k)
+      *reinterpret_cast<uint4 *>(dst + (tid + k * kGemmThreads) * 16) = pf[k];
+  };
+
+  for (uint32_t si = 0; si < nseq; ++si) {
+    const int32_t sigma = s_list[si];
+    // columns of other sequences: pass 1 never stores them, pass 2 compares
+    // against +inf (no score reaches it)
+    bool act[4];
+    float thr_f[4];
+    int32_t min_qp = INT32_MAX;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      act[j] = qs[j] == sigma;
+      if (act[j]) min_qp = min(min_qp, qp[j]);
+      // key >= t  <=>  score >= the float whose key is t (keys preserve order);
+      // t below the key of -FLT_MAX admits everything
+      const uint32_t t = tq[j];
+      const float tf = t < 0x00800000u ? -INFINITY
+                                       : __uint_as_float((t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t);
+      thr_f[j] = act[j] ? tf : INFINITY;
+    }
+    for (int d = 32; d >= 1; d >>= 1) min_qp = min(min_qp, __shfl_xor(min_qp, d, kWave));
+    const bool wave_act = min_qp != INT32_MAX;
+    const uint8_t *kb = idx_k + (int64_t)sigma * capacity * kPB;
+    const int n_st = (p_end - p_begin + kGemmStage - 1) / kGemmStage;
+    uint32_t sreg[kBlkGroup / 2];   // pass 1: this lane's query's block maxima, oldest lowest
+#pragma unroll
+    for (int k = 0; k < kBlkGroup / 2; ++k) sreg[k] = 0u;
+    int nshift = 0;
+    uint4 pf[kPieces];
+    load_stage(kb, p_begin, pf);
+    store_stage(stage[0], pf);
+    for (int it = 0; it < n_st; ++it) {
+      const int p0 = p_begin + it * kGemmStage;
+      __syncthreads();   // stage it&1 written; stage (it+1)&1 no longer read
+      load_stage(kb, min(p0 + kGemmStage, p_end - 1), pf);   // next stage (clamped on the last)
+      const uint8_t *cur = stage[it & 1];
+      if (wave_act) {
+#pragma unroll
+        for (int rt = 0; rt < kGemmStage / kBlk; ++rt) {
+          const int pt = p0 + rt * kBlk;
+          if (pt >= p_end) break;
+          v4f acc[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < kSteps; ++s) {
+            const uint8_t *src = cur + rt * kTileBytes + (2 * s) * 1024 + lane * 16;
+            const uint4 a = *reinterpret_cast<const uint4 *>(src);
+            const uint4 b = *reinterpret_cast<const uint4 *>(src + 1024);
+            const v8i av{(int)a.x, (int)a.y, (int)a.z, (int)a.w,
+                         (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, qb[j][s], acc[j], 0, 0,
+                                                                        0, 127, 0, 127);
+          }
+          const int prow = pt + 4 * grp;   // this lane's first row
+          // rows a column may not see become NaN: fmaxf skips them and every
+          // comparison with them fails.  Most tiles are visible to every
+          // active column (and tiles never straddle a range end: ranges are
+          // multiples of 16 positions).
+          if (pt + kBlk - 1 > min_qp) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (prow + i > qp[j]) acc[j][i] = __builtin_nanf("");
+          }
+          if (kPass == 1) {
+            // block maximum in fp32 (the key order is the float order, -0 == +0)
+            float mk[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              mk[j] = fmaxf(fmaxf(acc[j][0], acc[j][1]), fmaxf(acc[j][2], acc[j][3]));
+            // reduce over the four lane groups and scatter: lane group g ends
+            // with the maximum of column tile g
+            const bool hi2 = grp & 2;
+            float keep_a = hi2 ? mk[2] : mk[0], keep_b = hi2 ? mk[3] : mk[1];
+            const float send_a = hi2 ? mk[0] : mk[2], send_b = hi2 ? mk[1] : mk[3];
+            keep_a = fmaxf(keep_a, shfl_xor_f(send_a, 32));
+            keep_b = fmaxf(keep_b, shfl_xor_f(send_b, 32));
+            const bool lo1 = grp & 1;
+            const float keep = fmaxf(lo1 ? keep_b : keep_a, shfl_xor_f(lo1 ? keep_a : keep_b, 16));
+            const uint32_t kkey = score_key(keep);
+            // collect kBlkGroup consecutive blocks per lane, then one 32-B store
+            // (ranges start at multiples of kRangeAlign, so groups are aligned)
+#pragma unroll
+            for (int k = 0; k < kBlkGroup / 2 - 1; ++k) sreg[k] = (sreg[k] >> 16) | (sreg[k + 1] << 16);
+            sreg[kBlkGroup / 2 - 1] = (sreg[kBlkGroup / 2 - 1] >> 16) | (kkey & 0xFFFF0000u);
+            ++nshift;
+            const bool last = pt + kBlk >= p_end;
+            if (nshift == kBlkGroup || last) {
+              for (; nshift < kBlkGroup; ++nshift) {
+#pragma unroll
+                for (int k = 0; k < kBlkGroup / 2 - 1; ++k)
+                  sreg[k] = (sreg[k] >> 16) | (sreg[k + 1] << 16);
+                sreg[kBlkGroup / 2 - 1] >>= 16;
+              }
+              const int q = qbase + wave * 64 + lane;     // column tile grp, column col
+              const bool own_act = grp == 0 ? act[0] : grp == 1 ? act[1] : grp == 2 ? act[2] : act[3];
+              if (q < nq && own_act) {
+                const int g0 = (pt / kBlk) / kBlkGroup * kBlkGroup;
+                uint4 *dst = reinterpret_cast<uint4 *>(bmax + (int64_t)q * bmax_row + g0);
+                dst[0] = make_uint4(sreg[0], sreg[1], sreg[2], sreg[3]);
+                dst[1] = make_uint4(sreg[4], sreg[5], sreg[6], sreg[7]);
+              }
+              nshift = 0;
+            }
+          } else {
+            uint32_t selm[4];
+            uint32_t cp = 0u;   // byte j: candidates of column tile j in this lane
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              selm[j] = 0u;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) selm[j] |= (acc[j][i] >= thr_f[j] ? 1u : 0u) << i;
+              cp |= (uint32_t)__popc(selm[j]) << (8 * j);
+            }
+            if (__ballot(cp != 0u) != 0ull) {
+              // per column tile, candidates of the lower lane groups (earlier
+              // rows) and of all four
+              const uint32_t s1 = (uint32_t)__shfl((int)cp, (lane + 48) & 63, kWave);
+              const uint32_t s2 = (uint32_t)__shfl((int)cp, (lane + 32) & 63, kWave);
+              const uint32_t s3 = (uint32_t)__shfl((int)cp, (lane + 16) & 63, kWave);
+              const uint32_t pre = (grp >= 1 ? s1 : 0u) + (grp >= 2 ? s2 : 0u) + (grp >= 3 ? s3 : 0u);
+              const uint32_t tot = (uint32_t)__shfl((int)(pre + cp), col + 48, kWave);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                uint32_t off = run[j] + ((pre >> (8 * j)) & 0xFFu);
+                run[j] += (tot >> (8 * j)) & 0xFFu;
+                if (selm[j] != 0u) {
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    if (selm[j] & (1u << i)) {
+                      cbase[j][off] = make_uint2(score_key(acc[j][i]), (uint32_t)(prow + i));
+                      ++off;
+                    }
+                  }
+                }
+              }
+            }
+          }
+        }
+      }
+      store_stage(stage[(it + 1) & 1], pf);
+    }
+    __syncthreads();   // the next sequence's first stage reuses stage 0
+  }
+  if (kPass == 2) {
+    const int q = qbase + wave * 64 + lane;
+    const uint32_t own = grp == 0 ? run[0] : grp == 1 ? run[1] : grp == 2 ? run[2] : run[3];
+    if (q < nq) cnt[(int64_t)q * nranges + r] = own;
+  }
+}
+
+// Per wave: the bin of the 256 LDS bins `h` holding the element of rank `want`
+// (1-based from the top) -> {bin, elements in higher bins}, seen by every lane.
+__device__ __forceinline__ uint2 wave_select_bin256(const uint32_t *h, uint32_t want) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t c[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) c[b] = h[4 * lane + b];
+  const uint32_t sum = c[0] + c[1] + c[2] + c[3];
+  const uint32_t incl = wave_inclusive_scan(sum);
+  const uint32_t total = (uint32_t)__shfl((int)incl, kWave - 1, kWave);
+  uint32_t above = total - incl;   // elements in the bins of higher lanes
+  uint32_t found = 0xFFFFFFFFu, found_above = 0u;
+#pragma unroll
+  for (int b = 3; b >= 0; --b) {
+    if (above < want && above + c[b] >= want) {
+      found = 4 * lane + b;
+      found_above = above;
+    }
+    above += c[b];
+  }
+  const uint64_t who = __ballot(found != 0xFFFFFFFFu);
+  const int src = who ? __ffsll((unsigned long long)who) - 1 : 0;
+  return make_uint2((uint32_t)__shfl((int)found, src, kWave),
+                    (uint32_t)__shfl((int)found_above, src, kWave));
+}
+
+// thr[q] = (K-th largest 16-bit block maximum) << 16, or 0 when the query has
+// fewer than K blocks.  One workgroup per query.  The K-th largest value is
+// built bit by bit from the top: a bit stays set when at least K values reach
+// the prefix with it set.  Counting compares values held in LDS (dynamic
+// size, from the capacity; read from global memory beyond kKthLdsMax), so
+// values that crowd into a few bins cost nothing extra.
+template <bool kLds>
+__device__ __forceinline__ uint32_t kth_prefix(const uint16_t *v, int64_t n, uint32_t k,
+                                               uint32_t *part) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  uint32_t prefix = 0u;
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    uint32_t c = 0u;
+    for (int64_t i = (int64_t)tid * 8; i < n; i += kKthThreads * 8) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(v + i);   // rows hold whole groups of 16
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t x = (ws[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        c += (i + e < n && x >= cand) ? 1u : 0u;
+      }
+    }
+    for (int d = 32; d >= 1; d >>= 1) c += (uint32_t)__shfl_xor((int)c, d, kWave);
+    if (lane == 0) part[tid / kWave] = c;
+    __syncthreads();
+    uint32_t total = 0u;
+#pragma unroll
+    for (int w = 0; w < kKthThreads / kWave; ++w) total += part[w];
+    __syncthreads();
+    if (total >= k) prefix = cand;
+  }
+  return prefix;
+}
+
+__global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
+    const uint16_t *__restrict__ bmax, int64_t bmax_row, const int32_t *__restrict__ q_pos,
+    int32_t top_k, uint32_t *__restrict__ thr) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t kth_vals[];
+  __shared__ uint32_t part[kKthThreads / kWave];
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t nblk = ((int64_t)q_pos[q] + 1 + kBlk - 1) / kBlk;
+  if (nblk < top_k) {
+    if (tid == 0) thr[q] = 0u;
+    return;
+  }
+  const uint16_t *bq = bmax + (int64_t)q * bmax_row;
+  uint32_t t;
+  if (nblk <= kKthLdsMax) {
+    for (int64_t i = (int64_t)tid * 8; i < nblk; i += kKthThreads * 8)
+      *reinterpret_cast<uint4 *>(kth_vals + i) = *reinterpret_cast<const uint4 *>(bq + i);
+    __syncthreads();
+    t = kth_prefix<true>(kth_vals, nblk, (uint32_t)top_k, part);
+  } else {
+    t = kth_prefix<false>(bq, nblk, (uint32_t)top_k, part);
+  }
+  if (tid == 0) thr[q] = t << 16;
+}
+
+// Per query: the exact Top-K among the candidates of its slot regions.  The
+// first radix bin comes from the candidates themselves: every key above the
+// K-th largest is a candidate, so the candidates' histogram above that bin is
+// the full one.  Beyond kResolveCap candidates (ties, or few blocks) the
+// regions are compacted in place in global memory and streamed.
+__global__ void __launch_bounds__(kSelectThreads) gemm_resolve_kernel(
+    const int32_t *__restrict__ q_pos, int32_t top_k, const uint32_t *__restrict__ plan,
+    uint2 *__restrict__ cand, int64_t cand_stride, const uint32_t *__restrict__ cnt,
+    int32_t nranges, int32_t *__restrict__ out) {
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t scratch[kSelectThreads / kWave + 1];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t lkey[kResolveCap];
+  __shared__ int32_t lid[kResolveCap];
+  __shared__ uint32_t goff[kSelectThreads];
+
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t qp = q_pos[q];
+  const int64_t n_vis = (int64_t)qp + 1;
+  const uint32_t keff = (uint32_t)max((int64_t)0, min((int64_t)top_k, n_vis));
+  const int64_t sub = plan[0];
+  const int64_t nreg = min((int64_t)nranges, (n_vis + sub - 1) / sub);
+  uint2 *cq2 = cand + (int64_t)q * cand_stride;
+  const uint32_t *cq = cnt + (int64_t)q * nranges;
+  Emit<kOutPositions> emit{out + (int64_t)q * top_k, nullptr, qp};
+
+  const uint32_t total = gather_regions(cq, nreg, sub, PairSlots{cq2}, lkey, lid, goff, scratch);
+  const bool in_lds = total <= kResolveCap;
+  if (!in_lds) {
+    // regions -> one run from slot 0 (a region's destination never passes its source)
+    uint32_t dst = 0;
+    for (int64_t r = 0; r < nreg; ++r) {
+      const uint32_t c = (uint32_t)min((int64_t)cq[r], sub);
+      for (uint32_t b = 0; b < c; b += kSelectThreads) {
+        const uint32_t i = b + tid;
+        uint2 kv = make_uint2(0u, 0u);
+        if (i < c) kv = cq2[r * sub + i];
+        __syncthreads();
+        if (i < c) cq2[dst + i] = kv;
+        __syncthreads();
+      }
+      dst += c;
+    }
+  }
+  for (int i = tid; i < kHistBins; i += kSelectThreads) hist[i] = 0u;
+  __syncthreads();
+  for (uint32_t i = tid; i < total; i += kSelectThreads)
+    atomicAdd(&hist[(in_lds ? lkey[i] : cq2[i].x) >> 20], 1u);
+  __syncthreads();
+  uint32_t b1 = 0, above1 = 0;
+  if (keff > 0) {
+    select_bin(hist, kHistBins, keff, scratch, res);
+    b1 = res[0];
+    above1 = res[1];
+  }
+  if (in_lds)
+    select_core(LdsCands{lkey, lid}, (int64_t)total, keff, b1, above1, hist, scratch, res, emit);
+  else
+    select_core(PairSlots{cq2}, (int64_t)total, keff, b1, above1, hist, scratch, res, emit);
+  int32_t *oq = out + (int64_t)q * top_k;
+  for (int64_t i = (int64_t)keff + tid; i < top_k; i += kSelectThreads) oq[i] = -1;
+}
+
+// Position ranges per query group: enough workgroups for the chip, a multiple
+// of 8 (one XCD per range), and no more ranges than the capacity fills.
+int32_t gemm_ranges(int32_t nq, int32_t capacity) {
+  const int32_t groups = (nq + kGemmQ - 1) / kGemmQ;
+  int32_t r = (kGemmTargetGroups + groups - 1) / groups;
+  r = std::max((r + 7) / 8 * 8, 8);
+  return std::min(r, (capacity + kRangeAlign - 1) / kRangeAlign);
+}
+
+template <int H>
+void launch_gemm_scores(const IndexArgs &a, const GemmWorkspace &L, int pass, hipStream_t s) {
+  const csa2_cache &c = *a.cache;
+  uint8_t *w = a.ws;
+  const dim3 grid((unsigned)L.nranges, (unsigned)((a.nq + kGemmQ - 1) / kGemmQ));
+  auto args = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kGemmThreads), 0, s,
+                       static_cast<const uint8_t *>(c.idx_k), (int64_t)c.capacity,
+                       reinterpret_cast<const uint8_t *>(w + L.q8), a.q_seq, a.q_pos, a.nq,
+                       reinterpret_cast<const uint32_t *>(w + L.plan),
+                       reinterpret_cast<uint16_t *>(w + L.bmax), L.bmax_row,
+                       reinterpret_cast<const uint32_t *>(w + L.thr),
+                       reinterpret_cast<uint2 *>(w + L.cand), L.cand_stride,
+                       reinterpret_cast<uint32_t *>(w + L.cnt), L.nranges);
+  };
+  if (pass == 1) args(gemm_score_kernel<H, 1>);
+  else args(gemm_score_kernel<H, 2>);
+}
+
+}  // namespace
+
+bool gemm_eligible(const csa2_cache &c, csa2_mode mode, int32_t pool_len, int32_t pool_blocks) {
+  if (c.idx_k_dtype != CSA2_FP8_E4M3) return false;
+  return (mode == CSA2_FULL && pool_blocks == 0) || (mode == CSA2_REINDEX && pool_len == 0);
+}
+
+GemmWorkspace gemm_workspace_layout(const csa2_cache &c, int32_t nq) {
+  GemmWorkspace w;
+  w.nranges = gemm_ranges(nq, c.capacity);
+  const int64_t sub_max =
+      (((int64_t)c.capacity + w.nranges - 1) / w.nranges + kRangeAlign - 1) / kRangeAlign * kRangeAlign;
+  // one row of block maxima per query, whole 16-block groups
+  w.bmax_row = ((int64_t)c.capacity + kRangeAlign - 1) / kRangeAlign * kBlkGroup;
+  w.cand_stride = sub_max * w.nranges;
+  size_t off = 0;
+  w.q8 = off;
+  off = align256(off + (size_t)nq * c.idx_heads * 64);
+  w.plan = off;
+  off = align256(off + 16);
+  w.thr = off;
+  off = align256(off + (size_t)nq * 4);
+  w.bmax = off;
+  off = align256(off + (size_t)w.bmax_row * nq * 2);
+  w.cnt = off;
+  off = align256(off + (size_t)nq * w.nranges * 4);
+  w.cand = off;
+  off = align256(off + (size_t)nq * w.cand_stride * 8);
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEvent_t after,
+                                  hipStream_t s) {
+  const csa2_cache &c = *a.cache;
+  const GemmWorkspace &L = a.layout.gemm;
+  uint8_t *w = a.ws;
+  const int64_t n_elems = (int64_t)a.nq * c.idx_heads * 64;
+  hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)std::max<int64_t>(1, (n_elems / 8 + 255) / 256)),
+                     dim3(256), 0, s, a.q_idx, n_elems, w + L.q8, a.q_pos, a.nq, L.nranges,
+                     reinterpret_cast<uint32_t *>(w + L.plan));
+  if (before != nullptr) (void)hipEventRecord(before, s);
+  if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 1, s);
+  else launch_gemm_scores<4>(a, L, 1, s);
+  if (after != nullptr) (void)hipEventRecord(after, s);
+  const size_t kth_lds =
+      (size_t)std::min<int64_t>(L.bmax_row, kKthLdsMax) * sizeof(uint16_t);
+  hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), kth_lds, s,
+                     reinterpret_cast<const uint16_t *>(w + L.bmax), L.bmax_row, a.q_pos, a.top_k,
+                     reinterpret_cast<uint32_t *>(w + L.thr));
+  if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 2, s);
+  else launch_gemm_scores<4>(a, L, 2, s);
+  hipLaunchKernelGGL(gemm_resolve_kernel, dim3((unsigned)a.nq), dim3(kSelectThreads), 0, s,
+                     a.q_pos, a.top_k, reinterpret_cast<const uint32_t *>(w + L.plan),
+                     reinterpret_cast<uint2 *>(w + L.cand), L.cand_stride,
+                     reinterpret_cast<const uint32_t *>(w + L.cnt), L.nranges, a.topk_out);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -29,10 +29,25 @@ struct SelectArrays {      // one selection problem per query (tokens, or pool b
   int64_t nsub = 0;
 };
 
+// Workspace carve-up of the matrix-core scorer (E4M3 index queries and keys).
+struct GemmWorkspace {
+  size_t q8 = 0;           // uint8  [nq][idx_heads * 64]   E4M3 index queries
+  size_t plan = 0;         // uint32 [1]  positions per range
+  size_t thr = 0;          // uint32 [nq] candidate threshold key
+  size_t bmax = 0;         // uint16 [nq][bmax_row]  block maxima of 16 positions (top 16 key bits)
+  size_t cnt = 0;          // uint32 [nq][nranges]  candidates per (query, range)
+  size_t cand = 0;         // uint2  [nq][cand_stride]  (score key, position)
+  int64_t bmax_row = 0;
+  int64_t cand_stride = 0;
+  int32_t nranges = 0;
+  size_t total = 0;
+};
+
 struct TopkWorkspace {
   SelectArrays tok;        // candidate positions (or pool entries)
   SelectArrays blk;        // pool blocks (Full layer with a pool), else n = 0
-  size_t total = 0;
+  GemmWorkspace gemm;      // the matrix-core scorer's arrays, when it can run
+  size_t total = 0;        // covers either scorer
 };
 
 TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t nq,
@@ -58,6 +73,13 @@ struct IndexArgs {
 };
 
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream);
+
+// The matrix-core scorer serves E4M3 index queries against E4M3 keys when the
+// candidates are every visible position (FULL without a pool, REINDEX without one).
+bool gemm_eligible(const csa2_cache &c, csa2_mode mode, int32_t pool_len, int32_t pool_blocks);
+GemmWorkspace gemm_workspace_layout(const csa2_cache &c, int32_t nq);
+hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEvent_t after,
+                                  hipStream_t stream);
 
 // Events recorded around the scoring kernel (csa2_profile_index_scan); per host thread.
 void set_index_scan_events(hipEvent_t before, hipEvent_t after);

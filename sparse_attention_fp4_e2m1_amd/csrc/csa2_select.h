@@ -1,0 +1,220 @@
+// Exact Top-K selection on order-preserving score keys, shared by the
+// streaming scorer and the matrix-core scorer (device code, one workgroup of
+// kSelectThreads threads per query).
+//
+// Ordering rule (aiwiki "DeepSeek V4.1-Flash", section "Compressed Sparse
+// Attention 2", per-query Top-K): the K largest scores, ties to the lower
+// index, emitted in ascending index order.
+#pragma once
+
+#include "csa2_internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kSelectThreads = 1024;
+constexpr int kResolveCap = 8192;          // candidates held in LDS by a resolve
+constexpr int kStateWords = 16;            // per query after its histogram: see SelState
+
+// Selection state of one query and one key array, in the words after its histogram.
+enum SelState { kTicket = 0, kBin = 1, kAbove = 2, kKeff = 3 };
+
+// ---------------------------------------------------------------------------
+// Selection helpers
+// ---------------------------------------------------------------------------
+enum OutMode { kOutPositions = 0, kOutPoolIds = 1, kOutPoolBlocks = 2 };
+
+// Finds the bin holding the element of rank `want` (1-based, counted from the
+// largest key) among `nbins` LDS bins; result = {bin, elements in higher bins}.
+// All threads of the block take part and see the result.  Contains barriers.
+__device__ void select_bin(const uint32_t *bins, int nbins, uint32_t want, uint32_t *scratch,
+                           uint32_t *result) {
+  const int nt = blockDim.x;
+  const int per = (nbins + nt - 1) / nt;
+  const int lo = threadIdx.x * per;
+  uint32_t s = 0;
+  for (int b = lo; b < lo + per && b < nbins; ++b) s += bins[b];
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan(s, scratch, total);
+  uint32_t above = total - excl - s;   // elements in bins of higher threads
+  for (int b = lo + per - 1; b >= lo; --b) {
+    if (b >= nbins) continue;
+    const uint32_t c = bins[b];
+    if (above < want && above + c >= want) {
+      result[0] = (uint32_t)b;
+      result[1] = above;
+    }
+    above += c;
+  }
+  __syncthreads();
+}
+
+template <int kMode>
+__device__ __forceinline__ int64_t array_len(int32_t qp, int32_t pool_len) {
+  if (kMode == kOutPoolBlocks) return ((int64_t)qp + 1 + kPoolBlock - 1) / kPoolBlock;
+  if (kMode == kOutPoolIds) return pool_len;
+  return (int64_t)qp + 1;
+}
+
+
+// ---------------------------------------------------------------------------
+// Selection proper
+// ---------------------------------------------------------------------------
+struct GlobalKeys {   // keys[i], index i
+  const uint32_t *k;
+  __device__ uint32_t key(int64_t i) const { return k[i]; }
+  __device__ int64_t id(int64_t i) const { return i; }
+};
+
+struct LdsCands {     // candidates gathered in index order
+  const uint32_t *k;
+  const int32_t *ids;
+  __device__ uint32_t key(int64_t i) const { return k[i]; }
+  __device__ int64_t id(int64_t i) const { return ids[i]; }
+};
+
+template <int kMode>
+struct Emit {
+  int32_t *out;          // this query's output row
+  const int32_t *pool;   // this query's pool row (kOutPoolIds)
+  int32_t qp;
+  __device__ void operator()(uint32_t o, int64_t id) const {
+    if (kMode == kOutPositions) {
+      out[o] = (int32_t)id;
+    } else if (kMode == kOutPoolIds) {
+      out[o] = pool[id];
+    } else {
+      for (int m = 0; m < kPoolBlock; ++m) {
+        const int64_t p = id * kPoolBlock + m;
+        out[(int64_t)o * kPoolBlock + m] = p <= qp ? (int32_t)p : -1;
+      }
+    }
+  }
+};
+
+// Radix passes on bits 19..8 and 7..0 among the keys of bin b1 (above1 keys
+// lie in higher bins), then the ordered compaction.  One 1024-thread block;
+// `hist` has kHistBins words of LDS.
+template <class Src, class E>
+__device__ void select_core(const Src &src, int64_t n, uint32_t keff, uint32_t b1,
+                            uint32_t above1, uint32_t *hist, uint32_t *scratch, uint32_t *res,
+                            const E &emit) {
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  uint32_t tau = 0, c_gt = 0;
+  if (keff > 0) {
+    uint32_t above = above1;
+    for (int i = tid; i < kHistBins; i += nt) hist[i] = 0u;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += nt) {                  // bits 19..8 within bin b1
+      const uint32_t k = src.key(i);
+      if ((k >> 20) == b1) atomicAdd(&hist[(k >> 8) & 0xFFFu], 1u);
+    }
+    __syncthreads();
+    select_bin(hist, kHistBins, keff - above, scratch, res);
+    const uint32_t pre24 = (b1 << 12) | res[0];
+    above += res[1];
+    for (int i = tid; i < 256; i += nt) hist[i] = 0u;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += nt) {                  // bits 7..0
+      const uint32_t k = src.key(i);
+      if ((k >> 8) == pre24) atomicAdd(&hist[k & 0xFFu], 1u);
+    }
+    __syncthreads();
+    select_bin(hist, 256, keff - above, scratch, res);
+    tau = (pre24 << 8) | res[0];
+    c_gt = above + res[1];
+  }
+  const uint32_t ties_wanted = keff - c_gt;
+  // ordered compaction, 4 consecutive keys per thread per tile
+  uint32_t carry_eq = 0, carry_sel = 0;
+  for (int64_t base = 0; base < n && carry_sel < keff; base += 4 * (int64_t)nt) {
+    const int64_t i0 = base + 4 * tid;
+    uint32_t k4[4];
+    bool in4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      in4[u] = i0 + u < n;
+      k4[u] = in4[u] ? src.key(i0 + u) : 0u;
+    }
+    uint32_t neq = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) neq += (in4[u] && k4[u] == tau);
+    uint32_t tot_eq;
+    uint32_t eq_rank = carry_eq + block_exclusive_scan(neq, scratch, tot_eq);
+    bool sel[4];
+    uint32_t nsel = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool eq = in4[u] && k4[u] == tau;
+      sel[u] = in4[u] && (k4[u] > tau || (eq && eq_rank < ties_wanted));
+      eq_rank += eq;
+      nsel += sel[u];
+    }
+    uint32_t tot_sel;
+    uint32_t o = carry_sel + block_exclusive_scan(nsel, scratch, tot_sel);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (sel[u]) emit(o++, src.id(i0 + u));
+    carry_eq += tot_eq;
+    carry_sel += tot_sel;
+  }
+}
+
+// Candidate slots as two arrays (key, index).
+struct SplitSlots {
+  const uint32_t *k;
+  const int32_t *ids;
+  __device__ uint32_t key(int64_t i) const { return k[i]; }
+  __device__ int64_t id(int64_t i) const { return ids[i]; }
+};
+
+// Candidate slots as one array of (key, index) pairs.
+struct PairSlots {
+  const uint2 *kv;
+  __device__ uint32_t key(int64_t i) const { return kv[i].x; }
+  __device__ int64_t id(int64_t i) const { return (int32_t)kv[i].y; }
+};
+
+// Copies one query's candidates, held in `nreg` slot regions of `region`
+// entries each (counts in cq, region r at slots r * region of `slots`), into
+// LDS in region order when they fit (<= kResolveCap); returns the total either
+// way.  Slot offsets come from a block scan; every thread then finds the
+// region of each slot it copies by binary search over the offsets.  Contains
+// barriers.
+template <class Slots>
+__device__ uint32_t gather_regions(const uint32_t *cq, int64_t nreg, int64_t region,
+                                   const Slots &slots, uint32_t *lkey, int32_t *lid,
+                                   uint32_t *goff, uint32_t *scratch) {
+  const int tid = threadIdx.x;
+  uint32_t carry = 0;
+  for (int64_t c0 = 0; c0 < nreg; c0 += kSelectThreads) {
+    const int64_t c = c0 + tid;
+    // a region never holds more than `region` slots; the clamp keeps every
+    // read inside the query's slots whatever the counts say
+    const uint32_t mine = c < nreg ? (uint32_t)min((int64_t)cq[c], region) : 0u;
+    uint32_t tot;
+    const uint32_t off = carry + block_exclusive_scan(mine, scratch, tot);
+    goff[tid] = off;
+    __syncthreads();
+    if (carry + tot <= kResolveCap) {
+      const int group = (int)min((int64_t)kSelectThreads, nreg - c0);
+      for (uint32_t j = carry + tid; j < carry + tot; j += kSelectThreads) {
+        int lo = 0, hi = group - 1;           // last region with goff <= j
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (goff[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        const int64_t src = (c0 + lo) * region + (j - goff[lo]);
+        lkey[j] = slots.key(src);
+        lid[j] = (int32_t)slots.id(src);
+      }
+    }
+    carry += tot;
+    __syncthreads();
+  }
+  return carry;
+}
+
+}  // namespace
+}  // namespace csa2

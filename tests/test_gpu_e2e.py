@@ -6,7 +6,7 @@ import torch
 
 import synth
 from oracle import csa2 as O
-from gpu_util import ATTN_TOL, DEV, announce, attn_errors, dev_i32, dev_u16, host, lib
+from gpu_util import announce, check_stack, dev_i32, dev_u16, host, lib
 
 pytestmark = pytest.mark.gpu
 
@@ -58,14 +58,9 @@ def test_step_matches_oracle(name):
     # the append itself is bit-exact
     assert np.array_equal(host(gc.kv_codes), oc.kv_codes)
     assert np.array_equal(host(gc.kv_scales), oc.kv_scales)
-    sel = slice(None) if only is None else only
-    for li, layer in enumerate(wl.layers):
-        assert np.array_equal(host(stack.topk[li])[sel], ref[li]["topk"][sel]), f"layer {li} topk"
-        if ref[li]["pool"] is not None:
-            assert np.array_equal(host(stack.pool[li])[sel], ref[li]["pool"][sel]), f"layer {li} pool"
-        rel, dl = attn_errors(host(stack.out[li])[sel], host(stack.lse[li])[sel],
-                              ref[li]["out"][sel], ref[li]["lse"][sel])
-        assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL, (li, rel.max(), dl.max())
+    rows = [(i, i, int(wl.query_seq()[i])) for i in (range(wl.nq) if only is None else only)]
+    qs = [synth.gen_queries(wl, li) for li in range(len(wl.layers))]
+    check_stack(wl, oc, stack, ref, qs, rows, log=announce)
     if wl.prefill:   # causality: every selected row is visible to its query
         tk = host(stack.topk[0])
         qp = wl.query_pos()

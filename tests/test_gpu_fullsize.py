@@ -10,7 +10,7 @@ import torch
 
 import synth
 from oracle import csa2 as O
-from gpu_util import ATTN_TOL, DEV, announce, attn_errors, host, untile_idx
+from gpu_util import DEV, announce, check_stack, host, untile_idx
 
 pytestmark = pytest.mark.gpu
 
@@ -57,14 +57,8 @@ def test_full_size_sampled_queries(name):
     ref = O.run_layers(oc, wl.layers, np.array([seq_of[int(wl.query_seq()[i])] for i in queries]),
                        wl.query_pos()[queries], qs, wl.top_k, wl.q_idx_dtype)
     stack = run.stack
-    for li, layer in enumerate(wl.layers):
-        got = host(stack.topk[li])[queries]
-        assert np.array_equal(got, ref[li]["topk"]), f"{name} layer {li} Top-K"
-        if ref[li]["pool"] is not None:
-            assert np.array_equal(host(stack.pool[li])[queries], ref[li]["pool"]), f"layer {li} pool"
-        rel, dl = attn_errors(host(stack.out[li])[queries], host(stack.lse[li])[queries],
-                              ref[li]["out"], ref[li]["lse"])
-        assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL, (li, rel.max(), dl.max())
-        announce(f"  layer {li} ({layer.mode}) ok: max rel err {rel.max():.2e}")
+    rows = [(i, r, seq_of[int(wl.query_seq()[i])]) for r, i in enumerate(queries)]
+    check_stack(wl, oc, stack, ref, [synth.gen_queries(wl, li) for li in range(len(wl.layers))],
+                rows, log=announce)
     del run, stack
     torch.cuda.empty_cache()

@@ -1,14 +1,18 @@
 """GPU parity of csa2_index_topk in Full / Reindex / Reuse mode, with and
 without the candidate pool: Top-K index sets and pools bit-exact against the
-oracle (the decode scorer follows the canonical fp32 order, so the scores
-themselves are compared bit for bit too)."""
+oracle (the streaming scorer follows the canonical fp32 order, so the scores
+themselves are compared bit for bit too).  E4M3 index queries against E4M3
+keys over every visible position are scored on matrix cores, whose fp32 sums
+follow the hardware's order: those sets are checked with the relaxed rule of
+gpu_util.relaxed_topk_check, and exactly where no rounding can matter."""
 import numpy as np
 import pytest
 import torch
 
 import synth
 from oracle import csa2 as O
-from gpu_util import DEV, announce, dev_i32, dev_u16, filled_caches, host, lib
+from gpu_util import (DEV, announce, dev_i32, dev_u16, filled_caches, host, lib,
+                      relaxed_topk_check)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,8 +50,8 @@ def _oracle_full(wl, oc, qd, q_dtype, top_k, pool_blocks=0, layer_q=None):
 
 
 @pytest.mark.parametrize("heads,idx_dtype,q_dtype", [
-    (8, "fp8", "bf16"), (4, "bf16", "bf16"), (8, "fp8", "fp8"), (4, "fp8", "bf16"),
-    (8, "bf16", "bf16"), (4, "bf16", "fp8")])
+    (8, "fp8", "bf16"), (4, "bf16", "bf16"), (4, "fp8", "bf16"), (8, "bf16", "bf16"),
+    (4, "bf16", "fp8"), (8, "bf16", "fp8")])
 @pytest.mark.parametrize("top_k", [1, 37, 256, 3000])
 def test_full_topk_bit_exact(heads, idx_dtype, q_dtype, top_k):
     announce(f"full topk heads={heads} idx={idx_dtype} q={q_dtype} k={top_k}")
@@ -168,3 +172,91 @@ def test_tie_heavy_keys(distinct, cap):
         assert np.array_equal(host(pool)[i], p)
     if distinct == 1:
         assert list(host(tk)[0]) == list(range(500))
+
+
+# ---------------------------------------------------------------------------
+# matrix-core scorer (E4M3 index query, E4M3 keys, every visible position)
+# ---------------------------------------------------------------------------
+
+def _relaxed_query(oc, seq, qp, qi, got_row, top_k):
+    cand = np.arange(qp + 1)
+    keys = oc.index_key_values(seq, cand)
+    canon = O.index_scores(qi, keys)
+    exact, mag = O.index_scores_exact(qi, keys)
+    want = O.topk_select(canon, cand, top_k)
+    return relaxed_topk_check(got_row, want, cand, canon, exact, mag)
+
+
+@pytest.mark.parametrize("mode", ["full", "reindex"])
+@pytest.mark.parametrize("heads", [8, 4])
+@pytest.mark.parametrize("top_k", [1, 37, 256, 3000])
+def test_matrix_core_topk(mode, heads, top_k):
+    # six queries, each of its own sequence: one query group spanning six sequences
+    announce(f"matrix-core {mode} heads={heads} k={top_k}")
+    m = lib()
+    wl, gc, oc = _setup(heads, "fp8")
+    qd = synth.gen_queries(wl, 0)
+    ws_bytes = m.csa2_index_topk_workspace(gc, mode, len(QPOS), top_k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    topk, _ = m.csa2_index_topk(gc, mode, dev_u16(qd.q_idx), dev_i32(np.arange(len(QPOS))),
+                                dev_i32(QPOS), top_k, q_dtype="fp8", workspace=ws)
+    torch.cuda.synchronize()
+    got = host(topk)
+    swaps = 0
+    for i, p in enumerate(QPOS):
+        qi = O.query_index_values(qd.q_idx[i], "fp8")
+        swaps += _relaxed_query(oc, i, p, qi, got[i], top_k)
+        if p + 1 <= top_k:   # everything visible is selected: exact
+            assert list(got[i, :p + 1]) == list(range(p + 1))
+    announce(f"  swaps at the K-th score: {swaps}")
+
+
+def test_matrix_core_prefill_chunk():
+    # 700 consecutive queries of one sequence (two query groups, the second
+    # ragged), causal: query i sees positions [0, 4308 + i]
+    announce("matrix-core prefill chunk")
+    m = lib()
+    wl, gc, oc = _setup(8, "fp8")
+    nq, top_k, seq = 700, 256, 3
+    qpos = np.arange(CAP - nq, CAP)
+    rng = np.random.default_rng(21)
+    qidx = synth.f32_to_bf16_bits(rng.standard_normal((nq, 8, 64)).astype(np.float32) * 2)
+    topk, _ = m.csa2_index_topk(gc, "full", dev_u16(qidx), dev_i32(np.full(nq, seq)),
+                                dev_i32(qpos), top_k, q_dtype="fp8")
+    torch.cuda.synchronize()
+    got = host(topk)
+    assert np.all((got >= 0) & (got <= qpos[:, None]))          # causal, no padding needed
+    assert np.all(np.diff(got, axis=1) > 0)
+    swaps = 0
+    for i in list(range(0, nq, 23)) + [511, 512, nq - 1]:
+        qi = O.query_index_values(qidx[i], "fp8")
+        swaps += _relaxed_query(oc, seq, int(qpos[i]), qi, got[i], top_k)
+    announce(f"  swaps at the K-th score: {swaps}")
+
+
+@pytest.mark.parametrize("distinct,cap", [(1, 20000), (2, 40000), (3, 3008)])
+def test_matrix_core_tie_heavy(distinct, cap):
+    # few distinct scores: every position of a tied block reaches the
+    # threshold, so the candidates overflow the LDS resolve (cap >= 20000)
+    announce(f"matrix-core ties distinct={distinct} cap={cap}")
+    m = lib()
+    gc = m.Cache(2, cap, idx_heads=8, idx_k_dtype="fp8")
+    oc = O.OracleCache(2, cap, idx_heads=8, idx_k_dtype="fp8")
+    rng = np.random.default_rng(distinct)
+    base = synth.f32_to_bf16_bits(rng.standard_normal((distinct, 8, 64)).astype(np.float32))
+    ik = base[rng.integers(0, distinct, cap)]
+    kv = synth.f32_to_bf16_bits(rng.standard_normal((cap, 128)).astype(np.float32))
+    for b in range(2):
+        seq, pos = np.full(cap, b, np.int32), np.arange(cap, dtype=np.int32)
+        m.csa2_kv_append(gc, dev_u16(kv), dev_u16(kv), dev_u16(ik), dev_i32(seq), dev_i32(pos))
+        oc.append(kv, kv, ik, seq, pos)
+    qi = synth.f32_to_bf16_bits(rng.standard_normal((2, 8, 64)).astype(np.float32))
+    qpos = [cap - 1, 1234]
+    tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qi), dev_i32([0, 1]), dev_i32(qpos), 500,
+                              q_dtype="fp8")
+    torch.cuda.synchronize()
+    got = host(tk)
+    for i in range(2):
+        _relaxed_query(oc, i, qpos[i], O.query_index_values(qi[i], "fp8"), got[i], 500)
+    if distinct == 1:   # identical keys give identical sums: ties to the lower position
+        assert list(got[0]) == list(range(500)) and list(got[1]) == list(range(500))

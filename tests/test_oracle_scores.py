@@ -101,3 +101,33 @@ def test_head_order_is_balanced_tree_on_cancellation():
     want = rnd(a01 + a23)
     assert Fraction(float(O.index_scores(q, k)[0])) == want
     assert want == 1   # the unrounded sum would be 2
+
+
+def test_exact_scores_equal_rational_sums_for_e4m3():
+    # The claim of index_scores_exact: for E4M3 x E4M3 the float64 sum is the
+    # exact rational sum, whatever order BLAS takes.  Checked against Fractions
+    # over the full E4M3 range (subnormals up to 448, both signs).
+    rng = np.random.default_rng(11)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    for heads in (4, 8):
+        q = F.e4m3_value(rng.choice(finite, (heads, 64))).astype(np.float32)
+        k = F.e4m3_value(rng.choice(finite, (40, heads, 64))).astype(np.float32)
+        got, mag = O.index_scores_exact(q, k)
+        for n in range(len(k)):
+            want = sum(Fraction(float(a)) * Fraction(float(b))
+                       for a, b in zip(q.reshape(-1), k[n].reshape(-1)))
+            assert Fraction(float(got[n])) == want
+            assert Fraction(float(mag[n])) == sum(abs(Fraction(float(a)) * Fraction(float(b)))
+                                                  for a, b in zip(q.reshape(-1), k[n].reshape(-1)))
+
+
+def test_canonical_scores_within_rounding_bound_of_exact():
+    # The fp32 canonical score sits within 512 * 2^-24 * sum|q||k| of the exact
+    # one: the bound the relaxed index-set rule leans on.
+    rng = np.random.default_rng(12)
+    q = F.e4m3_value(F.e4m3_encode(rng.standard_normal((8, 64)) * 4)).astype(np.float32)
+    k = F.e4m3_value(F.e4m3_encode(rng.standard_normal((3000, 8, 64)) * 2)).astype(np.float32)
+    exact, mag = O.index_scores_exact(q, k)
+    got = O.index_scores(q, k).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= 512 * 2.0 ** -24 * mag)
+    assert np.any(got != exact)   # the rounding is really there
