@@ -9,17 +9,19 @@
 //
 // attn_partial_kernel: one workgroup per (query, split of the selected rows),
 // one wave per 16 query heads; the split is walked in sub-chunks of 64 rows
-// with an online softmax, and the gathers of the next sub-chunk are in flight
-// while the current one is computed.
-//   * K rows are gathered straight into MFMA A-operand registers: lane l owns
-//     row l%16 and channels 32g..32g+31 (g = l/16): 16 B of codes + 2 scale
-//     bytes, dequantized exactly to bf16.  The contraction index is permuted
-//     (k-slice s, lane group g <-> channels 32g + 8s .. +7) identically for Q.
+// with an online softmax.
+//   * The workgroup gathers a sub-chunk's codes one sub-chunk ahead and
+//     dequantizes them once into LDS, shared by every head wave: K^ in bf16 as
+//     MFMA A fragments (the contraction index permuted, k-slice s and lane
+//     group g <-> channels 32g + 8s .. +7, identically for Q), V^ in fp16
+//     transposed [channel][row].  E2M1 codes go through the hardware FP4
+//     conversion; every value is exact.
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (fp32 accumulation); exp2-based
-//     softmax statistics per head; P rounded to fp16.
-//   * V rows are dequantized into LDS, transposed [channel][row] in fp16
-//     (exact), double-buffered, and O += P V runs on v_mfma_f32_16x16x32_f16.
+//     softmax statistics per head; P rounded to fp16; O += P V with
+//     v_mfma_f32_16x16x32_f16.
 // attn_combine_kernel: merges the splits of each (query, head).
+#include <algorithm>
+
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -27,177 +29,221 @@ namespace {
 
 constexpr int kSub = 64;                      // rows per sub-chunk
 constexpr int kVtPitch = kSub + 4;            // fp16 elements per LDS row of V^T
-constexpr int kMaxRowsPerSplit = 256;
+constexpr int kMaxRowsPerSplit = 2048;
+constexpr int kTargetGroups = 512;            // workgroups aimed for (two per CU)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-// E2M1 code (4 bits, bit 3 sign) times a decoded scale; exact in fp32.
-// Placing the code's 3 magnitude bits at fp32 bits 24..22 gives the value
-// scaled by 2^-126 (code 1 lands on the subnormal 0.5 * 2^-126), so one
-// multiply by 2^126 restores it.
-__device__ __forceinline__ float e2m1_times(uint32_t code, float s) {
-  const float tiny = __uint_as_float(((code & 8u) << 28) | ((code & 7u) << 22));
-  return (tiny * 0x1p126f) * s;
+// Two E2M1 codes (byte kByte of w) -> their values times s, as a bf16 pair.
+// The hardware conversion applies only the exponent of its scale, so it runs
+// with scale 1 and the E4M3 scale multiplies in fp32: every product has at
+// most 6 significant bits, so it is exact in fp32 and its bf16 truncation.
+template <int kByte>
+__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float s) {
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kByte);
+  return (__float_as_uint(v[0] * s) >> 16) | (__float_as_uint(v[1] * s) & 0xFFFF0000u);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  // values here have <= 6 significant bits: truncation is exact
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+// Two E2M1 codes (byte kByte of w) times s (given as an fp16 pair), as fp16:
+// E2M1 and E4M3 values and their products are exact in fp16.
+template <int kByte>
+__device__ __forceinline__ f16x2 fp4x2_f16(uint32_t w, f16x2 s2) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, kByte) * s2;
 }
 
-// Gathered codes of one sub-chunk held in registers between prefetch and use.
-template <int kWaves>
-struct SubChunk {
-  // (row, 16-channel block) items of V per thread; the last round may be partial
-  static constexpr int kVItems = (kSub * 8 + kWaves * 64 - 1) / (kWaves * 64);
-  uint4 kc[4];          // K codes of rows 16t + l16, channels 32g..32g+31
-  uint32_t ks[4];       // their two scale bytes
-  uint2 vc[kVItems];
-  uint32_t vs[kVItems];
+// Gathered codes of one sub-chunk, held in registers between load and dequant.
+//   K item (tile t, lane l): row 16t + l%16, channels 32g..32g+31 (g = l/16):
+//     16 B of codes and their two scale bytes.
+//   V item (row pair p, block b): rows 2p, 2p+1, channels 16b..16b+15: 8 B of
+//     codes and one scale byte per row.
+template <int kThreads>
+struct Gathered {
+  static constexpr int kItems = (4 * 64 + kThreads - 1) / kThreads;   // of each kind
+  uint4 kc[kItems];
+  uint32_t ks[kItems];
+  uint2 vc[kItems][2];
+  uint32_t vs[kItems];
 };
 
-template <int kWaves>
-__device__ __forceinline__ void gather(SubChunk<kWaves> &sc, const int32_t *rows, int base,
+template <int kThreads>
+__device__ __forceinline__ void gather(Gathered<kThreads> &gd, const int32_t *rows, int base,
                                        const uint8_t *__restrict__ kv_codes,
                                        const uint8_t *__restrict__ kv_scales, int64_t seq_base,
-                                       int l16, int g, int tid) {
+                                       int tid) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int32_t row = rows[base + 16 * t + l16];
-    const int64_t slot = seq_base + (row >= 0 ? row : 0);
-    sc.kc[t] = *reinterpret_cast<const uint4 *>(kv_codes + slot * 128 + 16 * g);
-    sc.ks[t] = *reinterpret_cast<const uint16_t *>(kv_scales + slot * 16 + 2 * g);
-  }
+  for (int it = 0; it < Gathered<kThreads>::kItems; ++it) {
+    const int item = min(tid + it * kThreads, 4 * 64 - 1);
+    {
+      const int g = (item & 63) >> 4;
+      const int32_t row = rows[base + 16 * (item >> 6) + (item & 15)];
+      const int64_t slot = seq_base + (row >= 0 ? row : 0);
+      gd.kc[it] = *reinterpret_cast<const uint4 *>(kv_codes + slot * 128 + 16 * g);
+      gd.ks[it] = *reinterpret_cast<const uint16_t *>(kv_scales + slot * 16 + 2 * g);
+    }
+    {
+      const int pr = item & 31, b = item >> 5;
+      uint32_t sc = 0u;
 #pragma unroll
-  for (int v = 0; v < SubChunk<kWaves>::kVItems; ++v) {
-    const int item = min(tid + v * kWaves * 64, kSub * 8 - 1);
-    const int32_t row = rows[base + (item >> 3)];
-    const int64_t slot = seq_base + (row >= 0 ? row : 0);
-    sc.vc[v] = *reinterpret_cast<const uint2 *>(kv_codes + slot * 128 + 64 + (item & 7) * 8);
-    sc.vs[v] = kv_scales[slot * 16 + 8 + (item & 7)];
+      for (int h = 0; h < 2; ++h) {
+        const int32_t row = rows[base + 2 * pr + h];
+        const int64_t slot = seq_base + (row >= 0 ? row : 0);
+        gd.vc[it][h] = *reinterpret_cast<const uint2 *>(kv_codes + slot * 128 + 64 + 8 * b);
+        sc |= (uint32_t)kv_scales[slot * 16 + 8 + b] << (8 * h);
+      }
+      gd.vs[it] = sc;
+    }
   }
 }
 
-// One sub-chunk of 64 rows: V to LDS, S^T on matrix cores, online softmax,
-// O += P V.  Contains one barrier.
-template <int kWaves>
-__device__ __forceinline__ void attend_sub(const SubChunk<kWaves> &sc, const int32_t *rows, int base,
-                                           _Float16 *vbuf, const bf16x8 (&qf)[4], float scale_log2,
-                                           int g, int l16, int tid, float &m_run, float &l_run,
-                                           f32x4 (&o)[8]) {
-  constexpr int kVItems = SubChunk<kWaves>::kVItems;
-    // V of this sub-chunk -> LDS, transposed, fp16 (exact)
+// Dequantizes one gathered sub-chunk into LDS: K^ as bf16 MFMA A fragments
+// kq[tile][k-step][lane] (16 B each: k-step s of lane group g is channels
+// 32g + 8s .. +7), V^ transposed as fp16 vt[channel][row].
+template <int kThreads>
+__device__ __forceinline__ void dequant(const Gathered<kThreads> &gd, uint4 *kq, _Float16 *vt,
+                                        int tid) {
 #pragma unroll
-    for (int v = 0; v < kVItems; ++v) {
-      const int item = tid + v * kWaves * 64;
-      if (item >= kSub * 8) break;
-      const int r = item >> 3;
-      const int blk = item & 7;
-      const bool ok = rows[base + r] >= 0;
-      const float s = ok ? e4m3_to_f32(sc.vs[v]) : 0.0f;
-#pragma unroll
-      for (int cc = 0; cc < 16; ++cc) {
-        const uint32_t word = cc < 8 ? sc.vc[v].x : sc.vc[v].y;
-        const uint32_t code = (word >> (4 * (cc & 7))) & 0xFu;
-        vbuf[(blk * 16 + cc) * kVtPitch + r] = (_Float16)e2m1_times(code, s);
-      }
-    }
-
-    // S^T tiles: rows base + 16t + 4g + i, head l16
-    f32x4 st[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float s0 = e4m3_to_f32(sc.ks[t] & 0xFFu);
-      const float s1 = e4m3_to_f32((sc.ks[t] >> 8) & 0xFFu);
-      const uint32_t w[4] = {sc.kc[t].x, sc.kc[t].y, sc.kc[t].z, sc.kc[t].w};
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int it = 0; it < Gathered<kThreads>::kItems; ++it) {
+    const int item = tid + it * kThreads;
+    if (Gathered<kThreads>::kItems * kThreads > 4 * 64 && item >= 4 * 64) break;
+    {
+      const float s0 = e4m3_to_f32(gd.ks[it] & 0xFFu);
+      const float s1 = e4m3_to_f32((gd.ks[it] >> 8) & 0xFFu);
+      const uint32_t w[4] = {gd.kc[it].x, gd.kc[it].y, gd.kc[it].z, gd.kc[it].w};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        // channels 32g + 8s .. +7 = code word s; scale block 2g + (s >= 2)
         const float sc = s < 2 ? s0 : s1;
-        const uint32_t cw = w[s];
-        uint32_t packed[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          packed[e] = pack_bf16x2(e2m1_times((cw >> (8 * e)) & 0xFu, sc),
-                                  e2m1_times((cw >> (8 * e + 4)) & 0xFu, sc));
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(packed[0], packed[1], packed[2], packed[3]));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
-      }
-      st[t] = acc;
-    }
-
-    // online softmax for head 16*wave + l16
-    float z[16];
-    float mc = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = rows[base + 16 * t + 4 * g + i] >= 0;
-        const float v = ok ? st[t][i] * scale_log2 : -INFINITY;
-        z[4 * t + i] = v;
-        mc = fmaxf(mc, v);
-      }
-    mc = fmaxf(mc, shfl_xor_f(mc, 16));
-    mc = fmaxf(mc, shfl_xor_f(mc, 32));
-    const float m_new = fmaxf(m_run, mc);
-    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
-    _Float16 p16[16];
-    float lsum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float p = (m_new == -INFINITY) ? 0.0f : exp2f(z[k] - m_new);
-      p16[k] = (_Float16)p;
-      lsum += (float)p16[k];
-    }
-    lsum += shfl_xor_f(lsum, 16);
-    lsum += shfl_xor_f(lsum, 32);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-    // O rows are heads 16*wave + 4g + i: fetch their alpha from lane 4g + i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][i] *= a;
-    }
-
-    __syncthreads();   // V^T of this sub-chunk complete (and the other buffer free)
-
-    // O += P V: k-slice sg covers tiles 2sg, 2sg+1; lane group g holds rows
-    // 32sg + 4g + 0..3 and 32sg + 16 + 4g + 0..3
-#pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
-      f16x8 pa;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pa[i] = p16[4 * (2 * sg) + i];
-        pa[4 + i] = p16[4 * (2 * sg + 1) + i];
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const _Float16 *vrow = vbuf + (dt * 16 + l16) * kVtPitch + 32 * sg + 4 * g;
-        const uint2 a = *reinterpret_cast<const uint2 *>(vrow);
-        const uint2 b = *reinterpret_cast<const uint2 *>(vrow + 16);
-        const f16x8 vb = __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[dt], 0, 0, 0);
+        kq[((item >> 6) * 4 + s) * 64 + (item & 63)] =
+            make_uint4(fp4x2_bf16<0>(w[s], sc), fp4x2_bf16<1>(w[s], sc),
+                       fp4x2_bf16<2>(w[s], sc), fp4x2_bf16<3>(w[s], sc));
       }
     }
+    {
+      const int pr = item & 31, b = item >> 5;
+      const _Float16 sa = (_Float16)e4m3_to_f32(gd.vs[it] & 0xFFu);
+      const _Float16 sb = (_Float16)e4m3_to_f32((gd.vs[it] >> 8) & 0xFFu);
+      const f16x2 s2a = {sa, sa}, s2b = {sb, sb};
+      uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + 2 * pr);
+#pragma unroll
+      for (int hw = 0; hw < 2; ++hw) {
+        const uint32_t wa = hw ? gd.vc[it][0].y : gd.vc[it][0].x;
+        const uint32_t wb = hw ? gd.vc[it][1].y : gd.vc[it][1].x;
+        f16x2 ra[4], rb[4];
+        ra[0] = fp4x2_f16<0>(wa, s2a), ra[1] = fp4x2_f16<1>(wa, s2a);
+        ra[2] = fp4x2_f16<2>(wa, s2a), ra[3] = fp4x2_f16<3>(wa, s2a);
+        rb[0] = fp4x2_f16<0>(wb, s2b), rb[1] = fp4x2_f16<1>(wb, s2b);
+        rb[2] = fp4x2_f16<2>(wb, s2b), rb[3] = fp4x2_f16<3>(wb, s2b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t a = __builtin_bit_cast(uint32_t, ra[e]);
+          const uint32_t c = __builtin_bit_cast(uint32_t, rb[e]);
+          // channel 8hw + 2e: (row 2pr, row 2pr+1); channel 8hw + 2e + 1 likewise
+          dst[((8 * hw + 2 * e) * kVtPitch) / 2] = (a & 0xFFFFu) | (c << 16);
+          dst[((8 * hw + 2 * e + 1) * kVtPitch) / 2] = (a >> 16) | (c & 0xFFFF0000u);
+        }
+      }
+    }
+  }
 }
 
+// One sub-chunk of 64 rows from LDS: S^T on matrix cores, online softmax,
+// O += P V.
+__device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf,
+                                           const int32_t *rows, int base, const bf16x8 (&qf)[4],
+                                           float scale_log2, int g, int l16, int lane,
+                                           float &m_run, float &l_run, f32x4 (&o)[8]) {
+  // S^T tiles: rows base + 16t + 4g + i, head l16
+  f32x4 st[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, kq[(t * 4 + s) * 64 + lane]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+    }
+    st[t] = acc;
+  }
+
+  // online softmax for head 16*wave + l16
+  float z[16];
+  float mc = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = rows[base + 16 * t + 4 * g + i] >= 0;
+      const float v = ok ? st[t][i] * scale_log2 : -INFINITY;
+      z[4 * t + i] = v;
+      mc = fmaxf(mc, v);
+    }
+  mc = fmaxf(mc, shfl_xor_f(mc, 16));
+  mc = fmaxf(mc, shfl_xor_f(mc, 32));
+  const float m_new = fmaxf(m_run, mc);
+  const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+  _Float16 p16[16];
+  float lsum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float p = (m_new == -INFINITY) ? 0.0f : exp2f(z[k] - m_new);
+    p16[k] = (_Float16)p;
+    lsum += (float)p16[k];
+  }
+  lsum += shfl_xor_f(lsum, 16);
+  lsum += shfl_xor_f(lsum, 32);
+  l_run = l_run * alpha + lsum;
+  m_run = m_new;
+  // O rows are heads 16*wave + 4g + i: fetch their alpha from lane 4g + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt][i] *= a;
+  }
+
+  // O += P V: k-slice sg covers tiles 2sg, 2sg+1; lane group g holds rows
+  // 32sg + 4g + 0..3 and 32sg + 16 + 4g + 0..3
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    f16x8 pa;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pa[i] = p16[4 * (2 * sg) + i];
+      pa[4 + i] = p16[4 * (2 * sg + 1) + i];
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const _Float16 *vrow = vbuf + (dt * 16 + l16) * kVtPitch + 32 * sg + 4 * g;
+      const uint2 a = *reinterpret_cast<const uint2 *>(vrow);
+      const uint2 b = *reinterpret_cast<const uint2 *>(vrow + 16);
+      const f16x8 vb = __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[dt], 0, 0, 0);
+    }
+  }
+}
+
+// One workgroup per (query, split of the selected rows), one wave per 16
+// heads.  Per sub-chunk of 64 rows the workgroup gathers the codes (one
+// sub-chunk ahead, in registers), dequantizes K^ and V^ once into LDS
+// (double buffered) and every wave runs its heads over them.  With a single
+// split the results are final (normalized output and lse); otherwise partial
+// (O, max, sum) per split go to attn_combine_kernel.
 template <int kWaves>
 __global__ void __launch_bounds__(kWaves * 64) attn_partial_kernel(
     const uint8_t *__restrict__ kv_codes, const uint8_t *__restrict__ kv_scales,
     int64_t capacity, const uint16_t *__restrict__ qg, int32_t n_heads,
     const int32_t *__restrict__ q_seq, const int32_t *__restrict__ topk, int32_t top_k,
     int32_t rows_per_split, float scale_log2, float *__restrict__ part_acc,
-    float2 *__restrict__ part_ml, int32_t splits) {
-  __shared__ int32_t rows[kMaxRowsPerSplit + 2 * kSub];   
+    float2 *__restrict__ part_ml, int32_t splits, float *__restrict__ out,
+    float *__restrict__ lse) {
+  constexpr int kThreads = kWaves * 64;
+  __shared__ int32_t rows[kMaxRowsPerSplit + 2 * kSub];
+  __shared__ uint4 kq[2][4 * 4 * 64];
   __shared__ _Float16 vt[2][128 * kVtPitch];
 
   const int split = blockIdx.x;
@@ -212,7 +258,7 @@ __global__ void __launch_bounds__(kWaves * 64) attn_partial_kernel(
   const int nrows = min(rows_per_split, top_k - row0);
   const int nsub = (nrows + kSub - 1) / kSub;
 
-  for (int r = tid; r < (nsub + 2) * kSub; r += kWaves * 64)
+  for (int r = tid; r < (nsub + 2) * kSub; r += kThreads)
     rows[r] = r < nrows ? topk[(int64_t)q * top_k + row0 + r] : -1;
 
   // Q fragment (B operand): head 16*wave + l16, channels 32g..32g+31
@@ -230,20 +276,43 @@ __global__ void __launch_bounds__(kWaves * 64) attn_partial_kernel(
   float m_run = -INFINITY;   // for head 16*wave + l16 (same in all four lane groups)
   float l_run = 0.0f;
 
-  SubChunk<kWaves> bufA, bufB;
-  gather(bufA, rows, 0, kv_codes, kv_scales, seq_base, l16, g, tid);
-  // ping-pong: the gathers of sub-chunk c+1 are issued before sub-chunk c is
-  // computed, with no branch around them and no register copy between buffers
-  // (either would make the compiler wait for the prefetch)
+  // sub-chunk c lives in LDS stage c & 1; its codes were gathered during c - 1
+  Gathered<kThreads> ga, gb;
+  gather(ga, rows, 0, kv_codes, kv_scales, seq_base, tid);
+  dequant(ga, kq[0], vt[0], tid);
+  gather(gb, rows, kSub, kv_codes, kv_scales, seq_base, tid);
+  // ping-pong: each step issues the gathers of c + 2 before computing c, with
+  // no branch around them and no register copy between the two sets
   for (int c = 0; c < nsub; c += 2) {
-    gather(bufB, rows, (c + 1) * kSub, kv_codes, kv_scales, seq_base, l16, g, tid);
-    attend_sub<kWaves>(bufA, rows, c * kSub, vt[0], qf, scale_log2, g, l16, tid, m_run, l_run, o);
+    __syncthreads();
+    gather(ga, rows, (c + 2) * kSub, kv_codes, kv_scales, seq_base, tid);
+    attend_sub(kq[0], vt[0], rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+    dequant(gb, kq[1], vt[1], tid);
     if (c + 1 >= nsub) break;
-    gather(bufA, rows, (c + 2) * kSub, kv_codes, kv_scales, seq_base, l16, g, tid);
-    attend_sub<kWaves>(bufB, rows, (c + 1) * kSub, vt[1], qf, scale_log2, g, l16, tid, m_run, l_run, o);
+    __syncthreads();
+    gather(gb, rows, (c + 3) * kSub, kv_codes, kv_scales, seq_base, tid);
+    attend_sub(kq[1], vt[1], rows, (c + 1) * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+    dequant(ga, kq[0], vt[0], tid);
   }
 
-  // partial results: O rows = heads 16*wave + 4g + i, column d = 16 dt + l16
+  // O rows = heads 16*wave + 4g + i, column d = 16 dt + l16
+  if (splits == 1) {
+    float inv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float l = __shfl(l_run, 4 * g + i, 64);
+      inv[i] = l > 0.0f ? 1.0f / l : 0.0f;
+    }
+    const int64_t obase = (int64_t)q * n_heads;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        out[(obase + wave * 16 + 4 * g + i) * 128 + dt * 16 + l16] = o[dt][i] * inv[i];
+    if (lse != nullptr && g == 0)
+      lse[obase + wave * 16 + l16] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    return;
+  }
   const int64_t pbase = ((int64_t)q * splits + split) * n_heads;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
@@ -315,12 +384,15 @@ __global__ void __launch_bounds__(512) attn_combine_kernel(
   if (lse != nullptr && d == 0) lse[oi] = lse_sh[hl];
 }
 
-// Rows per split: enough workgroups to fill the chip (>= 256 when the batch
-// allows), at most kMaxRowsPerSplit, a multiple of the sub-chunk.
+// Rows per split: as many as possible (one split needs no combine) while the
+// grid still has kTargetGroups workgroups, at most kMaxRowsPerSplit, a
+// multiple of the sub-chunk.
 int32_t rows_per_split(int32_t nq, int32_t top_k) {
   const int32_t subs = (top_k + kSub - 1) / kSub;
-  int32_t per = kMaxRowsPerSplit / kSub;
-  while (per > 1 && (int64_t)nq * ((subs + per - 1) / per) < 256) per /= 2;
+  int32_t splits = (kTargetGroups + nq - 1) / nq;
+  splits = std::max(1, std::min(splits, subs));
+  int32_t per = (subs + splits - 1) / splits;
+  per = std::min(per, kMaxRowsPerSplit / kSub);
   return per * kSub;
 }
 
@@ -331,10 +403,11 @@ AttnWorkspace attn_workspace_layout(const csa2_cache &c, int32_t nq, int32_t n_h
   AttnWorkspace w;
   const int32_t rps = rows_per_split(nq, top_k);
   w.splits = (top_k + rps - 1) / rps;
-  const size_t units = (size_t)nq * w.splits * n_heads;
+  // a single split writes the final results directly (no partials)
+  const size_t units = w.splits > 1 ? (size_t)nq * w.splits * n_heads : 0;
   w.part_acc = 0;
   w.part_ml = align256(units * c.dv * sizeof(float));
-  w.total = align256(w.part_ml + units * sizeof(float2));
+  w.total = std::max<size_t>(256, align256(w.part_ml + units * sizeof(float2)));
   return w;
 }
 
@@ -352,7 +425,7 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
   case W:                                                                                        \
     hipLaunchKernelGGL(attn_partial_kernel<W>, grid, dim3(W * 64), 0, s, c.kv_codes, c.kv_scales, \
                        (int64_t)c.capacity, q, n_heads, q_seq, topk, top_k, rps, scale_log2, acc, \
-                       ml, L.splits);                                                            \
+                       ml, L.splits, out, lse);                                                  \
     break;
   switch (waves) {
     CSA2_ATTN_CASE(1)
@@ -367,6 +440,7 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
       return hipErrorInvalidValue;
   }
 #undef CSA2_ATTN_CASE
+  if (L.splits == 1) return hipGetLastError();
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(n_heads / 4), (unsigned)nq), dim3(512),
                      0, s, acc, ml, n_heads, L.splits, out, lse);
   return hipGetLastError();
