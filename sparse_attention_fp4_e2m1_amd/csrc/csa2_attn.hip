@@ -30,7 +30,7 @@ namespace {
 constexpr int kSub = 64;                      // rows per sub-chunk
 constexpr int kVtPitch = kSub + 4;            // fp16 elements per LDS row of V^T
 constexpr int kMaxRowsPerSplit = 2048;
-constexpr int kTargetGroups = 512;            // workgroups aimed for (two per CU)
+constexpr int kTargetGroups = 256;            // workgroups aimed for (one per CU)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -277,12 +277,15 @@ __global__ void __launch_bounds__(kWaves * 64) attn_partial_kernel(
   float l_run = 0.0f;
 
   // sub-chunk c lives in LDS stage c & 1; its codes were gathered during c - 1
+  // Sub-chunk c lives in LDS stage c & 1; its codes are gathered one
+  // sub-chunk ahead, into register set c & 1 (the loop is unrolled by two so
+  // that each set is a fixed register array): no branch around a gather and no
+  // copy between sets, so the compiler waits only for the set being
+  // dequantized.  (Deeper register rings measured slower: code size.)
   Gathered<kThreads> ga, gb;
   gather(ga, rows, 0, kv_codes, kv_scales, seq_base, tid);
   dequant(ga, kq[0], vt[0], tid);
   gather(gb, rows, kSub, kv_codes, kv_scales, seq_base, tid);
-  // ping-pong: each step issues the gathers of c + 2 before computing c, with
-  // no branch around them and no register copy between the two sets
   for (int c = 0; c < nsub; c += 2) {
     __syncthreads();
     gather(ga, rows, (c + 2) * kSub, kv_codes, kv_scales, seq_base, tid);

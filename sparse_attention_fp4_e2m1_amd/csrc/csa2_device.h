@@ -57,40 +57,51 @@ __device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int mask) {
   return (uint32_t)__shfl_xor((int)v, mask, kWave);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// x + (x of the lane selected by the DPP control kCtrl); lanes without a
+// source, or in rows outside kRowMask, add 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_add(uint32_t x) {
+  return x + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, in DPP moves: shifts by
+// 1, 2, 4, 8 within each row of 16 lanes, then row 0's total into row 1 and
+// row 2's into row 3 (row_bcast:15), then rows 0-1's total into rows 2-3
+// (row_bcast:31).
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t t = (uint32_t)__shfl_up((int)v, d, kWave);
-    if (lane >= d) v += t;
-  }
+  v = dpp_add<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);   // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+  v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
   return v;
 }
 
 // Exclusive prefix sum over the block; `scratch` holds >= blockDim/64 + 1 words.
-// Returns the exclusive prefix, writes the block total.  Contains barriers.
+// Returns the exclusive prefix, writes the block total.  Two barriers; every
+// thread adds the wave totals before its own (at most 16).
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
                                                          uint32_t &total) {
+  constexpr int kMaxWaves = 16;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int nwaves = blockDim.x / kWave;
-  uint32_t inc = wave_inclusive_scan(v);
-  __syncthreads();
+  const uint32_t inc = wave_inclusive_scan(v);
+  __syncthreads();   // scratch free: readers of a previous scan are done
   if (lane == kWave - 1) scratch[wave] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t acc = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      uint32_t t = scratch[w];
-      scratch[w] = acc;
-      acc += t;
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kMaxWaves; ++w) {
+    if (w < nwaves) {
+      const uint32_t t = scratch[w];
+      all += t;
+      before += w < wave ? t : 0u;
     }
-    scratch[nwaves] = acc;
   }
-  __syncthreads();
-  total = scratch[nwaves];
-  return scratch[wave] + inc - v;
+  total = all;
+  return before + inc - v;
 }
 
 }  // namespace csa2

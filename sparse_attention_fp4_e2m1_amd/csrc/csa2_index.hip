@@ -11,21 +11,28 @@
 //
 // Kernels, in launch order for one call:
 //   zero2_u32_kernel clear the per-query histograms
-//   score_kernel     stream the (tiled) index keys, compute the canonical fp32
+//   score_kernel     (Full, or Reindex without a pool; gather_score_kernel for
+//                    a Reindex pool) stream the (tiled) index keys, compute the canonical fp32
 //                    score of each candidate, keep its order-preserving key
 //                    (written out per workgroup in one burst), histogram the
 //                    top 12 key bits, and for a pool-building Full layer the
 //                    8-position block maxima and their histogram.
-//   bins_kernel      per query: the bin b1 of the 12-bit histogram holding the
-//                    K-th largest key.
 //   filter_kernel    per wave and 1024 keys: keep every key whose top 12 bits
-//                    reach b1, with its index, in index order (ballot compaction)
+//                    reach b1 -- the bin of the 12-bit histogram holding the
+//                    K-th largest key, which each workgroup reads off the
+//                    histogram itself -- with its index, in index order
+//                    (ballot compaction)
 //   resolve_kernel   per query: the candidates (typically K plus one bin) in
 //                    LDS; radix passes on bits 19..8 and 7..0 within bin b1 give
 //                    the K-th largest key tau; an ordered compaction emits every
 //                    key > tau and the first ties == tau, ascending, -1 padded.
 //                    With more candidates than LDS holds (heavy ties) it
 //                    streams the full key array with the same logic.
+//                    A pool-building Full layer selects its pool blocks in the
+//                    same filter and resolve launches (a second grid slice).
+//                    Key arrays of at most kDirectMax entries (a Reindex pool)
+//                    skip the filter: the resolve reads and compacts them.
+// Small score chunks (one wave) count keys straight into the global histogram.
 //   copy_i32_kernel  Reuse mode: topk_out = reuse_src.
 // The selection helpers (select_bin, select_core, gather_regions) live in
 // csa2_select.h; E4M3 index queries against E4M3 keys over every visible
@@ -39,6 +46,7 @@ namespace {
 
 constexpr int kFilterThreads = 256;
 constexpr int kFilterSub = 1024;           // keys per filter wave (one candidate slot region)
+constexpr int64_t kDirectMax = 32768;      // up to this many keys the resolve filters them itself
 
 #ifndef CSA2_SCORE_UNROLL
 #define CSA2_SCORE_UNROLL 4            // 16-B loads per lane per prefetch batch
@@ -97,17 +105,20 @@ __global__ void copy_i32_kernel(int32_t *__restrict__ dst, const int32_t *__rest
 // quads are uniform by then) DPP adds.  Every lane of a token ends with the
 // same bits.
 // ---------------------------------------------------------------------------
-template <int H, bool kFp8Keys, bool kPool, bool kReindexPool, int kThreads, int kChunk>
+template <int H, bool kFp8Keys, bool kPool, int kThreads, int kChunk>
 struct ScoreCtx {
+  // Small chunks count their keys straight into the query's global histogram
+  // (one atomic per key) instead of clearing and flushing 4096 LDS bins.
+  static constexpr bool kDirectHist = kChunk <= kWave && !kPool;
   static constexpr int kEsz = kFp8Keys ? 1 : 2;
   static constexpr int TPI = kWave / H;
   static constexpr int kLoads = 4 * kEsz;
   static constexpr int kNumWaves = kThreads / kWave;
   const uint8_t *seq_base;
-  const int32_t *spool;    // this chunk's pool entries, staged in LDS (Reindex)
   int32_t qp;
   int64_t t_begin, t_end;
   int wave, h, tl, lane;
+  uint32_t *ghist;         // the query's global histogram (kDirectHist)
 
   // Step s of this wave covers tile s * kNumWaves + wave of the chunk, so at
   // any step the workgroup's waves read adjacent tiles (one moving window).
@@ -123,13 +134,8 @@ struct ScoreCtx {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t t = token(s0 + u);
-      bool valid = t < t_end;
-      int64_t row = valid ? t : t_begin;
-      if (kReindexPool) {
-        const int32_t p = valid ? spool[t - t_begin] : -1;
-        valid = valid && p >= 0 && p <= qp;
-        row = valid ? (int64_t)p : 0;
-      }
+      const bool valid = t < t_end;
+      const int64_t row = valid ? t : t_begin;
       val[u] = valid;
       // Full mode: row % TPI == tl, so a wave's loads cover one tile contiguously
       const uint8_t *src = seq_base + idx_chunk_offset<H, kEsz>(row, h, 0);
@@ -197,7 +203,10 @@ struct ScoreCtx {
     const int64_t t = tile_start(grp * H + lane / TPI) + lane % TPI;
     if (t < t_end) {
       skeys[t - t_begin] = key;
-      atomicAdd(&hist[key >> 21], 1u << ((key >> 16) & 16u));
+      if (kDirectHist)
+        atomicAdd(&ghist[key >> 20], 1u);
+      else
+        atomicAdd(&hist[key >> 21], 1u << ((key >> 16) & 16u));
     }
     if (kPool) {
       // block maximum over lanes 8b..8b+7 (keys of tokens past the end count as 0)
@@ -213,13 +222,12 @@ struct ScoreCtx {
   }
 };
 
-template <int H, bool kFp8Keys, bool kPool, bool kReindexPool, int kThreads, int kChunk>
+template <int H, bool kFp8Keys, bool kPool, int kThreads, int kChunk>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kThreads == 64 ? 2 : (kFp8Keys ? CSA2_SCORE_WAVES : CSA2_SCORE_WAVES - 1))))
 score_kernel(
     const uint8_t *__restrict__ idx_k, int64_t capacity, const uint16_t *__restrict__ q_idx,
     int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
-    const int32_t *__restrict__ pool_in, int32_t pool_len,
     uint32_t *__restrict__ keys_tok, int64_t tok_stride, uint32_t *__restrict__ hist_tok,
     uint32_t *__restrict__ keys_blk, int64_t blk_stride, uint32_t *__restrict__ hist_blk) {
   constexpr int kEsz = kFp8Keys ? 1 : 2;
@@ -238,25 +246,24 @@ score_kernel(
   __shared__ uint32_t histb[kPool ? kHistBins / 2 : 1];
   __shared__ uint32_t sblk[kPool ? kChunk / kPoolBlock : 1];
   __shared__ float qlds[H * 64];
-  __shared__ int32_t spool[kReindexPool ? kChunk : 1];
   uint32_t *hist = lds_main;
   uint32_t *skeys = lds_main + kHistBins / 2;
 
   const int q = blockIdx.y;
   const int32_t qp = q_pos[q];
-  const int64_t n = kReindexPool ? (int64_t)pool_len : (int64_t)qp + 1;
+  const int64_t n = (int64_t)qp + 1;
   const int64_t t_begin = (int64_t)blockIdx.x * kChunk;
   if (t_begin >= n) return;
   const int64_t t_end = min(n, t_begin + kChunk);
 
-  for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
-    hist[i] = 0u;
-    if (kPool) histb[i] = 0u;
+  using Ctx = ScoreCtx<H, kFp8Keys, kPool, kThreads, kChunk>;
+  uint32_t *hq = hist_tok + (int64_t)q * (kHistBins + kStateWords);
+  if (!Ctx::kDirectHist) {
+    for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
+      hist[i] = 0u;
+      if (kPool) histb[i] = 0u;
+    }
   }
-  // Reindex: the chunk's pool entries, staged once (no dependent load per gather)
-  if (kReindexPool)
-    for (int64_t i = threadIdx.x; i < t_end - t_begin; i += kThreads)
-      spool[i] = pool_in[(int64_t)q * pool_len + t_begin + i];
   // the index query as scored (bf16, or cast to E4M3), staged once through LDS
   for (int i = threadIdx.x; i < H * 64; i += kThreads) {
     float f = bf16_to_f32(q_idx[(int64_t)q * H * 64 + i]);
@@ -285,8 +292,7 @@ score_kernel(
   const int64_t ntiles = (t_end - t_begin + TPI - 1) / TPI;
   const int64_t wave_steps = (ntiles + kNumWaves - 1) / kNumWaves;
   const int nsteps = (int)((wave_steps + H - 1) / H * H);
-  ScoreCtx<H, kFp8Keys, kPool, kReindexPool, kThreads, kChunk> cx{
-      seq_base, spool, qp, t_begin, t_end, wave, h, tl, lane};
+  Ctx cx{seq_base, qp, t_begin, t_end, wave, h, tl, lane, hq};
   uint4 bufA[kUnroll][kLoads], bufB[kUnroll][kLoads];
   bool valA[kUnroll], valB[kUnroll];
   uint32_t mykey = 0u;
@@ -313,7 +319,7 @@ score_kernel(
       for (int64_t i = threadIdx.x; i < nb; i += kThreads) db[i] = sblk[i];
     }
   }
-  uint32_t *hq = hist_tok + (int64_t)q * (kHistBins + kStateWords);
+  if (Ctx::kDirectHist) return;
   uint32_t *hbq = kPool ? hist_blk + (int64_t)q * (kHistBins + kStateWords) : nullptr;
   for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
     const uint32_t w = hist[i];
@@ -328,58 +334,159 @@ score_kernel(
 
 }
 
-// One workgroup per (query, key array): bin b1 of the K-th largest key from the
-// query's 12-bit histogram, written to the state words after the histogram.
-__global__ void __launch_bounds__(kSelectThreads) bins_kernel(
-    uint32_t *__restrict__ hist_tok, uint32_t *__restrict__ hist_blk, const int32_t *__restrict__ q_pos,
-    int32_t pool_len, int32_t reindex_pool, int32_t top_k, int32_t pool_blocks) {
-  __shared__ uint32_t lds[kHistBins];
-  __shared__ uint32_t scratch[kSelectThreads / kWave + 1];
-  __shared__ uint32_t res[2];
-  const int q = blockIdx.x;
-  const bool blocks = blockIdx.y == 1;
+// ---------------------------------------------------------------------------
+// gather_score_kernel: Reindex over a pool.  Each lane takes one pool entry:
+// it gathers the entry's index keys (all its 16-B pieces in flight at once;
+// the pool's positions are scattered, so there is nothing to coalesce across
+// lanes) and runs the canonical fp32 order in-lane -- per head and 16-channel
+// block an FMA chain in channel order, blocks (b0+b1)+(b2+b3), heads a
+// balanced pairwise tree -- the same bits as score_kernel.  Keys go out as one
+// coalesced store per lane; the 12-bit histogram is aggregated in LDS, where
+// only the bins in use are cleared and flushed.
+// ---------------------------------------------------------------------------
+constexpr int kGatherThreads = 256;
+
+template <int H, bool kFp8Keys>
+__global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
+    const uint8_t *__restrict__ idx_k, int64_t capacity, const uint16_t *__restrict__ q_idx,
+    int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
+    const int32_t *__restrict__ pool_in, int32_t pool_len, uint32_t *__restrict__ keys_tok,
+    int64_t tok_stride, uint32_t *__restrict__ hist_tok) {
+  constexpr int kEsz = kFp8Keys ? 1 : 2;
+  constexpr int kLoadsPerHead = 4 * kEsz;                  // 16-B pieces per head (64 channels)
+  constexpr int kHeadsPerBatch = 32 / kLoadsPerHead < H ? 32 / kLoadsPerHead : H;
+  __shared__ float qlds[H * 64];
+  __shared__ uint32_t lh[kHistBins];
+  const int q = blockIdx.y;
+  const int tid = threadIdx.x;
   const int32_t qp = q_pos[q];
-  int64_t n = reindex_pool ? (int64_t)pool_len : (int64_t)qp + 1;
-  if (blocks) n = (n + kPoolBlock - 1) / kPoolBlock;
-  uint32_t *hq = (blocks ? hist_blk : hist_tok) + (int64_t)q * (kHistBins + kStateWords);
-  for (int i = threadIdx.x; i < kHistBins; i += kSelectThreads) lds[i] = hq[i];
-  __syncthreads();
-  const int64_t n_valid = n - (int64_t)lds[0];   // key 0 marks an empty pool slot
-  const uint32_t keff = (uint32_t)min((int64_t)(blocks ? pool_blocks : top_k), n_valid);
-  if (keff > 0) {
-    select_bin(lds, kHistBins, keff, scratch, res);
-  } else if (threadIdx.x == 0) {
-    res[0] = 0u;
-    res[1] = 0u;
+  const int64_t t = (int64_t)blockIdx.x * kGatherThreads + tid;
+  const bool in = t < pool_len;
+  const int32_t p = in ? pool_in[(int64_t)q * pool_len + t] : -1;
+  const bool valid = p >= 0 && p <= qp;
+  const int64_t row = valid ? p : 0;
+  const uint8_t *base = idx_k + (int64_t)q_seq[q] * capacity * (H * 64 * kEsz);
+  for (int i = tid; i < H * 64; i += kGatherThreads) {
+    float f = bf16_to_f32(q_idx[(int64_t)q * H * 64 + i]);
+    if (q_fp8) f = e4m3_to_f32(e4m3_from_f32_nonneg(fabsf(f)) | ((__float_as_uint(f) >> 24) & 0x80u));
+    qlds[i] = f;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    hq[kHistBins + kBin] = res[0];
-    hq[kHistBins + kAbove] = res[1];
-    hq[kHistBins + kKeff] = keff;
+
+  float hs[H];
+#pragma unroll
+  for (int hb = 0; hb < H; hb += kHeadsPerBatch) {
+    uint4 buf[kHeadsPerBatch][kLoadsPerHead];
+#pragma unroll
+    for (int hh = 0; hh < kHeadsPerBatch; ++hh) {
+      const uint8_t *src = base + idx_chunk_offset<H, kEsz>(row, hb + hh, 0);
+#pragma unroll
+      for (int v = 0; v < kLoadsPerHead; ++v)
+        buf[hh][v] = *reinterpret_cast<const uint4 *>(src + v * 1024);
+    }
+    // every load of the batch in flight before the math: the empty asm uses
+    // each result here, so the compiler cannot sink a load next to its use
+#pragma unroll
+    for (int hh = 0; hh < kHeadsPerBatch; ++hh)
+#pragma unroll
+      for (int v = 0; v < kLoadsPerHead; ++v)
+        asm volatile("" ::"v"(buf[hh][v].x), "v"(buf[hh][v].y), "v"(buf[hh][v].z),
+                     "v"(buf[hh][v].w));
+#pragma unroll
+    for (int hh = 0; hh < kHeadsPerBatch; ++hh) {
+      const float *qh = qlds + (hb + hh) * 64;
+      float blk[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float acc = 0.0f;
+        if (kFp8Keys) {
+          const uint4 a = buf[hh][j];
+          const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
+            auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
+            acc = __builtin_fmaf(qh[16 * j + 4 * k + 0], lo[0], acc);
+            acc = __builtin_fmaf(qh[16 * j + 4 * k + 1], lo[1], acc);
+            acc = __builtin_fmaf(qh[16 * j + 4 * k + 2], hi[0], acc);
+            acc = __builtin_fmaf(qh[16 * j + 4 * k + 3], hi[1], acc);
+          }
+        } else {
+#pragma unroll
+          for (int hv = 0; hv < 2; ++hv) {
+            const uint4 a = buf[hh][2 * j + hv];
+            const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              acc = __builtin_fmaf(qh[16 * j + 8 * hv + 2 * k], __uint_as_float(w[k] << 16), acc);
+              acc = __builtin_fmaf(qh[16 * j + 8 * hv + 2 * k + 1],
+                                   __uint_as_float(w[k] & 0xFFFF0000u), acc);
+            }
+          }
+        }
+        blk[j] = acc;
+      }
+      hs[hb + hh] = (blk[0] + blk[1]) + (blk[2] + blk[3]);
+    }
+  }
+#pragma unroll
+  for (int w = 1; w < H; w *= 2)      // balanced pairwise tree over heads
+#pragma unroll
+    for (int i = 0; i < H; i += 2 * w) hs[i] = hs[i] + hs[i + w];
+  const uint32_t key = valid ? score_key(hs[0]) : 0u;
+  if (in) keys_tok[(int64_t)q * tok_stride + t] = key;
+
+  const uint32_t bin = key >> 20;
+  if (in) lh[bin] = 0u;
+  __syncthreads();
+  if (in) atomicAdd(&lh[bin], 1u);
+  __syncthreads();
+  if (in) {
+    const uint32_t c = atomicExch(&lh[bin], 0u);
+    if (c) atomicAdd(&hist_tok[(int64_t)q * (kHistBins + kStateWords) + bin], c);
   }
 }
 
-// One wave per kFilterSub keys: keep every key whose top 12 bits reach bin b1,
-// with its index, in index order, into the wave's own slot region.
-template <int kMode>
+// One selection problem of a call: per query, the kk largest keys of an array
+// (the scored candidates, or the pool blocks of a pool-building Full layer).
+struct SelProblem {
+  const uint32_t *keys;   // [nq][n_stride] order-preserving keys
+  int64_t n_stride;
+  const uint32_t *hist;   // [nq][kHistBins + kStateWords] top-12-bit histogram
+  uint32_t *cand_key;     // [nq][cand_stride] filter output, one region per kFilterSub keys
+  int32_t *cand_id;
+  int64_t cand_stride;
+  uint32_t *cnt;          // [nq][nsub] candidates per region
+  int64_t nsub;
+  int32_t *out;           // [nq][out_stride]
+  int64_t out_stride;
+  int32_t kk;
+  int32_t mode;           // OutMode
+  int32_t direct;         // short arrays: no filter pass, the resolve reads the keys
+};
+
+struct SelProblems {
+  SelProblem p[2];
+};
+
+// grid (filter groups, nq, problems).  Each wave takes kFilterSub keys and
+// keeps every key whose top 12 bits reach bin b1, with its index, in index
+// order, in its own slot region.  Every workgroup derives b1 from the query's
+// histogram itself (16 KB from L2), so no separate pass is needed.
 __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
-    const uint32_t *__restrict__ keys, int64_t stride, const uint32_t *__restrict__ hist_g,
-    const int32_t *__restrict__ q_pos, int32_t pool_len, uint32_t *__restrict__ cand_key,
-    int32_t *__restrict__ cand_id, int64_t cand_stride, uint32_t *__restrict__ cnt,
-    int64_t cnt_stride) {
+    const SelProblems P, const int32_t *__restrict__ q_pos, int32_t pool_len) {
+  __shared__ uint32_t lh[kHistBins];
+  __shared__ uint32_t scratch[kFilterThreads / kWave + 1];
+  __shared__ uint32_t res[4];
+  const SelProblem &A = P.p[blockIdx.z];
   const int q = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
+  const int64_t n = sel_len(A.mode, q_pos[q], pool_len);
+  if (A.direct || (int64_t)blockIdx.x * (kFilterThreads / kWave) * kFilterSub >= n) return;   // uniform
+  // the wave's keys first (their loads overlap the threshold's)
   const int64_t sub = (int64_t)blockIdx.x * (kFilterThreads / kWave) + threadIdx.x / kWave;
-  const int64_t n = array_len<kMode>(q_pos[q], pool_len);
   const int64_t start = sub * kFilterSub;
-  if (start >= n) return;
-  const uint32_t *st = hist_g + (int64_t)q * (kHistBins + kStateWords) + kHistBins;
-  const bool none = st[kKeff] == 0u;
-  const uint32_t thr = st[kBin] << 20;
-  const uint32_t *kq = keys + (int64_t)q * stride;
-  uint32_t *ck = cand_key + (int64_t)q * cand_stride + start;
-  int32_t *ci = cand_id + (int64_t)q * cand_stride + start;
+  const uint32_t *kq = A.keys + (int64_t)q * A.n_stride;
   // 4 x 4 keys per lane; key (k, lane, e) sits at start + k*256 + lane*4 + e
   uint32_t kv[4][4];
 #pragma unroll
@@ -396,6 +503,13 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
       for (int e = 0; e < 4; ++e) kv[k][e] = i0 + e < n ? kq[i0 + e] : 0u;
     }
   }
+  const Threshold th =
+      hist_threshold(A.hist + (int64_t)q * (kHistBins + kStateWords), n, A.kk, lh, scratch, res);
+  if (start >= n) return;
+  const bool none = th.keff == 0u;
+  const uint32_t thr = th.b1 << 20;
+  uint32_t *ck = A.cand_key + (int64_t)q * A.cand_stride + start;
+  int32_t *ci = A.cand_id + (int64_t)q * A.cand_stride + start;
   const uint64_t lt = (1ull << lane) - 1ull;
   uint32_t written = 0;
 #pragma unroll
@@ -421,114 +535,184 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
     }
     written += total;
   }
-  if (lane == 0) cnt[(int64_t)q * cnt_stride + sub] = written;
+  if (lane == 0) A.cnt[(int64_t)q * A.nsub + sub] = written;
 }
 
-template <int kMode>
+// grid (nq, problems).  Per query: b1 from the histogram, the candidates of
+// the filter's regions in index order into LDS, the radix passes and the
+// ordered compaction; with more candidates than LDS holds (heavy ties) it
+// streams the full key array instead.  Then the -1 padding.
 __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
-    const uint32_t *__restrict__ keys, int64_t stride, const uint32_t *__restrict__ hist_g,
-    const int32_t *__restrict__ q_pos, const int32_t *__restrict__ pool_in, int32_t pool_len,
-    int32_t kk, const uint32_t *__restrict__ cand_key, const int32_t *__restrict__ cand_id,
-    int64_t cand_stride, const uint32_t *__restrict__ cnt, int64_t cnt_stride,
-    int32_t *__restrict__ out, int64_t out_stride) {
+    const SelProblems P, const int32_t *__restrict__ q_pos, const int32_t *__restrict__ pool_in,
+    int32_t pool_len) {
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t scratch[kSelectThreads / kWave + 1];
-  __shared__ uint32_t res[2];
+  __shared__ uint32_t res[4];
   __shared__ uint32_t lkey[kResolveCap];
   __shared__ int32_t lid[kResolveCap];
   __shared__ uint32_t goff[kSelectThreads];
 
+  const SelProblem &A = P.p[blockIdx.y];
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t qp = q_pos[q];
-  const int64_t n = array_len<kMode>(qp, pool_len);
-  const uint32_t *st = hist_g + (int64_t)q * (kHistBins + kStateWords) + kHistBins;
-  const uint32_t keff = st[kKeff];
-  const uint32_t b1 = st[kBin];
-  const uint32_t above1 = st[kAbove];
-  Emit<kMode> emit{out + (int64_t)q * out_stride,
-                   pool_in ? pool_in + (int64_t)q * pool_len : nullptr, qp};
-
-  // candidates of the filter's slot regions, in index order, into LDS
+  const int64_t n = sel_len(A.mode, qp, pool_len);
+  // A short key array is read here, in one batch of loads issued before the
+  // histogram's (keys 4*tid + 4096*it .. +3 of iteration it).
+  constexpr int kDirectIters = (int)(kDirectMax / (4 * kSelectThreads));
+  const uint32_t *kq = A.keys + (int64_t)q * A.n_stride;
+  uint4 kr[kDirectIters];
+  if (A.direct) {
+#pragma unroll
+    for (int it = 0; it < kDirectIters; ++it) {
+      const int64_t i0 = (int64_t)it * 4 * kSelectThreads + 4 * tid;
+      kr[it] = i0 + 3 < n ? *reinterpret_cast<const uint4 *>(kq + i0) : make_uint4(0u, 0u, 0u, 0u);
+      if (i0 < n && i0 + 3 >= n) {
+        kr[it].x = kq[i0];
+        if (i0 + 1 < n) kr[it].y = kq[i0 + 1];
+        if (i0 + 2 < n) kr[it].z = kq[i0 + 2];
+      }
+    }
+  }
   const int64_t nsub = (n + kFilterSub - 1) / kFilterSub;
-  const uint32_t carry =
-      gather_regions(cnt + (int64_t)q * cnt_stride, nsub, kFilterSub,
-                     SplitSlots{cand_key + (int64_t)q * cand_stride,
-                                cand_id + (int64_t)q * cand_stride},
-                     lkey, lid, goff, scratch);
-  if (carry <= kResolveCap) {
-    select_core(LdsCands{lkey, lid}, (int64_t)carry, keff, b1, above1, hist, scratch, res, emit);
+  const uint32_t *cq = A.cnt + (int64_t)q * A.nsub;
+  const uint32_t first_count = A.direct ? 0u : first_region_count(cq, nsub);
+  const Threshold th =
+      hist_threshold(A.hist + (int64_t)q * (kHistBins + kStateWords), n, A.kk, hist, scratch, res);
+  const EmitAny emit{A.mode, A.out + (int64_t)q * A.out_stride,
+                     pool_in ? pool_in + (int64_t)q * pool_len : nullptr, qp, (uint32_t)A.kk};
+
+  // the candidates (keys whose top 12 bits reach b1), in index order, into LDS:
+  // straight from a short key array, or from the filter's slot regions
+  uint32_t carry = 0;
+  if (A.direct) {
+    const uint32_t thr = th.b1 << 20;
+#pragma unroll
+    for (int it = 0; it < kDirectIters; ++it) {
+      const int64_t base = (int64_t)it * 4 * kSelectThreads;
+      if (base >= n) break;   // uniform
+      const int64_t i0 = base + 4 * tid;
+      const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c += (th.keff > 0 && i0 + e < n && k4[e] >= thr) ? 1u : 0u;
+      uint32_t tot;
+      uint32_t o = carry + block_exclusive_scan(c, scratch, tot);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (th.keff > 0 && i0 + e < n && k4[e] >= thr) {
+          if (o < kResolveCap) {
+            lkey[o] = k4[e];
+            lid[o] = (int32_t)(i0 + e);
+          }
+          ++o;
+        }
+      }
+      carry += tot;
+    }
+    __syncthreads();
   } else {
-    select_core(GlobalKeys{keys + (int64_t)q * stride}, n, keff, b1, above1, hist, scratch, res,
-                emit);
+    carry = gather_regions(cq, nsub, kFilterSub,
+                           SplitSlots{A.cand_key + (int64_t)q * A.cand_stride,
+                                      A.cand_id + (int64_t)q * A.cand_stride},
+                           lkey, lid, goff, scratch, first_count);
+  }
+  if (carry <= kResolveCap) {
+    select_core(LdsCands{lkey, lid}, (int64_t)carry, th.keff, th.b1, th.above, hist, scratch,
+                res, emit);
+  } else {
+    select_core(GlobalKeys{A.keys + (int64_t)q * A.n_stride}, n, th.keff, th.b1, th.above, hist,
+                scratch, res, emit);
   }
   // padding
-  const int64_t pad_from = (kMode == kOutPoolBlocks) ? (int64_t)keff * kPoolBlock : keff;
-  const int64_t pad_to = (kMode == kOutPoolBlocks) ? (int64_t)kk * kPoolBlock : kk;
-  int32_t *oq = out + (int64_t)q * out_stride;
+  const bool blocks = A.mode == kOutPoolBlocks;
+  const int64_t pad_from = blocks ? (int64_t)th.keff * kPoolBlock : th.keff;
+  const int64_t pad_to = blocks ? (int64_t)A.kk * kPoolBlock : A.kk;
+  int32_t *oq = A.out + (int64_t)q * A.out_stride;
   for (int64_t i = pad_from + tid; i < pad_to; i += kSelectThreads) oq[i] = -1;
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int H, bool kFp8, bool kPool, bool kReindexPool, int kThreads, int kChunk>
+template <int H, bool kFp8, bool kPool, int kThreads, int kChunk>
 void launch_score_shape(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
   const csa2_cache &c = *a.cache;
   const TopkWorkspace &L = a.layout;
   dim3 grid((unsigned)((n_cand_max + kChunk - 1) / kChunk), (unsigned)a.nq);
-  const int32_t *pool = kReindexPool ? a.pool_in : nullptr;
-  hipLaunchKernelGGL((score_kernel<H, kFp8, kPool, kReindexPool, kThreads, kChunk>), grid,
-                     dim3(kThreads), 0, s, static_cast<const uint8_t *>(c.idx_k),
-                     (int64_t)c.capacity, a.q_idx, a.q_fp8, a.q_seq, a.q_pos, pool, a.pool_len,
-                     reinterpret_cast<uint32_t *>(a.ws + L.tok.keys),
-                     L.tok.n, reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
+  hipLaunchKernelGGL((score_kernel<H, kFp8, kPool, kThreads, kChunk>), grid, dim3(kThreads), 0, s,
+                     static_cast<const uint8_t *>(c.idx_k), (int64_t)c.capacity, a.q_idx, a.q_fp8,
+                     a.q_seq, a.q_pos, reinterpret_cast<uint32_t *>(a.ws + L.tok.keys), L.tok.n,
+                     reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
                      kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.keys) : nullptr, L.blk.n,
                      kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr);
 }
 
 // Workgroup shape from the amount of work: long streams when there are enough
-// groups, one-wave groups for small searches (a Reindex pool) so that the
-// gathers spread over the chip.
-template <int H, bool kFp8, bool kPool, bool kReindexPool>
+// groups, one-wave groups for small searches so that they spread over the chip.
+template <int H, bool kFp8, bool kPool>
 void launch_score(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
   const int64_t big = (int64_t)a.nq * ((n_cand_max + 4095) / 4096);
   const int64_t mid = (int64_t)a.nq * ((n_cand_max + 2047) / 2048);
   if (big >= kBigChunkMinGroups)
-    launch_score_shape<H, kFp8, kPool, kReindexPool, 256, 4096>(a, n_cand_max, s);
+    launch_score_shape<H, kFp8, kPool, 256, 4096>(a, n_cand_max, s);
   else if (mid >= kSmallGridGroups || kPool)
-    launch_score_shape<H, kFp8, kPool, kReindexPool, 256, 2048>(a, n_cand_max, s);
+    launch_score_shape<H, kFp8, kPool, 256, 2048>(a, n_cand_max, s);
   else
-    launch_score_shape<H, kFp8, false, kReindexPool, 64, 64>(a, n_cand_max, s);
+    launch_score_shape<H, kFp8, false, 64, 64>(a, n_cand_max, s);
 }
 
 template <int H, bool kFp8>
 void launch_score_mode(const IndexArgs &a, int64_t n, bool pool, bool reindex_pool, hipStream_t s) {
-  if (pool) launch_score<H, kFp8, true, false>(a, n, s);
-  else if (reindex_pool) launch_score<H, kFp8, false, true>(a, n, s);
-  else launch_score<H, kFp8, false, false>(a, n, s);
+  if (reindex_pool) {
+    const TopkWorkspace &L = a.layout;
+    hipLaunchKernelGGL((gather_score_kernel<H, kFp8>),
+                       dim3((unsigned)((a.pool_len + kGatherThreads - 1) / kGatherThreads),
+                            (unsigned)a.nq),
+                       dim3(kGatherThreads), 0, s, static_cast<const uint8_t *>(a.cache->idx_k),
+                       (int64_t)a.cache->capacity, a.q_idx, a.q_fp8, a.q_seq, a.q_pos, a.pool_in,
+                       a.pool_len, reinterpret_cast<uint32_t *>(a.ws + L.tok.keys), L.tok.n,
+                       reinterpret_cast<uint32_t *>(a.ws + L.tok.hist));
+  } else if (pool) {
+    launch_score<H, kFp8, true>(a, n, s);
+  } else {
+    launch_score<H, kFp8, false>(a, n, s);
+  }
 }
 
-template <int kMode>
-void launch_select(const IndexArgs &a, const SelectArrays &A, int32_t kk, int32_t *out,
-                   int64_t out_stride, hipStream_t s) {
+SelProblem sel_problem(const IndexArgs &a, const SelectArrays &A, int32_t kk, int mode,
+                       int32_t *out, int64_t out_stride) {
   uint8_t *w = a.ws;
-  const int32_t pool_len = kMode == kOutPoolIds ? a.pool_len : 0;
+  SelProblem p;
+  p.keys = reinterpret_cast<const uint32_t *>(w + A.keys);
+  p.n_stride = A.n;
+  p.hist = reinterpret_cast<const uint32_t *>(w + A.hist);
+  p.cand_key = reinterpret_cast<uint32_t *>(w + A.cand_key);
+  p.cand_id = reinterpret_cast<int32_t *>(w + A.cand_id);
+  p.cand_stride = A.cand_stride;
+  p.cnt = reinterpret_cast<uint32_t *>(w + A.cnt);
+  p.nsub = A.nsub;
+  p.out = out;
+  p.out_stride = out_stride;
+  p.kk = kk;
+  p.mode = mode;
+  p.direct = A.n <= kDirectMax;
+  return p;
+}
+
+// Filter + resolve of one or two selection problems (tokens, pool blocks),
+// both problems in the same two launches.
+void launch_select(const IndexArgs &a, const SelProblems &P, int nprob, int64_t max_nsub,
+                   hipStream_t s) {
   const int64_t waves = kFilterThreads / kWave;
-  hipLaunchKernelGGL((filter_kernel<kMode>),
-                     dim3((unsigned)((A.nsub + waves - 1) / waves), (unsigned)a.nq),
-                     dim3(kFilterThreads), 0, s, reinterpret_cast<const uint32_t *>(w + A.keys), A.n,
-                     reinterpret_cast<const uint32_t *>(w + A.hist), a.q_pos, pool_len,
-                     reinterpret_cast<uint32_t *>(w + A.cand_key),
-                     reinterpret_cast<int32_t *>(w + A.cand_id), A.cand_stride,
-                     reinterpret_cast<uint32_t *>(w + A.cnt), A.nsub);
-  hipLaunchKernelGGL((resolve_kernel<kMode>), dim3((unsigned)a.nq), dim3(kSelectThreads), 0, s,
-                     reinterpret_cast<const uint32_t *>(w + A.keys), A.n,
-                     reinterpret_cast<const uint32_t *>(w + A.hist), a.q_pos,
-                     kMode == kOutPoolIds ? a.pool_in : nullptr, pool_len, kk,
-                     reinterpret_cast<const uint32_t *>(w + A.cand_key),
-                     reinterpret_cast<const int32_t *>(w + A.cand_id), A.cand_stride,
-                     reinterpret_cast<const uint32_t *>(w + A.cnt), A.nsub, out, out_stride);
+  bool all_direct = true;
+  for (int i = 0; i < nprob; ++i) all_direct = all_direct && P.p[i].direct;
+  if (!all_direct)
+    hipLaunchKernelGGL(filter_kernel, dim3((unsigned)((max_nsub + waves - 1) / waves), (unsigned)a.nq,
+                                         (unsigned)nprob),
+                     dim3(kFilterThreads), 0, s, P, a.q_pos, a.pool_len);
+  hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)a.nq, (unsigned)nprob), dim3(kSelectThreads),
+                     0, s, P, a.q_pos, a.pool_in, a.pool_len);
 }
 
 thread_local hipEvent_t g_scan_before = nullptr;
@@ -608,18 +792,17 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
     else launch_score_mode<4, false>(a, n_cand, pool, reindex_pool, s);
   }
   if (g_scan_after != nullptr) (void)hipEventRecord(g_scan_after, s);
-  // 3. first-pass bins, then selection
-  hipLaunchKernelGGL(bins_kernel, dim3((unsigned)a.nq, pool ? 2u : 1u), dim3(kSelectThreads), 0, s,
-                     reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
-                     pool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr, a.q_pos,
-                     a.pool_len, (int32_t)reindex_pool, a.top_k, a.pool_blocks);
-  if (reindex_pool)
-    launch_select<kOutPoolIds>(a, L.tok, a.top_k, a.topk_out, a.top_k, s);
-  else
-    launch_select<kOutPositions>(a, L.tok, a.top_k, a.topk_out, a.top_k, s);
-  if (pool)
-    launch_select<kOutPoolBlocks>(a, L.blk, a.pool_blocks, a.pool_out,
-                                  (int64_t)a.pool_blocks * kPoolBlock, s);
+  // 3. selection: the Top-K, and the pool blocks in the same launches
+  SelProblems P;
+  P.p[0] = sel_problem(a, L.tok, a.top_k, reindex_pool ? kOutPoolIds : kOutPositions, a.topk_out,
+                       a.top_k);
+  int64_t max_nsub = L.tok.nsub;
+  if (pool) {
+    P.p[1] = sel_problem(a, L.blk, a.pool_blocks, kOutPoolBlocks, a.pool_out,
+                         (int64_t)a.pool_blocks * kPoolBlock);
+    max_nsub = std::max(max_nsub, L.blk.nsub);
+  }
+  launch_select(a, P, pool ? 2 : 1, max_nsub, s);
   return hipGetLastError();
 }
 

@@ -475,7 +475,7 @@ __global__ void __launch_bounds__(kSelectThreads) gemm_resolve_kernel(
     int32_t nranges, int32_t *__restrict__ out) {
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t scratch[kSelectThreads / kWave + 1];
-  __shared__ uint32_t res[2];
+  __shared__ uint32_t res[4];
   __shared__ uint32_t lkey[kResolveCap];
   __shared__ int32_t lid[kResolveCap];
   __shared__ uint32_t goff[kSelectThreads];
@@ -489,9 +489,10 @@ __global__ void __launch_bounds__(kSelectThreads) gemm_resolve_kernel(
   const int64_t nreg = min((int64_t)nranges, (n_vis + sub - 1) / sub);
   uint2 *cq2 = cand + (int64_t)q * cand_stride;
   const uint32_t *cq = cnt + (int64_t)q * nranges;
-  Emit<kOutPositions> emit{out + (int64_t)q * top_k, nullptr, qp};
+  Emit<kOutPositions> emit{out + (int64_t)q * top_k, nullptr, qp, (uint32_t)top_k};
 
-  const uint32_t total = gather_regions(cq, nreg, sub, PairSlots{cq2}, lkey, lid, goff, scratch);
+  const uint32_t total = gather_regions(cq, nreg, sub, PairSlots{cq2}, lkey, lid, goff, scratch,
+                                        first_region_count(cq, nreg));
   const bool in_lds = total <= kResolveCap;
   if (!in_lds) {
     // regions -> one run from slot 0 (a region's destination never passes its source)

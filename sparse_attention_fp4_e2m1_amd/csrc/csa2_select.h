@@ -14,10 +14,7 @@ namespace {
 
 constexpr int kSelectThreads = 1024;
 constexpr int kResolveCap = 8192;          // candidates held in LDS by a resolve
-constexpr int kStateWords = 16;            // per query after its histogram: see SelState
-
-// Selection state of one query and one key array, in the words after its histogram.
-enum SelState { kTicket = 0, kBin = 1, kAbove = 2, kKeff = 3 };
+constexpr int kStateWords = 16;            // spare words after each query's histogram
 
 // ---------------------------------------------------------------------------
 // Selection helpers
@@ -49,14 +46,6 @@ __device__ void select_bin(const uint32_t *bins, int nbins, uint32_t want, uint3
   __syncthreads();
 }
 
-template <int kMode>
-__device__ __forceinline__ int64_t array_len(int32_t qp, int32_t pool_len) {
-  if (kMode == kOutPoolBlocks) return ((int64_t)qp + 1 + kPoolBlock - 1) / kPoolBlock;
-  if (kMode == kOutPoolIds) return pool_len;
-  return (int64_t)qp + 1;
-}
-
-
 // ---------------------------------------------------------------------------
 // Selection proper
 // ---------------------------------------------------------------------------
@@ -78,7 +67,9 @@ struct Emit {
   int32_t *out;          // this query's output row
   const int32_t *pool;   // this query's pool row (kOutPoolIds)
   int32_t qp;
+  uint32_t limit;        // entries in the row (a guard: o < keff <= limit by construction)
   __device__ void operator()(uint32_t o, int64_t id) const {
+    if (o >= limit) return;
     if (kMode == kOutPositions) {
       out[o] = (int32_t)id;
     } else if (kMode == kOutPoolIds) {
@@ -92,16 +83,73 @@ struct Emit {
   }
 };
 
-// Radix passes on bits 19..8 and 7..0 among the keys of bin b1 (above1 keys
-// lie in higher bins), then the ordered compaction.  One 1024-thread block;
-// `hist` has kHistBins words of LDS.
+// Emitter whose output kind (OutMode) is chosen at run time.
+struct EmitAny {
+  int mode;
+  int32_t *out;
+  const int32_t *pool;
+  int32_t qp;
+  uint32_t limit;        // entries (blocks) in the row; o < keff <= limit by construction
+  __device__ void operator()(uint32_t o, int64_t id) const {
+    if (o >= limit) return;
+    if (mode == kOutPositions) {
+      out[o] = (int32_t)id;
+    } else if (mode == kOutPoolIds) {
+      out[o] = pool[id];
+    } else {
+      for (int m = 0; m < kPoolBlock; ++m) {
+        const int64_t p = id * kPoolBlock + m;
+        out[(int64_t)o * kPoolBlock + m] = p <= qp ? (int32_t)p : -1;
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ int64_t sel_len(int mode, int32_t qp, int32_t pool_len) {
+  if (mode == kOutPoolBlocks) return ((int64_t)qp + 1 + kPoolBlock - 1) / kPoolBlock;
+  if (mode == kOutPoolIds) return pool_len;
+  return (int64_t)qp + 1;
+}
+
+// First radix pass of one query from its 12-bit histogram (global): keff =
+// min(kk, keys present), b1 = the bin of the keff-th largest key, above = keys
+// in higher bins.  Key 0 marks an empty pool slot (no score maps there).  The
+// whole block takes part; `lh` holds kHistBins words of LDS.  Contains barriers.
+struct Threshold {
+  uint32_t keff, b1, above;
+};
+
+__device__ Threshold hist_threshold(const uint32_t *__restrict__ hq, int64_t n, int32_t kk,
+                                    uint32_t *lh, uint32_t *scratch, uint32_t *res) {
+  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x)
+    reinterpret_cast<uint4 *>(lh)[i] = reinterpret_cast<const uint4 *>(hq)[i];
+  __syncthreads();
+  Threshold t;
+  t.keff = (uint32_t)max((int64_t)0, min((int64_t)kk, n - (int64_t)lh[0]));
+  t.b1 = 0u;
+  t.above = 0u;
+  if (t.keff > 0) {
+    select_bin(lh, kHistBins, t.keff, scratch, res);
+    t.b1 = res[0];
+    t.above = res[1];
+  }
+  __syncthreads();   // res and lh free again
+  return t;
+}
+
+// The K-th largest key tau and the selection: keys > tau, then the first ties
+// == tau in index order, emitted in index order.  One block; `hist` has
+// kHistBins words of LDS, `res` 4.  tau comes from radix passes on bits 19..8
+// and 7..0 among the keys of bin b1 (above1 keys lie in higher bins).  The
+// ordered compaction takes 4 consecutive keys per thread per tile; when every
+// tie is selected (the usual case) one block scan per tile suffices.
 template <class Src, class E>
 __device__ void select_core(const Src &src, int64_t n, uint32_t keff, uint32_t b1,
                             uint32_t above1, uint32_t *hist, uint32_t *scratch, uint32_t *res,
                             const E &emit) {
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
-  uint32_t tau = 0, c_gt = 0;
+  uint32_t tau = 0, c_gt = 0, n_tau = 0;
   if (keff > 0) {
     uint32_t above = above1;
     for (int i = tid; i < kHistBins; i += nt) hist[i] = 0u;
@@ -124,8 +172,10 @@ __device__ void select_core(const Src &src, int64_t n, uint32_t keff, uint32_t b
     select_bin(hist, 256, keff - above, scratch, res);
     tau = (pre24 << 8) | res[0];
     c_gt = above + res[1];
+    n_tau = hist[res[0]];   // every key equal to tau
   }
   const uint32_t ties_wanted = keff - c_gt;
+  const bool all_ties = ties_wanted == n_tau;
   // ordered compaction, 4 consecutive keys per thread per tile
   uint32_t carry_eq = 0, carry_sel = 0;
   for (int64_t base = 0; base < n && carry_sel < keff; base += 4 * (int64_t)nt) {
@@ -137,26 +187,34 @@ __device__ void select_core(const Src &src, int64_t n, uint32_t keff, uint32_t b
       in4[u] = i0 + u < n;
       k4[u] = in4[u] ? src.key(i0 + u) : 0u;
     }
-    uint32_t neq = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) neq += (in4[u] && k4[u] == tau);
-    uint32_t tot_eq;
-    uint32_t eq_rank = carry_eq + block_exclusive_scan(neq, scratch, tot_eq);
     bool sel[4];
     uint32_t nsel = 0;
+    if (all_ties) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool eq = in4[u] && k4[u] == tau;
-      sel[u] = in4[u] && (k4[u] > tau || (eq && eq_rank < ties_wanted));
-      eq_rank += eq;
-      nsel += sel[u];
+      for (int u = 0; u < 4; ++u) {
+        sel[u] = in4[u] && k4[u] >= tau;
+        nsel += sel[u];
+      }
+    } else {
+      uint32_t neq = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) neq += (in4[u] && k4[u] == tau);
+      uint32_t tot_eq;
+      uint32_t eq_rank = carry_eq + block_exclusive_scan(neq, scratch, tot_eq);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool eq = in4[u] && k4[u] == tau;
+        sel[u] = in4[u] && (k4[u] > tau || (eq && eq_rank < ties_wanted));
+        eq_rank += eq;
+        nsel += sel[u];
+      }
+      carry_eq += tot_eq;
     }
     uint32_t tot_sel;
     uint32_t o = carry_sel + block_exclusive_scan(nsel, scratch, tot_sel);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (sel[u]) emit(o++, src.id(i0 + u));
-    carry_eq += tot_eq;
     carry_sel += tot_sel;
   }
 }
@@ -182,17 +240,24 @@ struct PairSlots {
 // way.  Slot offsets come from a block scan; every thread then finds the
 // region of each slot it copies by binary search over the offsets.  Contains
 // barriers.
+// first_count: this thread's count of the first group (region tid), loaded by
+// the caller early so that its latency overlaps other work.
+__device__ __forceinline__ uint32_t first_region_count(const uint32_t *cq, int64_t nreg) {
+  return (int64_t)threadIdx.x < nreg ? cq[threadIdx.x] : 0u;
+}
+
 template <class Slots>
 __device__ uint32_t gather_regions(const uint32_t *cq, int64_t nreg, int64_t region,
                                    const Slots &slots, uint32_t *lkey, int32_t *lid,
-                                   uint32_t *goff, uint32_t *scratch) {
+                                   uint32_t *goff, uint32_t *scratch, uint32_t first_count) {
   const int tid = threadIdx.x;
   uint32_t carry = 0;
   for (int64_t c0 = 0; c0 < nreg; c0 += kSelectThreads) {
     const int64_t c = c0 + tid;
+    const uint32_t raw = c0 == 0 ? first_count : (c < nreg ? cq[c] : 0u);
     // a region never holds more than `region` slots; the clamp keeps every
     // read inside the query's slots whatever the counts say
-    const uint32_t mine = c < nreg ? (uint32_t)min((int64_t)cq[c], region) : 0u;
+    const uint32_t mine = c < nreg ? (uint32_t)min((int64_t)raw, region) : 0u;
     uint32_t tot;
     const uint32_t off = carry + block_exclusive_scan(mine, scratch, tot);
     goff[tid] = off;
