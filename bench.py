@@ -9,7 +9,10 @@ synthetic tensors (``synth``) resident in HBM before the timed region.
 
 Headline workload: decode_64k_b32 (batch 32, 65536-token contexts, 64 query
 heads on one FP4 KV head, indexer 8x64 E4M3 keys, Top-K 2048).  The 1M-token
-decode (decode_1m) is measured in the same run and reported under "extra".
+decode (decode_1m), the 8-layer Full/Reindex/Reuse chain (chain8_256k_b8) and
+the 4096-query prefill chunk on a 128K cache (prefill_4k_on_128k, index
+product on matrix cores, reported against the fp8 MFMA peak) are measured in
+the same run and reported under "extra".
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-extra]
                     [--no-cpu-baseline] [--graph] [--copy-probe MIB]
@@ -28,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0      # dense E4M3 matrix-core peak of MI355X
 METRIC = "CSA2 decode queries/s and achieved HBM GB/s (% of peak), 64K and 1M context"
 
 
@@ -111,6 +115,13 @@ class WorkloadRun:
         self.stack.run(self.q, self.q_idx, self.q_seq, self.q_pos, append=self.append,
                        scan_events=scan_events)
 
+    def scan_flops(self) -> int:
+        """Multiply-adds x 2 of the first Full layer's index product (every query
+        against every visible position, idx_heads x 64 channels)."""
+        wl = self.wl
+        vis = int((wl.query_pos().astype("int64") + 1).sum())
+        return 2 * vis * wl.idx_heads * wl.idx_dim
+
     # ---- algorithmic bytes (what the method must move; scratch and re-reads excluded)
     def scan_bytes(self) -> int:
         """Index keys streamed by the first Full layer's scoring kernel, plus its queries."""
@@ -125,8 +136,17 @@ class WorkloadRun:
         vis = int((wl.query_pos().astype("int64") + 1).sum())
         total += wl.batch * wl.appended * (wl.dk * 2 + wl.dv * 2 + wl.idx_heads * wl.idx_dim * 2)  # append in
         total += wl.batch * wl.appended * (144 + wl.idx_bytes_per_token())                       # append out
+        # a dense (matrix-core) product reads each sequence's keys once, not once per query
+        seq_vis = {}
+        for b, p in zip(wl.query_seq(), wl.query_pos()):
+            seq_vis[int(b)] = max(seq_vis.get(int(b), 0), int(p) + 1)
+        dense_keys = sum(seq_vis.values()) * wl.idx_bytes_per_token()
         for L in wl.layers:
-            if L.mode == "full":
+            if L.mode == "full" and matrix_core_scan(wl) and L is wl.layers[0]:
+                total += dense_keys
+                total += nq * wl.idx_heads * wl.idx_dim * 2
+                total += nq * wl.top_k * 4
+            elif L.mode == "full":
                 total += vis * wl.idx_bytes_per_token()
                 total += nq * wl.idx_heads * wl.idx_dim * 2
                 total += nq * wl.top_k * 4 + (nq * 8 * L.pool_blocks * 4 if L.pool_blocks else 0)
@@ -140,6 +160,13 @@ class WorkloadRun:
             total += nq * wl.top_k * (144 + 4)                   # selected rows + their indices
             total += nq * wl.heads * (wl.dk * 2 + wl.dv * 4 + 4)  # q in, out + lse out
         return total
+
+
+def matrix_core_scan(wl) -> bool:
+    """The first layer is scored on matrix cores (E4M3 index query and keys, no pool)."""
+    L = wl.layers[0]
+    return (wl.q_idx_dtype == "fp8" and wl.idx_k_dtype == "fp8" and L.mode == "full"
+            and L.pool_blocks == 0)
 
 
 def time_run(run, steps, warmup, hip, use_graph=False):
@@ -212,7 +239,15 @@ def measure(name, steps, warmup, hip, use_graph):
         "algorithmic_bytes_per_step": run.step_bytes(),
         "setup_s": round(run.setup_s, 1),
     }
-    if scan_ms is not None:
+    if scan_ms is not None and matrix_core_scan(wl):
+        # the first product pass of the matrix-core scorer: one dense E4M3 GEMM
+        flops = run.scan_flops()
+        ach = flops / (scan_ms * 1e-3) / 1e12
+        res["roofline"] = {"bound": "mfma", "kernel": "gemm_score_kernel pass 1 (fp8 index product)",
+                           "achieved": ach, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / FP8_PEAK_TFLOPS, "traffic": None,
+                           "flops_per_launch": flops, "avg_launch_ms": scan_ms}
+    elif scan_ms is not None:
         ach = run.scan_bytes() / (scan_ms * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "score_kernel (index scan, first Full layer)",
                            "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -223,9 +258,10 @@ def measure(name, steps, warmup, hip, use_graph):
     return wl, res
 
 
-def cpu_baseline(name, n_sample=4):
+def cpu_baseline(name, n_sample=32):
     """The oracle (as it stands) on a bounded sample of the same step: the first
-    n_sample queries with their full contexts, one step, one thread."""
+    n_sample queries (the whole batch of the headline workload) with their full
+    contexts, one step, one thread."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     import synth
@@ -294,12 +330,20 @@ def main():
         "step_hbm_gbps": res["step_hbm_gbps"], "step_hbm_frac": res["step_hbm_frac"],
         "roofline": res.get("roofline"),
     }
-    if not args.no_extra and args.workload != "decode_1m":
-        print("[bench] decode_1m line item", file=sys.stderr, flush=True)
-        wl2, res2 = measure("decode_1m", args.steps, args.warmup, hip, args.graph)
-        line["extra"] = {"decode_1m": {k: res2[k] for k in
-                                       ("value", "ms_per_step", "step_hbm_gbps", "step_hbm_frac")}
-                         | {"roofline": res2.get("roofline")}}
+    if not args.no_extra:
+        line["extra"] = {}
+        for name in ("decode_1m", "chain8_256k_b8", "prefill_4k_on_128k"):
+            if name == args.workload:
+                continue
+            print(f"[bench] {name} line item", file=sys.stderr, flush=True)
+            # the prefill step is ~2 ms: fewer steps keep its share of the run small
+            steps = args.steps if name != "prefill_4k_on_128k" else max(3, args.steps // 5)
+            wl2, res2 = measure(name, steps, args.warmup, hip, args.graph)
+            line["extra"][name] = {k: res2[k] for k in
+                                   ("value", "ms_per_step", "step_hbm_gbps", "step_hbm_frac")}
+            line["extra"][name]["unit"] = "queries/s"
+            line["extra"][name]["steps"] = steps
+            line["extra"][name]["roofline"] = res2.get("roofline")
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.workload)
