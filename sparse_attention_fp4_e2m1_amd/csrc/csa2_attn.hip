@@ -47,7 +47,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 template <int kByte>
 __device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float s) {
   const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kByte);
-  return (__float_as_uint(v[0] * s) >> 16) | (__float_as_uint(v[1] * s) & 0xFFFF0000u);
+  // high halves of the two products: bytes 2,3 of v[0]*s then bytes 2,3 of v[1]*s
+  return __builtin_amdgcn_perm(__float_as_uint(v[1] * s), __float_as_uint(v[0] * s), 0x07060302u);
 }
 
 // Two E2M1 codes (byte kByte of w) times s (given as an fp16 pair), as fp16:
@@ -71,30 +72,28 @@ struct Gathered {
   uint32_t vs[kItems];
 };
 
+// codes / scales: the query's sequence (row 0); row offsets fit 32 bits.
 template <int kThreads>
 __device__ __forceinline__ void gather(Gathered<kThreads> &gd, const int32_t *rows, int base,
-                                       const uint8_t *__restrict__ kv_codes,
-                                       const uint8_t *__restrict__ kv_scales, int64_t seq_base,
-                                       int tid) {
+                                       const uint8_t *__restrict__ codes,
+                                       const uint8_t *__restrict__ scales, int tid) {
 #pragma unroll
   for (int it = 0; it < Gathered<kThreads>::kItems; ++it) {
     const int item = min(tid + it * kThreads, 4 * 64 - 1);
     {
       const int g = (item & 63) >> 4;
-      const int32_t row = rows[base + 16 * (item >> 6) + (item & 15)];
-      const int64_t slot = seq_base + (row >= 0 ? row : 0);
-      gd.kc[it] = *reinterpret_cast<const uint4 *>(kv_codes + slot * 128 + 16 * g);
-      gd.ks[it] = *reinterpret_cast<const uint16_t *>(kv_scales + slot * 16 + 2 * g);
+      const uint32_t row = (uint32_t)max(rows[base + 16 * (item >> 6) + (item & 15)], 0);
+      gd.kc[it] = *reinterpret_cast<const uint4 *>(codes + row * 128u + 16u * g);
+      gd.ks[it] = *reinterpret_cast<const uint16_t *>(scales + row * 16u + 2u * g);
     }
     {
       const int pr = item & 31, b = item >> 5;
       uint32_t sc = 0u;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int32_t row = rows[base + 2 * pr + h];
-        const int64_t slot = seq_base + (row >= 0 ? row : 0);
-        gd.vc[it][h] = *reinterpret_cast<const uint2 *>(kv_codes + slot * 128 + 64 + 8 * b);
-        sc |= (uint32_t)kv_scales[slot * 16 + 8 + b] << (8 * h);
+        const uint32_t row = (uint32_t)max(rows[base + 2 * pr + h], 0);
+        gd.vc[it][h] = *reinterpret_cast<const uint2 *>(codes + row * 128u + 64u + 8u * b);
+        sc |= (uint32_t)scales[row * 16u + 8u + b] << (8 * h);
       }
       gd.vs[it] = sc;
     }
@@ -143,8 +142,8 @@ __device__ __forceinline__ void dequant(const Gathered<kThreads> &gd, uint4 *kq,
           const uint32_t a = __builtin_bit_cast(uint32_t, ra[e]);
           const uint32_t c = __builtin_bit_cast(uint32_t, rb[e]);
           // channel 8hw + 2e: (row 2pr, row 2pr+1); channel 8hw + 2e + 1 likewise
-          dst[((8 * hw + 2 * e) * kVtPitch) / 2] = (a & 0xFFFFu) | (c << 16);
-          dst[((8 * hw + 2 * e + 1) * kVtPitch) / 2] = (a >> 16) | (c & 0xFFFF0000u);
+          dst[((8 * hw + 2 * e) * kVtPitch) / 2] = __builtin_amdgcn_perm(c, a, 0x05040100u);
+          dst[((8 * hw + 2 * e + 1) * kVtPitch) / 2] = __builtin_amdgcn_perm(c, a, 0x07060302u);
         }
       }
     }
@@ -185,25 +184,32 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
   mc = fmaxf(mc, shfl_xor_f(mc, 16));
   mc = fmaxf(mc, shfl_xor_f(mc, 32));
   const float m_new = fmaxf(m_run, mc);
-  const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+  // exp2 straight on the hardware instruction: arguments are <= 0 and the
+  // results go to fp16, so results below the fp32 normal range do not matter
+  const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
   _Float16 p16[16];
-  float lsum = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const float p = (m_new == -INFINITY) ? 0.0f : exp2f(z[k] - m_new);
-    p16[k] = (_Float16)p;
-    lsum += (float)p16[k];
-  }
+  for (int k = 0; k < 16; ++k)
+    p16[k] = (_Float16)((m_new == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[k] - m_new));
+  // the normalizer sums the fp16 weights the PV product uses
+  float lsum = 0.0f;
+  typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 h2;
+  const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int k = 0; k < 16; k += 2) lsum = __builtin_amdgcn_fdot2(h2{p16[k], p16[k + 1]}, one2, lsum, false);
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
   l_run = l_run * alpha + lsum;
   m_run = m_new;
-  // O rows are heads 16*wave + 4g + i: fetch their alpha from lane 4g + i
+  // O rows are heads 16*wave + 4g + i: fetch their alpha from lane 4g + i.
+  // Once the running maxima settle, alpha is 1 everywhere and O is left alone.
+  if (__ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = __shfl(alpha, 4 * g + i, 64);
+    for (int i = 0; i < 4; ++i) {
+      const float a = __shfl(alpha, 4 * g + i, 64);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt][i] *= a;
+      for (int dt = 0; dt < 8; ++dt) o[dt][i] *= a;
+    }
   }
 
   // O += P V: k-slice sg covers tiles 2sg, 2sg+1; lane group g holds rows
@@ -254,6 +260,8 @@ __global__ void __launch_bounds__(kWaves * 64) attn_partial_kernel(
   const int g = lane >> 4;
   const int l16 = lane & 15;
   const int64_t seq_base = (int64_t)q_seq[q] * capacity;
+  const uint8_t *codes = kv_codes + seq_base * 128;
+  const uint8_t *scales = kv_scales + seq_base * 16;
   const int row0 = split * rows_per_split;
   const int nrows = min(rows_per_split, top_k - row0);
   const int nsub = (nrows + kSub - 1) / kSub;
@@ -283,17 +291,17 @@ __global__ void __launch_bounds__(kWaves * 64) attn_partial_kernel(
   // copy between sets, so the compiler waits only for the set being
   // dequantized.  (Deeper register rings measured slower: code size.)
   Gathered<kThreads> ga, gb;
-  gather(ga, rows, 0, kv_codes, kv_scales, seq_base, tid);
+  gather(ga, rows, 0, codes, scales, tid);
   dequant(ga, kq[0], vt[0], tid);
-  gather(gb, rows, kSub, kv_codes, kv_scales, seq_base, tid);
+  gather(gb, rows, kSub, codes, scales, tid);
   for (int c = 0; c < nsub; c += 2) {
     __syncthreads();
-    gather(ga, rows, (c + 2) * kSub, kv_codes, kv_scales, seq_base, tid);
+    gather(ga, rows, (c + 2) * kSub, codes, scales, tid);
     attend_sub(kq[0], vt[0], rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
     dequant(gb, kq[1], vt[1], tid);
     if (c + 1 >= nsub) break;
     __syncthreads();
-    gather(gb, rows, (c + 3) * kSub, kv_codes, kv_scales, seq_base, tid);
+    gather(gb, rows, (c + 3) * kSub, codes, scales, tid);
     attend_sub(kq[1], vt[1], rows, (c + 1) * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
     dequant(ga, kq[0], vt[0], tid);
   }
