@@ -41,15 +41,24 @@ typedef float v4f __attribute__((__vector_size__(4 * sizeof(float))));
 constexpr int kGemmThreads = 512;       // 8 waves, two per SIMD
 constexpr int kGemmWaves = kGemmThreads / kWave;
 constexpr int kGemmQ = 512;             // queries per workgroup: 64 per wave, 4 column tiles of 16
-#ifndef CSA2_GEMM_STAGE
-#define CSA2_GEMM_STAGE 64
+// Positions per LDS stage (16-row tiles): the lighter block-maximum pass takes
+// longer stages (fewer barriers); the emitting pass needs the registers.
+#ifndef CSA2_GEMM_STAGE1
+#define CSA2_GEMM_STAGE1 128
 #endif
-constexpr int kGemmStage = CSA2_GEMM_STAGE;   // positions per LDS stage (16-row tiles)
+#ifndef CSA2_GEMM_STAGE2
+#define CSA2_GEMM_STAGE2 64
+#endif
 constexpr int kGemmTargetGroups = 256;  // workgroups aimed for (one per CU)
 constexpr int kBlk = 16;                // positions per block maximum (one row tile)
 constexpr int kBlkGroup = 16;           // block maxima a lane collects before one 32-B store
 constexpr int kRangeAlign = kBlk * kBlkGroup;   // positions per range: a multiple of this
 constexpr int kKthThreads = 256;
+// Candidates a gemm_resolve_kernel keeps in LDS: ~K(1 + a few %) with continuous
+// scores; the smaller footprint fits three workgroups per CU (thousands of
+// queries per call).
+constexpr int kGemmResolveCap = 4096;
+constexpr int kGemmResolveThreads = 256;
 constexpr int kKthLdsMax = 32768;       // block maxima a gemm_kth_kernel keeps in LDS
 
 __device__ __forceinline__ uint32_t e4m3_code(float f) {
@@ -118,6 +127,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const uint32_t *__restrict__ plan, uint16_t *__restrict__ bmax, int64_t bmax_row,
     const uint32_t *__restrict__ thr, uint2 *__restrict__ cand, int64_t cand_stride,
     uint32_t *__restrict__ cnt, int32_t nranges) {
+  constexpr int kGemmStage = kPass == 1 ? CSA2_GEMM_STAGE1 : CSA2_GEMM_STAGE2;
   constexpr int kPB = H * 64;                          // key bytes per position
   constexpr int kSteps = kPB / 128;                    // MFMA k-steps
   constexpr int kTileBytes = kBlk * kPB;               // one 16-row tile
@@ -467,18 +477,18 @@ __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
 // Per query: the exact Top-K among the candidates of its slot regions.  The
 // first radix bin comes from the candidates themselves: every key above the
 // K-th largest is a candidate, so the candidates' histogram above that bin is
-// the full one.  Beyond kResolveCap candidates (ties, or few blocks) the
+// the full one.  Beyond kGemmResolveCap candidates (ties, or few blocks) the
 // regions are compacted in place in global memory and streamed.
-__global__ void __launch_bounds__(kSelectThreads) gemm_resolve_kernel(
+__global__ void __launch_bounds__(kGemmResolveThreads) gemm_resolve_kernel(
     const int32_t *__restrict__ q_pos, int32_t top_k, const uint32_t *__restrict__ plan,
     uint2 *__restrict__ cand, int64_t cand_stride, const uint32_t *__restrict__ cnt,
     int32_t nranges, int32_t *__restrict__ out) {
   __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t scratch[kSelectThreads / kWave + 1];
+  __shared__ uint32_t scratch[kGemmResolveThreads / kWave + 1];
   __shared__ uint32_t res[4];
-  __shared__ uint32_t lkey[kResolveCap];
-  __shared__ int32_t lid[kResolveCap];
-  __shared__ uint32_t goff[kSelectThreads];
+  __shared__ uint32_t lkey[kGemmResolveCap];
+  __shared__ int32_t lid[kGemmResolveCap];
+  __shared__ uint32_t goff[kGemmResolveThreads];
 
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
@@ -491,15 +501,15 @@ __global__ void __launch_bounds__(kSelectThreads) gemm_resolve_kernel(
   const uint32_t *cq = cnt + (int64_t)q * nranges;
   Emit<kOutPositions> emit{out + (int64_t)q * top_k, nullptr, qp, (uint32_t)top_k};
 
-  const uint32_t total = gather_regions(cq, nreg, sub, PairSlots{cq2}, lkey, lid, goff, scratch,
-                                        first_region_count(cq, nreg));
-  const bool in_lds = total <= kResolveCap;
+  const uint32_t total = gather_regions<kGemmResolveCap, kGemmResolveThreads>(
+      cq, nreg, sub, PairSlots{cq2}, lkey, lid, goff, scratch, first_region_count(cq, nreg));
+  const bool in_lds = total <= kGemmResolveCap;
   if (!in_lds) {
     // regions -> one run from slot 0 (a region's destination never passes its source)
     uint32_t dst = 0;
     for (int64_t r = 0; r < nreg; ++r) {
       const uint32_t c = (uint32_t)min((int64_t)cq[r], sub);
-      for (uint32_t b = 0; b < c; b += kSelectThreads) {
+      for (uint32_t b = 0; b < c; b += kGemmResolveThreads) {
         const uint32_t i = b + tid;
         uint2 kv = make_uint2(0u, 0u);
         if (i < c) kv = cq2[r * sub + i];
@@ -510,9 +520,9 @@ __global__ void __launch_bounds__(kSelectThreads) gemm_resolve_kernel(
       dst += c;
     }
   }
-  for (int i = tid; i < kHistBins; i += kSelectThreads) hist[i] = 0u;
+  for (int i = tid; i < kHistBins; i += kGemmResolveThreads) hist[i] = 0u;
   __syncthreads();
-  for (uint32_t i = tid; i < total; i += kSelectThreads)
+  for (uint32_t i = tid; i < total; i += kGemmResolveThreads)
     atomicAdd(&hist[(in_lds ? lkey[i] : cq2[i].x) >> 20], 1u);
   __syncthreads();
   uint32_t b1 = 0, above1 = 0;
@@ -526,7 +536,7 @@ __global__ void __launch_bounds__(kSelectThreads) gemm_resolve_kernel(
   else
     select_core(PairSlots{cq2}, (int64_t)total, keff, b1, above1, hist, scratch, res, emit);
   int32_t *oq = out + (int64_t)q * top_k;
-  for (int64_t i = (int64_t)keff + tid; i < top_k; i += kSelectThreads) oq[i] = -1;
+  for (int64_t i = (int64_t)keff + tid; i < top_k; i += kGemmResolveThreads) oq[i] = -1;
 }
 
 // Position ranges per query group: enough workgroups for the chip, a multiple
@@ -609,7 +619,7 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
                      reinterpret_cast<uint32_t *>(w + L.thr));
   if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 2, s);
   else launch_gemm_scores<4>(a, L, 2, s);
-  hipLaunchKernelGGL(gemm_resolve_kernel, dim3((unsigned)a.nq), dim3(kSelectThreads), 0, s,
+  hipLaunchKernelGGL(gemm_resolve_kernel, dim3((unsigned)a.nq), dim3(kGemmResolveThreads), 0, s,
                      a.q_pos, a.top_k, reinterpret_cast<const uint32_t *>(w + L.plan),
                      reinterpret_cast<uint2 *>(w + L.cand), L.cand_stride,
                      reinterpret_cast<const uint32_t *>(w + L.cnt), L.nranges, a.topk_out);

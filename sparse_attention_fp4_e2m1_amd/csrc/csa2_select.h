@@ -236,7 +236,7 @@ struct PairSlots {
 
 // Copies one query's candidates, held in `nreg` slot regions of `region`
 // entries each (counts in cq, region r at slots r * region of `slots`), into
-// LDS in region order when they fit (<= kResolveCap); returns the total either
+// LDS in region order when they fit (<= kCap); returns the total either
 // way.  Slot offsets come from a block scan; every thread then finds the
 // region of each slot it copies by binary search over the offsets.  Contains
 // barriers.
@@ -246,13 +246,13 @@ __device__ __forceinline__ uint32_t first_region_count(const uint32_t *cq, int64
   return (int64_t)threadIdx.x < nreg ? cq[threadIdx.x] : 0u;
 }
 
-template <class Slots>
+template <int kCap = kResolveCap, int kThreads = kSelectThreads, class Slots>
 __device__ uint32_t gather_regions(const uint32_t *cq, int64_t nreg, int64_t region,
                                    const Slots &slots, uint32_t *lkey, int32_t *lid,
                                    uint32_t *goff, uint32_t *scratch, uint32_t first_count) {
   const int tid = threadIdx.x;
   uint32_t carry = 0;
-  for (int64_t c0 = 0; c0 < nreg; c0 += kSelectThreads) {
+  for (int64_t c0 = 0; c0 < nreg; c0 += kThreads) {
     const int64_t c = c0 + tid;
     const uint32_t raw = c0 == 0 ? first_count : (c < nreg ? cq[c] : 0u);
     // a region never holds more than `region` slots; the clamp keeps every
@@ -262,9 +262,9 @@ __device__ uint32_t gather_regions(const uint32_t *cq, int64_t nreg, int64_t reg
     const uint32_t off = carry + block_exclusive_scan(mine, scratch, tot);
     goff[tid] = off;
     __syncthreads();
-    if (carry + tot <= kResolveCap) {
-      const int group = (int)min((int64_t)kSelectThreads, nreg - c0);
-      for (uint32_t j = carry + tid; j < carry + tot; j += kSelectThreads) {
+    if (carry + tot <= kCap) {
+      const int group = (int)min((int64_t)kThreads, nreg - c0);
+      for (uint32_t j = carry + tid; j < carry + tot; j += kThreads) {
         int lo = 0, hi = group - 1;           // last region with goff <= j
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
