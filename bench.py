@@ -72,6 +72,9 @@ class Hip:
     def destroy(self, e):
         self.lib.hipEventDestroy(e)
 
+    def record(self, e, stream: int):
+        assert self.lib.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
+
 
 class WorkloadRun:
     """Cache filled with every row but the step's own, inputs resident on the GPU."""
@@ -188,22 +191,31 @@ def time_run(run, steps, warmup, hip, use_graph=False):
         for _ in range(warmup):
             graph.replay()
         torch.cuda.synchronize()
+    # one event at every step boundary: per-step times for the percentiles
+    bounds = [hip.event() for _ in range(steps + 1)]
+    stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    hip.record(bounds[0], stream)
     for i in range(steps):
         if graph is not None:
             graph.replay()
         else:
             run.step(scan_events=evs[i])
+        hip.record(bounds[i + 1], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     scan_ms = None
     if graph is None:
         scan_ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / steps
+    per_step = sorted(hip.elapsed_ms(bounds[i], bounds[i + 1]) for i in range(steps))
+    pct = {f"p{p}": per_step[min(steps - 1, (p * steps) // 100)] for p in (10, 50, 90)}
     for a, b in evs:
         hip.destroy(a)
         hip.destroy(b)
-    return (t1 - t0), scan_ms
+    for e in bounds:
+        hip.destroy(e)
+    return (t1 - t0), scan_ms, pct
 
 
 def score_kernel_sha() -> str:
@@ -229,12 +241,12 @@ def measure(name, steps, warmup, hip, use_graph):
     wl = synth.workload(name)
     dev = torch.device("cuda:0")
     run = WorkloadRun(wl, dev)
-    elapsed, scan_ms = time_run(run, steps, warmup, hip, use_graph)
+    elapsed, scan_ms, pct = time_run(run, steps, warmup, hip, use_graph)
     ms = elapsed * 1e3 / steps
     qps = wl.nq * steps / elapsed
     step_gbps = run.step_bytes() / (elapsed / steps) / 1e9
     res = {
-        "value": qps, "ms_per_step": ms,
+        "value": qps, "ms_per_step": ms, "step_ms_percentiles": pct,
         "step_hbm_gbps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": run.step_bytes(),
         "setup_s": round(run.setup_s, 1),
@@ -321,6 +333,7 @@ def main():
     line = {
         "metric": METRIC, "value": res["value"], "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "step_ms_percentiles": res["step_ms_percentiles"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
         "data": "synthetic (seeded numpy draws, shapes of the workload)",
         "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context,
@@ -340,7 +353,8 @@ def main():
             steps = args.steps if name != "prefill_4k_on_128k" else max(3, args.steps // 5)
             wl2, res2 = measure(name, steps, args.warmup, hip, args.graph)
             line["extra"][name] = {k: res2[k] for k in
-                                   ("value", "ms_per_step", "step_hbm_gbps", "step_hbm_frac")}
+                                   ("value", "ms_per_step", "step_ms_percentiles",
+                                    "step_hbm_gbps", "step_hbm_frac")}
             line["extra"][name]["unit"] = "queries/s"
             line["extra"][name]["steps"] = steps
             line["extra"][name]["roofline"] = res2.get("roofline")

@@ -35,9 +35,17 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source extra flags.  The attention kernel keeps its matrix-core
+# accumulators in ordinary VGPRs (gfx950 allows either file): with them in
+# AGPRs the compiler copies the output tile between the files around every
+# online-softmax update.
+EXTRA_FLAGS = {"csa2_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)

@@ -11,12 +11,15 @@
 // one wave per 16 query heads; the split is walked in sub-chunks of 64 rows
 // with an online softmax.
 //   * The workgroup gathers a sub-chunk's codes one sub-chunk ahead and
-//     dequantizes them once into LDS, shared by every head wave: K^ in bf16 as
+//     dequantizes them once into LDS, shared by every head wave: K^ in fp16 as
 //     MFMA A fragments (the contraction index permuted, k-slice s and lane
 //     group g <-> channels 32g + 8s .. +7, identically for Q), V^ in fp16
 //     transposed [channel][row].  E2M1 codes go through the hardware FP4
-//     conversion; every value is exact.
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (fp32 accumulation); exp2-based
+//     conversion; every value is exact (E2M1 times E4M3 has at most 6
+//     significant bits and lies in [2^-10, 2688]).
+//   * Q is rounded once to fp16 (exact for bf16 values of magnitude 2^-14 to
+//     65504; smaller ones move by less than 2^-25).
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_f16 (fp32 accumulation); exp2-based
 //     softmax statistics per head; P rounded to fp16; O += P V with
 //     v_mfma_f32_16x16x32_f16.
 // attn_combine_kernel: merges the splits of each (query, head).
@@ -34,22 +37,10 @@ constexpr int kTargetGroups = 256;            // workgroups aimed for (one per C
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-
-// Two E2M1 codes (byte kByte of w) -> their values times s, as a bf16 pair.
-// The hardware conversion applies only the exponent of its scale, so it runs
-// with scale 1 and the E4M3 scale multiplies in fp32: every product has at
-// most 6 significant bits, so it is exact in fp32 and its bf16 truncation.
-template <int kByte>
-__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float s) {
-  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, kByte);
-  // high halves of the two products: bytes 2,3 of v[0]*s then bytes 2,3 of v[1]*s
-  return __builtin_amdgcn_perm(__float_as_uint(v[1] * s), __float_as_uint(v[0] * s), 0x07060302u);
-}
 
 // Two E2M1 codes (byte kByte of w) times s (given as an fp16 pair), as fp16:
 // E2M1 and E4M3 values and their products are exact in fp16.
@@ -111,21 +102,25 @@ __device__ __forceinline__ void dequant(const Gathered<kThreads> &gd, uint4 *kq,
     const int item = tid + it * kThreads;
     if (Gathered<kThreads>::kItems * kThreads > 4 * 64 && item >= 4 * 64) break;
     {
-      const float s0 = e4m3_to_f32(gd.ks[it] & 0xFFu);
-      const float s1 = e4m3_to_f32((gd.ks[it] >> 8) & 0xFFu);
+      // E4M3 scales of the two 16-channel blocks, by the hardware OCP E4M3
+      // conversion (exact in fp16)
+      const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gd.ks[it], 1.0f, false);
+      const _Float16 s0 = s01[0], s1 = s01[1];
       const uint32_t w[4] = {gd.kc[it].x, gd.kc[it].y, gd.kc[it].z, gd.kc[it].w};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const float sc = s < 2 ? s0 : s1;
+        const f16x2 sc = s < 2 ? f16x2{s0, s0} : f16x2{s1, s1};
         kq[((item >> 6) * 4 + s) * 64 + (item & 63)] =
-            make_uint4(fp4x2_bf16<0>(w[s], sc), fp4x2_bf16<1>(w[s], sc),
-                       fp4x2_bf16<2>(w[s], sc), fp4x2_bf16<3>(w[s], sc));
+            make_uint4(__builtin_bit_cast(uint32_t, fp4x2_f16<0>(w[s], sc)),
+                       __builtin_bit_cast(uint32_t, fp4x2_f16<1>(w[s], sc)),
+                       __builtin_bit_cast(uint32_t, fp4x2_f16<2>(w[s], sc)),
+                       __builtin_bit_cast(uint32_t, fp4x2_f16<3>(w[s], sc)));
       }
     }
     {
       const int pr = item & 31, b = item >> 5;
-      const _Float16 sa = (_Float16)e4m3_to_f32(gd.vs[it] & 0xFFu);
-      const _Float16 sb = (_Float16)e4m3_to_f32((gd.vs[it] >> 8) & 0xFFu);
+      const f16x2 sab = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gd.vs[it], 1.0f, false);
+      const _Float16 sa = sab[0], sb = sab[1];
       const f16x2 s2a = {sa, sa}, s2b = {sb, sb};
       uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + 2 * pr);
 #pragma unroll
@@ -151,9 +146,11 @@ __device__ __forceinline__ void dequant(const Gathered<kThreads> &gd, uint4 *kq,
 }
 
 // One sub-chunk of 64 rows from LDS: S^T on matrix cores, online softmax,
-// O += P V.
+// O += P V.  scale_log2 = |softmax scale| * log2(e) (a negative scale was
+// folded into Q), so the running maximum of the scaled scores is the scaled
+// maximum of the raw ones.
 __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf,
-                                           const int32_t *rows, int base, const bf16x8 (&qf)[4],
+                                           const int32_t *rows, int base, const f16x8 (&qf)[4],
                                            float scale_log2, int g, int l16, int lane,
                                            float &m_run, float &l_run, f32x4 (&o)[8]) {
   // S^T tiles: rows base + 16t + 4g + i, head l16
@@ -163,40 +160,67 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, kq[(t * 4 + s) * 64 + lane]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+      const f16x8 kf = __builtin_bit_cast(f16x8, kq[(t * 4 + s) * 64 + lane]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[s], acc, 0, 0, 0);
     }
     st[t] = acc;
   }
 
-  // online softmax for head 16*wave + l16
-  float z[16];
+  // online softmax for head 16*wave + l16; rows marked -1 (bit set in `bad`)
+  // take no weight
+  const uint64_t bad = __ballot(rows[base + lane] < 0);
+  // this lane's rows: bit 4t + i <-> row 16t + 4g + i
+  uint32_t mine = 0u;
   float mc = -INFINITY;
+  if (bad != 0ull) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) mine |= ((uint32_t)(bad >> (16 * t + 4 * g)) & 0xFu) << (4 * t);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[t][i] = ((mine >> (4 * t + i)) & 1u) ? -INFINITY : st[t][i];
+  }
+  // max as med3(x, y, +inf): no NaN canonicalization of the matrix-core
+  // results (none is NaN: -1 rows hold -inf)
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = rows[base + 16 * t + 4 * g + i] >= 0;
-      const float v = ok ? st[t][i] * scale_log2 : -INFINITY;
-      z[4 * t + i] = v;
-      mc = fmaxf(mc, v);
-    }
+    for (int i = 0; i < 4; ++i) mc = __builtin_amdgcn_fmed3f(mc, st[t][i], INFINITY);
   mc = fmaxf(mc, shfl_xor_f(mc, 16));
   mc = fmaxf(mc, shfl_xor_f(mc, 32));
-  const float m_new = fmaxf(m_run, mc);
+  // (fmaxf drops the NaN of -inf * 0 for a zero scale)
+  const float m_new = fmaxf(m_run, mc * scale_log2);
   // exp2 straight on the hardware instruction: arguments are <= 0 and the
   // results go to fp16, so results below the fp32 normal range do not matter
   const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-  _Float16 p16[16];
+  f16x2 p2[8];
+  if (bad == 0ull) {
+    // every row valid: m_new is finite
 #pragma unroll
-  for (int k = 0; k < 16; ++k)
-    p16[k] = (_Float16)((m_new == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[k] - m_new));
+    for (int k = 0; k < 8; ++k) {
+      const int t = k >> 1, i = 2 * (k & 1);
+      const f32x2 e = {__builtin_amdgcn_exp2f(fmaf(st[t][i], scale_log2, -m_new)),
+                       __builtin_amdgcn_exp2f(fmaf(st[t][i + 1], scale_log2, -m_new))};
+      p2[k] = __builtin_convertvector(e, f16x2);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = k >> 1, i = 2 * (k & 1);
+      f32x2 e = {__builtin_amdgcn_exp2f(fmaf(st[t][i], scale_log2, -m_new)),
+                 __builtin_amdgcn_exp2f(fmaf(st[t][i + 1], scale_log2, -m_new))};
+      // no weight when nothing is visible yet, or for a -1 row (also with a
+      // zero scale, where the exponent is NaN)
+      e[0] = (m_new == -INFINITY || ((mine >> (4 * t + i)) & 1u)) ? 0.0f : e[0];
+      e[1] = (m_new == -INFINITY || ((mine >> (4 * t + i + 1)) & 1u)) ? 0.0f : e[1];
+      p2[k] = __builtin_convertvector(e, f16x2);
+    }
+  }
   // the normalizer sums the fp16 weights the PV product uses
   float lsum = 0.0f;
-  typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 h2;
-  const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-  for (int k = 0; k < 16; k += 2) lsum = __builtin_amdgcn_fdot2(h2{p16[k], p16[k + 1]}, one2, lsum, false);
+  for (int k = 0; k < 8; ++k) lsum = __builtin_amdgcn_fdot2(p2[k], one2, lsum, false);
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
   l_run = l_run * alpha + lsum;
@@ -216,12 +240,11 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
   // 32sg + 4g + 0..3 and 32sg + 16 + 4g + 0..3
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg) {
-    f16x8 pa;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pa[i] = p16[4 * (2 * sg) + i];
-      pa[4 + i] = p16[4 * (2 * sg + 1) + i];
-    }
+    const f16x8 pa = __builtin_bit_cast(
+        f16x8, make_uint4(__builtin_bit_cast(uint32_t, p2[4 * sg]),
+                          __builtin_bit_cast(uint32_t, p2[4 * sg + 1]),
+                          __builtin_bit_cast(uint32_t, p2[4 * sg + 2]),
+                          __builtin_bit_cast(uint32_t, p2[4 * sg + 3])));
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const _Float16 *vrow = vbuf + (dt * 16 + l16) * kVtPitch + 32 * sg + 4 * g;
@@ -234,23 +257,25 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
 }
 
 // One workgroup per (query, split of the selected rows), one wave per 16
-// heads.  Per sub-chunk of 64 rows the workgroup gathers the codes (one
-// sub-chunk ahead, in registers), dequantizes K^ and V^ once into LDS
-// (double buffered) and every wave runs its heads over them.  With a single
-// split the results are final (normalized output and lse); otherwise partial
-// (O, max, sum) per split go to attn_combine_kernel.
+// heads.  Per sub-chunk of 64 rows the workgroup gathers the codes (two
+// sub-chunks ahead, in registers), dequantizes K^ and V^ once into LDS and
+// every wave runs its heads over them.  One LDS stage (42 KB per workgroup)
+// and at most 168 VGPRs let three workgroups share a CU, which hides the
+// dequantization and softmax phases of one behind the others'.  With a
+// single split the results are final (normalized output and lse); otherwise
+// partial (O, max, sum) per split go to attn_combine_kernel.
 template <int kWaves>
-__global__ void __launch_bounds__(kWaves * 64) attn_partial_kernel(
+__global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial_kernel(
     const uint8_t *__restrict__ kv_codes, const uint8_t *__restrict__ kv_scales,
     int64_t capacity, const uint16_t *__restrict__ qg, int32_t n_heads,
     const int32_t *__restrict__ q_seq, const int32_t *__restrict__ topk, int32_t top_k,
-    int32_t rows_per_split, float scale_log2, float *__restrict__ part_acc,
+    int32_t rows_per_split, float scale_log2, bool q_negate, float *__restrict__ part_acc,
     float2 *__restrict__ part_ml, int32_t splits, float *__restrict__ out,
     float *__restrict__ lse) {
   constexpr int kThreads = kWaves * 64;
   __shared__ int32_t rows[kMaxRowsPerSplit + 2 * kSub];
-  __shared__ uint4 kq[2][4 * 4 * 64];
-  __shared__ _Float16 vt[2][128 * kVtPitch];
+  __shared__ uint4 kq[4 * 4 * 64];
+  __shared__ _Float16 vt[128 * kVtPitch];
 
   const int split = blockIdx.x;
   const int q = blockIdx.y;
@@ -269,12 +294,24 @@ __global__ void __launch_bounds__(kWaves * 64) attn_partial_kernel(
   for (int r = tid; r < (nsub + 2) * kSub; r += kThreads)
     rows[r] = r < nrows ? topk[(int64_t)q * top_k + row0 + r] : -1;
 
-  // Q fragment (B operand): head 16*wave + l16, channels 32g..32g+31
-  bf16x8 qf[4];
+  // Q fragment (B operand): head 16*wave + l16, channels 32g..32g+31, in fp16,
+  // negated when the softmax scale is negative
+  f16x8 qf[4];
   {
     const uint16_t *qp = qg + ((int64_t)q * n_heads + wave * 16 + l16) * 128 + 32 * g;
+    const uint32_t flip = q_negate ? 0x80008000u : 0u;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + 8 * s));
+    for (int s = 0; s < 4; ++s) {
+      const uint4 raw = *reinterpret_cast<const uint4 *>(qp + 8 * s);
+      const uint32_t w[4] = {raw.x ^ flip, raw.y ^ flip, raw.z ^ flip, raw.w ^ flip};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 h = __builtin_convertvector(
+            (f32x2{__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xFFFF0000u)}), f16x2);
+        qf[s][2 * e] = h[0];
+        qf[s][2 * e + 1] = h[1];
+      }
+    }
   }
   __syncthreads();
 
@@ -284,26 +321,25 @@ __global__ void __launch_bounds__(kWaves * 64) attn_partial_kernel(
   float m_run = -INFINITY;   // for head 16*wave + l16 (same in all four lane groups)
   float l_run = 0.0f;
 
-  // sub-chunk c lives in LDS stage c & 1; its codes were gathered during c - 1
-  // Sub-chunk c lives in LDS stage c & 1; its codes are gathered one
-  // sub-chunk ahead, into register set c & 1 (the loop is unrolled by two so
-  // that each set is a fixed register array): no branch around a gather and no
-  // copy between sets, so the compiler waits only for the set being
-  // dequantized.  (Deeper register rings measured slower: code size.)
+  // The codes of sub-chunk c are gathered two sub-chunks ahead, into register
+  // set c & 1 (the loop is unrolled by two so that each set is a fixed
+  // register array): no branch around a gather and no copy between sets, so
+  // the compiler waits only for the set being dequantized.
   Gathered<kThreads> ga, gb;
   gather(ga, rows, 0, codes, scales, tid);
-  dequant(ga, kq[0], vt[0], tid);
   gather(gb, rows, kSub, codes, scales, tid);
   for (int c = 0; c < nsub; c += 2) {
-    __syncthreads();
+    __syncthreads();   // the previous sub-chunk's readers are done with the stage
+    dequant(ga, kq, vt, tid);
     gather(ga, rows, (c + 2) * kSub, codes, scales, tid);
-    attend_sub(kq[0], vt[0], rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
-    dequant(gb, kq[1], vt[1], tid);
+    __syncthreads();
+    attend_sub(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
     if (c + 1 >= nsub) break;
     __syncthreads();
+    dequant(gb, kq, vt, tid);
     gather(gb, rows, (c + 3) * kSub, codes, scales, tid);
-    attend_sub(kq[1], vt[1], rows, (c + 1) * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
-    dequant(ga, kq[0], vt[0], tid);
+    __syncthreads();
+    attend_sub(kq, vt, rows, (c + 1) * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
   }
 
   // O rows = heads 16*wave + 4g + i, column d = 16 dt + l16
@@ -428,15 +464,16 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
                               uint8_t *ws, const AttnWorkspace &L, hipStream_t s) {
   float *acc = reinterpret_cast<float *>(ws + L.part_acc);
   float2 *ml = reinterpret_cast<float2 *>(ws + L.part_ml);
-  const float scale_log2 = softmax_scale * kLog2e;
+  const float scale_log2 = fabsf(softmax_scale) * kLog2e;
+  const bool q_negate = softmax_scale < 0.0f;
   const int32_t rps = rows_per_split(nq, top_k);
   dim3 grid((unsigned)L.splits, (unsigned)nq);
   const int waves = n_heads / 16;
 #define CSA2_ATTN_CASE(W)                                                                        \
   case W:                                                                                        \
     hipLaunchKernelGGL(attn_partial_kernel<W>, grid, dim3(W * 64), 0, s, c.kv_codes, c.kv_scales, \
-                       (int64_t)c.capacity, q, n_heads, q_seq, topk, top_k, rps, scale_log2, acc, \
-                       ml, L.splits, out, lse);                                                  \
+                       (int64_t)c.capacity, q, n_heads, q_seq, topk, top_k, rps, scale_log2,    \
+                       q_negate, acc, ml, L.splits, out, lse);                                   \
     break;
   switch (waves) {
     CSA2_ATTN_CASE(1)

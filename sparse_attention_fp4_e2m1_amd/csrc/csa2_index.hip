@@ -49,6 +49,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kFilterThreads = 256;
 constexpr int kFilterSub = 1024;           // keys per filter wave (one candidate slot region)
 constexpr int64_t kDirectMax = 32768;      // up to this many keys the resolve filters them itself
+constexpr int kEarlySlots = 8;             // candidate slots per resolve thread read before the counts
 
 #ifndef CSA2_SCORE_UNROLL
 #define CSA2_SCORE_UNROLL 4            // 16-B loads per lane per prefetch batch
@@ -548,7 +549,9 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
 // grid (nq, problems).  Per query: b1 from the histogram, the candidates of
 // the filter's regions in index order into LDS, the radix passes and the
 // ordered compaction; with more candidates than LDS holds (heavy ties) it
-// streams the full key array instead.  Then the -1 padding.
+// streams the full key array instead.  Then the -1 padding.  The first slots
+// of every region are read together with the histogram and the region counts,
+// before the counts say how many of them hold candidates.
 __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     const SelProblems P, const int32_t *__restrict__ q_pos, const int32_t *__restrict__ pool_in,
     int32_t pool_len) {
@@ -584,6 +587,10 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
   const int64_t nsub = (n + kFilterSub - 1) / kFilterSub;
   const uint32_t *cq = A.cnt + (int64_t)q * A.nsub;
   const uint32_t first_count = A.direct ? 0u : first_region_count(cq, nsub);
+  const SplitSlots slots{A.cand_key + (int64_t)q * A.cand_stride,
+                         A.cand_id + (int64_t)q * A.cand_stride};
+  const EarlySlots<kEarlySlots> early =
+      early_slots<kEarlySlots, kSelectThreads>(!A.direct, slots, nsub, kFilterSub);
   const Threshold th =
       hist_threshold(A.hist + (int64_t)q * (kHistBins + kStateWords), n, A.kk, hist, scratch, res);
   const EmitAny emit{A.mode, A.out + (int64_t)q * A.out_stride,
@@ -618,11 +625,11 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
       carry += tot;
     }
     __syncthreads();
+  } else if (early.on) {
+    carry = gather_regions_early<kResolveCap, kSelectThreads>(nsub, kFilterSub, slots, early, lkey,
+                                                              lid, goff, scratch, first_count);
   } else {
-    carry = gather_regions(cq, nsub, kFilterSub,
-                           SplitSlots{A.cand_key + (int64_t)q * A.cand_stride,
-                                      A.cand_id + (int64_t)q * A.cand_stride},
-                           lkey, lid, goff, scratch, first_count);
+    carry = gather_regions(cq, nsub, kFilterSub, slots, lkey, lid, goff, scratch, first_count);
   }
   if (carry <= kResolveCap) {
     select_core(LdsCands{lkey, lid}, (int64_t)carry, th.keff, th.b1, th.above, hist, scratch,

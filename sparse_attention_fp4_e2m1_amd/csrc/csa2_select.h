@@ -281,5 +281,98 @@ __device__ uint32_t gather_regions(const uint32_t *cq, int64_t nreg, int64_t reg
   return carry;
 }
 
+
+// Reads of the first slots of every region issued before the region counts
+// are known (with the counts and the histogram), so that for the usual
+// candidate counts the copy into LDS needs no second dependent round trip.
+// Entry u of a thread (e = tid + u * kThreads) reads slot e % S of region
+// e / S, S = 2^shift the largest power of two with nreg * S <= kSpec * kThreads
+// and S <= region.  Only for one group of regions (nreg <= kThreads) whose
+// slot total fits 21 bits (the overflow flags of gather_regions_early ride
+// above them in one scan).
+template <int kSpec>
+struct EarlySlots {
+  uint32_t key[kSpec];
+  int32_t id[kSpec];
+  uint32_t shift;
+  bool on;
+};
+
+template <int kSpec, int kThreads, class Slots>
+__device__ __forceinline__ EarlySlots<kSpec> early_slots(bool enable, const Slots &slots,
+                                                         int64_t nreg, int64_t region) {
+  EarlySlots<kSpec> e;
+  e.shift = 0;
+  e.on = enable && nreg > 0 && nreg <= kThreads && nreg * region < (1 << 21);
+  if (!e.on) return e;   // uniform
+  while ((nreg << (e.shift + 1)) <= (int64_t)kSpec * kThreads &&
+         ((int64_t)1 << (e.shift + 1)) <= region)
+    ++e.shift;
+  const int64_t mask = ((int64_t)1 << e.shift) - 1;
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const int64_t ent = (int64_t)threadIdx.x + (int64_t)u * kThreads;
+    // past the last region the read is clamped into it and later ignored
+    const int64_t r = min(ent >> e.shift, nreg - 1);
+    const int64_t src = r * region + (ent & mask);
+    e.key[u] = slots.key(src);
+    e.id[u] = (int32_t)slots.id(src);
+  }
+  return e;
+}
+
+// gather_regions for a group of regions read early by early_slots (e.on):
+// the early slots go to LDS straight from registers; only regions holding
+// more than S candidates send a second round of reads.  Contains barriers.
+template <int kCap, int kThreads, int kSpec, class Slots>
+__device__ uint32_t gather_regions_early(int64_t nreg, int64_t region, const Slots &slots,
+                                         const EarlySlots<kSpec> &e, uint32_t *lkey,
+                                         int32_t *lid, uint32_t *goff, uint32_t *scratch,
+                                         uint32_t first_count) {
+  constexpr uint32_t kLow = (1u << 21) - 1u;
+  const int tid = threadIdx.x;
+  const uint32_t S = 1u << e.shift;
+  const uint32_t mine = tid < nreg ? (uint32_t)min((int64_t)first_count, region) : 0u;
+  uint32_t tot_packed;
+  const uint32_t off =
+      block_exclusive_scan(mine | ((mine > S ? 1u : 0u) << 21), scratch, tot_packed) & kLow;
+  const uint32_t tot = tot_packed & kLow;
+  const bool more = (tot_packed >> 21) != 0u;
+  goff[tid] = off;
+  __syncthreads();
+  if (tot <= kCap) {
+#pragma unroll
+    for (int u = 0; u < kSpec; ++u) {
+      const uint32_t ent = (uint32_t)tid + (uint32_t)u * kThreads;
+      const uint32_t r = ent >> e.shift;
+      const uint32_t j = ent & (S - 1u);
+      if (r < (uint32_t)nreg) {
+        const uint32_t end = r + 1 < (uint32_t)nreg ? goff[r + 1] : tot;
+        if (goff[r] + j < end) {
+          lkey[goff[r] + j] = e.key[u];
+          lid[goff[r] + j] = e.id[u];
+        }
+      }
+    }
+    if (more) {
+      for (uint32_t j = tid; j < tot; j += kThreads) {
+        int lo = 0, hi = (int)nreg - 1;           // last region with goff <= j
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (goff[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        const uint32_t k = j - goff[lo];
+        if (k >= S) {
+          const int64_t src = (int64_t)lo * region + k;
+          lkey[j] = slots.key(src);
+          lid[j] = (int32_t)slots.id(src);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return tot;
+}
+
 }  // namespace
 }  // namespace csa2
