@@ -229,8 +229,9 @@ def traffic_for(workload: str):
     path = os.path.join(ROOT, "profiles", "index_scan_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(workload)
-    if not rec or rec.get("kernel_sha") != score_kernel_sha():
+    doc = json.load(open(path))
+    rec = doc.get(workload)
+    if not rec or doc.get("kernel_sha") != score_kernel_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -103,8 +103,8 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(
 // [g*512, g*512 + 512) and positions [r*sub, (r+1)*sub) clipped to 1 + the
 // largest q_pos among them.  Each wave keeps its 64 queries' E4M3 index
 // queries in registers as MFMA B operands (4 column tiles x kSteps k-steps of
-// 32 bytes per lane); the 8 waves share the index keys, staged through LDS
-// kGemmStage positions (16-row tiles) at a time, double buffered.  With grid.x a
+// 32 bytes per lane); the 8 waves share the index keys, loaded straight into
+// LDS kGemmStage positions (16-row tiles) at a time, two buffers.  With grid.x a
 // multiple of 8 all query groups of one range land on one XCD and share the
 // keys through its L2.
 //
@@ -135,7 +135,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
   constexpr int kPieces = kStageBytes / 16 / kGemmThreads;   // 16-B loads per thread per stage
   static_assert(kPieces >= 1 && kStageBytes % (16 * kGemmThreads) == 0, "stage shape");
 
-  __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stageA[kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stageB[kStageBytes];
   __shared__ int32_t s_seq[kGemmQ];
   __shared__ int32_t s_list[kGemmQ];
   __shared__ uint32_t s_scr[kGemmWaves + 1];
@@ -220,20 +221,22 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     piece_off[k] = chunk * 1024 + h * 16;   // plus the position's tile and slot
   }
   constexpr int T = kWave / H;   // positions per key tile
-  auto load_stage = [&](const uint8_t *kb, int p0, uint4 *pf) {
+  // A stage goes from global memory straight into LDS (16 B per lane, the
+  // wave's 64 pieces contiguous: lane l of wave w moves piece k*512 + 64w + l),
+  // with no registers in between.  Offsets within a sequence's keys fit 32
+  // bits.  The two stage buffers are separate LDS objects so that reads of
+  // one never wait on the loads into the other; the barrier that starts a
+  // stage waits for the loads into it.
+  auto dma_stage = [&](const uint8_t *kb, uint8_t *dst, int p0) {
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
       const int p = min(p0 + piece_pos[k], (int)capacity - 1);
-      pf[k] = *reinterpret_cast<const uint4 *>(kb + (int64_t)(p / T) * 4096 + (p % T) * H * 16 +
-                                               piece_off[k]);
+      const uint32_t off = (uint32_t)(p / T) * 4096u + (uint32_t)((p % T) * H * 16 + piece_off[k]);
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const uint32_t *>(kb + off),
+          reinterpret_cast<uint32_t *>(dst + (k * kGemmThreads + wave * 64) * 16), 16, 0, 0);
     }
   };
-  auto store_stage = [&](uint8_t *dst, const uint4 *pf) {
-#pragma unroll
-    for (int k = 0; k < kPieces; ++k)
-      *reinterpret_cast<uint4 *>(dst + (tid + k * kGemmThreads) * 16) = pf[k];
-  };
-
   for (uint32_t si = 0; si < nseq; ++si) {
     const int32_t sigma = s_list[si];
     // columns of other sequences: pass 1 never stores them, pass 2 compares
@@ -260,14 +263,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
 #pragma unroll
     for (int k = 0; k < kBlkGroup / 2; ++k) sreg[k] = 0u;
     int nshift = 0;
-    uint4 pf[kPieces];
-    load_stage(kb, p_begin, pf);
-    store_stage(stage[0], pf);
-    for (int it = 0; it < n_st; ++it) {
-      const int p0 = p_begin + it * kGemmStage;
-      __syncthreads();   // stage it&1 written; stage (it+1)&1 no longer read
-      load_stage(kb, min(p0 + kGemmStage, p_end - 1), pf);   // next stage (clamped on the last)
-      const uint8_t *cur = stage[it & 1];
+    // the products and the pass's epilogue over one staged buffer
+    auto compute = [&](const uint8_t *cur, int p0) {
       if (wave_act) {
 #pragma unroll
         for (int rt = 0; rt < kGemmStage / kBlk; ++rt) {
@@ -376,9 +373,21 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
           }
         }
       }
-      store_stage(stage[(it + 1) & 1], pf);
+    };
+    dma_stage(kb, stageA, p_begin);
+    for (int it = 0; it < n_st; ++it) {
+      const int p0 = p_begin + it * kGemmStage;
+      __syncthreads();   // this stage's loads done; the other buffer no longer read
+      const int p_next = min(p0 + kGemmStage, p_end - 1);   // next stage (clamped on the last)
+      if ((it & 1) == 0) {
+        dma_stage(kb, stageB, p_next);
+        compute(stageA, p0);
+      } else {
+        dma_stage(kb, stageA, p_next);
+        compute(stageB, p0);
+      }
     }
-    __syncthreads();   // the next sequence's first stage reuses stage 0
+    __syncthreads();   // the next sequence's first stage reuses stage A
   }
   if (kPass == 2) {
     const int q = qbase + wave * 64 + lane;
