@@ -74,15 +74,24 @@ def test_attention_empty_and_single():
     assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL
 
 
-def test_attention_custom_scale():
-    announce("attn scale")
-    wl, gc, oc = _setup(16)
+@pytest.mark.parametrize("heads", [16, 64])
+@pytest.mark.parametrize("scale", [0.3, -0.2, 0.0])
+def test_attention_custom_scale(heads, scale):
+    # a negative scale (folded into the query's sign on the GPU) and a zero
+    # scale (uniform weights over the valid rows, lse = ln n), with holes
+    announce(f"attn scale={scale} heads={heads}")
+    wl, gc, oc = _setup(heads)
     qd = synth.gen_queries(wl, 2)
-    topk = np.random.default_rng(3).integers(0, 3000, (3, 300)).astype(np.int32)
-    out, lse = _run(gc, qd.q, topk, scale=0.3)
-    ref_o, ref_l = _oracle(oc, qd.q, topk, scale=float(np.float32(0.3)))
+    rng = np.random.default_rng(3)
+    topk = rng.integers(0, 3000, (3, 300)).astype(np.int32)
+    topk[2, rng.random(300) < 0.4] = -1
+    out, lse = _run(gc, qd.q, topk, scale=scale)
+    ref_o, ref_l = _oracle(oc, qd.q, topk, scale=float(np.float32(scale)))
     rel, dl = attn_errors(out, lse, ref_o, ref_l)
     assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL
+    if scale == 0.0:
+        n = (topk >= 0).sum(1)
+        assert np.allclose(lse, np.log(n)[:, None], atol=1e-5)
 
 
 def test_attention_deterministic():
