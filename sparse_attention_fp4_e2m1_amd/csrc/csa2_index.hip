@@ -17,7 +17,7 @@
 //                    (written out per workgroup in one burst), histogram the
 //                    top 12 key bits, and for a pool-building Full layer the
 //                    8-position block maxima and their histogram.
-//   filter_kernel    per wave and 1024 keys: keep every key whose top 12 bits
+//   filter_kernel    per wave and 512 keys: keep every key whose top 12 bits
 //                    reach b1 -- the bin of the 12-bit histogram holding the
 //                    K-th largest key, which each workgroup reads off the
 //                    histogram itself -- with its index, in index order
@@ -46,8 +46,8 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kFilterThreads = 256;
-constexpr int kFilterSub = 1024;           // keys per filter wave (one candidate slot region)
+constexpr int kFilterThreads = 1024;      // few, wide workgroups: each derives the threshold bin
+constexpr int kFilterSub = 512;            // keys per filter wave (one candidate slot region)
 constexpr int64_t kDirectMax = 32768;      // up to this many keys the resolve filters them itself
 constexpr int kEarlySlots = 8;             // candidate slots per resolve thread read before the counts
 
@@ -495,10 +495,11 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
   const int64_t sub = (int64_t)blockIdx.x * (kFilterThreads / kWave) + threadIdx.x / kWave;
   const int64_t start = sub * kFilterSub;
   const uint32_t *kq = A.keys + (int64_t)q * A.n_stride;
-  // 4 x 4 keys per lane; key (k, lane, e) sits at start + k*256 + lane*4 + e
-  uint32_t kv[4][4];
+  // kFilterSub / 256 x 4 keys per lane; key (k, lane, e) sits at start + k*256 + lane*4 + e
+  constexpr int kIters = kFilterSub / 256;
+  uint32_t kv[kIters][4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kIters; ++k) {
     const int64_t i0 = start + k * 256 + lane * 4;
     if (i0 + 3 < n) {
       const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kq + i0));
@@ -521,7 +522,7 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
   const uint64_t lt = (1ull << lane) - 1ull;
   uint32_t written = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kIters; ++k) {
     bool f[4];
     uint32_t before = 0, total = 0;
 #pragma unroll

@@ -434,16 +434,25 @@ __device__ __forceinline__ uint32_t kth_prefix(const uint16_t *v, int64_t n, uin
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   uint32_t prefix = 0u;
+  const int64_t n8 = n & ~(int64_t)7;   // whole 16-byte groups; the tail is checked per value
   for (int bit = 15; bit >= 0; --bit) {
     const uint32_t cand = prefix | (1u << bit);
+    const uint32_t cand_hi = cand << 16;   // hi half >= cand  <=>  word >= cand << 16
     uint32_t c = 0u;
-    for (int64_t i = (int64_t)tid * 8; i < n; i += kKthThreads * 8) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(v + i);   // rows hold whole groups of 16
+    for (int64_t i = (int64_t)tid * 8; i < n8; i += kKthThreads * 8) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(v + i);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        c += ((ws[e] & 0xFFFFu) >= cand ? 1u : 0u) + (ws[e] >= cand_hi ? 1u : 0u);
+    }
+    if (n8 < n && tid == (int)((n8 / 8) % kKthThreads)) {   // rows hold whole groups of 16
+      const uint4 w = *reinterpret_cast<const uint4 *>(v + n8);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t x = (ws[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        c += (i + e < n && x >= cand) ? 1u : 0u;
+        c += (n8 + e < n && x >= cand) ? 1u : 0u;
       }
     }
     for (int d = 32; d >= 1; d >>= 1) c += (uint32_t)__shfl_xor((int)c, d, kWave);
