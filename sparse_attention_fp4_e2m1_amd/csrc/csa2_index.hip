@@ -17,7 +17,7 @@
 //                    (written out per workgroup in one burst), histogram the
 //                    top 12 key bits, and for a pool-building Full layer the
 //                    8-position block maxima and their histogram.
-//   filter_kernel    per wave and 512 keys: keep every key whose top 12 bits
+//   filter_kernel    per wave and 512 or 1024 keys: keep every key whose top 12 bits
 //                    reach b1 -- the bin of the 12-bit histogram holding the
 //                    K-th largest key, which each workgroup reads off the
 //                    histogram itself -- with its index, in index order
@@ -47,9 +47,17 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFilterThreads = 1024;      // few, wide workgroups: each derives the threshold bin
-constexpr int kFilterSub = 512;            // keys per filter wave (one candidate slot region)
+// Keys per filter wave (one candidate slot region): 512, or 1024 for key
+// arrays past kFilterSmallMax keys, so that the resolve's one round of early
+// slot reads covers every region (at most one region per resolve thread).
+constexpr int kFilterSubMin = 512;
+constexpr int kFilterSubMax = 1024;
+constexpr int64_t kFilterSmallMax = (int64_t)kFilterSubMin * 1024;
 constexpr int64_t kDirectMax = 32768;      // up to this many keys the resolve filters them itself
 constexpr int kEarlySlots = 8;             // candidate slots per resolve thread read before the counts
+// Keys in the threshold bin beyond which the filter leaves the bits 19..8 pass
+// to the resolve (heavy ties would serialize the global atomics).
+constexpr uint32_t kH2MaxKeys = 8192;
 
 #ifndef CSA2_SCORE_UNROLL
 #define CSA2_SCORE_UNROLL 4            // 16-B loads per lane per prefetch batch
@@ -265,7 +273,7 @@ score_kernel(
   const int64_t t_end = min(n, t_begin + kChunk);
 
   using Ctx = ScoreCtx<H, kFp8Keys, kPool, kThreads, kChunk>;
-  uint32_t *hq = hist_tok + (int64_t)q * (kHistBins + kStateWords);
+  uint32_t *hq = hist_tok + (int64_t)q * kHistStride;
   if (!Ctx::kDirectHist) {
     for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
       hist[i] = 0u;
@@ -328,7 +336,7 @@ score_kernel(
     }
   }
   if (Ctx::kDirectHist) return;
-  uint32_t *hbq = kPool ? hist_blk + (int64_t)q * (kHistBins + kStateWords) : nullptr;
+  uint32_t *hbq = kPool ? hist_blk + (int64_t)q * kHistStride : nullptr;
   for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
     const uint32_t w = hist[i];
     if (w & 0xFFFFu) atomicAdd(&hq[2 * i], w & 0xFFFFu);
@@ -451,7 +459,7 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
   __syncthreads();
   if (in) {
     const uint32_t c = atomicExch(&lh[bin], 0u);
-    if (c) atomicAdd(&hist_tok[(int64_t)q * (kHistBins + kStateWords) + bin], c);
+    if (c) atomicAdd(&hist_tok[(int64_t)q * kHistStride + bin], c);
   }
 }
 
@@ -460,8 +468,8 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
 struct SelProblem {
   const uint32_t *keys;   // [nq][n_stride] order-preserving keys
   int64_t n_stride;
-  const uint32_t *hist;   // [nq][kHistBins + kStateWords] top-12-bit histogram
-  uint32_t *cand_key;     // [nq][cand_stride] filter output, one region per kFilterSub keys
+  uint32_t *hist;         // [nq][kHistStride]: histogram, state, second histogram
+  uint32_t *cand_key;     // [nq][cand_stride] filter output, one region per `region` keys
   int32_t *cand_id;
   int64_t cand_stride;
   uint32_t *cnt;          // [nq][nsub] candidates per region
@@ -471,16 +479,21 @@ struct SelProblem {
   int32_t kk;
   int32_t mode;           // OutMode
   int32_t direct;         // short arrays: no filter pass, the resolve reads the keys
+  int32_t region;         // keys per filter wave: kFilterSubMin or kFilterSubMax
 };
 
 struct SelProblems {
   SelProblem p[2];
 };
 
-// grid (filter groups, nq, problems).  Each wave takes kFilterSub keys and
+// grid (filter groups, nq, problems).  Each wave takes A.region keys and
 // keeps every key whose top 12 bits reach bin b1, with its index, in index
 // order, in its own slot region.  Every workgroup derives b1 from the query's
-// histogram itself (16 KB from L2), so no separate pass is needed.
+// histogram itself (16 KB from L2), so no separate pass is needed.  The keys
+// of bin b1 itself also go into the query's second histogram (bits 19..8),
+// unless the bin holds more than kH2MaxKeys of them; the first workgroup
+// records (keff, b1, above, second histogram valid) in the query's state.
+template <int kIters>   // largest region / 256 among the launch's problems
 __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
     const SelProblems P, const int32_t *__restrict__ q_pos, int32_t pool_len) {
   __shared__ uint32_t lh[kHistBins];
@@ -490,18 +503,21 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
   const int q = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t n = sel_len(A.mode, q_pos[q], pool_len);
-  if (A.direct || (int64_t)blockIdx.x * (kFilterThreads / kWave) * kFilterSub >= n) return;   // uniform
+  if (A.direct || (int64_t)blockIdx.x * (kFilterThreads / kWave) * A.region >= n) return;   // uniform
   // the wave's keys first (their loads overlap the threshold's)
   const int64_t sub = (int64_t)blockIdx.x * (kFilterThreads / kWave) + threadIdx.x / kWave;
-  const int64_t start = sub * kFilterSub;
+  const int64_t start = sub * A.region;
   const uint32_t *kq = A.keys + (int64_t)q * A.n_stride;
-  // kFilterSub / 256 x 4 keys per lane; key (k, lane, e) sits at start + k*256 + lane*4 + e
-  constexpr int kIters = kFilterSub / 256;
+  // region / 256 x 4 keys per lane; key (k, lane, e) sits at start + k*256 + lane*4 + e
+  const int iters = A.region / 256;   // uniform, <= kIters
   uint32_t kv[kIters][4];
 #pragma unroll
   for (int k = 0; k < kIters; ++k) {
     const int64_t i0 = start + k * 256 + lane * 4;
-    if (i0 + 3 < n) {
+    if (k >= iters) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kv[k][e] = 0u;
+    } else if (i0 + 3 < n) {
       const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kq + i0));
       kv[k][0] = v.x;
       kv[k][1] = v.y;
@@ -512,11 +528,15 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
       for (int e = 0; e < 4; ++e) kv[k][e] = i0 + e < n ? kq[i0 + e] : 0u;
     }
   }
-  const Threshold th =
-      hist_threshold(A.hist + (int64_t)q * (kHistBins + kStateWords), n, A.kk, lh, scratch, res);
+  uint32_t *hs = A.hist + (int64_t)q * kHistStride;
+  const Threshold th = hist_threshold(hs, n, A.kk, lh, scratch, res);
+  const bool use_h2 = th.keff > 0u && lh[th.b1] <= kH2MaxKeys;   // lh still holds the histogram
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    *reinterpret_cast<uint4 *>(hs + kStateOff) = make_uint4(th.keff, th.b1, th.above, use_h2 ? 1u : 0u);
   if (start >= n) return;
   const bool none = th.keff == 0u;
   const uint32_t thr = th.b1 << 20;
+  uint32_t *h2 = hs + kH2Off;
   uint32_t *ck = A.cand_key + (int64_t)q * A.cand_stride + start;
   int32_t *ci = A.cand_id + (int64_t)q * A.cand_stride + start;
   const uint64_t lt = (1ull << lane) - 1ull;
@@ -528,7 +548,7 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t i = start + k * 256 + lane * 4 + e;
-      f[e] = !none && i < n && kv[k][e] >= thr;
+      f[e] = !none && k < iters && i < n && kv[k][e] >= thr;
       const uint64_t b = __ballot(f[e]);
       before += __popcll(b & lt);
       total += __popcll(b);
@@ -540,6 +560,7 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
         ck[o] = kv[k][e];
         ci[o] = (int32_t)(start + k * 256 + lane * 4 + e);
         ++o;
+        if (use_h2 && (kv[k][e] >> 20) == th.b1) atomicAdd(&h2[(kv[k][e] >> 8) & 0xFFFu], 1u);
       }
     }
     written += total;
@@ -585,15 +606,34 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
       }
     }
   }
-  const int64_t nsub = (n + kFilterSub - 1) / kFilterSub;
+  const int64_t nsub = (n + A.region - 1) / A.region;
   const uint32_t *cq = A.cnt + (int64_t)q * A.nsub;
   const uint32_t first_count = A.direct ? 0u : first_region_count(cq, nsub);
   const SplitSlots slots{A.cand_key + (int64_t)q * A.cand_stride,
                          A.cand_id + (int64_t)q * A.cand_stride};
   const EarlySlots<kEarlySlots> early =
-      early_slots<kEarlySlots, kSelectThreads>(!A.direct, slots, nsub, kFilterSub);
-  const Threshold th =
-      hist_threshold(A.hist + (int64_t)q * (kHistBins + kStateWords), n, A.kk, hist, scratch, res);
+      early_slots<kEarlySlots, kSelectThreads>(!A.direct, slots, nsub, A.region);
+  const uint32_t *hs = A.hist + (int64_t)q * kHistStride;
+  Threshold th;
+  Pass19 p19{false, 0u, 0u};
+  if (A.direct) {
+    th = hist_threshold(hs, n, A.kk, hist, scratch, res);
+  } else {
+    // the filter's threshold, and its second histogram (read before knowing
+    // whether it is valid, in the same round of loads)
+    const uint4 st = *reinterpret_cast<const uint4 *>(hs + kStateOff);
+    for (int i = tid; i < kHistBins / 4; i += kSelectThreads)
+      reinterpret_cast<uint4 *>(hist)[i] = reinterpret_cast<const uint4 *>(hs + kH2Off)[i];
+    th.keff = st.x;
+    th.b1 = st.y;
+    th.above = st.z;
+    __syncthreads();
+    if (st.w != 0u) {
+      select_bin(hist, kHistBins, th.keff - th.above, scratch, res);
+      p19 = Pass19{true, (th.b1 << 12) | res[0], th.above + res[1]};
+      __syncthreads();   // res and hist free again
+    }
+  }
   const EmitAny emit{A.mode, A.out + (int64_t)q * A.out_stride,
                      pool_in ? pool_in + (int64_t)q * pool_len : nullptr, qp, (uint32_t)A.kk};
 
@@ -627,17 +667,17 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     }
     __syncthreads();
   } else if (early.on) {
-    carry = gather_regions_early<kResolveCap, kSelectThreads>(nsub, kFilterSub, slots, early, lkey,
+    carry = gather_regions_early<kResolveCap, kSelectThreads>(nsub, A.region, slots, early, lkey,
                                                               lid, goff, scratch, first_count);
   } else {
-    carry = gather_regions(cq, nsub, kFilterSub, slots, lkey, lid, goff, scratch, first_count);
+    carry = gather_regions(cq, nsub, A.region, slots, lkey, lid, goff, scratch, first_count);
   }
   if (carry <= kResolveCap) {
     select_core(LdsCands{lkey, lid}, (int64_t)carry, th.keff, th.b1, th.above, hist, scratch,
-                res, emit);
+                res, emit, p19);
   } else {
     select_core(GlobalKeys{A.keys + (int64_t)q * A.n_stride}, n, th.keff, th.b1, th.above, hist,
-                scratch, res, emit);
+                scratch, res, emit, p19);
   }
   // padding
   const bool blocks = A.mode == kOutPoolBlocks;
@@ -701,7 +741,7 @@ SelProblem sel_problem(const IndexArgs &a, const SelectArrays &A, int32_t kk, in
   SelProblem p;
   p.keys = reinterpret_cast<const uint32_t *>(w + A.keys);
   p.n_stride = A.n;
-  p.hist = reinterpret_cast<const uint32_t *>(w + A.hist);
+  p.hist = reinterpret_cast<uint32_t *>(w + A.hist);
   p.cand_key = reinterpret_cast<uint32_t *>(w + A.cand_key);
   p.cand_id = reinterpret_cast<int32_t *>(w + A.cand_id);
   p.cand_stride = A.cand_stride;
@@ -712,6 +752,7 @@ SelProblem sel_problem(const IndexArgs &a, const SelectArrays &A, int32_t kk, in
   p.kk = kk;
   p.mode = mode;
   p.direct = A.n <= kDirectMax;
+  p.region = A.region;
   return p;
 }
 
@@ -722,10 +763,15 @@ void launch_select(const IndexArgs &a, const SelProblems &P, int nprob, int64_t 
   const int64_t waves = kFilterThreads / kWave;
   bool all_direct = true;
   for (int i = 0; i < nprob; ++i) all_direct = all_direct && P.p[i].direct;
-  if (!all_direct)
-    hipLaunchKernelGGL(filter_kernel, dim3((unsigned)((max_nsub + waves - 1) / waves), (unsigned)a.nq,
-                                         (unsigned)nprob),
-                     dim3(kFilterThreads), 0, s, P, a.q_pos, a.pool_len);
+  int32_t region = 0;
+  for (int i = 0; i < nprob; ++i) region = std::max(region, P.p[i].direct ? 0 : P.p[i].region);
+  const dim3 grid((unsigned)((max_nsub + waves - 1) / waves), (unsigned)a.nq, (unsigned)nprob);
+  if (region > kFilterSubMin)
+    hipLaunchKernelGGL(filter_kernel<kFilterSubMax / 256>, grid, dim3(kFilterThreads), 0, s, P,
+                       a.q_pos, a.pool_len);
+  else if (!all_direct)
+    hipLaunchKernelGGL(filter_kernel<kFilterSubMin / 256>, grid, dim3(kFilterThreads), 0, s, P,
+                       a.q_pos, a.pool_len);
   hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)a.nq, (unsigned)nprob), dim3(kSelectThreads),
                      0, s, P, a.q_pos, a.pool_in, a.pool_len);
 }
@@ -735,12 +781,13 @@ thread_local hipEvent_t g_scan_after = nullptr;
 
 size_t carve(SelectArrays &A, int64_t n_slots, int32_t nq, size_t off) {
   A.n = (n_slots + 63) / 64 * 64;
-  A.nsub = (A.n + kFilterSub - 1) / kFilterSub;
-  A.cand_stride = A.nsub * kFilterSub;
+  A.region = A.n > kFilterSmallMax ? kFilterSubMax : kFilterSubMin;
+  A.nsub = (A.n + A.region - 1) / A.region;
+  A.cand_stride = A.nsub * A.region;
   A.keys = off;
   off = align256(off + (size_t)nq * A.n * 4);
   A.hist = off;
-  off = align256(off + (size_t)nq * (kHistBins + kStateWords) * 4);
+  off = align256(off + (size_t)nq * kHistStride * 4);
   A.cand_key = off;
   off = align256(off + (size_t)nq * A.cand_stride * 4);
   A.cand_id = off;
@@ -789,7 +836,7 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
   // 1. clear the histograms (the token and block histograms are cleared by one
   //    launch when both exist: the block one follows the token arrays)
   {
-    const int64_t n_tok = (int64_t)a.nq * (kHistBins + kStateWords);
+    const int64_t n_tok = (int64_t)a.nq * kHistStride;
     const unsigned blocks = (unsigned)std::min<int64_t>((n_tok + 255) / 256, 2048);
     hipLaunchKernelGGL(zero2_u32_kernel, dim3(blocks), dim3(256), 0, s,
                        reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),

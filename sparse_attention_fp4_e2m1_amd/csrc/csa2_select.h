@@ -14,7 +14,14 @@ namespace {
 
 constexpr int kSelectThreads = 1024;
 constexpr int kResolveCap = 8192;          // candidates held in LDS by a resolve
-constexpr int kStateWords = 16;            // spare words after each query's histogram
+// Per query, a selection's global histogram region holds the 12-bit histogram
+// of the keys' top bits (filled by the scorer), kStateWords of state, then the
+// histogram of bits 19..8 of the keys in the threshold bin (filled by the
+// filter when it runs).
+constexpr int kStateWords = 16;
+constexpr int kStateOff = kHistBins;                    // keff, b1, above, second histogram valid
+constexpr int kH2Off = kHistBins + kStateWords;
+constexpr int kHistStride = 2 * kHistBins + kStateWords;
 
 // ---------------------------------------------------------------------------
 // Selection helpers
@@ -143,25 +150,37 @@ __device__ Threshold hist_threshold(const uint32_t *__restrict__ hq, int64_t n, 
 // and 7..0 among the keys of bin b1 (above1 keys lie in higher bins).  The
 // ordered compaction takes 4 consecutive keys per thread per tile; when every
 // tie is selected (the usual case) one block scan per tile suffices.
+// Known result of the bits 19..8 pass (from a histogram built elsewhere).
+struct Pass19 {
+  bool known;
+  uint32_t pre24, above;   // top 24 bits of tau, keys above that 24-bit bin
+};
+
 template <class Src, class E>
 __device__ void select_core(const Src &src, int64_t n, uint32_t keff, uint32_t b1,
                             uint32_t above1, uint32_t *hist, uint32_t *scratch, uint32_t *res,
-                            const E &emit) {
+                            const E &emit, Pass19 p19 = Pass19{false, 0u, 0u}) {
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
   uint32_t tau = 0, c_gt = 0, n_tau = 0;
   if (keff > 0) {
     uint32_t above = above1;
-    for (int i = tid; i < kHistBins; i += nt) hist[i] = 0u;
-    __syncthreads();
-    for (int64_t i = tid; i < n; i += nt) {                  // bits 19..8 within bin b1
-      const uint32_t k = src.key(i);
-      if ((k >> 20) == b1) atomicAdd(&hist[(k >> 8) & 0xFFFu], 1u);
+    uint32_t pre24;
+    if (p19.known) {
+      pre24 = p19.pre24;
+      above = p19.above;
+    } else {
+      for (int i = tid; i < kHistBins; i += nt) hist[i] = 0u;
+      __syncthreads();
+      for (int64_t i = tid; i < n; i += nt) {                // bits 19..8 within bin b1
+        const uint32_t k = src.key(i);
+        if ((k >> 20) == b1) atomicAdd(&hist[(k >> 8) & 0xFFFu], 1u);
+      }
+      __syncthreads();
+      select_bin(hist, kHistBins, keff - above, scratch, res);
+      pre24 = (b1 << 12) | res[0];
+      above += res[1];
     }
-    __syncthreads();
-    select_bin(hist, kHistBins, keff - above, scratch, res);
-    const uint32_t pre24 = (b1 << 12) | res[0];
-    above += res[1];
     for (int i = tid; i < 256; i += nt) hist[i] = 0u;
     __syncthreads();
     for (int64_t i = tid; i < n; i += nt) {                  // bits 7..0
