@@ -31,7 +31,9 @@
 //                    A pool-building Full layer selects its pool blocks in the
 //                    same filter and resolve launches (a second grid slice).
 //                    Key arrays of at most kDirectMax entries (a Reindex pool)
-//                    skip the filter: the resolve reads and compacts them.
+//                    skip the filter: the resolve reads them, builds their
+//                    histogram in LDS and compacts them (such a pool's scorer
+//                    builds no global histogram, and nothing is cleared).
 // Small score chunks (one wave) count keys straight into the global histogram.
 //   copy_i32_kernel  Reuse mode: topk_out = reuse_src.
 // The selection helpers (select_bin, select_core, gather_regions) live in
@@ -351,16 +353,19 @@ score_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// gather_score_kernel: Reindex over a pool.  Each lane takes one pool entry:
-// it gathers the entry's index keys (all its 16-B pieces in flight at once;
-// the pool's positions are scattered, so there is nothing to coalesce across
-// lanes) and runs the canonical fp32 order in-lane -- per head and 16-channel
-// block an FMA chain in channel order, blocks (b0+b1)+(b2+b3), heads a
-// balanced pairwise tree -- the same bits as score_kernel.  Keys go out as one
-// coalesced store per lane; the 12-bit histogram is aggregated in LDS, where
-// only the bins in use are cleared and flushed.
+// gather_score_kernel: Reindex over a pool.  Each pool entry takes H lanes,
+// one per index head: lane h gathers the entry's head-h keys (all its 16-B
+// pieces in flight at once; the pool's positions are scattered, so there is
+// nothing to coalesce across entries) and runs the canonical fp32 order of
+// that head -- per 16-channel block an FMA chain in channel order, blocks
+// (b0+b1)+(b2+b3).  The heads' balanced pairwise tree then runs across the H
+// lanes with DPP moves (each level adds a lane's value to its partner's, so
+// both partners hold the same bits): the same bits as score_kernel.  The
+// group's first lane stores the key; the 12-bit histogram is aggregated in
+// LDS, where only the bins in use are cleared and flushed.
 // ---------------------------------------------------------------------------
 constexpr int kGatherThreads = 256;
+constexpr int kQPitch = 68;   // floats per head row of the staged query (spreads LDS banks)
 
 template <int H, bool kFp8Keys>
 __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
@@ -368,15 +373,18 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
     int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
     const int32_t *__restrict__ pool_in, int32_t pool_len, uint32_t *__restrict__ keys_tok,
     int64_t tok_stride, uint32_t *__restrict__ hist_tok) {
+  // hist_tok == nullptr: no global histogram (the resolve builds its own for a
+  // pool it reads whole)
   constexpr int kEsz = kFp8Keys ? 1 : 2;
-  constexpr int kLoadsPerHead = 4 * kEsz;                  // 16-B pieces per head (64 channels)
-  constexpr int kHeadsPerBatch = 32 / kLoadsPerHead < H ? 32 / kLoadsPerHead : H;
-  __shared__ float qlds[H * 64];
+  constexpr int kLoads = 4 * kEsz;                   // 16-B pieces per head (64 channels)
+  constexpr int kEntries = kGatherThreads / H;       // pool entries per workgroup
+  __shared__ __attribute__((aligned(16))) float qlds[H * kQPitch];
   __shared__ uint32_t lh[kHistBins];
   const int q = blockIdx.y;
   const int tid = threadIdx.x;
+  const int h = tid % H;                             // this lane's head
   const int32_t qp = q_pos[q];
-  const int64_t t = (int64_t)blockIdx.x * kGatherThreads + tid;
+  const int64_t t = (int64_t)blockIdx.x * kEntries + tid / H;
   const bool in = t < pool_len;
   const int32_t p = in ? pool_in[(int64_t)q * pool_len + t] : -1;
   const bool valid = p >= 0 && p <= qp;
@@ -385,79 +393,72 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
   for (int i = tid; i < H * 64; i += kGatherThreads) {
     float f = bf16_to_f32(q_idx[(int64_t)q * H * 64 + i]);
     if (q_fp8) f = e4m3_to_f32(e4m3_from_f32_nonneg(fabsf(f)) | ((__float_as_uint(f) >> 24) & 0x80u));
-    qlds[i] = f;
+    qlds[(i / 64) * kQPitch + i % 64] = f;
+  }
+
+  uint4 buf[kLoads];
+  {
+    const uint8_t *src = base + idx_chunk_offset<H, kEsz>(row, h, 0);
+#pragma unroll
+    for (int v = 0; v < kLoads; ++v) buf[v] = *reinterpret_cast<const uint4 *>(src + v * 1024);
   }
   __syncthreads();
-
-  float hs[H];
+  const float *qh = qlds + h * kQPitch;
+  float blk[4];
 #pragma unroll
-  for (int hb = 0; hb < H; hb += kHeadsPerBatch) {
-    uint4 buf[kHeadsPerBatch][kLoadsPerHead];
+  for (int j = 0; j < 4; ++j) {
+    float qv[16];
 #pragma unroll
-    for (int hh = 0; hh < kHeadsPerBatch; ++hh) {
-      const uint8_t *src = base + idx_chunk_offset<H, kEsz>(row, hb + hh, 0);
-#pragma unroll
-      for (int v = 0; v < kLoadsPerHead; ++v)
-        buf[hh][v] = *reinterpret_cast<const uint4 *>(src + v * 1024);
+    for (int k = 0; k < 4; ++k) {
+      const float4 f = *reinterpret_cast<const float4 *>(qh + 16 * j + 4 * k);
+      qv[4 * k] = f.x;
+      qv[4 * k + 1] = f.y;
+      qv[4 * k + 2] = f.z;
+      qv[4 * k + 3] = f.w;
     }
-    // every load of the batch in flight before the math: the empty asm uses
-    // each result here, so the compiler cannot sink a load next to its use
+    float acc = 0.0f;
+    if (kFp8Keys) {
+      const uint4 a = buf[j];
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-    for (int hh = 0; hh < kHeadsPerBatch; ++hh)
-#pragma unroll
-      for (int v = 0; v < kLoadsPerHead; ++v)
-        asm volatile("" ::"v"(buf[hh][v].x), "v"(buf[hh][v].y), "v"(buf[hh][v].z),
-                     "v"(buf[hh][v].w));
-#pragma unroll
-    for (int hh = 0; hh < kHeadsPerBatch; ++hh) {
-      const float *qh = qlds + (hb + hh) * 64;
-      float blk[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float acc = 0.0f;
-        if (kFp8Keys) {
-          const uint4 a = buf[hh][j];
-          const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
-            auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
-            acc = __builtin_fmaf(qh[16 * j + 4 * k + 0], lo[0], acc);
-            acc = __builtin_fmaf(qh[16 * j + 4 * k + 1], lo[1], acc);
-            acc = __builtin_fmaf(qh[16 * j + 4 * k + 2], hi[0], acc);
-            acc = __builtin_fmaf(qh[16 * j + 4 * k + 3], hi[1], acc);
-          }
-        } else {
-#pragma unroll
-          for (int hv = 0; hv < 2; ++hv) {
-            const uint4 a = buf[hh][2 * j + hv];
-            const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              acc = __builtin_fmaf(qh[16 * j + 8 * hv + 2 * k], __uint_as_float(w[k] << 16), acc);
-              acc = __builtin_fmaf(qh[16 * j + 8 * hv + 2 * k + 1],
-                                   __uint_as_float(w[k] & 0xFFFF0000u), acc);
-            }
-          }
-        }
-        blk[j] = acc;
+      for (int k = 0; k < 4; ++k) {
+        auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
+        auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
+        acc = __builtin_fmaf(qv[4 * k + 0], lo[0], acc);
+        acc = __builtin_fmaf(qv[4 * k + 1], lo[1], acc);
+        acc = __builtin_fmaf(qv[4 * k + 2], hi[0], acc);
+        acc = __builtin_fmaf(qv[4 * k + 3], hi[1], acc);
       }
-      hs[hb + hh] = (blk[0] + blk[1]) + (blk[2] + blk[3]);
+    } else {
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv) {
+        const uint4 a = buf[2 * j + hv];
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc = __builtin_fmaf(qv[8 * hv + 2 * k], __uint_as_float(w[k] << 16), acc);
+          acc = __builtin_fmaf(qv[8 * hv + 2 * k + 1], __uint_as_float(w[k] & 0xFFFF0000u), acc);
+        }
+      }
     }
+    blk[j] = acc;
   }
-#pragma unroll
-  for (int w = 1; w < H; w *= 2)      // balanced pairwise tree over heads
-#pragma unroll
-    for (int i = 0; i < H; i += 2 * w) hs[i] = hs[i] + hs[i + w];
-  const uint32_t key = valid ? score_key(hs[0]) : 0u;
-  if (in) keys_tok[(int64_t)q * tok_stride + t] = key;
+  float hs = (blk[0] + blk[1]) + (blk[2] + blk[3]);
+  // balanced pairwise tree over the heads, across the entry's lanes
+  hs = hs + dpp_xor1(hs);
+  hs = hs + dpp_xor2(hs);
+  if (H == 8) hs = hs + dpp_half_mirror(hs);
+  const uint32_t key = valid ? score_key(hs) : 0u;
+  const bool lead = in && h == 0;
+  if (lead) keys_tok[(int64_t)q * tok_stride + t] = key;
+  if (hist_tok == nullptr) return;   // uniform
 
   const uint32_t bin = key >> 20;
-  if (in) lh[bin] = 0u;
+  if (lead) lh[bin] = 0u;
   __syncthreads();
-  if (in) atomicAdd(&lh[bin], 1u);
+  if (lead) atomicAdd(&lh[bin], 1u);
   __syncthreads();
-  if (in) {
+  if (lead) {
     const uint32_t c = atomicExch(&lh[bin], 0u);
     if (c) atomicAdd(&hist_tok[(int64_t)q * kHistStride + bin], c);
   }
@@ -617,7 +618,21 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
   Threshold th;
   Pass19 p19{false, 0u, 0u};
   if (A.direct) {
-    th = hist_threshold(hs, n, A.kk, hist, scratch, res);
+    // the 12-bit histogram of the short key array, built here in LDS (the
+    // keys past n are not counted)
+    for (int i = tid; i < kHistBins; i += kSelectThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kDirectIters; ++it) {
+      const int64_t i0 = (int64_t)it * 4 * kSelectThreads + 4 * tid;
+      if ((int64_t)it * 4 * kSelectThreads >= n) break;   // uniform
+      const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e < n) atomicAdd(&hist[k4[e] >> 20], 1u);
+    }
+    __syncthreads();
+    th = lds_threshold(n, A.kk, hist, scratch, res);
   } else {
     // the filter's threshold, and its second histogram (read before knowing
     // whether it is valid, in the same round of loads)
@@ -721,13 +736,14 @@ template <int H, bool kFp8>
 void launch_score_mode(const IndexArgs &a, int64_t n, bool pool, bool reindex_pool, hipStream_t s) {
   if (reindex_pool) {
     const TopkWorkspace &L = a.layout;
+    constexpr int kEntries = kGatherThreads / H;
     hipLaunchKernelGGL((gather_score_kernel<H, kFp8>),
-                       dim3((unsigned)((a.pool_len + kGatherThreads - 1) / kGatherThreads),
-                            (unsigned)a.nq),
+                       dim3((unsigned)((a.pool_len + kEntries - 1) / kEntries), (unsigned)a.nq),
                        dim3(kGatherThreads), 0, s, static_cast<const uint8_t *>(a.cache->idx_k),
                        (int64_t)a.cache->capacity, a.q_idx, a.q_fp8, a.q_seq, a.q_pos, a.pool_in,
                        a.pool_len, reinterpret_cast<uint32_t *>(a.ws + L.tok.keys), L.tok.n,
-                       reinterpret_cast<uint32_t *>(a.ws + L.tok.hist));
+                       a.pool_len <= kDirectMax ? nullptr
+                                                : reinterpret_cast<uint32_t *>(a.ws + L.tok.hist));
   } else if (pool) {
     launch_score<H, kFp8, true>(a, n, s);
   } else {
@@ -834,8 +850,9 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
   const bool pool = a.mode == CSA2_FULL && a.pool_blocks > 0;
   const bool reindex_pool = a.mode == CSA2_REINDEX && a.pool_in != nullptr;
   // 1. clear the histograms (the token and block histograms are cleared by one
-  //    launch when both exist: the block one follows the token arrays)
-  {
+  //    launch when both exist: the block one follows the token arrays).  A
+  //    pool short enough for the resolve to read whole needs none.
+  if (!(reindex_pool && a.pool_len <= kDirectMax)) {
     const int64_t n_tok = (int64_t)a.nq * kHistStride;
     const unsigned blocks = (unsigned)std::min<int64_t>((n_tok + 255) / 256, 2048);
     hipLaunchKernelGGL(zero2_u32_kernel, dim3(blocks), dim3(256), 0, s,

@@ -126,11 +126,9 @@ struct Threshold {
   uint32_t keff, b1, above;
 };
 
-__device__ Threshold hist_threshold(const uint32_t *__restrict__ hq, int64_t n, int32_t kk,
-                                    uint32_t *lh, uint32_t *scratch, uint32_t *res) {
-  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x)
-    reinterpret_cast<uint4 *>(lh)[i] = reinterpret_cast<const uint4 *>(hq)[i];
-  __syncthreads();
+// The same from a histogram already in LDS (all threads, barriers).
+__device__ Threshold lds_threshold(int64_t n, int32_t kk, uint32_t *lh, uint32_t *scratch,
+                                   uint32_t *res) {
   Threshold t;
   t.keff = (uint32_t)max((int64_t)0, min((int64_t)kk, n - (int64_t)lh[0]));
   t.b1 = 0u;
@@ -142,6 +140,14 @@ __device__ Threshold hist_threshold(const uint32_t *__restrict__ hq, int64_t n, 
   }
   __syncthreads();   // res and lh free again
   return t;
+}
+
+__device__ Threshold hist_threshold(const uint32_t *__restrict__ hq, int64_t n, int32_t kk,
+                                    uint32_t *lh, uint32_t *scratch, uint32_t *res) {
+  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x)
+    reinterpret_cast<uint4 *>(lh)[i] = reinterpret_cast<const uint4 *>(hq)[i];
+  __syncthreads();
+  return lds_threshold(n, kk, lh, scratch, res);
 }
 
 // The K-th largest key tau and the selection: keys > tau, then the first ties
