@@ -656,18 +656,42 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
   // straight from a short key array, or from the filter's slot regions
   uint32_t carry = 0;
   if (A.direct) {
+    // ordered compaction with two barriers: per iteration a wave-local scan,
+    // then one wave scans the (iteration, wave) totals in key order
     const uint32_t thr = th.b1 << 20;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    constexpr int kWaves = kSelectThreads / kWave;
+    constexpr int kEnt = kDirectIters * kWaves;
+    static_assert(kEnt <= 2 * kWave && kEnt + 1 <= kSelectThreads, "totals fit one wave's scan");
+    uint32_t wexcl[kDirectIters];
 #pragma unroll
     for (int it = 0; it < kDirectIters; ++it) {
-      const int64_t base = (int64_t)it * 4 * kSelectThreads;
-      if (base >= n) break;   // uniform
-      const int64_t i0 = base + 4 * tid;
+      const int64_t i0 = (int64_t)it * 4 * kSelectThreads + 4 * tid;
       const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
       uint32_t c = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) c += (th.keff > 0 && i0 + e < n && k4[e] >= thr) ? 1u : 0u;
-      uint32_t tot;
-      uint32_t o = carry + block_exclusive_scan(c, scratch, tot);
+      const uint32_t inc = wave_inclusive_scan(c);
+      wexcl[it] = inc - c;
+      if (lane == kWave - 1) goff[it * kWaves + wave] = inc;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int e0 = 2 * lane, e1 = 2 * lane + 1;
+      const uint32_t v0 = e0 < kEnt ? goff[e0] : 0u, v1 = e1 < kEnt ? goff[e1] : 0u;
+      const uint32_t inc = wave_inclusive_scan(v0 + v1);
+      if (e0 < kEnt) goff[e0] = inc - v0 - v1;
+      if (e1 < kEnt) goff[e1] = inc - v1;
+      if (lane == kWave - 1) goff[kEnt] = inc;
+    }
+    __syncthreads();
+    carry = goff[kEnt];
+#pragma unroll
+    for (int it = 0; it < kDirectIters; ++it) {
+      const int64_t i0 = (int64_t)it * 4 * kSelectThreads + 4 * tid;
+      const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
+      uint32_t o = goff[it * kWaves + wave] + wexcl[it];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (th.keff > 0 && i0 + e < n && k4[e] >= thr) {
@@ -678,7 +702,6 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
           ++o;
         }
       }
-      carry += tot;
     }
     __syncthreads();
   } else if (early.on) {
