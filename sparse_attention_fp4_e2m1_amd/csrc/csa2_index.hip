@@ -247,7 +247,8 @@ score_kernel(
     const uint8_t *__restrict__ idx_k, int64_t capacity, const uint16_t *__restrict__ q_idx,
     int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
     uint32_t *__restrict__ keys_tok, int64_t tok_stride, uint32_t *__restrict__ hist_tok,
-    uint32_t *__restrict__ keys_blk, int64_t blk_stride, uint32_t *__restrict__ hist_blk) {
+    uint32_t *__restrict__ keys_blk, int64_t blk_stride, uint32_t *__restrict__ hist_blk,
+    int64_t hstride, int32_t hcopies) {
   constexpr int kEsz = kFp8Keys ? 1 : 2;
   constexpr int TPI = kWave / H;
   constexpr int kBpt = H * 64 * kEsz;     // bytes per token
@@ -275,7 +276,9 @@ score_kernel(
   const int64_t t_end = min(n, t_begin + kChunk);
 
   using Ctx = ScoreCtx<H, kFp8Keys, kPool, kThreads, kChunk>;
-  uint32_t *hq = hist_tok + (int64_t)q * kHistStride;
+  // this workgroup's copy of the query's histogram(s)
+  const int64_t hoff = (int64_t)q * hstride + (int64_t)(blockIdx.x % hcopies) * kHistBins;
+  uint32_t *hq = hist_tok + hoff;
   if (!Ctx::kDirectHist) {
     for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
       hist[i] = 0u;
@@ -338,7 +341,7 @@ score_kernel(
     }
   }
   if (Ctx::kDirectHist) return;
-  uint32_t *hbq = kPool ? hist_blk + (int64_t)q * kHistStride : nullptr;
+  uint32_t *hbq = kPool ? hist_blk + hoff : nullptr;
   for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
     const uint32_t w = hist[i];
     if (w & 0xFFFFu) atomicAdd(&hq[2 * i], w & 0xFFFFu);
@@ -372,7 +375,7 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
     const uint8_t *__restrict__ idx_k, int64_t capacity, const uint16_t *__restrict__ q_idx,
     int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
     const int32_t *__restrict__ pool_in, int32_t pool_len, uint32_t *__restrict__ keys_tok,
-    int64_t tok_stride, uint32_t *__restrict__ hist_tok) {
+    int64_t tok_stride, uint32_t *__restrict__ hist_tok, int64_t hstride, int32_t hcopies) {
   // hist_tok == nullptr: no global histogram (the resolve builds its own for a
   // pool it reads whole)
   constexpr int kEsz = kFp8Keys ? 1 : 2;
@@ -460,7 +463,8 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
   __syncthreads();
   if (lead) {
     const uint32_t c = atomicExch(&lh[bin], 0u);
-    if (c) atomicAdd(&hist_tok[(int64_t)q * kHistStride + bin], c);
+    if (c)
+      atomicAdd(&hist_tok[(int64_t)q * hstride + (int64_t)(blockIdx.x % hcopies) * kHistBins + bin], c);
   }
 }
 
@@ -469,7 +473,9 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
 struct SelProblem {
   const uint32_t *keys;   // [nq][n_stride] order-preserving keys
   int64_t n_stride;
-  uint32_t *hist;         // [nq][kHistStride]: histogram, state, second histogram
+  uint32_t *hist;         // [nq][hstride]: histogram copies, state, second histogram
+  int64_t hstride;
+  int32_t hcopies;
   uint32_t *cand_key;     // [nq][cand_stride] filter output, one region per `region` keys
   int32_t *cand_id;
   int64_t cand_stride;
@@ -529,15 +535,16 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
       for (int e = 0; e < 4; ++e) kv[k][e] = i0 + e < n ? kq[i0 + e] : 0u;
     }
   }
-  uint32_t *hs = A.hist + (int64_t)q * kHistStride;
-  const Threshold th = hist_threshold(hs, n, A.kk, lh, scratch, res);
+  uint32_t *hs = A.hist + (int64_t)q * A.hstride;
+  const Threshold th = hist_threshold(hs, A.hcopies, n, A.kk, lh, scratch, res);
   const bool use_h2 = th.keff > 0u && lh[th.b1] <= kH2MaxKeys;   // lh still holds the histogram
   if (blockIdx.x == 0 && threadIdx.x == 0)
-    *reinterpret_cast<uint4 *>(hs + kStateOff) = make_uint4(th.keff, th.b1, th.above, use_h2 ? 1u : 0u);
+    *reinterpret_cast<uint4 *>(hs + state_off(A.hcopies)) =
+        make_uint4(th.keff, th.b1, th.above, use_h2 ? 1u : 0u);
   if (start >= n) return;
   const bool none = th.keff == 0u;
   const uint32_t thr = th.b1 << 20;
-  uint32_t *h2 = hs + kH2Off;
+  uint32_t *h2 = hs + h2_off(A.hcopies);
   uint32_t *ck = A.cand_key + (int64_t)q * A.cand_stride + start;
   int32_t *ci = A.cand_id + (int64_t)q * A.cand_stride + start;
   const uint64_t lt = (1ull << lane) - 1ull;
@@ -614,7 +621,7 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
                          A.cand_id + (int64_t)q * A.cand_stride};
   const EarlySlots<kEarlySlots> early =
       early_slots<kEarlySlots, kSelectThreads>(!A.direct, slots, nsub, A.region);
-  const uint32_t *hs = A.hist + (int64_t)q * kHistStride;
+  const uint32_t *hs = A.hist + (int64_t)q * A.hstride;
   Threshold th;
   Pass19 p19{false, 0u, 0u};
   if (A.direct) {
@@ -636,9 +643,9 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
   } else {
     // the filter's threshold, and its second histogram (read before knowing
     // whether it is valid, in the same round of loads)
-    const uint4 st = *reinterpret_cast<const uint4 *>(hs + kStateOff);
+    const uint4 st = *reinterpret_cast<const uint4 *>(hs + state_off(A.hcopies));
     for (int i = tid; i < kHistBins / 4; i += kSelectThreads)
-      reinterpret_cast<uint4 *>(hist)[i] = reinterpret_cast<const uint4 *>(hs + kH2Off)[i];
+      reinterpret_cast<uint4 *>(hist)[i] = reinterpret_cast<const uint4 *>(hs + h2_off(A.hcopies))[i];
     th.keff = st.x;
     th.b1 = st.y;
     th.above = st.z;
@@ -738,7 +745,8 @@ void launch_score_shape(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
                      a.q_seq, a.q_pos, reinterpret_cast<uint32_t *>(a.ws + L.tok.keys), L.tok.n,
                      reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
                      kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.keys) : nullptr, L.blk.n,
-                     kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr);
+                     kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr,
+                     L.tok.hstride, L.tok.hcopies);
 }
 
 // Workgroup shape from the amount of work: long streams when there are enough
@@ -766,7 +774,8 @@ void launch_score_mode(const IndexArgs &a, int64_t n, bool pool, bool reindex_po
                        (int64_t)a.cache->capacity, a.q_idx, a.q_fp8, a.q_seq, a.q_pos, a.pool_in,
                        a.pool_len, reinterpret_cast<uint32_t *>(a.ws + L.tok.keys), L.tok.n,
                        a.pool_len <= kDirectMax ? nullptr
-                                                : reinterpret_cast<uint32_t *>(a.ws + L.tok.hist));
+                                                : reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
+                       L.tok.hstride, L.tok.hcopies);
   } else if (pool) {
     launch_score<H, kFp8, true>(a, n, s);
   } else {
@@ -781,6 +790,8 @@ SelProblem sel_problem(const IndexArgs &a, const SelectArrays &A, int32_t kk, in
   p.keys = reinterpret_cast<const uint32_t *>(w + A.keys);
   p.n_stride = A.n;
   p.hist = reinterpret_cast<uint32_t *>(w + A.hist);
+  p.hstride = A.hstride;
+  p.hcopies = A.hcopies;
   p.cand_key = reinterpret_cast<uint32_t *>(w + A.cand_key);
   p.cand_id = reinterpret_cast<int32_t *>(w + A.cand_id);
   p.cand_stride = A.cand_stride;
@@ -818,15 +829,24 @@ void launch_select(const IndexArgs &a, const SelProblems &P, int nprob, int64_t 
 thread_local hipEvent_t g_scan_before = nullptr;
 thread_local hipEvent_t g_scan_after = nullptr;
 
-size_t carve(SelectArrays &A, int64_t n_slots, int32_t nq, size_t off) {
+// Histogram copies for a key array of n_slots: one per 128K keys, at most 4
+// (a single query's hundreds of scorer workgroups would otherwise queue their
+// atomics on the same few hot bins; readers add the copies up).
+int32_t hist_copies(int64_t n_slots) {
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(4, n_slots / 131072));
+}
+
+size_t carve(SelectArrays &A, int64_t n_slots, int32_t nq, size_t off, int32_t hcopies) {
   A.n = (n_slots + 63) / 64 * 64;
+  A.hcopies = hcopies;
+  A.hstride = hist_stride(hcopies);
   A.region = A.n > kFilterSmallMax ? kFilterSubMax : kFilterSubMin;
   A.nsub = (A.n + A.region - 1) / A.region;
   A.cand_stride = A.nsub * A.region;
   A.keys = off;
   off = align256(off + (size_t)nq * A.n * 4);
   A.hist = off;
-  off = align256(off + (size_t)nq * kHistStride * 4);
+  off = align256(off + (size_t)nq * A.hstride * 4);
   A.cand_key = off;
   off = align256(off + (size_t)nq * A.cand_stride * 4);
   A.cand_id = off;
@@ -849,8 +869,12 @@ TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t
   if (mode == CSA2_REUSE) return w;
   const bool reindex_pool = mode == CSA2_REINDEX && pool_len > 0;
   const bool pool = mode == CSA2_FULL && pool_blocks > 0;
-  size_t off = carve(w.tok, reindex_pool ? (int64_t)pool_len : (int64_t)c.capacity, nq, 0);
-  if (pool) off = carve(w.blk, ((int64_t)c.capacity + kPoolBlock - 1) / kPoolBlock, nq, off);
+  // the token and block histograms are filled by the same scorer launch and
+  // cleared by one launch: the same number of copies
+  const int64_t n_tok = reindex_pool ? (int64_t)pool_len : (int64_t)c.capacity;
+  const int32_t hc = hist_copies(n_tok);
+  size_t off = carve(w.tok, n_tok, nq, 0, hc);
+  if (pool) off = carve(w.blk, ((int64_t)c.capacity + kPoolBlock - 1) / kPoolBlock, nq, off, hc);
   w.total = off;
   if (gemm_eligible(c, mode, pool_len, pool_blocks)) {
     w.gemm = gemm_workspace_layout(c, nq);
@@ -876,7 +900,7 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
   //    launch when both exist: the block one follows the token arrays).  A
   //    pool short enough for the resolve to read whole needs none.
   if (!(reindex_pool && a.pool_len <= kDirectMax)) {
-    const int64_t n_tok = (int64_t)a.nq * kHistStride;
+    const int64_t n_tok = (int64_t)a.nq * L.tok.hstride;
     const unsigned blocks = (unsigned)std::min<int64_t>((n_tok + 255) / 256, 2048);
     hipLaunchKernelGGL(zero2_u32_kernel, dim3(blocks), dim3(256), 0, s,
                        reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),

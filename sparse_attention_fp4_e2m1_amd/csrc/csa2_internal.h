@@ -20,7 +20,7 @@ hipError_t launch_kv_append(const csa2_cache &c, const uint16_t *k, const uint16
 // Workspace carve-up of csa2_index_topk (byte offsets, 256-B aligned).
 struct SelectArrays {      // one selection problem per query (tokens, or pool blocks)
   size_t keys = 0;         // uint32 [nq][n]      order-preserving score keys
-  size_t hist = 0;         // uint32 [nq][2 * kHistBins + 16]  histogram, state words, second histogram
+  size_t hist = 0;         // uint32 [nq][hstride]  histogram copies, state words, second histogram
   size_t cand_key = 0;     // uint32 [nq][cand_stride] filter output, one slot region per wave
   size_t cand_id = 0;      // int32  [nq][cand_stride]
   size_t cnt = 0;          // uint32 [nq][nsub]   candidates per slot region
@@ -28,6 +28,8 @@ struct SelectArrays {      // one selection problem per query (tokens, or pool b
   int64_t cand_stride = 0;
   int64_t nsub = 0;
   int32_t region = 0;      // keys per filter wave (slots per region)
+  int32_t hcopies = 1;     // copies of the 12-bit histogram (scorer workgroups spread over them)
+  int64_t hstride = 0;     // words per query: hcopies histograms, state words, second histogram
 };
 
 // Workspace carve-up of the matrix-core scorer (E4M3 index queries and keys).

@@ -14,14 +14,19 @@ namespace {
 
 constexpr int kSelectThreads = 1024;
 constexpr int kResolveCap = 8192;          // candidates held in LDS by a resolve
-// Per query, a selection's global histogram region holds the 12-bit histogram
-// of the keys' top bits (filled by the scorer), kStateWords of state, then the
-// histogram of bits 19..8 of the keys in the threshold bin (filled by the
-// filter when it runs).
+// Per query, a selection's global histogram region holds `copies` copies of
+// the 12-bit histogram of the keys' top bits (the scorer's workgroups spread
+// their atomics over them; readers add them up), kStateWords of state (keff,
+// b1, above, second histogram valid), then the histogram of bits 19..8 of the
+// keys in the threshold bin (filled by the filter when it runs).
 constexpr int kStateWords = 16;
-constexpr int kStateOff = kHistBins;                    // keff, b1, above, second histogram valid
-constexpr int kH2Off = kHistBins + kStateWords;
-constexpr int kHistStride = 2 * kHistBins + kStateWords;
+__host__ __device__ constexpr int64_t hist_stride(int copies) {
+  return (int64_t)(copies + 1) * kHistBins + kStateWords;
+}
+__host__ __device__ constexpr int64_t state_off(int copies) { return (int64_t)copies * kHistBins; }
+__host__ __device__ constexpr int64_t h2_off(int copies) {
+  return (int64_t)copies * kHistBins + kStateWords;
+}
 
 // ---------------------------------------------------------------------------
 // Selection helpers
@@ -142,10 +147,19 @@ __device__ Threshold lds_threshold(int64_t n, int32_t kk, uint32_t *lh, uint32_t
   return t;
 }
 
-__device__ Threshold hist_threshold(const uint32_t *__restrict__ hq, int64_t n, int32_t kk,
-                                    uint32_t *lh, uint32_t *scratch, uint32_t *res) {
-  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x)
-    reinterpret_cast<uint4 *>(lh)[i] = reinterpret_cast<const uint4 *>(hq)[i];
+__device__ Threshold hist_threshold(const uint32_t *__restrict__ hq, int copies, int64_t n,
+                                    int32_t kk, uint32_t *lh, uint32_t *scratch, uint32_t *res) {
+  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x) {
+    uint4 v = reinterpret_cast<const uint4 *>(hq)[i];
+    for (int c = 1; c < copies; ++c) {
+      const uint4 w = reinterpret_cast<const uint4 *>(hq + (int64_t)c * kHistBins)[i];
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+    reinterpret_cast<uint4 *>(lh)[i] = v;
+  }
   __syncthreads();
   return lds_threshold(n, kk, lh, scratch, res);
 }
