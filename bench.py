@@ -159,7 +159,7 @@ class WorkloadRun:
                 total += cand * wl.idx_bytes_per_token() + nq * pool * 4
                 total += nq * wl.idx_heads * wl.idx_dim * 2 + nq * wl.top_k * 4
             else:
-                total += 2 * nq * wl.top_k * 4
+                pass                                             # Reuse: the source list itself
             total += nq * wl.top_k * (144 + 4)                   # selected rows + their indices
             total += nq * wl.heads * (wl.dk * 2 + wl.dv * 4 + 4)  # q in, out + lse out
         return total
@@ -218,20 +218,24 @@ def time_run(run, steps, warmup, hip, use_graph=False):
     return (t1 - t0), scan_ms, pct
 
 
-def score_kernel_sha() -> str:
-    src = os.path.join(ROOT, "sparse_attention_fp4_e2m1_amd", "csrc", "csa2_index.hip")
+def source_sha(name: str = "csa2_index.hip") -> str:
+    src = os.path.join(ROOT, "sparse_attention_fp4_e2m1_amd", "csrc", name)
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
 def traffic_for(workload: str):
-    """HBM bytes per scoring launch from committed rocprofv3 counter runs, if they
-    were taken on the current scoring kernel (else None)."""
+    """HBM bytes per launch of the workload's dominant kernel from committed
+    rocprofv3 counter runs, if they were taken on the current source of that
+    kernel (else None)."""
     path = os.path.join(ROOT, "profiles", "index_scan_traffic.json")
     if not os.path.exists(path):
         return None
     doc = json.load(open(path))
     rec = doc.get(workload)
-    if not rec or doc.get("kernel_sha") != score_kernel_sha():
+    if not rec:
+        return None
+    want = rec.get("source_sha", doc.get("kernel_sha"))
+    if want != source_sha(rec.get("source", "csa2_index.hip")):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -258,7 +262,7 @@ def measure(name, steps, warmup, hip, use_graph):
         ach = flops / (scan_ms * 1e-3) / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": "gemm_score_kernel pass 1 (fp8 index product)",
                            "achieved": ach, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / FP8_PEAK_TFLOPS, "traffic": None,
+                           "frac": ach / FP8_PEAK_TFLOPS, "traffic": traffic_for(name),
                            "flops_per_launch": flops, "avg_launch_ms": scan_ms}
     elif scan_ms is not None:
         ach = run.scan_bytes() / (scan_ms * 1e-3) / 1e9

@@ -26,7 +26,15 @@ class LayerStack:
         self.q_idx_dtype = q_idx_dtype
         self.softmax_scale = softmax_scale
         d = cache.device
-        self.topk = [torch.full((nq, top_k), -1, dtype=torch.int32, device=d) for _ in self.layers]
+        # a Reuse layer's list is its source's list itself (an alias: the
+        # indices are unchanged, so no copy is enqueued; csa2_index_topk's
+        # Reuse mode is the copying form for callers that need their own buffer)
+        self.topk = []
+        for L in self.layers:
+            if L.mode == "reuse":
+                self.topk.append(self.topk[L.reuse_from])
+            else:
+                self.topk.append(torch.full((nq, top_k), -1, dtype=torch.int32, device=d))
         self.pool = [torch.full((nq, 8 * L.pool_blocks), -1, dtype=torch.int32, device=d)
                      if (L.mode == "full" and L.pool_blocks > 0) else None for L in self.layers]
         self.out = [torch.zeros((nq, heads, cache.dv), dtype=torch.float32, device=d) for _ in self.layers]
@@ -52,9 +60,7 @@ class LayerStack:
             B.csa2_kv_append(self.cache, k, v, ik, seq, pos, stream=stream)
         for li, L in enumerate(self.layers):
             if L.mode == "reuse":
-                B.csa2_index_topk(self.cache, "reuse", None, None, None, self.top_k,
-                                  reuse_src=self.topk[L.reuse_from], topk_out=self.topk[li],
-                                  stream=stream)
+                pass   # self.topk[li] is self.topk[L.reuse_from]
             elif L.mode == "full":
                 if scan_events is not None:
                     B.LIB.csa2_profile_index_scan(scan_events[0], scan_events[1])
