@@ -145,6 +145,28 @@ __device__ __forceinline__ void dequant(const Gathered<kThreads> &gd, uint4 *kq,
   }
 }
 
+// Cross-row reductions with gfx950's lane swaps (VALU, no LDS round trip):
+// with both operands x, permlane16_swap leaves a lane's own value and that of
+// lane ^ 16 in the two results (permlane32_swap: lane ^ 32), in an order that
+// depends on the lane; the operations are commutative, so every lane of a
+// pair gets the same bits.
+__device__ __forceinline__ float xor16_partner_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_partner_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float lane_pair_sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float lane_pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // One sub-chunk of 64 rows from LDS: S^T on matrix cores, online softmax,
 // O += P V.  scale_log2 = |softmax scale| * log2(e) (a negative scale was
 // folded into Q), so the running maximum of the scaled scores is the scaled
@@ -180,14 +202,17 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
 #pragma unroll
       for (int i = 0; i < 4; ++i) st[t][i] = ((mine >> (4 * t + i)) & 1u) ? -INFINITY : st[t][i];
   }
-  // max as med3(x, y, +inf): no NaN canonicalization of the matrix-core
-  // results (none is NaN: -1 rows hold -inf)
+  // max as med3(x, y, +inf), as a tree: no NaN canonicalization of the
+  // matrix-core results (none is NaN: -1 rows hold -inf)
+  float m4[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mc = __builtin_amdgcn_fmed3f(mc, st[t][i], INFINITY);
-  mc = fmaxf(mc, shfl_xor_f(mc, 16));
-  mc = fmaxf(mc, shfl_xor_f(mc, 32));
+    m4[t] = __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(st[t][0], st[t][1], INFINITY),
+                                    __builtin_amdgcn_fmed3f(st[t][2], st[t][3], INFINITY), INFINITY);
+  mc = __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(m4[0], m4[1], INFINITY),
+                               __builtin_amdgcn_fmed3f(m4[2], m4[3], INFINITY), INFINITY);
+  mc = xor16_partner_max(mc);
+  mc = xor32_partner_max(mc);
   // (fmaxf drops the NaN of -inf * 0 for a zero scale)
   const float m_new = fmaxf(m_run, mc * scale_log2);
   // exp2 straight on the hardware instruction: arguments are <= 0 and the
@@ -217,12 +242,13 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
     }
   }
   // the normalizer sums the fp16 weights the PV product uses
-  float lsum = 0.0f;
   const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  float ls[2] = {0.0f, 0.0f};
 #pragma unroll
-  for (int k = 0; k < 8; ++k) lsum = __builtin_amdgcn_fdot2(p2[k], one2, lsum, false);
-  lsum += shfl_xor_f(lsum, 16);
-  lsum += shfl_xor_f(lsum, 32);
+  for (int k = 0; k < 8; ++k) ls[k & 1] = __builtin_amdgcn_fdot2(p2[k], one2, ls[k & 1], false);
+  float lsum = ls[0] + ls[1];
+  lsum = lane_pair_sum16(lsum);
+  lsum = lane_pair_sum32(lsum);
   l_run = l_run * alpha + lsum;
   m_run = m_new;
   // O rows are heads 16*wave + 4g + i: fetch their alpha from lane 4g + i.
