@@ -670,7 +670,8 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     const int wave = tid / kWave;
     constexpr int kWaves = kSelectThreads / kWave;
     constexpr int kEnt = kDirectIters * kWaves;
-    static_assert(kEnt <= 2 * kWave && kEnt + 1 <= kSelectThreads, "totals fit one wave's scan");
+    constexpr int kPerLane = (kEnt + kWave - 1) / kWave;   // totals per lane in the one-wave scan
+    static_assert(kEnt + 1 <= kSelectThreads, "totals and the sum fit goff");
     uint32_t wexcl[kDirectIters];
 #pragma unroll
     for (int it = 0; it < kDirectIters; ++it) {
@@ -685,12 +686,21 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     }
     __syncthreads();
     if (wave == 0) {
-      const int e0 = 2 * lane, e1 = 2 * lane + 1;
-      const uint32_t v0 = e0 < kEnt ? goff[e0] : 0u, v1 = e1 < kEnt ? goff[e1] : 0u;
-      const uint32_t inc = wave_inclusive_scan(v0 + v1);
-      if (e0 < kEnt) goff[e0] = inc - v0 - v1;
-      if (e1 < kEnt) goff[e1] = inc - v1;
-      if (lane == kWave - 1) goff[kEnt] = inc;
+      uint32_t v[kPerLane], sum = 0u;
+#pragma unroll
+      for (int u = 0; u < kPerLane; ++u) {
+        const int e = kPerLane * lane + u;
+        v[u] = e < kEnt ? goff[e] : 0u;
+        sum += v[u];
+      }
+      uint32_t ex = wave_inclusive_scan(sum) - sum;
+#pragma unroll
+      for (int u = 0; u < kPerLane; ++u) {
+        const int e = kPerLane * lane + u;
+        if (e < kEnt) goff[e] = ex;
+        ex += v[u];
+      }
+      if (lane == kWave - 1) goff[kEnt] = ex;
     }
     __syncthreads();
     carry = goff[kEnt];

@@ -174,6 +174,43 @@ def test_tie_heavy_keys(distinct, cap):
         assert list(host(tk)[0]) == list(range(500))
 
 
+@pytest.mark.parametrize("context,batch,qpos", [
+    (70000, 2, [69999, 40000, 33000, 5000, 100]),
+    (532480, 1, [532479, 300000, 7])])
+def test_filter_path_bit_exact(context, batch, qpos):
+    # key arrays past the short-array limit (32768 keys) go through the filter
+    # kernel (second-level histogram of the threshold bin, early slot reads in
+    # the resolve); past 512K keys the filter regions hold 1024 keys and the
+    # scorer's histogram comes in several copies.  Tokens and pool blocks.
+    announce(f"filter path context={context} batch={batch}")
+    m = lib()
+    wl = synth.workload("decode_1m", context=context, batch=batch)
+    gc = m.Cache(batch, context, idx_heads=8, idx_k_dtype="fp8")
+    oc = O.OracleCache(batch, context, idx_heads=8, idx_k_dtype="fp8", lazy=True)
+    data = synth.gen_batch(wl)
+    for b in range(batch):
+        seq, pos = np.full(context, b, np.int32), np.arange(context, dtype=np.int32)
+        m.csa2_kv_append(gc, dev_u16(data.k[b]), dev_u16(data.v[b]), dev_u16(data.ik[b]),
+                         dev_i32(seq), dev_i32(pos))
+        oc.append(data.k[b], data.v[b], data.ik[b], seq, pos)
+    del data
+    rng = np.random.default_rng(context)
+    nq = len(qpos)
+    qi = synth.f32_to_bf16_bits(rng.standard_normal((nq, 8, 64)).astype(np.float32))
+    qseq = [i % batch for i in range(nq)]
+    for top_k, pool_blocks in ((2048, 2048), (37, 0)):
+        tk, pool = m.csa2_index_topk(gc, "full", dev_u16(qi), dev_i32(qseq), dev_i32(qpos), top_k,
+                                     pool_blocks=pool_blocks)
+        torch.cuda.synchronize()
+        for i in range(nq):
+            t, p, _, _ = O.index_topk("full", oc, qseq[i], qpos[i],
+                                      O.query_index_values(qi[i], "bf16"), top_k,
+                                      pool_blocks=pool_blocks)
+            assert np.array_equal(host(tk)[i], t), (top_k, i)
+            if pool_blocks:
+                assert np.array_equal(host(pool)[i], p), (top_k, i)
+
+
 # ---------------------------------------------------------------------------
 # matrix-core scorer (E4M3 index query, E4M3 keys, every visible position)
 # ---------------------------------------------------------------------------
