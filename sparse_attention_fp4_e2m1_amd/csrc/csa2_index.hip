@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
   constexpr int kLoads = 4 * kEsz;                   // 16-B pieces per head (64 channels)
   constexpr int kEntries = kGatherThreads / H;       // pool entries per workgroup
   __shared__ __attribute__((aligned(16))) float qlds[H * kQPitch];
-  __shared__ uint32_t lh[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kHistBins];
   const int q = blockIdx.y;
   const int tid = threadIdx.x;
   const int h = tid % H;                             // this lane's head
@@ -503,7 +503,7 @@ struct SelProblems {
 template <int kIters>   // largest region / 256 among the launch's problems
 __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
     const SelProblems P, const int32_t *__restrict__ q_pos, int32_t pool_len) {
-  __shared__ uint32_t lh[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kHistBins];
   __shared__ uint32_t scratch[kFilterThreads / kWave + 1];
   __shared__ uint32_t res[4];
   const SelProblem &A = P.p[blockIdx.z];
@@ -585,7 +585,7 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
 __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     const SelProblems P, const int32_t *__restrict__ q_pos, const int32_t *__restrict__ pool_in,
     int32_t pool_len) {
-  __shared__ uint32_t hist[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
   __shared__ uint32_t scratch[kSelectThreads / kWave + 1];
   __shared__ uint32_t res[4];
   __shared__ uint32_t lkey[kResolveCap];

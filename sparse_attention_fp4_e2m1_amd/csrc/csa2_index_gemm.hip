@@ -396,32 +396,6 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
   }
 }
 
-// Per wave: the bin of the 256 LDS bins `h` holding the element of rank `want`
-// (1-based from the top) -> {bin, elements in higher bins}, seen by every lane.
-__device__ __forceinline__ uint2 wave_select_bin256(const uint32_t *h, uint32_t want) {
-  const int lane = threadIdx.x & (kWave - 1);
-  uint32_t c[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) c[b] = h[4 * lane + b];
-  const uint32_t sum = c[0] + c[1] + c[2] + c[3];
-  const uint32_t incl = wave_inclusive_scan(sum);
-  const uint32_t total = (uint32_t)__shfl((int)incl, kWave - 1, kWave);
-  uint32_t above = total - incl;   // elements in the bins of higher lanes
-  uint32_t found = 0xFFFFFFFFu, found_above = 0u;
-#pragma unroll
-  for (int b = 3; b >= 0; --b) {
-    if (above < want && above + c[b] >= want) {
-      found = 4 * lane + b;
-      found_above = above;
-    }
-    above += c[b];
-  }
-  const uint64_t who = __ballot(found != 0xFFFFFFFFu);
-  const int src = who ? __ffsll((unsigned long long)who) - 1 : 0;
-  return make_uint2((uint32_t)__shfl((int)found, src, kWave),
-                    (uint32_t)__shfl((int)found_above, src, kWave));
-}
-
 // thr[q] = (K-th largest 16-bit block maximum) << 16, or 0 when the query has
 // fewer than K blocks.  One workgroup per query.  The K-th largest value is
 // built bit by bit from the top: a bit stays set when at least K values reach
@@ -501,7 +475,7 @@ __global__ void __launch_bounds__(kGemmResolveThreads) gemm_resolve_kernel(
     const int32_t *__restrict__ q_pos, int32_t top_k, const uint32_t *__restrict__ plan,
     uint2 *__restrict__ cand, int64_t cand_stride, const uint32_t *__restrict__ cnt,
     int32_t nranges, int32_t *__restrict__ out) {
-  __shared__ uint32_t hist[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
   __shared__ uint32_t scratch[kGemmResolveThreads / kWave + 1];
   __shared__ uint32_t res[4];
   __shared__ uint32_t lkey[kGemmResolveCap];

@@ -33,12 +33,83 @@ __host__ __device__ constexpr int64_t h2_off(int copies) {
 // ---------------------------------------------------------------------------
 enum OutMode { kOutPositions = 0, kOutPoolIds = 1, kOutPoolBlocks = 2 };
 
+// Per wave: the bin of the 256 LDS bins `h` holding the element of rank `want`
+// (1-based from the top) -> {bin, elements in higher bins}, seen by every lane.
+__device__ __forceinline__ uint2 wave_select_bin256(const uint32_t *h, uint32_t want) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t c[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) c[b] = h[4 * lane + b];
+  const uint32_t sum = c[0] + c[1] + c[2] + c[3];
+  const uint32_t incl = wave_inclusive_scan(sum);
+  const uint32_t total = (uint32_t)__shfl((int)incl, kWave - 1, kWave);
+  uint32_t above = total - incl;   // elements in the bins of higher lanes
+  uint32_t found = 0xFFFFFFFFu, found_above = 0u;
+#pragma unroll
+  for (int b = 3; b >= 0; --b) {
+    if (above < want && above + c[b] >= want) {
+      found = 4 * lane + b;
+      found_above = above;
+    }
+    above += c[b];
+  }
+  const uint64_t who = __ballot(found != 0xFFFFFFFFu);
+  const int src = who ? __ffsll((unsigned long long)who) - 1 : 0;
+  return make_uint2((uint32_t)__shfl((int)found, src, kWave),
+                    (uint32_t)__shfl((int)found_above, src, kWave));
+}
+
 // Finds the bin holding the element of rank `want` (1-based, counted from the
 // largest key) among `nbins` LDS bins; result = {bin, elements in higher bins}.
 // All threads of the block take part and see the result.  Contains barriers.
+// 4096 bins (with at least 256 threads): sums of 16 bins by 256 threads, one
+// wave picks the 16-bin group and then the bin in it.  256 bins: one wave.
 __device__ void select_bin(const uint32_t *bins, int nbins, uint32_t want, uint32_t *scratch,
                            uint32_t *result) {
   const int nt = blockDim.x;
+  const int tid = threadIdx.x;
+  if (nbins == 4096 && nt >= 256) {
+    __shared__ uint32_t coarse[256];
+    if (tid < 256) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(bins + 16 * tid);
+      uint32_t s = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 v = p[k];
+        s += v.x + v.y + v.z + v.w;
+      }
+      coarse[tid] = s;
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      const uint2 cb = wave_select_bin256(coarse, want);
+      const uint32_t v = tid < 16 ? bins[16 * cb.x + tid] : 0u;
+      const uint32_t inc = wave_inclusive_scan(v);
+      const uint32_t tot16 = (uint32_t)__shfl((int)inc, 15, kWave);
+      const uint32_t above = cb.y + tot16 - inc;   // elements in the group's higher bins and above
+      const bool hit = tid < 16 && above < want && above + v >= want;
+      const uint64_t who = __ballot(hit);
+      const int f = who ? __ffsll((unsigned long long)who) - 1 : 0;
+      const uint32_t fa = (uint32_t)__shfl((int)above, f, kWave);
+      if (tid == 0 && who) {
+        result[0] = 16 * cb.x + (uint32_t)f;
+        result[1] = fa;
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  if (nbins == 256) {
+    if (tid < kWave) {
+      const uint2 r = wave_select_bin256(bins, want);
+      if (tid == 0) {
+        result[0] = r.x;
+        result[1] = r.y;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   const int per = (nbins + nt - 1) / nt;
   const int lo = threadIdx.x * per;
   uint32_t s = 0;
