@@ -59,6 +59,7 @@ constexpr int kKthThreads = 256;
 // queries per call).
 constexpr int kGemmResolveCap = 4096;
 constexpr int kGemmResolveThreads = 256;
+constexpr int kGemmEarlySlots = 16;     // candidate slots per resolve thread read before the counts
 constexpr int kKthLdsMax = 32768;       // block maxima a gemm_kth_kernel keeps in LDS
 
 __device__ __forceinline__ uint32_t e4m3_code(float f) {
@@ -493,8 +494,16 @@ __global__ void __launch_bounds__(kGemmResolveThreads) gemm_resolve_kernel(
   const uint32_t *cq = cnt + (int64_t)q * nranges;
   Emit<kOutPositions> emit{out + (int64_t)q * top_k, nullptr, qp, (uint32_t)top_k};
 
-  const uint32_t total = gather_regions<kGemmResolveCap, kGemmResolveThreads>(
-      cq, nreg, sub, PairSlots{cq2}, lkey, lid, goff, scratch, first_region_count(cq, nreg));
+  // the first slots of every range are read with the counts (one round of
+  // reads for the usual candidate counts)
+  const uint32_t first_count = first_region_count(cq, nreg);
+  const EarlySlots<kGemmEarlySlots> early =
+      early_slots<kGemmEarlySlots, kGemmResolveThreads>(true, PairSlots{cq2}, nreg, sub);
+  const uint32_t total =
+      early.on ? gather_regions_early<kGemmResolveCap, kGemmResolveThreads>(
+                     nreg, sub, PairSlots{cq2}, early, lkey, lid, goff, scratch, first_count)
+               : gather_regions<kGemmResolveCap, kGemmResolveThreads>(
+                     cq, nreg, sub, PairSlots{cq2}, lkey, lid, goff, scratch, first_count);
   const bool in_lds = total <= kGemmResolveCap;
   if (!in_lds) {
     // regions -> one run from slot 0 (a region's destination never passes its source)
