@@ -34,6 +34,10 @@ constexpr int kSub = 64;                      // rows per sub-chunk
 constexpr int kVtPitch = kSub + 4;            // fp16 elements per LDS row of V^T
 constexpr int kMaxRowsPerSplit = 2048;
 constexpr int kTargetGroups = 256;            // workgroups aimed for (one per CU)
+constexpr int kMaxSplits = 256;               // splits of one query, at most
+constexpr int kCombineBatch = 32;             // split outputs per round of combine loads
+static_assert(kTargetGroups <= kMaxSplits && (65536 + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit <= kMaxSplits,
+              "every accepted top_k fits the combine's split table");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -398,11 +402,16 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
 }
 
 // One workgroup per (query, 4 heads): thread (head, d) merges every split.
+// Every load is issued before its value is needed: the outputs of the
+// thread's channel in batches of kCombineBatch splits (the first batch before
+// the statistics), the split statistics one per lane of the head's first
+// wave, so that the usual split counts take a single round of loads.
 __global__ void __launch_bounds__(512) attn_combine_kernel(
     const float *__restrict__ part_acc, const float2 *__restrict__ part_ml, int32_t n_heads,
     int32_t splits, float *__restrict__ out, float *__restrict__ lse) {
   constexpr int kHeadsPer = 4;
-  __shared__ float mx_sh[kHeadsPer];
+  constexpr int kStatPerLane = kMaxSplits / 64;
+  __shared__ float w_sh[kHeadsPer][kMaxSplits];   // exp2(m_s - max) per split
   __shared__ float inv_sh[kHeadsPer];
   __shared__ float lse_sh[kHeadsPer];
   const int q = blockIdx.y;
@@ -410,47 +419,50 @@ __global__ void __launch_bounds__(512) attn_combine_kernel(
   const int h = blockIdx.x * kHeadsPer + hl;
   const int d = threadIdx.x & 127;
   const float2 *ml = part_ml + (int64_t)q * splits * n_heads + h;
+  const float *pa = part_acc + ((int64_t)q * splits * n_heads + h) * 128 + d;
+  const int64_t sstride = (int64_t)n_heads * 128;
+  float a[kCombineBatch];
+#pragma unroll
+  for (int u = 0; u < kCombineBatch; ++u) a[u] = u < splits ? pa[u * sstride] : 0.0f;
   if (d < 64) {
-    // the split statistics of head h: overall max and normalizer
+    // the split statistics of head h: overall max, weights and normalizer
+    float2 v[kStatPerLane];
     float mx = -INFINITY;
-    for (int s = d; s < splits; s += 64) mx = fmaxf(mx, ml[(int64_t)s * n_heads].x);
+#pragma unroll
+    for (int u = 0; u < kStatPerLane; ++u) {
+      const int sp = d + 64 * u;
+      v[u] = sp < splits ? ml[(int64_t)sp * n_heads] : make_float2(-INFINITY, 0.0f);
+      mx = fmaxf(mx, v[u].x);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     float tot = 0.0f;
-    for (int s = d; s < splits; s += 64) {
-      const float2 v = ml[(int64_t)s * n_heads];
-      if (v.x != -INFINITY) tot += exp2f(v.x - mx) * v.y;
+#pragma unroll
+    for (int u = 0; u < kStatPerLane; ++u) {
+      const int sp = d + 64 * u;
+      const float w = v[u].x == -INFINITY ? 0.0f : exp2f(v[u].x - mx);
+      if (sp < splits) w_sh[hl][sp] = w;
+      tot += w * v[u].y;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
     if (d == 0) {
-      mx_sh[hl] = mx;
       inv_sh[hl] = tot > 0.0f ? 1.0f / tot : 0.0f;
       lse_sh[hl] = tot > 0.0f ? (mx + log2f(tot)) * kLn2 : -INFINITY;
     }
   }
   __syncthreads();
-  const float mx = mx_sh[hl];
   float acc = 0.0f;
-  if (mx != -INFINITY) {
-    const float *pa = part_acc + ((int64_t)q * splits * n_heads + h) * 128 + d;
-    const int64_t sstride = (int64_t)n_heads * 128;
-    int s = 0;
-    for (; s + 4 <= splits; s += 4) {
-      float a[4], w[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = pa[(s + u) * sstride];
-        const float m = ml[(int64_t)(s + u) * n_heads].x;
-        w[u] = (m == -INFINITY) ? 0.0f : exp2f(m - mx);
-      }
+  for (int u = 0; u < kCombineBatch; ++u)
+    if (u < splits) acc += w_sh[hl][u] * a[u];
+  for (int s0 = kCombineBatch; s0 < splits; s0 += kCombineBatch) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc += w[u] * a[u];
-    }
-    for (; s < splits; ++s) {
-      const float m = ml[(int64_t)s * n_heads].x;
-      if (m != -INFINITY) acc += exp2f(m - mx) * pa[s * sstride];
-    }
+    for (int u = 0; u < kCombineBatch; ++u)
+      a[u] = s0 + u < splits ? pa[(int64_t)(s0 + u) * sstride] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+      if (s0 + u < splits) acc += w_sh[hl][s0 + u] * a[u];
   }
   const int64_t oi = (int64_t)q * n_heads + h;
   out[oi * 128 + d] = acc * inv_sh[hl];
@@ -476,6 +488,7 @@ AttnWorkspace attn_workspace_layout(const csa2_cache &c, int32_t nq, int32_t n_h
   AttnWorkspace w;
   const int32_t rps = rows_per_split(nq, top_k);
   w.splits = (top_k + rps - 1) / rps;
+  // splits <= max(kTargetGroups, top_k / kMaxRowsPerSplit) <= kMaxSplits for top_k <= 65536
   // a single split writes the final results directly (no partials)
   const size_t units = w.splits > 1 ? (size_t)nq * w.splits * n_heads : 0;
   w.part_acc = 0;
@@ -493,6 +506,7 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
   const float scale_log2 = fabsf(softmax_scale) * kLog2e;
   const bool q_negate = softmax_scale < 0.0f;
   const int32_t rps = rows_per_split(nq, top_k);
+  if (L.splits > kMaxSplits) return hipErrorInvalidValue;
   dim3 grid((unsigned)L.splits, (unsigned)nq);
   const int waves = n_heads / 16;
 #define CSA2_ATTN_CASE(W)                                                                        \

@@ -53,6 +53,7 @@ constexpr int kGemmTargetGroups = 256;  // workgroups aimed for (one per CU)
 constexpr int kBlk = 16;                // positions per block maximum (one row tile)
 constexpr int kBlkGroup = 16;           // block maxima a lane collects before one 32-B store
 constexpr int kRangeAlign = kBlk * kBlkGroup;   // positions per range: a multiple of this
+constexpr int kDmaPerTile = 2;          // next-stage pieces a thread loads per row tile
 constexpr int kKthThreads = 256;
 // Candidates a gemm_resolve_kernel keeps in LDS: ~K(1 + a few %) with continuous
 // scores; the smaller footprint fits three workgroups per CU (thousands of
@@ -135,6 +136,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
   constexpr int kStageBytes = kGemmStage * kPB;
   constexpr int kPieces = kStageBytes / 16 / kGemmThreads;   // 16-B loads per thread per stage
   static_assert(kPieces >= 1 && kStageBytes % (16 * kGemmThreads) == 0, "stage shape");
+  static_assert(kPass == 2 || kGemmStage * 2 == kBlk * kBlkGroup, "a block group spans two stages");
+  static_assert(kPieces <= kDmaPerTile * (kGemmStage / kBlk), "the next stage's pieces fit the row tiles");
 
   __shared__ __attribute__((aligned(16))) uint8_t stageA[kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stageB[kStageBytes];
@@ -145,7 +148,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int sub = (int)plan[0];
@@ -205,7 +208,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
   }
 
   // stage loads: piece i of a stage -> LDS offset 16 i; its key bytes are
-  // (row tile rt, k-step s, half hf, lane l) of the operand layout above
+  // (row tile rt, k-step s, half hf, lane l) of the operand layout above.
+  // Piece k of thread tid is piece tid + k * kGemmThreads.
   int piece_off[kPieces];         // byte offset within the position's tile
   int piece_pos[kPieces];         // position within the stage
 #pragma unroll
@@ -222,20 +226,28 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     piece_off[k] = chunk * 1024 + h * 16;   // plus the position's tile and slot
   }
   constexpr int T = kWave / H;   // positions per key tile
-  // A stage goes from global memory straight into LDS (16 B per lane, the
+  // The keys of positions [p0, p0 + kGemmStage) (p0 a multiple of 16) are
+  // contiguous bytes from p0 * kPB, and piece k of a thread sits at byte
+  // k * kGemmThreads * 16 + rel0 of them: one uniform base per stage and one
+  // 32-bit offset per thread.
+  const uint32_t rel0 =
+      (uint32_t)((piece_pos[0] / T) * 4096 + (piece_pos[0] % T) * H * 16 + piece_off[0]);
+  // A piece goes from global memory straight into LDS (16 B per lane, the
   // wave's 64 pieces contiguous: lane l of wave w moves piece k*512 + 64w + l),
-  // with no registers in between.  Offsets within a sequence's keys fit 32
-  // bits.  The two stage buffers are separate LDS objects so that reads of
-  // one never wait on the loads into the other; the barrier that starts a
-  // stage waits for the loads into it.
-  auto dma_stage = [&](const uint8_t *kb, uint8_t *dst, int p0) {
-#pragma unroll
-    for (int k = 0; k < kPieces; ++k) {
+  // with no registers in between.  A stage running past the capacity reads
+  // its last position instead.  The two stage buffers are separate LDS
+  // objects so that reads of one never wait on the loads into the other; the
+  // barrier that starts a stage waits for the loads into it.
+  auto dma_piece = [&](const uint8_t *kb, uint8_t *dst, int p0, int k) {
+    uint32_t *ldst = reinterpret_cast<uint32_t *>(dst + (k * kGemmThreads + wave * 64) * 16);
+    if (p0 + kGemmStage <= capacity) {
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const uint32_t *>(kb + (int64_t)p0 * kPB + k * (kGemmThreads * 16) + rel0),
+          ldst, 16, 0, 0);
+    } else {
       const int p = min(p0 + piece_pos[k], (int)capacity - 1);
       const uint32_t off = (uint32_t)(p / T) * 4096u + (uint32_t)((p % T) * H * 16 + piece_off[k]);
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const uint32_t *>(kb + off),
-          reinterpret_cast<uint32_t *>(dst + (k * kGemmThreads + wave * 64) * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t *>(kb + off), ldst, 16, 0, 0);
     }
   };
   for (uint32_t si = 0; si < nseq; ++si) {
@@ -261,112 +273,133 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const uint8_t *kb = idx_k + (int64_t)sigma * capacity * kPB;
     const int n_st = (p_end - p_begin + kGemmStage - 1) / kGemmStage;
     uint32_t sreg[kBlkGroup / 2];   // pass 1: this lane's query's block maxima, oldest lowest
+    // A operand of (row tile rt, k-step s) from a staged buffer
+    auto lds_a = [&](const uint8_t *cur, int rt, int s) -> v8i {
+      const uint8_t *src = cur + rt * kTileBytes + (2 * s) * 1024 + lane * 16;
+      const uint4 a = *reinterpret_cast<const uint4 *>(src);
+      const uint4 b = *reinterpret_cast<const uint4 *>(src + 1024);
+      return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    };
+    // The products and the pass's epilogue over one staged buffer (the
+    // stage's half of a group of kBlkGroup blocks); meanwhile the next stage
+    // goes into `nxt`, kDmaPerTile pieces per row tile, so that no wave stalls
+    // on a burst of loads.
+    auto compute = [&](const uint8_t *cur, int p0, uint8_t *nxt, bool more, int half) {
+      if (!wave_act) {
+        if (more) {
 #pragma unroll
-    for (int k = 0; k < kBlkGroup / 2; ++k) sreg[k] = 0u;
-    int nshift = 0;
-    // the products and the pass's epilogue over one staged buffer
-    auto compute = [&](const uint8_t *cur, int p0) {
-      if (wave_act) {
+          for (int k = 0; k < kPieces; ++k) dma_piece(kb, nxt, p0 + kGemmStage, k);
+        }
+        return;
+      }
+      v8i an = lds_a(cur, 0, 0);   // the next k-step's A operand, read one k-step ahead
 #pragma unroll
-        for (int rt = 0; rt < kGemmStage / kBlk; ++rt) {
-          const int pt = p0 + rt * kBlk;
-          if (pt >= p_end) break;
-          v4f acc[4];
+      for (int rt = 0; rt < kGemmStage / kBlk; ++rt) {
+        const int pt = p0 + rt * kBlk;
+        if (more) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+          for (int k = rt * kDmaPerTile; k < (rt + 1) * kDmaPerTile; ++k)
+            if (k < kPieces) dma_piece(kb, nxt, p0 + kGemmStage, k);
+        }
+        if (pt >= p_end) break;
+        v4f acc[4];
 #pragma unroll
-          for (int s = 0; s < kSteps; ++s) {
-            const uint8_t *src = cur + rt * kTileBytes + (2 * s) * 1024 + lane * 16;
-            const uint4 a = *reinterpret_cast<const uint4 *>(src);
-            const uint4 b = *reinterpret_cast<const uint4 *>(src + 1024);
-            const v8i av{(int)a.x, (int)a.y, (int)a.z, (int)a.w,
-                         (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+        for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, qb[j][s], acc[j], 0, 0,
-                                                                        0, 127, 0, 127);
+        for (int s = 0; s < kSteps; ++s) {
+          const v8i av = an;
+          if (s + 1 < kSteps) an = lds_a(cur, rt, s + 1);
+          else if (rt + 1 < kGemmStage / kBlk) an = lds_a(cur, rt + 1, 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, qb[j][s], acc[j], 0, 0, 0,
+                                                                      127, 0, 127);
+        }
+        const int prow = pt + 4 * grp;   // this lane's first row
+        // rows a column may not see: -inf in pass 1 (never the block maximum
+        // of a block the column sees), NaN in pass 2 (every comparison with it
+        // fails).  Most tiles are visible to every active column (and tiles
+        // never straddle a range end: ranges are multiples of 16 positions).
+        if (pt + kBlk - 1 > min_qp) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (prow + i > qp[j]) acc[j][i] = kPass == 1 ? -INFINITY : __builtin_nanf("");
+        }
+        if (kPass == 1) {
+          // block maximum in fp32 (the key order is the float order, -0 ==
+          // +0); E4M3 products keep every score finite, so the NaN-propagating
+          // maximum (no operand canonicalization) is the maximum
+          float mk[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            mk[j] = __builtin_elementwise_maximum(
+                __builtin_elementwise_maximum(acc[j][0], acc[j][1]),
+                __builtin_elementwise_maximum(acc[j][2], acc[j][3]));
+          // reduce over the four lane groups and scatter, lane group g ending
+          // with the maximum of column tile g.  permlane32_swap(x, y) returns,
+          // in lanes 0..31, (x, x of lane + 32) and in lanes 32..63 (y of
+          // lane - 32, y); permlane16_swap likewise for rows of 16 lanes.
+          const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mk[0]),
+                                                           __float_as_uint(mk[2]), false, false);
+          const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mk[1]),
+                                                           __float_as_uint(mk[3]), false, false);
+          const float ma = __builtin_elementwise_maximum(__uint_as_float(s1[0]), __uint_as_float(s1[1]));
+          const float mb = __builtin_elementwise_maximum(__uint_as_float(s2[0]), __uint_as_float(s2[1]));
+          const auto s3 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ma), __float_as_uint(mb),
+                                                           false, false);
+          const float keep =
+              __builtin_elementwise_maximum(__uint_as_float(s3[0]), __uint_as_float(s3[1]));
+          const uint32_t kkey = score_key(keep);
+          // kBlkGroup consecutive blocks per lane (two stages; ranges start at
+          // multiples of kRangeAlign, so groups are aligned), then one 32-B
+          // store; blocks past the range's end stay 0
+          const int slot = half * (kGemmStage / kBlk) + rt;
+          if (slot == 0) {
+#pragma unroll
+            for (int k = 0; k < kBlkGroup / 2; ++k) sreg[k] = 0u;
           }
-          const int prow = pt + 4 * grp;   // this lane's first row
-          // rows a column may not see become NaN: fmaxf skips them and every
-          // comparison with them fails.  Most tiles are visible to every
-          // active column (and tiles never straddle a range end: ranges are
-          // multiples of 16 positions).
-          if (pt + kBlk - 1 > min_qp) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (prow + i > qp[j]) acc[j][i] = __builtin_nanf("");
-          }
-          if (kPass == 1) {
-            // block maximum in fp32 (the key order is the float order, -0 == +0)
-            float mk[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              mk[j] = fmaxf(fmaxf(acc[j][0], acc[j][1]), fmaxf(acc[j][2], acc[j][3]));
-            // reduce over the four lane groups and scatter: lane group g ends
-            // with the maximum of column tile g
-            const bool hi2 = grp & 2;
-            float keep_a = hi2 ? mk[2] : mk[0], keep_b = hi2 ? mk[3] : mk[1];
-            const float send_a = hi2 ? mk[0] : mk[2], send_b = hi2 ? mk[1] : mk[3];
-            keep_a = fmaxf(keep_a, shfl_xor_f(send_a, 32));
-            keep_b = fmaxf(keep_b, shfl_xor_f(send_b, 32));
-            const bool lo1 = grp & 1;
-            const float keep = fmaxf(lo1 ? keep_b : keep_a, shfl_xor_f(lo1 ? keep_a : keep_b, 16));
-            const uint32_t kkey = score_key(keep);
-            // collect kBlkGroup consecutive blocks per lane, then one 32-B store
-            // (ranges start at multiples of kRangeAlign, so groups are aligned)
-#pragma unroll
-            for (int k = 0; k < kBlkGroup / 2 - 1; ++k) sreg[k] = (sreg[k] >> 16) | (sreg[k + 1] << 16);
-            sreg[kBlkGroup / 2 - 1] = (sreg[kBlkGroup / 2 - 1] >> 16) | (kkey & 0xFFFF0000u);
-            ++nshift;
-            const bool last = pt + kBlk >= p_end;
-            if (nshift == kBlkGroup || last) {
-              for (; nshift < kBlkGroup; ++nshift) {
-#pragma unroll
-                for (int k = 0; k < kBlkGroup / 2 - 1; ++k)
-                  sreg[k] = (sreg[k] >> 16) | (sreg[k + 1] << 16);
-                sreg[kBlkGroup / 2 - 1] >>= 16;
-              }
-              const int q = qbase + wave * 64 + lane;     // column tile grp, column col
-              const bool own_act = grp == 0 ? act[0] : grp == 1 ? act[1] : grp == 2 ? act[2] : act[3];
-              if (q < nq && own_act) {
-                const int g0 = (pt / kBlk) / kBlkGroup * kBlkGroup;
-                uint4 *dst = reinterpret_cast<uint4 *>(bmax + (int64_t)q * bmax_row + g0);
-                dst[0] = make_uint4(sreg[0], sreg[1], sreg[2], sreg[3]);
-                dst[1] = make_uint4(sreg[4], sreg[5], sreg[6], sreg[7]);
-              }
-              nshift = 0;
+          if (slot & 1) sreg[slot >> 1] |= kkey & 0xFFFF0000u;
+          else sreg[slot >> 1] = kkey >> 16;
+          if (slot == kBlkGroup - 1 || pt + kBlk >= p_end) {
+            const int q = qbase + wave * 64 + lane;     // column tile grp, column col
+            const bool own_act = grp == 0 ? act[0] : grp == 1 ? act[1] : grp == 2 ? act[2] : act[3];
+            if (q < nq && own_act) {
+              const int g0 = (pt / kBlk) / kBlkGroup * kBlkGroup;
+              uint4 *dst = reinterpret_cast<uint4 *>(bmax + (int64_t)q * bmax_row + g0);
+              dst[0] = make_uint4(sreg[0], sreg[1], sreg[2], sreg[3]);
+              dst[1] = make_uint4(sreg[4], sreg[5], sreg[6], sreg[7]);
             }
-          } else {
-            uint32_t selm[4];
-            uint32_t cp = 0u;   // byte j: candidates of column tile j in this lane
+          }
+        } else {
+          uint32_t selm[4];
+          uint32_t cp = 0u;   // byte j: candidates of column tile j in this lane
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            selm[j] = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) selm[j] |= (acc[j][i] >= thr_f[j] ? 1u : 0u) << i;
+            cp |= (uint32_t)__popc(selm[j]) << (8 * j);
+          }
+          if (__ballot(cp != 0u) != 0ull) {
+            // per column tile, candidates of the lower lane groups (earlier
+            // rows) and of all four, with the lane swaps described above
+            const auto r16 = __builtin_amdgcn_permlane16_swap(cp, cp, false, false);
+            const uint32_t pair = r16[0] + r16[1];
+            const auto r32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+            const uint32_t tot = r32[0] + r32[1];
+            const uint32_t pre = ((grp & 1) ? r16[0] : 0u) + ((grp & 2) ? r32[0] : 0u);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              selm[j] = 0u;
+              uint32_t off = run[j] + ((pre >> (8 * j)) & 0xFFu);
+              run[j] += (tot >> (8 * j)) & 0xFFu;
+              if (selm[j] != 0u) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) selm[j] |= (acc[j][i] >= thr_f[j] ? 1u : 0u) << i;
-              cp |= (uint32_t)__popc(selm[j]) << (8 * j);
-            }
-            if (__ballot(cp != 0u) != 0ull) {
-              // per column tile, candidates of the lower lane groups (earlier
-              // rows) and of all four
-              const uint32_t s1 = (uint32_t)__shfl((int)cp, (lane + 48) & 63, kWave);
-              const uint32_t s2 = (uint32_t)__shfl((int)cp, (lane + 32) & 63, kWave);
-              const uint32_t s3 = (uint32_t)__shfl((int)cp, (lane + 16) & 63, kWave);
-              const uint32_t pre = (grp >= 1 ? s1 : 0u) + (grp >= 2 ? s2 : 0u) + (grp >= 3 ? s3 : 0u);
-              const uint32_t tot = (uint32_t)__shfl((int)(pre + cp), col + 48, kWave);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                uint32_t off = run[j] + ((pre >> (8 * j)) & 0xFFu);
-                run[j] += (tot >> (8 * j)) & 0xFFu;
-                if (selm[j] != 0u) {
-#pragma unroll
-                  for (int i = 0; i < 4; ++i) {
-                    if (selm[j] & (1u << i)) {
-                      cbase[j][off] = make_uint2(score_key(acc[j][i]), (uint32_t)(prow + i));
-                      ++off;
-                    }
+                for (int i = 0; i < 4; ++i) {
+                  if (selm[j] & (1u << i)) {
+                    cbase[j][off] = make_uint2(score_key(acc[j][i]), (uint32_t)(prow + i));
+                    ++off;
                   }
                 }
               }
@@ -375,18 +408,14 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
         }
       }
     };
-    dma_stage(kb, stageA, p_begin);
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) dma_piece(kb, stageA, p_begin, k);
     for (int it = 0; it < n_st; ++it) {
       const int p0 = p_begin + it * kGemmStage;
       __syncthreads();   // this stage's loads done; the other buffer no longer read
-      const int p_next = min(p0 + kGemmStage, p_end - 1);   // next stage (clamped on the last)
-      if ((it & 1) == 0) {
-        dma_stage(kb, stageB, p_next);
-        compute(stageA, p0);
-      } else {
-        dma_stage(kb, stageA, p_next);
-        compute(stageB, p0);
-      }
+      const bool more = it + 1 < n_st;
+      if ((it & 1) == 0) compute(stageA, p0, stageB, more, 0);
+      else compute(stageB, p0, stageA, more, 1);
     }
     __syncthreads();   // the next sequence's first stage reuses stage A
   }
