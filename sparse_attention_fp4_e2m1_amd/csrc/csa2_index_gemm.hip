@@ -98,6 +98,20 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(
   *reinterpret_cast<uint2 *>(q8 + i0) = make_uint2(lo, hi);
 }
 
+// The lowest remaining candidate row of mask m (rows of a, m != 0) into slot
+// off of c, then off + 1 and m without that row.
+__device__ __forceinline__ void emit_lowest(uint2 *c, uint32_t &off, uint32_t &m, const v4f &a,
+                                            int prow) {
+  const uint32_t i = (uint32_t)__builtin_ctz(m);
+  float v = a[3];   // selects, not a branch per row
+  v = (m & 4u) ? a[2] : v;
+  v = (m & 2u) ? a[1] : v;
+  v = (m & 1u) ? a[0] : v;
+  c[off] = make_uint2(score_key(v), (uint32_t)prow + i);
+  ++off;
+  m &= m - 1u;
+}
+
 // ---------------------------------------------------------------------------
 // gemm_score_kernel
 //
@@ -280,10 +294,58 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
       const uint4 b = *reinterpret_cast<const uint4 *>(src + 1024);
       return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
     };
+    // Pass 2: the rows of one tile's products that reach their column's
+    // threshold, in row order, into the column's slot region.  The lane's
+    // candidates of column tile j take consecutive slots, one store per
+    // candidate rank (most lanes have none, a few one).
+    auto emit = [&](v4f (&acc)[4], int pt) {
+      const int prow = pt + 4 * grp;   // this lane's first row
+      if (pt + kBlk - 1 > min_qp) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (prow + i > qp[j]) acc[j][i] = __builtin_nanf("");   // every comparison fails
+      }
+      uint32_t selm[4];
+      uint32_t cp = 0u;   // byte j: candidates of column tile j in this lane
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        selm[j] = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) selm[j] |= (acc[j][i] >= thr_f[j] ? 1u : 0u) << i;
+        cp |= (uint32_t)__popc(selm[j]) << (8 * j);
+      }
+      if (__ballot(cp != 0u) == 0ull) return;
+      // per column tile, candidates of the lower lane groups (earlier rows)
+      // and of all four, with the lane swaps described below
+      const auto r16 = __builtin_amdgcn_permlane16_swap(cp, cp, false, false);
+      const uint32_t pair = r16[0] + r16[1];
+      const auto r32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+      const uint32_t tot = r32[0] + r32[1];
+      const uint32_t pre = ((grp & 1) ? r16[0] : 0u) + ((grp & 2) ? r32[0] : 0u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t off = run[j] + ((pre >> (8 * j)) & 0xFFu);
+        run[j] += (tot >> (8 * j)) & 0xFFu;
+        uint32_t m = selm[j];
+        if (m != 0u) {
+          emit_lowest(cbase[j], off, m, acc[j], prow);
+          if (m != 0u) {
+            emit_lowest(cbase[j], off, m, acc[j], prow);
+            if (m != 0u) {
+              emit_lowest(cbase[j], off, m, acc[j], prow);
+              if (m != 0u) emit_lowest(cbase[j], off, m, acc[j], prow);
+            }
+          }
+        }
+      }
+    };
     // The products and the pass's epilogue over one staged buffer (the
     // stage's half of a group of kBlkGroup blocks); meanwhile the next stage
     // goes into `nxt`, kDmaPerTile pieces per row tile, so that no wave stalls
-    // on a burst of loads.
+    // on a burst of loads.  Pass 2 emits a tile's candidates after issuing
+    // the next tile's products, so that the matrix cores work meanwhile.
     auto compute = [&](const uint8_t *cur, int p0, uint8_t *nxt, bool more, int half) {
       if (!wave_act) {
         if (more) {
@@ -293,6 +355,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
         return;
       }
       v8i an = lds_a(cur, 0, 0);   // the next k-step's A operand, read one k-step ahead
+      v4f accp[4];                 // pass 2: the previous tile's products
+      int ptl = p0;                // pass 2: the previous tile's first position
 #pragma unroll
       for (int rt = 0; rt < kGemmStage / kBlk; ++rt) {
         const int pt = p0 + rt * kBlk;
@@ -315,98 +379,70 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
             acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, qb[j][s], acc[j], 0, 0, 0,
                                                                       127, 0, 127);
         }
+        if (kPass == 2) {
+          if (rt > 0) emit(accp, ptl);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) accp[j] = acc[j];
+          ptl = pt;
+          continue;
+        }
         const int prow = pt + 4 * grp;   // this lane's first row
-        // rows a column may not see: -inf in pass 1 (never the block maximum
-        // of a block the column sees), NaN in pass 2 (every comparison with it
-        // fails).  Most tiles are visible to every active column (and tiles
-        // never straddle a range end: ranges are multiples of 16 positions).
+        // rows a column may not see hold -inf, never the block maximum of a
+        // block the column sees.  Most tiles are visible to every active
+        // column (and tiles never straddle a range end: ranges are multiples
+        // of 16 positions).
         if (pt + kBlk - 1 > min_qp) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (prow + i > qp[j]) acc[j][i] = kPass == 1 ? -INFINITY : __builtin_nanf("");
+              if (prow + i > qp[j]) acc[j][i] = -INFINITY;
         }
-        if (kPass == 1) {
-          // block maximum in fp32 (the key order is the float order, -0 ==
-          // +0); E4M3 products keep every score finite, so the NaN-propagating
-          // maximum (no operand canonicalization) is the maximum
-          float mk[4];
+        // block maximum in fp32 (the key order is the float order, -0 == +0);
+        // E4M3 products keep every score finite, so the NaN-propagating
+        // maximum (no operand canonicalization) is the maximum
+        float mk[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            mk[j] = __builtin_elementwise_maximum(
-                __builtin_elementwise_maximum(acc[j][0], acc[j][1]),
-                __builtin_elementwise_maximum(acc[j][2], acc[j][3]));
-          // reduce over the four lane groups and scatter, lane group g ending
-          // with the maximum of column tile g.  permlane32_swap(x, y) returns,
-          // in lanes 0..31, (x, x of lane + 32) and in lanes 32..63 (y of
-          // lane - 32, y); permlane16_swap likewise for rows of 16 lanes.
-          const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mk[0]),
-                                                           __float_as_uint(mk[2]), false, false);
-          const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mk[1]),
-                                                           __float_as_uint(mk[3]), false, false);
-          const float ma = __builtin_elementwise_maximum(__uint_as_float(s1[0]), __uint_as_float(s1[1]));
-          const float mb = __builtin_elementwise_maximum(__uint_as_float(s2[0]), __uint_as_float(s2[1]));
-          const auto s3 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ma), __float_as_uint(mb),
-                                                           false, false);
-          const float keep =
-              __builtin_elementwise_maximum(__uint_as_float(s3[0]), __uint_as_float(s3[1]));
-          const uint32_t kkey = score_key(keep);
-          // kBlkGroup consecutive blocks per lane (two stages; ranges start at
-          // multiples of kRangeAlign, so groups are aligned), then one 32-B
-          // store; blocks past the range's end stay 0
-          const int slot = half * (kGemmStage / kBlk) + rt;
-          if (slot == 0) {
+        for (int j = 0; j < 4; ++j)
+          mk[j] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(acc[j][0], acc[j][1]),
+                                                __builtin_elementwise_maximum(acc[j][2], acc[j][3]));
+        // reduce over the four lane groups and scatter, lane group g ending
+        // with the maximum of column tile g.  permlane32_swap(x, y) returns,
+        // in lanes 0..31, (x, x of lane + 32) and in lanes 32..63 (y of
+        // lane - 32, y); permlane16_swap likewise for rows of 16 lanes.
+        const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mk[0]),
+                                                         __float_as_uint(mk[2]), false, false);
+        const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mk[1]),
+                                                         __float_as_uint(mk[3]), false, false);
+        const float ma = __builtin_elementwise_maximum(__uint_as_float(s1[0]), __uint_as_float(s1[1]));
+        const float mb = __builtin_elementwise_maximum(__uint_as_float(s2[0]), __uint_as_float(s2[1]));
+        const auto s3 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ma), __float_as_uint(mb),
+                                                         false, false);
+        const float keep =
+            __builtin_elementwise_maximum(__uint_as_float(s3[0]), __uint_as_float(s3[1]));
+        const uint32_t kkey = score_key(keep);
+        // kBlkGroup consecutive blocks per lane (two stages; ranges start at
+        // multiples of kRangeAlign, so groups are aligned), then one 32-B
+        // store; blocks past the range's end stay 0
+        const int slot = half * (kGemmStage / kBlk) + rt;
+        if (slot == 0) {
 #pragma unroll
-            for (int k = 0; k < kBlkGroup / 2; ++k) sreg[k] = 0u;
-          }
-          if (slot & 1) sreg[slot >> 1] |= kkey & 0xFFFF0000u;
-          else sreg[slot >> 1] = kkey >> 16;
-          if (slot == kBlkGroup - 1 || pt + kBlk >= p_end) {
-            const int q = qbase + wave * 64 + lane;     // column tile grp, column col
-            const bool own_act = grp == 0 ? act[0] : grp == 1 ? act[1] : grp == 2 ? act[2] : act[3];
-            if (q < nq && own_act) {
-              const int g0 = (pt / kBlk) / kBlkGroup * kBlkGroup;
-              uint4 *dst = reinterpret_cast<uint4 *>(bmax + (int64_t)q * bmax_row + g0);
-              dst[0] = make_uint4(sreg[0], sreg[1], sreg[2], sreg[3]);
-              dst[1] = make_uint4(sreg[4], sreg[5], sreg[6], sreg[7]);
-            }
-          }
-        } else {
-          uint32_t selm[4];
-          uint32_t cp = 0u;   // byte j: candidates of column tile j in this lane
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            selm[j] = 0u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) selm[j] |= (acc[j][i] >= thr_f[j] ? 1u : 0u) << i;
-            cp |= (uint32_t)__popc(selm[j]) << (8 * j);
-          }
-          if (__ballot(cp != 0u) != 0ull) {
-            // per column tile, candidates of the lower lane groups (earlier
-            // rows) and of all four, with the lane swaps described above
-            const auto r16 = __builtin_amdgcn_permlane16_swap(cp, cp, false, false);
-            const uint32_t pair = r16[0] + r16[1];
-            const auto r32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
-            const uint32_t tot = r32[0] + r32[1];
-            const uint32_t pre = ((grp & 1) ? r16[0] : 0u) + ((grp & 2) ? r32[0] : 0u);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              uint32_t off = run[j] + ((pre >> (8 * j)) & 0xFFu);
-              run[j] += (tot >> (8 * j)) & 0xFFu;
-              if (selm[j] != 0u) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  if (selm[j] & (1u << i)) {
-                    cbase[j][off] = make_uint2(score_key(acc[j][i]), (uint32_t)(prow + i));
-                    ++off;
-                  }
-                }
-              }
-            }
+          for (int k = 0; k < kBlkGroup / 2; ++k) sreg[k] = 0u;
+        }
+        if (slot & 1) sreg[slot >> 1] |= kkey & 0xFFFF0000u;
+        else sreg[slot >> 1] = kkey >> 16;
+        if (slot == kBlkGroup - 1 || pt + kBlk >= p_end) {
+          const int q = qbase + wave * 64 + lane;     // column tile grp, column col
+          const bool own_act = grp == 0 ? act[0] : grp == 1 ? act[1] : grp == 2 ? act[2] : act[3];
+          if (q < nq && own_act) {
+            const int g0 = (pt / kBlk) / kBlkGroup * kBlkGroup;
+            uint4 *dst = reinterpret_cast<uint4 *>(bmax + (int64_t)q * bmax_row + g0);
+            dst[0] = make_uint4(sreg[0], sreg[1], sreg[2], sreg[3]);
+            dst[1] = make_uint4(sreg[4], sreg[5], sreg[6], sreg[7]);
           }
         }
       }
+      if (kPass == 2) emit(accp, ptl);   // the stage's last tile
     };
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) dma_piece(kb, stageA, p_begin, k);
