@@ -39,7 +39,7 @@ def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--workload", default="decode_64k_b32")
     p.add_argument("--no-extra", action="store_true", help="skip the 1M-context line item")
     p.add_argument("--no-cpu-baseline", action="store_true")
