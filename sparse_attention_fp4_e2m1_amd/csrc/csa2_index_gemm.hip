@@ -61,7 +61,7 @@ constexpr int kKthThreads = 256;
 constexpr int kGemmResolveCap = 4096;
 constexpr int kGemmResolveThreads = 256;
 constexpr int kGemmEarlySlots = 16;     // candidate slots per resolve thread read before the counts
-constexpr int kKthLdsMax = 32768;       // block maxima a gemm_kth_kernel keeps in LDS
+constexpr int kKthRegMax = 32768;       // block maxima a gemm_kth_kernel keeps in registers
 
 __device__ __forceinline__ uint32_t e4m3_code(float f) {
   return e4m3_from_f32_nonneg(fabsf(f)) | ((__float_as_uint(f) >> 24) & 0x80u);
@@ -465,53 +465,34 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
 // thr[q] = (K-th largest 16-bit block maximum) << 16, or 0 when the query has
 // fewer than K blocks.  One workgroup per query.  The K-th largest value is
 // built bit by bit from the top: a bit stays set when at least K values reach
-// the prefix with it set.  Counting compares values held in LDS (dynamic
-// size, from the capacity; read from global memory beyond kKthLdsMax), so
-// values that crowd into a few bins cost nothing extra.
-template <bool kLds>
-__device__ __forceinline__ uint32_t kth_prefix(const uint16_t *v, int64_t n, uint32_t k,
-                                               uint32_t *part) {
+// the prefix with it set.  Each thread holds its share of the values in
+// registers (kKthWords words of two values, the ones past the row's end 0,
+// which no candidate prefix reaches), so a bit costs two compares per word, a
+// wave sum and one barrier; rows longer than the registers hold are counted
+// from global memory.
+constexpr int kKthWords = 64;   // 16-bit values per thread / 2: 32768 per row
+static_assert(kKthRegMax <= 2 * kKthWords * kKthThreads, "register-held rows");
+
+__device__ __forceinline__ uint32_t kth_count_word(uint32_t w, uint32_t cand) {
+  return ((w & 0xFFFFu) >= cand ? 1u : 0u) + ((w >> 16) >= cand ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t kth_block_sum(uint32_t c, uint32_t (*part)[kKthThreads / kWave],
+                                                  int parity) {
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  uint32_t prefix = 0u;
-  const int64_t n8 = n & ~(int64_t)7;   // whole 16-byte groups; the tail is checked per value
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t cand = prefix | (1u << bit);
-    const uint32_t cand_hi = cand << 16;   // hi half >= cand  <=>  word >= cand << 16
-    uint32_t c = 0u;
-    for (int64_t i = (int64_t)tid * 8; i < n8; i += kKthThreads * 8) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(v + i);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  c = __builtin_amdgcn_readlane(wave_inclusive_scan(c), kWave - 1);
+  if ((tid & (kWave - 1)) == 0) part[parity][tid / kWave] = c;
+  __syncthreads();   // one barrier per bit: the two part rows alternate
+  uint32_t total = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        c += ((ws[e] & 0xFFFFu) >= cand ? 1u : 0u) + (ws[e] >= cand_hi ? 1u : 0u);
-    }
-    if (n8 < n && tid == (int)((n8 / 8) % kKthThreads)) {   // rows hold whole groups of 16
-      const uint4 w = *reinterpret_cast<const uint4 *>(v + n8);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t x = (ws[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        c += (n8 + e < n && x >= cand) ? 1u : 0u;
-      }
-    }
-    for (int d = 32; d >= 1; d >>= 1) c += (uint32_t)__shfl_xor((int)c, d, kWave);
-    if (lane == 0) part[tid / kWave] = c;
-    __syncthreads();
-    uint32_t total = 0u;
-#pragma unroll
-    for (int w = 0; w < kKthThreads / kWave; ++w) total += part[w];
-    __syncthreads();
-    if (total >= k) prefix = cand;
-  }
-  return prefix;
+  for (int w = 0; w < kKthThreads / kWave; ++w) total += part[parity][w];
+  return total;
 }
 
 __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
     const uint16_t *__restrict__ bmax, int64_t bmax_row, const int32_t *__restrict__ q_pos,
     int32_t top_k, uint32_t *__restrict__ thr) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t kth_vals[];
-  __shared__ uint32_t part[kKthThreads / kWave];
+  __shared__ uint32_t part[2][kKthThreads / kWave];
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t nblk = ((int64_t)q_pos[q] + 1 + kBlk - 1) / kBlk;
@@ -520,16 +501,60 @@ __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
     return;
   }
   const uint16_t *bq = bmax + (int64_t)q * bmax_row;
-  uint32_t t;
-  if (nblk <= kKthLdsMax) {
-    for (int64_t i = (int64_t)tid * 8; i < nblk; i += kKthThreads * 8)
-      *reinterpret_cast<uint4 *>(kth_vals + i) = *reinterpret_cast<const uint4 *>(bq + i);
-    __syncthreads();
-    t = kth_prefix<true>(kth_vals, nblk, (uint32_t)top_k, part);
+  const uint32_t k = (uint32_t)top_k;
+  uint32_t prefix = 0u;
+  if (nblk <= kKthRegMax) {
+    // group u of thread tid: values 8 (u * kKthThreads + tid) .. +7
+    const int ngroups = (int)((nblk + 8 * kKthThreads - 1) / (8 * kKthThreads));   // uniform
+    uint32_t v[kKthWords];
+#pragma unroll
+    for (int u = 0; u < kKthWords / 4; ++u) {
+      const int64_t i = 8 * ((int64_t)u * kKthThreads + tid);
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (u < ngroups && i < nblk) {
+        w = *reinterpret_cast<const uint4 *>(bq + i);
+        if (i + 8 > nblk) {   // the row's last group: values past its end count as 0
+          uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (i + e >= nblk) ws[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          w = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+        }
+      }
+      v[4 * u] = w.x;
+      v[4 * u + 1] = w.y;
+      v[4 * u + 2] = w.z;
+      v[4 * u + 3] = w.w;
+    }
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t cand = prefix | (1u << bit);
+      uint32_t c = 0u;
+#pragma unroll
+      for (int u = 0; u < kKthWords / 4; ++u) {
+        if (u < ngroups) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c += kth_count_word(v[4 * u + e], cand);
+        }
+      }
+      if (kth_block_sum(c, part, bit & 1) >= k) prefix = cand;
+    }
   } else {
-    t = kth_prefix<false>(bq, nblk, (uint32_t)top_k, part);
+    const int64_t n8 = nblk & ~(int64_t)7;   // whole 16-byte groups; the tail is checked per value
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t cand = prefix | (1u << bit);
+      uint32_t c = 0u;
+      for (int64_t i = (int64_t)tid * 8; i < n8; i += kKthThreads * 8) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(bq + i);
+        c += kth_count_word(w.x, cand) + kth_count_word(w.y, cand) + kth_count_word(w.z, cand) +
+             kth_count_word(w.w, cand);
+      }
+      if (n8 < nblk && tid == (int)((n8 / 8) % kKthThreads)) {
+        for (int64_t i = n8; i < nblk; ++i) c += bq[i] >= cand ? 1u : 0u;
+      }
+      if (kth_block_sum(c, part, bit & 1) >= k) prefix = cand;
+    }
   }
-  if (tid == 0) thr[q] = t << 16;
+  if (tid == 0) thr[q] = prefix << 16;
 }
 
 // Per query: the exact Top-K among the candidates of its slot regions.  The
@@ -678,9 +703,7 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
   if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 1, s);
   else launch_gemm_scores<4>(a, L, 1, s);
   if (after != nullptr) (void)hipEventRecord(after, s);
-  const size_t kth_lds =
-      (size_t)std::min<int64_t>(L.bmax_row, kKthLdsMax) * sizeof(uint16_t);
-  hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), kth_lds, s,
+  hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
                      reinterpret_cast<const uint16_t *>(w + L.bmax), L.bmax_row, a.q_pos, a.top_k,
                      reinterpret_cast<uint32_t *>(w + L.thr));
   if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 2, s);
