@@ -20,8 +20,9 @@
 //   * Q is rounded once to fp16 (exact for bf16 values of magnitude 2^-14 to
 //     65504; smaller ones move by less than 2^-25).
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_f16 (fp32 accumulation); exp2-based
-//     softmax statistics per head; P rounded to fp16; O += P V with
-//     v_mfma_f32_16x16x32_f16.
+//     softmax statistics per head; P rounded to fp16; O^T += V^T P^T with
+//     v_mfma_f32_16x16x32_f16 (a lane's output column is its own head, so the
+//     softmax rescale and normalization need no cross-lane moves).
 // attn_combine_kernel: merges the splits of each (query, head).
 #include <algorithm>
 
@@ -172,7 +173,7 @@ __device__ __forceinline__ float lane_pair_sum32(float x) {
 }
 
 // One sub-chunk of 64 rows from LDS: S^T on matrix cores, online softmax,
-// O += P V.  scale_log2 = |softmax scale| * log2(e) (a negative scale was
+// O^T += V^T P^T.  scale_log2 = |softmax scale| * log2(e) (a negative scale was
 // folded into Q), so the running maximum of the scaled scores is the scaled
 // maximum of the raw ones.
 __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf,
@@ -255,19 +256,16 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
   lsum = lane_pair_sum32(lsum);
   l_run = l_run * alpha + lsum;
   m_run = m_new;
-  // O rows are heads 16*wave + 4g + i: fetch their alpha from lane 4g + i.
-  // Once the running maxima settle, alpha is 1 everywhere and O is left alone.
+  // O^T columns are this lane's head.  Once the running maxima settle, alpha
+  // is 1 everywhere and O is left alone.
   if (__ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][i] *= a;
-    }
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
   }
 
-  // O += P V: k-slice sg covers tiles 2sg, 2sg+1; lane group g holds rows
-  // 32sg + 4g + 0..3 and 32sg + 16 + 4g + 0..3
+  // O^T += V^T P^T (so that a lane's output column is its own head): k-slice
+  // sg covers tiles 2sg, 2sg+1; lane group g holds rows 32sg + 4g + 0..3 and
+  // 32sg + 16 + 4g + 0..3 of both operands
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg) {
     const f16x8 pa = __builtin_bit_cast(
@@ -281,7 +279,7 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
       const uint2 a = *reinterpret_cast<const uint2 *>(vrow);
       const uint2 b = *reinterpret_cast<const uint2 *>(vrow + 16);
       const f16x8 vb = __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb, pa, o[dt], 0, 0, 0);
     }
   }
 }
@@ -372,32 +370,21 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
     attend_sub(kq, vt, rows, (c + 1) * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
   }
 
-  // O rows = heads 16*wave + 4g + i, column d = 16 dt + l16
+  // O^T tile dt: this lane's head 16*wave + l16, channels 16 dt + 4g + 0..3
+  const int head = wave * 16 + l16;
   if (splits == 1) {
-    float inv[4];
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    float *oq = out + ((int64_t)q * n_heads + head) * 128 + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float l = __shfl(l_run, 4 * g + i, 64);
-      inv[i] = l > 0.0f ? 1.0f / l : 0.0f;
-    }
-    const int64_t obase = (int64_t)q * n_heads;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        out[(obase + wave * 16 + 4 * g + i) * 128 + dt * 16 + l16] = o[dt][i] * inv[i];
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4 *>(oq + dt * 16) = o[dt] * inv;
     if (lse != nullptr && g == 0)
-      lse[obase + wave * 16 + l16] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+      lse[(int64_t)q * n_heads + head] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
     return;
   }
   const int64_t pbase = ((int64_t)q * splits + split) * n_heads;
+  float *pq = part_acc + (pbase + head) * 128 + 4 * g;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int head = wave * 16 + 4 * g + i;
-      part_acc[(pbase + head) * 128 + dt * 16 + l16] = o[dt][i];
-    }
+  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4 *>(pq + dt * 16) = o[dt];
   if (g == 0) part_ml[pbase + wave * 16 + l16] = make_float2(m_run, l_run);
 }
 
