@@ -297,3 +297,33 @@ def test_matrix_core_tie_heavy(distinct, cap):
         _relaxed_query(oc, i, qpos[i], O.query_index_values(qi[i], "fp8"), got[i], 500)
     if distinct == 1:   # identical keys give identical sums: ties to the lower position
         assert list(got[0]) == list(range(500)) and list(got[1]) == list(range(500))
+
+
+def test_matrix_core_long_rows():
+    # positions past 524288: a query's block maxima (one per 16 positions) no
+    # longer fit the threshold kernel's registers and are counted from global
+    # memory; a query below the limit in the same call keeps the register path
+    context = 540000
+    qpos = [539999, 530000, 100000]
+    announce(f"matrix-core long rows context={context}")
+    m = lib()
+    wl = synth.workload("decode_1m", context=context, batch=1)
+    gc = m.Cache(1, context, idx_heads=8, idx_k_dtype="fp8")
+    oc = O.OracleCache(1, context, idx_heads=8, idx_k_dtype="fp8", lazy=True)
+    data = synth.gen_batch(wl)
+    seq, pos = np.zeros(context, np.int32), np.arange(context, dtype=np.int32)
+    m.csa2_kv_append(gc, dev_u16(data.k[0]), dev_u16(data.v[0]), dev_u16(data.ik[0]),
+                     dev_i32(seq), dev_i32(pos))
+    oc.append(data.k[0], data.v[0], data.ik[0], seq, pos)
+    del data
+    rng = np.random.default_rng(context)
+    qi = synth.f32_to_bf16_bits(rng.standard_normal((len(qpos), 8, 64)).astype(np.float32))
+    top_k = 2048
+    tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qi), dev_i32([0] * len(qpos)), dev_i32(qpos),
+                              top_k, q_dtype="fp8")
+    torch.cuda.synchronize()
+    got = host(tk)
+    swaps = 0
+    for i, p in enumerate(qpos):
+        swaps += _relaxed_query(oc, 0, p, O.query_index_values(qi[i], "fp8"), got[i], top_k)
+    announce(f"  swaps at the K-th score: {swaps}")
