@@ -55,10 +55,11 @@ constexpr int kBlkGroup = 16;           // block maxima a lane collects before o
 constexpr int kRangeAlign = kBlk * kBlkGroup;   // positions per range: a multiple of this
 constexpr int kDmaPerTile = 2;          // next-stage pieces a thread loads per row tile
 constexpr int kKthThreads = 256;
-// Candidates a gemm_resolve_kernel keeps in LDS: ~K(1 + a few %) with continuous
-// scores; the smaller footprint fits three workgroups per CU (thousands of
-// queries per call).
-constexpr int kGemmResolveCap = 4096;
+// Candidates a gemm_resolve_kernel keeps in LDS: ~K(1 + 10 %) with continuous
+// scores for K = 2048 (blocks holding two candidates, the threshold's 16-bit
+// granularity); under 40 KB of LDS per workgroup four share a CU (thousands
+// of queries per call).  More candidates take the streamed path.
+constexpr int kGemmResolveCap = 2560;
 constexpr int kGemmResolveThreads = 256;
 constexpr int kGemmEarlySlots = 16;     // candidate slots per resolve thread read before the counts
 constexpr int kKthRegMax = 32768;       // block maxima a gemm_kth_kernel keeps in registers
