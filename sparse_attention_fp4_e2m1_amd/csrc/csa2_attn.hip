@@ -35,6 +35,7 @@ constexpr int kSub = 64;                      // rows per sub-chunk
 constexpr int kVtPitch = kSub + 4;            // fp16 elements per LDS row of V^T
 constexpr int kMaxRowsPerSplit = 2048;
 constexpr int kTargetGroups = 256;            // workgroups aimed for (one per CU)
+constexpr int kTwoSubMinGroups = 128;         // see rows_per_split
 constexpr int kMaxSplits = 256;               // splits of one query, at most
 constexpr int kCombineBatch = 32;             // split outputs per round of combine loads
 static_assert(kTargetGroups <= kMaxSplits && (65536 + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit <= kMaxSplits,
@@ -458,11 +459,14 @@ __global__ void __launch_bounds__(512) attn_combine_kernel(
 
 // Rows per split: as many as possible (one split needs no combine) while the
 // grid still has kTargetGroups workgroups, at most kMaxRowsPerSplit, a
-// multiple of the sub-chunk.
+// multiple of the sub-chunk.  Splits of one sub-chunk become two (whose
+// gathers overlap) when that still leaves kTwoSubMinGroups workgroups.
 int32_t rows_per_split(int32_t nq, int32_t top_k) {
   const int32_t subs = (top_k + kSub - 1) / kSub;
   int32_t splits = (kTargetGroups + nq - 1) / nq;
   splits = std::max(1, std::min(splits, subs));
+  if (subs / splits < 2 && (int64_t)nq * (subs / 2) >= kTwoSubMinGroups)
+    splits = std::max(1, subs / 2);
   int32_t per = (subs + splits - 1) / splits;
   per = std::min(per, kMaxRowsPerSplit / kSub);
   return per * kSub;
