@@ -672,14 +672,18 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     constexpr int kEnt = kDirectIters * kWaves;
     constexpr int kPerLane = (kEnt + kWave - 1) / kWave;   // totals per lane in the one-wave scan
     static_assert(kEnt + 1 <= kSelectThreads, "totals and the sum fit goff");
+    // only the iterations that hold keys (uniform); the totals of the others count as 0
+    const int nd = (int)n;   // <= kDirectMax
+    const int nit = (nd + 4 * kSelectThreads - 1) / (4 * kSelectThreads);
     uint32_t wexcl[kDirectIters];
 #pragma unroll
     for (int it = 0; it < kDirectIters; ++it) {
-      const int64_t i0 = (int64_t)it * 4 * kSelectThreads + 4 * tid;
+      if (it >= nit) break;
+      const int i0 = it * 4 * kSelectThreads + 4 * tid;
       const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
       uint32_t c = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c += (th.keff > 0 && i0 + e < n && k4[e] >= thr) ? 1u : 0u;
+      for (int e = 0; e < 4; ++e) c += (th.keff > 0 && i0 + e < nd && k4[e] >= thr) ? 1u : 0u;
       const uint32_t inc = wave_inclusive_scan(c);
       wexcl[it] = inc - c;
       if (lane == kWave - 1) goff[it * kWaves + wave] = inc;
@@ -690,7 +694,7 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
 #pragma unroll
       for (int u = 0; u < kPerLane; ++u) {
         const int e = kPerLane * lane + u;
-        v[u] = e < kEnt ? goff[e] : 0u;
+        v[u] = (e < kEnt && e / kWaves < nit) ? goff[e] : 0u;
         sum += v[u];
       }
       uint32_t ex = wave_inclusive_scan(sum) - sum;
@@ -706,12 +710,13 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     carry = goff[kEnt];
 #pragma unroll
     for (int it = 0; it < kDirectIters; ++it) {
-      const int64_t i0 = (int64_t)it * 4 * kSelectThreads + 4 * tid;
+      if (it >= nit) break;
+      const int i0 = it * 4 * kSelectThreads + 4 * tid;
       const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
       uint32_t o = goff[it * kWaves + wave] + wexcl[it];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (th.keff > 0 && i0 + e < n && k4[e] >= thr) {
+        if (th.keff > 0 && i0 + e < nd && k4[e] >= thr) {
           if (o < kResolveCap) {
             lkey[o] = k4[e];
             lid[o] = (int32_t)(i0 + e);

@@ -145,23 +145,25 @@ struct LdsCands {     // candidates gathered in index order
   __device__ int64_t id(int64_t i) const { return ids[i]; }
 };
 
+// An emitter turns a selected candidate into output entries in two steps:
+// value(id) (for pool ids the pool lookup, a global load, issued before the
+// compaction's scans so that its latency overlaps them), then store(o, v).
 template <int kMode>
 struct Emit {
   int32_t *out;          // this query's output row
   const int32_t *pool;   // this query's pool row (kOutPoolIds)
   int32_t qp;
   uint32_t limit;        // entries in the row (a guard: o < keff <= limit by construction)
-  __device__ void operator()(uint32_t o, int64_t id) const {
+  __device__ int64_t value(int64_t id) const { return kMode == kOutPoolIds ? (int64_t)pool[id] : id; }
+  __device__ void store(uint32_t o, int64_t v) const {
     if (o >= limit) return;
-    if (kMode == kOutPositions) {
-      out[o] = (int32_t)id;
-    } else if (kMode == kOutPoolIds) {
-      out[o] = pool[id];
-    } else {
+    if (kMode == kOutPoolBlocks) {
       for (int m = 0; m < kPoolBlock; ++m) {
-        const int64_t p = id * kPoolBlock + m;
+        const int64_t p = v * kPoolBlock + m;
         out[(int64_t)o * kPoolBlock + m] = p <= qp ? (int32_t)p : -1;
       }
+    } else {
+      out[o] = (int32_t)v;
     }
   }
 };
@@ -173,17 +175,18 @@ struct EmitAny {
   const int32_t *pool;
   int32_t qp;
   uint32_t limit;        // entries (blocks) in the row; o < keff <= limit by construction
-  __device__ void operator()(uint32_t o, int64_t id) const {
+  __device__ int64_t value(int64_t id) const {
+    return mode == kOutPoolIds ? (int64_t)pool[id] : id;
+  }
+  __device__ void store(uint32_t o, int64_t v) const {
     if (o >= limit) return;
-    if (mode == kOutPositions) {
-      out[o] = (int32_t)id;
-    } else if (mode == kOutPoolIds) {
-      out[o] = pool[id];
-    } else {
+    if (mode == kOutPoolBlocks) {
       for (int m = 0; m < kPoolBlock; ++m) {
-        const int64_t p = id * kPoolBlock + m;
+        const int64_t p = v * kPoolBlock + m;
         out[(int64_t)o * kPoolBlock + m] = p <= qp ? (int32_t)p : -1;
       }
+    } else {
+      out[o] = (int32_t)v;
     }
   }
 };
@@ -292,10 +295,12 @@ __device__ void select_core(const Src &src, int64_t n, uint32_t keff, uint32_t b
     const int64_t i0 = base + 4 * tid;
     uint32_t k4[4];
     bool in4[4];
+    int64_t v4[4];   // output values, loaded before the scans
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       in4[u] = i0 + u < n;
       k4[u] = in4[u] ? src.key(i0 + u) : 0u;
+      v4[u] = in4[u] ? emit.value(src.id(i0 + u)) : 0;
     }
     bool sel[4];
     uint32_t nsel = 0;
@@ -324,7 +329,7 @@ __device__ void select_core(const Src &src, int64_t n, uint32_t keff, uint32_t b
     uint32_t o = carry_sel + block_exclusive_scan(nsel, scratch, tot_sel);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (sel[u]) emit(o++, src.id(i0 + u));
+      if (sel[u]) emit.store(o++, v4[u]);
     carry_sel += tot_sel;
   }
 }
