@@ -97,7 +97,7 @@ __device__ __forceinline__ void gather(Gathered<kThreads> &gd, const int32_t *ro
   }
 }
 
-// Dequantizes one gathered sub-chunk into LDS: K^ as bf16 MFMA A fragments
+// Dequantizes one gathered sub-chunk into LDS: K^ as fp16 MFMA A fragments
 // kq[tile][k-step][lane] (16 B each: k-step s of lane group g is channels
 // 32g + 8s .. +7), V^ transposed as fp16 vt[channel][row].
 template <int kThreads>
