@@ -198,7 +198,7 @@ size_t csa2_sparse_attn_workspace(const csa2_cache *cache, int32_t nq, int32_t n
  *              z_j = softmax_scale * q_h . K_j, K and V dequantized exactly.
  *   lse        [nq][n_heads] fp32 natural-log sum of exp(z_j), or NULL.
  * An empty selection gives out = 0 and lse = -inf.  Accumulation is fp32 on
- * matrix cores (bf16 q.K products, fp16 probabilities times V).
+ * matrix cores (fp16 q.K products, fp16 probabilities times V).
  * Supported: n_heads a multiple of 16 up to 128; dk = dv = 128.
  * Device preconditions: 0 <= q_seq < batch; topk entries < capacity.
  * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED,
@@ -208,6 +208,66 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
                              const int32_t *q_seq, int32_t nq, const int32_t *topk, int32_t top_k,
                              float softmax_scale, float *out, float *lse, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/*
+ * The local sliding-window KV of one layer (aiwiki "DeepSeek V4.1-Flash",
+ * section "Compressed Sparse Attention 2": besides its query, every CSA2 layer
+ * creates its own local sliding-window keys and values; section "KV-cache
+ * formats and bounded replay": that local window KV is stored in FP8).
+ * Caller-owned device memory, a ring of `window` slots per sequence:
+ *   k, v   [batch][window][dk], [batch][window][dv] bytes: E4M3 codes of the
+ *          bf16 rows (round to nearest even, saturating at +-448, sign kept,
+ *          no scale).
+ *   pos    [batch][window] int32: the position a slot holds, -1 = none (fill
+ *          with -1 before first use).
+ * Position p of sequence s lives in slot p % window.
+ * Supported: dk = dv = 128, window 1 .. 1024.
+ */
+typedef struct csa2_local_cache {
+  uint8_t *k;
+  uint8_t *v;
+  int32_t *pos;
+  int32_t batch;
+  int32_t window;
+  int32_t dk;
+  int32_t dv;
+} csa2_local_cache;
+
+/*
+ * Quantize-and-append n rows into the local window (E4M3 codes as above).
+ *   k, v       [n][dk], [n][dv] bf16 bits.
+ *   seq, pos   [n] int32: row r is position pos[r] of sequence seq[r]; it
+ *              replaces whatever slot pos[r] % window held.
+ * Device preconditions: 0 <= seq[r] < batch, pos[r] >= 0; no two rows of one
+ * call share a (seq, slot).
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (n < 0), CSA2_ERR_UNSUPPORTED, CSA2_ERR_HIP.
+ * n = 0 is a no-op returning CSA2_OK.
+ */
+csa2_status csa2_local_append(const csa2_local_cache *cache, const uint16_t *k, const uint16_t *v,
+                              const int32_t *seq, const int32_t *pos, int32_t n, void *stream);
+
+/*
+ * The local window branch, merged into the sparse branch's result (the same
+ * softmax over both sets of rows, through the sparse branch's lse).
+ *   q          [nq][n_heads][dk] bf16 bits (the same queries as the sparse call).
+ *   q_seq, q_pos [nq] int32: the window rows of a query are the positions
+ *              max(0, q_pos - window + 1) .. q_pos of its sequence whose slot
+ *              holds that position.
+ *   out, lse   on entry csa2_sparse_attn's out [nq][n_heads][dv] and lse
+ *              [nq][n_heads]; on return the softmax attention over the union
+ *              of the selected FP4 rows and the window's FP8 rows:
+ *              out = sum_j softmax(z)_j V_j, lse = ln sum_j exp(z_j), with
+ *              z_j = softmax_scale * q_h . K_j over both sets.
+ * Rows of both sets are different cached values (the global FP4 KV and the
+ * layer's own FP8 window), so a position in both counts twice.  Accumulation
+ * is fp32 on matrix cores (fp16 q.K products, fp16 probabilities times V).
+ * Supported: n_heads a multiple of 16 up to 128; dk = dv = 128.
+ * Device preconditions: 0 <= q_seq < batch, q_pos >= 0.
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED, CSA2_ERR_HIP.
+ */
+csa2_status csa2_local_attn(const csa2_local_cache *cache, const uint16_t *q, int32_t n_heads,
+                            const int32_t *q_seq, const int32_t *q_pos, int32_t nq,
+                            float softmax_scale, float *out, float *lse, void *stream);
 
 /*
  * Profiling hook for callers that measure the index scan against the HBM

@@ -372,6 +372,92 @@ def sparse_attention(q_bits: np.ndarray, cache: OracleCache, seq: int, topk: np.
 
 
 # ---------------------------------------------------------------------------
+# The local sliding-window branch
+# ---------------------------------------------------------------------------
+
+class OracleLocalCache:
+    """One layer's local sliding-window K and V in FP8: a ring of `window`
+    slots per sequence, position p in slot p % window, with the position each
+    slot holds (-1 = none).
+
+    Source: aiwiki "DeepSeek V4.1-Flash", section "Compressed Sparse Attention
+    2" (every CSA2 layer creates its own local sliding-window keys and values)
+    and section "KV-cache formats and bounded replay" (the local window KV is
+    stored in FP8).  Readings (the pages give no format detail): each bf16
+    element becomes its OCP E4M3 code (round to nearest even, saturating at
+    448, sign kept), with no scale; the window of a query at position p is
+    positions max(0, p - window + 1) .. p.
+    """
+
+    def __init__(self, batch, window, dk=128, dv=128):
+        self.batch, self.window, self.dk, self.dv = batch, window, dk, dv
+        self.k = np.zeros((batch, window, dk), np.uint8)
+        self.v = np.zeros((batch, window, dv), np.uint8)
+        self.pos = np.full((batch, window), -1, np.int64)
+
+    def append(self, k_bits, v_bits, seq, pos):
+        enc = _e4m3_tables()[0]
+        k_bits = np.asarray(k_bits, np.uint16)
+        v_bits = np.asarray(v_bits, np.uint16)
+        for r, (b, p) in enumerate(zip(np.asarray(seq), np.asarray(pos))):
+            s = int(p) % self.window
+            self.k[b, s] = enc[k_bits[r]]
+            self.v[b, s] = enc[v_bits[r]]
+            self.pos[b, s] = int(p)
+
+    def window_rows(self, b, q_pos):
+        """(positions, K, V) of the window of a query at q_pos in sequence b:
+        the positions whose slot holds them, ascending; K, V float64."""
+        val = _e4m3_tables()[1]
+        want = np.arange(max(0, q_pos - self.window + 1), q_pos + 1)
+        slots = want % self.window
+        have = self.pos[b, slots] == want
+        sl = slots[have]
+        return want[have], val[self.k[b, sl]].astype(np.float64), val[self.v[b, sl]].astype(np.float64)
+
+
+def attention_with_window(q_bits: np.ndarray, cache: OracleCache, seq: int, topk: np.ndarray,
+                          local: OracleLocalCache, q_pos: int, scale: Optional[float] = None):
+    """Softmax attention of every head over the selected FP4 rows and the
+    layer's FP8 window rows together, in float64.
+
+    Source: as sparse_attention for the selected rows; aiwiki "Compressed
+    Sparse Attention 2" for the local window every layer also attends over.
+    One softmax over both sets: z_j = scale * (q_h . K_j) for the entries of
+    `topk` (>= 0) and the window rows, o_h = sum_j softmax(z)_j V_j,
+    lse_h = ln sum_j exp(z_j).  Reading: the two sets are different cached
+    values (the shared FP4 global KV, the layer's own FP8 window) side by side,
+    so a position in both counts twice; no positional term.
+
+    q_bits: bf16 bits [heads, dk].  Returns (out [heads, dv], lse [heads]).
+    """
+    q = bf16_value(q_bits)
+    H = q.shape[0]
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(cache.dk)))
+    rows = np.asarray(topk, np.int64)
+    rows = rows[rows >= 0]
+    ks, vs = [], []
+    if len(rows):
+        k, v = cache.kv_values(seq, rows)
+        ks.append(k)
+        vs.append(v)
+    _, kl, vl = local.window_rows(seq, q_pos)
+    if len(kl):
+        ks.append(kl)
+        vs.append(vl)
+    if not ks:
+        return np.zeros((H, cache.dv)), np.full(H, -np.inf)
+    k = np.concatenate(ks)
+    v = np.concatenate(vs)
+    z = (q @ k.T) * scale
+    m = z.max(axis=1, keepdims=True)
+    p = np.exp(z - m)
+    ell = p.sum(axis=1, keepdims=True)
+    return (p @ v) / ell, (m + np.log(ell))[:, 0]
+
+
+# ---------------------------------------------------------------------------
 # A whole step over a layer stack
 # ---------------------------------------------------------------------------
 

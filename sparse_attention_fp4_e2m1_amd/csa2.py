@@ -33,6 +33,12 @@ class csa2_cache(ctypes.Structure):
                 ("idx_k_dtype", ctypes.c_int32)]
 
 
+class csa2_local_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("window", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -46,6 +52,8 @@ def _load():
         "csa2_index_topk": (I32, [C, I32, P, I32, P, P, I32, I32, P, I32, I32, P, P, P, P, SZ, P]),
         "csa2_sparse_attn_workspace": (SZ, [C, I32, I32, I32]),
         "csa2_sparse_attn": (I32, [C, P, I32, P, I32, P, I32, F32, P, P, P, SZ, P]),
+        "csa2_local_append": (I32, [ctypes.POINTER(csa2_local_cache), P, P, P, P, I32, P]),
+        "csa2_local_attn": (I32, [ctypes.POINTER(csa2_local_cache), P, I32, P, P, I32, F32, P, P, P]),
         "csa2_profile_index_scan": (None, [P, P]),
         "csa2_strerror": (ctypes.c_char_p, [I32]),
         "csa2_abi_version": (ctypes.c_int, []),
@@ -206,4 +214,52 @@ def csa2_sparse_attn(cache: Cache, q, q_seq, topk, softmax_scale: Optional[float
     _check(LIB.csa2_sparse_attn(cache.ref, _ptr(q), n_heads, _ptr(q_seq), nq, _ptr(topk), top_k,
                                 float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                 workspace.numel(), _stream(stream)), "csa2_sparse_attn")
+    return out, lse
+
+
+class LocalCache:
+    """One layer's local sliding-window KV: E4M3 codes in a ring of `window`
+    slots per sequence, with the position each slot holds (-1 = none)."""
+
+    def __init__(self, batch: int, window: int, dk: int = 128, dv: int = 128, device="cuda"):
+        self.batch, self.window, self.dk, self.dv = batch, window, dk, dv
+        dev = torch.device(device)
+        self.k = torch.zeros((batch, window, dk), dtype=torch.uint8, device=dev)
+        self.v = torch.zeros((batch, window, dv), dtype=torch.uint8, device=dev)
+        self.pos = torch.full((batch, window), -1, dtype=torch.int32, device=dev)
+        self.device = self.k.device
+        self._c = csa2_local_cache(self.k.data_ptr(), self.v.data_ptr(), self.pos.data_ptr(), batch,
+                                   window, dk, dv)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._c)
+
+
+def csa2_local_append(cache: LocalCache, k, v, seq, pos, stream=None) -> None:
+    n = k.shape[0]
+    d = cache.device
+    _need(k, "k", _B16, (n, cache.dk), d)
+    _need(v, "v", _B16, (n, cache.dv), d)
+    _need(seq, "seq", _I32, (n,), d)
+    _need(pos, "pos", _I32, (n,), d)
+    _check(LIB.csa2_local_append(cache.ref, _ptr(k), _ptr(v), _ptr(seq), _ptr(pos), n,
+                                 _stream(stream)), "csa2_local_append")
+
+
+def csa2_local_attn(cache: LocalCache, q, q_seq, q_pos, out, lse,
+                    softmax_scale: Optional[float] = None, stream=None):
+    """Merges the window branch into (out, lse) of csa2_sparse_attn, in place."""
+    d = cache.device
+    nq, n_heads = q.shape[0], q.shape[1]
+    _need(q, "q", _B16, (nq, n_heads, cache.dk), d)
+    _need(q_seq, "q_seq", _I32, (nq,), d)
+    _need(q_pos, "q_pos", _I32, (nq,), d)
+    _need(out, "out", (torch.float32,), (nq, n_heads, cache.dv), d)
+    _need(lse, "lse", (torch.float32,), (nq, n_heads), d)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(cache.dk)
+    _check(LIB.csa2_local_attn(cache.ref, _ptr(q), n_heads, _ptr(q_seq), _ptr(q_pos), nq,
+                               float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "csa2_local_attn")
     return out, lse

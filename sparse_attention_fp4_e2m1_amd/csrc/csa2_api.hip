@@ -19,6 +19,13 @@ csa2_status check_cache(const csa2_cache *c, bool need_idx) {
 
 constexpr int32_t kMaxTopK = 1 << 16;
 
+csa2_status check_local(const csa2_local_cache *c) {
+  if (c == nullptr || c->k == nullptr || c->v == nullptr || c->pos == nullptr) return CSA2_ERR_NULL;
+  if (c->batch < 1 || c->window < 1 || c->window > kMaxLocalWindow) return CSA2_ERR_SHAPE;
+  if (c->dk != 128 || c->dv != 128) return CSA2_ERR_UNSUPPORTED;
+  return CSA2_OK;
+}
+
 csa2_status check_topk_args(const csa2_cache *cache, csa2_mode mode, int32_t nq, int32_t top_k,
                             int32_t pool_len, int32_t pool_blocks) {
   csa2_status st = check_cache(cache, mode != CSA2_REUSE);
@@ -144,6 +151,34 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
   if (workspace == nullptr || workspace_bytes < L.total) return CSA2_ERR_WORKSPACE;
   if (launch_sparse_attn(*cache, q, n_heads, q_seq, nq, topk, top_k, softmax_scale, out, lse,
                          static_cast<uint8_t *>(workspace), L, (hipStream_t)stream) != hipSuccess)
+    return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
+csa2_status csa2_local_append(const csa2_local_cache *cache, const uint16_t *k, const uint16_t *v,
+                              const int32_t *seq, const int32_t *pos, int32_t n, void *stream) {
+  csa2_status st = check_local(cache);
+  if (st != CSA2_OK) return st;
+  if (n < 0) return CSA2_ERR_SHAPE;
+  if (n == 0) return CSA2_OK;
+  if (k == nullptr || v == nullptr || seq == nullptr || pos == nullptr) return CSA2_ERR_NULL;
+  if (launch_local_append(*cache, k, v, seq, pos, n, (hipStream_t)stream) != hipSuccess)
+    return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
+csa2_status csa2_local_attn(const csa2_local_cache *cache, const uint16_t *q, int32_t n_heads,
+                            const int32_t *q_seq, const int32_t *q_pos, int32_t nq,
+                            float softmax_scale, float *out, float *lse, void *stream) {
+  csa2_status st = check_local(cache);
+  if (st != CSA2_OK) return st;
+  if (n_heads < 16 || n_heads > 128 || n_heads % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  if (nq < 0 || nq > 65535) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (q == nullptr || q_seq == nullptr || q_pos == nullptr || out == nullptr || lse == nullptr)
+    return CSA2_ERR_NULL;
+  if (launch_local_attn(*cache, q, n_heads, q_seq, q_pos, nq, softmax_scale, out, lse,
+                        (hipStream_t)stream) != hipSuccess)
     return CSA2_ERR_HIP;
   return CSA2_OK;
 }

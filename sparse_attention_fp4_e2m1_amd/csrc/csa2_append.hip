@@ -10,6 +10,11 @@
 // One wave per appended row.  Lanes 0..15 each own one 16-channel block
 // (8 K blocks, then 8 V blocks): 32 B of bf16 in, 8 B of codes + 1 scale byte
 // out.  All 64 lanes then move the row's index keys (bf16 copy or E4M3 cast).
+//
+// aiwiki "DeepSeek V4.1-Flash", "Compressed Sparse Attention 2" and "KV-cache
+// formats and bounded replay": each layer's own local sliding-window K and V
+// are kept in FP8; local_append_kernel casts them to E4M3 into a ring of
+// window slots per sequence.
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -112,7 +117,45 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
   }
 }
 
+// Local window rows: E4M3 codes of every bf16 element (no scale), into slot
+// pos % window; one wave per row, two elements per lane per tensor.
+__global__ void __launch_bounds__(256) local_append_kernel(
+    uint8_t *__restrict__ lk, uint8_t *__restrict__ lv, int32_t *__restrict__ lpos,
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, int32_t n, int32_t window) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (row >= n) return;
+  const int32_t p = pos[row];
+  const int64_t slot = (int64_t)seq[row] * window + p % window;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t *src = (t == 0 ? k : v) + (int64_t)row * 128 + 2 * lane;
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(src);
+    uint32_t codes = 0u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t hb = (w >> (16 * i)) & 0xFFFFu;
+      const float f = __uint_as_float(hb << 16);
+      codes |= (e4m3_from_f32_nonneg(fabsf(f)) | ((hb >> 8) & 0x80u)) << (8 * i);
+    }
+    uint8_t *dst = (t == 0 ? lk : lv) + slot * 128 + 2 * lane;
+    *reinterpret_cast<uint16_t *>(dst) = (uint16_t)codes;
+  }
+  if (lane == 0) lpos[slot] = p;
+}
+
 }  // namespace
+
+hipError_t launch_local_append(const csa2_local_cache &c, const uint16_t *k, const uint16_t *v,
+                               const int32_t *seq, const int32_t *pos, int32_t n,
+                               hipStream_t stream) {
+  const int rows_per_block = 4;
+  hipLaunchKernelGGL(local_append_kernel, dim3((n + rows_per_block - 1) / rows_per_block),
+                     dim3(rows_per_block * kWave), 0, stream, c.k, c.v, c.pos, k, v, seq, pos, n,
+                     c.window);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const csa2_cache &c, const uint16_t *k, const uint16_t *v,
                             const uint16_t *idx_in, const int32_t *seq, const int32_t *pos,

@@ -457,6 +457,135 @@ __global__ void __launch_bounds__(512) attn_combine_kernel(
   if (lse != nullptr && d == 0) lse[oi] = lse_sh[hl];
 }
 
+// The local window branch (aiwiki "DeepSeek V4.1-Flash", "Compressed Sparse
+// Attention 2": every layer's own sliding-window K and V; "KV-cache formats
+// and bounded replay": kept in FP8).  One workgroup per query, one wave per 16
+// heads; the window's rows (ascending positions, -1 where the slot holds
+// another position) in sub-chunks of 64: the E4M3 codes convert exactly to
+// fp16 into the LDS layouts of the FP4 path and attend_sub runs over them.
+// The result is merged into the sparse branch's (out, lse) in place:
+//   lse = ln(e^lse_s + e^lse_l),
+//   out = out_s e^(lse_s - lse) + out_l e^(lse_l - lse).
+template <int kWaves>
+__global__ void __launch_bounds__(kWaves * 64) local_attn_kernel(
+    const uint8_t *__restrict__ lk, const uint8_t *__restrict__ lv,
+    const int32_t *__restrict__ lpos, int32_t window, const uint16_t *__restrict__ qg,
+    int32_t n_heads, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
+    float scale_log2, bool q_negate, float *__restrict__ out, float *__restrict__ lse) {
+  constexpr int kThreads = kWaves * 64;
+  __shared__ int32_t rows[kMaxLocalWindow + kSub];   // slot of each row, -1: no row
+  __shared__ uint4 kq[4 * 4 * 64];
+  __shared__ _Float16 vt[128 * kVtPitch];
+
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int32_t p = q_pos[q];
+  const int nrows = min(window, p + 1);   // positions p - nrows + 1 .. p
+  const int nsub = (nrows + kSub - 1) / kSub;
+  const int64_t sbase = (int64_t)q_seq[q] * window;
+  for (int r = tid; r < nsub * kSub; r += kThreads) {
+    int32_t slot = -1;
+    if (r < nrows) {
+      const int32_t pr = p - nrows + 1 + r;
+      const int32_t sl = pr % window;
+      if (lpos[sbase + sl] == pr) slot = sl;
+    }
+    rows[r] = slot;
+  }
+
+  f16x8 qf[4];
+  {
+    const uint16_t *qp = qg + ((int64_t)q * n_heads + wave * 16 + l16) * 128 + 32 * g;
+    const uint32_t flip = q_negate ? 0x80008000u : 0u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 raw = *reinterpret_cast<const uint4 *>(qp + 8 * s);
+      const uint32_t w[4] = {raw.x ^ flip, raw.y ^ flip, raw.z ^ flip, raw.w ^ flip};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 h = __builtin_convertvector(
+            (f32x2{__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xFFFF0000u)}), f16x2);
+        qf[s][2 * e] = h[0];
+        qf[s][2 * e + 1] = h[1];
+      }
+    }
+  }
+  __syncthreads();
+
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  for (int c = 0; c < nsub; ++c) {
+    // K^: fragment (tile t, k-step s, lane l) = row 16t + l%16, channels
+    // 32(l/16) + 8s .. +7
+    for (int item = tid; item < 4 * 4 * 64; item += kThreads) {
+      const int t = item >> 8, s = (item >> 6) & 3, l = item & 63;
+      const int slot = max(rows[c * kSub + 16 * t + (l & 15)], 0);
+      const uint2 w = *reinterpret_cast<const uint2 *>(lk + (sbase + slot) * 128 + 32 * (l >> 4) + 8 * s);
+      kq[(t * 4 + s) * 64 + l] = make_uint4(
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true)));
+    }
+    // V^ transposed: item (row pair pr, block b) = rows 2pr, 2pr+1, channels
+    // 16b .. 16b+15, written as (row 2pr, row 2pr+1) fp16 pairs per channel
+    for (int item = tid; item < 32 * 8; item += kThreads) {
+      const int pr = item & 31, b = item >> 5;
+      const int sa = max(rows[c * kSub + 2 * pr], 0), sb = max(rows[c * kSub + 2 * pr + 1], 0);
+      const uint4 wa = *reinterpret_cast<const uint4 *>(lv + (sbase + sa) * 128 + 16 * b);
+      const uint4 wb = *reinterpret_cast<const uint4 *>(lv + (sbase + sb) * 128 + 16 * b);
+      const uint32_t xa[4] = {wa.x, wa.y, wa.z, wa.w}, xb[4] = {wb.x, wb.y, wb.z, wb.w};
+      uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + 2 * pr);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a[2] = {
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xa[w], 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xa[w], 1.0f, true))};
+        const uint32_t bb[2] = {
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xb[w], 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xb[w], 1.0f, true))};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // channels 4w + 2h, 4w + 2h + 1 of the block
+          const int e = 2 * w + h;
+          dst[((2 * e) * kVtPitch) / 2] = __builtin_amdgcn_perm(bb[h], a[h], 0x05040100u);
+          dst[((2 * e + 1) * kVtPitch) / 2] = __builtin_amdgcn_perm(bb[h], a[h], 0x07060302u);
+        }
+      }
+    }
+    __syncthreads();
+    attend_sub(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+    __syncthreads();   // the stage is rewritten next
+  }
+
+  // merge into the sparse branch's result (natural-log lse)
+  const int head = wave * 16 + l16;
+  const int64_t hi = (int64_t)q * n_heads + head;
+  const float lse_l = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  const float lse_s = lse[hi];
+  const float mx = fmaxf(lse_s, lse_l);
+  if (mx == -INFINITY) return;   // no row in either set: out stays 0, lse -inf
+  const float ws = lse_s == -INFINITY ? 0.0f : expf(lse_s - mx);
+  const float wl = lse_l == -INFINITY ? 0.0f : expf(lse_l - mx);
+  const float den = ws + wl;
+  const float cs = ws / den;
+  const float cl = l_run > 0.0f ? (wl / den) / l_run : 0.0f;
+  float *oq = out + hi * 128 + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    f32x4 *po = reinterpret_cast<f32x4 *>(oq + dt * 16);
+    *po = *po * cs + o[dt] * cl;
+  }
+  if (g == 0) lse[hi] = mx + logf(den);
+}
+
 // Rows per split: as many as possible (one split needs no combine) while the
 // grid still has kTargetGroups workgroups, at most kMaxRowsPerSplit, a
 // multiple of the sub-chunk.  Splits of one sub-chunk become two (whose
@@ -522,6 +651,32 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
   if (L.splits == 1) return hipGetLastError();
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(n_heads / 4), (unsigned)nq), dim3(512),
                      0, s, acc, ml, n_heads, L.splits, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_local_attn(const csa2_local_cache &c, const uint16_t *q, int32_t n_heads,
+                             const int32_t *q_seq, const int32_t *q_pos, int32_t nq,
+                             float softmax_scale, float *out, float *lse, hipStream_t s) {
+  const float scale_log2 = fabsf(softmax_scale) * kLog2e;
+  const bool q_negate = softmax_scale < 0.0f;
+#define CSA2_LOCAL_CASE(W)                                                                       \
+  case W:                                                                                        \
+    hipLaunchKernelGGL(local_attn_kernel<W>, dim3((unsigned)nq), dim3(W * 64), 0, s, c.k, c.v,   \
+                       c.pos, c.window, q, n_heads, q_seq, q_pos, scale_log2, q_negate, out, lse); \
+    break;
+  switch (n_heads / 16) {
+    CSA2_LOCAL_CASE(1)
+    CSA2_LOCAL_CASE(2)
+    CSA2_LOCAL_CASE(3)
+    CSA2_LOCAL_CASE(4)
+    CSA2_LOCAL_CASE(5)
+    CSA2_LOCAL_CASE(6)
+    CSA2_LOCAL_CASE(7)
+    CSA2_LOCAL_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef CSA2_LOCAL_CASE
   return hipGetLastError();
 }
 

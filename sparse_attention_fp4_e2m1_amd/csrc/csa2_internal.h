@@ -102,6 +102,14 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
                               int32_t top_k, float softmax_scale, float *out, float *lse,
                               uint8_t *ws, const AttnWorkspace &layout, hipStream_t stream);
 
+hipError_t launch_local_append(const csa2_local_cache &c, const uint16_t *k, const uint16_t *v,
+                               const int32_t *seq, const int32_t *pos, int32_t n,
+                               hipStream_t stream);
+hipError_t launch_local_attn(const csa2_local_cache &c, const uint16_t *q, int32_t n_heads,
+                             const int32_t *q_seq, const int32_t *q_pos, int32_t nq,
+                             float softmax_scale, float *out, float *lse, hipStream_t stream);
+constexpr int32_t kMaxLocalWindow = 1024;
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace csa2

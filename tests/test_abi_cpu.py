@@ -27,6 +27,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ("csa2_kv_append", "csa2_index_topk", "csa2_sparse_attn",
                  "csa2_index_topk_workspace", "csa2_sparse_attn_workspace",
+                 "csa2_local_append", "csa2_local_attn",
                  "csa2_strerror", "csa2_abi_version"):
         assert want in names
 
@@ -129,3 +130,36 @@ def test_sparse_attn_validation(lib):
     assert call(ws=None) == lib.CSA2_ERR_WORKSPACE
     assert call(ws_bytes=8) == lib.CSA2_ERR_WORKSPACE
     assert call(nq=0) == lib.CSA2_OK
+
+
+def test_local_window_validation(lib):
+    L = lib.LIB
+    P = ctypes.c_void_p
+
+    def lc(batch=2, window=128, dk=128, dv=128, k=P(1), v=P(1), pos=P(1)):
+        return ctypes.byref(lib.csa2_local_cache(k, v, pos, batch, window, dk, dv))
+
+    def app(c=None, n=4, k=P(1), seq=P(1)):
+        return L.csa2_local_append(lc() if c is None else c, k, P(1), seq, P(1), n, None)
+
+    def att(c=None, heads=64, nq=2, out=P(1), lse=P(1), qpos=P(1)):
+        return L.csa2_local_attn(lc() if c is None else c, P(1), heads, P(1), qpos, nq, 0.1,
+                                 out, lse, None)
+
+    assert app(c=lc(k=None)) == lib.CSA2_ERR_NULL
+    assert app(c=lc(pos=None)) == lib.CSA2_ERR_NULL
+    assert app(c=lc(window=0)) == lib.CSA2_ERR_SHAPE
+    assert app(c=lc(window=1025)) == lib.CSA2_ERR_SHAPE
+    assert app(c=lc(batch=0)) == lib.CSA2_ERR_SHAPE
+    assert app(c=lc(dk=64)) == lib.CSA2_ERR_UNSUPPORTED
+    assert app(n=-1) == lib.CSA2_ERR_SHAPE
+    assert app(n=0) == lib.CSA2_OK
+    assert app(k=None) == lib.CSA2_ERR_NULL
+    assert app(seq=None) == lib.CSA2_ERR_NULL
+    assert att(heads=24) == lib.CSA2_ERR_UNSUPPORTED
+    assert att(heads=144) == lib.CSA2_ERR_UNSUPPORTED
+    assert att(nq=-1) == lib.CSA2_ERR_SHAPE
+    assert att(nq=0) == lib.CSA2_OK
+    assert att(lse=None) == lib.CSA2_ERR_NULL      # the merge needs the sparse lse
+    assert att(out=None) == lib.CSA2_ERR_NULL
+    assert att(qpos=None) == lib.CSA2_ERR_NULL
