@@ -43,6 +43,8 @@ def _args():
     p.add_argument("--workload", default="decode_64k_b32")
     p.add_argument("--no-extra", action="store_true", help="skip the 1M-context line item")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--local-window", type=int, default=0,
+                   help="also time the local window branch (csa2_local_attn) over this many rows")
     p.add_argument("--graph", action="store_true", help="replay the step as a captured graph")
     p.add_argument("--copy-probe", type=int, default=0,
                    help="only run a plain device copy of this many MiB (counter calibration)")
@@ -328,6 +330,55 @@ def cpu_baseline(name, n_sample=32):
                       f"contexts), one step incl. append, numpy oracle, 1 thread; {t:.1f} s"}
 
 
+def local_item(name, window, steps, warmup, hip):
+    """The local window branch alone on the workload's queries: every query's
+    window full (positions q_pos - window + 1 .. q_pos), merged into a finite
+    (out, lse).  Algorithmic bytes per launch: per query the window's K and V
+    codes (2 x 128 B per row) and slot positions (4 B per row), the bf16
+    queries, and out and lse read and written back in fp32."""
+    import numpy as np
+    import torch
+    import synth
+    import sparse_attention_fp4_e2m1_amd as m
+    wl = synth.workload(name)
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(11)
+    lc = m.LocalCache(wl.batch, window)
+    qpos = wl.query_pos()
+    for b in range(wl.batch):
+        p = np.arange(max(0, int(qpos.max()) - window + 1), int(qpos.max()) + 1)
+        rows = rng.standard_normal((2, len(p), 128)).astype(np.float32)
+        kv = torch.from_numpy(synth.f32_to_bf16_bits(rows).view(np.int16)).to(dev)
+        m.csa2_local_append(lc, kv[0], kv[1], torch.full((len(p),), b, dtype=torch.int32, device=dev),
+                            torch.from_numpy(p.astype(np.int32)).to(dev))
+    q = torch.from_numpy(synth.gen_queries(wl, 0).q.view(np.int16)).to(dev)
+    q_seq = torch.from_numpy(wl.query_seq().astype(np.int32)).to(dev)
+    q_pos = torch.from_numpy(qpos.astype(np.int32)).to(dev)
+    out = torch.zeros((wl.nq, wl.heads, 128), dtype=torch.float32, device=dev)
+    lse = torch.zeros((wl.nq, wl.heads), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        m.csa2_local_attn(lc, q, q_seq, q_pos, out, lse)
+    stream = torch.cuda.current_stream().cuda_stream
+    a, b = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(a, stream)
+    for _ in range(steps):
+        m.csa2_local_attn(lc, q, q_seq, q_pos, out, lse)
+    hip.record(b, stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(a, b) / steps
+    hip.destroy(a)
+    hip.destroy(b)
+    rows = int(np.minimum(qpos + 1, window).sum())
+    nbytes = rows * (2 * 128 + 4) + wl.nq * wl.heads * (128 * 2 + 2 * 128 * 4 + 2 * 4)
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return {"window": window, "queries": wl.nq, "heads": wl.heads, "avg_launch_ms": ms,
+            "queries_per_s": wl.nq / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "kernel": "local_attn_kernel", "achieved": ach,
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                         "traffic": None, "bytes_per_launch": nbytes}}
+
+
 def copy_probe(mib):
     import torch
     n = mib << 20
@@ -383,6 +434,10 @@ def main():
             line["extra"][name]["unit"] = "queries/s"
             line["extra"][name]["steps"] = steps
             line["extra"][name]["roofline"] = res2.get("roofline")
+    if args.local_window:
+        print(f"[bench] local window branch, {args.local_window} rows", file=sys.stderr, flush=True)
+        line["local_window_branch"] = local_item(args.workload, args.local_window, args.steps,
+                                                 args.warmup, hip)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.workload)
