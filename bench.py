@@ -146,23 +146,26 @@ class WorkloadRun:
         for b, p in zip(wl.query_seq(), wl.query_pos()):
             seq_vis[int(b)] = max(seq_vis.get(int(b), 0), int(p) + 1)
         dense_keys = sum(seq_vis.values()) * wl.idx_bytes_per_token()
-        for L in wl.layers:
+        for li, L in enumerate(wl.layers):
+            k = self.stack.k[li]
             if L.mode == "full" and matrix_core_scan(wl) and L is wl.layers[0]:
                 total += dense_keys
                 total += nq * wl.idx_heads * wl.idx_dim * 2
-                total += nq * wl.top_k * 4
+                total += nq * k * 4
             elif L.mode == "full":
                 total += vis * wl.idx_bytes_per_token()
                 total += nq * wl.idx_heads * wl.idx_dim * 2
-                total += nq * wl.top_k * 4 + (nq * 8 * L.pool_blocks * 4 if L.pool_blocks else 0)
+                total += nq * k * 4 + (nq * 8 * L.pool_blocks * 4 if L.pool_blocks else 0)
             elif L.mode == "reindex":
                 pool = 8 * wl.layers[L.pool_from].pool_blocks if L.pool_from >= 0 else 0
-                cand = nq * pool if pool else vis
-                total += cand * wl.idx_bytes_per_token() + nq * pool * 4
-                total += nq * wl.idx_heads * wl.idx_dim * 2 + nq * wl.top_k * 4
+                if pool:
+                    total += nq * pool * (wl.idx_bytes_per_token() + 4)
+                else:
+                    total += dense_keys if matrix_core_scan(wl) else vis * wl.idx_bytes_per_token()
+                total += nq * wl.idx_heads * wl.idx_dim * 2 + nq * k * 4
             else:
                 pass                                             # Reuse: the source list itself
-            total += nq * wl.top_k * (144 + 4)                   # selected rows + their indices
+            total += nq * k * (144 + 4)                          # selected rows + their indices
             total += nq * wl.heads * (wl.dk * 2 + wl.dv * 4 + 4)  # q in, out + lse out
         return total
 
@@ -276,6 +279,7 @@ def measure(name, steps, warmup, hip, use_graph):
         "step_hbm_gbps": step_gbps, "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": run.step_bytes(),
         "setup_s": round(run.setup_s, 1),
+        "layer_top_k": list(run.stack.k),
     }
     if scan_ms is not None and matrix_core_scan(wl):
         # the first product pass of the matrix-core scorer: one dense E4M3 GEMM
@@ -379,6 +383,11 @@ def local_item(name, window, steps, warmup, hip):
                          "traffic": None, "bytes_per_launch": nbytes}}
 
 
+def synth_prefill(name) -> bool:
+    import synth
+    return synth.workload(name).prefill > 0
+
+
 def copy_probe(mib):
     import torch
     n = mib << 20
@@ -415,18 +424,21 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context,
                    "heads": wl.heads, "idx_heads": wl.idx_heads, "idx_k_dtype": wl.idx_k_dtype,
                    "top_k": wl.top_k, "layers": [L.mode for L in wl.layers],
+                   "layer_top_k": res["layer_top_k"],
                    "graph": bool(args.graph)},
         "step_hbm_gbps": res["step_hbm_gbps"], "step_hbm_frac": res["step_hbm_frac"],
         "roofline": res.get("roofline"),
     }
     if not args.no_extra:
         line["extra"] = {}
-        for name in ("decode_1m", "chain8_256k_b8", "prefill_4k_on_128k"):
+        for name in ("decode_1m", "chain8_256k_b8", "prefill_4k_on_128k", "released_256k_b8",
+                     "encoder_4k_on_128k"):
             if name == args.workload:
                 continue
             print(f"[bench] {name} line item", file=sys.stderr, flush=True)
-            # the prefill step is ~2 ms: fewer steps keep its share of the run small
-            steps = args.steps if name != "prefill_4k_on_128k" else max(3, args.steps // 5)
+            # a prefill step is ~1-2 ms: fewer steps keep its share of the run small
+            prefill = synth_prefill(name)
+            steps = args.steps if not prefill else max(3, args.steps // 5)
             wl2, res2 = measure(name, steps, args.warmup, hip, args.graph)
             line["extra"][name] = {k: res2[k] for k in
                                    ("value", "ms_per_step", "step_ms_percentiles",

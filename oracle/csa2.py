@@ -465,7 +465,8 @@ def run_layers(cache: OracleCache, layers: Sequence, q_seq, q_pos, queries, top_
                q_idx_dtype: str, scale: Optional[float] = None, only=None):
     """Index Top-K and attention for every layer of a stack, per query.
 
-    layers: objects with .mode, .pool_blocks, .pool_from, .reuse_from
+    layers: objects with .mode, .pool_blocks, .pool_from, .reuse_from (and
+    optionally .top_k: a layer's own K; 0 or absent means top_k)
     queries: per layer, objects with .q [nq, heads, dk] and .q_idx [nq, H_I, D] bf16 bits.
     only: optional list of query indices to compute (others are skipped).
     Returns per layer a dict with 'topk' [nq, K], 'pool' (or None), 'out', 'lse'.
@@ -475,7 +476,13 @@ def run_layers(cache: OracleCache, layers: Sequence, q_seq, q_pos, queries, top_
     results = []
     for li, layer in enumerate(layers):
         qd = queries[li]
-        res = {"topk": np.full((nq, top_k), -1, np.int32), "pool": None,
+        # this layer's K: a Reuse layer keeps its source's list; otherwise the
+        # layer's own top_k when it has one (> 0), else the stack's
+        if layer.mode == "reuse":
+            k_li = results[layer.reuse_from]["topk"].shape[1]
+        else:
+            k_li = getattr(layer, "top_k", 0) or top_k
+        res = {"topk": np.full((nq, k_li), -1, np.int32), "pool": None,
                "out": np.zeros((nq, qd.q.shape[1], cache.dv)),
                "lse": np.full((nq, qd.q.shape[1]), -np.inf)}
         if layer.mode == "full" and layer.pool_blocks > 0:
@@ -487,7 +494,7 @@ def run_layers(cache: OracleCache, layers: Sequence, q_seq, q_pos, queries, top_
                 pool_in = results[layer.pool_from]["pool"][i]
             reuse = results[layer.reuse_from]["topk"][i] if layer.mode == "reuse" else None
             qi = query_index_values(qd.q_idx[i], q_idx_dtype)
-            topk, pool, _, _ = index_topk(layer.mode, cache, b, p, qi, top_k, pool_in=pool_in,
+            topk, pool, _, _ = index_topk(layer.mode, cache, b, p, qi, k_li, pool_in=pool_in,
                                           pool_blocks=layer.pool_blocks, reuse_src=reuse)
             res["topk"][i] = topk
             if pool is not None:

@@ -54,6 +54,7 @@ class Layer:
     pool_blocks: int = 0      # full: number of 8-position blocks kept in the pool (0: no pool)
     pool_from: int = -1       # reindex: layer whose pool is searched (-1: no pool, all visible)
     reuse_from: int = -1      # reuse: layer whose Top-K indices are recycled
+    top_k: int = 0            # full / reindex: this layer's K (0: the workload's); reuse: its source's
 
 
 @dataclasses.dataclass(frozen=True)
@@ -136,6 +137,29 @@ WORKLOADS = {
                           idx_heads=8, idx_k_dtype="fp8", q_idx_dtype="bf16", top_k=2048,
                           layers=(_full(2048), Layer("reindex", pool_from=0)),
                           keys="outlier_tokens"),
+    # the released pool setting: batch 8, 262144 context; layer 0 Full (K 2048)
+    # building a 2048-block (16384-position) pool, layers 1-3 Reindex over the
+    # pool selecting 512 each, layers 4-7 Reuse layer 3's 512 indices.
+    "released_256k_b8": Workload("released_256k_b8", seed=5, batch=8, context=262144, heads=64,
+                                 idx_heads=8, idx_k_dtype="fp8", q_idx_dtype="bf16", top_k=2048,
+                                 layers=(_full(2048),
+                                         Layer("reindex", pool_from=0, top_k=512),
+                                         Layer("reindex", pool_from=0, top_k=512),
+                                         Layer("reindex", pool_from=0, top_k=512),
+                                         Layer("reuse", reuse_from=3),
+                                         Layer("reuse", reuse_from=3),
+                                         Layer("reuse", reuse_from=3),
+                                         Layer("reuse", reuse_from=3)),
+                                 keys="plain"),
+    # encoder side (no candidate pool): 4096 new causal query tokens on a
+    # 131072-row cache; layer 0 Full (K 2048), layer 1 Reindex over every
+    # visible position selecting 512, layer 2 Reuse layer 1's indices.
+    "encoder_4k_on_128k": Workload("encoder_4k_on_128k", seed=6, batch=1, context=131072 + 4096,
+                                   heads=64, idx_heads=8, idx_k_dtype="fp8", q_idx_dtype="fp8",
+                                   top_k=2048,
+                                   layers=(_full(), Layer("reindex", top_k=512),
+                                           Layer("reuse", reuse_from=1)),
+                                   keys="plain", prefill=4096),
     # 4096 new causal query tokens appended to a 131072-row cache; fp8 indexer
     # scoring, per-query causal Top-K 2048, 64-head sparse attention.
     "prefill_4k_on_128k": Workload("prefill_4k_on_128k", seed=4, batch=1, context=131072 + 4096,

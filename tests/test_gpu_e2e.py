@@ -16,6 +16,8 @@ REDUCED = {
     "chain8_256k_b8": dict(context=16384, batch=2),
     "decode_1m": dict(context=65536),
     "prefill_4k_on_128k": dict(context=4096 + 256, prefill=256),
+    "released_256k_b8": dict(context=32768, batch=2),
+    "encoder_4k_on_128k": dict(context=4096 + 256, prefill=256),
 }
 
 

@@ -19,6 +19,8 @@ SAMPLES = {
     "decode_1m": [0],
     "chain8_256k_b8": [5],
     "prefill_4k_on_128k": [0, 1365, 2730, 4095],
+    "released_256k_b8": [3],
+    "encoder_4k_on_128k": [0, 2047, 4095],
 }
 
 

@@ -118,3 +118,30 @@ def test_full_topk_is_causal_and_matches_brute_force():
     assert list(cand) == list(range(61))
     assert np.all(topk <= 60)
     assert list(topk) == _brute_topk(scores, list(range(61)), 10)
+
+
+def test_layer_stack_with_a_smaller_reindex_k():
+    # the released pool setting in miniature: Full (K 16) builds a 4-block pool,
+    # Reindex selects 5 from it, Reuse recycles those 5
+    wl, c = _small_cache(seed=7)
+    layers = (synth.Layer("full", pool_blocks=4), synth.Layer("reindex", pool_from=0, top_k=5),
+              synth.Layer("reuse", reuse_from=1))
+    qs = [synth.gen_queries(wl, li) for li in range(3)]
+    q_seq, q_pos = np.array([0, 1]), np.array([199, 120])
+    res = O.run_layers(c, layers, q_seq, q_pos, qs, 16, "bf16")
+    assert [r["topk"].shape[1] for r in res] == [16, 5, 5]
+    for i in range(2):
+        qi = O.query_index_values(qs[1].q_idx[i], "bf16")
+        pool = res[0]["pool"][i]
+        k16, _, scores, cand = O.index_topk("reindex", c, int(q_seq[i]), int(q_pos[i]), qi, 16,
+                                            pool_in=pool)
+        k5 = res[1]["topk"][i]
+        # the 5 best pool members by brute force, and a prefix-closed selection
+        assert sorted(k5) == sorted(_brute_topk(scores, list(cand), 5))
+        assert set(k5) <= set(k16)
+        assert set(k5) <= set(pool[pool >= 0])
+        assert np.array_equal(res[2]["topk"][i], k5)
+    # the released preset: Reindex layers select 512 from the 2048-block pool
+    rel = synth.workload("released_256k_b8")
+    assert rel.layers[0].pool_blocks == 2048 and rel.layers[0].top_k == 0 and rel.top_k == 2048
+    assert all(L.top_k == 512 for L in rel.layers[1:4])
