@@ -270,6 +270,55 @@ csa2_status csa2_local_attn(const csa2_local_cache *cache, const uint16_t *q, in
                             float softmax_scale, float *out, float *lse, void *stream);
 
 /*
+ * Persistent KV (aiwiki "DeepSeek V4.1-Flash", section "KV-cache formats and
+ * bounded replay": the long-lived global state is kept apart from the runtime
+ * cache, on SSD or host memory, to resume or reuse a prefix).  The persistent
+ * form of positions [0, len) of one sequence is the byte image of its rows,
+ * in this order, with no header:
+ *   kv_codes  len * 128 bytes          (kv_codes[seq][0 .. len), row-major)
+ *   kv_scales len * 16 bytes           (kv_scales[seq][0 .. len))
+ *   idx_k     ceil(len / T) whole tiles of 64 * 64 * E bytes (the tiled
+ *             layout above; T = 64 / idx_heads positions per tile).
+ * A last, partly filled tile also carries the bytes of positions len ..
+ * ceil(len / T) * T - 1, which no query sees before they are appended.
+ * csa2_kv_export_bytes gives the image's size (0 for an invalid cache or len).
+ */
+size_t csa2_kv_export_bytes(const csa2_cache *cache, int32_t len);
+
+/*
+ * Copies the persistent image of positions [0, len) of sequence seq to dst
+ * (device memory or pinned host memory from hipHostMalloc, dst_bytes >=
+ * csa2_kv_export_bytes), ordered on the stream; synchronize the stream before
+ * reading a host dst.
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (seq outside [0, batch), len outside
+ * [0, capacity]), CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE (dst_bytes too
+ * small), CSA2_ERR_HIP.  len = 0 is a no-op returning CSA2_OK.
+ */
+csa2_status csa2_kv_export(const csa2_cache *cache, int32_t seq, int32_t len, void *dst,
+                           size_t dst_bytes, void *stream);
+
+/*
+ * Writes a persistent image (from csa2_kv_export of a cache with the same
+ * idx_heads and idx_k_dtype; capacity and batch may differ) into positions
+ * [0, len) of sequence seq, ordered on the stream; src as for dst above.
+ * Appends after it continue at position len.
+ * Errors: as csa2_kv_export (src_bytes too small: CSA2_ERR_WORKSPACE).
+ */
+csa2_status csa2_kv_import(const csa2_cache *cache, int32_t seq, int32_t len, const void *src,
+                           size_t src_bytes, void *stream);
+
+/*
+ * Empties sequence seq's local window (every slot's position set to -1) by a
+ * small kernel on the stream (no memset node, so the call can be captured).
+ * With csa2_local_append of the most recent min(window, len) positions this
+ * is the bounded replay of the page's section "KV-cache formats and bounded
+ * replay": the window is rebuilt from recent tokens instead of being stored.
+ * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE (seq outside [0, batch)),
+ * CSA2_ERR_UNSUPPORTED, CSA2_ERR_HIP.
+ */
+csa2_status csa2_local_clear(const csa2_local_cache *cache, int32_t seq, void *stream);
+
+/*
  * Profiling hook for callers that measure the index scan against the HBM
  * roofline.  After a call with non-NULL events (two hipEvent_t), every
  * csa2_index_topk call made later from the same host thread records `before`

@@ -54,6 +54,10 @@ def _load():
         "csa2_sparse_attn": (I32, [C, P, I32, P, I32, P, I32, F32, P, P, P, SZ, P]),
         "csa2_local_append": (I32, [ctypes.POINTER(csa2_local_cache), P, P, P, P, I32, P]),
         "csa2_local_attn": (I32, [ctypes.POINTER(csa2_local_cache), P, I32, P, P, I32, F32, P, P, P]),
+        "csa2_kv_export_bytes": (SZ, [C, I32]),
+        "csa2_kv_export": (I32, [C, I32, I32, P, SZ, P]),
+        "csa2_kv_import": (I32, [C, I32, I32, P, SZ, P]),
+        "csa2_local_clear": (I32, [ctypes.POINTER(csa2_local_cache), I32, P]),
         "csa2_profile_index_scan": (None, [P, P]),
         "csa2_strerror": (ctypes.c_char_p, [I32]),
         "csa2_abi_version": (ctypes.c_int, []),
@@ -263,3 +267,39 @@ def csa2_local_attn(cache: LocalCache, q, q_seq, q_pos, out, lse,
                                float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)),
            "csa2_local_attn")
     return out, lse
+
+
+def csa2_kv_export_bytes(cache: Cache, length: int) -> int:
+    return int(LIB.csa2_kv_export_bytes(cache.ref, int(length)))
+
+
+def _image_buffer(t, name, nbytes):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or not t.is_contiguous():
+        raise TypeError(f"{name}: a contiguous uint8 tensor is required")
+    if t.device.type == "cpu" and not t.is_pinned():
+        raise ValueError(f"{name}: host memory must be pinned (pin_memory=True)")
+    if t.numel() < nbytes:
+        raise ValueError(f"{name}: {t.numel()} bytes, {nbytes} needed")
+
+
+def csa2_kv_export(cache: Cache, seq: int, length: int, dst=None, stream=None):
+    """Persistent image of positions [0, length) of sequence seq, into dst (a
+    uint8 tensor on the device or in pinned host memory; allocated on the
+    device when None).  Ordered on the stream."""
+    n = csa2_kv_export_bytes(cache, length)
+    if dst is None:
+        dst = torch.empty(max(n, 1), dtype=torch.uint8, device=cache.device)
+    _image_buffer(dst, "dst", n)
+    _check(LIB.csa2_kv_export(cache.ref, int(seq), int(length), _ptr(dst), dst.numel(),
+                              _stream(stream)), "csa2_kv_export")
+    return dst
+
+
+def csa2_kv_import(cache: Cache, seq: int, length: int, src, stream=None) -> None:
+    _image_buffer(src, "src", csa2_kv_export_bytes(cache, length))
+    _check(LIB.csa2_kv_import(cache.ref, int(seq), int(length), _ptr(src), src.numel(),
+                              _stream(stream)), "csa2_kv_import")
+
+
+def csa2_local_clear(cache: LocalCache, seq: int, stream=None) -> None:
+    _check(LIB.csa2_local_clear(cache.ref, int(seq), _stream(stream)), "csa2_local_clear")

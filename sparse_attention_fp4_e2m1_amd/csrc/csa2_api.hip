@@ -183,4 +183,91 @@ csa2_status csa2_local_attn(const csa2_local_cache *cache, const uint16_t *q, in
   return CSA2_OK;
 }
 
+namespace {
+
+struct KvImage {
+  size_t codes, scales, idx, total;   // section sizes in bytes
+};
+
+KvImage kv_image(const csa2_cache &c, int32_t len) {
+  const size_t esz = c.idx_k_dtype == CSA2_FP8_E4M3 ? 1 : 2;
+  const int32_t per_tile = 64 / c.idx_heads;
+  KvImage im;
+  im.codes = (size_t)len * 128;
+  im.scales = (size_t)len * 16;
+  im.idx = (size_t)((len + per_tile - 1) / per_tile) * 64 * 64 * esz;
+  im.total = im.codes + im.scales + im.idx;
+  return im;
+}
+
+csa2_status check_image_args(const csa2_cache *c, int32_t seq, int32_t len, const void *buf,
+                             size_t bytes) {
+  csa2_status st = check_cache(c, true);
+  if (st != CSA2_OK) return st;
+  if (seq < 0 || seq >= c->batch || len < 0 || len > c->capacity) return CSA2_ERR_SHAPE;
+  if (len == 0) return CSA2_OK;
+  if (buf == nullptr) return CSA2_ERR_NULL;
+  if (bytes < kv_image(*c, len).total) return CSA2_ERR_WORKSPACE;
+  return CSA2_OK;
+}
+
+// The three sections of one sequence's prefix, as (device address, bytes).
+void kv_sections(const csa2_cache &c, int32_t seq, int32_t len, uint8_t *dev[3], size_t n[3]) {
+  const KvImage im = kv_image(c, len);
+  const size_t esz = c.idx_k_dtype == CSA2_FP8_E4M3 ? 1 : 2;
+  dev[0] = c.kv_codes + (size_t)seq * c.capacity * 128;
+  dev[1] = c.kv_scales + (size_t)seq * c.capacity * 16;
+  dev[2] = static_cast<uint8_t *>(c.idx_k) + (size_t)seq * c.capacity * c.idx_heads * 64 * esz;
+  n[0] = im.codes;
+  n[1] = im.scales;
+  n[2] = im.idx;
+}
+
+}  // namespace
+
+size_t csa2_kv_export_bytes(const csa2_cache *cache, int32_t len) {
+  if (check_cache(cache, true) != CSA2_OK || len < 0 || len > cache->capacity) return 0;
+  return kv_image(*cache, len).total;
+}
+
+csa2_status csa2_kv_export(const csa2_cache *cache, int32_t seq, int32_t len, void *dst,
+                           size_t dst_bytes, void *stream) {
+  csa2_status st = check_image_args(cache, seq, len, dst, dst_bytes);
+  if (st != CSA2_OK || len == 0) return st;
+  uint8_t *dev[3];
+  size_t n[3];
+  kv_sections(*cache, seq, len, dev, n);
+  uint8_t *out = static_cast<uint8_t *>(dst);
+  for (int i = 0; i < 3; ++i) {
+    if (hipMemcpyAsync(out, dev[i], n[i], hipMemcpyDefault, (hipStream_t)stream) != hipSuccess)
+      return CSA2_ERR_HIP;
+    out += n[i];
+  }
+  return CSA2_OK;
+}
+
+csa2_status csa2_kv_import(const csa2_cache *cache, int32_t seq, int32_t len, const void *src,
+                           size_t src_bytes, void *stream) {
+  csa2_status st = check_image_args(cache, seq, len, src, src_bytes);
+  if (st != CSA2_OK || len == 0) return st;
+  uint8_t *dev[3];
+  size_t n[3];
+  kv_sections(*cache, seq, len, dev, n);
+  const uint8_t *in = static_cast<const uint8_t *>(src);
+  for (int i = 0; i < 3; ++i) {
+    if (hipMemcpyAsync(dev[i], in, n[i], hipMemcpyDefault, (hipStream_t)stream) != hipSuccess)
+      return CSA2_ERR_HIP;
+    in += n[i];
+  }
+  return CSA2_OK;
+}
+
+csa2_status csa2_local_clear(const csa2_local_cache *cache, int32_t seq, void *stream) {
+  csa2_status st = check_local(cache);
+  if (st != CSA2_OK) return st;
+  if (seq < 0 || seq >= cache->batch) return CSA2_ERR_SHAPE;
+  if (launch_local_clear(*cache, seq, (hipStream_t)stream) != hipSuccess) return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
 }  // extern "C"

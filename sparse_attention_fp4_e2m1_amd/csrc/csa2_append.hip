@@ -145,7 +145,19 @@ __global__ void __launch_bounds__(256) local_append_kernel(
   if (lane == 0) lpos[slot] = p;
 }
 
+// Empties one sequence's window: every slot's position becomes -1.
+__global__ void __launch_bounds__(256) local_clear_kernel(int32_t *__restrict__ lpos, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) lpos[i] = -1;
+}
+
 }  // namespace
+
+hipError_t launch_local_clear(const csa2_local_cache &c, int32_t seq, hipStream_t stream) {
+  hipLaunchKernelGGL(local_clear_kernel, dim3((c.window + 255) / 256), dim3(256), 0, stream,
+                     c.pos + (int64_t)seq * c.window, c.window);
+  return hipGetLastError();
+}
 
 hipError_t launch_local_append(const csa2_local_cache &c, const uint16_t *k, const uint16_t *v,
                                const int32_t *seq, const int32_t *pos, int32_t n,

@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ("csa2_kv_append", "csa2_index_topk", "csa2_sparse_attn",
                  "csa2_index_topk_workspace", "csa2_sparse_attn_workspace",
-                 "csa2_local_append", "csa2_local_attn",
+                 "csa2_local_append", "csa2_local_attn", "csa2_local_clear",
+                 "csa2_kv_export", "csa2_kv_export_bytes", "csa2_kv_import",
                  "csa2_strerror", "csa2_abi_version"):
         assert want in names
 
@@ -163,3 +164,30 @@ def test_local_window_validation(lib):
     assert att(lse=None) == lib.CSA2_ERR_NULL      # the merge needs the sparse lse
     assert att(out=None) == lib.CSA2_ERR_NULL
     assert att(qpos=None) == lib.CSA2_ERR_NULL
+
+
+def test_persistent_image_sizes_and_validation(lib):
+    L = lib.LIB
+    P = ctypes.c_void_p
+    c = _cache(lib)                       # 8 E4M3 index heads: tiles of 8 positions, 4 KB
+    ref = ctypes.byref(c)
+    assert L.csa2_kv_export_bytes(ref, 0) == 0
+    assert L.csa2_kv_export_bytes(ref, 1) == 128 + 16 + 4096
+    assert L.csa2_kv_export_bytes(ref, 8) == 8 * 144 + 4096
+    assert L.csa2_kv_export_bytes(ref, 9) == 9 * 144 + 2 * 4096
+    assert L.csa2_kv_export_bytes(ref, 4096) == 4096 * 144 + 512 * 4096
+    assert L.csa2_kv_export_bytes(ref, 4097) == 0          # beyond capacity
+    bf = ctypes.byref(_cache(lib, idx_heads=4, idx_k_dtype=0))   # bf16, 4 heads: 16 positions, 8 KB
+    assert L.csa2_kv_export_bytes(bf, 17) == 17 * 144 + 2 * 8192
+    n = L.csa2_kv_export_bytes(ref, 100)
+    for fn in (L.csa2_kv_export, L.csa2_kv_import):
+        assert fn(ref, 0, 0, None, 0, None) == lib.CSA2_OK        # empty prefix: nothing to copy
+        assert fn(ref, 2, 100, P(1), n, None) == lib.CSA2_ERR_SHAPE
+        assert fn(ref, -1, 100, P(1), n, None) == lib.CSA2_ERR_SHAPE
+        assert fn(ref, 0, 4097, P(1), 1 << 30, None) == lib.CSA2_ERR_SHAPE
+        assert fn(ref, 0, 100, None, n, None) == lib.CSA2_ERR_NULL
+        assert fn(ref, 0, 100, P(1), n - 1, None) == lib.CSA2_ERR_WORKSPACE
+        assert fn(ctypes.byref(_cache(lib, idx_k=None)), 0, 100, P(1), n, None) == lib.CSA2_ERR_NULL
+    lc = lib.csa2_local_cache(P(1), P(1), P(1), 2, 128, 128, 128)
+    assert L.csa2_local_clear(ctypes.byref(lc), 2, None) == lib.CSA2_ERR_SHAPE
+    assert L.csa2_local_clear(ctypes.byref(lc), -1, None) == lib.CSA2_ERR_SHAPE

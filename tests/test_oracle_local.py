@@ -119,3 +119,27 @@ def test_nothing_visible():
     q = synth.gen_queries(wl, 0).q[0]
     out, lse = O.attention_with_window(q, c, 0, np.full(3, -1), O.OracleLocalCache(1, 8), q_pos=5)
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_bounded_replay_rebuilds_the_window_exactly():
+    # after positions 0 .. n-1 the ring holds exactly the last min(n, window)
+    # of them, so replaying only those rows into an empty ring gives the same
+    # codes and slot positions; replaying fewer leaves the older slots empty
+    rng = np.random.default_rng(5)
+    for n, window in ((300, 64), (40, 64), (64, 64), (65, 64), (1, 1), (7, 1)):
+        k = _bits(rng.standard_normal((n, 128)))
+        v = _bits(rng.standard_normal((n, 128)))
+        live = O.OracleLocalCache(1, window)
+        live.append(k, v, np.zeros(n, int), np.arange(n))
+        replay = O.OracleLocalCache(1, window)
+        lo = max(0, n - window)
+        replay.append(k[lo:], v[lo:], np.zeros(n - lo, int), np.arange(lo, n))
+        assert np.array_equal(live.k, replay.k) and np.array_equal(live.v, replay.v)
+        assert np.array_equal(live.pos, replay.pos)
+        for q_pos in (n - 1, max(0, n - 3)):
+            a, b = live.window_rows(0, q_pos), replay.window_rows(0, q_pos)
+            assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    rows = _bits(rng.standard_normal((10, 128)))
+    short = O.OracleLocalCache(1, 64)
+    short.append(rows, rows, np.zeros(10, int), np.arange(290, 300))
+    assert list(short.window_rows(0, 299)[0]) == list(range(290, 300))
