@@ -270,6 +270,27 @@ csa2_status csa2_local_attn(const csa2_local_cache *cache, const uint16_t *q, in
                             float softmax_scale, float *out, float *lse, void *stream);
 
 /*
+ * The encoder-side projection fused into quantize-and-append (aiwiki
+ * "DeepSeek V4.1-Flash", section "Causal Encoder-Decoder": a decoder layer's
+ * global keys and values are projected from the final causal-encoder hidden
+ * states with that layer's own projection weights).  For each of n tokens:
+ *   y = w . x   (fp32 accumulation of bf16 products), rounded to bf16
+ * (nearest, ties to even); y's channels are K (0..127), V (128..255) and the
+ * index keys (256 .. 256 + idx_heads * 64 - 1, head-major); they are then
+ * quantized and stored exactly as csa2_kv_append stores those bf16 rows.
+ *   x          [n][d_model] bf16 bits, the hidden states.
+ *   w          [256 + idx_heads * 64][d_model] bf16 bits, the projection
+ *              weights, one row per output channel.
+ *   seq, pos   [n] int32, as for csa2_kv_append.
+ * Supported: d_model a multiple of 32, 32 .. 65536.
+ * Device preconditions and errors as csa2_kv_append (CSA2_ERR_SHAPE also
+ * for d_model).  n = 0 is a no-op returning CSA2_OK.
+ */
+csa2_status csa2_proj_append(const csa2_cache *cache, const uint16_t *x, int32_t d_model,
+                             const uint16_t *w, const int32_t *seq, const int32_t *pos, int32_t n,
+                             void *stream);
+
+/*
  * Persistent KV (aiwiki "DeepSeek V4.1-Flash", section "KV-cache formats and
  * bounded replay": the long-lived global state is kept apart from the runtime
  * cache, on SSD or host memory, to resume or reuse a prefix).  The persistent

@@ -502,3 +502,44 @@ def run_layers(cache: OracleCache, layers: Sequence, q_seq, q_pos, queries, top_
             res["out"][i], res["lse"][i] = sparse_attention(qd.q[i], cache, b, topk, scale)
         results.append(res)
     return results
+
+
+def bf16_round_bits(v: np.ndarray) -> np.ndarray:
+    """bf16 bits of finite float64 values rounded to nearest, ties to even
+    (8 significant bits; the exponent range of float32, with its subnormals
+    spaced 2^-133).  Values are assumed to lie within bf16's finite range."""
+    v = np.asarray(v, np.float64)
+    _, e = np.frexp(v)                                  # |v| = m 2^e, 0.5 <= m < 1
+    step = np.ldexp(1.0, np.maximum(e, -125) - 8)       # spacing of bf16 values near v
+    r = np.rint(v / step) * step                        # np.rint: ties to even
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def project_rows(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """The encoder-side projection of hidden states to the rows csa2 appends.
+
+    Source: aiwiki "DeepSeek V4.1-Flash", section "Causal Encoder-Decoder": a
+    decoder layer's global keys and values are projected from the final
+    causal-encoder hidden states with that layer's own weights.  Readings (the
+    pages give no precision or layout): y = W x per token, taken exactly (the
+    float64 sum of bf16 products, exact when the products and partial sums
+    fit 53 bits) and rounded once to bf16; W has one row per output channel:
+    K channels 0..127, V 128..255, then the index keys head by head.
+
+    x_bits [n, d_model], w_bits [channels, d_model] bf16 bits.  Returns the
+    bf16 bits of y [n, channels].
+    """
+    x = bf16_value(x_bits).astype(np.float64)
+    w = bf16_value(w_bits).astype(np.float64)
+    return bf16_round_bits(x @ w.T)
+
+
+def project_and_append(cache: OracleCache, x_bits, w_bits, seq, pos):
+    """project_rows, then the cache's own quantize-and-append of the K, V and
+    index-key parts of the projected rows."""
+    y = project_rows(x_bits, w_bits)
+    H, D = cache.idx_k.shape[2], cache.idx_k.shape[3]
+    n = y.shape[0]
+    cache.append(y[:, :cache.dk], y[:, cache.dk:cache.dk + cache.dv],
+                 y[:, cache.dk + cache.dv:].reshape(n, H, D), seq, pos)
+    return y

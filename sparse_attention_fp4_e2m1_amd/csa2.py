@@ -54,6 +54,7 @@ def _load():
         "csa2_sparse_attn": (I32, [C, P, I32, P, I32, P, I32, F32, P, P, P, SZ, P]),
         "csa2_local_append": (I32, [ctypes.POINTER(csa2_local_cache), P, P, P, P, I32, P]),
         "csa2_local_attn": (I32, [ctypes.POINTER(csa2_local_cache), P, I32, P, P, I32, F32, P, P, P]),
+        "csa2_proj_append": (I32, [C, P, I32, P, P, P, I32, P]),
         "csa2_kv_export_bytes": (SZ, [C, I32]),
         "csa2_kv_export": (I32, [C, I32, I32, P, SZ, P]),
         "csa2_kv_import": (I32, [C, I32, I32, P, SZ, P]),
@@ -303,3 +304,16 @@ def csa2_kv_import(cache: Cache, seq: int, length: int, src, stream=None) -> Non
 
 def csa2_local_clear(cache: LocalCache, seq: int, stream=None) -> None:
     _check(LIB.csa2_local_clear(cache.ref, int(seq), _stream(stream)), "csa2_local_clear")
+
+
+def csa2_proj_append(cache: Cache, x, w, seq, pos, stream=None) -> None:
+    """Projects hidden states x [n, d_model] with w [256 + idx_heads*64, d_model]
+    (bf16 bits) and appends the K, V and index-key rows (include/csa2.h)."""
+    n, d_model = x.shape[0], x.shape[1]
+    d = cache.device
+    _need(x, "x", _B16, (n, d_model), d)
+    _need(w, "w", _B16, (256 + cache.idx_heads * 64, d_model), d)
+    _need(seq, "seq", _I32, (n,), d)
+    _need(pos, "pos", _I32, (n,), d)
+    _check(LIB.csa2_proj_append(cache.ref, _ptr(x), d_model, _ptr(w), _ptr(seq), _ptr(pos), n,
+                                _stream(stream)), "csa2_proj_append")

@@ -262,6 +262,20 @@ csa2_status csa2_kv_import(const csa2_cache *cache, int32_t seq, int32_t len, co
   return CSA2_OK;
 }
 
+csa2_status csa2_proj_append(const csa2_cache *cache, const uint16_t *x, int32_t d_model,
+                             const uint16_t *w, const int32_t *seq, const int32_t *pos, int32_t n,
+                             void *stream) {
+  csa2_status st = check_cache(cache, true);
+  if (st != CSA2_OK) return st;
+  if (n < 0 || d_model < 32 || d_model > 65536 || d_model % 32 != 0) return CSA2_ERR_SHAPE;
+  if (n == 0) return CSA2_OK;
+  if (x == nullptr || w == nullptr || seq == nullptr || pos == nullptr) return CSA2_ERR_NULL;
+  if ((n + 63) / 64 > 0x7FFFFFFF) return CSA2_ERR_SHAPE;
+  if (launch_proj_append(*cache, x, d_model, w, seq, pos, n, (hipStream_t)stream) != hipSuccess)
+    return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
 csa2_status csa2_local_clear(const csa2_local_cache *cache, int32_t seq, void *stream) {
   csa2_status st = check_local(cache);
   if (st != CSA2_OK) return st;

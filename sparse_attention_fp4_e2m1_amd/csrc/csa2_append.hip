@@ -36,6 +36,55 @@ __device__ __forceinline__ uint32_t e2m1_mag(float ax, float s) {
   return c;
 }
 
+// One 16-channel block: E4M3 scale code (returned) and the 16 E2M1 codes,
+// channel i in nibble i of (lo, hi).
+__device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], uint32_t &lo,
+                                                  uint32_t &hi) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  // amax is a bf16 value; the correctly rounded quotient never lands on an
+  // E4M3 midpoint unless the exact quotient does, so rounding it to E4M3
+  // equals rounding the exact amax/6.
+  const uint32_t sc = e4m3_from_f32_nonneg(amax / 6.0f);
+  const float s = e4m3_to_f32(sc);
+  lo = 0;
+  hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t c = s > 0.0f ? e2m1_mag(fabsf(x[i]), s) : 0u;
+    c |= (__float_as_uint(x[i]) >> 28) & 8u;   // sign bit, -0 kept
+    if (i < 8) lo |= c << (4 * i);
+    else hi |= c << (4 * (i - 8));
+  }
+  return sc;
+}
+
+// Eight consecutive index-key channels (bf16 bits in a) of head h at
+// position p into the tiled layout (tiles of 64/H positions;
+// [chunk][position-in-tile][head][16 B]), as bf16 or cast to E4M3.
+__device__ __forceinline__ void store_idx8(uint8_t *seq_idx, int H, int esz, int64_t p, int h,
+                                           int ch, uint4 a) {
+  const int T = kWave / H;
+  uint8_t *tile = seq_idx + (p / T) * (64 * 64 * esz);
+  const int byte = ch * esz;                         // byte of channel ch within the head
+  uint8_t *dst = tile + (byte / 16) * 1024 + ((p % T) * H + h) * 16 + byte % 16;
+  if (esz == 1) {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+    uint32_t out[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t hb = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+      const float f = __uint_as_float(hb << 16);
+      const uint32_t c = e4m3_from_f32_nonneg(fabsf(f)) | ((hb >> 8) & 0x80u);
+      out[i >> 2] |= c << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(out[0], out[1]);
+  } else {
+    *reinterpret_cast<uint4 *>(dst) = a;
+  }
+}
+
 __global__ void __launch_bounds__(256) kv_append_kernel(
     uint8_t *__restrict__ kv_codes, uint8_t *__restrict__ kv_scales, void *__restrict__ idx_k,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -60,59 +109,115 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
       x[2 * i] = __uint_as_float(w[i] << 16);
       x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    // amax is a bf16 value; the correctly rounded quotient never lands on an
-    // E4M3 midpoint unless the exact quotient does, so rounding it to E4M3
-    // equals rounding the exact amax/6.
-    const uint32_t sc = e4m3_from_f32_nonneg(amax / 6.0f);
-    const float s = e4m3_to_f32(sc);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t c = s > 0.0f ? e2m1_mag(fabsf(x[i]), s) : 0u;
-      c |= (__float_as_uint(x[i]) >> 28) & 8u;   // sign bit, -0 kept
-      if (i < 8) lo |= c << (4 * i);
-      else hi |= c << (4 * (i - 8));
-    }
+    uint32_t lo, hi;
+    const uint32_t sc = quant_block16(x, lo, hi);
     uint2 *dst = reinterpret_cast<uint2 *>(kv_codes + slot * 128 + (is_v ? 64 : 0) + blk * 8);
     *dst = make_uint2(lo, hi);
     kv_scales[slot * 16 + (is_v ? 8 : 0) + blk] = (uint8_t)sc;
   }
 
   if (idx_in != nullptr) {
-    // idx_elems = H * 64 bf16 values: 8 per lane-step, stored in the tiled
-    // layout (tiles of 64/H positions; [chunk][position-in-tile][head][16 B]).
+    // idx_elems = H * 64 bf16 values: 8 per lane-step
     const int H = idx_elems / 64;
-    const int T = kWave / H;
     const int esz = idx_fp8 ? 1 : 2;
-    const int64_t p = pos[row];
     const int64_t seq_bytes = (int64_t)capacity * idx_elems * esz;
-    uint8_t *tile = static_cast<uint8_t *>(idx_k) + (int64_t)seq[row] * seq_bytes +
-                    (p / T) * (64 * 64 * esz);
-    const int64_t slot16 = (p % T) * H;
+    uint8_t *seq_idx = static_cast<uint8_t *>(idx_k) + (int64_t)seq[row] * seq_bytes;
     const uint16_t *src = idx_in + (int64_t)row * idx_elems;
-    for (int e = lane * 8; e < idx_elems; e += kWave * 8) {
-      const uint4 a = *reinterpret_cast<const uint4 *>(src + e);
-      const int h = e / 64;
-      const int ch = e % 64;
-      const int byte = ch * esz;                         // byte of channel ch within the head
-      uint8_t *dst = tile + (byte / 16) * 1024 + (slot16 + h) * 16 + byte % 16;
-      if (idx_fp8) {
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-        uint32_t out[2] = {0, 0};
+    for (int e = lane * 8; e < idx_elems; e += kWave * 8)
+      store_idx8(seq_idx, H, esz, pos[row], e / 64, e % 64,
+                 *reinterpret_cast<const uint4 *>(src + e));
+  }
+}
+
+// The encoder-side projection fused into quantize-and-append (aiwiki "DeepSeek
+// V4.1-Flash", section "Causal Encoder-Decoder": the decoder's global keys and
+// values are projected from the final causal-encoder hidden states).  One
+// workgroup computes 64 tokens x 128 output channels of Y = X W^T on matrix
+// cores (bf16 operands, fp32 accumulation), stages the tile in LDS, rounds it
+// to bf16 and quantizes it exactly as kv_append_kernel does.  Column group
+// blockIdx.y: 0 = K, 1 = V, 2 + j = index-key heads 2j and 2j + 1.
+// Operand fragments of v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16
+// and contraction indices k0 + 8 (l / 16) .. +7 of both X and W (16 B each,
+// straight from memory); the result lane holds rows 4 (l / 16) + 0..3 of
+// column l % 16.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+constexpr int kProjRows = 64;
+constexpr int kProjCols = 128;
+constexpr int kProjPitch = kProjCols + 4;
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ void __launch_bounds__(256) proj_append_kernel(
+    uint8_t *__restrict__ kv_codes, uint8_t *__restrict__ kv_scales, uint8_t *__restrict__ idx_k,
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int32_t d_model,
+    const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, int32_t n,
+    int32_t capacity, int32_t H, int32_t esz) {
+  __shared__ float tile[kProjRows * kProjPitch];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int kg = lane >> 4;
+  const int r0 = blockIdx.x * kProjRows;
+  const int cg = blockIdx.y;
+  const int arow = min(r0 + 16 * wave + l16, n - 1);   // rows past n read row n - 1, never stored
+  const uint16_t *xa = x + (int64_t)arow * d_model + 8 * kg;
+  const uint16_t *wb = w + (int64_t)(cg * kProjCols + l16) * d_model + 8 * kg;
+  const int64_t tstride = (int64_t)16 * d_model;
+
+  f32x4 acc[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t hb = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-          const float f = __uint_as_float(hb << 16);
-          const uint32_t c = e4m3_from_f32_nonneg(fabsf(f)) | ((hb >> 8) & 0x80u);
-          out[i >> 2] |= c << (8 * (i & 3));
-        }
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(out[0], out[1]);
-      } else {
-        *reinterpret_cast<uint4 *>(dst) = a;
-      }
+  for (int t = 0; t < 8; ++t) acc[t] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+  for (int k0 = 0; k0 < d_model; k0 += 32) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(xa + k0));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bf16x8 b =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(wb + t * tstride + k0));
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[t], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      tile[(16 * wave + 4 * kg + i) * kProjPitch + 16 * t + l16] = acc[t][i];
+  __syncthreads();
+
+  if (cg < 2) {
+    // (token, 16-channel block): E4M3 scale and E2M1 codes
+    for (int item = tid; item < kProjRows * 8; item += 256) {
+      const int r = item >> 3, b = item & 7;
+      const int row = r0 + r;
+      if (row >= n) continue;
+      const float *src = tile + r * kProjPitch + 16 * b;
+      float xv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xv[i] = __uint_as_float(bf16_rne(src[i]) << 16);
+      uint32_t lo, hi;
+      const uint32_t sc = quant_block16(xv, lo, hi);
+      const int64_t slot = (int64_t)seq[row] * capacity + pos[row];
+      *reinterpret_cast<uint2 *>(kv_codes + slot * 128 + 64 * cg + 8 * b) = make_uint2(lo, hi);
+      kv_scales[slot * 16 + 8 * cg + b] = (uint8_t)sc;
+    }
+  } else {
+    // (token, head of the pair, 8 channels): bf16 bits, stored as bf16 or E4M3
+    const int64_t seq_bytes = (int64_t)capacity * H * 64 * esz;
+    for (int item = tid; item < kProjRows * 16; item += 256) {
+      const int r = item >> 4, hh = (item >> 3) & 1, e = item & 7;
+      const int row = r0 + r;
+      if (row >= n) continue;
+      const float *src = tile + r * kProjPitch + 64 * hh + 8 * e;
+      uint32_t q[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = bf16_rne(src[2 * i]) | (bf16_rne(src[2 * i + 1]) << 16);
+      store_idx8(idx_k + (int64_t)seq[row] * seq_bytes, H, esz, pos[row], 2 * (cg - 2) + hh, 8 * e,
+                 make_uint4(q[0], q[1], q[2], q[3]));
     }
   }
 }
@@ -152,6 +257,16 @@ __global__ void __launch_bounds__(256) local_clear_kernel(int32_t *__restrict__ 
 }
 
 }  // namespace
+
+hipError_t launch_proj_append(const csa2_cache &c, const uint16_t *x, int32_t d_model,
+                              const uint16_t *w, const int32_t *seq, const int32_t *pos,
+                              int32_t n, hipStream_t stream) {
+  dim3 grid((n + kProjRows - 1) / kProjRows, 2 + c.idx_heads / 2);
+  hipLaunchKernelGGL(proj_append_kernel, grid, dim3(256), 0, stream, c.kv_codes, c.kv_scales,
+                     static_cast<uint8_t *>(c.idx_k), x, w, d_model, seq, pos, n, c.capacity,
+                     c.idx_heads, c.idx_k_dtype == CSA2_FP8_E4M3 ? 1 : 2);
+  return hipGetLastError();
+}
 
 hipError_t launch_local_clear(const csa2_local_cache &c, int32_t seq, hipStream_t stream) {
   hipLaunchKernelGGL(local_clear_kernel, dim3((c.window + 255) / 256), dim3(256), 0, stream,

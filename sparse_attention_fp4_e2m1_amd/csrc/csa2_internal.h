@@ -102,6 +102,9 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
                               int32_t top_k, float softmax_scale, float *out, float *lse,
                               uint8_t *ws, const AttnWorkspace &layout, hipStream_t stream);
 
+hipError_t launch_proj_append(const csa2_cache &c, const uint16_t *x, int32_t d_model,
+                              const uint16_t *w, const int32_t *seq, const int32_t *pos,
+                              int32_t n, hipStream_t stream);
 hipError_t launch_local_clear(const csa2_local_cache &c, int32_t seq, hipStream_t stream);
 hipError_t launch_local_append(const csa2_local_cache &c, const uint16_t *k, const uint16_t *v,
                                const int32_t *seq, const int32_t *pos, int32_t n,

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     for want in ("csa2_kv_append", "csa2_index_topk", "csa2_sparse_attn",
                  "csa2_index_topk_workspace", "csa2_sparse_attn_workspace",
                  "csa2_local_append", "csa2_local_attn", "csa2_local_clear",
-                 "csa2_kv_export", "csa2_kv_export_bytes", "csa2_kv_import",
+                 "csa2_kv_export", "csa2_kv_export_bytes", "csa2_kv_import", "csa2_proj_append",
                  "csa2_strerror", "csa2_abi_version"):
         assert want in names
 
@@ -191,3 +191,23 @@ def test_persistent_image_sizes_and_validation(lib):
     lc = lib.csa2_local_cache(P(1), P(1), P(1), 2, 128, 128, 128)
     assert L.csa2_local_clear(ctypes.byref(lc), 2, None) == lib.CSA2_ERR_SHAPE
     assert L.csa2_local_clear(ctypes.byref(lc), -1, None) == lib.CSA2_ERR_SHAPE
+
+
+def test_proj_append_validation(lib):
+    L = lib.LIB
+    P = ctypes.c_void_p
+    ref = ctypes.byref(_cache(lib))
+
+    def call(c=ref, x=P(1), d=512, w=P(1), seq=P(1), n=4):
+        return L.csa2_proj_append(c, x, d, w, seq, P(1), n, None)
+
+    assert call(n=0) == lib.CSA2_OK
+    assert call(n=-1) == lib.CSA2_ERR_SHAPE
+    assert call(d=0) == lib.CSA2_ERR_SHAPE
+    assert call(d=48) == lib.CSA2_ERR_SHAPE
+    assert call(d=65536 + 32) == lib.CSA2_ERR_SHAPE
+    assert call(x=None) == lib.CSA2_ERR_NULL
+    assert call(w=None) == lib.CSA2_ERR_NULL
+    assert call(seq=None) == lib.CSA2_ERR_NULL
+    assert call(c=ctypes.byref(_cache(lib, idx_k=None))) == lib.CSA2_ERR_NULL
+    assert call(c=ctypes.byref(_cache(lib, idx_heads=2))) == lib.CSA2_ERR_UNSUPPORTED

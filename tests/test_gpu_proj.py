@@ -1,0 +1,70 @@
+"""GPU parity of csa2_proj_append (the encoder-side projection fused into
+quantize-and-append) against the oracle's project_and_append.
+
+Bit-exact on hidden states and weights drawn from a coarse grid (x in
+{-1, -3/4, .., 1}, w in {-1/2, -3/8, .., 1/2}): every product and partial sum
+is a multiple of 2^-5 below 2^12, exact in fp32 in any order, so the matrix
+cores' sums equal the oracle's exact ones and the bf16 rounding, codes, scales
+and index keys agree byte for byte.  On random normal inputs the fp32
+accumulation order differs from the exact sum, so a value that lands next to
+a bf16 rounding boundary may round the other way: there the rule is relaxed
+to at least 99% equal bytes."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import csa2 as O
+from gpu_util import announce, dev_i32, dev_u16, host, lib, untile_idx
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(heads, dtype, n, d_model, grid=True, seed=0, capacity=512):
+    m = lib()
+    rng = np.random.default_rng(seed)
+    ch = 256 + heads * 64
+    if grid:
+        x = synth.f32_to_bf16_bits(rng.integers(-4, 5, (n, d_model)).astype(np.float32) / 4)
+        w = synth.f32_to_bf16_bits(rng.integers(-4, 5, (ch, d_model)).astype(np.float32) / 8)
+    else:
+        x = synth.f32_to_bf16_bits(rng.standard_normal((n, d_model)).astype(np.float32))
+        w = synth.f32_to_bf16_bits((rng.standard_normal((ch, d_model)) / np.sqrt(d_model)).astype(np.float32))
+    # rows scattered over two sequences, positions in no particular order
+    slots = rng.permutation(2 * capacity)[:n]
+    seq, pos = (slots // capacity).astype(np.int32), (slots % capacity).astype(np.int32)
+    gc = m.Cache(2, capacity, idx_heads=heads, idx_k_dtype=dtype)
+    m.csa2_proj_append(gc, dev_u16(x), dev_u16(w), dev_i32(seq), dev_i32(pos))
+    torch.cuda.synchronize()
+    oc = O.OracleCache(2, capacity, idx_heads=heads, idx_k_dtype=dtype)
+    O.project_and_append(oc, x, w, seq, pos)
+    gidx = untile_idx(host(gc.idx_k), heads, oc.idx_k.dtype)
+    return (host(gc.kv_codes), host(gc.kv_scales), gidx), (oc.kv_codes, oc.kv_scales, oc.idx_k)
+
+
+@pytest.mark.parametrize("heads,dtype", [(8, "fp8"), (4, "bf16")])
+@pytest.mark.parametrize("n,d_model", [(1, 32), (100, 512), (200, 1056), (64, 4096)])
+def test_proj_append_bit_exact_on_exact_sums(heads, dtype, n, d_model):
+    announce(f"proj append heads={heads} idx={dtype} n={n} d={d_model}")
+    got, want = _run(heads, dtype, n, d_model, seed=n + d_model)
+    for g, w in zip(got, want):
+        assert np.array_equal(g, w)
+
+
+def test_proj_append_random_inputs_relaxed():
+    announce("proj append random inputs")
+    got, want = _run(8, "fp8", 300, 2048, grid=False, seed=11)
+    for g, w in zip(got, want):
+        frac = float(np.mean(g == w))
+        assert frac >= 0.99, frac
+
+
+def test_proj_append_empty_is_a_no_op():
+    m = lib()
+    gc = m.Cache(1, 64, idx_heads=8, idx_k_dtype="fp8")
+    e = torch.empty((0, 64), dtype=torch.int16, device="cuda")
+    w = torch.zeros((256 + 512, 64), dtype=torch.int16, device="cuda")
+    z = torch.empty(0, dtype=torch.int32, device="cuda")
+    m.csa2_proj_append(gc, e, w, z, z)
+    torch.cuda.synchronize()
+    assert int(host(gc.kv_codes).sum()) == 0
