@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0      # dense E4M3 matrix-core peak of MI355X
+BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak of MI355X
 METRIC = "CSA2 decode queries/s and achieved HBM GB/s (% of peak), 64K and 1M context"
 
 
@@ -43,6 +44,8 @@ def _args():
     p.add_argument("--workload", default="decode_64k_b32")
     p.add_argument("--no-extra", action="store_true", help="skip the 1M-context line item")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--proj-append", action="store_true",
+                   help="also time csa2_proj_append (d_model 4096) on 4096 and 32 tokens")
     p.add_argument("--local-window", type=int, default=0,
                    help="also time the local window branch (csa2_local_attn) over this many rows")
     p.add_argument("--graph", action="store_true", help="replay the step as a captured graph")
@@ -383,6 +386,54 @@ def local_item(name, window, steps, warmup, hip):
                          "traffic": None, "bytes_per_launch": nbytes}}
 
 
+def proj_item(steps, warmup, hip, d_model=4096):
+    """csa2_proj_append alone: n tokens of hidden states (d_model bf16) through
+    the 768 x d_model projection (K, V, 8 E4M3 index-key heads) into the cache.
+    FLOPs per launch 2 n d_model 768; algorithmic bytes: x and w read once, the
+    appended rows (144 B main KV + 512 B index keys) written."""
+    import numpy as np
+    import torch
+    import sparse_attention_fp4_e2m1_amd as m
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(12)
+    ch = 256 + 8 * 64
+    res = {}
+    for n in (4096, 32):
+        cache = m.Cache(1, 4096, idx_heads=8, idx_k_dtype="fp8")
+        x = torch.from_numpy(rng.standard_normal((n, d_model)).astype(np.float32)).to(dev)
+        w = torch.from_numpy((rng.standard_normal((ch, d_model)) / np.sqrt(d_model)).astype(np.float32)).to(dev)
+        x, w = x.to(torch.bfloat16), w.to(torch.bfloat16)
+        seq = torch.zeros(n, dtype=torch.int32, device=dev)
+        pos = torch.arange(n, dtype=torch.int32, device=dev)
+        for _ in range(warmup):
+            m.csa2_proj_append(cache, x, w, seq, pos)
+        stream = torch.cuda.current_stream().cuda_stream
+        a, b = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(a, stream)
+        for _ in range(steps):
+            m.csa2_proj_append(cache, x, w, seq, pos)
+        hip.record(b, stream)
+        torch.cuda.synchronize()
+        ms = hip.elapsed_ms(a, b) / steps
+        hip.destroy(a)
+        hip.destroy(b)
+        flops = 2 * n * d_model * ch
+        nbytes = 2 * n * d_model + 2 * ch * d_model + n * (144 + 512) + 8 * n
+        tf = flops / (ms * 1e-3) / 1e12
+        gb = nbytes / (ms * 1e-3) / 1e9
+        res[f"tokens_{n}"] = {"avg_launch_ms": ms, "tokens_per_s": n / (ms * 1e-3),
+                              "roofline": {"bound": "mfma", "kernel": "proj_append_kernel",
+                                           "achieved": tf, "peak": BF16_PEAK_TFLOPS,
+                                           "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                                           "traffic": None, "flops_per_launch": flops},
+                              "hbm": {"achieved": gb, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                      "frac": gb / HBM_PEAK_GBPS, "bytes_per_launch": nbytes}}
+        del cache, x, w
+    res["d_model"] = d_model
+    return res
+
+
 def synth_prefill(name) -> bool:
     import synth
     return synth.workload(name).prefill > 0
@@ -446,6 +497,9 @@ def main():
             line["extra"][name]["unit"] = "queries/s"
             line["extra"][name]["steps"] = steps
             line["extra"][name]["roofline"] = res2.get("roofline")
+    if args.proj_append:
+        print("[bench] projection + append", file=sys.stderr, flush=True)
+        line["proj_append"] = proj_item(args.steps, args.warmup, hip)
     if args.local_window:
         print(f"[bench] local window branch, {args.local_window} rows", file=sys.stderr, flush=True)
         line["local_window_branch"] = local_item(args.workload, args.local_window, args.steps,
