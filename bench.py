@@ -379,7 +379,45 @@ def local_item(name, window, steps, warmup, hip):
     rows = int(np.minimum(qpos + 1, window).sum())
     nbytes = rows * (2 * 128 + 4) + wl.nq * wl.heads * (128 * 2 + 2 * 128 * 4 + 2 * 4)
     ach = nbytes / (ms * 1e-3) / 1e9
+
+    # the sparse branch alone, both branches as two calls, and both in one
+    # launch (csa2_sparse_local_attn), over the workload's K rows of a
+    # zero-filled FP4 cache of the workload's size (the gather's traffic and
+    # the arithmetic do not depend on the values)
+    cache = m.Cache(wl.batch, wl.context, idx_heads=wl.idx_heads, idx_k_dtype=wl.idx_k_dtype)
+    topk = torch.from_numpy(rng.integers(0, wl.context, (wl.nq, wl.top_k)).astype(np.int32)).to(dev)
+    ws_s = torch.empty(max(m.csa2_sparse_attn_workspace(cache, wl.nq, wl.heads, wl.top_k), 256),
+                       dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(max(int(m.LIB.csa2_sparse_local_attn_workspace(
+        cache.ref, lc.ref, wl.nq, wl.heads, wl.top_k)), 256), dtype=torch.uint8, device=dev)
+
+    def sparse():
+        m.csa2_sparse_attn(cache, q, q_seq, topk, out=out, lse=lse, workspace=ws_s)
+
+    def two_calls():
+        sparse()
+        m.csa2_local_attn(lc, q, q_seq, q_pos, out, lse)
+
+    def fused():
+        m.csa2_sparse_local_attn(cache, lc, q, q_seq, q_pos, topk, out=out, lse=lse, workspace=ws_f)
+
+    times = {}
+    for name, fn in (("sparse_only", sparse), ("sparse_then_local", two_calls), ("fused", fused)):
+        for _ in range(warmup):
+            fn()
+        a, b = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(a, stream)
+        for _ in range(steps):
+            fn()
+        hip.record(b, stream)
+        torch.cuda.synchronize()
+        times[name + "_ms"] = hip.elapsed_ms(a, b) / steps
+        hip.destroy(a)
+        hip.destroy(b)
+    del cache
     return {"window": window, "queries": wl.nq, "heads": wl.heads, "avg_launch_ms": ms,
+            "with_sparse_branch": times,
             "queries_per_s": wl.nq / (ms * 1e-3),
             "roofline": {"bound": "hbm", "kernel": "local_attn_kernel", "achieved": ach,
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,

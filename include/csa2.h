@@ -270,6 +270,29 @@ csa2_status csa2_local_attn(const csa2_local_cache *cache, const uint16_t *q, in
                             float softmax_scale, float *out, float *lse, void *stream);
 
 /*
+ * Both branches of a layer in one pass: the selected FP4 rows (as
+ * csa2_sparse_attn) and the layer's FP8 window rows (as csa2_local_attn) in
+ * one softmax, written to out and lse directly.  The window rows become extra
+ * splits of the same launch, merged with the selected rows' splits by one
+ * combine, so the window costs no launch of its own.
+ *   cache, q, n_heads, q_seq, nq, topk, top_k, softmax_scale: as for
+ *              csa2_sparse_attn; local, q_pos: as for csa2_local_attn
+ *              (local->batch >= cache->batch; q_seq indexes both).
+ *   out, lse   [nq][n_heads][dv], [nq][n_heads] (lse may be NULL): the
+ *              softmax attention over the union of both sets of rows.
+ *   workspace  device scratch of csa2_sparse_local_attn_workspace bytes.
+ * Supported, device preconditions and errors: as csa2_sparse_attn together
+ * with csa2_local_attn (CSA2_ERR_SHAPE also for local->batch < batch).
+ */
+size_t csa2_sparse_local_attn_workspace(const csa2_cache *cache, const csa2_local_cache *local,
+                                        int32_t nq, int32_t n_heads, int32_t top_k);
+csa2_status csa2_sparse_local_attn(const csa2_cache *cache, const csa2_local_cache *local,
+                                   const uint16_t *q, int32_t n_heads, const int32_t *q_seq,
+                                   const int32_t *q_pos, int32_t nq, const int32_t *topk,
+                                   int32_t top_k, float softmax_scale, float *out, float *lse,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The encoder-side projection fused into quantize-and-append (aiwiki
  * "DeepSeek V4.1-Flash", section "Causal Encoder-Decoder": a decoder layer's
  * global keys and values are projected from the final causal-encoder hidden

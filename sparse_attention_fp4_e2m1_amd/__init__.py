@@ -8,6 +8,6 @@ from .csa2 import (  # noqa: F401
     Cache, Csa2Error, csa2_kv_append, csa2_index_topk, csa2_index_topk_workspace,
     csa2_sparse_attn, csa2_sparse_attn_workspace, LocalCache, csa2_local_append, csa2_local_attn,
     csa2_local_clear, csa2_kv_export, csa2_kv_export_bytes, csa2_kv_import,
-    csa2_proj_append,
+    csa2_proj_append, csa2_sparse_local_attn,
     LIB, LIB_PATH,
 )

@@ -55,6 +55,9 @@ def _load():
         "csa2_local_append": (I32, [ctypes.POINTER(csa2_local_cache), P, P, P, P, I32, P]),
         "csa2_local_attn": (I32, [ctypes.POINTER(csa2_local_cache), P, I32, P, P, I32, F32, P, P, P]),
         "csa2_proj_append": (I32, [C, P, I32, P, P, P, I32, P]),
+        "csa2_sparse_local_attn_workspace": (SZ, [C, ctypes.POINTER(csa2_local_cache), I32, I32, I32]),
+        "csa2_sparse_local_attn": (I32, [C, ctypes.POINTER(csa2_local_cache), P, I32, P, P, I32, P,
+                                         I32, F32, P, P, P, SZ, P]),
         "csa2_kv_export_bytes": (SZ, [C, I32]),
         "csa2_kv_export": (I32, [C, I32, I32, P, SZ, P]),
         "csa2_kv_import": (I32, [C, I32, I32, P, SZ, P]),
@@ -317,3 +320,32 @@ def csa2_proj_append(cache: Cache, x, w, seq, pos, stream=None) -> None:
     _need(pos, "pos", _I32, (n,), d)
     _check(LIB.csa2_proj_append(cache.ref, _ptr(x), d_model, _ptr(w), _ptr(seq), _ptr(pos), n,
                                 _stream(stream)), "csa2_proj_append")
+
+
+def csa2_sparse_local_attn(cache: Cache, local: LocalCache, q, q_seq, q_pos, topk,
+                           softmax_scale: Optional[float] = None, out=None, lse=None,
+                           workspace=None, stream=None):
+    """Both branches in one pass (include/csa2.h); returns (out, lse)."""
+    d = cache.device
+    nq, n_heads = q.shape[0], q.shape[1]
+    top_k = topk.shape[1]
+    _need(q, "q", _B16, (nq, n_heads, cache.dk), d)
+    _need(q_seq, "q_seq", _I32, (nq,), d)
+    _need(q_pos, "q_pos", _I32, (nq,), d)
+    _need(topk, "topk", _I32, (nq, top_k), d)
+    if out is None:
+        out = torch.empty((nq, n_heads, cache.dv), dtype=torch.float32, device=d)
+    if lse is None:
+        lse = torch.empty((nq, n_heads), dtype=torch.float32, device=d)
+    _need(out, "out", (torch.float32,), (nq, n_heads, cache.dv), d)
+    _need(lse, "lse", (torch.float32,), (nq, n_heads), d)
+    ws = int(LIB.csa2_sparse_local_attn_workspace(cache.ref, local.ref, nq, n_heads, top_k))
+    if workspace is None:
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=d)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(cache.dk)
+    _check(LIB.csa2_sparse_local_attn(cache.ref, local.ref, _ptr(q), n_heads, _ptr(q_seq),
+                                      _ptr(q_pos), nq, _ptr(topk), top_k, float(softmax_scale),
+                                      _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)), "csa2_sparse_local_attn")
+    return out, lse

@@ -155,6 +155,37 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
   return CSA2_OK;
 }
 
+size_t csa2_sparse_local_attn_workspace(const csa2_cache *cache, const csa2_local_cache *local,
+                                        int32_t nq, int32_t n_heads, int32_t top_k) {
+  if (check_cache(cache, false) != CSA2_OK || check_local(local) != CSA2_OK) return 0;
+  if (nq < 0 || n_heads < 16 || n_heads > 128 || n_heads % 16 != 0) return 0;
+  if (top_k < 1 || top_k > kMaxTopK) return 0;
+  return attn_workspace_layout(*cache, nq, n_heads, top_k, local->window).total;
+}
+
+csa2_status csa2_sparse_local_attn(const csa2_cache *cache, const csa2_local_cache *local,
+                                   const uint16_t *q, int32_t n_heads, const int32_t *q_seq,
+                                   const int32_t *q_pos, int32_t nq, const int32_t *topk,
+                                   int32_t top_k, float softmax_scale, float *out, float *lse,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+  csa2_status st = check_cache(cache, false);
+  if (st != CSA2_OK) return st;
+  if ((st = check_local(local)) != CSA2_OK) return st;
+  if (local->batch < cache->batch) return CSA2_ERR_SHAPE;
+  if (n_heads < 16 || n_heads > 128 || n_heads % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  if (nq < 0 || top_k < 1 || top_k > kMaxTopK || nq > 65535) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (q == nullptr || q_seq == nullptr || q_pos == nullptr || topk == nullptr || out == nullptr)
+    return CSA2_ERR_NULL;
+  const AttnWorkspace L = attn_workspace_layout(*cache, nq, n_heads, top_k, local->window);
+  if (workspace == nullptr || workspace_bytes < L.total) return CSA2_ERR_WORKSPACE;
+  if (launch_sparse_attn(*cache, q, n_heads, q_seq, nq, topk, top_k, softmax_scale, out, lse,
+                         static_cast<uint8_t *>(workspace), L, (hipStream_t)stream, local,
+                         q_pos) != hipSuccess)
+    return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
 csa2_status csa2_local_append(const csa2_local_cache *cache, const uint16_t *k, const uint16_t *v,
                               const int32_t *seq, const int32_t *pos, int32_t n, void *stream) {
   csa2_status st = check_local(cache);

@@ -37,7 +37,8 @@ constexpr int kMaxRowsPerSplit = 2048;
 constexpr int kTargetGroups = 256;            // workgroups aimed for (one per CU)
 constexpr int kTwoSubMinGroups = 128;         // see rows_per_split
 constexpr int kMaxSplits = 256;               // splits of one query, at most
-constexpr int kCombineBatch = 32;             // split outputs per round of combine loads
+constexpr int kCombineBatch = 32;
+constexpr int kLocalRowsPerSplit = 128;       // window rows per split of the fused call             // split outputs per round of combine loads
 static_assert(kTargetGroups <= kMaxSplits && (65536 + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit <= kMaxSplits,
               "every accepted top_k fits the combine's split table");
 constexpr float kLog2e = 1.4426950408889634f;
@@ -293,6 +294,104 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
 // dequantization and softmax phases of one behind the others'.  With a
 // single split the results are final (normalized output and lse); otherwise
 // partial (O, max, sum) per split go to attn_combine_kernel.
+// Q fragment (B operand): head 16*wave + l16, channels 32g..32g+31, in fp16,
+// negated when the softmax scale is negative.
+__device__ __forceinline__ void load_q(const uint16_t *__restrict__ qg, int q, int n_heads,
+                                       int wave, int l16, int g, bool q_negate, f16x8 (&qf)[4]) {
+  const uint16_t *qp = qg + ((int64_t)q * n_heads + wave * 16 + l16) * 128 + 32 * g;
+  const uint32_t flip = q_negate ? 0x80008000u : 0u;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(qp + 8 * s);
+    const uint32_t w[4] = {raw.x ^ flip, raw.y ^ flip, raw.z ^ flip, raw.w ^ flip};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f16x2 h = __builtin_convertvector(
+          (f32x2{__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xFFFF0000u)}), f16x2);
+      qf[s][2 * e] = h[0];
+      qf[s][2 * e + 1] = h[1];
+    }
+  }
+}
+
+// Window rows [first, first + count) of a query at position p, whose window
+// holds nall = min(window, p + 1) rows (row r = position p - nall + 1 + r):
+// rows[i] = the slot of row first + i when the slot holds that position,
+// else -1; padded with -1 to whole sub-chunks.  Returns the sub-chunk count.
+__device__ __forceinline__ int fill_window_rows(const int32_t *__restrict__ lpos, int64_t sbase,
+                                                int window, int32_t p, int nall, int first,
+                                                int count, int32_t *rows, int tid, int nthreads) {
+  const int nsub = (count + kSub - 1) / kSub;
+  for (int r = tid; r < nsub * kSub; r += nthreads) {
+    int32_t slot = -1;
+    if (r < count) {
+      const int32_t pr = p - nall + 1 + first + r;
+      const int32_t sl = pr % window;
+      if (lpos[sbase + sl] == pr) slot = sl;
+    }
+    rows[r] = slot;
+  }
+  return nsub;
+}
+
+// One sub-chunk of window rows (slots rows[base..base+63], -1 read as slot 0
+// and masked later) into the LDS layouts of the FP4 path: E4M3 codes convert
+// exactly to fp16.  K^ fragment (tile t, k-step s, lane l) = row 16t + l%16,
+// channels 32(l/16) + 8s .. +7; V^ transposed as (row 2pr, row 2pr+1) fp16
+// pairs per channel.
+template <int kThreads>
+__device__ __forceinline__ void stage_local(const uint8_t *__restrict__ lk,
+                                            const uint8_t *__restrict__ lv, int64_t sbase,
+                                            const int32_t *rows, int base, uint4 *kq,
+                                            _Float16 *vt, int tid) {
+  for (int item = tid; item < 4 * 4 * 64; item += kThreads) {
+    const int t = item >> 8, s = (item >> 6) & 3, l = item & 63;
+    const int slot = max(rows[base + 16 * t + (l & 15)], 0);
+    const uint2 w = *reinterpret_cast<const uint2 *>(lk + (sbase + slot) * 128 + 32 * (l >> 4) + 8 * s);
+    kq[(t * 4 + s) * 64 + l] = make_uint4(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true)));
+  }
+  for (int item = tid; item < 32 * 8; item += kThreads) {
+    const int pr = item & 31, b = item >> 5;
+    const int sa = max(rows[base + 2 * pr], 0), sb = max(rows[base + 2 * pr + 1], 0);
+    const uint4 wa = *reinterpret_cast<const uint4 *>(lv + (sbase + sa) * 128 + 16 * b);
+    const uint4 wb = *reinterpret_cast<const uint4 *>(lv + (sbase + sb) * 128 + 16 * b);
+    const uint32_t xa[4] = {wa.x, wa.y, wa.z, wa.w}, xb[4] = {wb.x, wb.y, wb.z, wb.w};
+    uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + 2 * pr);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a[2] = {
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xa[w], 1.0f, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xa[w], 1.0f, true))};
+      const uint32_t bb[2] = {
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xb[w], 1.0f, false)),
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xb[w], 1.0f, true))};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // channels 4w + 2h, 4w + 2h + 1 of the block
+        const int e = 2 * w + h;
+        dst[((2 * e) * kVtPitch) / 2] = __builtin_amdgcn_perm(bb[h], a[h], 0x05040100u);
+        dst[((2 * e + 1) * kVtPitch) / 2] = __builtin_amdgcn_perm(bb[h], a[h], 0x07060302u);
+      }
+    }
+  }
+}
+
+// A split's unnormalized output and (max, sum) statistics, for the combine.
+__device__ __forceinline__ void store_partial(float *__restrict__ part_acc,
+                                              float2 *__restrict__ part_ml, int q, int splits,
+                                              int split, int n_heads, int head, int g,
+                                              const f32x4 (&o)[8], float m_run, float l_run) {
+  const int64_t pbase = ((int64_t)q * splits + split) * n_heads;
+  float *pq = part_acc + (pbase + head) * 128 + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4 *>(pq + dt * 16) = o[dt];
+  if (g == 0) part_ml[pbase + head] = make_float2(m_run, l_run);
+}
+
 template <int kWaves>
 __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial_kernel(
     const uint8_t *__restrict__ kv_codes, const uint8_t *__restrict__ kv_scales,
@@ -300,7 +399,9 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
     const int32_t *__restrict__ q_seq, const int32_t *__restrict__ topk, int32_t top_k,
     int32_t rows_per_split, float scale_log2, bool q_negate, float *__restrict__ part_acc,
     float2 *__restrict__ part_ml, int32_t splits, float *__restrict__ out,
-    float *__restrict__ lse) {
+    float *__restrict__ lse, int32_t sparse_splits, const uint8_t *__restrict__ lk,
+    const uint8_t *__restrict__ lv, const int32_t *__restrict__ lpos, int32_t window,
+    const int32_t *__restrict__ q_pos) {
   constexpr int kThreads = kWaves * 64;
   __shared__ int32_t rows[kMaxRowsPerSplit + 2 * kSub];
   __shared__ uint4 kq[4 * 4 * 64];
@@ -313,6 +414,32 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
   const int wave = tid >> 6;
   const int g = lane >> 4;
   const int l16 = lane & 15;
+
+  if (split >= sparse_splits) {
+    // a split of the layer's FP8 window rows (kLocalRowsPerSplit of them),
+    // attended like the sparse rows and merged by the same combine
+    const int32_t p = q_pos[q];
+    const int nall = min(window, p + 1);
+    const int first = (split - sparse_splits) * kLocalRowsPerSplit;
+    const int count = max(0, min(kLocalRowsPerSplit, nall - first));
+    const int64_t sbase = (int64_t)q_seq[q] * window;
+    const int nsub = fill_window_rows(lpos, sbase, window, p, nall, first, count, rows, tid, kThreads);
+    f16x8 qf[4];
+    load_q(qg, q, n_heads, wave, l16, g, q_negate, qf);
+    __syncthreads();
+    f32x4 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;
+    for (int c = 0; c < nsub; ++c) {
+      stage_local<kThreads>(lk, lv, sbase, rows, c * kSub, kq, vt, tid);
+      __syncthreads();
+      attend_sub(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+      __syncthreads();
+    }
+    store_partial(part_acc, part_ml, q, splits, split, n_heads, wave * 16 + l16, g, o, m_run, l_run);
+    return;
+  }
   const int64_t seq_base = (int64_t)q_seq[q] * capacity;
   const uint8_t *codes = kv_codes + seq_base * 128;
   const uint8_t *scales = kv_scales + seq_base * 16;
@@ -323,25 +450,8 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
   for (int r = tid; r < (nsub + 2) * kSub; r += kThreads)
     rows[r] = r < nrows ? topk[(int64_t)q * top_k + row0 + r] : -1;
 
-  // Q fragment (B operand): head 16*wave + l16, channels 32g..32g+31, in fp16,
-  // negated when the softmax scale is negative
   f16x8 qf[4];
-  {
-    const uint16_t *qp = qg + ((int64_t)q * n_heads + wave * 16 + l16) * 128 + 32 * g;
-    const uint32_t flip = q_negate ? 0x80008000u : 0u;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 raw = *reinterpret_cast<const uint4 *>(qp + 8 * s);
-      const uint32_t w[4] = {raw.x ^ flip, raw.y ^ flip, raw.z ^ flip, raw.w ^ flip};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 h = __builtin_convertvector(
-            (f32x2{__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xFFFF0000u)}), f16x2);
-        qf[s][2 * e] = h[0];
-        qf[s][2 * e + 1] = h[1];
-      }
-    }
-  }
+  load_q(qg, q, n_heads, wave, l16, g, q_negate, qf);
   __syncthreads();
 
   f32x4 o[8];
@@ -382,11 +492,7 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
       lse[(int64_t)q * n_heads + head] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
     return;
   }
-  const int64_t pbase = ((int64_t)q * splits + split) * n_heads;
-  float *pq = part_acc + (pbase + head) * 128 + 4 * g;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4 *>(pq + dt * 16) = o[dt];
-  if (g == 0) part_ml[pbase + wave * 16 + l16] = make_float2(m_run, l_run);
+  store_partial(part_acc, part_ml, q, splits, split, n_heads, head, g, o, m_run, l_run);
 }
 
 // One workgroup per (query, 4 heads): thread (head, d) merges every split.
@@ -484,36 +590,11 @@ __global__ void __launch_bounds__(kWaves * 64) local_attn_kernel(
   const int g = lane >> 4;
   const int l16 = lane & 15;
   const int32_t p = q_pos[q];
-  const int nrows = min(window, p + 1);   // positions p - nrows + 1 .. p
-  const int nsub = (nrows + kSub - 1) / kSub;
+  const int nall = min(window, p + 1);   // positions p - nall + 1 .. p
   const int64_t sbase = (int64_t)q_seq[q] * window;
-  for (int r = tid; r < nsub * kSub; r += kThreads) {
-    int32_t slot = -1;
-    if (r < nrows) {
-      const int32_t pr = p - nrows + 1 + r;
-      const int32_t sl = pr % window;
-      if (lpos[sbase + sl] == pr) slot = sl;
-    }
-    rows[r] = slot;
-  }
-
+  const int nsub = fill_window_rows(lpos, sbase, window, p, nall, 0, nall, rows, tid, kThreads);
   f16x8 qf[4];
-  {
-    const uint16_t *qp = qg + ((int64_t)q * n_heads + wave * 16 + l16) * 128 + 32 * g;
-    const uint32_t flip = q_negate ? 0x80008000u : 0u;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 raw = *reinterpret_cast<const uint4 *>(qp + 8 * s);
-      const uint32_t w[4] = {raw.x ^ flip, raw.y ^ flip, raw.z ^ flip, raw.w ^ flip};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 h = __builtin_convertvector(
-            (f32x2{__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xFFFF0000u)}), f16x2);
-        qf[s][2 * e] = h[0];
-        qf[s][2 * e + 1] = h[1];
-      }
-    }
-  }
+  load_q(qg, q, n_heads, wave, l16, g, q_negate, qf);
   __syncthreads();
 
   f32x4 o[8];
@@ -522,44 +603,7 @@ __global__ void __launch_bounds__(kWaves * 64) local_attn_kernel(
   float m_run = -INFINITY;
   float l_run = 0.0f;
   for (int c = 0; c < nsub; ++c) {
-    // K^: fragment (tile t, k-step s, lane l) = row 16t + l%16, channels
-    // 32(l/16) + 8s .. +7
-    for (int item = tid; item < 4 * 4 * 64; item += kThreads) {
-      const int t = item >> 8, s = (item >> 6) & 3, l = item & 63;
-      const int slot = max(rows[c * kSub + 16 * t + (l & 15)], 0);
-      const uint2 w = *reinterpret_cast<const uint2 *>(lk + (sbase + slot) * 128 + 32 * (l >> 4) + 8 * s);
-      kq[(t * 4 + s) * 64 + l] = make_uint4(
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false)),
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true)),
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false)),
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true)));
-    }
-    // V^ transposed: item (row pair pr, block b) = rows 2pr, 2pr+1, channels
-    // 16b .. 16b+15, written as (row 2pr, row 2pr+1) fp16 pairs per channel
-    for (int item = tid; item < 32 * 8; item += kThreads) {
-      const int pr = item & 31, b = item >> 5;
-      const int sa = max(rows[c * kSub + 2 * pr], 0), sb = max(rows[c * kSub + 2 * pr + 1], 0);
-      const uint4 wa = *reinterpret_cast<const uint4 *>(lv + (sbase + sa) * 128 + 16 * b);
-      const uint4 wb = *reinterpret_cast<const uint4 *>(lv + (sbase + sb) * 128 + 16 * b);
-      const uint32_t xa[4] = {wa.x, wa.y, wa.z, wa.w}, xb[4] = {wb.x, wb.y, wb.z, wb.w};
-      uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + 2 * pr);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a[2] = {
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xa[w], 1.0f, false)),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xa[w], 1.0f, true))};
-        const uint32_t bb[2] = {
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xb[w], 1.0f, false)),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xb[w], 1.0f, true))};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // channels 4w + 2h, 4w + 2h + 1 of the block
-          const int e = 2 * w + h;
-          dst[((2 * e) * kVtPitch) / 2] = __builtin_amdgcn_perm(bb[h], a[h], 0x05040100u);
-          dst[((2 * e + 1) * kVtPitch) / 2] = __builtin_amdgcn_perm(bb[h], a[h], 0x07060302u);
-        }
-      }
-    }
+    stage_local<kThreads>(lk, lv, sbase, rows, c * kSub, kq, vt, tid);
     __syncthreads();
     attend_sub(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
     __syncthreads();   // the stage is rewritten next
@@ -590,9 +634,9 @@ __global__ void __launch_bounds__(kWaves * 64) local_attn_kernel(
 // grid still has kTargetGroups workgroups, at most kMaxRowsPerSplit, a
 // multiple of the sub-chunk.  Splits of one sub-chunk become two (whose
 // gathers overlap) when that still leaves kTwoSubMinGroups workgroups.
-int32_t rows_per_split(int32_t nq, int32_t top_k) {
+int32_t rows_per_split(int32_t nq, int32_t top_k, int32_t max_splits) {
   const int32_t subs = (top_k + kSub - 1) / kSub;
-  int32_t splits = (kTargetGroups + nq - 1) / nq;
+  int32_t splits = std::min((kTargetGroups + nq - 1) / nq, max_splits);
   splits = std::max(1, std::min(splits, subs));
   if (subs / splits < 2 && (int64_t)nq * (subs / 2) >= kTwoSubMinGroups)
     splits = std::max(1, subs / 2);
@@ -604,13 +648,16 @@ int32_t rows_per_split(int32_t nq, int32_t top_k) {
 }  // namespace
 
 AttnWorkspace attn_workspace_layout(const csa2_cache &c, int32_t nq, int32_t n_heads,
-                                    int32_t top_k) {
+                                    int32_t top_k, int32_t window) {
   AttnWorkspace w;
-  const int32_t rps = rows_per_split(nq, top_k);
+  w.local_splits = window > 0 ? (window + kLocalRowsPerSplit - 1) / kLocalRowsPerSplit : 0;
+  const int32_t rps = rows_per_split(nq, top_k, kMaxSplits - w.local_splits);
   w.splits = (top_k + rps - 1) / rps;
-  // splits <= max(kTargetGroups, top_k / kMaxRowsPerSplit) <= kMaxSplits for top_k <= 65536
-  // a single split writes the final results directly (no partials)
-  const size_t units = w.splits > 1 ? (size_t)nq * w.splits * n_heads : 0;
+  // sparse splits <= max(kMaxSplits - local splits, top_k / kMaxRowsPerSplit), and
+  // top_k / kMaxRowsPerSplit <= 32 for top_k <= 65536: the total stays <= kMaxSplits.
+  // A single split writes the final results directly (no partials).
+  const int32_t total = w.splits + w.local_splits;
+  const size_t units = total > 1 ? (size_t)nq * total * n_heads : 0;
   w.part_acc = 0;
   w.part_ml = align256(units * c.dv * sizeof(float));
   w.total = std::max<size_t>(256, align256(w.part_ml + units * sizeof(float2)));
@@ -620,20 +667,27 @@ AttnWorkspace attn_workspace_layout(const csa2_cache &c, int32_t nq, int32_t n_h
 hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_heads,
                               const int32_t *q_seq, int32_t nq, const int32_t *topk,
                               int32_t top_k, float softmax_scale, float *out, float *lse,
-                              uint8_t *ws, const AttnWorkspace &L, hipStream_t s) {
+                              uint8_t *ws, const AttnWorkspace &L, hipStream_t s,
+                              const csa2_local_cache *lc, const int32_t *q_pos) {
   float *acc = reinterpret_cast<float *>(ws + L.part_acc);
   float2 *ml = reinterpret_cast<float2 *>(ws + L.part_ml);
   const float scale_log2 = fabsf(softmax_scale) * kLog2e;
   const bool q_negate = softmax_scale < 0.0f;
-  const int32_t rps = rows_per_split(nq, top_k);
-  if (L.splits > kMaxSplits) return hipErrorInvalidValue;
-  dim3 grid((unsigned)L.splits, (unsigned)nq);
+  const int32_t rps = rows_per_split(nq, top_k, kMaxSplits - L.local_splits);
+  const int32_t total = L.splits + L.local_splits;
+  if (total > kMaxSplits || (L.local_splits > 0 && (lc == nullptr || q_pos == nullptr)))
+    return hipErrorInvalidValue;
+  const uint8_t *lk = lc ? lc->k : nullptr, *lv = lc ? lc->v : nullptr;
+  const int32_t *lpos = lc ? lc->pos : nullptr;
+  const int32_t window = lc ? lc->window : 0;
+  dim3 grid((unsigned)total, (unsigned)nq);
   const int waves = n_heads / 16;
 #define CSA2_ATTN_CASE(W)                                                                        \
   case W:                                                                                        \
     hipLaunchKernelGGL(attn_partial_kernel<W>, grid, dim3(W * 64), 0, s, c.kv_codes, c.kv_scales, \
                        (int64_t)c.capacity, q, n_heads, q_seq, topk, top_k, rps, scale_log2,    \
-                       q_negate, acc, ml, L.splits, out, lse);                                   \
+                       q_negate, acc, ml, total, out, lse, L.splits, lk, lv, lpos, window,      \
+                       q_pos);                                                                   \
     break;
   switch (waves) {
     CSA2_ATTN_CASE(1)
@@ -648,9 +702,9 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
       return hipErrorInvalidValue;
   }
 #undef CSA2_ATTN_CASE
-  if (L.splits == 1) return hipGetLastError();
+  if (total == 1) return hipGetLastError();
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(n_heads / 4), (unsigned)nq), dim3(512),
-                     0, s, acc, ml, n_heads, L.splits, out, lse);
+                     0, s, acc, ml, n_heads, total, out, lse);
   return hipGetLastError();
 }
 

@@ -91,16 +91,19 @@ struct AttnWorkspace {
   size_t part_acc = 0;     // float [nq][splits][heads][dv]
   size_t part_ml = 0;      // float2 [nq][splits][heads]  (max, sum) of exp2-scaled scores
   size_t total = 0;
-  int32_t splits = 0;
+  int32_t splits = 0;         // splits of the selected rows
+  int32_t local_splits = 0;   // splits of the window rows (fused call)
 };
 
 AttnWorkspace attn_workspace_layout(const csa2_cache &c, int32_t nq, int32_t n_heads,
-                                    int32_t top_k);
+                                    int32_t top_k, int32_t window = 0);
 
 hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_heads,
                               const int32_t *q_seq, int32_t nq, const int32_t *topk,
                               int32_t top_k, float softmax_scale, float *out, float *lse,
-                              uint8_t *ws, const AttnWorkspace &layout, hipStream_t stream);
+                              uint8_t *ws, const AttnWorkspace &layout, hipStream_t stream,
+                              const csa2_local_cache *lc = nullptr,
+                              const int32_t *q_pos = nullptr);
 
 hipError_t launch_proj_append(const csa2_cache &c, const uint16_t *x, int32_t d_model,
                               const uint16_t *w, const int32_t *seq, const int32_t *pos,

@@ -29,6 +29,7 @@ def test_header_declares_the_boundary():
                  "csa2_index_topk_workspace", "csa2_sparse_attn_workspace",
                  "csa2_local_append", "csa2_local_attn", "csa2_local_clear",
                  "csa2_kv_export", "csa2_kv_export_bytes", "csa2_kv_import", "csa2_proj_append",
+                 "csa2_sparse_local_attn", "csa2_sparse_local_attn_workspace",
                  "csa2_strerror", "csa2_abi_version"):
         assert want in names
 

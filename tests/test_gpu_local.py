@@ -113,3 +113,53 @@ def test_local_attention_nothing_visible():
     out, lse, ro, rl, _ = _run(64, 64, np.full((2, 8), -1, np.int32), np.array([2400, 2400], np.int32),
                                np.array([0, 2], np.int32))
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def _run_fused(heads, window, topk, qpos, qseq, scale=None, qset=0):
+    m = lib()
+    wl, gc, oc = _global(heads)
+    gl, ol = _local(window)
+    q = synth.gen_queries(wl, qset).q
+    q = np.concatenate([q] * ((len(qpos) + len(q) - 1) // len(q)))[: len(qpos)]
+    out, lse = m.csa2_sparse_local_attn(gc, gl, dev_u16(q), dev_i32(qseq), dev_i32(qpos),
+                                        dev_i32(topk), softmax_scale=scale)
+    torch.cuda.synchronize()
+    s = DEFAULT_SCALE if scale is None else float(np.float32(scale))
+    ref = [O.attention_with_window(q[i], oc, int(qseq[i]), topk[i], ol, int(qpos[i]), s)
+           for i in range(len(qpos))]
+    return host(out), host(lse), np.stack([r[0] for r in ref]), np.stack([r[1] for r in ref])
+
+
+@pytest.mark.parametrize("heads", [16, 64])
+@pytest.mark.parametrize("window", [64, 300, 1024])
+def test_fused_both_branches(heads, window):
+    # one launch for both sets of rows: the same cases as the two-call merge
+    announce(f"fused sparse+local heads={heads} window={window}")
+    qseq = np.array([0, 1, 2, 0, 2], np.int32)
+    qpos = np.array([2999, 40, 2999, 2400, 2995], np.int32)
+    rng = np.random.default_rng(heads + window + 1)
+    topk = rng.integers(0, 2400, (5, 256)).astype(np.int32)
+    topk[2, rng.random(256) < 0.3] = -1
+    topk[4] = -1
+    out, lse, ro, rl = _run_fused(heads, window, topk, qpos, qseq)
+    rel, dl = attn_errors(out, lse, ro, rl)
+    assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL, (rel.max(), dl.max())
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_fused_single_query_many_splits(scale):
+    # one query and a long list: the selected rows take nearly every split the
+    # combine holds, the window's splits come on top
+    announce(f"fused one query k=3000 scale={scale}")
+    topk = np.random.default_rng(4).integers(0, 3000, (1, 3000)).astype(np.int32)
+    out, lse, ro, rl = _run_fused(48, 300, topk, np.array([2999], np.int32),
+                                  np.array([0], np.int32), scale=scale)
+    rel, dl = attn_errors(out, lse, ro, rl)
+    assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL, (rel.max(), dl.max())
+
+
+def test_fused_nothing_visible():
+    announce("fused nothing visible")
+    out, lse, _, _ = _run_fused(64, 64, np.full((2, 8), -1, np.int32),
+                                np.array([2400, 2400], np.int32), np.array([0, 2], np.int32))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
