@@ -43,7 +43,8 @@ def _run(heads, dtype, n, d_model, grid=True, seed=0, capacity=512):
 
 
 @pytest.mark.parametrize("heads,dtype", [(8, "fp8"), (4, "bf16")])
-@pytest.mark.parametrize("n,d_model", [(1, 32), (100, 512), (200, 1056), (64, 4096)])
+@pytest.mark.parametrize("n,d_model", [(1, 32), (100, 512), (200, 1056), (64, 4096), (257, 96),
+                                       (300, 512), (1000, 1056)])
 def test_proj_append_bit_exact_on_exact_sums(heads, dtype, n, d_model):
     announce(f"proj append heads={heads} idx={dtype} n={n} d={d_model}")
     got, want = _run(heads, dtype, n, d_model, seed=n + d_model)
