@@ -392,7 +392,9 @@ __device__ __forceinline__ void store_partial(float *__restrict__ part_acc,
   if (g == 0) part_ml[pbase + head] = make_float2(m_run, l_run);
 }
 
-template <int kWaves>
+// kWithLocal: the launch also holds the window splits (csa2_sparse_local_attn); the
+// sparse-only instantiation carries none of their code.
+template <int kWaves, bool kWithLocal>
 __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial_kernel(
     const uint8_t *__restrict__ kv_codes, const uint8_t *__restrict__ kv_scales,
     int64_t capacity, const uint16_t *__restrict__ qg, int32_t n_heads,
@@ -415,7 +417,7 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
   const int g = lane >> 4;
   const int l16 = lane & 15;
 
-  if (split >= sparse_splits) {
+  if (kWithLocal && split >= sparse_splits) {
     // a split of the layer's FP8 window rows (kLocalRowsPerSplit of them),
     // attended like the sparse rows and merged by the same combine
     const int32_t p = q_pos[q];
@@ -684,10 +686,16 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
   const int waves = n_heads / 16;
 #define CSA2_ATTN_CASE(W)                                                                        \
   case W:                                                                                        \
-    hipLaunchKernelGGL(attn_partial_kernel<W>, grid, dim3(W * 64), 0, s, c.kv_codes, c.kv_scales, \
-                       (int64_t)c.capacity, q, n_heads, q_seq, topk, top_k, rps, scale_log2,    \
-                       q_negate, acc, ml, total, out, lse, L.splits, lk, lv, lpos, window,      \
-                       q_pos);                                                                   \
+    if (L.local_splits > 0)                                                                      \
+      hipLaunchKernelGGL((attn_partial_kernel<W, true>), grid, dim3(W * 64), 0, s, c.kv_codes,   \
+                         c.kv_scales, (int64_t)c.capacity, q, n_heads, q_seq, topk, top_k, rps,  \
+                         scale_log2, q_negate, acc, ml, total, out, lse, L.splits, lk, lv, lpos, \
+                         window, q_pos);                                                         \
+    else                                                                                         \
+      hipLaunchKernelGGL((attn_partial_kernel<W, false>), grid, dim3(W * 64), 0, s, c.kv_codes,  \
+                         c.kv_scales, (int64_t)c.capacity, q, n_heads, q_seq, topk, top_k, rps,  \
+                         scale_log2, q_negate, acc, ml, total, out, lse, L.splits, lk, lv, lpos, \
+                         window, q_pos);                                                         \
     break;
   switch (waves) {
     CSA2_ATTN_CASE(1)
