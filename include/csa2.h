@@ -47,7 +47,7 @@ typedef enum {
   CSA2_OK = 0,
   CSA2_ERR_NULL = 1,         /* a required pointer is NULL */
   CSA2_ERR_SHAPE = 2,        /* a size is out of range */
-  CSA2_ERR_UNSUPPORTED = 3,  /* a dimension or dtype this build does not implement */
+  CSA2_ERR_UNSUPPORTED = 3,  /* a dimension or dtype the library does not implement */
   CSA2_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the query function returns */
   CSA2_ERR_HIP = 5,          /* a HIP launch reported an error */
   CSA2_ERR_ARG = 6           /* inconsistent arguments (e.g. mode vs. pool/reuse pointers) */

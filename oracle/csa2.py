@@ -254,7 +254,7 @@ def index_scores_exact(q: np.ndarray, keys: np.ndarray):
     bits; float64 carries 53, in any order.
 
     q: float32 [H, D]; keys: float32 [n, H, D]; returns (float64 [n], float64 [n]).
-    Used to judge index sets of a scorer whose fp32 sums follow another order.
+    Used to check index sets of a scorer whose fp32 sums follow another order.
     """
     q = np.asarray(q, np.float64).reshape(-1)
     k = np.asarray(keys, np.float64).reshape(len(keys), -1)
