@@ -133,10 +133,10 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
 // V4.1-Flash", section "Causal Encoder-Decoder": the decoder's global keys and
 // values are projected from the final causal-encoder hidden states).  One
 // workgroup computes a tile of 16 kRT tokens x 16 kCT output channels of
-// Y = X W^T on matrix cores (bf16 operands, fp32 accumulation).  Its four
-// waves split the contraction (wave w takes k-steps w, w + 4, ...) and each
+// Y = X W^T on matrix cores (bf16 operands, fp32 accumulation).  Its kW
+// waves split the contraction (wave w takes k-steps w, w + kW, ...) and each
 // holds the whole tile, so every operand fragment feeds kRT or kCT products;
-// the four partial tiles are summed in LDS in wave order, rounded to bf16 and
+// the kW partial tiles are summed in LDS in wave order, rounded to bf16 and
 // quantized exactly as kv_append_kernel does.  Output channels: K 0..127,
 // V 128..255, index keys 256.. (head-major).
 // Operand fragments of v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16
@@ -151,8 +151,8 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int kRT, int kCT>
-__global__ void __launch_bounds__(256) proj_append_kernel(
+template <int kRT, int kCT, int kW>
+__global__ void __launch_bounds__(64 * kW) proj_append_kernel(
     uint8_t *__restrict__ kv_codes, uint8_t *__restrict__ kv_scales, uint8_t *__restrict__ idx_k,
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int32_t d_model,
     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, int32_t n,
@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(256) proj_append_kernel(
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) acc[rt][ct] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 2
-  for (int k0 = 32 * wave; k0 < d_model; k0 += 128) {
+  for (int k0 = 32 * wave; k0 < d_model; k0 += 32 * kW) {
     bf16x8 a[kRT];
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt)
@@ -194,7 +194,7 @@ __global__ void __launch_bounds__(256) proj_append_kernel(
     }
   }
   // sum of the four partial tiles, wave 0 first
-  for (int wv = 0; wv < 4; ++wv) {
+  for (int wv = 0; wv < kW; ++wv) {
     if (wave == wv) {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(256) proj_append_kernel(
   // (token, 16-channel block): K or V block -> E4M3 scale and E2M1 codes;
   // index-key block -> two groups of 8 channels, bf16 or E4M3
   const int64_t seq_bytes = (int64_t)capacity * H * 64 * esz;
-  for (int item = tid; item < kRows * kCT; item += 256) {
+  for (int item = tid; item < kRows * kCT; item += 64 * kW) {
     const int r = item / kCT, j = item % kCT;
     const int row = r0 + r;
     if (row >= n) continue;
@@ -283,19 +283,20 @@ __global__ void __launch_bounds__(256) local_clear_kernel(int32_t *__restrict__ 
 hipError_t launch_proj_append(const csa2_cache &c, const uint16_t *x, int32_t d_model,
                               const uint16_t *w, const int32_t *seq, const int32_t *pos,
                               int32_t n, hipStream_t stream) {
-  // 64 x 64 tiles (a wave holds 16 accumulators: three waves per SIMD); below
-  // 256 tokens 32 x 64 tiles, which give twice the workgroups.  Measured at
-  // d_model 4096: 64 x 64 beats 64 x 128 (one wave per SIMD) by 1.4x at 4096
-  // tokens; 32 x 64 beats it by 10% at 32 tokens.
+  // 64 x 64 tiles, four waves (a wave holds 16 accumulators: three waves per
+  // SIMD); below 256 tokens 16 x 64 tiles and eight waves, which give more
+  // workgroups and shorter contraction loops.  Measured at d_model 4096:
+  // 64 x 64 beats 64 x 128 by 1.4x at 4096 tokens; at 32 tokens the small
+  // tiles take 21.9 us against 25.4 us for 32 x 64 with four waves.
   const int cols = 256 + 64 * c.idx_heads;
   const int32_t esz = c.idx_k_dtype == CSA2_FP8_E4M3 ? 1 : 2;
   uint8_t *ik = static_cast<uint8_t *>(c.idx_k);
   if (n >= 256) {
-    hipLaunchKernelGGL((proj_append_kernel<4, 4>), dim3((n + 63) / 64, cols / 64), dim3(256), 0,
+    hipLaunchKernelGGL((proj_append_kernel<4, 4, 4>), dim3((n + 63) / 64, cols / 64), dim3(256), 0,
                        stream, c.kv_codes, c.kv_scales, ik, x, w, d_model, seq, pos, n,
                        c.capacity, c.idx_heads, esz);
   } else {
-    hipLaunchKernelGGL((proj_append_kernel<2, 4>), dim3((n + 31) / 32, cols / 64), dim3(256), 0,
+    hipLaunchKernelGGL((proj_append_kernel<1, 4, 8>), dim3((n + 15) / 16, cols / 64), dim3(512), 0,
                        stream, c.kv_codes, c.kv_scales, ik, x, w, d_model, seq, pos, n,
                        c.capacity, c.idx_heads, esz);
   }
