@@ -23,10 +23,11 @@ membership) is taken: there the oracle computes in the precision the reading
 fixes (fp32 canonical index scores), so both sides decide on the same numbers.
 
 Parity pins: every function is pinned by ``tests/test_oracle_*.py`` against
-closed forms, brute force or textbook routines.  The one function whose exact
-fp32 rounding sequence is a reading with no outside value to pin it
-(``index_scores``) is pinned by an error bound against the exact dot product
-and by exact integer cases, not bit for bit; see its docstring.
+closed forms, brute force or textbook routines.  The fp32 rounding sequence of
+``index_scores`` is a reading (the plain left-to-right order); it is pinned by
+hand-derived results on cancelling inputs, by exact rational evaluation of that
+order with one rounding per step, by exact integer cases and by the fp32 error
+bound against the exact dot product; see its docstring.
 """
 from .formats import (  # noqa: F401
     E2M1_MAGNITUDES, e2m1_value, e4m3_value, e4m3_encode_ratio, e4m3_encode,

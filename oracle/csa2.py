@@ -201,15 +201,6 @@ def query_index_values(q_idx_bits, dtype: str) -> np.ndarray:
     return v.astype(np.float32)
 
 
-def _pairwise_f32(x: np.ndarray, axis: int) -> np.ndarray:
-    """Balanced pairwise fp32 sum along `axis` (length a power of two):
-    ((x0+x1)+(x2+x3)) + ((x4+x5)+(x6+x7)) for eight terms."""
-    x = np.moveaxis(np.asarray(x, np.float32), axis, -1)
-    while x.shape[-1] > 1:
-        x = (x[..., 0::2] + x[..., 1::2]).astype(np.float32)
-    return x[..., 0]
-
-
 def index_scores(q: np.ndarray, keys: np.ndarray) -> np.ndarray:
     """Index score of every candidate: sum over indexer heads of q_h . k_h, in fp32.
 
@@ -217,29 +208,29 @@ def index_scores(q: np.ndarray, keys: np.ndarray) -> np.ndarray:
     score candidate positions with a new index query against the shared index
     keys).  The pages do not give the score's form.  Reading: the plain sum over
     heads of the head dot products, no activation or head weights, accumulated
-    in fp32 in this fixed order, so that the Top-K decision is reproducible:
-      * per head h and 16-channel block j: a chain of fp32 fused multiply-adds
-        over the block's channels in increasing order, starting from 0;
-      * per head: the four block sums added pairwise, (b0+b1)+(b2+b3);
-      * over heads: the head sums added pairwise (a balanced tree).
+    in fp32 the plain way, left to right, so that the Top-K decision is
+    reproducible:
+      * per head h: acc_h = 0, then acc_h = fma(q[h][c], k[h][c], acc_h) for
+        c = 0, 1, ..., D-1 (one chain of fused multiply-adds, a single rounding
+        per step);
+      * over heads: s = acc_0, then s = s + acc_h for h = 1, ..., H-1.
 
     q: float32 [H, D]; keys: float32 [n, H, D]; returns float32 [n].
-    Parity pin: error bound against the exact dot product, and exact integer
-    cases (tests/test_oracle_scores.py); the rounding sequence itself is the
-    reading above.
+    Pins: exact rational evaluation of this order on cancelling inputs, exact
+    integer cases, and the fp32 error bound against the exact dot product
+    (tests/test_oracle_scores.py).
     """
     q = np.asarray(q, np.float32)
     keys = np.asarray(keys, np.float32)
     n = keys.shape[0]
     H, D = q.shape
-    nb = D // BLOCK
-    qb = q.reshape(H, nb, BLOCK)
-    kb = keys.reshape(n, H, nb, BLOCK)
-    part = np.zeros((n, H, nb), np.float32)
-    for t in range(BLOCK):
-        part = fma_f32(qb[None, :, :, t], kb[:, :, :, t], part)
-    per_head = _pairwise_f32(part, axis=2)
-    return _pairwise_f32(per_head, axis=1)
+    acc = np.zeros((n, H), np.float32)
+    for c in range(D):
+        acc = fma_f32(q[None, :, c], keys[:, :, c], acc)
+    s = acc[:, 0].copy()
+    for h in range(1, H):
+        s = (s + acc[:, h]).astype(np.float32)
+    return s
 
 
 def index_scores_exact(q: np.ndarray, keys: np.ndarray):

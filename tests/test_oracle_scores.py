@@ -1,9 +1,12 @@
 """Pins of the oracle's index score (sum over indexer heads of q_h . k_h in fp32).
 
-The pages give no score values; the fp32 rounding sequence is a reading.  These
-tests pin the oracle against the exact dot product: bit-exact where every
-partial sum is exactly representable, and within the fp32 error bound of the
-fixed evaluation order otherwise.
+The pages give no score values; the fp32 rounding sequence is a reading: per
+head one chain of fused multiply-adds over the channels in increasing order,
+then the head sums added left to right.  These tests pin the oracle against the
+exact dot product (bit-exact where every partial sum is representable, within
+the fp32 error bound otherwise) and pin the order itself with cancelling inputs
+whose left-to-right fp32 result is derived by hand and by exact rational
+evaluation, and differs from the exact sum and from the other plausible orders.
 """
 from fractions import Fraction
 
@@ -58,7 +61,7 @@ def test_error_bound_vs_exact(heads, dtype):
     got = O.index_scores(q, k).astype(np.float64)
     exact = _exact_scores(q, k)          # fp64; its own error is ~2^-53 relative
     mag = np.einsum("hd,nhd->n", np.abs(q).astype(np.float64), np.abs(k).astype(np.float64))
-    depth = 16 + 2 + 3                   # longest chain of roundings in the fixed order
+    depth = 64 + 7                       # roundings: a 64-step chain per head, 7 head additions
     bound = depth * 2.0 ** -24 * mag * (1 + 1e-6)
     assert np.all(np.abs(got - exact) <= bound)
     # and the fixed order actually rounds (not computed in higher precision)
@@ -71,7 +74,7 @@ def test_one_hot_query_selects_channel_sum():
     q = np.zeros((8, 64), np.float32)
     q[:, 17] = 1.0
     got = O.index_scores(q, k)
-    # eight terms in a balanced fp32 tree; fp8 values sum exactly in fp32 here (|v| <= 448, 2^-9 grid)
+    # eight terms summed in fp32; fp8 values sum exactly in fp32 here (|v| <= 448, 2^-9 grid)
     want = k[:, :, 17].astype(np.float64).sum(axis=1)
     assert np.array_equal(got.astype(np.float64), want)
 
@@ -84,23 +87,104 @@ def test_sign_and_linearity_exact_cases():
     assert np.array_equal(O.index_scores(2 * q, k), 2 * O.index_scores(q, k))
 
 
-def test_head_order_is_balanced_tree_on_cancellation():
-    # The sum over heads is a balanced fp32 tree: with head sums (2^24, 1, -2^24, 1, 0...)
-    # the tree gives round(2^24 + 1) + (-2^24 + 1) = 2^24 - 2^24 + 1 = 1, not 2.
-    # Check only against exact rational evaluation of that tree, not against the code.
-    heads = [2.0 ** 24, 1.0, -(2.0 ** 24), 1.0, 0.0, 0.0, 0.0, 0.0]
-    q = np.zeros((8, 64), np.float32)
-    q[:, 0] = 1.0
-    k = np.zeros((1, 8, 64), np.float32)
-    k[0, :, 0] = heads
+def _rnd(x):
+    """Exact rational -> the nearest fp32 value (ties to even), as a Fraction.
 
-    def rnd(x):   # exact rational -> nearest fp32, ties to even
-        return Fraction(float(np.float32(float(x))))
-    a01 = rnd(Fraction(heads[0]) + Fraction(heads[1]))     # 2^24 + 1 -> 2^24 (tie to even)
-    a23 = rnd(Fraction(heads[2]) + Fraction(heads[3]))     # -2^24 + 1 -> -2^24 + 1 (exact)
-    want = rnd(a01 + a23)
-    assert Fraction(float(O.index_scores(q, k)[0])) == want
-    assert want == 1   # the unrounded sum would be 2
+    Rounded once, straight from the rational (no float64 step in between):
+    24 significant bits, spacing 2^(e-23) for 2^e <= |x| < 2^(e+1), subnormal
+    spacing 2^-149."""
+    x = Fraction(x)
+    if x == 0:
+        return Fraction(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (max(e, -126) - 23)
+    r = round(a / ulp) * ulp          # Fraction.__round__: nearest integer, ties to even
+    return r if x > 0 else -r
+
+
+def _left_to_right(q, k):
+    """The reading's order evaluated in exact rationals with one fp32 rounding
+    per step: per head fma(q, k, acc) over channels 0..D-1, then the head sums
+    from head 0 up.  q [H, D], k [H, D] float32."""
+    heads = []
+    for h in range(q.shape[0]):
+        acc = Fraction(0)
+        for c in range(q.shape[1]):
+            acc = _rnd(Fraction(float(q[h, c])) * Fraction(float(k[h, c])) + acc)
+        heads.append(acc)
+    s = heads[0]
+    for a in heads[1:]:
+        s = _rnd(s + a)
+    return s
+
+
+@pytest.mark.parametrize("heads", [4, 8])
+def test_channel_order_is_one_chain_from_channel_0(heads):
+    # Terms 1, 2^24, 1, -2^24 at channels 0, 16, 32, 48 of head 0 (q = 1 there).
+    # Left to right in fp32: 1 -> 1 + 2^24 is a tie between 2^24 and 2^24 + 2,
+    # kept at the even 2^24 -> + 1 ties again, 2^24 -> - 2^24 = 0.  The exact sum
+    # is 2; 16-channel block sums added (b0+b1)+(b2+b3) give 1; the reversed
+    # chain gives -2^24 + 1 (exact) + 1 + 2^24 = 2.
+    q = np.zeros((heads, 64), np.float32)
+    k = np.zeros((1, heads, 64), np.float32)
+    for c, v in zip((0, 16, 32, 48), (1.0, 2.0 ** 24, 1.0, -(2.0 ** 24))):
+        q[0, c] = 1.0
+        k[0, 0, c] = v
+    got = Fraction(float(O.index_scores(q, k)[0]))
+    assert got == 0
+    assert got == _left_to_right(q, k[0])
+    # neighbouring channels: the same terms at channels 5, 6, 7, 8
+    q2 = np.zeros_like(q)
+    k2 = np.zeros_like(k)
+    for c, v in zip((5, 6, 7, 8), (1.0, 2.0 ** 24, 1.0, -(2.0 ** 24))):
+        q2[0, c] = 1.0
+        k2[0, 0, c] = v
+    assert O.index_scores(q2, k2)[0] == 0.0
+
+
+@pytest.mark.parametrize("heads", [4, 8])
+def test_head_order_is_left_to_right(heads):
+    # Head sums 2^24, 1, 1, -2^24 (heads 0..3; the rest 0).  Left to right:
+    # 2^24 + 1 -> 2^24 (tie to even), + 1 -> 2^24, - 2^24 -> 0.  The exact sum
+    # is 2; a balanced tree gives (2^24 + 1 -> 2^24) + (1 - 2^24, exact) = 1.
+    q = np.zeros((heads, 64), np.float32)
+    q[:, 0] = 1.0
+    k = np.zeros((1, heads, 64), np.float32)
+    k[0, :4, 0] = [2.0 ** 24, 1.0, 1.0, -(2.0 ** 24)]
+    got = Fraction(float(O.index_scores(q, k)[0]))
+    assert got == 0
+    assert got == _left_to_right(q, k[0])
+
+
+def test_heads_summed_after_their_chains():
+    # Summing per channel over heads first would mix the heads' terms: head 0
+    # holds 2^24 at channel 0 and -2^24 at channel 1, head 1 holds 1 at channel 0
+    # and 1 at channel 1.  Per head: acc_0 = 0 exactly, acc_1 = 2, total 2.
+    # Channel-outer order: 2^24 + 1 -> 2^24, then + (-2^24) -> 0, + 1 -> 1.
+    q = np.ones((4, 64), np.float32)
+    k = np.zeros((1, 4, 64), np.float32)
+    k[0, 0, 0], k[0, 0, 1] = 2.0 ** 24, -(2.0 ** 24)
+    k[0, 1, 0], k[0, 1, 1] = 1.0, 1.0
+    got = Fraction(float(O.index_scores(q, k)[0]))
+    assert got == 2
+    assert got == _left_to_right(q, k[0])
+
+
+def test_random_cancellation_matches_rational_left_to_right():
+    # Mixed magnitudes (2^-20 .. 2^20, both signs) on the bf16 and E4M3 grids,
+    # so nearly every step rounds; the oracle must equal the exact rational
+    # evaluation of the stated order with one rounding per step, bit for bit.
+    rng = np.random.default_rng(21)
+    for heads in (4, 8):
+        mant = rng.integers(1, 256, (6, heads, 64)) * rng.choice([-1, 1], (6, heads, 64))
+        k = (mant * np.exp2(rng.integers(-20, 20, (6, heads, 64)))).astype(np.float32)
+        q = F.e4m3_value(rng.integers(0, 0x7E, (heads, 64))).astype(np.float32)
+        got = O.index_scores(q, k)
+        for n in range(len(k)):
+            assert Fraction(float(got[n])) == _left_to_right(q, k[n])
 
 
 def test_exact_scores_equal_rational_sums_for_e4m3():
