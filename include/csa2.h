@@ -90,7 +90,9 @@ typedef enum {
  * One cached position = dk/2 + dv/2 + dk/16 + dv/16 bytes of main KV
  * (144 B for dk = dv = 128) plus idx_heads * idx_dim * (1 or 2) bytes.
  * Supported: dk = dv = 128, idx_dim = 64, idx_heads in {4, 8}; capacity a
- * multiple of 16.
+ * multiple of 16, at most 8388608 (2^23) positions per sequence (the kernels
+ * use 32-bit byte offsets within a sequence); a larger capacity is rejected
+ * with CSA2_ERR_SHAPE by every call that takes the cache.
  */
 typedef struct csa2_cache {
   uint8_t *kv_codes;
@@ -152,9 +154,9 @@ size_t csa2_index_topk_workspace(const csa2_cache *cache, csa2_mode mode, int32_
  *   REUSE:     topk_out = reuse_src [nq][top_k], copied unchanged; q_idx,
  *              q_seq, q_pos may be NULL.
  * Score of candidate j: sum over indexer heads h of q_h . k_{j,h}, in fp32 in
- * a fixed order: per head and 16-channel block, fused multiply-adds in channel
- * order from 0; per head the four block sums pairwise; over heads a balanced
- * pairwise tree.  The result is bit-reproducible.
+ * the plain left-to-right order: per head one chain of fused multiply-adds
+ * over channels 0 .. idx_dim-1 starting from 0, then the head sums added from
+ * head 0 up.  The result is bit-reproducible.
  * Matrix-core scoring: with q_dtype = CSA2_FP8_E4M3 against E4M3 keys and
  * every visible position a candidate (FULL without a pool, REINDEX without
  * pool_in), all queries of the call are scored as one dense E4M3 product on

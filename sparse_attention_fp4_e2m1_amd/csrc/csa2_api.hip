@@ -7,10 +7,16 @@ using namespace csa2;
 
 namespace {
 
+// Largest capacity: the kernels address a sequence's rows and index-key tiles
+// with 32-bit byte offsets (a tile of positions p is (p / T) * 64 * 64 * E
+// bytes in, which reaches 2^32 at p = 2^23).
+constexpr int32_t kMaxCapacity = 1 << 23;
+
 csa2_status check_cache(const csa2_cache *c, bool need_idx) {
   if (c == nullptr || c->kv_codes == nullptr || c->kv_scales == nullptr) return CSA2_ERR_NULL;
   if (need_idx && c->idx_k == nullptr) return CSA2_ERR_NULL;
   if (c->batch < 1 || c->capacity < 1 || c->capacity % 16 != 0) return CSA2_ERR_SHAPE;
+  if (c->capacity > kMaxCapacity) return CSA2_ERR_SHAPE;
   if (c->dk != 128 || c->dv != 128 || c->idx_dim != 64) return CSA2_ERR_UNSUPPORTED;
   if (c->idx_heads != 4 && c->idx_heads != 8) return CSA2_ERR_UNSUPPORTED;
   if (c->idx_k_dtype != CSA2_BF16 && c->idx_k_dtype != CSA2_FP8_E4M3) return CSA2_ERR_UNSUPPORTED;

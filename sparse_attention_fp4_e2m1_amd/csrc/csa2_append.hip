@@ -132,11 +132,11 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
 // The encoder-side projection fused into quantize-and-append (aiwiki "DeepSeek
 // V4.1-Flash", section "Causal Encoder-Decoder": the decoder's global keys and
 // values are projected from the final causal-encoder hidden states).  One
-// workgroup computes a tile of 16 kRT tokens x 16 kCT output channels of
-// Y = X W^T on matrix cores (bf16 operands, fp32 accumulation).  Its kW
-// waves split the contraction (wave w takes k-steps w, w + kW, ...) and each
-// holds the whole tile, so every operand fragment feeds kRT or kCT products;
-// the kW partial tiles are summed in LDS in wave order, rounded to bf16 and
+// workgroup computes a tile of 16 kRT tokens x 16 kCT kCG output channels of
+// Y = X W^T on matrix cores (bf16 operands, fp32 accumulation).  Four waves
+// per group of 16 kCT channels split the contraction and each holds the
+// group's whole tile, so every operand fragment feeds kRT or kCT products;
+// the partial tiles are summed in LDS in wave order, rounded to bf16 and
 // quantized exactly as kv_append_kernel does.  Output channels: K 0..127,
 // V 128..255, index keys 256.. (head-major).
 // Operand fragments of v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16
@@ -151,21 +151,32 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int kRT, int kCT, int kW>
-__global__ void __launch_bounds__(64 * kW) proj_append_kernel(
+// The contraction is split over four waves in every launch shape: wave ks of
+// a channel group takes k-steps ks, ks + 4, ks + 8, ... (32 channels of
+// d_model each) in order, and the four partial tiles are added in wave order,
+// ((p0 + p1) + p2) + p3.  So the fp32 order of every output element depends on
+// d_model only, not on the call's token count or the tile shape, and a row
+// projects to the same bytes whichever call carries it.
+constexpr int kProjSplit = 4;
+
+template <int kRT, int kCT, int kCG>   // 16 kRT rows x 16 kCT columns per wave, kCG column groups
+__global__ void __launch_bounds__(64 * kProjSplit * kCG) proj_append_kernel(
     uint8_t *__restrict__ kv_codes, uint8_t *__restrict__ kv_scales, uint8_t *__restrict__ idx_k,
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, int32_t d_model,
     const int32_t *__restrict__ seq, const int32_t *__restrict__ pos, int32_t n,
     int32_t capacity, int32_t H, int32_t esz) {
-  constexpr int kRows = 16 * kRT, kCols = 16 * kCT, kPitch = kCols + 4;
+  constexpr int kW = kProjSplit * kCG;
+  constexpr int kRows = 16 * kRT, kCols = 16 * kCT * kCG, kPitch = kCols + 4;
   __shared__ float tile[kRows * kPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int ks = wave % kProjSplit;   // contraction slice
+  const int cg = wave / kProjSplit;   // column group
   const int l16 = lane & 15;
   const int kg = lane >> 4;
   const int r0 = blockIdx.x * kRows;
-  const int c0 = blockIdx.y * kCols;
+  const int c0 = blockIdx.y * kCols + cg * 16 * kCT;
   const uint16_t *xa[kRT];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt)   // rows past n read row n - 1, never stored
@@ -179,7 +190,7 @@ __global__ void __launch_bounds__(64 * kW) proj_append_kernel(
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) acc[rt][ct] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 2
-  for (int k0 = 32 * wave; k0 < d_model; k0 += 32 * kW) {
+  for (int k0 = 32 * ks; k0 < d_model; k0 += 32 * kProjSplit) {
     bf16x8 a[kRT];
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt)
@@ -193,17 +204,17 @@ __global__ void __launch_bounds__(64 * kW) proj_append_kernel(
         acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt], b, acc[rt][ct], 0, 0, 0);
     }
   }
-  // sum of the four partial tiles, wave 0 first
-  for (int wv = 0; wv < kW; ++wv) {
-    if (wave == wv) {
+  // sum of the four partial tiles of each column group, slice 0 first
+  for (int sv = 0; sv < kProjSplit; ++sv) {
+    if (ks == sv) {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float *t = tile + (16 * rt + 4 * kg + i) * kPitch + 16 * ct + l16;
-            *t = wv == 0 ? acc[rt][ct][i] : *t + acc[rt][ct][i];
+            float *t = tile + (16 * rt + 4 * kg + i) * kPitch + cg * 16 * kCT + 16 * ct + l16;
+            *t = sv == 0 ? acc[rt][ct][i] : *t + acc[rt][ct][i];
           }
     }
     __syncthreads();
@@ -212,12 +223,13 @@ __global__ void __launch_bounds__(64 * kW) proj_append_kernel(
   // (token, 16-channel block): K or V block -> E4M3 scale and E2M1 codes;
   // index-key block -> two groups of 8 channels, bf16 or E4M3
   const int64_t seq_bytes = (int64_t)capacity * H * 64 * esz;
-  for (int item = tid; item < kRows * kCT; item += 64 * kW) {
-    const int r = item / kCT, j = item % kCT;
+  constexpr int kBlocks = kCols / 16;   // 16-channel blocks per row of the tile
+  for (int item = tid; item < kRows * kBlocks; item += 64 * kW) {
+    const int r = item / kBlocks, j = item % kBlocks;
     const int row = r0 + r;
     if (row >= n) continue;
     const float *src = tile + r * kPitch + 16 * j;
-    const int c = c0 + 16 * j;
+    const int c = blockIdx.y * kCols + 16 * j;
     if (c < 256) {
       float xv[16];
 #pragma unroll
@@ -284,19 +296,19 @@ hipError_t launch_proj_append(const csa2_cache &c, const uint16_t *x, int32_t d_
                               const uint16_t *w, const int32_t *seq, const int32_t *pos,
                               int32_t n, hipStream_t stream) {
   // 64 x 64 tiles, four waves (a wave holds 16 accumulators: three waves per
-  // SIMD); below 256 tokens 16 x 64 tiles and eight waves, which give more
-  // workgroups and shorter contraction loops.  Measured at d_model 4096:
-  // 64 x 64 beats 64 x 128 by 1.4x at 4096 tokens; at 32 tokens the small
-  // tiles take 21.9 us against 25.4 us for 32 x 64 with four waves.
+  // SIMD); below 256 tokens 16 x 64 tiles of two column groups (eight waves),
+  // which give more workgroups.  Both split the contraction over four waves
+  // the same way.  Measured at d_model 4096: 64 x 64 beats 64 x 128 by 1.4x at
+  // 4096 tokens.
   const int cols = 256 + 64 * c.idx_heads;
   const int32_t esz = c.idx_k_dtype == CSA2_FP8_E4M3 ? 1 : 2;
   uint8_t *ik = static_cast<uint8_t *>(c.idx_k);
   if (n >= 256) {
-    hipLaunchKernelGGL((proj_append_kernel<4, 4, 4>), dim3((n + 63) / 64, cols / 64), dim3(256), 0,
+    hipLaunchKernelGGL((proj_append_kernel<4, 4, 1>), dim3((n + 63) / 64, cols / 64), dim3(256), 0,
                        stream, c.kv_codes, c.kv_scales, ik, x, w, d_model, seq, pos, n,
                        c.capacity, c.idx_heads, esz);
   } else {
-    hipLaunchKernelGGL((proj_append_kernel<1, 4, 8>), dim3((n + 15) / 16, cols / 64), dim3(512), 0,
+    hipLaunchKernelGGL((proj_append_kernel<1, 2, 2>), dim3((n + 15) / 16, cols / 64), dim3(512), 0,
                        stream, c.kv_codes, c.kv_scales, ik, x, w, d_model, seq, pos, n,
                        c.capacity, c.idx_heads, esz);
   }

@@ -73,18 +73,51 @@ constexpr int64_t kBigChunkMinGroups = 512;   // use 4096-candidate chunks when 
 constexpr int64_t kSmallGridGroups = 256;     // below this, one-wave groups of 64 candidates
 
 // ---------------------------------------------------------------------------
-// cross-lane sums inside quads / half rows (commutative, so both lanes of a
-// butterfly pair compute the same bits)
+// The sum over the index heads, left to right.  The H lanes of a candidate
+// (lanes H*t .. H*t+H-1, head h in lane H*t+h) each hold one head's dot
+// product; every lane of the group ends with ((a_0 + a_1) + a_2) + ... + a_{H-1}
+// in fp32, the same bits in each lane: each lane fetches the group's values
+// in head order with DPP moves and adds them up itself.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float dpp_xor1(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+template <int kLane>   // quad_perm [kLane, kLane, kLane, kLane]: lane kLane of each quad
+__device__ __forceinline__ float dpp_quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kLane * 0x55, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float dpp_xor2(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+// The value of the lane at the same position in the other quad of an 8-lane
+// half row: quad_perm [3, 2, 1, 0] then row_half_mirror (lane i <- 7 - i).
+// Both are uniform patterns run by every lane: a DPP move reads its source
+// lane only while that lane is active, so no DPP move may sit under a
+// lane-dependent branch.
+__device__ __forceinline__ float dpp_other_quad(float v) {
+  const int r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x1B, 0xF, 0xF, true);
+  return __int_as_float(__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, true));
 }
-// lane i <-> 7 - i within each group of 8: pairs quad 0 with quad 1
-__device__ __forceinline__ float dpp_half_mirror(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+
+template <int H>
+__device__ __forceinline__ float head_sum_ltr(float x) {
+  static_assert(H == 4 || H == 8, "four or eight index heads");
+  // lo: heads 0..3 of the lane's group, hi: heads 4..7, each at the lane's
+  // position in its own quad (an 8-lane group is two quads of one row); the
+  // choice is a bitwise select, so the compiler keeps it branch-free
+  float lo = x, hi = 0.0f;
+  if (H == 8) {
+    const uint32_t m = 0u - ((threadIdx.x >> 2) & 1u);   // all ones in the upper quad
+    const uint32_t xb = __float_as_uint(x);
+    const uint32_t ob = __float_as_uint(dpp_other_quad(x));
+    lo = __uint_as_float((xb & ~m) | (ob & m));
+    hi = __uint_as_float((ob & ~m) | (xb & m));
+  }
+  float s = dpp_quad_bcast<0>(lo);
+  s = s + dpp_quad_bcast<1>(lo);
+  s = s + dpp_quad_bcast<2>(lo);
+  s = s + dpp_quad_bcast<3>(lo);
+  if (H == 8) {
+    s = s + dpp_quad_bcast<0>(hi);
+    s = s + dpp_quad_bcast<1>(hi);
+    s = s + dpp_quad_bcast<2>(hi);
+    s = s + dpp_quad_bcast<3>(hi);
+  }
+  return s;
 }
 
 __global__ void zero2_u32_kernel(uint32_t *__restrict__ p, uint32_t *__restrict__ p2, int64_t n) {
@@ -111,12 +144,9 @@ __global__ void copy_i32_kernel(int32_t *__restrict__ dst, const int32_t *__rest
 // 64 B (E4M3) or 128 B (bf16) of the token's index keys; a wave covers
 // TPI = 64 / H tokens per step = one tile of the tiled index-key layout, so
 // each of its 16-B loads is one contiguous 1 KB span across the wave.  Each
-// lane runs the canonical fp32 chains -- per 16-channel block, fused
-// multiply-adds in channel order -- as four independent chains, adds the
-// block sums as (b0+b1)+(b2+b3), and the head sums meet in a balanced tree
-// over lanes: xor-1, xor-2 (quad permutes) and xor-4 (half-row mirror; the
-// quads are uniform by then) DPP adds.  Every lane of a token ends with the
-// same bits.
+// lane runs its head's fp32 chain of fused multiply-adds over channels 0..63
+// in order; head_sum_ltr then adds the head sums from head 0 up.  Every lane
+// of a token ends with the same bits.
 // ---------------------------------------------------------------------------
 template <int H, bool kFp8Keys, bool kPool, int kThreads, int kChunk>
 struct ScoreCtx {
@@ -169,10 +199,9 @@ struct ScoreCtx {
                                         uint32_t *hist, uint32_t *sblk, uint32_t *histb) const {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float blk[4];
+      float acc = 0.0f;   // one chain over the head's 64 channels
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float acc = 0.0f;
         if (kFp8Keys) {
           const uint4 a = buf[u][j];
           const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -198,12 +227,8 @@ struct ScoreCtx {
             }
           }
         }
-        blk[j] = acc;
       }
-      float acc = (blk[0] + blk[1]) + (blk[2] + blk[3]);
-      acc = acc + dpp_xor1(acc);
-      acc = acc + dpp_xor2(acc);
-      if (H == 8) acc = acc + dpp_half_mirror(acc);
+      acc = head_sum_ltr<H>(acc);
       const uint32_t key = val[u] ? score_key(acc) : 0u;
       const int s = s0 + u;
       mykey = (h == s % H) ? key : mykey;
@@ -359,13 +384,11 @@ score_kernel(
 // gather_score_kernel: Reindex over a pool.  Each pool entry takes H lanes,
 // one per index head: lane h gathers the entry's head-h keys (all its 16-B
 // pieces in flight at once; the pool's positions are scattered, so there is
-// nothing to coalesce across entries) and runs the canonical fp32 order of
-// that head -- per 16-channel block an FMA chain in channel order, blocks
-// (b0+b1)+(b2+b3).  The heads' balanced pairwise tree then runs across the H
-// lanes with DPP moves (each level adds a lane's value to its partner's, so
-// both partners hold the same bits): the same bits as score_kernel.  The
-// group's first lane stores the key; the 12-bit histogram is aggregated in
-// LDS, where only the bins in use are cleared and flushed.
+// nothing to coalesce across entries) and runs that head's fp32 chain of
+// fused multiply-adds over channels 0..63 in order; head_sum_ltr adds the
+// head sums from head 0 up: the same bits as score_kernel.  The group's first
+// lane stores the key; the 12-bit histogram is aggregated in LDS, where only
+// the bins in use are cleared and flushed.
 // ---------------------------------------------------------------------------
 constexpr int kGatherThreads = 256;
 constexpr int kQPitch = 68;   // floats per head row of the staged query (spreads LDS banks)
@@ -407,7 +430,7 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
   }
   __syncthreads();
   const float *qh = qlds + h * kQPitch;
-  float blk[4];
+  float acc = 0.0f;   // one chain over the head's 64 channels
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float qv[16];
@@ -419,7 +442,6 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
       qv[4 * k + 2] = f.z;
       qv[4 * k + 3] = f.w;
     }
-    float acc = 0.0f;
     if (kFp8Keys) {
       const uint4 a = buf[j];
       const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -444,13 +466,8 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
         }
       }
     }
-    blk[j] = acc;
   }
-  float hs = (blk[0] + blk[1]) + (blk[2] + blk[3]);
-  // balanced pairwise tree over the heads, across the entry's lanes
-  hs = hs + dpp_xor1(hs);
-  hs = hs + dpp_xor2(hs);
-  if (H == 8) hs = hs + dpp_half_mirror(hs);
+  const float hs = head_sum_ltr<H>(acc);
   const uint32_t key = valid ? score_key(hs) : 0u;
   const bool lead = in && h == 0;
   if (lead) keys_tok[(int64_t)q * tok_stride + t] = key;

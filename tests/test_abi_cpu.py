@@ -72,6 +72,14 @@ def test_append_validation(lib):
     assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_SHAPE
     c = _cache(lib, capacity=1000)          # the tiled index keys need capacity % 16 == 0
     assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_SHAPE
+    # 32-bit offsets within a sequence: at most 2^23 positions
+    c = _cache(lib, capacity=1 << 23)
+    assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 0, None) == lib.CSA2_OK
+    c = _cache(lib, capacity=(1 << 23) + 16)
+    assert L.csa2_kv_append(ctypes.byref(c), P(1), P(1), None, P(1), P(1), 4, None) == lib.CSA2_ERR_SHAPE
+    assert L.csa2_index_topk_workspace(ctypes.byref(c), lib.CSA2_FULL, 1, 16, 0, 0) == 0
+    assert L.csa2_sparse_attn_workspace(ctypes.byref(c), 1, 64, 16) == 0
+    assert L.csa2_kv_export_bytes(ctypes.byref(c), 16) == 0
 
 
 def test_index_topk_validation(lib):
