@@ -212,6 +212,29 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
                              size_t workspace_bytes, void *stream);
 
 /*
+ * csa2_sparse_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, arguments and results as csa2_sparse_attn, without a
+ * workspace argument.  The split partials go to a static device array of
+ * 16 MiB (16777216 bytes) that the library holds on every device it runs on
+ * until the process ends; the call allocates nothing.
+ *   Limit: csa2_sparse_attn_workspace(cache, nq, n_heads, top_k) must not
+ *   exceed 16 MiB (for example 32 queries x 64 heads x top_k 2048 need 8.5
+ *   MiB); larger calls return CSA2_ERR_WORKSPACE and enqueue nothing.
+ *   The stream must belong to the calling thread's current device (the array
+ *   of that device is used).  Every call on one device shares its array:
+ *   calls that overlap on one device (concurrent streams, or another thread)
+ *   race and give undefined results; calls ordered on one stream are safe.
+ *   The first call on a device looks up the array's device address
+ *   (hipGetSymbolAddress) once.
+ * Errors: as csa2_sparse_attn.
+ */
+csa2_status csa2_sparse_attn_noalloc(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,
+                                     const int32_t *q_seq, int32_t nq, const int32_t *topk,
+                                     int32_t top_k, float softmax_scale, float *out, float *lse,
+                                     void *stream);
+
+/*
  * The local sliding-window KV of one layer (aiwiki "DeepSeek V4.1-Flash",
  * section "Compressed Sparse Attention 2": besides its query, every CSA2 layer
  * creates its own local sliding-window keys and values; section "KV-cache

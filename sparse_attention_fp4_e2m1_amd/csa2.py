@@ -52,6 +52,7 @@ def _load():
         "csa2_index_topk": (I32, [C, I32, P, I32, P, P, I32, I32, P, I32, I32, P, P, P, P, SZ, P]),
         "csa2_sparse_attn_workspace": (SZ, [C, I32, I32, I32]),
         "csa2_sparse_attn": (I32, [C, P, I32, P, I32, P, I32, F32, P, P, P, SZ, P]),
+        "csa2_sparse_attn_noalloc": (I32, [C, P, I32, P, I32, P, I32, F32, P, P, P]),
         "csa2_local_append": (I32, [ctypes.POINTER(csa2_local_cache), P, P, P, P, I32, P]),
         "csa2_local_attn": (I32, [ctypes.POINTER(csa2_local_cache), P, I32, P, P, I32, F32, P, P, P]),
         "csa2_proj_append": (I32, [C, P, I32, P, P, P, I32, P]),
@@ -222,6 +223,27 @@ def csa2_sparse_attn(cache: Cache, q, q_seq, topk, softmax_scale: Optional[float
     _check(LIB.csa2_sparse_attn(cache.ref, _ptr(q), n_heads, _ptr(q_seq), nq, _ptr(topk), top_k,
                                 float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                 workspace.numel(), _stream(stream)), "csa2_sparse_attn")
+    return out, lse
+
+
+def csa2_sparse_attn_noalloc(cache: Cache, q, q_seq, topk, softmax_scale: Optional[float] = None,
+                             out=None, lse=None, stream=None):
+    """csa2_sparse_attn with the library's static scratch (no workspace); out
+    and lse must be given (the call allocates nothing).  Returns (out, lse)."""
+    d = cache.device
+    nq, n_heads = q.shape[0], q.shape[1]
+    top_k = topk.shape[1]
+    _need(q, "q", _B16, (nq, n_heads, cache.dk), d)
+    _need(q_seq, "q_seq", _I32, (nq,), d)
+    _need(topk, "topk", _I32, (nq, top_k), d)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(cache.dk)
+    _need(out, "out", (torch.float32,), (nq, n_heads, cache.dv), d)
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), (nq, n_heads), d)
+    _check(LIB.csa2_sparse_attn_noalloc(cache.ref, _ptr(q), n_heads, _ptr(q_seq), nq, _ptr(topk),
+                                        top_k, float(softmax_scale), _ptr(out), _ptr(lse),
+                                        _stream(stream)), "csa2_sparse_attn_noalloc")
     return out, lse
 
 

@@ -161,6 +161,26 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
   return CSA2_OK;
 }
 
+csa2_status csa2_sparse_attn_noalloc(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,
+                                     const int32_t *q_seq, int32_t nq, const int32_t *topk,
+                                     int32_t top_k, float softmax_scale, float *out, float *lse,
+                                     void *stream) {
+  csa2_status st = check_cache(cache, false);
+  if (st != CSA2_OK) return st;
+  if (n_heads < 16 || n_heads > 128 || n_heads % 16 != 0) return CSA2_ERR_UNSUPPORTED;
+  if (nq < 0 || top_k < 1 || top_k > kMaxTopK || nq > 65535) return CSA2_ERR_SHAPE;
+  if (nq == 0) return CSA2_OK;
+  if (q == nullptr || q_seq == nullptr || topk == nullptr || out == nullptr) return CSA2_ERR_NULL;
+  const AttnWorkspace L = attn_workspace_layout(*cache, nq, n_heads, top_k);
+  if (L.total > kNoallocScratchBytes) return CSA2_ERR_WORKSPACE;
+  uint8_t *ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return CSA2_ERR_HIP;
+  if (launch_sparse_attn(*cache, q, n_heads, q_seq, nq, topk, top_k, softmax_scale, out, lse, ws,
+                         L, (hipStream_t)stream) != hipSuccess)
+    return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
 size_t csa2_sparse_local_attn_workspace(const csa2_cache *cache, const csa2_local_cache *local,
                                         int32_t nq, int32_t n_heads, int32_t top_k) {
   if (check_cache(cache, false) != CSA2_OK || check_local(local) != CSA2_OK) return 0;

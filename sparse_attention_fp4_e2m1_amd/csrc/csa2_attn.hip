@@ -25,6 +25,7 @@
 //     softmax rescale and normalization need no cross-lane moves).
 // attn_combine_kernel: merges the splits of each (query, head).
 #include <algorithm>
+#include <mutex>
 
 #include "csa2_internal.h"
 
@@ -647,7 +648,36 @@ int32_t rows_per_split(int32_t nq, int32_t top_k, int32_t max_splits) {
   return per * kSub;
 }
 
+// Scratch of csa2_sparse_attn_noalloc (callers that cannot allocate): the
+// split partials live in this file-scope array instead of a caller workspace.
+// Every device the library runs on holds its own copy until the process ends;
+// host code reaches a device's copy only through the address that
+// hipGetSymbolAddress returns on that device (the array's name is a host-side
+// stand-in, not a device address).
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+uint8_t *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
 }  // namespace
+
+hipError_t noalloc_scratch(uint8_t **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  // once per device, with that device current (this thread's current device)
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = static_cast<uint8_t *>(p);
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 AttnWorkspace attn_workspace_layout(const csa2_cache &c, int32_t nq, int32_t n_heads,
                                     int32_t top_k, int32_t window) {

@@ -105,6 +105,13 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
                               const csa2_local_cache *lc = nullptr,
                               const int32_t *q_pos = nullptr);
 
+// The allocation-free attention call: its split partials in a static device
+// array of this many bytes (per device), reached through noalloc_scratch,
+// which returns the current device's address of the array (looked up once per
+// device).
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(uint8_t **ptr);
+
 hipError_t launch_proj_append(const csa2_cache &c, const uint16_t *x, int32_t d_model,
                               const uint16_t *w, const int32_t *seq, const int32_t *pos,
                               int32_t n, hipStream_t stream);
