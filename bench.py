@@ -33,7 +33,20 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0      # dense E4M3 matrix-core peak of MI355X
 BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix-core peak of MI355X
+FP16_PEAK_TFLOPS = 2500.0     # dense fp16 matrix-core peak of MI355X
 METRIC = "CSA2 decode queries/s and achieved HBM GB/s (% of peak), 64K and 1M context"
+MIN_WARMUP_S = 0.3            # the GPU clock needs ~0.3 s of work to ramp
+# What the path computes in: every sum is fp32; the operands of the products are
+# narrower (and the products exact).
+DTYPE = "fp32 (accumulation; operands bf16/E4M3 index, fp16 attention)"
+PRECISION = {
+    "index_scores": "fp32 fused multiply-adds of the bf16 (or E4M3) index query and the E4M3 or "
+                    "bf16 keys, exact products, left-to-right order",
+    "prefill_index_product": "E4M3 x E4M3 on matrix cores (exact products), fp32 accumulation",
+    "attention": "FP4 rows dequantized exactly to fp16; q rounded to fp16, probabilities fp16; "
+                 "fp32 accumulation on matrix cores",
+    "cache": "main KV FP4 E2M1 + E4M3 scale per 16 channels; index keys E4M3 or bf16",
+}
 
 
 def _args():
@@ -119,9 +132,15 @@ class WorkloadRun:
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
 
-    def step(self, scan_events=None):
+    def step(self, scan_events=None, mark=None):
         self.stack.run(self.q, self.q_idx, self.q_seq, self.q_pos, append=self.append,
-                       scan_events=scan_events)
+                       scan_events=scan_events, mark=mark)
+
+    def attn_flops(self, layer: int = 0) -> int:
+        """Multiply-adds x 2 of one layer's attention: per query and head,
+        q.K over K rows of 128 channels and P.V over the same rows."""
+        wl = self.wl
+        return 4 * wl.nq * wl.heads * self.stack.k[layer] * 128
 
     def scan_flops(self) -> int:
         """Multiply-adds x 2 of the first Full layer's index product (every query
@@ -189,9 +208,20 @@ def time_run(run, steps, warmup, hip, use_graph=False):
     time the index scan (on the stream it runs on) and the step boundaries are
     recorded in a second pass of the same K steps right after it."""
     import torch
+    t_warm = time.perf_counter()
+    done = 0
     for _ in range(warmup):
         run.step()
+        done += 1
     torch.cuda.synchronize()
+    # at least MIN_WARMUP_S of steps whatever `warmup` says, so that a short
+    # run is not timed on a cold clock
+    while time.perf_counter() - t_warm < MIN_WARMUP_S:
+        for _ in range(5):
+            run.step()
+        done += 5
+        torch.cuda.synchronize()
+    run.warmup_steps = done
     graph = None
     if use_graph:
         graph = torch.cuda.CUDAGraph()
@@ -206,11 +236,11 @@ def time_run(run, steps, warmup, hip, use_graph=False):
             graph.replay()
         torch.cuda.synchronize()
 
-    def one(i, scan_events=None):
+    def one(i, scan_events=None, mark=None):
         if graph is not None:
             graph.replay()
         else:
-            run.step(scan_events=scan_events)
+            run.step(scan_events=scan_events, mark=mark)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -222,21 +252,31 @@ def time_run(run, steps, warmup, hip, use_graph=False):
     # instrumented pass: an event at every step boundary (per-step times for
     # the percentiles) and around every scan launch
     evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    aevs = [(hip.event(), hip.event()) for _ in range(steps)]
     bounds = [hip.event() for _ in range(steps + 1)]
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
+
+    def marker(i):
+        def mark(kind, layer, when):   # the first layer's attention call
+            if kind == "attn" and layer == 0:
+                hip.record(aevs[i][0 if when == "before" else 1], stream)
+        return mark
+
     hip.record(bounds[0], stream)
     for i in range(steps):
-        one(i, evs[i])
+        one(i, evs[i], marker(i))
         hip.record(bounds[i + 1], stream)
     torch.cuda.synchronize()
     scan_ms = None
+    run.attn_ms = None
     if graph is None:
         scan_ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / steps
+        run.attn_ms = sum(hip.elapsed_ms(a, b) for a, b in aevs) / steps
     per_step = sorted(hip.elapsed_ms(bounds[i], bounds[i + 1]) for i in range(steps))
     pct = {f"p{p}": per_step[min(steps - 1, (p * steps) // 100)] for p in (10, 50, 90)}
     inst_ms = hip.elapsed_ms(bounds[0], bounds[steps]) / steps
-    for a, b in evs:
+    for a, b in evs + aevs:
         hip.destroy(a)
         hip.destroy(b)
     for e in bounds:
@@ -284,14 +324,26 @@ def measure(name, steps, warmup, hip, use_graph):
         "setup_s": round(run.setup_s, 1),
         "layer_top_k": list(run.stack.k),
     }
+    res["warmup_steps_run"] = run.warmup_steps
     if scan_ms is not None and matrix_core_scan(wl):
-        # the first product pass of the matrix-core scorer: one dense E4M3 GEMM
+        # the matrix-core scorer: the method's index product (every query
+        # against every visible position) counted once, over the time of both
+        # product passes and the threshold kernel between them
         flops = run.scan_flops()
         ach = flops / (scan_ms * 1e-3) / 1e12
-        res["roofline"] = {"bound": "mfma", "kernel": "gemm_score_kernel pass 1 (fp8 index product)",
+        res["roofline"] = {"bound": "mfma",
+                           "kernel": "gemm_score_kernel passes 1 and 2 + gemm_kth_kernel "
+                                     "(fp8 index product, counted once)",
                            "achieved": ach, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / FP8_PEAK_TFLOPS, "traffic": traffic_for(name),
+                           "frac": ach / FP8_PEAK_TFLOPS, "traffic": None,
                            "flops_per_launch": flops, "avg_launch_ms": scan_ms}
+        if run.attn_ms:
+            af = run.attn_flops(0)
+            aach = af / (run.attn_ms * 1e-3) / 1e12
+            res["attention_roofline"] = {
+                "bound": "mfma", "kernel": "attn_partial_kernel + attn_combine_kernel (layer 0)",
+                "achieved": aach, "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": aach / FP16_PEAK_TFLOPS, "flops_per_call": af, "avg_call_ms": run.attn_ms}
     elif scan_ms is not None:
         ach = run.scan_bytes() / (scan_ms * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "score_kernel (index scan, first Full layer)",
@@ -303,11 +355,25 @@ def measure(name, steps, warmup, hip, use_graph):
     return wl, res
 
 
-def cpu_baseline(name, n_sample=32):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name, n_sample=32, runs=3):
     """The oracle (as it stands) on a bounded sample of the same step: the first
     n_sample queries (the whole batch of the headline workload) with their full
-    contexts, one step, one thread."""
+    contexts, one step (the new rows' append, then every layer), on the host's
+    cores: a thread pool over the queries (numpy releases the interpreter lock
+    inside its array operations; BLAS limited to one thread per worker).  The
+    median of `runs` runs."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
     import synth
     from oracle import csa2 as O
@@ -325,16 +391,28 @@ def cpu_baseline(name, n_sample=32):
         q = synth.gen_queries(wl, li)
         qs.append(synth.QueryData(q.q[samp], q.q_idx[samp]))
     qpos = wl.query_pos()[samp]
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        for i in range(len(samp)):
-            k, v, ik = rows[i]
-            oc.append(k, v, ik, np.full(wl.appended, i), np.arange(pre, wl.context))
-        O.run_layers(oc, wl.layers, np.arange(len(samp)), qpos, qs, wl.top_k, wl.q_idx_dtype)
-        t = time.perf_counter() - t0
-    return {"value": len(samp) / t, "unit": "queries/s", "cores": 1, "kind": "oracle",
+    # the machine's CPU share for one GPU is 16 cores, whatever the host reports
+    workers = max(1, min(16, os.cpu_count() or 1, len(samp)))
+
+    def one_query(i):
+        k, v, ik = rows[i]
+        oc.append(k, v, ik, np.full(wl.appended, i), np.arange(pre, wl.context))
+        O.run_layers(oc, wl.layers, np.arange(len(samp)), qpos, qs, wl.top_k, wl.q_idx_dtype,
+                     only=[i])
+
+    times = []
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            list(ex.map(one_query, range(len(samp))))
+            times.append(time.perf_counter() - t0)
+    t = sorted(times)[len(times) // 2]
+    return {"value": len(samp) / t, "unit": "queries/s", "cores": workers, "kind": "oracle",
+            "cpu": cpu_model(), "host_cpus": os.cpu_count(),
+            "runs_s": [round(x, 3) for x in times],
             "sample": f"{len(samp)} of {wl.nq} queries of {name} (full {wl.context}-token "
-                      f"contexts), one step incl. append, numpy oracle, 1 thread; {t:.1f} s"}
+                      f"contexts), one step incl. append, numpy oracle, {workers} threads over "
+                      f"queries; median of {runs} runs {t:.2f} s"}
 
 
 def local_item(name, window, steps, warmup, hip):
@@ -508,7 +586,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
         "step_ms_percentiles": res["step_ms_percentiles"],
         "instrumented_ms_per_step": res["instrumented_ms_per_step"],
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
+        "precision": PRECISION, "warmup_steps_run": res["warmup_steps_run"],
         "data": "synthetic (seeded numpy draws, shapes of the workload)",
         "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context,
                    "heads": wl.heads, "idx_heads": wl.idx_heads, "idx_k_dtype": wl.idx_k_dtype,
@@ -535,6 +614,8 @@ def main():
             line["extra"][name]["unit"] = "queries/s"
             line["extra"][name]["steps"] = steps
             line["extra"][name]["roofline"] = res2.get("roofline")
+            if "attention_roofline" in res2:
+                line["extra"][name]["attention_roofline"] = res2["attention_roofline"]
     if args.proj_append:
         print("[bench] projection + append", file=sys.stderr, flush=True)
         line["proj_append"] = proj_item(args.steps, args.warmup, hip)

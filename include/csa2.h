@@ -388,12 +388,14 @@ csa2_status csa2_kv_import(const csa2_cache *cache, int32_t seq, int32_t len, co
 csa2_status csa2_local_clear(const csa2_local_cache *cache, int32_t seq, void *stream);
 
 /*
- * Profiling hook for callers that measure the index scan against the HBM
- * roofline.  After a call with non-NULL events (two hipEvent_t), every
- * csa2_index_topk call made later from the same host thread records `before`
- * and `after` on its stream immediately around its scoring kernel, the one
- * that streams the index keys.  csa2_profile_index_scan(NULL, NULL) turns the
- * hook off.  The events are caller-owned; the library only records them.
+ * Profiling hook for callers that measure the index scan against its
+ * roofline (bench use; no effect on results).  After a call with non-NULL
+ * events (two hipEvent_t), every csa2_index_topk call made later from the same
+ * host thread records `before` and `after` on its stream around its scoring:
+ * the streaming scorer's one kernel that reads the index keys, or the
+ * matrix-core scorer's two product passes together with the threshold kernel
+ * between them.  csa2_profile_index_scan(NULL, NULL) turns the hook off.  The
+ * events are caller-owned; the library only records them.
  */
 void csa2_profile_index_scan(void *before, void *after);
 

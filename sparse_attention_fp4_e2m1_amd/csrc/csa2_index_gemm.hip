@@ -703,12 +703,13 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
   if (before != nullptr) (void)hipEventRecord(before, s);
   if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 1, s);
   else launch_gemm_scores<4>(a, L, 1, s);
-  if (after != nullptr) (void)hipEventRecord(after, s);
   hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
                      reinterpret_cast<const uint16_t *>(w + L.bmax), L.bmax_row, a.q_pos, a.top_k,
                      reinterpret_cast<uint32_t *>(w + L.thr));
   if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 2, s);
   else launch_gemm_scores<4>(a, L, 2, s);
+  // the profiling events cover both product passes and the threshold between them
+  if (after != nullptr) (void)hipEventRecord(after, s);
   hipLaunchKernelGGL(gemm_resolve_kernel, dim3((unsigned)a.nq), dim3(kGemmResolveThreads), 0, s,
                      a.q_pos, a.top_k, reinterpret_cast<const uint32_t *>(w + L.plan),
                      reinterpret_cast<uint2 *>(w + L.cand), L.cand_stride,

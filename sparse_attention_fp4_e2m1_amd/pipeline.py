@@ -58,11 +58,14 @@ class LayerStack:
 
     def run(self, q: Sequence[torch.Tensor], q_idx: Sequence[torch.Tensor], q_seq: torch.Tensor,
             q_pos: torch.Tensor, append: Optional[tuple] = None, stream=None,
-            scan_events: Optional[tuple] = None):
+            scan_events: Optional[tuple] = None, mark=None):
         """Enqueue one step: optional append (k, v, idx_k, seq, pos), then every layer.
 
         scan_events: optional (before, after) hipEvent_t handles recorded around the
-        index-scan kernel of the first Full layer (csa2_profile_index_scan)."""
+        index scoring of the first Full layer (csa2_profile_index_scan).
+        mark: optional callable, called with ("attn", layer, "before" / "after")
+        right before and after each layer's attention call is enqueued (a
+        caller records its own events there)."""
         if append is not None:
             k, v, ik, seq, pos = append
             B.csa2_kv_append(self.cache, k, v, ik, seq, pos, stream=stream)
@@ -86,6 +89,10 @@ class LayerStack:
                 B.csa2_index_topk(self.cache, "reindex", q_idx[li], q_seq, q_pos, self.k[li],
                                   q_dtype=self.q_idx_dtype, pool_in=pool_in,
                                   topk_out=self.topk[li], workspace=self.ws_topk, stream=stream)
+            if mark is not None:
+                mark("attn", li, "before")
             B.csa2_sparse_attn(self.cache, q[li], q_seq, self.topk[li],
                                softmax_scale=self.softmax_scale, out=self.out[li],
                                lse=self.lse[li], workspace=self.ws_attn, stream=stream)
+            if mark is not None:
+                mark("attn", li, "after")

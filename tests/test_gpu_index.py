@@ -327,3 +327,27 @@ def test_matrix_core_long_rows():
     for i, p in enumerate(qpos):
         swaps += _relaxed_query(oc, 0, p, O.query_index_values(qi[i], "fp8"), got[i], top_k)
     announce(f"  swaps at the K-th score: {swaps}")
+
+
+def test_matrix_core_topk_is_deterministic():
+    # run twice on the same inputs: identical bytes (the block maxima, the
+    # threshold and the candidate compaction use atomics and cross-workgroup
+    # ordering, which must not leak into the result); a 700-query chunk of one
+    # sequence plus six queries of six sequences
+    announce("matrix-core determinism")
+    m = lib()
+    wl, gc, oc = _setup(8, "fp8")
+    rng = np.random.default_rng(5)
+    nq = 700
+    qpos = np.arange(CAP - nq, CAP)
+    qidx = synth.f32_to_bf16_bits(rng.standard_normal((nq, 8, 64)).astype(np.float32) * 2)
+    cases = [(dev_u16(qidx), dev_i32(np.full(nq, 3)), dev_i32(qpos), 2048),
+             (dev_u16(synth.gen_queries(wl, 0).q_idx), dev_i32(np.arange(len(QPOS))),
+              dev_i32(QPOS), 256)]
+    for q_idx, q_seq, q_pos, top_k in cases:
+        runs = []
+        for _ in range(2):
+            tk, _ = m.csa2_index_topk(gc, "full", q_idx, q_seq, q_pos, top_k, q_dtype="fp8")
+            torch.cuda.synchronize()
+            runs.append(host(tk))
+        assert np.array_equal(runs[0], runs[1])

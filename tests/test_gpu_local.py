@@ -163,3 +163,23 @@ def test_fused_nothing_visible():
     out, lse, _, _ = _run_fused(64, 64, np.full((2, 8), -1, np.int32),
                                 np.array([2400, 2400], np.int32), np.array([0, 2], np.int32))
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_fused_is_deterministic():
+    # the fused call twice on the same inputs: identical bytes of out and lse
+    announce("fused determinism")
+    m = lib()
+    wl, gc, oc = _global(64)
+    gl, ol = _local(300)
+    qseq = np.array([0, 1, 2, 0, 2], np.int32)
+    qpos = np.array([2999, 40, 2999, 2400, 2995], np.int32)
+    q = synth.gen_queries(wl, 0).q
+    q = np.concatenate([q] * 2)[:5]
+    topk = np.random.default_rng(8).integers(0, 2400, (5, 2048)).astype(np.int32)
+    runs = []
+    for _ in range(2):
+        out, lse = m.csa2_sparse_local_attn(gc, gl, dev_u16(q), dev_i32(qseq), dev_i32(qpos),
+                                            dev_i32(topk))
+        torch.cuda.synchronize()
+        runs.append((host(out), host(lse)))
+    assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1])
