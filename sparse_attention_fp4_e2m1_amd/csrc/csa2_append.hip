@@ -85,6 +85,11 @@ __device__ __forceinline__ void store_idx8(uint8_t *seq_idx, int H, int esz, int
   }
 }
 
+// One wave per row.  Every load of the row is issued first, with no branch
+// around it (a load under a lane-dependent branch is waited for before the
+// branch closes), so a decode step's handful of rows costs one memory round
+// trip: lanes 0..15 quantize one 16-channel block each (K blocks 0..7, then V),
+// and every lane stores eight channels of the index keys.
 __global__ void __launch_bounds__(256) kv_append_kernel(
     uint8_t *__restrict__ kv_codes, uint8_t *__restrict__ kv_scales, void *__restrict__ idx_k,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -94,15 +99,24 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (row >= n) return;
-  const int64_t slot = (int64_t)seq[row] * capacity + pos[row];
+  const int32_t sq = seq[row];
+  const int32_t ps = pos[row];
+  // K / V block (lanes 16..63 load lane % 16's block again, unused)
+  const bool is_v = (lane & 8) != 0;
+  const int blk = lane & 7;
+  const uint4 *s4 = reinterpret_cast<const uint4 *>((is_v ? v : k) + (int64_t)row * 128 + blk * 16);
+  const uint4 a = s4[0], b = s4[1];
+  // index keys: 8 channels per lane (lanes past the row's H * 64 channels
+  // load the last group again, unused; without index keys the row's K
+  // channels stand in, unused)
+  const int e = min(lane * 8, idx_elems - 8);
+  const uint16_t *isrc = idx_in != nullptr ? idx_in + (int64_t)row * idx_elems + e
+                                           : k + (int64_t)row * 128;
+  const uint4 ik = *reinterpret_cast<const uint4 *>(isrc);
+  const int64_t slot = (int64_t)sq * capacity + ps;
 
   if (lane < 16) {
-    const bool is_v = lane >= 8;
-    const int blk = lane & 7;
-    const uint16_t *src = (is_v ? v : k) + (int64_t)row * 128 + blk * 16;
-    const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
-    uint4 a = s4[0], b = s4[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     float x[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -116,16 +130,12 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
     kv_scales[slot * 16 + (is_v ? 8 : 0) + blk] = (uint8_t)sc;
   }
 
-  if (idx_in != nullptr) {
-    // idx_elems = H * 64 bf16 values: 8 per lane-step
+  if (idx_in != nullptr && lane * 8 < idx_elems) {
     const int H = idx_elems / 64;
     const int esz = idx_fp8 ? 1 : 2;
     const int64_t seq_bytes = (int64_t)capacity * idx_elems * esz;
-    uint8_t *seq_idx = static_cast<uint8_t *>(idx_k) + (int64_t)seq[row] * seq_bytes;
-    const uint16_t *src = idx_in + (int64_t)row * idx_elems;
-    for (int e = lane * 8; e < idx_elems; e += kWave * 8)
-      store_idx8(seq_idx, H, esz, pos[row], e / 64, e % 64,
-                 *reinterpret_cast<const uint4 *>(src + e));
+    uint8_t *seq_idx = static_cast<uint8_t *>(idx_k) + (int64_t)sq * seq_bytes;
+    store_idx8(seq_idx, H, esz, ps, e / 64, e % 64, ik);
   }
 }
 

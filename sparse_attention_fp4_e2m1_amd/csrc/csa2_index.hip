@@ -10,7 +10,8 @@
 // indexer bounds the deeper indexers' cost by the pool size.
 //
 // Kernels, in launch order for one call:
-//   zero2_u32_kernel clear the per-query histograms
+//   zero2_u32_kernel clear the per-query histograms (only where the scorer
+//                    adds into a global histogram)
 //   score_kernel     (Full, or Reindex without a pool; gather_score_kernel for
 //                    a Reindex pool) stream the (tiled) index keys, compute the canonical fp32
 //                    score of each candidate, keep its order-preserving key
@@ -30,10 +31,15 @@
 //                    streams the full key array with the same logic.
 //                    A pool-building Full layer selects its pool blocks in the
 //                    same filter and resolve launches (a second grid slice).
-//                    Key arrays of at most kDirectMax entries (a Reindex pool)
-//                    skip the filter: the resolve reads them, builds their
-//                    histogram in LDS and compacts them (such a pool's scorer
-//                    builds no global histogram, and nothing is cleared).
+//                    Key arrays of at most kDirectMax entries skip the
+//                    filter: the resolve reads them and compacts them itself.
+//                    The 12-bit histogram comes from the scorer's per-chunk
+//                    slots (a Full layer without a pool over at most
+//                    kMaxSlots chunks: each scorer workgroup stores its
+//                    chunk's histogram, nothing is cleared, and the filter
+//                    leaves the bits 19..8 pass to the resolve), from the
+//                    global histogram (a pool-building Full layer, long
+//                    contexts), or is counted by the resolve (a Reindex pool).
 // Small score chunks (one wave) count keys straight into the global histogram.
 //   copy_i32_kernel  Reuse mode: topk_out = reuse_src.
 // The selection helpers (select_bin, select_core, gather_regions) live in
@@ -56,6 +62,10 @@ constexpr int kFilterSubMin = 512;
 constexpr int kFilterSubMax = 1024;
 constexpr int64_t kFilterSmallMax = (int64_t)kFilterSubMin * 1024;
 constexpr int64_t kDirectMax = 32768;      // up to this many keys the resolve filters them itself
+constexpr int kSlotWords = kHistBins / 2;  // words of one chunk's packed histogram
+// Chunk histograms a selection adds up at most (every filter workgroup reads
+// them all); past this the scorer adds into the global histogram instead.
+constexpr int64_t kMaxSlots = 16;
 constexpr int kEarlySlots = 8;             // candidate slots per resolve thread read before the counts
 // Keys in the threshold bin beyond which the filter leaves the bits 19..8 pass
 // to the resolve (heavy ties would serialize the global atomics).
@@ -273,7 +283,9 @@ score_kernel(
     int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
     uint32_t *__restrict__ keys_tok, int64_t tok_stride, uint32_t *__restrict__ hist_tok,
     uint32_t *__restrict__ keys_blk, int64_t blk_stride, uint32_t *__restrict__ hist_blk,
-    int64_t hstride, int32_t hcopies) {
+    int64_t hstride, int32_t hcopies, uint32_t *__restrict__ hist_slots) {
+  // hist_slots != nullptr: store this chunk's packed histogram in slot
+  // (q, blockIdx.x) instead of adding it into the global histogram
   constexpr int kEsz = kFp8Keys ? 1 : 2;
   constexpr int TPI = kWave / H;
   constexpr int kBpt = H * 64 * kEsz;     // bytes per token
@@ -366,6 +378,12 @@ score_kernel(
     }
   }
   if (Ctx::kDirectHist) return;
+  if (!kPool && hist_slots != nullptr) {   // uniform
+    uint4 *dst = reinterpret_cast<uint4 *>(hist_slots + ((int64_t)q * gridDim.x + blockIdx.x) * kSlotWords);
+    for (int i = threadIdx.x; i < kSlotWords / 4; i += kThreads)
+      dst[i] = reinterpret_cast<const uint4 *>(hist)[i];
+    return;
+  }
   uint32_t *hbq = kPool ? hist_blk + hoff : nullptr;
   for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
     const uint32_t w = hist[i];
@@ -504,11 +522,45 @@ struct SelProblem {
   int32_t mode;           // OutMode
   int32_t direct;         // short arrays: no filter pass, the resolve reads the keys
   int32_t region;         // keys per filter wave: kFilterSubMin or kFilterSubMax
+  int32_t hsrc;           // HistSource of a direct array
+  const uint32_t *slots;  // [nq][nslots][kSlotWords] (kHistSlots)
+  int32_t nslots;
+  int32_t slot_chunk;     // keys per slot
 };
 
 struct SelProblems {
   SelProblem p[2];
 };
+
+// The 12-bit histogram of one query from the scorer's chunk slots (kHistSlots)
+// into LDS: the slots of the chunks that hold visible keys, added up (every
+// such slot was written by this call).  Thread t adds bins 4t .. 4t+3 (words
+// 2t, 2t+1 of every slot), loading 16 slots at a time with no branch around
+// the loads.  A block of kSlotWords / 2 threads; ends with a barrier.
+static_assert(kSlotWords / 2 == kSelectThreads && kSlotWords / 2 == kFilterThreads,
+              "one word pair of every slot per thread");
+__device__ __forceinline__ void slot_hist_to_lds(const SelProblem &A, int q, int64_t n,
+                                                 uint32_t *lh) {
+  const int tid = threadIdx.x;
+  const int nsl = (int)((n + A.slot_chunk - 1) / A.slot_chunk);
+  const uint2 *sq = reinterpret_cast<const uint2 *>(A.slots + (int64_t)q * A.nslots * kSlotWords) + tid;
+  uint32_t b0 = 0u, b1 = 0u, b2 = 0u, b3 = 0u;
+  for (int s0 = 0; s0 < nsl; s0 += 16) {
+    uint2 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = sq[(int64_t)min(s0 + u, nsl - 1) * (kSlotWords / 2)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const bool in = s0 + u < nsl;
+      b0 += in ? (v[u].x & 0xFFFFu) : 0u;
+      b1 += in ? (v[u].x >> 16) : 0u;
+      b2 += in ? (v[u].y & 0xFFFFu) : 0u;
+      b3 += in ? (v[u].y >> 16) : 0u;
+    }
+  }
+  reinterpret_cast<uint4 *>(lh)[tid] = make_uint4(b0, b1, b2, b3);
+  __syncthreads();
+}
 
 // grid (filter groups, nq, problems).  Each wave takes A.region keys and
 // keeps every key whose top 12 bits reach bin b1, with its index, in index
@@ -532,29 +584,32 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
   const int64_t sub = (int64_t)blockIdx.x * (kFilterThreads / kWave) + threadIdx.x / kWave;
   const int64_t start = sub * A.region;
   const uint32_t *kq = A.keys + (int64_t)q * A.n_stride;
-  // region / 256 x 4 keys per lane; key (k, lane, e) sits at start + k*256 + lane*4 + e
+  // region / 256 x 4 keys per lane; key (k, lane, e) sits at start + k*256 + lane*4 + e.
+  // Branch-free loads (all in flight together): addresses clamped into the
+  // query's row; keys of steps past `iters` or at or past n are masked below.
   const int iters = A.region / 256;   // uniform, <= kIters
+  const int64_t last4 = A.n_stride - 4;
   uint32_t kv[kIters][4];
 #pragma unroll
   for (int k = 0; k < kIters; ++k) {
-    const int64_t i0 = start + k * 256 + lane * 4;
-    if (k >= iters) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kv[k][e] = 0u;
-    } else if (i0 + 3 < n) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kq + i0));
-      kv[k][0] = v.x;
-      kv[k][1] = v.y;
-      kv[k][2] = v.z;
-      kv[k][3] = v.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kv[k][e] = i0 + e < n ? kq[i0 + e] : 0u;
-    }
+    const int64_t i0 = min(start + k * 256 + lane * 4, last4);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kq + i0));
+    kv[k][0] = v.x;
+    kv[k][1] = v.y;
+    kv[k][2] = v.z;
+    kv[k][3] = v.w;
   }
   uint32_t *hs = A.hist + (int64_t)q * A.hstride;
-  const Threshold th = hist_threshold(hs, A.hcopies, n, A.kk, lh, scratch, res);
-  const bool use_h2 = th.keff > 0u && lh[th.b1] <= kH2MaxKeys;   // lh still holds the histogram
+  Threshold th;
+  if (A.hsrc == kHistSlots) {   // uniform
+    slot_hist_to_lds(A, q, n, lh);
+    th = lds_threshold(n, A.kk, lh, scratch, res);
+  } else {
+    th = hist_threshold(hs, A.hcopies, n, A.kk, lh, scratch, res);
+  }
+  // the second histogram (bits 19..8 of the threshold bin's keys) is added
+  // into global memory: only where the call clears its histograms
+  const bool use_h2 = A.hsrc == kHistGlobal && th.keff > 0u && lh[th.b1] <= kH2MaxKeys;
   if (blockIdx.x == 0 && threadIdx.x == 0)
     *reinterpret_cast<uint4 *>(hs + state_off(A.hcopies)) =
         make_uint4(th.keff, th.b1, th.above, use_h2 ? 1u : 0u);
@@ -614,23 +669,27 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
   const int tid = threadIdx.x;
   const int32_t qp = q_pos[q];
   const int64_t n = sel_len(A.mode, qp, pool_len);
-  // A short key array is read here, in one batch of loads issued before the
-  // histogram's (keys 4*tid + 4096*it .. +3 of iteration it).
+  // A short key array is read by this workgroup whole, in passes of
+  // kDirectBatch quads per thread (keys 4*tid + 4096*it .. +3 of iteration it),
+  // each pass one batch of loads: for the histogram when the resolve counts
+  // the keys itself, then to count the candidates and to write them (the
+  // passes after the first read from L2).  The loads are branch-free, so that
+  // a batch is in flight together (a load under a lane-dependent branch is
+  // waited for before the branch closes): every lane loads four whole keys,
+  // its address clamped into the query's row; keys at or past n are masked
+  // wherever they are used.
   constexpr int kDirectIters = (int)(kDirectMax / (4 * kSelectThreads));
+  constexpr int kDirectBatch = 8;
+  static_assert(kDirectIters % kDirectBatch == 0, "whole batches");
   const uint32_t *kq = A.keys + (int64_t)q * A.n_stride;
-  uint4 kr[kDirectIters];
-  if (A.direct) {
+  auto load_batch = [&](int it0, uint4 (&kb)[kDirectBatch]) {
+    const int64_t last4 = A.n_stride - 4;
 #pragma unroll
-    for (int it = 0; it < kDirectIters; ++it) {
-      const int64_t i0 = (int64_t)it * 4 * kSelectThreads + 4 * tid;
-      kr[it] = i0 + 3 < n ? *reinterpret_cast<const uint4 *>(kq + i0) : make_uint4(0u, 0u, 0u, 0u);
-      if (i0 < n && i0 + 3 >= n) {
-        kr[it].x = kq[i0];
-        if (i0 + 1 < n) kr[it].y = kq[i0 + 1];
-        if (i0 + 2 < n) kr[it].z = kq[i0 + 2];
-      }
+    for (int j = 0; j < kDirectBatch; ++j) {
+      const int64_t i0 = min((int64_t)(it0 + j) * 4 * kSelectThreads + 4 * tid, last4);
+      kb[j] = *reinterpret_cast<const uint4 *>(kq + i0);
     }
-  }
+  };
   const int64_t nsub = (n + A.region - 1) / A.region;
   const uint32_t *cq = A.cnt + (int64_t)q * A.nsub;
   const uint32_t first_count = A.direct ? 0u : first_region_count(cq, nsub);
@@ -641,19 +700,28 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
   const uint32_t *hs = A.hist + (int64_t)q * A.hstride;
   Threshold th;
   Pass19 p19{false, 0u, 0u};
-  if (A.direct) {
+  if (A.direct && A.hsrc == kHistSlots) {
+    slot_hist_to_lds(A, q, n, hist);
+    th = lds_threshold(n, A.kk, hist, scratch, res);
+  } else if (A.direct && A.hsrc == kHistGlobal) {
+    th = hist_threshold(hs, A.hcopies, n, A.kk, hist, scratch, res);
+  } else if (A.direct) {
     // the 12-bit histogram of the short key array, built here in LDS (the
     // keys past n are not counted)
     for (int i = tid; i < kHistBins; i += kSelectThreads) hist[i] = 0u;
     __syncthreads();
+    for (int it0 = 0; it0 < kDirectIters && (int64_t)it0 * 4 * kSelectThreads < n;
+         it0 += kDirectBatch) {
+      uint4 kb[kDirectBatch];
+      load_batch(it0, kb);
 #pragma unroll
-    for (int it = 0; it < kDirectIters; ++it) {
-      const int64_t i0 = (int64_t)it * 4 * kSelectThreads + 4 * tid;
-      if ((int64_t)it * 4 * kSelectThreads >= n) break;   // uniform
-      const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
+      for (int j = 0; j < kDirectBatch; ++j) {
+        const int64_t i0 = (int64_t)(it0 + j) * 4 * kSelectThreads + 4 * tid;
+        const uint32_t k4[4] = {kb[j].x, kb[j].y, kb[j].z, kb[j].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (i0 + e < n) atomicAdd(&hist[k4[e] >> 20], 1u);
+        for (int e = 0; e < 4; ++e)
+          if (i0 + e < n) atomicAdd(&hist[k4[e] >> 20], 1u);
+      }
     }
     __syncthreads();
     th = lds_threshold(n, A.kk, hist, scratch, res);
@@ -692,18 +760,29 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     // only the iterations that hold keys (uniform); the totals of the others count as 0
     const int nd = (int)n;   // <= kDirectMax
     const int nit = (nd + 4 * kSelectThreads - 1) / (4 * kSelectThreads);
-    uint32_t wexcl[kDirectIters];
+    // pass 1: per iteration this lane's candidates and the wave's exclusive
+    // scan of them (at most 252: two 16-bit halves per word)
+    uint32_t wx[kDirectIters / 2];
 #pragma unroll
-    for (int it = 0; it < kDirectIters; ++it) {
-      if (it >= nit) break;
-      const int i0 = it * 4 * kSelectThreads + 4 * tid;
-      const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
-      uint32_t c = 0;
+    for (int i = 0; i < kDirectIters / 2; ++i) wx[i] = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c += (th.keff > 0 && i0 + e < nd && k4[e] >= thr) ? 1u : 0u;
-      const uint32_t inc = wave_inclusive_scan(c);
-      wexcl[it] = inc - c;
-      if (lane == kWave - 1) goff[it * kWaves + wave] = inc;
+    for (int bt = 0; bt < kDirectIters / kDirectBatch; ++bt) {
+      const int it0 = bt * kDirectBatch;
+      if (it0 >= nit) continue;   // uniform
+      uint4 kb[kDirectBatch];
+      load_batch(it0, kb);
+#pragma unroll
+      for (int j = 0; j < kDirectBatch; ++j) {
+        const int it = it0 + j;
+        const int i0 = it * 4 * kSelectThreads + 4 * tid;
+        const uint32_t k4[4] = {kb[j].x, kb[j].y, kb[j].z, kb[j].w};
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += (th.keff > 0 && i0 + e < nd && k4[e] >= thr) ? 1u : 0u;
+        const uint32_t inc = wave_inclusive_scan(c);
+        wx[it / 2] |= (inc - c) << (16 * (it & 1));
+        if (lane == kWave - 1) goff[it * kWaves + wave] = inc;
+      }
     }
     __syncthreads();
     if (wave == 0) {
@@ -725,20 +804,28 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     }
     __syncthreads();
     carry = goff[kEnt];
+    // pass 2: the keys again (from L2), the candidates written in index order
 #pragma unroll
-    for (int it = 0; it < kDirectIters; ++it) {
-      if (it >= nit) break;
-      const int i0 = it * 4 * kSelectThreads + 4 * tid;
-      const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
-      uint32_t o = goff[it * kWaves + wave] + wexcl[it];
+    for (int bt = 0; bt < kDirectIters / kDirectBatch; ++bt) {
+      const int it0 = bt * kDirectBatch;
+      if (it0 >= nit) continue;   // uniform
+      uint4 kb[kDirectBatch];
+      load_batch(it0, kb);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (th.keff > 0 && i0 + e < nd && k4[e] >= thr) {
-          if (o < kResolveCap) {
-            lkey[o] = k4[e];
-            lid[o] = (int32_t)(i0 + e);
+      for (int j = 0; j < kDirectBatch; ++j) {
+        const int it = it0 + j;
+        const int i0 = it * 4 * kSelectThreads + 4 * tid;
+        const uint32_t k4[4] = {kb[j].x, kb[j].y, kb[j].z, kb[j].w};
+        uint32_t o = goff[it * kWaves + wave] + ((wx[it / 2] >> (16 * (it & 1))) & 0xFFFFu);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (th.keff > 0 && i0 + e < nd && k4[e] >= thr) {
+            if (o < kResolveCap) {
+              lkey[o] = k4[e];
+              lid[o] = (int32_t)(i0 + e);
+            }
+            ++o;
           }
-          ++o;
         }
       }
     }
@@ -772,27 +859,38 @@ void launch_score_shape(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
   const csa2_cache &c = *a.cache;
   const TopkWorkspace &L = a.layout;
   dim3 grid((unsigned)((n_cand_max + kChunk - 1) / kChunk), (unsigned)a.nq);
+  uint32_t *slots = nullptr;
+  if (L.tok.hsrc == kHistSlots) {
+    slots = reinterpret_cast<uint32_t *>(a.ws + L.tok.slots);
+    if (L.tok.slot_chunk != kChunk || (int64_t)L.tok.nslots != (int64_t)grid.x) return;   // never: same rule
+  }
   hipLaunchKernelGGL((score_kernel<H, kFp8, kPool, kThreads, kChunk>), grid, dim3(kThreads), 0, s,
                      static_cast<const uint8_t *>(c.idx_k), (int64_t)c.capacity, a.q_idx, a.q_fp8,
                      a.q_seq, a.q_pos, reinterpret_cast<uint32_t *>(a.ws + L.tok.keys), L.tok.n,
                      reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
                      kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.keys) : nullptr, L.blk.n,
                      kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr,
-                     L.tok.hstride, L.tok.hcopies);
+                     L.tok.hstride, L.tok.hcopies, slots);
 }
 
 // Workgroup shape from the amount of work: long streams when there are enough
 // groups, one-wave groups for small searches so that they spread over the chip.
+// Returns the candidates per workgroup (4096, 2048 or 64).
+int32_t score_chunk(int32_t nq, int64_t n_cand_max, bool pool) {
+  const int64_t big = (int64_t)nq * ((n_cand_max + 4095) / 4096);
+  const int64_t mid = (int64_t)nq * ((n_cand_max + 2047) / 2048);
+  if (big >= kBigChunkMinGroups) return 4096;
+  if (mid >= kSmallGridGroups || pool) return 2048;
+  return 64;
+}
+
 template <int H, bool kFp8, bool kPool>
 void launch_score(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
-  const int64_t big = (int64_t)a.nq * ((n_cand_max + 4095) / 4096);
-  const int64_t mid = (int64_t)a.nq * ((n_cand_max + 2047) / 2048);
-  if (big >= kBigChunkMinGroups)
-    launch_score_shape<H, kFp8, kPool, 256, 4096>(a, n_cand_max, s);
-  else if (mid >= kSmallGridGroups || kPool)
-    launch_score_shape<H, kFp8, kPool, 256, 2048>(a, n_cand_max, s);
-  else
-    launch_score_shape<H, kFp8, false, 64, 64>(a, n_cand_max, s);
+  switch (score_chunk(a.nq, n_cand_max, kPool)) {
+    case 4096: launch_score_shape<H, kFp8, kPool, 256, 4096>(a, n_cand_max, s); break;
+    case 2048: launch_score_shape<H, kFp8, kPool, 256, 2048>(a, n_cand_max, s); break;
+    default: launch_score_shape<H, kFp8, false, 64, 64>(a, n_cand_max, s); break;
+  }
 }
 
 template <int H, bool kFp8>
@@ -805,8 +903,8 @@ void launch_score_mode(const IndexArgs &a, int64_t n, bool pool, bool reindex_po
                        dim3(kGatherThreads), 0, s, static_cast<const uint8_t *>(a.cache->idx_k),
                        (int64_t)a.cache->capacity, a.q_idx, a.q_fp8, a.q_seq, a.q_pos, a.pool_in,
                        a.pool_len, reinterpret_cast<uint32_t *>(a.ws + L.tok.keys), L.tok.n,
-                       a.pool_len <= kDirectMax ? nullptr
-                                                : reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
+                       L.tok.hsrc == kHistKeys ? nullptr
+                                               : reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
                        L.tok.hstride, L.tok.hcopies);
   } else if (pool) {
     launch_score<H, kFp8, true>(a, n, s);
@@ -835,6 +933,10 @@ SelProblem sel_problem(const IndexArgs &a, const SelectArrays &A, int32_t kk, in
   p.mode = mode;
   p.direct = A.n <= kDirectMax;
   p.region = A.region;
+  p.hsrc = A.hsrc;
+  p.slots = reinterpret_cast<const uint32_t *>(w + A.slots);
+  p.nslots = A.nslots;
+  p.slot_chunk = A.slot_chunk;
   return p;
 }
 
@@ -907,6 +1009,20 @@ TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t
   const int32_t hc = hist_copies(n_tok);
   size_t off = carve(w.tok, n_tok, nq, 0, hc);
   if (pool) off = carve(w.blk, ((int64_t)c.capacity + kPoolBlock - 1) / kPoolBlock, nq, off, hc);
+  // where each selection finds its histogram (see HistSource)
+  w.tok.hsrc = reindex_pool ? (pool_len <= kDirectMax ? kHistKeys : kHistGlobal) : kHistGlobal;
+  w.blk.hsrc = kHistGlobal;
+  if (!reindex_pool && !pool) {
+    const int32_t chunk = score_chunk(nq, n_tok, false);
+    const int64_t nslots = (n_tok + chunk - 1) / chunk;
+    if (chunk >= 2048 && nslots <= kMaxSlots) {   // a handful of chunks per query: one slot each
+      w.tok.hsrc = kHistSlots;
+      w.tok.slot_chunk = chunk;
+      w.tok.nslots = (int32_t)nslots;
+      w.tok.slots = off;
+      off = align256(off + (size_t)nq * w.tok.nslots * kSlotWords * 4);
+    }
+  }
   w.total = off;
   if (gemm_eligible(c, mode, pool_len, pool_blocks)) {
     w.gemm = gemm_workspace_layout(c, nq);
@@ -928,10 +1044,11 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
   const TopkWorkspace &L = a.layout;
   const bool pool = a.mode == CSA2_FULL && a.pool_blocks > 0;
   const bool reindex_pool = a.mode == CSA2_REINDEX && a.pool_in != nullptr;
-  // 1. clear the histograms (the token and block histograms are cleared by one
-  //    launch when both exist: the block one follows the token arrays).  A
-  //    pool short enough for the resolve to read whole needs none.
-  if (!(reindex_pool && a.pool_len <= kDirectMax)) {
+  // 1. clear the global histograms (the token and block histograms are
+  //    cleared by one launch when both exist: the block one follows the token
+  //    arrays).  Slot histograms and a pool short enough for the resolve to
+  //    count need none.
+  if (L.tok.hsrc == kHistGlobal) {
     const int64_t n_tok = (int64_t)a.nq * L.tok.hstride;
     const unsigned blocks = (unsigned)std::min<int64_t>((n_tok + 255) / 256, 2048);
     hipLaunchKernelGGL(zero2_u32_kernel, dim3(blocks), dim3(256), 0, s,

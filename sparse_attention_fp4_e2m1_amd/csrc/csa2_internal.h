@@ -11,6 +11,16 @@
 namespace csa2 {
 
 constexpr int kHistBins = 4096;      // first radix pass: top 12 bits of the score key
+// Where a selection's 12-bit histogram comes from:
+//   kHistKeys    the resolve counts the keys itself (a Reindex pool: its scorer
+//                builds no histogram);
+//   kHistGlobal  the scorer's workgroups add theirs into the query's global
+//                histogram copies (cleared by a launch before the scorer);
+//   kHistSlots   each scorer workgroup stores its chunk's histogram (16-bit
+//                bins packed in pairs) in a slot of its own; the resolve adds
+//                the slots up (nothing to clear: every slot a resolve reads is
+//                written by the same call).
+enum HistSource { kHistKeys = 0, kHistGlobal = 1, kHistSlots = 2 };
 constexpr int kPoolBlock = 8;        // positions per candidate-pool block
 
 hipError_t launch_kv_append(const csa2_cache &c, const uint16_t *k, const uint16_t *v,
@@ -30,6 +40,10 @@ struct SelectArrays {      // one selection problem per query (tokens, or pool b
   int32_t region = 0;      // keys per filter wave (slots per region)
   int32_t hcopies = 1;     // copies of the 12-bit histogram (scorer workgroups spread over them)
   int64_t hstride = 0;     // words per query: hcopies histograms, state words, second histogram
+  int32_t hsrc = 0;        // HistSource: where the resolve finds the 12-bit histogram
+  size_t slots = 0;        // uint32 [nq][nslots][kHistBins / 2]: per-chunk histograms (kHistSlots)
+  int32_t nslots = 0;      // scorer chunks per query (kHistSlots)
+  int32_t slot_chunk = 0;  // candidates per scorer chunk (kHistSlots)
 };
 
 // Workspace carve-up of the matrix-core scorer (E4M3 index queries and keys).

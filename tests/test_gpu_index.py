@@ -351,3 +351,36 @@ def test_matrix_core_topk_is_deterministic():
             torch.cuda.synchronize()
             runs.append(host(tk))
         assert np.array_equal(runs[0], runs[1])
+
+
+@pytest.mark.parametrize("nq,heads,idx_dtype,cap", [(64, 8, "fp8", 16400), (128, 8, "fp8", 16400),
+                                                     (128, 4, "bf16", 16400), (64, 8, "fp8", 40000)])
+def test_full_topk_chunk_histograms(nq, heads, idx_dtype, cap):
+    # enough queries x candidates for the scorer's 2048- (64 queries x 16400)
+    # and 4096-candidate workgroups: each workgroup stores its chunk's
+    # histogram in a slot of its own and the selection adds up the slots of
+    # the chunks a query sees -- the resolve alone up to 32768 keys, the
+    # filter's workgroups each (and no second histogram) past that (40000).
+    # Queries at chunk boundaries and in the ragged last chunk.
+    announce(f"chunk histograms nq={nq} heads={heads} idx={idx_dtype}")
+    m = lib()
+    nseq = 4
+    wl = synth.workload("decode_64k_b32", context=cap, batch=nseq, idx_heads=heads,
+                        idx_k_dtype=idx_dtype, seed=9)
+    gc, oc, _ = filled_caches(wl)
+    rng = np.random.default_rng(nq + heads)
+    special = [p for p in (0, 5, 2047, 2048, 4095, 4096, 8191, 12288, 16383, 16384, 36863, 36864)
+               if p < cap] + [cap - 1]
+    qpos = np.concatenate([special, rng.integers(0, cap, nq - len(special))]).astype(np.int32)
+    qseq = (np.arange(nq) % nseq).astype(np.int32)
+    qidx = synth.f32_to_bf16_bits(rng.standard_normal((nq, heads, 64)).astype(np.float32))
+    got = {}
+    for top_k in (2048, 100):
+        tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qidx), dev_i32(qseq), dev_i32(qpos), top_k)
+        torch.cuda.synchronize()
+        got[top_k] = host(tk)
+    for i in range(nq):
+        qi = O.query_index_values(qidx[i], "bf16")
+        want, _, scores, cand = O.index_topk("full", oc, int(qseq[i]), int(qpos[i]), qi, 2048)
+        assert np.array_equal(got[2048][i], want), (2048, i, int(qpos[i]))
+        assert np.array_equal(got[100][i], O.topk_select(scores, cand, 100)), (100, i, int(qpos[i]))
