@@ -201,6 +201,9 @@ size_t csa2_sparse_attn_workspace(const csa2_cache *cache, int32_t nq, int32_t n
  *   lse        [nq][n_heads] fp32 natural-log sum of exp(z_j), or NULL.
  * An empty selection gives out = 0 and lse = -inf.  Accumulation is fp32 on
  * matrix cores (fp16 q.K products, fp16 probabilities times V).
+ * Input range: q is rounded once to fp16, so every |q| element must be at most
+ * 65504 (larger finite bf16 values overflow to infinity and make out and lse
+ * NaN); elements below 2^-14 in magnitude lose bits below 2^-24.
  * Supported: n_heads a multiple of 16 up to 128; dk = dv = 128.
  * Device preconditions: 0 <= q_seq < batch; topk entries < capacity.
  * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED,
@@ -285,7 +288,8 @@ csa2_status csa2_local_append(const csa2_local_cache *cache, const uint16_t *k, 
  *              z_j = softmax_scale * q_h . K_j over both sets.
  * Rows of both sets are different cached values (the global FP4 KV and the
  * layer's own FP8 window), so a position in both counts twice.  Accumulation
- * is fp32 on matrix cores (fp16 q.K products, fp16 probabilities times V).
+ * is fp32 on matrix cores (fp16 q.K products, fp16 probabilities times V);
+ * q must lie within the fp16 range (|q| <= 65504), as for csa2_sparse_attn.
  * Supported: n_heads a multiple of 16 up to 128; dk = dv = 128.
  * Device preconditions: 0 <= q_seq < batch, q_pos >= 0.
  * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED, CSA2_ERR_HIP.
@@ -306,8 +310,9 @@ csa2_status csa2_local_attn(const csa2_local_cache *cache, const uint16_t *q, in
  *   out, lse   [nq][n_heads][dv], [nq][n_heads] (lse may be NULL): the
  *              softmax attention over the union of both sets of rows.
  *   workspace  device scratch of csa2_sparse_local_attn_workspace bytes.
- * Supported, device preconditions and errors: as csa2_sparse_attn together
- * with csa2_local_attn (CSA2_ERR_SHAPE also for local->batch < batch).
+ * Supported, input range, device preconditions and errors: as
+ * csa2_sparse_attn together with csa2_local_attn (CSA2_ERR_SHAPE also for
+ * local->batch < batch).
  */
 size_t csa2_sparse_local_attn_workspace(const csa2_cache *cache, const csa2_local_cache *local,
                                         int32_t nq, int32_t n_heads, int32_t top_k);

@@ -669,27 +669,24 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
   const int tid = threadIdx.x;
   const int32_t qp = q_pos[q];
   const int64_t n = sel_len(A.mode, qp, pool_len);
-  // A short key array is read by this workgroup whole, in passes of
-  // kDirectBatch quads per thread (keys 4*tid + 4096*it .. +3 of iteration it),
-  // each pass one batch of loads: for the histogram when the resolve counts
-  // the keys itself, then to count the candidates and to write them (the
-  // passes after the first read from L2).  The loads are branch-free, so that
-  // a batch is in flight together (a load under a lane-dependent branch is
-  // waited for before the branch closes): every lane loads four whole keys,
-  // its address clamped into the query's row; keys at or past n are masked
-  // wherever they are used.
+  // A short key array is read by this workgroup whole, in one batch of loads
+  // issued first (keys 4*tid + 4096*it .. +3 of iteration it) and held in
+  // registers for the histogram, the count and the compaction.  The loads
+  // are branch-free, so that all of them are in flight together (a load under
+  // a lane-dependent branch is waited for before the branch closes): every
+  // lane loads four whole keys, its address clamped into the query's row;
+  // keys at or past n are masked wherever they are used.
   constexpr int kDirectIters = (int)(kDirectMax / (4 * kSelectThreads));
-  constexpr int kDirectBatch = 8;
-  static_assert(kDirectIters % kDirectBatch == 0, "whole batches");
   const uint32_t *kq = A.keys + (int64_t)q * A.n_stride;
-  auto load_batch = [&](int it0, uint4 (&kb)[kDirectBatch]) {
+  uint4 kr[kDirectIters];
+  if (A.direct) {
     const int64_t last4 = A.n_stride - 4;
 #pragma unroll
-    for (int j = 0; j < kDirectBatch; ++j) {
-      const int64_t i0 = min((int64_t)(it0 + j) * 4 * kSelectThreads + 4 * tid, last4);
-      kb[j] = *reinterpret_cast<const uint4 *>(kq + i0);
+    for (int it = 0; it < kDirectIters; ++it) {
+      const int64_t i0 = min((int64_t)it * 4 * kSelectThreads + 4 * tid, last4);
+      kr[it] = *reinterpret_cast<const uint4 *>(kq + i0);
     }
-  };
+  }
   const int64_t nsub = (n + A.region - 1) / A.region;
   const uint32_t *cq = A.cnt + (int64_t)q * A.nsub;
   const uint32_t first_count = A.direct ? 0u : first_region_count(cq, nsub);
@@ -710,18 +707,13 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     // keys past n are not counted)
     for (int i = tid; i < kHistBins; i += kSelectThreads) hist[i] = 0u;
     __syncthreads();
-    for (int it0 = 0; it0 < kDirectIters && (int64_t)it0 * 4 * kSelectThreads < n;
-         it0 += kDirectBatch) {
-      uint4 kb[kDirectBatch];
-      load_batch(it0, kb);
 #pragma unroll
-      for (int j = 0; j < kDirectBatch; ++j) {
-        const int64_t i0 = (int64_t)(it0 + j) * 4 * kSelectThreads + 4 * tid;
-        const uint32_t k4[4] = {kb[j].x, kb[j].y, kb[j].z, kb[j].w};
+    for (int it = 0; it < kDirectIters; ++it) {
+      const int64_t i0 = (int64_t)it * 4 * kSelectThreads + 4 * tid;
+      const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i0 + e < n) atomicAdd(&hist[k4[e] >> 20], 1u);
-      }
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e < n) atomicAdd(&hist[k4[e] >> 20], 1u);
     }
     __syncthreads();
     th = lds_threshold(n, A.kk, hist, scratch, res);
@@ -760,29 +752,21 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     // only the iterations that hold keys (uniform); the totals of the others count as 0
     const int nd = (int)n;   // <= kDirectMax
     const int nit = (nd + 4 * kSelectThreads - 1) / (4 * kSelectThreads);
-    // pass 1: per iteration this lane's candidates and the wave's exclusive
-    // scan of them (at most 252: two 16-bit halves per word)
+    // per iteration this lane's candidates and the wave's exclusive scan of
+    // them (at most 252: two 16-bit halves per word)
     uint32_t wx[kDirectIters / 2];
 #pragma unroll
     for (int i = 0; i < kDirectIters / 2; ++i) wx[i] = 0u;
 #pragma unroll
-    for (int bt = 0; bt < kDirectIters / kDirectBatch; ++bt) {
-      const int it0 = bt * kDirectBatch;
-      if (it0 >= nit) continue;   // uniform
-      uint4 kb[kDirectBatch];
-      load_batch(it0, kb);
+    for (int it = 0; it < kDirectIters; ++it) {
+      const int i0 = it * 4 * kSelectThreads + 4 * tid;
+      const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
+      uint32_t c = 0;
 #pragma unroll
-      for (int j = 0; j < kDirectBatch; ++j) {
-        const int it = it0 + j;
-        const int i0 = it * 4 * kSelectThreads + 4 * tid;
-        const uint32_t k4[4] = {kb[j].x, kb[j].y, kb[j].z, kb[j].w};
-        uint32_t c = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c += (th.keff > 0 && i0 + e < nd && k4[e] >= thr) ? 1u : 0u;
-        const uint32_t inc = wave_inclusive_scan(c);
-        wx[it / 2] |= (inc - c) << (16 * (it & 1));
-        if (lane == kWave - 1) goff[it * kWaves + wave] = inc;
-      }
+      for (int e = 0; e < 4; ++e) c += (th.keff > 0 && i0 + e < nd && k4[e] >= thr) ? 1u : 0u;
+      const uint32_t inc = wave_inclusive_scan(c);
+      wx[it / 2] |= (inc - c) << (16 * (it & 1));
+      if (lane == kWave - 1) goff[it * kWaves + wave] = inc;
     }
     __syncthreads();
     if (wave == 0) {
@@ -804,28 +788,20 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
     }
     __syncthreads();
     carry = goff[kEnt];
-    // pass 2: the keys again (from L2), the candidates written in index order
+    // the candidates written in index order
 #pragma unroll
-    for (int bt = 0; bt < kDirectIters / kDirectBatch; ++bt) {
-      const int it0 = bt * kDirectBatch;
-      if (it0 >= nit) continue;   // uniform
-      uint4 kb[kDirectBatch];
-      load_batch(it0, kb);
+    for (int it = 0; it < kDirectIters; ++it) {
+      const int i0 = it * 4 * kSelectThreads + 4 * tid;
+      const uint32_t k4[4] = {kr[it].x, kr[it].y, kr[it].z, kr[it].w};
+      uint32_t o = goff[it * kWaves + wave] + ((wx[it / 2] >> (16 * (it & 1))) & 0xFFFFu);
 #pragma unroll
-      for (int j = 0; j < kDirectBatch; ++j) {
-        const int it = it0 + j;
-        const int i0 = it * 4 * kSelectThreads + 4 * tid;
-        const uint32_t k4[4] = {kb[j].x, kb[j].y, kb[j].z, kb[j].w};
-        uint32_t o = goff[it * kWaves + wave] + ((wx[it / 2] >> (16 * (it & 1))) & 0xFFFFu);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (th.keff > 0 && i0 + e < nd && k4[e] >= thr) {
-            if (o < kResolveCap) {
-              lkey[o] = k4[e];
-              lid[o] = (int32_t)(i0 + e);
-            }
-            ++o;
+      for (int e = 0; e < 4; ++e) {
+        if (th.keff > 0 && i0 + e < nd && k4[e] >= thr) {
+          if (o < kResolveCap) {
+            lkey[o] = k4[e];
+            lid[o] = (int32_t)(i0 + e);
           }
+          ++o;
         }
       }
     }
