@@ -1,8 +1,13 @@
 """Builds libcsa2.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python sparse_attention_fp4_e2m1_amd/build.py
+    python sparse_attention_fp4_e2m1_amd/build.py [--sanitize]
 
 (Run it as a script: importing the package loads the library it builds.)
+--sanitize builds _build/libcsa2_sanitize.so instead: the same sources with
+AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (the
+GPU code is built as usual), for the host-side validation and workspace
+sizing tests; load it with the ASan runtime preloaded and CSA2_LIBRARY set to
+its path (tests/test_sanitize_cpu.py does this).
 """
 from __future__ import annotations
 
@@ -42,9 +47,19 @@ def _hipcc() -> str:
 EXTRA_FLAGS = {"csa2_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+# Host-only sanitizers: each -fsanitize= goes to the host pass alone.
+SANITIZE_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                  "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZE_BUILD = os.path.join(BUILD, "sanitize")
+SANITIZE_LIB = os.path.join(BUILD, "libcsa2_sanitize.so")
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    out_dir = SANITIZE_BUILD if sanitize else BUILD
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    flags = HIPCC_FLAGS + (SANITIZE_FLAGS if sanitize else [])
+    cmd = [_hipcc(), *flags, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
            "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
@@ -56,21 +71,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, sanitize: bool = False) -> str:
     """Compiles every source and links the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(SANITIZE_BUILD if sanitize else BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    lib = SANITIZE_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
+    link_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"] \
+        if sanitize else []
+    cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *link_san, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv[1:])

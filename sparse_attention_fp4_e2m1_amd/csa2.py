@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+# CSA2_LIBRARY names another build of the library (the sanitizer build of the
+# host code); by default the in-tree libcsa2.so.
+LIB_PATH = os.environ.get("CSA2_LIBRARY") or os.path.join(_HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP, \
     CSA2_ERR_ARG = range(7)

@@ -1,11 +1,25 @@
 // C ABI of the CSA2 library: host-side validation, workspace sizing, dispatch.
 // Every check runs before anything is enqueued, so a rejected call leaves the
 // device untouched.
+#include <cstring>
+
 #include "csa2_internal.h"
 
 using namespace csa2;
 
 namespace {
+
+// The integer a caller passed for an enum parameter.  A C caller may pass any
+// int, and reading a value outside the enumerators' range through the C++
+// enum type is undefined, so the bits are copied out, unread as the enum, and
+// validated as an int.
+template <class E>
+int32_t raw_enum(const E &e) {
+  static_assert(sizeof(E) == sizeof(int32_t), "int-sized enum");
+  int32_t v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
 
 // Largest capacity: the kernels address a sequence's rows and index-key tiles
 // with 32-bit byte offsets (a tile of positions p is (p / T) * 64 * 64 * E
@@ -32,7 +46,7 @@ csa2_status check_local(const csa2_local_cache *c) {
   return CSA2_OK;
 }
 
-csa2_status check_topk_args(const csa2_cache *cache, csa2_mode mode, int32_t nq, int32_t top_k,
+csa2_status check_topk_args(const csa2_cache *cache, int32_t mode, int32_t nq, int32_t top_k,
                             int32_t pool_len, int32_t pool_blocks) {
   csa2_status st = check_cache(cache, mode != CSA2_REUSE);
   if (st != CSA2_OK) return st;
@@ -49,8 +63,8 @@ csa2_status check_topk_args(const csa2_cache *cache, csa2_mode mode, int32_t nq,
 
 extern "C" {
 
-const char *csa2_strerror(csa2_status s) {
-  switch (s) {
+const char *csa2_strerror(csa2_status status) {
+  switch (raw_enum(status)) {
     case CSA2_OK: return "ok";
     case CSA2_ERR_NULL: return "a required pointer is NULL";
     case CSA2_ERR_SHAPE: return "a size is out of range";
@@ -81,18 +95,21 @@ csa2_status csa2_kv_append(const csa2_cache *cache, const uint16_t *k, const uin
   return CSA2_OK;
 }
 
-size_t csa2_index_topk_workspace(const csa2_cache *cache, csa2_mode mode, int32_t nq,
+size_t csa2_index_topk_workspace(const csa2_cache *cache, csa2_mode mode_arg, int32_t nq,
                                  int32_t top_k, int32_t pool_len, int32_t pool_blocks) {
+  const int32_t mode = raw_enum(mode_arg);
   if (check_topk_args(cache, mode, nq, top_k, pool_len, pool_blocks) != CSA2_OK) return 0;
-  return topk_workspace_layout(*cache, mode, nq, pool_len, pool_blocks).total;
+  return topk_workspace_layout(*cache, static_cast<csa2_mode>(mode), nq, pool_len, pool_blocks).total;
 }
 
-csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode, const uint16_t *q_idx,
-                            csa2_dtype q_dtype, const int32_t *q_seq, const int32_t *q_pos,
+csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode_arg, const uint16_t *q_idx,
+                            csa2_dtype q_dtype_arg, const int32_t *q_seq, const int32_t *q_pos,
                             int32_t nq, int32_t top_k, const int32_t *pool_in, int32_t pool_len,
                             int32_t pool_blocks, int32_t *pool_out, const int32_t *reuse_src,
                             int32_t *topk_out, void *workspace, size_t workspace_bytes,
                             void *stream) {
+  const int32_t mode = raw_enum(mode_arg);
+  const int32_t q_dtype = raw_enum(q_dtype_arg);
   csa2_status st = check_topk_args(cache, mode, nq, top_k, pool_len, pool_blocks);
   if (st != CSA2_OK) return st;
   if (topk_out == nullptr) return CSA2_ERR_NULL;
@@ -114,7 +131,7 @@ csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode, const uint1
   if (nq == 0) return CSA2_OK;
   IndexArgs a;
   a.cache = cache;
-  a.mode = mode;
+  a.mode = static_cast<csa2_mode>(mode);
   a.q_idx = q_idx;
   a.q_fp8 = q_dtype == CSA2_FP8_E4M3;
   a.q_seq = q_seq;
@@ -127,7 +144,7 @@ csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode, const uint1
   a.pool_out = pool_out;
   a.reuse_src = reuse_src;
   a.topk_out = topk_out;
-  a.layout = topk_workspace_layout(*cache, mode, nq, pool_len, pool_blocks);
+  a.layout = topk_workspace_layout(*cache, a.mode, nq, pool_len, pool_blocks);
   if (a.layout.total > 0 && (workspace == nullptr || workspace_bytes < a.layout.total))
     return CSA2_ERR_WORKSPACE;
   a.ws = static_cast<uint8_t *>(workspace);
