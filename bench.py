@@ -597,6 +597,8 @@ def main():
         "step_hbm_gbps": res["step_hbm_gbps"], "step_hbm_frac": res["step_hbm_frac"],
         "roofline": res.get("roofline"),
     }
+    if "attention_roofline" in res:
+        line["attention_roofline"] = res["attention_roofline"]
     if not args.no_extra:
         line["extra"] = {}
         for name in ("decode_1m", "chain8_256k_b8", "prefill_4k_on_128k", "released_256k_b8",

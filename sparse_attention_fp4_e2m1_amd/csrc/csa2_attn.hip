@@ -297,14 +297,18 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
 // partial (O, max, sum) per split go to attn_combine_kernel.
 // Q fragment (B operand): head 16*wave + l16, channels 32g..32g+31, in fp16,
 // negated when the softmax scale is negative.
-__device__ __forceinline__ void load_q(const uint16_t *__restrict__ qg, int q, int n_heads,
-                                       int wave, int l16, int g, bool q_negate, f16x8 (&qf)[4]) {
+__device__ __forceinline__ void load_q_raw(const uint16_t *__restrict__ qg, int q, int n_heads,
+                                           int wave, int l16, int g, uint4 (&raw)[4]) {
   const uint16_t *qp = qg + ((int64_t)q * n_heads + wave * 16 + l16) * 128 + 32 * g;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const uint4 *>(qp + 8 * s);
+}
+
+__device__ __forceinline__ void convert_q(const uint4 (&raw)[4], bool q_negate, f16x8 (&qf)[4]) {
   const uint32_t flip = q_negate ? 0x80008000u : 0u;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const uint4 raw = *reinterpret_cast<const uint4 *>(qp + 8 * s);
-    const uint32_t w[4] = {raw.x ^ flip, raw.y ^ flip, raw.z ^ flip, raw.w ^ flip};
+    const uint32_t w[4] = {raw[s].x ^ flip, raw[s].y ^ flip, raw[s].z ^ flip, raw[s].w ^ flip};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const f16x2 h = __builtin_convertvector(
@@ -315,6 +319,13 @@ __device__ __forceinline__ void load_q(const uint16_t *__restrict__ qg, int q, i
   }
 }
 
+__device__ __forceinline__ void load_q(const uint16_t *__restrict__ qg, int q, int n_heads,
+                                       int wave, int l16, int g, bool q_negate, f16x8 (&qf)[4]) {
+  uint4 raw[4];
+  load_q_raw(qg, q, n_heads, wave, l16, g, raw);
+  convert_q(raw, q_negate, qf);
+}
+
 // Window rows [first, first + count) of a query at position p, whose window
 // holds nall = min(window, p + 1) rows (row r = position p - nall + 1 + r):
 // rows[i] = the slot of row first + i when the slot holds that position,
@@ -323,14 +334,22 @@ __device__ __forceinline__ int fill_window_rows(const int32_t *__restrict__ lpos
                                                 int window, int32_t p, int nall, int first,
                                                 int count, int32_t *rows, int tid, int nthreads) {
   const int nsub = (count + kSub - 1) / kSub;
-  for (int r = tid; r < nsub * kSub; r += nthreads) {
-    int32_t slot = -1;
-    if (r < count) {
+  // eight slot positions per thread per batch of loads, branch-free (a row
+  // past `count` reads slot 0 of the window and is dropped)
+  for (int r0 = 0; r0 < nsub * kSub; r0 += 8 * nthreads) {
+    int32_t have[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u * nthreads + tid;
       const int32_t pr = p - nall + 1 + first + r;
-      const int32_t sl = pr % window;
-      if (lpos[sbase + sl] == pr) slot = sl;
+      have[u] = lpos[sbase + (r < count ? pr % window : 0)];
     }
-    rows[r] = slot;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u * nthreads + tid;
+      const int32_t pr = p - nall + 1 + first + r;
+      if (r < nsub * kSub) rows[r] = (r < count && have[u] == pr) ? pr % window : -1;
+    }
   }
   return nsub;
 }
@@ -450,11 +469,29 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
   const int nrows = min(rows_per_split, top_k - row0);
   const int nsub = (nrows + kSub - 1) / kSub;
 
-  for (int r = tid; r < (nsub + 2) * kSub; r += kThreads)
-    rows[r] = r < nrows ? topk[(int64_t)q * top_k + row0 + r] : -1;
-
+  // the query's rows of Q first (their loads overlap the row list's)
+  uint4 qraw[4];
+  load_q_raw(qg, q, n_heads, wave, l16, g, qraw);
+  // the split's row list (and -1 for two sub-chunks past its end, which the
+  // look-ahead gathers read), eight entries per thread per batch of loads:
+  // branch-free (an index clamped into the split), so that a batch is in
+  // flight together
+  {
+    const int32_t *src = topk + (int64_t)q * top_k + row0;
+    const int nslots = (nsub + 2) * kSub;
+    for (int r0 = 0; r0 < nslots; r0 += 8 * kThreads) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[min(r0 + u * kThreads + tid, nrows - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = r0 + u * kThreads + tid;
+        if (r < nslots) rows[r] = r < nrows ? v[u] : -1;
+      }
+    }
+  }
   f16x8 qf[4];
-  load_q(qg, q, n_heads, wave, l16, g, q_negate, qf);
+  convert_q(qraw, q_negate, qf);
   __syncthreads();
 
   f32x4 o[8];
