@@ -55,12 +55,14 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFilterThreads = 1024;      // few, wide workgroups: each derives the threshold bin
-// Keys per filter wave (one candidate slot region): 512, or 1024 for key
-// arrays past kFilterSmallMax keys, so that the resolve's one round of early
-// slot reads covers every region (at most one region per resolve thread).
+// Keys per filter wave (one candidate slot region): 512 for key arrays up to
+// kFilterSmallMax keys, else 1024 -- half the filter workgroups, each of
+// which reads the query's histogram (up to 128 KB of chunk slots), and at
+// most 1024 regions for arrays up to 1M keys, so that the resolve's one round
+// of early slot reads covers every region (one region per resolve thread).
 constexpr int kFilterSubMin = 512;
 constexpr int kFilterSubMax = 1024;
-constexpr int64_t kFilterSmallMax = (int64_t)kFilterSubMin * 1024;
+constexpr int64_t kFilterSmallMax = 32768;
 constexpr int64_t kDirectMax = 32768;      // up to this many keys the resolve filters them itself
 constexpr int kSlotWords = kHistBins / 2;  // words of one chunk's packed histogram
 // Chunk histograms a selection adds up at most (every filter workgroup reads
