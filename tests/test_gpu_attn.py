@@ -102,3 +102,35 @@ def test_attention_deterministic():
     a = _run(gc, qd.q, topk)
     b = _run(gc, qd.q, topk)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("nq,top_k,heads", [(32, 2048, 64), (32, 1500, 64), (16, 1000, 48),
+                                            (256, 300, 16), (64, 2048, 32), (8, 2048, 64)])
+def test_attention_batch_shapes(nq, top_k, heads):
+    # Batch shapes whose splits hold several 64-row sub-chunks (an odd count:
+    # 1500 rows give 3 per split), one split per query (256 queries: the final
+    # output written directly, no combine) and 16 splits of two sub-chunks (8
+    # queries of 2048 rows).  Holes, an empty list, duplicates; determinism.
+    announce(f"attn batch shape nq={nq} k={top_k} heads={heads}")
+    m = lib()
+    wl, gc, oc = _setup(heads)
+    rng = np.random.default_rng(nq + top_k + heads)
+    q = synth.f32_to_bf16_bits(rng.standard_normal((nq, heads, 128)).astype(np.float32))
+    topk = rng.integers(0, 3000, (nq, top_k)).astype(np.int32)
+    topk[1, rng.random(top_k) < 0.3] = -1
+    topk[2] = -1
+    topk[3, : top_k // 2] = topk[3, 0]
+    q_seq = np.arange(nq) % gc.batch
+    out, lse = m.csa2_sparse_attn(gc, dev_u16(q), dev_i32(q_seq), dev_i32(topk))
+    torch.cuda.synchronize()
+    out, lse = host(out), host(lse)
+    check = list(range(min(nq, 8))) + [nq - 1]
+    for i in check:
+        ro, rl = O.sparse_attention(q[i], oc, int(q_seq[i]), topk[i])
+        rel, dl = attn_errors(out[i], lse[i], ro, rl)
+        assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL, (i, rel.max(), dl.max())
+    assert np.all(out[2] == 0.0) and np.all(np.isneginf(lse[2]))
+    # deterministic
+    out2, lse2 = m.csa2_sparse_attn(gc, dev_u16(q), dev_i32(q_seq), dev_i32(topk))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out2), out) and np.array_equal(host(lse2), lse)
