@@ -18,6 +18,18 @@
 //                    (written out per workgroup in one burst), histogram the
 //                    top 12 key bits, and for a pool-building Full layer the
 //                    8-position block maxima and their histogram.
+// Then the selection, in one of two forms:
+//   Ranked chunks (a Full layer without a pool, or a Reindex layer without
+//   one, over at most kMaxRankedChunks scorer chunks per query -- decode
+//   batches at up to 64K context): each scorer workgroup sorts its chunk's
+//   keys by 12-bit bin in LDS and stores them with their positions and the
+//   count of keys at or above every bin, so that
+//   ranked_select_kernel  one workgroup per query reads the threshold bin b1
+//                    off the counts (a 64-entry coarse table, then one
+//                    64-bin window), then only the keys at or above b1 (the
+//                    first entries of each chunk's list), and selects in LDS:
+//                    one launch instead of two, and no histogram to clear.
+//   Otherwise:
 //   filter_kernel    per wave and 512 or 1024 keys: keep every key whose top 12 bits
 //                    reach b1 -- the bin of the 12-bit histogram holding the
 //                    K-th largest key, which each workgroup reads off the
@@ -33,13 +45,9 @@
 //                    same filter and resolve launches (a second grid slice).
 //                    Key arrays of at most kDirectMax entries skip the
 //                    filter: the resolve reads them and compacts them itself.
-//                    The 12-bit histogram comes from the scorer's per-chunk
-//                    slots (a Full layer without a pool over at most
-//                    kMaxSlots chunks: each scorer workgroup stores its
-//                    chunk's histogram, nothing is cleared, and the filter
-//                    leaves the bits 19..8 pass to the resolve), from the
-//                    global histogram (a pool-building Full layer, long
-//                    contexts), or is counted by the resolve (a Reindex pool).
+//                    The 12-bit histogram comes from the global histogram (a
+//                    pool-building Full layer, long contexts), or is counted
+//                    by the resolve (a Reindex pool).
 // Small score chunks (one wave) count keys straight into the global histogram.
 //   copy_i32_kernel  Reuse mode: topk_out = reuse_src.
 // The selection helpers (select_bin, select_core, gather_regions) live in
@@ -57,17 +65,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kFilterThreads = 1024;      // few, wide workgroups: each derives the threshold bin
 // Keys per filter wave (one candidate slot region): 512 for key arrays up to
 // kFilterSmallMax keys, else 1024 -- half the filter workgroups, each of
-// which reads the query's histogram (up to 128 KB of chunk slots), and at
-// most 1024 regions for arrays up to 1M keys, so that the resolve's one round
-// of early slot reads covers every region (one region per resolve thread).
+// which reads the query's histogram copies, and at most 1024 regions for
+// arrays up to 1M keys, so that the resolve's one round of early slot reads
+// covers every region (one region per resolve thread).
 constexpr int kFilterSubMin = 512;
 constexpr int kFilterSubMax = 1024;
 constexpr int64_t kFilterSmallMax = 32768;
 constexpr int64_t kDirectMax = 32768;      // up to this many keys the resolve filters them itself
-constexpr int kSlotWords = kHistBins / 2;  // words of one chunk's packed histogram
-// Chunk histograms a selection adds up at most (every filter workgroup reads
-// them all); past this the scorer adds into the global histogram instead.
-constexpr int64_t kMaxSlots = 16;
+// Ranked chunks (kRanked): at most this many scorer chunks per query (one
+// selection wave each), chunks of at least 2048 keys.
+constexpr int64_t kMaxRankedChunks = 16;
 constexpr int kEarlySlots = 8;             // candidate slots per resolve thread read before the counts
 // Keys in the threshold bin beyond which the filter leaves the bits 19..8 pass
 // to the resolve (heavy ties would serialize the global atomics).
@@ -277,7 +284,18 @@ struct ScoreCtx {
   }
 };
 
-template <int H, bool kFp8Keys, bool kPool, int kThreads, int kChunk>
+// Ranked chunk records (kRanked), written by the scorer's workgroup of chunk
+// c of query q: keys[q][c*chunk + i] (the keys array) and pos[q][c*chunk + i]
+// for i < the chunk's key count, ordered by 12-bit bin from the highest (in
+// no particular order inside a bin); ge[q][c][b] = the chunk's keys in bin b
+// or above; coarse[q][c][j] = ge[q][c][64 j].
+struct RankedOut {
+  uint16_t *pos;
+  uint16_t *ge;
+  uint16_t *coarse;
+};
+
+template <int H, bool kFp8Keys, bool kPool, int kThreads, int kChunk, bool kRanked = false>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kThreads == 64 ? 2 : (kFp8Keys ? CSA2_SCORE_WAVES : CSA2_SCORE_WAVES - 1))))
 score_kernel(
@@ -285,9 +303,10 @@ score_kernel(
     int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
     uint32_t *__restrict__ keys_tok, int64_t tok_stride, uint32_t *__restrict__ hist_tok,
     uint32_t *__restrict__ keys_blk, int64_t blk_stride, uint32_t *__restrict__ hist_blk,
-    int64_t hstride, int32_t hcopies, uint32_t *__restrict__ hist_slots) {
-  // hist_slots != nullptr: store this chunk's packed histogram in slot
-  // (q, blockIdx.x) instead of adding it into the global histogram
+    int64_t hstride, int32_t hcopies, RankedOut rk) {
+  // kRanked: the chunk's record goes to rk (and the keys array, in bin order)
+  // instead of adding its histogram into the global one
+  static_assert(!kRanked || (!kPool && kThreads * 16 == kHistBins), "ranked chunks: 16 bins per thread");
   constexpr int kEsz = kFp8Keys ? 1 : 2;
   constexpr int TPI = kWave / H;
   constexpr int kBpt = H * 64 * kEsz;     // bytes per token
@@ -300,10 +319,13 @@ score_kernel(
   // LDS: 16-bit histogram bins packed in pairs, the chunk's keys (written out
   // in one burst at the end: small stores interleaved with the read stream
   // cost HBM efficiency), block maxima, the index query.
-  __shared__ uint32_t lds_main[kMainWords];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_main[kMainWords];
   __shared__ uint32_t histb[kPool ? kHistBins / 2 : 1];
   __shared__ uint32_t sblk[kPool ? kChunk / kPoolBlock : 1];
   __shared__ float qlds[H * 64];
+  __shared__ __attribute__((aligned(16))) uint32_t rsk[kRanked ? kChunk : 1];   // the chunk's keys in bin order
+  __shared__ __attribute__((aligned(16))) uint16_t rsp[kRanked ? kChunk : 1];   // and their chunk-local positions
+  __shared__ uint32_t rscr[kThreads / kWave + 1];
   uint32_t *hist = lds_main;
   uint32_t *skeys = lds_main + kHistBins / 2;
 
@@ -368,8 +390,78 @@ score_kernel(
   }
   __syncthreads();
 
-  // the chunk's keys and block maxima in one burst of coalesced stores
   const int64_t cnt = t_end - t_begin;
+  if constexpr (kRanked) {
+    // Thread t owns bins 16t .. 16t+15 (LDS words 8t .. 8t+7).  ge of a bin =
+    // keys in the bins of higher threads + the thread's own bins from that
+    // one up; the bin's keys start at ge - count in the bin-ordered list.
+    const int tid = threadIdx.x;
+    const uint4 wa = reinterpret_cast<const uint4 *>(hist)[2 * tid];
+    const uint4 wb = reinterpret_cast<const uint4 *>(hist)[2 * tid + 1];
+    const uint32_t w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+    uint32_t c[16], ge[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      c[2 * k] = w[k] & 0xFFFFu;
+      c[2 * k + 1] = w[k] >> 16;
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int b = 15; b >= 0; --b) {
+      s += c[b];
+      ge[b] = s;
+    }
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan(s, rscr, total);
+    const uint32_t higher = total - before - s;   // keys in the bins of higher threads
+    uint32_t g[8], cur[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t lo = ge[2 * k] + higher, hi = ge[2 * k + 1] + higher;
+      g[k] = lo | (hi << 16);
+      cur[k] = (lo - c[2 * k]) | ((hi - c[2 * k + 1]) << 16);
+    }
+    // every thread has read its words: they become the bins' insertion cursors
+    reinterpret_cast<uint4 *>(hist)[2 * tid] = make_uint4(cur[0], cur[1], cur[2], cur[3]);
+    reinterpret_cast<uint4 *>(hist)[2 * tid + 1] = make_uint4(cur[4], cur[5], cur[6], cur[7]);
+    __syncthreads();
+    // a fixed trip count with the tail masked (an atomic adding 0), so that a
+    // thread's atomics issue back to back
+#pragma unroll
+    for (int u = 0; u < kChunk / kThreads; ++u) {
+      const int i = tid + u * kThreads;
+      const bool v = i < (int)cnt;
+      const uint32_t key = skeys[i];
+      const uint32_t sh = (key >> 16) & 16u;
+      const uint32_t slot = (atomicAdd(&hist[key >> 21], v ? 1u << sh : 0u) >> sh) & 0xFFFFu;
+      if (v) {
+        rsk[slot] = key;
+        rsp[slot] = (uint16_t)i;
+      }
+    }
+    __syncthreads();
+    // the global stores last: a barrier waits for a thread's stores to land
+    const int64_t rec = (int64_t)q * gridDim.x + blockIdx.x;
+    uint4 *gq = reinterpret_cast<uint4 *>(rk.ge + rec * kHistBins);
+    gq[2 * tid] = make_uint4(g[0], g[1], g[2], g[3]);
+    gq[2 * tid + 1] = make_uint4(g[4], g[5], g[6], g[7]);
+    if ((tid & 3) == 0) rk.coarse[rec * (kHistBins / 64) + tid / 4] = (uint16_t)(g[0] & 0xFFFFu);
+    uint32_t *dk = keys_tok + (int64_t)q * tok_stride + t_begin;
+    uint16_t *dp = rk.pos + (int64_t)q * tok_stride + t_begin;
+    for (int i = 4 * tid; i < (int)cnt; i += 4 * kThreads) {
+      if (i + 4 <= (int)cnt) {
+        *reinterpret_cast<uint4 *>(dk + i) = *reinterpret_cast<const uint4 *>(rsk + i);
+        *reinterpret_cast<uint2 *>(dp + i) = *reinterpret_cast<const uint2 *>(rsp + i);
+      } else {
+        for (int e = i; e < (int)cnt; ++e) {
+          dk[e] = rsk[e];
+          dp[e] = rsp[e];
+        }
+      }
+    }
+    return;
+  }
+  // the chunk's keys and block maxima in one burst of coalesced stores
   {
     uint32_t *dst = keys_tok + (int64_t)q * tok_stride + t_begin;
     for (int64_t i = threadIdx.x; i < cnt; i += kThreads) dst[i] = skeys[i];
@@ -380,12 +472,6 @@ score_kernel(
     }
   }
   if (Ctx::kDirectHist) return;
-  if (!kPool && hist_slots != nullptr) {   // uniform
-    uint4 *dst = reinterpret_cast<uint4 *>(hist_slots + ((int64_t)q * gridDim.x + blockIdx.x) * kSlotWords);
-    for (int i = threadIdx.x; i < kSlotWords / 4; i += kThreads)
-      dst[i] = reinterpret_cast<const uint4 *>(hist)[i];
-    return;
-  }
   uint32_t *hbq = kPool ? hist_blk + hoff : nullptr;
   for (int i = threadIdx.x; i < kHistBins / 2; i += kThreads) {
     const uint32_t w = hist[i];
@@ -524,45 +610,12 @@ struct SelProblem {
   int32_t mode;           // OutMode
   int32_t direct;         // short arrays: no filter pass, the resolve reads the keys
   int32_t region;         // keys per filter wave: kFilterSubMin or kFilterSubMax
-  int32_t hsrc;           // HistSource of a direct array
-  const uint32_t *slots;  // [nq][nslots][kSlotWords] (kHistSlots)
-  int32_t nslots;
-  int32_t slot_chunk;     // keys per slot
+  int32_t hsrc;           // HistSource of a direct array (kHistKeys or kHistGlobal)
 };
 
 struct SelProblems {
   SelProblem p[2];
 };
-
-// The 12-bit histogram of one query from the scorer's chunk slots (kHistSlots)
-// into LDS: the slots of the chunks that hold visible keys, added up (every
-// such slot was written by this call).  Thread t adds bins 4t .. 4t+3 (words
-// 2t, 2t+1 of every slot), loading 16 slots at a time with no branch around
-// the loads.  A block of kSlotWords / 2 threads; ends with a barrier.
-static_assert(kSlotWords / 2 == kSelectThreads && kSlotWords / 2 == kFilterThreads,
-              "one word pair of every slot per thread");
-__device__ __forceinline__ void slot_hist_to_lds(const SelProblem &A, int q, int64_t n,
-                                                 uint32_t *lh) {
-  const int tid = threadIdx.x;
-  const int nsl = (int)((n + A.slot_chunk - 1) / A.slot_chunk);
-  const uint2 *sq = reinterpret_cast<const uint2 *>(A.slots + (int64_t)q * A.nslots * kSlotWords) + tid;
-  uint32_t b0 = 0u, b1 = 0u, b2 = 0u, b3 = 0u;
-  for (int s0 = 0; s0 < nsl; s0 += 16) {
-    uint2 v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = sq[(int64_t)min(s0 + u, nsl - 1) * (kSlotWords / 2)];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const bool in = s0 + u < nsl;
-      b0 += in ? (v[u].x & 0xFFFFu) : 0u;
-      b1 += in ? (v[u].x >> 16) : 0u;
-      b2 += in ? (v[u].y & 0xFFFFu) : 0u;
-      b3 += in ? (v[u].y >> 16) : 0u;
-    }
-  }
-  reinterpret_cast<uint4 *>(lh)[tid] = make_uint4(b0, b1, b2, b3);
-  __syncthreads();
-}
 
 // grid (filter groups, nq, problems).  Each wave takes A.region keys and
 // keeps every key whose top 12 bits reach bin b1, with its index, in index
@@ -602,16 +655,10 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(
     kv[k][3] = v.w;
   }
   uint32_t *hs = A.hist + (int64_t)q * A.hstride;
-  Threshold th;
-  if (A.hsrc == kHistSlots) {   // uniform
-    slot_hist_to_lds(A, q, n, lh);
-    th = lds_threshold(n, A.kk, lh, scratch, res);
-  } else {
-    th = hist_threshold(hs, A.hcopies, n, A.kk, lh, scratch, res);
-  }
+  const Threshold th = hist_threshold(hs, A.hcopies, n, A.kk, lh, scratch, res);
   // the second histogram (bits 19..8 of the threshold bin's keys) is added
-  // into global memory: only where the call clears its histograms
-  const bool use_h2 = A.hsrc == kHistGlobal && th.keff > 0u && lh[th.b1] <= kH2MaxKeys;
+  // into global memory (cleared with the first)
+  const bool use_h2 = th.keff > 0u && lh[th.b1] <= kH2MaxKeys;
   if (blockIdx.x == 0 && threadIdx.x == 0)
     *reinterpret_cast<uint4 *>(hs + state_off(A.hcopies)) =
         make_uint4(th.keff, th.b1, th.above, use_h2 ? 1u : 0u);
@@ -699,10 +746,7 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
   const uint32_t *hs = A.hist + (int64_t)q * A.hstride;
   Threshold th;
   Pass19 p19{false, 0u, 0u};
-  if (A.direct && A.hsrc == kHistSlots) {
-    slot_hist_to_lds(A, q, n, hist);
-    th = lds_threshold(n, A.kk, hist, scratch, res);
-  } else if (A.direct && A.hsrc == kHistGlobal) {
+  if (A.direct && A.hsrc == kHistGlobal) {
     th = hist_threshold(hs, A.hcopies, n, A.kk, hist, scratch, res);
   } else if (A.direct) {
     // the 12-bit histogram of the short key array, built here in LDS (the
@@ -830,6 +874,284 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// ranked_select_kernel: the Top-K of one query from its ranked chunk records
+// (kRanked).  grid (nq), kRankThreads threads; wave w takes chunk w.
+//   1. the coarse tables: per 64-bin group j, the keys at or above bin 64 j
+//      summed over the chunks; the keff-th largest key lies in the last group
+//      J whose sum reaches keff (the sums fall with j).
+//   2. ge of the 64 bins of group J in every chunk: likewise the bin b1.  Per
+//      chunk, its first ge(b1 + 1) keys lie above bin b1 and are all taken,
+//      the next ge(b1) - ge(b1 + 1) are bin b1's.
+//   3. those keys: the ones above b1 set their positions in the selection
+//      bitmap, bin b1's go to LDS.  Radix passes on bits 19..8 and 7..0 of
+//      bin b1's keys give the keff-th largest key tau; keys above tau are
+//      taken, and of the keys equal to tau the ones at the lowest positions
+//      (a tie bitmap, scanned in position order).
+// The bitmap, scanned in order, gives the positions ascending; -1 padding.
+// The first kRankEarly keys of every chunk are read with the coarse tables,
+// before anything says how many are needed (usually all that are); bin b1
+// holding more keys than LDS takes (heavy ties) is read from the records
+// again in each pass.
+// ---------------------------------------------------------------------------
+constexpr int kRankThreads = 1024;
+constexpr int kRankWaves = kRankThreads / kWave;
+constexpr int kRankCap = 8192;                       // bin-b1 keys held in LDS
+constexpr int kRankMaxKeys = (int)kMaxRankedChunks * 4096;
+constexpr int kRankWords = kRankMaxKeys / 32;        // selection bitmap words
+constexpr int kRankEarly = kRankThreads * 4 / (int)kMaxRankedChunks;   // keys per chunk read early
+static_assert(kRankWaves == kMaxRankedChunks, "one wave per chunk");
+static_assert(kRankWords == 2 * kRankThreads, "two bitmap words per thread");
+
+struct RankedSel {
+  const uint32_t *keys;     // [nq][n_stride] each chunk's keys in bin order
+  const uint16_t *pos;      // [nq][n_stride] their chunk-local positions
+  const uint16_t *ge;       // [nq][nchunks][kHistBins]
+  const uint16_t *coarse;   // [nq][nchunks][kHistBins / 64]
+  int64_t n_stride;
+  int32_t nchunks;
+  int32_t chunk;
+  int32_t *out;             // [nq][kk]
+  int32_t kk;
+};
+
+// The query's taken keys as one list: first every chunk's keys above bin b1,
+// then every chunk's bin-b1 keys.  Per chunk (LDS tables): lo = its keys above
+// b1, hi = lo + its bin-b1 keys, aoff / boff = where its part of each half
+// starts.  Entry g of the bin-b1 half lies in the last chunk whose boff
+// reaches g (chunks without such keys share the next one's offset).
+struct RankedTabs {
+  const uint32_t *lo, *hi, *boff;
+  int chunk;
+  __device__ __forceinline__ int64_t bin_index(uint32_t g) const {
+    int c = 0;
+#pragma unroll
+    for (int k = 1; k < (int)kMaxRankedChunks; ++k) c += boff[k] <= g ? 1 : 0;
+    return (int64_t)c * chunk + lo[c] + (g - boff[c]);
+  }
+};
+
+__device__ __forceinline__ void set_bit(uint32_t *bm, uint32_t p) {
+  atomicOr(&bm[p >> 5], 1u << (p & 31u));
+}
+
+// The passes over bin b1's keys: the key and position of its entry g.
+struct RankedBinLds {
+  const uint32_t *k;
+  const uint16_t *p;
+  __device__ __forceinline__ uint32_t key(uint32_t g) const { return k[g]; }
+  __device__ __forceinline__ uint32_t pos(uint32_t g) const { return p[g]; }
+};
+struct RankedBinGlobal {
+  const uint32_t *k;   // the query's keys row
+  const uint16_t *p;   // the query's positions row
+  RankedTabs t;
+  __device__ __forceinline__ uint32_t key(uint32_t g) const { return k[t.bin_index(g)]; }
+  __device__ __forceinline__ uint32_t pos(uint32_t g) const {
+    const int64_t r = t.bin_index(g);
+    return (uint32_t)(r / t.chunk * t.chunk) + p[r];
+  }
+};
+
+// tau among bin b1's T keys (need = how many of them are taken), then the
+// selection bits of the ones taken.  All threads; barriers.
+template <class Bin>
+__device__ void ranked_refine(const Bin &bin, uint32_t T, uint32_t b1, uint32_t need,
+                              uint32_t *hist, uint32_t *sel, uint32_t *tie, int nwords,
+                              uint32_t *scratch, uint32_t *res) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kHistBins; i += kRankThreads) hist[i] = 0u;
+  __syncthreads();
+  for (uint32_t g = tid; g < T; g += kRankThreads) atomicAdd(&hist[(bin.key(g) >> 8) & 0xFFFu], 1u);
+  __syncthreads();
+  select_bin(hist, kHistBins, need, scratch, res);
+  const uint32_t pre24 = (b1 << 12) | res[0];
+  const uint32_t need2 = need - res[1];
+  __syncthreads();   // res read
+  for (int i = tid; i < 256; i += kRankThreads) hist[i] = 0u;
+  __syncthreads();
+  for (uint32_t g = tid; g < T; g += kRankThreads) {
+    const uint32_t k = bin.key(g);
+    if ((k >> 8) == pre24) atomicAdd(&hist[k & 0xFFu], 1u);
+  }
+  __syncthreads();
+  select_bin(hist, 256, need2, scratch, res);
+  const uint32_t tau = (pre24 << 8) | res[0];
+  const uint32_t ties_wanted = need2 - res[1];
+  const bool all_ties = ties_wanted == hist[res[0]];   // uniform
+  for (uint32_t g = tid; g < T; g += kRankThreads) {
+    const uint32_t k = bin.key(g);
+    if (k > tau || (all_ties && k == tau)) set_bit(sel, bin.pos(g));
+    else if (k == tau) set_bit(tie, bin.pos(g));
+  }
+  __syncthreads();
+  if (all_ties) return;
+  // the ties_wanted ties at the lowest positions: thread t holds words 2t, 2t+1
+  const int w0 = 2 * tid;
+  const uint32_t t0 = w0 < nwords ? tie[w0] : 0u;
+  const uint32_t t1 = w0 + 1 < nwords ? tie[w0 + 1] : 0u;
+  uint32_t total;
+  uint32_t rank = block_exclusive_scan((uint32_t)(__popc(t0) + __popc(t1)), scratch, total);
+  uint32_t m[2] = {t0, t1};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    uint32_t take = 0u;
+    while (m[e] != 0u && rank < ties_wanted) {
+      const uint32_t b = m[e] & (0u - m[e]);
+      take |= b;
+      m[e] ^= b;
+      ++rank;
+    }
+    if (take) sel[w0 + e] |= take;
+  }
+  __syncthreads();
+}
+
+// One taken key (entry i of chunk c's record, a key of the query's list):
+// above b1 -> its selection bit; in bin b1 -> LDS slot boff + i - lo.
+__device__ __forceinline__ void ranked_take(uint32_t i, int c, int C, uint32_t key, uint32_t pos,
+                                            const uint32_t *lo, const uint32_t *hi,
+                                            const uint32_t *boff, bool in_lds, uint32_t *sel,
+                                            uint32_t *bkey, uint16_t *bpos) {
+  if (i < lo[c]) {
+    set_bit(sel, (uint32_t)(c * C) + pos);
+  } else if (i < hi[c] && in_lds) {
+    const uint32_t g = boff[c] + i - lo[c];
+    bkey[g] = key;
+    bpos[g] = (uint16_t)((uint32_t)(c * C) + pos);
+  }
+}
+
+__global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
+    const RankedSel R, const int32_t *__restrict__ q_pos) {
+  __shared__ uint32_t tabc[kMaxRankedChunks][65];   // coarse tables (padded rows)
+  __shared__ uint32_t tabf[kMaxRankedChunks][65];   // the 64-bin window of group J
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
+  __shared__ uint32_t sel[kRankWords];
+  __shared__ uint32_t tie[kRankWords];
+  __shared__ uint32_t bkey[kRankCap];
+  __shared__ uint16_t bpos[kRankCap];
+  __shared__ uint32_t tlo[kMaxRankedChunks], thi[kMaxRankedChunks], tboff[kMaxRankedChunks];
+  __shared__ uint32_t scratch[kRankWaves + 1];
+  __shared__ uint32_t res[4];
+
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int C = R.chunk;
+  const int64_t rec = (int64_t)q * R.nchunks;
+  const uint32_t *kq = R.keys + (int64_t)q * R.n_stride;
+  const uint16_t *pq = R.pos + (int64_t)q * R.n_stride;
+  // round 1, all independent of q_pos: the coarse tables (chunks past the
+  // query's are masked below) and the first kRankEarly keys of every chunk
+  // (thread t: entry t % kRankEarly of chunks t / kRankEarly + 4u), addresses
+  // clamped into the query's rows
+  const uint32_t cv = R.coarse[(rec + min(wave, R.nchunks - 1)) * (kHistBins / 64) + lane];
+  constexpr int kPer = kRankThreads / kRankEarly;   // chunks per early round: 4
+  const uint32_t ei = (uint32_t)(tid % kRankEarly);
+  uint32_t ek[4], ep[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t r = min((int64_t)(tid / kRankEarly + kPer * u) * C + ei, R.n_stride - 1);
+    ek[u] = kq[r];
+    ep[u] = pq[r];
+  }
+  const int32_t qp = q_pos[q];
+  sel[2 * tid] = 0u;
+  sel[2 * tid + 1] = 0u;
+  tie[2 * tid] = 0u;
+  tie[2 * tid + 1] = 0u;
+  // visible keys (q_pos < capacity; clamped to the records regardless)
+  const int64_t n = max((int64_t)1, min((int64_t)qp + 1, (int64_t)R.nchunks * C));
+  const int nch = (int)((n + C - 1) / C);
+  const uint32_t keff = (uint32_t)min((int64_t)R.kk, n);
+  const int nwords = (int)((n + 31) / 32);
+  int32_t *oq = R.out + (int64_t)q * R.kk;
+  tabc[wave][lane] = wave < nch ? cv : 0u;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t t = 0u;
+#pragma unroll
+    for (int w = 0; w < (int)kMaxRankedChunks; ++w) t += tabc[w][lane];
+    const uint64_t b = __ballot(t >= keff);   // lane 0: t = n >= keff
+    if (lane == 0) res[0] = (uint32_t)__popcll(b) - 1u;
+  }
+  __syncthreads();
+  const uint32_t J = res[0];
+  // round 2
+  const uint32_t fv = R.ge[(rec + min(wave, nch - 1)) * kHistBins + 64 * J + lane];
+  tabf[wave][lane] = wave < nch ? fv : 0u;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t t = 0u;
+#pragma unroll
+    for (int w = 0; w < (int)kMaxRankedChunks; ++w) t += tabf[w][lane];
+    const uint32_t L = (uint32_t)__popcll(__ballot(t >= keff)) - 1u;
+    // lanes 0..15: chunk `lane`'s keys in bin b1 or above (hi) and above it (lo)
+    const int c = lane & ((int)kMaxRankedChunks - 1);
+    const uint32_t hi = tabf[c][L];
+    const uint32_t lo = L < 63u ? tabf[c][L + 1] : (J < 63u ? tabc[c][J + 1] : 0u);
+    const bool mine = lane < (int)kMaxRankedChunks;
+    const uint32_t a = mine ? lo : 0u, bb = mine ? hi - lo : 0u;
+    const uint32_t ia = wave_inclusive_scan(a);
+    const uint32_t ib = wave_inclusive_scan(bb);
+    if (mine) {
+      tlo[c] = lo;
+      thi[c] = hi;
+      tboff[c] = ib - bb;
+    }
+    const bool more = __ballot(mine && hi > (uint32_t)kRankEarly) != 0ull;
+    if (lane == kWave - 1) {
+      res[0] = 64u * J + L;
+      res[1] = ia;   // keys above bin b1
+      res[2] = ib;   // keys in bin b1
+      res[3] = more ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t b1 = res[0], above = res[1], T = res[2];
+  const bool more = res[3] != 0u;   // some chunk needs keys past the early ones
+  const bool in_lds = T <= (uint32_t)kRankCap;   // uniform
+  // round 3: the early keys, then any a chunk needs beyond them
+  if (keff > 0u) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid / kRankEarly + kPer * u;
+      if (c < nch) ranked_take(ei, c, C, ek[u], ep[u], tlo, thi, tboff, in_lds, sel, bkey, bpos);
+    }
+    for (int c = 0; more && c < nch; ++c) {
+      const uint32_t h = thi[c];   // uniform
+      for (uint32_t i = kRankEarly + tid; i < h; i += kRankThreads) {
+        const int64_t r = (int64_t)c * C + i;
+        ranked_take(i, c, C, kq[r], pq[r], tlo, thi, tboff, in_lds, sel, bkey, bpos);
+      }
+    }
+    __syncthreads();
+    const uint32_t need = keff - above;   // >= 1: the keff-th key lies in bin b1
+    if (in_lds)
+      ranked_refine(RankedBinLds{bkey, bpos}, T, b1, need, hist, sel, tie, nwords, scratch, res);
+    else
+      ranked_refine(RankedBinGlobal{kq, pq, RankedTabs{tlo, thi, tboff, C}}, T, b1, need, hist,
+                    sel, tie, nwords, scratch, res);
+  }
+  // the selection in position order: thread t emits positions 64t .. 64t+63
+  const int w0 = 2 * tid;
+  uint32_t m[2] = {w0 < nwords ? sel[w0] : 0u, w0 + 1 < nwords ? sel[w0 + 1] : 0u};
+  uint32_t total;
+  uint32_t o = block_exclusive_scan((uint32_t)(__popc(m[0]) + __popc(m[1])), scratch, total);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    while (m[e] != 0u) {
+      const int b = __ffs(m[e]) - 1;
+      m[e] &= m[e] - 1u;
+      if (o < keff) oq[o] = 32 * (w0 + e) + b;
+      ++o;
+    }
+  }
+  for (int64_t i = (int64_t)keff + tid; i < R.kk; i += kRankThreads) oq[i] = -1;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <int H, bool kFp8, bool kPool, int kThreads, int kChunk>
@@ -837,18 +1159,28 @@ void launch_score_shape(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
   const csa2_cache &c = *a.cache;
   const TopkWorkspace &L = a.layout;
   dim3 grid((unsigned)((n_cand_max + kChunk - 1) / kChunk), (unsigned)a.nq);
-  uint32_t *slots = nullptr;
-  if (L.tok.hsrc == kHistSlots) {
-    slots = reinterpret_cast<uint32_t *>(a.ws + L.tok.slots);
-    if (L.tok.slot_chunk != kChunk || (int64_t)L.tok.nslots != (int64_t)grid.x) return;   // never: same rule
+  uint32_t *keys = reinterpret_cast<uint32_t *>(a.ws + L.tok.keys);
+  if (L.tok.hsrc == kRanked) {
+    // the layout chose ranked chunks by the same shape rule (score_chunk)
+    if constexpr (!kPool && kThreads == 256) {
+      if (L.tok.chunk != kChunk || (int64_t)L.tok.nchunks != (int64_t)grid.x) return;   // never
+      const RankedOut rk{reinterpret_cast<uint16_t *>(a.ws + L.tok.rk_pos),
+                         reinterpret_cast<uint16_t *>(a.ws + L.tok.rk_ge),
+                         reinterpret_cast<uint16_t *>(a.ws + L.tok.rk_coarse)};
+      hipLaunchKernelGGL((score_kernel<H, kFp8, false, kThreads, kChunk, true>), grid, dim3(kThreads),
+                         0, s, static_cast<const uint8_t *>(c.idx_k), (int64_t)c.capacity, a.q_idx,
+                         a.q_fp8, a.q_seq, a.q_pos, keys, L.tok.n, nullptr, nullptr, (int64_t)0,
+                         nullptr, (int64_t)0, 1, rk);
+    }
+    return;
   }
   hipLaunchKernelGGL((score_kernel<H, kFp8, kPool, kThreads, kChunk>), grid, dim3(kThreads), 0, s,
                      static_cast<const uint8_t *>(c.idx_k), (int64_t)c.capacity, a.q_idx, a.q_fp8,
-                     a.q_seq, a.q_pos, reinterpret_cast<uint32_t *>(a.ws + L.tok.keys), L.tok.n,
+                     a.q_seq, a.q_pos, keys, L.tok.n,
                      reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
                      kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.keys) : nullptr, L.blk.n,
                      kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr,
-                     L.tok.hstride, L.tok.hcopies, slots);
+                     L.tok.hstride, L.tok.hcopies, RankedOut{nullptr, nullptr, nullptr});
 }
 
 // Workgroup shape from the amount of work: long streams when there are enough
@@ -912,9 +1244,6 @@ SelProblem sel_problem(const IndexArgs &a, const SelectArrays &A, int32_t kk, in
   p.direct = A.n <= kDirectMax;
   p.region = A.region;
   p.hsrc = A.hsrc;
-  p.slots = reinterpret_cast<const uint32_t *>(w + A.slots);
-  p.nslots = A.nslots;
-  p.slot_chunk = A.slot_chunk;
   return p;
 }
 
@@ -968,6 +1297,25 @@ size_t carve(SelectArrays &A, int64_t n_slots, int32_t nq, size_t off, int32_t h
   return off;
 }
 
+// Ranked chunks: the keys (in bin order per chunk), their positions, the
+// per-bin counts and their coarse tables; no histogram or filter arrays.
+size_t carve_ranked(SelectArrays &A, int64_t n_slots, int32_t nq, int32_t chunk) {
+  A.n = (n_slots + 63) / 64 * 64;
+  A.hsrc = kRanked;
+  A.chunk = chunk;
+  A.nchunks = (int32_t)((n_slots + chunk - 1) / chunk);
+  size_t off = 0;
+  A.keys = off;
+  off = align256(off + (size_t)nq * A.n * 4);
+  A.rk_pos = off;
+  off = align256(off + (size_t)nq * A.n * 2);
+  A.rk_ge = off;
+  off = align256(off + (size_t)nq * A.nchunks * kHistBins * 2);
+  A.rk_coarse = off;
+  off = align256(off + (size_t)nq * A.nchunks * (kHistBins / 64) * 2);
+  return off;
+}
+
 }  // namespace
 
 void set_index_scan_events(hipEvent_t before, hipEvent_t after) {
@@ -981,25 +1329,21 @@ TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t
   if (mode == CSA2_REUSE) return w;
   const bool reindex_pool = mode == CSA2_REINDEX && pool_len > 0;
   const bool pool = mode == CSA2_FULL && pool_blocks > 0;
-  // the token and block histograms are filled by the same scorer launch and
-  // cleared by one launch: the same number of copies
   const int64_t n_tok = reindex_pool ? (int64_t)pool_len : (int64_t)c.capacity;
-  const int32_t hc = hist_copies(n_tok);
-  size_t off = carve(w.tok, n_tok, nq, 0, hc);
-  if (pool) off = carve(w.blk, ((int64_t)c.capacity + kPoolBlock - 1) / kPoolBlock, nq, off, hc);
-  // where each selection finds its histogram (see HistSource)
-  w.tok.hsrc = reindex_pool ? (pool_len <= kDirectMax ? kHistKeys : kHistGlobal) : kHistGlobal;
-  w.blk.hsrc = kHistGlobal;
-  if (!reindex_pool && !pool) {
-    const int32_t chunk = score_chunk(nq, n_tok, false);
-    const int64_t nslots = (n_tok + chunk - 1) / chunk;
-    if (chunk >= 2048 && nslots <= kMaxSlots) {   // a handful of chunks per query: one slot each
-      w.tok.hsrc = kHistSlots;
-      w.tok.slot_chunk = chunk;
-      w.tok.nslots = (int32_t)nslots;
-      w.tok.slots = off;
-      off = align256(off + (size_t)nq * w.tok.nslots * kSlotWords * 4);
-    }
+  size_t off;
+  const int32_t chunk = score_chunk(nq, n_tok, false);
+  if (!reindex_pool && !pool && chunk >= 2048 && (n_tok + chunk - 1) / chunk <= kMaxRankedChunks) {
+    // a handful of scorer chunks per query: ranked chunk records
+    off = carve_ranked(w.tok, n_tok, nq, chunk);
+  } else {
+    // the token and block histograms are filled by the same scorer launch and
+    // cleared by one launch: the same number of copies
+    const int32_t hc = hist_copies(n_tok);
+    off = carve(w.tok, n_tok, nq, 0, hc);
+    if (pool) off = carve(w.blk, ((int64_t)c.capacity + kPoolBlock - 1) / kPoolBlock, nq, off, hc);
+    // where each selection finds its histogram (see HistSource)
+    w.tok.hsrc = reindex_pool ? (pool_len <= kDirectMax ? kHistKeys : kHistGlobal) : kHistGlobal;
+    w.blk.hsrc = kHistGlobal;
   }
   w.total = off;
   if (gemm_eligible(c, mode, pool_len, pool_blocks)) {
@@ -1046,6 +1390,16 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
   }
   if (g_scan_after != nullptr) (void)hipEventRecord(g_scan_after, s);
   // 3. selection: the Top-K, and the pool blocks in the same launches
+  if (L.tok.hsrc == kRanked) {
+    const RankedSel R{reinterpret_cast<const uint32_t *>(a.ws + L.tok.keys),
+                      reinterpret_cast<const uint16_t *>(a.ws + L.tok.rk_pos),
+                      reinterpret_cast<const uint16_t *>(a.ws + L.tok.rk_ge),
+                      reinterpret_cast<const uint16_t *>(a.ws + L.tok.rk_coarse),
+                      L.tok.n, L.tok.nchunks, L.tok.chunk, a.topk_out, a.top_k};
+    hipLaunchKernelGGL(ranked_select_kernel, dim3((unsigned)a.nq), dim3(kRankThreads), 0, s, R,
+                       a.q_pos);
+    return hipGetLastError();
+  }
   SelProblems P;
   P.p[0] = sel_problem(a, L.tok, a.top_k, reindex_pool ? kOutPoolIds : kOutPositions, a.topk_out,
                        a.top_k);

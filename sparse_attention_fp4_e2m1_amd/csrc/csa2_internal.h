@@ -16,11 +16,14 @@ constexpr int kHistBins = 4096;      // first radix pass: top 12 bits of the sco
 //                builds no histogram);
 //   kHistGlobal  the scorer's workgroups add theirs into the query's global
 //                histogram copies (cleared by a launch before the scorer);
-//   kHistSlots   each scorer workgroup stores its chunk's histogram (16-bit
-//                bins packed in pairs) in a slot of its own; the resolve adds
-//                the slots up (nothing to clear: every slot a resolve reads is
-//                written by the same call).
-enum HistSource { kHistKeys = 0, kHistGlobal = 1, kHistSlots = 2 };
+//   kRanked      no histogram as such: each scorer workgroup stores its
+//                chunk's keys ordered by 12-bit bin, highest bin first, with
+//                their positions and, per bin, the count of the chunk's keys
+//                in that bin or above; ranked_select_kernel reads the
+//                threshold bin off those counts and then only the keys at or
+//                above it (nothing to clear: every chunk record a selection
+//                reads is written by the same call).
+enum HistSource { kHistKeys = 0, kHistGlobal = 1, kRanked = 2 };
 constexpr int kPoolBlock = 8;        // positions per candidate-pool block
 
 hipError_t launch_kv_append(const csa2_cache &c, const uint16_t *k, const uint16_t *v,
@@ -41,9 +44,12 @@ struct SelectArrays {      // one selection problem per query (tokens, or pool b
   int32_t hcopies = 1;     // copies of the 12-bit histogram (scorer workgroups spread over them)
   int64_t hstride = 0;     // words per query: hcopies histograms, state words, second histogram
   int32_t hsrc = 0;        // HistSource: where the resolve finds the 12-bit histogram
-  size_t slots = 0;        // uint32 [nq][nslots][kHistBins / 2]: per-chunk histograms (kHistSlots)
-  int32_t nslots = 0;      // scorer chunks per query (kHistSlots)
-  int32_t slot_chunk = 0;  // candidates per scorer chunk (kHistSlots)
+  // ranked chunks (kRanked): the keys array holds each chunk's keys in bin order
+  size_t rk_pos = 0;       // uint16 [nq][n]  chunk-local position of each ranked key
+  size_t rk_ge = 0;        // uint16 [nq][nchunks][kHistBins]  keys in bin b or above, per chunk
+  size_t rk_coarse = 0;    // uint16 [nq][nchunks][kHistBins / 64]  every 64th entry of rk_ge
+  int32_t nchunks = 0;     // scorer chunks per query
+  int32_t chunk = 0;       // candidates per scorer chunk
 };
 
 // Workspace carve-up of the matrix-core scorer (E4M3 index queries and keys).

@@ -357,11 +357,11 @@ def test_matrix_core_topk_is_deterministic():
                                                      (128, 4, "bf16", 16400), (64, 8, "fp8", 40000)])
 def test_full_topk_chunk_histograms(nq, heads, idx_dtype, cap):
     # enough queries x candidates for the scorer's 2048- (64 queries x 16400)
-    # and 4096-candidate workgroups: each workgroup stores its chunk's
-    # histogram in a slot of its own and the selection adds up the slots of
-    # the chunks a query sees -- the resolve alone up to 32768 keys, the
-    # filter's workgroups each (and no second histogram) past that (40000).
-    # Queries at chunk boundaries and in the ragged last chunk.
+    # and 4096-candidate workgroups, at most 16 chunks per query: each
+    # workgroup stores its chunk's keys in bin order with the counts at or
+    # above every bin (ranked chunk records), and one selection workgroup per
+    # query reads the threshold bin off the counts and then only the keys at
+    # or above it.  Queries at chunk boundaries and in the ragged last chunk.
     announce(f"chunk histograms nq={nq} heads={heads} idx={idx_dtype}")
     m = lib()
     nseq = 4
@@ -384,3 +384,84 @@ def test_full_topk_chunk_histograms(nq, heads, idx_dtype, cap):
         want, _, scores, cand = O.index_topk("full", oc, int(qseq[i]), int(qpos[i]), qi, 2048)
         assert np.array_equal(got[2048][i], want), (2048, i, int(qpos[i]))
         assert np.array_equal(got[100][i], O.topk_select(scores, cand, 100)), (100, i, int(qpos[i]))
+
+
+def _ranked_ws_keys(ws, nq, cap):
+    """(keys, positions) of a ranked-chunk call from its workspace: the
+    library's internal layout -- keys [nq][n] uint32 (each chunk's keys in bin
+    order), then at the next 256-B boundary their chunk-local positions
+    [nq][n] uint16, n = roundup64(capacity)."""
+    n = (cap + 63) // 64 * 64
+    kb = nq * n * 4
+    raw = host(ws).view(np.uint8)
+    keys = raw[:kb].view(np.uint32).reshape(nq, n)
+    po = (kb + 255) // 256 * 256
+    pos = raw[po:po + nq * n * 2].view(np.uint16).reshape(nq, n)
+    return keys, pos
+
+
+@pytest.mark.parametrize("nq,cap,chunk", [(64, 16400, 2048), (128, 16400, 4096)])
+def test_ranked_chunk_records(nq, cap, chunk):
+    # the scorer's ranked records: per chunk the keys are the oracle's score
+    # keys of the chunk's positions (bit for bit), each position once, in
+    # non-increasing order of their top 12 bits
+    announce(f"ranked chunk records nq={nq} cap={cap}")
+    m = lib()
+    wl = synth.workload("decode_64k_b32", context=cap, batch=4, seed=21)
+    gc, oc, _ = filled_caches(wl)
+    rng = np.random.default_rng(nq)
+    qpos = np.concatenate([[0, chunk - 1, chunk, cap - 1],
+                           rng.integers(0, cap, nq - 4)]).astype(np.int32)
+    qseq = (np.arange(nq) % 4).astype(np.int32)
+    qidx = synth.f32_to_bf16_bits(rng.standard_normal((nq, 8, 64)).astype(np.float32))
+    ws = torch.empty(m.csa2_index_topk_workspace(gc, "full", nq, 2048), dtype=torch.uint8, device=DEV)
+    m.csa2_index_topk(gc, "full", dev_u16(qidx), dev_i32(qseq), dev_i32(qpos), 2048, workspace=ws)
+    torch.cuda.synchronize()
+    keys, pos = _ranked_ws_keys(ws, nq, cap)
+    for i in range(0, nq, 7):
+        p = int(qpos[i])
+        cand = np.arange(p + 1)
+        want = _score_keys(O.index_scores(O.query_index_values(qidx[i], "bf16"),
+                                          oc.index_key_values(int(qseq[i]), cand)))
+        for c0 in range(0, p + 1, chunk):
+            cnt = min(chunk, p + 1 - c0)
+            k = keys[i, c0:c0 + cnt]
+            lp = pos[i, c0:c0 + cnt].astype(np.int64)
+            assert np.array_equal(np.sort(lp), np.arange(cnt)), (i, c0)
+            assert np.array_equal(k, want[c0 + lp]), (i, c0)
+            assert np.all(np.diff((k >> 20).astype(np.int64)) <= 0), (i, c0)
+
+
+@pytest.mark.parametrize("distinct", [1, 2, 3])
+def test_ranked_tie_heavy_keys(distinct):
+    # few distinct index keys over 16400 positions, 64 queries (ranked chunk
+    # records of 2048 keys): the threshold bin holds thousands of equal keys
+    # -- past 8192 of them the selection reads them from the records in every
+    # pass -- and the keys equal to the K-th go to the lowest positions
+    announce(f"ranked ties distinct={distinct}")
+    m = lib()
+    cap, nq = 16400, 64
+    gc = m.Cache(2, cap, idx_heads=8, idx_k_dtype="fp8")
+    oc = O.OracleCache(2, cap, idx_heads=8, idx_k_dtype="fp8")
+    rng = np.random.default_rng(100 + distinct)
+    base = synth.f32_to_bf16_bits(rng.standard_normal((distinct, 8, 64)).astype(np.float32))
+    kv = synth.f32_to_bf16_bits(rng.standard_normal((cap, 128)).astype(np.float32))
+    for b in range(2):
+        ik = base[rng.integers(0, distinct, cap)]
+        seq, pos = np.full(cap, b, np.int32), np.arange(cap, dtype=np.int32)
+        m.csa2_kv_append(gc, dev_u16(kv), dev_u16(kv), dev_u16(ik), dev_i32(seq), dev_i32(pos))
+        oc.append(kv, kv, ik, seq, pos)
+    qpos = np.concatenate([[cap - 1, 0, 99, 2047, 2048, 9000],
+                           rng.integers(0, cap, nq - 6)]).astype(np.int32)
+    qseq = (np.arange(nq) % 2).astype(np.int32)
+    qidx = synth.f32_to_bf16_bits(rng.standard_normal((nq, 8, 64)).astype(np.float32))
+    got = {}
+    for top_k in (2048, 100, 9000):
+        tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qidx), dev_i32(qseq), dev_i32(qpos), top_k)
+        torch.cuda.synchronize()
+        got[top_k] = host(tk)
+    for i in range(nq):
+        _, _, scores, cand = O.index_topk("full", oc, int(qseq[i]), int(qpos[i]),
+                                          O.query_index_values(qidx[i], "bf16"), 1)
+        for top_k, g in got.items():
+            assert np.array_equal(g[i], O.topk_select(scores, cand, top_k)), (top_k, i, int(qpos[i]))
