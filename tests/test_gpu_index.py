@@ -465,3 +465,31 @@ def test_ranked_tie_heavy_keys(distinct):
                                           O.query_index_values(qidx[i], "bf16"), 1)
         for top_k, g in got.items():
             assert np.array_equal(g[i], O.topk_select(scores, cand, top_k)), (top_k, i, int(qpos[i]))
+
+
+def test_ranked_poisoned_workspace_reused():
+    # a workspace full of stale bytes, then the same workspace again (ranked
+    # records of 2048 keys): the same exact Top-K both times
+    announce("ranked selection, poisoned then reused workspace")
+    m = lib()
+    cap, nq = 16400, 64
+    wl = synth.workload("decode_64k_b32", context=cap, batch=2, seed=5)
+    gc, oc, _ = filled_caches(wl)
+    rng = np.random.default_rng(3)
+    qpos = rng.integers(0, cap, nq).astype(np.int32)
+    qpos[0] = cap - 1
+    qseq = (np.arange(nq) % 2).astype(np.int32)
+    qidx = synth.f32_to_bf16_bits(rng.standard_normal((nq, 8, 64)).astype(np.float32))
+    ws = torch.full((m.csa2_index_topk_workspace(gc, "full", nq, 300),), 0xAB, dtype=torch.uint8,
+                    device=DEV)
+    runs = []
+    for _ in range(2):
+        tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qidx), dev_i32(qseq), dev_i32(qpos), 300,
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        runs.append(host(tk))
+    for i in range(nq):
+        want, _, _, _ = O.index_topk("full", oc, int(qseq[i]), int(qpos[i]),
+                                     O.query_index_values(qidx[i], "bf16"), 300)
+        assert np.array_equal(runs[0][i], want), i
+        assert np.array_equal(runs[1][i], want), i
