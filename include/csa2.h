@@ -182,6 +182,32 @@ csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode, const uint1
                             int32_t *topk_out, void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/*
+ * csa2_kv_append of the n_append rows (k, v, idx_k_in, a_seq, a_pos) followed
+ * by csa2_index_topk (every other argument), in one call on one stream, with
+ * the same results as the two calls: a decode step's append and its first
+ * index layer (aiwiki "DeepSeek V4.1-Flash", section "Compressed Sparse
+ * Attention 2": the new token's index key is scored with the rest).
+ * Where the index scoring streams the keys in workgroups of 2048 or 4096
+ * candidates (FULL, or REINDEX without pool_in, with enough queries x
+ * candidates to fill the chip; not the matrix-core scorer) and n_append <=
+ * 256, the rows are stored by extra workgroups of the scoring launch and each
+ * appended position a query sees is scored from its row's input, so the
+ * step needs no separate append launch; otherwise the append runs first as
+ * its own launch.  Workspace: csa2_index_topk_workspace's.
+ * Preconditions: csa2_kv_append's for the rows, csa2_index_topk's for the rest.
+ * Errors: csa2_kv_append's (rows checked first), then csa2_index_topk's.
+ */
+csa2_status csa2_index_topk_append(const csa2_cache *cache, const uint16_t *k, const uint16_t *v,
+                                   const uint16_t *idx_k_in, const int32_t *a_seq,
+                                   const int32_t *a_pos, int32_t n_append, csa2_mode mode,
+                                   const uint16_t *q_idx, csa2_dtype q_dtype,
+                                   const int32_t *q_seq, const int32_t *q_pos, int32_t nq,
+                                   int32_t top_k, const int32_t *pool_in, int32_t pool_len,
+                                   int32_t pool_blocks, int32_t *pool_out,
+                                   const int32_t *reuse_src, int32_t *topk_out, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace csa2_sparse_attn needs (0 for invalid arguments). */
 size_t csa2_sparse_attn_workspace(const csa2_cache *cache, int32_t nq, int32_t n_heads,
                                   int32_t top_k);

@@ -52,6 +52,8 @@ def _load():
         "csa2_kv_append": (I32, [C, P, P, P, P, P, I32, P]),
         "csa2_index_topk_workspace": (SZ, [C, I32, I32, I32, I32, I32]),
         "csa2_index_topk": (I32, [C, I32, P, I32, P, P, I32, I32, P, I32, I32, P, P, P, P, SZ, P]),
+        "csa2_index_topk_append": (I32, [C, P, P, P, P, P, I32, I32, P, I32, P, P, I32, I32, P, I32,
+                                         I32, P, P, P, P, SZ, P]),
         "csa2_sparse_attn_workspace": (SZ, [C, I32, I32, I32]),
         "csa2_sparse_attn": (I32, [C, P, I32, P, I32, P, I32, F32, P, P, P, SZ, P]),
         "csa2_sparse_attn_noalloc": (I32, [C, P, I32, P, I32, P, I32, F32, P, P, P]),
@@ -163,8 +165,11 @@ def csa2_index_topk_workspace(cache: Cache, mode: str, nq: int, top_k: int, pool
 
 def csa2_index_topk(cache: Cache, mode: str, q_idx, q_seq, q_pos, top_k: int, q_dtype: str = "bf16",
                     pool_in=None, pool_blocks: int = 0, reuse_src=None, topk_out=None,
-                    pool_out=None, workspace=None, stream=None):
-    """Returns (topk_out [nq, top_k] int32, pool_out [nq, 8*pool_blocks] int32 or None)."""
+                    pool_out=None, workspace=None, stream=None, append=None):
+    """Returns (topk_out [nq, top_k] int32, pool_out [nq, 8*pool_blocks] int32 or None).
+
+    append: optional (k, v, idx_k_in, seq, pos), csa2_kv_append's rows, appended
+    first in the same call (csa2_index_topk_append)."""
     d = cache.device
     if mode == "reuse":
         _need(reuse_src, "reuse_src", _I32, None, d)
@@ -189,12 +194,31 @@ def csa2_index_topk(cache: Cache, mode: str, q_idx, q_seq, q_pos, top_k: int, q_
     ws_bytes = csa2_index_topk_workspace(cache, mode, nq, top_k, pool_len, pool_blocks)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=d)
-    _check(LIB.csa2_index_topk(cache.ref, MODES[mode], _ptr(q_idx), DTYPES[q_dtype], _ptr(q_seq),
-                               _ptr(q_pos), nq, top_k, _ptr(pool_in), pool_len, pool_blocks,
-                               _ptr(pool_out), _ptr(reuse_src), _ptr(topk_out), _ptr(workspace),
-                               0 if workspace is None else workspace.numel(), _stream(stream)),
-           "csa2_index_topk")
+    tail = (MODES[mode], _ptr(q_idx), DTYPES[q_dtype], _ptr(q_seq), _ptr(q_pos), nq, top_k,
+            _ptr(pool_in), pool_len, pool_blocks, _ptr(pool_out), _ptr(reuse_src), _ptr(topk_out),
+            _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
+    if append is None:
+        _check(LIB.csa2_index_topk(cache.ref, *tail), "csa2_index_topk")
+    else:
+        k, v, ik, seq, pos = append
+        n = k.shape[0]
+        _need(k, "k", _B16, (n, cache.dk), d)
+        _need(v, "v", _B16, (n, cache.dv), d)
+        if ik is not None:
+            _need(ik, "idx_k_in", _B16, (n, cache.idx_heads, cache.idx_dim), d)
+        _need(seq, "seq", _I32, (n,), d)
+        _need(pos, "pos", _I32, (n,), d)
+        _check(LIB.csa2_index_topk_append(cache.ref, _ptr(k), _ptr(v), _ptr(ik), _ptr(seq),
+                                          _ptr(pos), n, *tail), "csa2_index_topk_append")
     return topk_out, pool_out
+
+
+def csa2_index_topk_append(cache: Cache, k, v, idx_k_in, seq, pos, mode: str, q_idx, q_seq, q_pos,
+                           top_k: int, **kw):
+    """csa2_kv_append(cache, k, v, idx_k_in, seq, pos) then csa2_index_topk(cache,
+    mode, q_idx, q_seq, q_pos, top_k, **kw) in one call; returns csa2_index_topk's."""
+    return csa2_index_topk(cache, mode, q_idx, q_seq, q_pos, top_k,
+                           append=(k, v, idx_k_in, seq, pos), **kw)
 
 
 def csa2_sparse_attn_workspace(cache: Cache, nq: int, n_heads: int, top_k: int) -> int:

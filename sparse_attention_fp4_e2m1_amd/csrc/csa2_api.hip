@@ -102,14 +102,19 @@ size_t csa2_index_topk_workspace(const csa2_cache *cache, csa2_mode mode_arg, in
   return topk_workspace_layout(*cache, static_cast<csa2_mode>(mode), nq, pool_len, pool_blocks).total;
 }
 
-csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode_arg, const uint16_t *q_idx,
-                            csa2_dtype q_dtype_arg, const int32_t *q_seq, const int32_t *q_pos,
-                            int32_t nq, int32_t top_k, const int32_t *pool_in, int32_t pool_len,
-                            int32_t pool_blocks, int32_t *pool_out, const int32_t *reuse_src,
-                            int32_t *topk_out, void *workspace, size_t workspace_bytes,
-                            void *stream) {
-  const int32_t mode = raw_enum(mode_arg);
-  const int32_t q_dtype = raw_enum(q_dtype_arg);
+}  // extern "C"
+
+namespace {
+
+// csa2_index_topk with rows to append first (ap.n = 0: none).
+// (mode and q_dtype as the caller's raw values: an out-of-range one is an
+// error, not an enum load)
+csa2_status index_topk(const csa2_cache *cache, int32_t mode, const uint16_t *q_idx,
+                       int32_t q_dtype, const int32_t *q_seq, const int32_t *q_pos,
+                       int32_t nq, int32_t top_k, const int32_t *pool_in, int32_t pool_len,
+                       int32_t pool_blocks, int32_t *pool_out, const int32_t *reuse_src,
+                       int32_t *topk_out, void *workspace, size_t workspace_bytes, void *stream,
+                       const AppendRows &ap) {
   csa2_status st = check_topk_args(cache, mode, nq, top_k, pool_len, pool_blocks);
   if (st != CSA2_OK) return st;
   if (topk_out == nullptr) return CSA2_ERR_NULL;
@@ -128,7 +133,12 @@ csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode_arg, const u
       if ((pool_in == nullptr) != (pool_len == 0)) return CSA2_ERR_ARG;
     }
   }
-  if (nq == 0) return CSA2_OK;
+  if (nq == 0) {
+    if (ap.n > 0 && launch_kv_append(*cache, ap.k, ap.v, ap.idx_in, ap.seq, ap.pos, ap.n,
+                                     (hipStream_t)stream) != hipSuccess)
+      return CSA2_ERR_HIP;
+    return CSA2_OK;
+  }
   IndexArgs a;
   a.cache = cache;
   a.mode = static_cast<csa2_mode>(mode);
@@ -148,8 +158,47 @@ csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode_arg, const u
   if (a.layout.total > 0 && (workspace == nullptr || workspace_bytes < a.layout.total))
     return CSA2_ERR_WORKSPACE;
   a.ws = static_cast<uint8_t *>(workspace);
+  a.ap = ap;
   if (launch_index_topk(a, (hipStream_t)stream) != hipSuccess) return CSA2_ERR_HIP;
   return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode, const uint16_t *q_idx,
+                            csa2_dtype q_dtype, const int32_t *q_seq, const int32_t *q_pos,
+                            int32_t nq, int32_t top_k, const int32_t *pool_in, int32_t pool_len,
+                            int32_t pool_blocks, int32_t *pool_out, const int32_t *reuse_src,
+                            int32_t *topk_out, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  AppendRows none{};
+  none.n = 0;
+  return index_topk(cache, raw_enum(mode), q_idx, raw_enum(q_dtype), q_seq, q_pos, nq, top_k,
+                    pool_in, pool_len, pool_blocks, pool_out, reuse_src, topk_out, workspace,
+                    workspace_bytes, stream, none);
+}
+
+csa2_status csa2_index_topk_append(const csa2_cache *cache, const uint16_t *k, const uint16_t *v,
+                                   const uint16_t *idx_k_in, const int32_t *a_seq,
+                                   const int32_t *a_pos, int32_t n_append, csa2_mode mode,
+                                   const uint16_t *q_idx, csa2_dtype q_dtype,
+                                   const int32_t *q_seq, const int32_t *q_pos, int32_t nq,
+                                   int32_t top_k, const int32_t *pool_in, int32_t pool_len,
+                                   int32_t pool_blocks, int32_t *pool_out,
+                                   const int32_t *reuse_src, int32_t *topk_out, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  // the append's own checks first (csa2_kv_append's), then the index call's
+  csa2_status st = check_cache(cache, idx_k_in != nullptr);
+  if (st != CSA2_OK) return st;
+  if (n_append < 0) return CSA2_ERR_SHAPE;
+  if (n_append > 0 && (k == nullptr || v == nullptr || a_seq == nullptr || a_pos == nullptr))
+    return CSA2_ERR_NULL;
+  AppendRows ap = append_rows(*cache, k, v, idx_k_in, a_seq, a_pos, n_append);
+  return index_topk(cache, raw_enum(mode), q_idx, raw_enum(q_dtype), q_seq, q_pos, nq, top_k,
+                    pool_in, pool_len, pool_blocks, pool_out, reuse_src, topk_out, workspace,
+                    workspace_bytes, stream, ap);
 }
 
 size_t csa2_sparse_attn_workspace(const csa2_cache *cache, int32_t nq, int32_t n_heads,

@@ -15,128 +15,16 @@
 // formats and bounded replay": each layer's own local sliding-window K and V
 // are kept in FP8; local_append_kernel casts them to E4M3 into a ring of
 // window slots per sequence.
-#include "csa2_internal.h"
+#include "csa2_kv_row.h"
 
 namespace csa2 {
 namespace {
 
-// E2M1 magnitude code of |x| under decoded scale s > 0: the count of midpoints
-// (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) * s below |x|; a value exactly on a
-// midpoint moves up only when the upper neighbour's code is even.  Every
-// midpoint * s is exact in fp32 (<= 3 significant bits times <= 4).
-__device__ __forceinline__ uint32_t e2m1_mag(float ax, float s) {
-  uint32_t c = 0;
-  c += (ax > 0.25f * s);
-  c += (ax >= 0.75f * s);   // tie -> code 2 (even)
-  c += (ax > 1.25f * s);
-  c += (ax >= 1.75f * s);   // tie -> code 4
-  c += (ax > 2.5f * s);
-  c += (ax >= 3.5f * s);    // tie -> code 6
-  c += (ax > 5.0f * s);
-  return c;
-}
-
-// One 16-channel block: E4M3 scale code (returned) and the 16 E2M1 codes,
-// channel i in nibble i of (lo, hi).
-__device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], uint32_t &lo,
-                                                  uint32_t &hi) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  // amax is a bf16 value; the correctly rounded quotient never lands on an
-  // E4M3 midpoint unless the exact quotient does, so rounding it to E4M3
-  // equals rounding the exact amax/6.
-  const uint32_t sc = e4m3_from_f32_nonneg(amax / 6.0f);
-  const float s = e4m3_to_f32(sc);
-  lo = 0;
-  hi = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t c = s > 0.0f ? e2m1_mag(fabsf(x[i]), s) : 0u;
-    c |= (__float_as_uint(x[i]) >> 28) & 8u;   // sign bit, -0 kept
-    if (i < 8) lo |= c << (4 * i);
-    else hi |= c << (4 * (i - 8));
-  }
-  return sc;
-}
-
-// Eight consecutive index-key channels (bf16 bits in a) of head h at
-// position p into the tiled layout (tiles of 64/H positions;
-// [chunk][position-in-tile][head][16 B]), as bf16 or cast to E4M3.
-__device__ __forceinline__ void store_idx8(uint8_t *seq_idx, int H, int esz, int64_t p, int h,
-                                           int ch, uint4 a) {
-  const int T = kWave / H;
-  uint8_t *tile = seq_idx + (p / T) * (64 * 64 * esz);
-  const int byte = ch * esz;                         // byte of channel ch within the head
-  uint8_t *dst = tile + (byte / 16) * 1024 + ((p % T) * H + h) * 16 + byte % 16;
-  if (esz == 1) {
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-    uint32_t out[2] = {0, 0};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t hb = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-      const float f = __uint_as_float(hb << 16);
-      const uint32_t c = e4m3_from_f32_nonneg(fabsf(f)) | ((hb >> 8) & 0x80u);
-      out[i >> 2] |= c << (8 * (i & 3));
-    }
-    *reinterpret_cast<uint2 *>(dst) = make_uint2(out[0], out[1]);
-  } else {
-    *reinterpret_cast<uint4 *>(dst) = a;
-  }
-}
-
-// One wave per row.  Every load of the row is issued first, with no branch
-// around it (a load under a lane-dependent branch is waited for before the
-// branch closes), so a decode step's handful of rows costs one memory round
-// trip: lanes 0..15 quantize one 16-channel block each (K blocks 0..7, then V),
-// and every lane stores eight channels of the index keys.
-__global__ void __launch_bounds__(256) kv_append_kernel(
-    uint8_t *__restrict__ kv_codes, uint8_t *__restrict__ kv_scales, void *__restrict__ idx_k,
-    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const uint16_t *__restrict__ idx_in, const int32_t *__restrict__ seq,
-    const int32_t *__restrict__ pos, int32_t n, int32_t capacity, int32_t idx_elems,
-    int32_t idx_fp8) {
-  const int lane = threadIdx.x & (kWave - 1);
+// One wave per row (append_row).
+__global__ void __launch_bounds__(256) kv_append_kernel(const AppendRows A) {
   const int row = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (row >= n) return;
-  const int32_t sq = seq[row];
-  const int32_t ps = pos[row];
-  // K / V block (lanes 16..63 load lane % 16's block again, unused)
-  const bool is_v = (lane & 8) != 0;
-  const int blk = lane & 7;
-  const uint4 *s4 = reinterpret_cast<const uint4 *>((is_v ? v : k) + (int64_t)row * 128 + blk * 16);
-  const uint4 a = s4[0], b = s4[1];
-  // index keys: 8 channels per lane (lanes past the row's H * 64 channels
-  // load the last group again, unused; without index keys the row's K
-  // channels stand in, unused)
-  const int e = min(lane * 8, idx_elems - 8);
-  const uint16_t *isrc = idx_in != nullptr ? idx_in + (int64_t)row * idx_elems + e
-                                           : k + (int64_t)row * 128;
-  const uint4 ik = *reinterpret_cast<const uint4 *>(isrc);
-  const int64_t slot = (int64_t)sq * capacity + ps;
-
-  if (lane < 16) {
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-    uint32_t lo, hi;
-    const uint32_t sc = quant_block16(x, lo, hi);
-    uint2 *dst = reinterpret_cast<uint2 *>(kv_codes + slot * 128 + (is_v ? 64 : 0) + blk * 8);
-    *dst = make_uint2(lo, hi);
-    kv_scales[slot * 16 + (is_v ? 8 : 0) + blk] = (uint8_t)sc;
-  }
-
-  if (idx_in != nullptr && lane * 8 < idx_elems) {
-    const int H = idx_elems / 64;
-    const int esz = idx_fp8 ? 1 : 2;
-    const int64_t seq_bytes = (int64_t)capacity * idx_elems * esz;
-    uint8_t *seq_idx = static_cast<uint8_t *>(idx_k) + (int64_t)sq * seq_bytes;
-    store_idx8(seq_idx, H, esz, ps, e / 64, e % 64, ik);
-  }
+  if (row >= A.n) return;
+  append_row(A, row, threadIdx.x & (kWave - 1));
 }
 
 // The encoder-side projection fused into quantize-and-append (aiwiki "DeepSeek
@@ -341,15 +229,20 @@ hipError_t launch_local_append(const csa2_local_cache &c, const uint16_t *k, con
   return hipGetLastError();
 }
 
+AppendRows append_rows(const csa2_cache &c, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *idx_in, const int32_t *seq, const int32_t *pos, int32_t n) {
+  return AppendRows{static_cast<uint8_t *>(c.kv_codes), static_cast<uint8_t *>(c.kv_scales),
+                    c.idx_k, k, v, idx_in, seq, pos, n, c.capacity, c.idx_heads * c.idx_dim,
+                    (int32_t)(c.idx_k_dtype == CSA2_FP8_E4M3)};
+}
+
 hipError_t launch_kv_append(const csa2_cache &c, const uint16_t *k, const uint16_t *v,
                             const uint16_t *idx_in, const int32_t *seq, const int32_t *pos,
                             int32_t n, hipStream_t stream) {
   const int rows_per_block = 4;
   dim3 grid((n + rows_per_block - 1) / rows_per_block);
-  const int32_t idx_elems = c.idx_heads * c.idx_dim;
-  hipLaunchKernelGGL(kv_append_kernel, grid, dim3(rows_per_block * kWave), 0, stream, c.kv_codes,
-                     c.kv_scales, c.idx_k, k, v, idx_in, seq, pos, n, c.capacity, idx_elems,
-                     (int32_t)(c.idx_k_dtype == CSA2_FP8_E4M3));
+  hipLaunchKernelGGL(kv_append_kernel, grid, dim3(rows_per_block * kWave), 0, stream,
+                     append_rows(c, k, v, idx_in, seq, pos, n));
   return hipGetLastError();
 }
 

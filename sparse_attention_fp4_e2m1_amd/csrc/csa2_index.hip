@@ -55,6 +55,7 @@
 // position go to the matrix-core scorer in csa2_index_gemm.hip instead.
 #include <algorithm>
 
+#include "csa2_kv_row.h"
 #include "csa2_select.h"
 
 namespace csa2 {
@@ -303,9 +304,14 @@ score_kernel(
     int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
     uint32_t *__restrict__ keys_tok, int64_t tok_stride, uint32_t *__restrict__ hist_tok,
     uint32_t *__restrict__ keys_blk, int64_t blk_stride, uint32_t *__restrict__ hist_blk,
-    int64_t hstride, int32_t hcopies, RankedOut rk) {
+    int64_t hstride, int32_t hcopies, RankedOut rk, const AppendRows ap, int32_t nq) {
   // kRanked: the chunk's record goes to rk (and the keys array, in bin order)
-  // instead of adding its histogram into the global one
+  // instead of adding its histogram into the global one.
+  // ap.n > 0 (a fused append, 256-thread shapes, ap.n <= kThreads): the
+  // workgroups past the nq query rows store the appended rows, one wave per
+  // row; a scoring workgroup whose chunk holds an appended position of its
+  // query's sequence scores that position from the row's input instead of
+  // the cache (which those workgroups may not have written yet).
   static_assert(!kRanked || (!kPool && kThreads * 16 == kHistBins), "ranked chunks: 16 bins per thread");
   constexpr int kEsz = kFp8Keys ? 1 : 2;
   constexpr int TPI = kWave / H;
@@ -326,9 +332,19 @@ score_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t rsk[kRanked ? kChunk : 1];   // the chunk's keys in bin order
   __shared__ __attribute__((aligned(16))) uint16_t rsp[kRanked ? kChunk : 1];   // and their chunk-local positions
   __shared__ uint32_t rscr[kThreads / kWave + 1];
+  __shared__ uint32_t fix_n;                          // a fused append's rows in this chunk
+  __shared__ int32_t fix_row[kThreads > 64 ? kThreads : 1];
+  __shared__ int32_t fix_pos[kThreads > 64 ? kThreads : 1];
+  __shared__ uint32_t fix_key[kThreads > 64 ? kThreads : 1];
   uint32_t *hist = lds_main;
   uint32_t *skeys = lds_main + kHistBins / 2;
 
+  if ((int)blockIdx.y >= nq) {   // a fused append's rows
+    const int row = (int)(((int64_t)(blockIdx.y - nq) * gridDim.x + blockIdx.x) * kNumWaves +
+                          threadIdx.x / kWave);
+    if (row < ap.n) append_row(ap, row, threadIdx.x & (kWave - 1));
+    return;
+  }
   const int q = blockIdx.y;
   const int32_t qp = q_pos[q];
   const int64_t n = (int64_t)qp + 1;
@@ -363,7 +379,13 @@ score_kernel(
   for (int i = 0; i < 64; ++i) qf[i] = qlds[h * 64 + i];
 
   // tiled index keys: the lane slot of (position-in-tile tl, head h) is `lane`
-  const uint8_t *seq_base = idx_k + (int64_t)q_seq[q] * capacity * kBpt;
+  const int32_t sq = q_seq[q];
+  const uint8_t *seq_base = idx_k + (int64_t)sq * capacity * kBpt;
+  // a fused append: thread r's row (read now, used after the stream; the
+  // arrays hold at least one entry, so the clamped read is in bounds)
+  const bool fuse = ap.n > 0 && ap.idx_in != nullptr && !Ctx::kDirectHist;   // uniform
+  const int ar = max(0, min((int)threadIdx.x, ap.n - 1));
+  const int32_t aseq = ap.seq[ar], apos = ap.pos[ar];
 
   // The wave walks its steps (one tile each; H steps make a group of 64
   // tokens) with a ping-pong prefetch: the loads of the next kUnroll steps are
@@ -389,6 +411,59 @@ score_kernel(
     }
   }
   __syncthreads();
+  if (fuse) {
+    // appended positions in this chunk: their keys from the rows' input
+    if (threadIdx.x == 0) fix_n = 0;
+    __syncthreads();
+    if ((int)threadIdx.x < ap.n && aseq == sq && apos >= t_begin && apos < t_end) {
+      const uint32_t f = atomicAdd(&fix_n, 1u);
+      fix_row[f] = threadIdx.x;
+      fix_pos[f] = apos;
+    }
+    __syncthreads();
+    const int nfix = (int)fix_n;
+    for (int f = wave; f < nfix; f += kNumWaves) {   // uniform per wave
+      // lane (tl, h): head h's chain over the row's channels 0..63, then the
+      // heads added in order -- the canonical score (every group of H lanes
+      // computes the same)
+      const int r = fix_row[f];
+      const uint4 *src = reinterpret_cast<const uint4 *>(ap.idx_in + (int64_t)r * ap.idx_elems + h * 64);
+      const float *qh = qlds + h * 64;   // (the query from LDS and a rolled loop: few registers)
+      float acc = 0.0f;
+#pragma unroll 1
+      for (int j = 0; j < 8; ++j) {
+        const uint4 rw = src[j];
+        const uint32_t w4[4] = {rw.x, rw.y, rw.z, rw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc = __builtin_fmaf(qh[8 * j + 2 * e], idx_key_value(w4[e] & 0xFFFFu, kFp8Keys), acc);
+          acc = __builtin_fmaf(qh[8 * j + 2 * e + 1], idx_key_value(w4[e] >> 16, kFp8Keys), acc);
+        }
+      }
+      const uint32_t key = score_key(head_sum_ltr<H>(acc));
+      if (lane == 0) fix_key[f] = key;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int f = 0; f < nfix; ++f) {
+        const int64_t i = fix_pos[f] - t_begin;
+        const uint32_t old = skeys[i], key = fix_key[f];
+        skeys[i] = key;
+        hist[old >> 21] -= 1u << ((old >> 16) & 16u);
+        hist[key >> 21] += 1u << ((key >> 16) & 16u);
+        if (kPool) {   // the block maximum of the position's 8-block
+          const int64_t b0 = i / kPoolBlock * kPoolBlock;
+          uint32_t m = 0u;
+          for (int64_t j = b0; j < min(b0 + kPoolBlock, t_end - t_begin); ++j) m = max(m, skeys[j]);
+          const uint32_t om = sblk[i / kPoolBlock];
+          sblk[i / kPoolBlock] = m;
+          histb[om >> 21] -= 1u << ((om >> 16) & 16u);
+          histb[m >> 21] += 1u << ((m >> 16) & 16u);
+        }
+      }
+    }
+    __syncthreads();
+  }
 
   const int64_t cnt = t_end - t_begin;
   if constexpr (kRanked) {
@@ -1160,6 +1235,18 @@ void launch_score_shape(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
   const TopkWorkspace &L = a.layout;
   dim3 grid((unsigned)((n_cand_max + kChunk - 1) / kChunk), (unsigned)a.nq);
   uint32_t *keys = reinterpret_cast<uint32_t *>(a.ws + L.tok.keys);
+  // a fused append (only the 256-thread shapes take one): its rows in extra
+  // workgroup rows past the queries, kThreads / 64 rows per workgroup; the
+  // append arrays always point at valid memory (the kernel reads entry 0)
+  AppendRows ap = a.ap;
+  if (kThreads != 256 || ap.n <= 0) {
+    ap.n = 0;
+    ap.seq = a.q_seq;
+    ap.pos = a.q_pos;
+  } else {
+    const int64_t per = (int64_t)grid.x * (kThreads / kWave);
+    grid.y += (unsigned)((ap.n + per - 1) / per);
+  }
   if (L.tok.hsrc == kRanked) {
     // the layout chose ranked chunks by the same shape rule (score_chunk)
     if constexpr (!kPool && kThreads == 256) {
@@ -1170,7 +1257,7 @@ void launch_score_shape(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
       hipLaunchKernelGGL((score_kernel<H, kFp8, false, kThreads, kChunk, true>), grid, dim3(kThreads),
                          0, s, static_cast<const uint8_t *>(c.idx_k), (int64_t)c.capacity, a.q_idx,
                          a.q_fp8, a.q_seq, a.q_pos, keys, L.tok.n, nullptr, nullptr, (int64_t)0,
-                         nullptr, (int64_t)0, 1, rk);
+                         nullptr, (int64_t)0, 1, rk, ap, a.nq);
     }
     return;
   }
@@ -1180,7 +1267,7 @@ void launch_score_shape(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
                      reinterpret_cast<uint32_t *>(a.ws + L.tok.hist),
                      kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.keys) : nullptr, L.blk.n,
                      kPool ? reinterpret_cast<uint32_t *>(a.ws + L.blk.hist) : nullptr,
-                     L.tok.hstride, L.tok.hcopies, RankedOut{nullptr, nullptr, nullptr});
+                     L.tok.hstride, L.tok.hcopies, RankedOut{nullptr, nullptr, nullptr}, ap, a.nq);
 }
 
 // Workgroup shape from the amount of work: long streams when there are enough
@@ -1353,7 +1440,23 @@ TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t
   return w;
 }
 
-hipError_t launch_index_topk(const IndexArgs &a, hipStream_t s) {
+bool append_fusable(const IndexArgs &a) {
+  if (a.ap.n <= 0 || a.ap.n > kFuseMaxRows || a.mode == CSA2_REUSE) return false;
+  if (a.q_fp8 && gemm_eligible(*a.cache, a.mode, a.pool_len, a.pool_blocks)) return false;
+  const bool pool = a.mode == CSA2_FULL && a.pool_blocks > 0;
+  const bool reindex_pool = a.mode == CSA2_REINDEX && a.pool_in != nullptr;
+  return !reindex_pool && score_chunk(a.nq, a.cache->capacity, pool) >= 2048;
+}
+
+hipError_t launch_index_topk(const IndexArgs &a_in, hipStream_t s) {
+  // an append the scorer cannot take runs first, on its own
+  IndexArgs a = a_in;
+  if (a.ap.n > 0 && !append_fusable(a)) {
+    const AppendRows &p = a.ap;
+    const hipError_t e = launch_kv_append(*a.cache, p.k, p.v, p.idx_in, p.seq, p.pos, p.n, s);
+    if (e != hipSuccess) return e;
+    a.ap.n = 0;
+  }
   const csa2_cache &c = *a.cache;
   if (a.mode == CSA2_REUSE) {
     const int64_t n = (int64_t)a.nq * a.top_k;

@@ -76,6 +76,23 @@ struct TopkWorkspace {
 TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t nq,
                                     int32_t pool_len, int32_t pool_blocks);
 
+// The rows of one append call (csa2_kv_append's arguments).
+struct AppendRows {
+  uint8_t *kv_codes;
+  uint8_t *kv_scales;
+  void *idx_k;
+  const uint16_t *k, *v, *idx_in;   // idx_in may be null: index keys untouched
+  const int32_t *seq, *pos;
+  int32_t n;
+  int32_t capacity;
+  int32_t idx_elems;                // index heads x 64
+  int32_t idx_fp8;
+};
+AppendRows append_rows(const csa2_cache &c, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *idx_in, const int32_t *seq, const int32_t *pos, int32_t n);
+// Appended rows the scorer takes in one launch at most (more run on their own).
+constexpr int32_t kFuseMaxRows = 256;
+
 struct IndexArgs {
   const csa2_cache *cache;
   csa2_mode mode;
@@ -93,6 +110,7 @@ struct IndexArgs {
   int32_t *topk_out;
   uint8_t *ws;
   TopkWorkspace layout;
+  AppendRows ap;           // rows to append first (ap.n = 0: none)
 };
 
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream);

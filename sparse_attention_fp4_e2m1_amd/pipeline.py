@@ -59,16 +59,20 @@ class LayerStack:
     def run(self, q: Sequence[torch.Tensor], q_idx: Sequence[torch.Tensor], q_seq: torch.Tensor,
             q_pos: torch.Tensor, append: Optional[tuple] = None, stream=None,
             scan_events: Optional[tuple] = None, mark=None):
-        """Enqueue one step: optional append (k, v, idx_k, seq, pos), then every layer.
+        """Enqueue one step: optional append (k, v, idx_k, seq, pos), then every layer
+        (the append rides in the first index layer's call, csa2_index_topk_append).
 
         scan_events: optional (before, after) hipEvent_t handles recorded around the
         index scoring of the first Full layer (csa2_profile_index_scan).
         mark: optional callable, called with ("attn", layer, "before" / "after")
         right before and after each layer's attention call is enqueued (a
         caller records its own events there)."""
-        if append is not None:
+        # the step's append goes into the first index layer's call (one launch
+        # fewer where the scorer can take it), else on its own
+        if append is not None and self.layers[0].mode == "reuse":
             k, v, ik, seq, pos = append
             B.csa2_kv_append(self.cache, k, v, ik, seq, pos, stream=stream)
+            append = None
         for li, L in enumerate(self.layers):
             if L.mode == "reuse":
                 pass   # self.topk[li] is self.topk[L.reuse_from]
@@ -79,7 +83,7 @@ class LayerStack:
                     B.csa2_index_topk(self.cache, "full", q_idx[li], q_seq, q_pos, self.k[li],
                                       q_dtype=self.q_idx_dtype, pool_blocks=L.pool_blocks,
                                       topk_out=self.topk[li], pool_out=self.pool[li],
-                                      workspace=self.ws_topk, stream=stream)
+                                      workspace=self.ws_topk, stream=stream, append=append)
                 finally:
                     if scan_events is not None:
                         B.LIB.csa2_profile_index_scan(None, None)
@@ -88,7 +92,10 @@ class LayerStack:
                 pool_in = self.pool[L.pool_from] if L.pool_from >= 0 else None
                 B.csa2_index_topk(self.cache, "reindex", q_idx[li], q_seq, q_pos, self.k[li],
                                   q_dtype=self.q_idx_dtype, pool_in=pool_in,
-                                  topk_out=self.topk[li], workspace=self.ws_topk, stream=stream)
+                                  topk_out=self.topk[li], workspace=self.ws_topk, stream=stream,
+                                  append=append)
+            if L.mode != "reuse":
+                append = None
             if mark is not None:
                 mark("attn", li, "before")
             B.csa2_sparse_attn(self.cache, q[li], q_seq, self.topk[li],

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
                  "csa2_local_append", "csa2_local_attn", "csa2_local_clear",
                  "csa2_kv_export", "csa2_kv_export_bytes", "csa2_kv_import", "csa2_proj_append",
                  "csa2_sparse_local_attn", "csa2_sparse_local_attn_workspace",
-                 "csa2_strerror", "csa2_abi_version"):
+                 "csa2_index_topk_append", "csa2_strerror", "csa2_abi_version"):
         assert want in names
 
 
@@ -108,6 +108,30 @@ def test_index_topk_validation(lib):
     assert call(ws_bytes=16) == lib.CSA2_ERR_WORKSPACE
     assert call(nq=0) == lib.CSA2_OK
     assert call(mode=2, reuse=P(1), nq=0) == lib.CSA2_OK
+
+
+def test_index_topk_append_validation(lib):
+    # the rows are checked first (csa2_kv_append's rules), then the index call
+    L = lib.LIB
+    P = ctypes.c_void_p
+    c = ctypes.byref(_cache(lib))
+
+    def call(n=4, k=P(1), seq=P(1), ik=None, cache=c, mode=0, nq=2, top_k=16, out=P(1), ws=P(1),
+             ws_bytes=1 << 40):
+        return L.csa2_index_topk_append(cache, k, P(1), ik, seq, P(1), n, mode, P(1), 0, P(1),
+                                        P(1), nq, top_k, None, 0, 0, None, None, out, ws,
+                                        ws_bytes, None)
+
+    assert call(cache=None) == lib.CSA2_ERR_NULL
+    assert call(n=-1) == lib.CSA2_ERR_SHAPE
+    assert call(k=None) == lib.CSA2_ERR_NULL
+    assert call(seq=None) == lib.CSA2_ERR_NULL
+    assert call(ik=P(1), cache=ctypes.byref(_cache(lib, idx_k=None))) == lib.CSA2_ERR_NULL
+    assert call(top_k=0) == lib.CSA2_ERR_SHAPE
+    assert call(mode=7) == lib.CSA2_ERR_ARG
+    assert call(out=None) == lib.CSA2_ERR_NULL
+    assert call(ws=None) == lib.CSA2_ERR_WORKSPACE
+    assert call(n=0, k=None, seq=None, nq=0) == lib.CSA2_OK        # nothing to do
 
 
 def test_workspace_queries(lib):
