@@ -149,7 +149,8 @@ size_t csa2_index_topk_workspace(const csa2_cache *cache, csa2_mode mode, int32_
  *              blocks kept; pool_out [nq][8*pool_blocks] receives their visible
  *              positions in ascending order, -1 padded.
  *   REINDEX:   candidates are the entries of pool_in [nq][pool_len] that lie
- *              in [0, q_pos] (-1 = empty slot); pool_in = NULL means all visible
+ *              in [0, q_pos] (-1 = empty slot), a row's positions in ascending
+ *              order (as pool_out lists them); pool_in = NULL means all visible
  *              positions (as FULL, no pool).  Entries must be distinct.
  *   REUSE:     topk_out = reuse_src [nq][top_k], copied unchanged; q_idx,
  *              q_seq, q_pos may be NULL.

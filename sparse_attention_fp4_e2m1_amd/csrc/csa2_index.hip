@@ -19,15 +19,16 @@
 //                    top 12 key bits, and for a pool-building Full layer the
 //                    8-position block maxima and their histogram.
 // Then the selection, in one of two forms:
-//   Ranked chunks (a Full layer without a pool, or a Reindex layer without
-//   one, over at most kMaxRankedChunks scorer chunks per query -- decode
-//   batches at up to 64K context): each scorer workgroup sorts its chunk's
-//   keys by 12-bit bin in LDS and stores them with their positions and the
-//   count of keys at or above every bin, so that
+//   Ranked records (a Full layer without a pool, or a Reindex layer without
+//   one, over at most 65536 positions in at most kMaxRankedChunks scorer
+//   chunks -- decode batches up to 64K context -- and a Reindex pool of at
+//   most 64 x kGatherRec entries, scored by gather_rank_kernel): each scorer
+//   workgroup sorts its keys by 12-bit bin in LDS and stores them with their
+//   indices and the count of keys at or above every bin, so that
 //   ranked_select_kernel  one workgroup per query reads the threshold bin b1
 //                    off the counts (a 64-entry coarse table, then one
 //                    64-bin window), then only the keys at or above b1 (the
-//                    first entries of each chunk's list), and selects in LDS:
+//                    first entries of each record), and selects in LDS:
 //                    one launch instead of two, and no histogram to clear.
 //   Otherwise:
 //   filter_kernel    per wave and 512 or 1024 keys: keep every key whose top 12 bits
@@ -73,9 +74,13 @@ constexpr int kFilterSubMin = 512;
 constexpr int kFilterSubMax = 1024;
 constexpr int64_t kFilterSmallMax = 32768;
 constexpr int64_t kDirectMax = 32768;      // up to this many keys the resolve filters them itself
-// Ranked chunks (kRanked): at most this many scorer chunks per query (one
-// selection wave each), chunks of at least 2048 keys.
-constexpr int64_t kMaxRankedChunks = 16;
+// Ranked records (kRanked): at most this many records per query (a
+// selection wave reads four) and 65536 candidates; a Full scan's records
+// are its chunks of 2048 or 4096 positions, a Reindex pool's are runs of
+// kGatherRec entries.
+constexpr int64_t kMaxRankedChunks = 64;
+constexpr int64_t kMaxRankedKeys = 65536;
+constexpr int kGatherRec = 256;
 constexpr int kEarlySlots = 8;             // candidate slots per resolve thread read before the counts
 // Keys in the threshold bin beyond which the filter leaves the bits 19..8 pass
 // to the resolve (heavy ties would serialize the global atomics).
@@ -285,6 +290,84 @@ struct ScoreCtx {
   }
 };
 
+// A ranked record from a workgroup's staged keys: skeys[i] for the slots i
+// with valid(i), counted in the packed 16-bit LDS histogram `hist`.  Thread
+// t owns bins 16t .. 16t+15 (LDS words 8t .. 8t+7): ge of a bin = keys in
+// the bins of higher threads + the thread's own bins from that one up; a
+// bin's keys start at ge - count in the bin-ordered list, where LDS atomics
+// on the bins' cursors place them (in no particular order inside a bin).
+// Then the record (keys, slot indices), its ge table and coarse table go out
+// with the global stores last (a barrier waits for a thread's stores).
+// Contains barriers; uses rsk, rsp (kSlots each) and rscr.
+template <int kThreads, int kSlots, class Valid>
+__device__ __forceinline__ void rank_record(uint32_t *hist, const uint32_t *skeys, Valid valid,
+                                            uint32_t *rsk, uint16_t *rsp, uint32_t *rscr,
+                                            uint32_t *keys_out, uint16_t *pos_out,
+                                            uint16_t *ge_out, uint16_t *coarse_out) {
+  static_assert(kThreads * 16 == kHistBins && kSlots % kThreads == 0, "16 bins per thread");
+  const int tid = threadIdx.x;
+  const uint4 wa = reinterpret_cast<const uint4 *>(hist)[2 * tid];
+  const uint4 wb = reinterpret_cast<const uint4 *>(hist)[2 * tid + 1];
+  const uint32_t w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+  uint32_t c[16], ge[16];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    c[2 * k] = w[k] & 0xFFFFu;
+    c[2 * k + 1] = w[k] >> 16;
+  }
+  uint32_t s = 0;
+#pragma unroll
+  for (int b = 15; b >= 0; --b) {
+    s += c[b];
+    ge[b] = s;
+  }
+  uint32_t total;
+  const uint32_t before = block_exclusive_scan(s, rscr, total);
+  const uint32_t higher = total - before - s;   // keys in the bins of higher threads
+  uint32_t g[8], cur[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t lo = ge[2 * k] + higher, hi = ge[2 * k + 1] + higher;
+    g[k] = lo | (hi << 16);
+    cur[k] = (lo - c[2 * k]) | ((hi - c[2 * k + 1]) << 16);
+  }
+  // every thread has read its words: they become the bins' insertion cursors
+  reinterpret_cast<uint4 *>(hist)[2 * tid] = make_uint4(cur[0], cur[1], cur[2], cur[3]);
+  reinterpret_cast<uint4 *>(hist)[2 * tid + 1] = make_uint4(cur[4], cur[5], cur[6], cur[7]);
+  __syncthreads();
+  // a fixed trip count with the empty slots masked (an atomic adding 0), so
+  // that a thread's atomics issue back to back
+#pragma unroll
+  for (int u = 0; u < kSlots / kThreads; ++u) {
+    const int i = tid + u * kThreads;
+    const bool v = valid(i);
+    const uint32_t key = skeys[i];
+    const uint32_t sh = (key >> 16) & 16u;
+    const uint32_t slot = (atomicAdd(&hist[key >> 21], v ? 1u << sh : 0u) >> sh) & 0xFFFFu;
+    if (v) {
+      rsk[slot] = key;
+      rsp[slot] = (uint16_t)i;
+    }
+  }
+  __syncthreads();
+  uint4 *gq = reinterpret_cast<uint4 *>(ge_out);
+  gq[2 * tid] = make_uint4(g[0], g[1], g[2], g[3]);
+  gq[2 * tid + 1] = make_uint4(g[4], g[5], g[6], g[7]);
+  if ((tid & 3) == 0) coarse_out[tid / 4] = (uint16_t)(g[0] & 0xFFFFu);
+  const int cnt = (int)total;
+  for (int i = 4 * tid; i < cnt; i += 4 * kThreads) {
+    if (i + 4 <= cnt) {
+      *reinterpret_cast<uint4 *>(keys_out + i) = *reinterpret_cast<const uint4 *>(rsk + i);
+      *reinterpret_cast<uint2 *>(pos_out + i) = *reinterpret_cast<const uint2 *>(rsp + i);
+    } else {
+      for (int e = i; e < cnt; ++e) {
+        keys_out[e] = rsk[e];
+        pos_out[e] = rsp[e];
+      }
+    }
+  }
+}
+
 // Ranked chunk records (kRanked), written by the scorer's workgroup of chunk
 // c of query q: keys[q][c*chunk + i] (the keys array) and pos[q][c*chunk + i]
 // for i < the chunk's key count, ordered by 12-bit bin from the highest (in
@@ -467,73 +550,11 @@ score_kernel(
 
   const int64_t cnt = t_end - t_begin;
   if constexpr (kRanked) {
-    // Thread t owns bins 16t .. 16t+15 (LDS words 8t .. 8t+7).  ge of a bin =
-    // keys in the bins of higher threads + the thread's own bins from that
-    // one up; the bin's keys start at ge - count in the bin-ordered list.
-    const int tid = threadIdx.x;
-    const uint4 wa = reinterpret_cast<const uint4 *>(hist)[2 * tid];
-    const uint4 wb = reinterpret_cast<const uint4 *>(hist)[2 * tid + 1];
-    const uint32_t w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-    uint32_t c[16], ge[16];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      c[2 * k] = w[k] & 0xFFFFu;
-      c[2 * k + 1] = w[k] >> 16;
-    }
-    uint32_t s = 0;
-#pragma unroll
-    for (int b = 15; b >= 0; --b) {
-      s += c[b];
-      ge[b] = s;
-    }
-    uint32_t total;
-    const uint32_t before = block_exclusive_scan(s, rscr, total);
-    const uint32_t higher = total - before - s;   // keys in the bins of higher threads
-    uint32_t g[8], cur[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t lo = ge[2 * k] + higher, hi = ge[2 * k + 1] + higher;
-      g[k] = lo | (hi << 16);
-      cur[k] = (lo - c[2 * k]) | ((hi - c[2 * k + 1]) << 16);
-    }
-    // every thread has read its words: they become the bins' insertion cursors
-    reinterpret_cast<uint4 *>(hist)[2 * tid] = make_uint4(cur[0], cur[1], cur[2], cur[3]);
-    reinterpret_cast<uint4 *>(hist)[2 * tid + 1] = make_uint4(cur[4], cur[5], cur[6], cur[7]);
-    __syncthreads();
-    // a fixed trip count with the tail masked (an atomic adding 0), so that a
-    // thread's atomics issue back to back
-#pragma unroll
-    for (int u = 0; u < kChunk / kThreads; ++u) {
-      const int i = tid + u * kThreads;
-      const bool v = i < (int)cnt;
-      const uint32_t key = skeys[i];
-      const uint32_t sh = (key >> 16) & 16u;
-      const uint32_t slot = (atomicAdd(&hist[key >> 21], v ? 1u << sh : 0u) >> sh) & 0xFFFFu;
-      if (v) {
-        rsk[slot] = key;
-        rsp[slot] = (uint16_t)i;
-      }
-    }
-    __syncthreads();
-    // the global stores last: a barrier waits for a thread's stores to land
     const int64_t rec = (int64_t)q * gridDim.x + blockIdx.x;
-    uint4 *gq = reinterpret_cast<uint4 *>(rk.ge + rec * kHistBins);
-    gq[2 * tid] = make_uint4(g[0], g[1], g[2], g[3]);
-    gq[2 * tid + 1] = make_uint4(g[4], g[5], g[6], g[7]);
-    if ((tid & 3) == 0) rk.coarse[rec * (kHistBins / 64) + tid / 4] = (uint16_t)(g[0] & 0xFFFFu);
-    uint32_t *dk = keys_tok + (int64_t)q * tok_stride + t_begin;
-    uint16_t *dp = rk.pos + (int64_t)q * tok_stride + t_begin;
-    for (int i = 4 * tid; i < (int)cnt; i += 4 * kThreads) {
-      if (i + 4 <= (int)cnt) {
-        *reinterpret_cast<uint4 *>(dk + i) = *reinterpret_cast<const uint4 *>(rsk + i);
-        *reinterpret_cast<uint2 *>(dp + i) = *reinterpret_cast<const uint2 *>(rsp + i);
-      } else {
-        for (int e = i; e < (int)cnt; ++e) {
-          dk[e] = rsk[e];
-          dp[e] = rsp[e];
-        }
-      }
-    }
+    rank_record<kThreads, kChunk>(hist, skeys, [&](int i) { return i < (int)cnt; }, rsk, rsp, rscr,
+                                  keys_tok + (int64_t)q * tok_stride + t_begin,
+                                  rk.pos + (int64_t)q * tok_stride + t_begin,
+                                  rk.ge + rec * kHistBins, rk.coarse + rec * (kHistBins / 64));
     return;
   }
   // the chunk's keys and block maxima in one burst of coalesced stores
@@ -664,6 +685,119 @@ __global__ void __launch_bounds__(kGatherThreads) gather_score_kernel(
     if (c)
       atomicAdd(&hist_tok[(int64_t)q * hstride + (int64_t)(blockIdx.x % hcopies) * kHistBins + bin], c);
   }
+}
+
+// gather_rank_kernel: Reindex over a pool whose selection takes ranked
+// records (kRanked).  grid (records, nq); workgroup w scores the pool
+// entries [w kGatherRec, (w+1) kGatherRec) in rounds of kGatherThreads / H
+// entries (H lanes per entry, as gather_score_kernel: the same bits), the
+// next round's loads in flight while one is scored, and stores the record of
+// its candidates (the entries in [0, q_pos]) by rank_record.
+template <int H, bool kFp8Keys>
+__global__ void __launch_bounds__(kGatherThreads) gather_rank_kernel(
+    const uint8_t *__restrict__ idx_k, int64_t capacity, const uint16_t *__restrict__ q_idx,
+    int32_t q_fp8, const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos,
+    const int32_t *__restrict__ pool_in, int32_t pool_len, uint32_t *__restrict__ keys,
+    int64_t stride, uint16_t *__restrict__ rpos, uint16_t *__restrict__ rge,
+    uint16_t *__restrict__ rcoarse) {
+  constexpr int kEsz = kFp8Keys ? 1 : 2;
+  constexpr int kLoads = 4 * kEsz;                   // 16-B pieces per head (64 channels)
+  constexpr int kEntries = kGatherThreads / H;       // entries per round
+  constexpr int kRounds = kGatherRec / kEntries;
+  static_assert(kGatherRec == kGatherThreads, "one pool entry per thread staged");
+  __shared__ __attribute__((aligned(16))) float qlds[H * kQPitch];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins / 2];   // 16-bit bins in pairs
+  __shared__ uint32_t skeys[kGatherRec];
+  __shared__ int32_t spos[kGatherRec];   // the entries' positions, -1: not a candidate
+  __shared__ __attribute__((aligned(16))) uint32_t rsk[kGatherRec];
+  __shared__ __attribute__((aligned(16))) uint16_t rsp[kGatherRec];
+  __shared__ uint32_t rscr[kGatherThreads / kWave + 1];
+  const int q = blockIdx.y;
+  const int w = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int h = tid % H;
+  const int32_t qp = q_pos[q];
+  {
+    // this thread's pool entry (a clamped read: entries past the pool are dropped)
+    const int64_t e = (int64_t)w * kGatherRec + tid;
+    const int32_t p = pool_in[(int64_t)q * pool_len + min(e, (int64_t)pool_len - 1)];
+    spos[tid] = (e < pool_len && p >= 0 && p <= qp) ? p : -1;
+  }
+  for (int i = tid; i < kHistBins / 2; i += kGatherThreads) hist[i] = 0u;
+  for (int i = tid; i < H * 64; i += kGatherThreads) {
+    float f = bf16_to_f32(q_idx[(int64_t)q * H * 64 + i]);
+    if (q_fp8) f = e4m3_to_f32(e4m3_from_f32_nonneg(fabsf(f)) | ((__float_as_uint(f) >> 24) & 0x80u));
+    qlds[(i / 64) * kQPitch + i % 64] = f;
+  }
+  __syncthreads();
+  const uint8_t *base = idx_k + (int64_t)q_seq[q] * capacity * (H * 64 * kEsz);
+  const float *qh = qlds + h * kQPitch;
+  auto load = [&](int r, uint4 (&buf)[kLoads]) {
+    const int32_t p = spos[r * kEntries + tid / H];
+    const uint8_t *src = base + idx_chunk_offset<H, kEsz>(p >= 0 ? p : 0, h, 0);
+#pragma unroll
+    for (int v = 0; v < kLoads; ++v) buf[v] = *reinterpret_cast<const uint4 *>(src + v * 1024);
+  };
+  auto score = [&](int r, const uint4 (&buf)[kLoads]) {
+    float acc = 0.0f;   // one chain over the head's 64 channels
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float qv[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 f = *reinterpret_cast<const float4 *>(qh + 16 * j + 4 * k);
+        qv[4 * k] = f.x;
+        qv[4 * k + 1] = f.y;
+        qv[4 * k + 2] = f.z;
+        qv[4 * k + 3] = f.w;
+      }
+      if (kFp8Keys) {
+        const uint4 a = buf[j];
+        const uint32_t wd[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], false);
+          auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], true);
+          acc = __builtin_fmaf(qv[4 * k + 0], lo[0], acc);
+          acc = __builtin_fmaf(qv[4 * k + 1], lo[1], acc);
+          acc = __builtin_fmaf(qv[4 * k + 2], hi[0], acc);
+          acc = __builtin_fmaf(qv[4 * k + 3], hi[1], acc);
+        }
+      } else {
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+          const uint4 a = buf[2 * j + hv];
+          const uint32_t wd[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            acc = __builtin_fmaf(qv[8 * hv + 2 * k], __uint_as_float(wd[k] << 16), acc);
+            acc = __builtin_fmaf(qv[8 * hv + 2 * k + 1], __uint_as_float(wd[k] & 0xFFFF0000u), acc);
+          }
+        }
+      }
+    }
+    const uint32_t key = score_key(head_sum_ltr<H>(acc));
+    if (h == 0) skeys[r * kEntries + tid / H] = key;
+  };
+  uint4 bA[kLoads], bB[kLoads];
+  load(0, bA);
+#pragma unroll
+  for (int r = 0; r < kRounds; r += 2) {
+    load(r + 1, bB);
+    score(r, bA);
+    if (r + 2 < kRounds) load(r + 2, bA);
+    score(r + 1, bB);
+  }
+  __syncthreads();
+  const uint32_t mykey = skeys[tid];
+  if (spos[tid] >= 0) atomicAdd(&hist[mykey >> 21], 1u << ((mykey >> 16) & 16u));
+  __syncthreads();
+  const int64_t rec = (int64_t)q * gridDim.x + w;
+  rank_record<kGatherThreads, kGatherRec>(
+      hist, skeys, [&](int i) { return spos[i] >= 0; }, rsk, rsp, rscr,
+      keys + (int64_t)q * stride + (int64_t)w * kGatherRec,
+      rpos + (int64_t)q * stride + (int64_t)w * kGatherRec, rge + rec * kHistBins,
+      rcoarse + rec * (kHistBins / 64));
 }
 
 // One selection problem of a call: per query, the kk largest keys of an array
@@ -949,44 +1083,51 @@ __global__ void __launch_bounds__(kSelectThreads) resolve_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// ranked_select_kernel: the Top-K of one query from its ranked chunk records
-// (kRanked).  grid (nq), kRankThreads threads; wave w takes chunk w.
+// ranked_select_kernel: the Top-K of one query from its ranked records
+// (kRanked): a Full scan's chunk records, or a Reindex pool's records of
+// kGatherRec entries.  grid (nq), kRankThreads threads; wave w takes records
+// w, w + 16, w + 32, w + 48.
 //   1. the coarse tables: per 64-bin group j, the keys at or above bin 64 j
-//      summed over the chunks; the keff-th largest key lies in the last group
-//      J whose sum reaches keff (the sums fall with j).
-//   2. ge of the 64 bins of group J in every chunk: likewise the bin b1.  Per
-//      chunk, its first ge(b1 + 1) keys lie above bin b1 and are all taken,
-//      the next ge(b1) - ge(b1 + 1) are bin b1's.
-//   3. those keys: the ones above b1 set their positions in the selection
-//      bitmap, bin b1's go to LDS.  Radix passes on bits 19..8 and 7..0 of
-//      bin b1's keys give the keff-th largest key tau; keys above tau are
-//      taken, and of the keys equal to tau the ones at the lowest positions
-//      (a tie bitmap, scanned in position order).
-// The bitmap, scanned in order, gives the positions ascending; -1 padding.
-// The first kRankEarly keys of every chunk are read with the coarse tables,
-// before anything says how many are needed (usually all that are); bin b1
-// holding more keys than LDS takes (heavy ties) is read from the records
-// again in each pass.
+//      summed over the records (group 0: the candidate count, so keff =
+//      min(K, candidates)); the keff-th largest key lies in the last group J
+//      whose sum reaches keff (the sums fall with j).
+//   2. ge of the 64 bins of group J in every record: likewise the bin b1.
+//      Per record, its first ge(b1 + 1) keys lie above bin b1 and are all
+//      taken, the next ge(b1) - ge(b1 + 1) are bin b1's.
+//   3. those keys: the ones above b1 set their candidate index (record *
+//      chunk + index in the record) in the selection bitmap, bin b1's go to
+//      LDS.  Radix passes on bits 19..8 and 7..0 of bin b1's keys give the
+//      keff-th largest key tau; keys above tau are taken, and of the keys
+//      equal to tau the ones at the lowest indices (a tie bitmap, scanned in
+//      index order).
+// The bitmap, scanned in order, gives the indices ascending -- positions, or
+// pool entries (looked up at the end; a pool lists its positions in
+// ascending order); -1 padding.  The first keys of every record (4096 over
+// the records) are read with the coarse tables, before anything says how
+// many are needed (usually all that are); bin b1 holding more keys than LDS
+// takes (heavy ties) is read from the records again in each pass.
 // ---------------------------------------------------------------------------
 constexpr int kRankThreads = 1024;
 constexpr int kRankWaves = kRankThreads / kWave;
 constexpr int kRankCap = 8192;                       // bin-b1 keys held in LDS
-constexpr int kRankMaxKeys = (int)kMaxRankedChunks * 4096;
+constexpr int kRankMaxKeys = (int)kMaxRankedKeys;
 constexpr int kRankWords = kRankMaxKeys / 32;        // selection bitmap words
-constexpr int kRankEarly = kRankThreads * 4 / (int)kMaxRankedChunks;   // keys per chunk read early
-static_assert(kRankWaves == kMaxRankedChunks, "one wave per chunk");
+static_assert(4 * kRankWaves == kMaxRankedChunks && kMaxRankedChunks == kWave,
+              "at most four records per wave; one per lane of a wave");
 static_assert(kRankWords == 2 * kRankThreads, "two bitmap words per thread");
 
 struct RankedSel {
-  const uint32_t *keys;     // [nq][n_stride] each chunk's keys in bin order
-  const uint16_t *pos;      // [nq][n_stride] their chunk-local positions
+  const uint32_t *keys;     // [nq][n_stride] each record's keys in bin order
+  const uint16_t *pos;      // [nq][n_stride] their indices within the record
   const uint16_t *ge;       // [nq][nchunks][kHistBins]
   const uint16_t *coarse;   // [nq][nchunks][kHistBins / 64]
   int64_t n_stride;
-  int32_t nchunks;
-  int32_t chunk;
+  int32_t nchunks;          // records per query
+  int32_t chunk;            // candidates per record: candidate = record * chunk + index
   int32_t *out;             // [nq][kk]
   int32_t kk;
+  const int32_t *pool;      // Reindex pool [nq][pool_len] (candidates = its entries), or nullptr
+  int32_t pool_len;
 };
 
 // The query's taken keys as one list: first every chunk's keys above bin b1,
@@ -997,10 +1138,11 @@ struct RankedSel {
 struct RankedTabs {
   const uint32_t *lo, *hi, *boff;
   int chunk;
+  int nrec;
   __device__ __forceinline__ int64_t bin_index(uint32_t g) const {
     int c = 0;
 #pragma unroll
-    for (int k = 1; k < (int)kMaxRankedChunks; ++k) c += boff[k] <= g ? 1 : 0;
+    for (int k = 1; k < nrec; ++k) c += boff[k] <= g ? 1 : 0;
     return (int64_t)c * chunk + lo[c] + (g - boff[c]);
   }
 };
@@ -1096,10 +1238,14 @@ __device__ __forceinline__ void ranked_take(uint32_t i, int c, int C, uint32_t k
   }
 }
 
+// kRecPerWave: records per wave, 1 (up to 16 records) or 4 (up to 64)
+template <int kRecPerWave>
 __global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
     const RankedSel R, const int32_t *__restrict__ q_pos) {
-  __shared__ uint32_t tabc[kMaxRankedChunks][65];   // coarse tables (padded rows)
-  __shared__ uint32_t tabf[kMaxRankedChunks][65];   // the 64-bin window of group J
+  constexpr int kRecs = kRecPerWave * kRankWaves;
+  __shared__ uint32_t tabc[kRecs][65];   // coarse tables (padded rows)
+  __shared__ uint32_t tabf[kRecs][65];   // the 64-bin window of group J
+  __shared__ uint32_t tsum[kRankWaves][65];         // per wave: its records' sums
   __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
   __shared__ uint32_t sel[kRankWords];
   __shared__ uint32_t tie[kRankWords];
@@ -1107,7 +1253,8 @@ __global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
   __shared__ uint16_t bpos[kRankCap];
   __shared__ uint32_t tlo[kMaxRankedChunks], thi[kMaxRankedChunks], tboff[kMaxRankedChunks];
   __shared__ uint32_t scratch[kRankWaves + 1];
-  __shared__ uint32_t res[4];
+  __shared__ uint32_t res[5];
+  static_assert(kRecs <= kMaxRankedChunks, "records");
 
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
@@ -1117,17 +1264,23 @@ __global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
   const int64_t rec = (int64_t)q * R.nchunks;
   const uint32_t *kq = R.keys + (int64_t)q * R.n_stride;
   const uint16_t *pq = R.pos + (int64_t)q * R.n_stride;
-  // round 1, all independent of q_pos: the coarse tables (chunks past the
-  // query's are masked below) and the first kRankEarly keys of every chunk
-  // (thread t: entry t % kRankEarly of chunks t / kRankEarly + 4u), addresses
-  // clamped into the query's rows
-  const uint32_t cv = R.coarse[(rec + min(wave, R.nchunks - 1)) * (kHistBins / 64) + lane];
-  constexpr int kPer = kRankThreads / kRankEarly;   // chunks per early round: 4
-  const uint32_t ei = (uint32_t)(tid % kRankEarly);
+  // round 1, all independent of q_pos: the coarse tables (records a query
+  // does not reach are masked below) and the first `early` keys of every
+  // record (thread t: entry t % early of records t / early + 1024 u / early),
+  // addresses clamped into the query's rows
+  uint32_t cv[kRecPerWave];
+#pragma unroll
+  for (int k = 0; k < kRecPerWave; ++k)
+    cv[k] = R.coarse[(rec + min(wave + kRankWaves * k, R.nchunks - 1)) * (kHistBins / 64) + lane];
+  // early keys per record: 4096 / (a power of two >= the record count)
+  const int esh = R.nchunks <= 16 ? 8 : (R.nchunks <= 32 ? 7 : 6);
+  const uint32_t early = 1u << esh;
+  const uint32_t ei = (uint32_t)tid & (early - 1u);
   uint32_t ek[4], ep[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int64_t r = min((int64_t)(tid / kRankEarly + kPer * u) * C + ei, R.n_stride - 1);
+    const int c = (tid + kRankThreads * u) >> esh;
+    const int64_t r = min((int64_t)c * C + ei, R.n_stride - 1);
     ek[u] = kq[r];
     ep[u] = pq[r];
   }
@@ -1136,46 +1289,74 @@ __global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
   sel[2 * tid + 1] = 0u;
   tie[2 * tid] = 0u;
   tie[2 * tid + 1] = 0u;
-  // visible keys (q_pos < capacity; clamped to the records regardless)
-  const int64_t n = max((int64_t)1, min((int64_t)qp + 1, (int64_t)R.nchunks * C));
-  const int nch = (int)((n + C - 1) / C);
-  const uint32_t keff = (uint32_t)min((int64_t)R.kk, n);
+  // the bitmap's range (candidate indices) and the records this call wrote:
+  // a Full scan writes the chunks that hold visible positions (q_pos <
+  // capacity; clamped to the records regardless), a pool's every record
+  const bool pooled = R.pool != nullptr;   // uniform
+  const int64_t n = pooled ? (int64_t)R.pool_len
+                           : max((int64_t)1, min((int64_t)qp + 1, (int64_t)R.nchunks * C));
+  const int nch = pooled ? R.nchunks : (int)((n + C - 1) / C);
   const int nwords = (int)((n + 31) / 32);
   int32_t *oq = R.out + (int64_t)q * R.kk;
-  tabc[wave][lane] = wave < nch ? cv : 0u;
+  {
+    uint32_t t = 0u;
+#pragma unroll
+    for (int k = 0; k < kRecPerWave; ++k) {
+      const int c = wave + kRankWaves * k;
+      const uint32_t v = c < nch ? cv[k] : 0u;
+      tabc[c][lane] = v;
+      t += v;
+    }
+    tsum[wave][lane] = t;
+  }
   __syncthreads();
   if (wave == 0) {
     uint32_t t = 0u;
 #pragma unroll
-    for (int w = 0; w < (int)kMaxRankedChunks; ++w) t += tabc[w][lane];
-    const uint64_t b = __ballot(t >= keff);   // lane 0: t = n >= keff
-    if (lane == 0) res[0] = (uint32_t)__popcll(b) - 1u;
+    for (int w = 0; w < kRankWaves; ++w) t += tsum[w][lane];
+    // lane 0 holds the candidate count (every candidate is at or above bin 0)
+    const uint32_t ncand = (uint32_t)__builtin_amdgcn_readfirstlane(t);
+    const uint32_t kf = (uint32_t)min((int64_t)R.kk, (int64_t)ncand);
+    const uint64_t b = __ballot(t >= kf);
+    if (lane == 0) {
+      res[0] = (uint32_t)__popcll(b) - 1u;
+      res[4] = kf;
+    }
   }
   __syncthreads();
   const uint32_t J = res[0];
+  const uint32_t keff = res[4];
   // round 2
-  const uint32_t fv = R.ge[(rec + min(wave, nch - 1)) * kHistBins + 64 * J + lane];
-  tabf[wave][lane] = wave < nch ? fv : 0u;
+  {
+    uint32_t t = 0u;
+#pragma unroll
+    for (int k = 0; k < kRecPerWave; ++k) {
+      const int c = wave + kRankWaves * k;
+      const uint32_t v = c < nch ? R.ge[(rec + min(c, nch - 1)) * kHistBins + 64 * J + lane] : 0u;
+      tabf[c][lane] = v;
+      t += v;
+    }
+    tsum[wave][lane] = t;   // (wave 0 read the round-1 sums before the barrier above)
+  }
   __syncthreads();
   if (wave == 0) {
     uint32_t t = 0u;
 #pragma unroll
-    for (int w = 0; w < (int)kMaxRankedChunks; ++w) t += tabf[w][lane];
+    for (int w = 0; w < kRankWaves; ++w) t += tsum[w][lane];
     const uint32_t L = (uint32_t)__popcll(__ballot(t >= keff)) - 1u;
-    // lanes 0..15: chunk `lane`'s keys in bin b1 or above (hi) and above it (lo)
-    const int c = lane & ((int)kMaxRankedChunks - 1);
-    const uint32_t hi = tabf[c][L];
-    const uint32_t lo = L < 63u ? tabf[c][L + 1] : (J < 63u ? tabc[c][J + 1] : 0u);
-    const bool mine = lane < (int)kMaxRankedChunks;
-    const uint32_t a = mine ? lo : 0u, bb = mine ? hi - lo : 0u;
+    // lane c: record c's keys in bin b1 or above (hi) and above it (lo)
+    const int c = lane;
+    const bool mine = c < nch;
+    const int cr = min(c, kRecs - 1);   // (rows past kRecs are not read: mine is false there)
+    const uint32_t hi = mine ? tabf[cr][L] : 0u;
+    const uint32_t lo = !mine ? 0u : (L < 63u ? tabf[cr][L + 1] : (J < 63u ? tabc[cr][J + 1] : 0u));
+    const uint32_t a = lo, bb = hi - lo;
     const uint32_t ia = wave_inclusive_scan(a);
     const uint32_t ib = wave_inclusive_scan(bb);
-    if (mine) {
-      tlo[c] = lo;
-      thi[c] = hi;
-      tboff[c] = ib - bb;
-    }
-    const bool more = __ballot(mine && hi > (uint32_t)kRankEarly) != 0ull;
+    tlo[c] = lo;
+    thi[c] = hi;
+    tboff[c] = ib - bb;
+    const bool more = __ballot(hi > early) != 0ull;
     if (lane == kWave - 1) {
       res[0] = 64u * J + L;
       res[1] = ia;   // keys above bin b1
@@ -1185,18 +1366,18 @@ __global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
   }
   __syncthreads();
   const uint32_t b1 = res[0], above = res[1], T = res[2];
-  const bool more = res[3] != 0u;   // some chunk needs keys past the early ones
+  const bool more = res[3] != 0u;   // some record needs keys past the early ones
   const bool in_lds = T <= (uint32_t)kRankCap;   // uniform
-  // round 3: the early keys, then any a chunk needs beyond them
+  // round 3: the early keys, then any a record needs beyond them
   if (keff > 0u) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = tid / kRankEarly + kPer * u;
+      const int c = (tid + kRankThreads * u) >> esh;
       if (c < nch) ranked_take(ei, c, C, ek[u], ep[u], tlo, thi, tboff, in_lds, sel, bkey, bpos);
     }
     for (int c = 0; more && c < nch; ++c) {
       const uint32_t h = thi[c];   // uniform
-      for (uint32_t i = kRankEarly + tid; i < h; i += kRankThreads) {
+      for (uint32_t i = early + tid; i < h; i += kRankThreads) {
         const int64_t r = (int64_t)c * C + i;
         ranked_take(i, c, C, kq[r], pq[r], tlo, thi, tboff, in_lds, sel, bkey, bpos);
       }
@@ -1206,22 +1387,34 @@ __global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
     if (in_lds)
       ranked_refine(RankedBinLds{bkey, bpos}, T, b1, need, hist, sel, tie, nwords, scratch, res);
     else
-      ranked_refine(RankedBinGlobal{kq, pq, RankedTabs{tlo, thi, tboff, C}}, T, b1, need, hist,
-                    sel, tie, nwords, scratch, res);
+      ranked_refine(RankedBinGlobal{kq, pq, RankedTabs{tlo, thi, tboff, C, nch}}, T, b1, need,
+                    hist, sel, tie, nwords, scratch, res);
   }
-  // the selection in position order: thread t emits positions 64t .. 64t+63
+  // the selection in index order: thread t emits indices 64t .. 64t+63 (a
+  // pool's entries are in ascending position order); pool entries are looked
+  // up after the indices are placed (through LDS, all loads at once)
   const int w0 = 2 * tid;
   uint32_t m[2] = {w0 < nwords ? sel[w0] : 0u, w0 + 1 < nwords ? sel[w0 + 1] : 0u};
   uint32_t total;
   uint32_t o = block_exclusive_scan((uint32_t)(__popc(m[0]) + __popc(m[1])), scratch, total);
+  const bool via_lds = pooled && keff <= (uint32_t)kRankCap;   // uniform
+  const int32_t *prow = pooled ? R.pool + (int64_t)q * R.pool_len : nullptr;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     while (m[e] != 0u) {
       const int b = __ffs(m[e]) - 1;
       m[e] &= m[e] - 1u;
-      if (o < keff) oq[o] = 32 * (w0 + e) + b;
+      const int32_t id = 32 * (w0 + e) + b;
+      if (o < keff) {
+        if (via_lds) bkey[o] = (uint32_t)id;
+        else oq[o] = pooled ? prow[id] : id;
+      }
       ++o;
     }
+  }
+  if (via_lds) {
+    __syncthreads();
+    for (uint32_t i = tid; i < keff; i += kRankThreads) oq[i] = prow[bkey[i]];
   }
   for (int64_t i = (int64_t)keff + tid; i < R.kk; i += kRankThreads) oq[i] = -1;
 }
@@ -1292,7 +1485,16 @@ void launch_score(const IndexArgs &a, int64_t n_cand_max, hipStream_t s) {
 
 template <int H, bool kFp8>
 void launch_score_mode(const IndexArgs &a, int64_t n, bool pool, bool reindex_pool, hipStream_t s) {
-  if (reindex_pool) {
+  if (reindex_pool && a.layout.tok.hsrc == kRanked) {
+    const TopkWorkspace &L = a.layout;
+    hipLaunchKernelGGL((gather_rank_kernel<H, kFp8>), dim3((unsigned)L.tok.nchunks, (unsigned)a.nq),
+                       dim3(kGatherThreads), 0, s, static_cast<const uint8_t *>(a.cache->idx_k),
+                       (int64_t)a.cache->capacity, a.q_idx, a.q_fp8, a.q_seq, a.q_pos, a.pool_in,
+                       a.pool_len, reinterpret_cast<uint32_t *>(a.ws + L.tok.keys), L.tok.n,
+                       reinterpret_cast<uint16_t *>(a.ws + L.tok.rk_pos),
+                       reinterpret_cast<uint16_t *>(a.ws + L.tok.rk_ge),
+                       reinterpret_cast<uint16_t *>(a.ws + L.tok.rk_coarse));
+  } else if (reindex_pool) {
     const TopkWorkspace &L = a.layout;
     constexpr int kEntries = kGatherThreads / H;
     hipLaunchKernelGGL((gather_score_kernel<H, kFp8>),
@@ -1419,9 +1621,13 @@ TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t
   const int64_t n_tok = reindex_pool ? (int64_t)pool_len : (int64_t)c.capacity;
   size_t off;
   const int32_t chunk = score_chunk(nq, n_tok, false);
-  if (!reindex_pool && !pool && chunk >= 2048 && (n_tok + chunk - 1) / chunk <= kMaxRankedChunks) {
+  if (!reindex_pool && !pool && chunk >= 2048 && n_tok <= kMaxRankedKeys &&
+      (n_tok + chunk - 1) / chunk <= kMaxRankedChunks) {
     // a handful of scorer chunks per query: ranked chunk records
     off = carve_ranked(w.tok, n_tok, nq, chunk);
+  } else if (reindex_pool && (int64_t)pool_len <= kMaxRankedChunks * kGatherRec) {
+    // a pool of up to 64 runs of kGatherRec entries: ranked records
+    off = carve_ranked(w.tok, pool_len, nq, kGatherRec);
   } else {
     // the token and block histograms are filled by the same scorer launch and
     // cleared by one launch: the same number of copies
@@ -1498,9 +1704,14 @@ hipError_t launch_index_topk(const IndexArgs &a_in, hipStream_t s) {
                       reinterpret_cast<const uint16_t *>(a.ws + L.tok.rk_pos),
                       reinterpret_cast<const uint16_t *>(a.ws + L.tok.rk_ge),
                       reinterpret_cast<const uint16_t *>(a.ws + L.tok.rk_coarse),
-                      L.tok.n, L.tok.nchunks, L.tok.chunk, a.topk_out, a.top_k};
-    hipLaunchKernelGGL(ranked_select_kernel, dim3((unsigned)a.nq), dim3(kRankThreads), 0, s, R,
-                       a.q_pos);
+                      L.tok.n, L.tok.nchunks, L.tok.chunk, a.topk_out, a.top_k,
+                      reindex_pool ? a.pool_in : nullptr, a.pool_len};
+    if (L.tok.nchunks <= kRankWaves)
+      hipLaunchKernelGGL(ranked_select_kernel<1>, dim3((unsigned)a.nq), dim3(kRankThreads), 0, s, R,
+                         a.q_pos);
+    else
+      hipLaunchKernelGGL(ranked_select_kernel<4>, dim3((unsigned)a.nq), dim3(kRankThreads), 0, s, R,
+                         a.q_pos);
     return hipGetLastError();
   }
   SelProblems P;
