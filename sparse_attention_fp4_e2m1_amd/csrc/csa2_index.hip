@@ -1252,6 +1252,7 @@ __global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
   __shared__ uint32_t bkey[kRankCap];
   __shared__ uint16_t bpos[kRankCap];
   __shared__ uint32_t tlo[kMaxRankedChunks], thi[kMaxRankedChunks], tboff[kMaxRankedChunks];
+  __shared__ uint32_t txoff[kMaxRankedChunks];
   __shared__ uint32_t scratch[kRankWaves + 1];
   __shared__ uint32_t res[5];
   static_assert(kRecs <= kMaxRankedChunks, "records");
@@ -1356,17 +1357,20 @@ __global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
     tlo[c] = lo;
     thi[c] = hi;
     tboff[c] = ib - bb;
-    const bool more = __ballot(hi > early) != 0ull;
+    // the keys a record needs past its early ones, as one list (record by record)
+    const uint32_t ex = hi > early ? hi - early : 0u;
+    const uint32_t ix = wave_inclusive_scan(ex);
+    txoff[c] = ix - ex;
     if (lane == kWave - 1) {
       res[0] = 64u * J + L;
       res[1] = ia;   // keys above bin b1
       res[2] = ib;   // keys in bin b1
-      res[3] = more ? 1u : 0u;
+      res[3] = ix;   // keys past the early ones
     }
   }
   __syncthreads();
   const uint32_t b1 = res[0], above = res[1], T = res[2];
-  const bool more = res[3] != 0u;   // some record needs keys past the early ones
+  const uint32_t nextra = res[3];   // keys some records need past their early ones
   const bool in_lds = T <= (uint32_t)kRankCap;   // uniform
   // round 3: the early keys, then any a record needs beyond them
   if (keff > 0u) {
@@ -1375,12 +1379,31 @@ __global__ void __launch_bounds__(kRankThreads) ranked_select_kernel(
       const int c = (tid + kRankThreads * u) >> esh;
       if (c < nch) ranked_take(ei, c, C, ek[u], ep[u], tlo, thi, tboff, in_lds, sel, bkey, bpos);
     }
-    for (int c = 0; more && c < nch; ++c) {
-      const uint32_t h = thi[c];   // uniform
-      for (uint32_t i = early + tid; i < h; i += kRankThreads) {
-        const int64_t r = (int64_t)c * C + i;
-        ranked_take(i, c, C, kq[r], pq[r], tlo, thi, tboff, in_lds, sel, bkey, bpos);
+    // entry f of the list: the last record whose offset reaches f (records
+    // needing none share the next one's offset), by a binary search over the
+    // offsets; all of a thread's loads issue together
+    for (uint32_t f0 = 0; f0 < nextra; f0 += 4 * kRankThreads) {   // uniform
+      uint32_t xk[4], xp[4];
+      int xc[4];
+      uint32_t xi[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t f = min(f0 + tid + u * kRankThreads, nextra - 1u);
+        int lo = 0, hi = nch - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (txoff[mid] <= f) lo = mid; else hi = mid - 1;
+        }
+        xc[u] = lo;
+        xi[u] = early + (f - txoff[lo]);
+        const int64_t r = (int64_t)lo * C + xi[u];
+        xk[u] = kq[r];
+        xp[u] = pq[r];
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (f0 + tid + u * kRankThreads < nextra)
+          ranked_take(xi[u], xc[u], C, xk[u], xp[u], tlo, thi, tboff, in_lds, sel, bkey, bpos);
     }
     __syncthreads();
     const uint32_t need = keff - above;   // >= 1: the keff-th key lies in bin b1
