@@ -558,6 +558,97 @@ __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
   if (tid == 0) thr[q] = prefix << 16;
 }
 
+// acc + [w >= cm1 + 1] per 16-bit half: a clamped packed subtract, a packed
+// min with 1 and a packed add. Written out: the compiler would otherwise turn
+// the pair into two compares and selects per word.
+__device__ __forceinline__ uint32_t pk_count_ge(uint32_t acc, uint32_t w, uint32_t cm1,
+                                                uint32_t one) {
+  uint32_t t;
+  asm("v_pk_sub_u16 %1, %2, %3 clamp\n\t"
+      "v_pk_min_u16 %1, %1, %4\n\t"
+      "v_pk_add_u16 %0, %0, %1"
+      : "+v"(acc), "=&v"(t)
+      : "v"(w), "v"(cm1), "v"(one));
+  return acc;
+}
+
+// The same threshold with one wave per query (four queries per workgroup)
+// for rows of at most kKthWaveMax block maxima: lane l holds the values
+// 8 (u 64 + l) .. +7 of groups u = 0 .. kKthWaveGroups - 1 in registers (past
+// the row's end: 0), and a bit costs three packed operations per word (two
+// values) and a wave sum -- no barrier anywhere. Bits that the row's largest
+// and smallest values share are taken from them without a pass.
+constexpr int kKthWaveGroups = 20;
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+constexpr int64_t kKthWaveMax = 8 * kWave * kKthWaveGroups;   // 10240 blocks: 163840 positions
+
+__global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
+    const uint16_t *__restrict__ bmax, int64_t bmax_row, const int32_t *__restrict__ q_pos,
+    int32_t nq, int32_t top_k, uint32_t *__restrict__ thr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int q = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (q >= nq) return;   // uniform per wave
+  // at most kKthWaveMax: the host launches this kernel only for such rows
+  const int nblk = (q_pos[q] + kBlk) / kBlk;
+  if (nblk < top_k) {
+    if (lane == 0) thr[q] = 0u;
+    return;
+  }
+  const uint16_t *bq = bmax + (int64_t)q * bmax_row;
+  const int ngroups = (nblk + 8 * kWave - 1) / (8 * kWave);   // uniform
+  const int last8 = (nblk - 1) / 8 * 8;                       // the row's last group of 8
+  uint32_t v[4 * kKthWaveGroups];
+  u16x2 vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};   // over the row's values only
+#pragma unroll
+  for (int u = 0; u < kKthWaveGroups; ++u) {
+    // branch-free: groups past the row read its last group and are masked
+    const int i = 8 * (u * kWave + lane);
+    const uint4 w = *reinterpret_cast<const uint4 *>(bq + min(i, last8));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = i + 2 * k < nblk ? 0x0000FFFFu : 0u;
+      const uint32_t hi = i + 2 * k + 1 < nblk ? 0xFFFF0000u : 0u;
+      v[4 * u + k] = ws[k] & (lo | hi);
+      vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, v[4 * u + k]));
+      vmin = __builtin_elementwise_min(vmin, __builtin_bit_cast(u16x2, ws[k] | ~(lo | hi)));
+    }
+  }
+  int hi_v = max((int)vmax.x, (int)vmax.y), lo_v = min((int)vmin.x, (int)vmin.y);
+  for (int d = 32; d >= 1; d >>= 1) {
+    hi_v = max(hi_v, __shfl_xor(hi_v, d, kWave));
+    lo_v = min(lo_v, __shfl_xor(lo_v, d, kWave));
+  }
+  // Every value lies in [lo_v, hi_v], so the K-th largest shares the bits
+  // above the highest one where the two differ: the search starts there, with
+  // at least K values (all nblk of them) at or above the starting prefix.
+  const uint32_t diff = (uint32_t)(hi_v ^ lo_v);
+  const int top = diff ? 31 - __builtin_clz(diff) : -1;
+  uint32_t prefix = (uint32_t)hi_v & ~(diff ? (2u << top) - 1u : 0u);
+  const uint32_t k = (uint32_t)top_k;
+  const uint32_t one = 0x00010001u;
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    // both halves at once: max(w - (cand - 1), 0) is nonzero exactly when
+    // w >= cand; clamped to 1 and summed per half (at most 80 per half)
+    const uint32_t cm1 = (cand - 1u) * 0x00010001u;
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int u = 0; u < kKthWaveGroups; ++u) {
+      if (u < ngroups) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc = pk_count_ge(acc, v[4 * u + e], cm1, one);
+        }
+      }
+    }
+    const uint32_t c = (acc & 0xFFFFu) + (acc >> 16);
+    const uint32_t total = __builtin_amdgcn_readlane(wave_inclusive_scan(c), kWave - 1);
+    if (total >= k) prefix = cand;
+  }
+  if (lane == 0) thr[q] = prefix << 16;
+}
+
 // Per query: the exact Top-K among the candidates of its slot regions.  The
 // first radix bin comes from the candidates themselves: every key above the
 // K-th largest is a candidate, so the candidates' histogram above that bin is
@@ -703,9 +794,14 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
   if (before != nullptr) (void)hipEventRecord(before, s);
   if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 1, s);
   else launch_gemm_scores<4>(a, L, 1, s);
-  hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
-                     reinterpret_cast<const uint16_t *>(w + L.bmax), L.bmax_row, a.q_pos, a.top_k,
-                     reinterpret_cast<uint32_t *>(w + L.thr));
+  if ((c.capacity + kBlk - 1) / kBlk <= kKthWaveMax)   // every row fits one wave's registers
+    hipLaunchKernelGGL(gemm_kth_wave_kernel, dim3((unsigned)((a.nq + 3) / 4)), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t *>(w + L.bmax), L.bmax_row, a.q_pos, a.nq,
+                       a.top_k, reinterpret_cast<uint32_t *>(w + L.thr));
+  else
+    hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
+                       reinterpret_cast<const uint16_t *>(w + L.bmax), L.bmax_row, a.q_pos, a.top_k,
+                       reinterpret_cast<uint32_t *>(w + L.thr));
   if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 2, s);
   else launch_gemm_scores<4>(a, L, 2, s);
   // the profiling events cover both product passes and the threshold between them
