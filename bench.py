@@ -539,7 +539,9 @@ def proj_item(steps, warmup, hip, d_model=4096):
         tf = flops / (ms * 1e-3) / 1e12
         gb = nbytes / (ms * 1e-3) / 1e9
         res[f"tokens_{n}"] = {"avg_launch_ms": ms, "tokens_per_s": n / (ms * 1e-3),
-                              "roofline": {"bound": "mfma", "kernel": "proj_append_kernel",
+                              "roofline": {"bound": "mfma",
+                                           "kernel": "proj_tile_kernel" if n >= 512
+                                           else "proj_append_kernel",
                                            "achieved": tf, "peak": BF16_PEAK_TFLOPS,
                                            "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
                                            "traffic": None, "flops_per_launch": flops},

@@ -358,6 +358,8 @@ csa2_status csa2_sparse_local_attn(const csa2_cache *cache, const csa2_local_cac
  * (nearest, ties to even); y's channels are K (0..127), V (128..255) and the
  * index keys (256 .. 256 + idx_heads * 64 - 1, head-major); they are then
  * quantized and stored exactly as csa2_kv_append stores those bf16 rows.
+ * The fp32 summation order depends on d_model only: a token's bytes do not
+ * depend on n or on the other tokens of the call.
  *   x          [n][d_model] bf16 bits, the hidden states.
  *   w          [256 + idx_heads * 64][d_model] bf16 bits, the projection
  *              weights, one row per output channel.

@@ -53,7 +53,7 @@ def _run(heads, dtype, n, d_model, grid=True, seed=0, capacity=512):
 
 @pytest.mark.parametrize("heads,dtype", [(8, "fp8"), (4, "bf16")])
 @pytest.mark.parametrize("n,d_model", [(1, 32), (100, 512), (200, 1056), (64, 4096), (257, 96),
-                                       (300, 512), (1000, 1056)])
+                                       (300, 512), (1000, 1056), (600, 96), (1024, 4096)])
 def test_proj_append_bit_exact_on_exact_sums(heads, dtype, n, d_model):
     announce(f"proj append heads={heads} idx={dtype} n={n} d={d_model}")
     got, want = _run(heads, dtype, n, d_model, seed=n + d_model)
@@ -62,9 +62,9 @@ def test_proj_append_bit_exact_on_exact_sums(heads, dtype, n, d_model):
 
 
 @pytest.mark.parametrize("heads,dtype", [(8, "fp8"), (4, "bf16")])
-@pytest.mark.parametrize("n,d_model", [(300, 2048), (40, 4096), (7, 1056)])
+@pytest.mark.parametrize("n,d_model", [(300, 2048), (40, 4096), (7, 1056), (700, 2080)])
 def test_proj_append_random_inputs_per_element(heads, dtype, n, d_model):
-    # both launch shapes (from 256 tokens up, and below)
+    # every launch shape (below 256 tokens, from 256, from 512)
     announce(f"proj append random inputs heads={heads} idx={dtype} n={n} d={d_model}")
     (x, w), (codes, scales, idx) = _run(heads, dtype, n, d_model, grid=False, seed=11 + n)
     amb = check_projection_bytes(x, w, heads, dtype, codes, scales, idx)
@@ -72,8 +72,9 @@ def test_proj_append_random_inputs_per_element(heads, dtype, n, d_model):
 
 
 def test_proj_append_bytes_do_not_depend_on_the_call():
-    # 32 random rows projected alone (small-call tiles) and at offsets 0, 5 and
-    # 261 inside 300-row calls (large-call tiles): identical bytes
+    # 32 random rows projected alone (small-call tiles), at offsets 0, 5 and
+    # 261 inside 300-row calls (64 x 64 tiles) and at offsets 0 and 600 inside
+    # 700-row calls (128 x 128 tiles): identical bytes
     m = lib()
     rng = np.random.default_rng(7)
     d_model, heads = 2048, 8
@@ -81,11 +82,11 @@ def test_proj_append_bytes_do_not_depend_on_the_call():
     rows = synth.f32_to_bf16_bits(rng.standard_normal((32, d_model)).astype(np.float32))
     w = dev_u16(synth.f32_to_bf16_bits((rng.standard_normal((ch, d_model)) / np.sqrt(d_model)).astype(np.float32)))
     results = []
-    for off, n in ((0, 32), (0, 300), (5, 300), (261, 300)):
+    for off, n in ((0, 32), (0, 300), (5, 300), (261, 300), (0, 700), (600, 700)):
         announce(f"proj append rows at offset {off} of a {n}-row call")
         x = synth.f32_to_bf16_bits(rng.standard_normal((n, d_model)).astype(np.float32))
         x[off:off + 32] = rows
-        gc = m.Cache(1, 512, idx_heads=heads, idx_k_dtype="fp8")
+        gc = m.Cache(1, 1024, idx_heads=heads, idx_k_dtype="fp8")
         m.csa2_proj_append(gc, dev_u16(x), w, dev_i32(np.zeros(n)), dev_i32(np.arange(n)))
         torch.cuda.synchronize()
         sl = slice(off, off + 32)
