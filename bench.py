@@ -332,8 +332,8 @@ def measure(name, steps, warmup, hip, use_graph):
         flops = run.scan_flops()
         ach = flops / (scan_ms * 1e-3) / 1e12
         res["roofline"] = {"bound": "mfma",
-                           "kernel": "gemm_score_kernel passes 1 and 2 + gemm_kth_kernel "
-                                     "(fp8 index product, counted once)",
+                           "kernel": "gemm_score_kernel passes 1 and 2 + the threshold kernel "
+                                     "between them (fp8 index product, counted once)",
                            "achieved": ach, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": ach / FP8_PEAK_TFLOPS, "traffic": None,
                            "flops_per_launch": flops, "avg_launch_ms": scan_ms}
