@@ -220,7 +220,6 @@ __global__ void __launch_bounds__(256) proj_tile_kernel(
     int32_t capacity, int32_t H, int32_t esz, int32_t nrt, int32_t nct) {
   constexpr int kWN = kBN / 2;                            // columns per wave
   constexpr int kCT = kWN / 16;                           // 16-column tiles per wave
-  constexpr int kPOpBytes = kPT * kPK * 2;                // the token rows of a stage: 32 KB
   constexpr int kPStageBytes = (kPT + kBN) * kPK * 2;     // 56 or 64 KB
   constexpr int kPLoads = kPStageBytes / 16 / 256;        // 16-B pieces per thread per stage
   constexpr int kPPitch = kBN + 4;                        // epilogue: fp32 rows (64 at a time)

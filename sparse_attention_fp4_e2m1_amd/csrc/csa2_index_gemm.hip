@@ -53,6 +53,15 @@ constexpr int kGemmTargetGroups = 256;  // workgroups aimed for (one per CU)
 constexpr int kBlk = 16;                // positions per block maximum (one row tile)
 constexpr int kBlkGroup = 16;           // block maxima a lane collects before one 32-B store
 constexpr int kRangeAlign = kBlk * kBlkGroup;   // positions per range: a multiple of this
+
+// The block maxima are stored group-major: the kBlkGroup values of block
+// group g of query q at [g][q][0 .. kBlkGroup), so that the 64 lanes of a
+// wave (64 consecutive queries) store one contiguous 2 KB run per group.
+// Block i of query q:
+__device__ __forceinline__ const uint16_t *bmax_at(const uint16_t *bmax, int32_t nq, int q,
+                                                   int64_t i) {
+  return bmax + ((i / kBlkGroup) * nq + q) * kBlkGroup + i % kBlkGroup;
+}
 constexpr int kDmaPerTile = 2;          // next-stage pieces a thread loads per row tile
 constexpr int kKthThreads = 256;
 // Candidates a gemm_resolve_kernel keeps in LDS: ~K(1 + 10 %) with continuous
@@ -141,7 +150,7 @@ template <int H, int kPass>
 __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const uint8_t *__restrict__ idx_k, int64_t capacity, const uint8_t *__restrict__ q8,
     const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos, int32_t nq,
-    const uint32_t *__restrict__ plan, uint16_t *__restrict__ bmax, int64_t bmax_row,
+    const uint32_t *__restrict__ plan, uint16_t *__restrict__ bmax,
     const uint32_t *__restrict__ thr, uint2 *__restrict__ cand, int64_t cand_stride,
     uint32_t *__restrict__ cnt, int32_t nranges) {
   constexpr int kGemmStage = kPass == 1 ? CSA2_GEMM_STAGE1 : CSA2_GEMM_STAGE2;
@@ -436,8 +445,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
           const int q = qbase + wave * 64 + lane;     // column tile grp, column col
           const bool own_act = grp == 0 ? act[0] : grp == 1 ? act[1] : grp == 2 ? act[2] : act[3];
           if (q < nq && own_act) {
-            const int g0 = (pt / kBlk) / kBlkGroup * kBlkGroup;
-            uint4 *dst = reinterpret_cast<uint4 *>(bmax + (int64_t)q * bmax_row + g0);
+            const int64_t g = (pt / kBlk) / kBlkGroup;   // the group's index
+            uint4 *dst = reinterpret_cast<uint4 *>(bmax + (g * nq + q) * kBlkGroup);
             dst[0] = make_uint4(sreg[0], sreg[1], sreg[2], sreg[3]);
             dst[1] = make_uint4(sreg[4], sreg[5], sreg[6], sreg[7]);
           }
@@ -491,7 +500,7 @@ __device__ __forceinline__ uint32_t kth_block_sum(uint32_t c, uint32_t (*part)[k
 }
 
 __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
-    const uint16_t *__restrict__ bmax, int64_t bmax_row, const int32_t *__restrict__ q_pos,
+    const uint16_t *__restrict__ bmax, int32_t nq, const int32_t *__restrict__ q_pos,
     int32_t top_k, uint32_t *__restrict__ thr) {
   __shared__ uint32_t part[2][kKthThreads / kWave];
   const int q = blockIdx.x;
@@ -501,7 +510,6 @@ __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
     if (tid == 0) thr[q] = 0u;
     return;
   }
-  const uint16_t *bq = bmax + (int64_t)q * bmax_row;
   const uint32_t k = (uint32_t)top_k;
   uint32_t prefix = 0u;
   if (nblk <= kKthRegMax) {
@@ -513,7 +521,7 @@ __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
       const int64_t i = 8 * ((int64_t)u * kKthThreads + tid);
       uint4 w = make_uint4(0u, 0u, 0u, 0u);
       if (u < ngroups && i < nblk) {
-        w = *reinterpret_cast<const uint4 *>(bq + i);
+        w = *reinterpret_cast<const uint4 *>(bmax_at(bmax, nq, q, i));
         if (i + 8 > nblk) {   // the row's last group: values past its end count as 0
           uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -545,12 +553,12 @@ __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
       const uint32_t cand = prefix | (1u << bit);
       uint32_t c = 0u;
       for (int64_t i = (int64_t)tid * 8; i < n8; i += kKthThreads * 8) {
-        const uint4 w = *reinterpret_cast<const uint4 *>(bq + i);
+        const uint4 w = *reinterpret_cast<const uint4 *>(bmax_at(bmax, nq, q, i));
         c += kth_count_word(w.x, cand) + kth_count_word(w.y, cand) + kth_count_word(w.z, cand) +
              kth_count_word(w.w, cand);
       }
       if (n8 < nblk && tid == (int)((n8 / 8) % kKthThreads)) {
-        for (int64_t i = n8; i < nblk; ++i) c += bq[i] >= cand ? 1u : 0u;
+        for (int64_t i = n8; i < nblk; ++i) c += *bmax_at(bmax, nq, q, i) >= cand ? 1u : 0u;
       }
       if (kth_block_sum(c, part, bit & 1) >= k) prefix = cand;
     }
@@ -583,8 +591,8 @@ typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 constexpr int64_t kKthWaveMax = 8 * kWave * kKthWaveGroups;   // 10240 blocks: 163840 positions
 
 __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
-    const uint16_t *__restrict__ bmax, int64_t bmax_row, const int32_t *__restrict__ q_pos,
-    int32_t nq, int32_t top_k, uint32_t *__restrict__ thr) {
+    const uint16_t *__restrict__ bmax, const int32_t *__restrict__ q_pos, int32_t nq,
+    int32_t top_k, uint32_t *__restrict__ thr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int q = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
   if (q >= nq) return;   // uniform per wave
@@ -594,7 +602,6 @@ __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
     if (lane == 0) thr[q] = 0u;
     return;
   }
-  const uint16_t *bq = bmax + (int64_t)q * bmax_row;
   const int ngroups = (nblk + 8 * kWave - 1) / (8 * kWave);   // uniform
   const int last8 = (nblk - 1) / 8 * 8;                       // the row's last group of 8
   uint32_t v[4 * kKthWaveGroups];
@@ -603,7 +610,7 @@ __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
   for (int u = 0; u < kKthWaveGroups; ++u) {
     // branch-free: groups past the row read its last group and are masked
     const int i = 8 * (u * kWave + lane);
-    const uint4 w = *reinterpret_cast<const uint4 *>(bq + min(i, last8));
+    const uint4 w = *reinterpret_cast<const uint4 *>(bmax_at(bmax, nq, q, min(i, last8)));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -741,7 +748,7 @@ void launch_gemm_scores(const IndexArgs &a, const GemmWorkspace &L, int pass, hi
                        static_cast<const uint8_t *>(c.idx_k), (int64_t)c.capacity,
                        reinterpret_cast<const uint8_t *>(w + L.q8), a.q_seq, a.q_pos, a.nq,
                        reinterpret_cast<const uint32_t *>(w + L.plan),
-                       reinterpret_cast<uint16_t *>(w + L.bmax), L.bmax_row,
+                       reinterpret_cast<uint16_t *>(w + L.bmax),
                        reinterpret_cast<const uint32_t *>(w + L.thr),
                        reinterpret_cast<uint2 *>(w + L.cand), L.cand_stride,
                        reinterpret_cast<uint32_t *>(w + L.cnt), L.nranges);
@@ -796,11 +803,11 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
   else launch_gemm_scores<4>(a, L, 1, s);
   if ((c.capacity + kBlk - 1) / kBlk <= kKthWaveMax)   // every row fits one wave's registers
     hipLaunchKernelGGL(gemm_kth_wave_kernel, dim3((unsigned)((a.nq + 3) / 4)), dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t *>(w + L.bmax), L.bmax_row, a.q_pos, a.nq,
-                       a.top_k, reinterpret_cast<uint32_t *>(w + L.thr));
+                       reinterpret_cast<const uint16_t *>(w + L.bmax), a.q_pos, a.nq, a.top_k,
+                       reinterpret_cast<uint32_t *>(w + L.thr));
   else
     hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
-                       reinterpret_cast<const uint16_t *>(w + L.bmax), L.bmax_row, a.q_pos, a.top_k,
+                       reinterpret_cast<const uint16_t *>(w + L.bmax), a.nq, a.q_pos, a.top_k,
                        reinterpret_cast<uint32_t *>(w + L.thr));
   if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 2, s);
   else launch_gemm_scores<4>(a, L, 2, s);

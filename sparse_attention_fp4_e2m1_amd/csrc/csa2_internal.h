@@ -57,7 +57,7 @@ struct GemmWorkspace {
   size_t q8 = 0;           // uint8  [nq][idx_heads * 64]   E4M3 index queries
   size_t plan = 0;         // uint32 [1]  positions per range
   size_t thr = 0;          // uint32 [nq] candidate threshold key
-  size_t bmax = 0;         // uint16 [nq][bmax_row]  block maxima of 16 positions (top 16 key bits)
+  size_t bmax = 0;         // uint16 [bmax_row / 16][nq][16]  block maxima of 16 positions (top 16 key bits), group-major
   size_t cnt = 0;          // uint32 [nq][nranges]  candidates per (query, range)
   size_t cand = 0;         // uint2  [nq][cand_stride]  (score key, position)
   int64_t bmax_row = 0;
