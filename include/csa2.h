@@ -175,6 +175,9 @@ size_t csa2_index_topk_workspace(const csa2_cache *cache, csa2_mode mode, int32_
  * Errors: CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_UNSUPPORTED, CSA2_ERR_ARG
  * (pool_out missing with pool_blocks > 0, pool arguments in the wrong mode,
  * reuse_src missing in REUSE), CSA2_ERR_WORKSPACE, CSA2_ERR_HIP.
+ * nq = 0 is a no-op returning CSA2_OK (after the checks of mode, top_k and
+ * the pool sizes); the query, list, pool and workspace pointers may then be
+ * NULL.
  */
 csa2_status csa2_index_topk(const csa2_cache *cache, csa2_mode mode, const uint16_t *q_idx,
                             csa2_dtype q_dtype, const int32_t *q_seq, const int32_t *q_pos,

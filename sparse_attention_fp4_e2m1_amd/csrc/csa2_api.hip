@@ -117,6 +117,12 @@ csa2_status index_topk(const csa2_cache *cache, int32_t mode, const uint16_t *q_
                        const AppendRows &ap) {
   csa2_status st = check_topk_args(cache, mode, nq, top_k, pool_len, pool_blocks);
   if (st != CSA2_OK) return st;
+  if (nq == 0) {   // no queries: the pointers of the index call may be NULL
+    if (ap.n > 0 && launch_kv_append(*cache, ap.k, ap.v, ap.idx_in, ap.seq, ap.pos, ap.n,
+                                     (hipStream_t)stream) != hipSuccess)
+      return CSA2_ERR_HIP;
+    return CSA2_OK;
+  }
   if (topk_out == nullptr) return CSA2_ERR_NULL;
   if (mode == CSA2_REUSE) {
     if (reuse_src == nullptr) return CSA2_ERR_ARG;
@@ -132,12 +138,6 @@ csa2_status index_topk(const csa2_cache *cache, int32_t mode, const uint16_t *q_
       if (pool_out != nullptr) return CSA2_ERR_ARG;
       if ((pool_in == nullptr) != (pool_len == 0)) return CSA2_ERR_ARG;
     }
-  }
-  if (nq == 0) {
-    if (ap.n > 0 && launch_kv_append(*cache, ap.k, ap.v, ap.idx_in, ap.seq, ap.pos, ap.n,
-                                     (hipStream_t)stream) != hipSuccess)
-      return CSA2_ERR_HIP;
-    return CSA2_OK;
   }
   IndexArgs a;
   a.cache = cache;

@@ -676,7 +676,8 @@ __global__ void __launch_bounds__(kWaves * 64) local_attn_kernel(
 // gathers overlap) when that still leaves kTwoSubMinGroups workgroups.
 int32_t rows_per_split(int32_t nq, int32_t top_k, int32_t max_splits) {
   const int32_t subs = (top_k + kSub - 1) / kSub;
-  int32_t splits = std::min((kTargetGroups + nq - 1) / nq, max_splits);
+  const int32_t nq1 = std::max(nq, 1);   // a size query may ask for no queries
+  int32_t splits = std::min((kTargetGroups + nq1 - 1) / nq1, max_splits);
   splits = std::max(1, std::min(splits, subs));
   if (subs / splits < 2 && (int64_t)nq * (subs / 2) >= kTwoSubMinGroups)
     splits = std::max(1, subs / 2);

@@ -732,7 +732,7 @@ __global__ void __launch_bounds__(kGemmResolveThreads) gemm_resolve_kernel(
 // Position ranges per query group: enough workgroups for the chip, a multiple
 // of 8 (one XCD per range), and no more ranges than the capacity fills.
 int32_t gemm_ranges(int32_t nq, int32_t capacity) {
-  const int32_t groups = (nq + kGemmQ - 1) / kGemmQ;
+  const int32_t groups = std::max((nq + kGemmQ - 1) / kGemmQ, 1);   // nq may be 0 in a size query
   int32_t r = (kGemmTargetGroups + groups - 1) / groups;
   r = std::max((r + 7) / 8 * 8, 8);
   return std::min(r, (capacity + kRangeAlign - 1) / kRangeAlign);

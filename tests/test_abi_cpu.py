@@ -108,6 +108,8 @@ def test_index_topk_validation(lib):
     assert call(ws_bytes=16) == lib.CSA2_ERR_WORKSPACE
     assert call(nq=0) == lib.CSA2_OK
     assert call(mode=2, reuse=P(1), nq=0) == lib.CSA2_OK
+    assert call(nq=0, q=None, out=None, ws=None) == lib.CSA2_OK   # nothing to point at
+    assert call(nq=0, top_k=0) == lib.CSA2_ERR_SHAPE
 
 
 def test_index_topk_append_validation(lib):
@@ -132,6 +134,7 @@ def test_index_topk_append_validation(lib):
     assert call(out=None) == lib.CSA2_ERR_NULL
     assert call(ws=None) == lib.CSA2_ERR_WORKSPACE
     assert call(n=0, k=None, seq=None, nq=0) == lib.CSA2_OK        # nothing to do
+    assert call(n=0, k=None, seq=None, nq=0, out=None, ws=None) == lib.CSA2_OK
 
 
 def test_workspace_queries(lib):
@@ -146,6 +149,21 @@ def test_workspace_queries(lib):
     attn = L.csa2_sparse_attn_workspace(c, 4, 64, 2048)
     assert attn >= 4 * 32 * 64 * 128 * 4
     assert L.csa2_sparse_attn_workspace(c, 4, 24, 2048) == 0
+
+
+def test_workspace_queries_for_no_queries(lib):
+    # nq = 0 is a valid call (a no-op), so its size queries must answer too,
+    # for both index-key dtypes (the E4M3 one also sizes the matrix-core
+    # scorer's layout) and every mode
+    L = lib.LIB
+    for dtype in (0, 1):
+        c = ctypes.byref(_cache(lib, idx_k_dtype=dtype))
+        for mode, pool_len, pool_blocks in ((0, 0, 0), (0, 0, 64), (1, 0, 0), (1, 512, 0), (2, 0, 0)):
+            L.csa2_index_topk_workspace(c, mode, 0, 256, pool_len, pool_blocks)
+        L.csa2_sparse_attn_workspace(c, 0, 64, 2048)
+        P = ctypes.c_void_p
+        lc = lib.csa2_local_cache(P(1), P(1), P(1), 2, 128, 128, 128)
+        L.csa2_sparse_local_attn_workspace(c, ctypes.byref(lc), 0, 64, 2048)
 
 
 def test_sparse_attn_validation(lib):

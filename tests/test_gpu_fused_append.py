@@ -108,6 +108,7 @@ def _run_case(nq, nseq, cap, heads=8, dtype="fp8", q_dtype="bf16", mode="full", 
     (8, 2, 70000, {"pool_blocks": 300, "top_k": 2048}),   # pool-building Full layer
     (64, 4, 16400, {"mode": "reindex"}),                  # Reindex over every visible position
     (64, 4, 16400, {"extra_rows": 40}),                   # rows no query reads / past positions
+    (64, 4, 16400, {"extra_rows": 192}),                  # 256 rows: the most one launch takes
     (64, 4, 16400, {"with_idx": False}),                  # rows without index keys
 ])
 def test_fused_append_matches_separate_calls(nq, nseq, cap, kw):
@@ -157,3 +158,38 @@ def test_fused_append_decode_steps_in_a_row():
         qpos = qpos + 1
     assert np.array_equal(host(g1.idx_k), host(g2.idx_k))
     assert np.array_equal(untile_idx(host(g1.idx_k), 8, np.uint8), oc.idx_k)
+
+
+def test_fused_append_without_queries_or_rows():
+    # no queries: the call is the append alone; no rows: the index call alone
+    announce("fused append, nq = 0 and n_append = 0")
+    m = lib()
+    rng = np.random.default_rng(5)
+    nseq, cap = 2, 16400
+    (g1, g2), oc = _twin_caches(m, nseq, cap, 8, "fp8", rng)
+    n = 20
+    aseq = np.array([i % nseq for i in range(n)], np.int32)
+    apos = rng.choice(cap, n, replace=False).astype(np.int32)
+    k, v, ik = _bf16(rng, (n, 128)), _bf16(rng, (n, 128)), _bf16(rng, (n, 8, 64))
+    app = (dev_u16(k), dev_u16(v), dev_u16(ik), dev_i32(aseq), dev_i32(apos))
+    empty_q = (torch.empty((0, 8, 64), dtype=torch.int16, device="cuda"),
+               torch.empty(0, dtype=torch.int32, device="cuda"),
+               torch.empty(0, dtype=torch.int32, device="cuda"))
+    m.csa2_index_topk_append(g1, *app, "full", *empty_q, 2048)
+    m.csa2_kv_append(g2, *app)
+    torch.cuda.synchronize()
+    for a, b in ((g1.kv_codes, g2.kv_codes), (g1.kv_scales, g2.kv_scales), (g1.idx_k, g2.idx_k)):
+        assert np.array_equal(host(a), host(b))
+    nq = 16
+    qseq = (np.arange(nq) % nseq).astype(np.int32)
+    qpos = rng.choice(cap, nq, replace=False).astype(np.int32)
+    qidx = _bf16(rng, (nq, 8, 64))
+    none = (torch.empty((0, 128), dtype=torch.int16, device="cuda"),
+            torch.empty((0, 128), dtype=torch.int16, device="cuda"), None,
+            torch.empty(0, dtype=torch.int32, device="cuda"),
+            torch.empty(0, dtype=torch.int32, device="cuda"))
+    t1, _ = m.csa2_index_topk_append(g1, *none, "full", dev_u16(qidx), dev_i32(qseq),
+                                     dev_i32(qpos), 2048)
+    t2, _ = m.csa2_index_topk(g2, "full", dev_u16(qidx), dev_i32(qseq), dev_i32(qpos), 2048)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(t1), host(t2))

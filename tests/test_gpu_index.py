@@ -329,6 +329,39 @@ def test_matrix_core_long_rows():
     announce(f"  swaps at the K-th score: {swaps}")
 
 
+@pytest.mark.parametrize("context", [163840, 163856])
+def test_matrix_core_threshold_register_edge(context):
+    # 163840 positions: 10240 block maxima per row, every register group of the
+    # one-wave threshold search full; 16 positions more and the calls take the
+    # workgroup threshold kernel.  Queries at the last position, inside the
+    # last block, with exactly K blocks, and with fewer than K blocks (no
+    # threshold: every visible position is a candidate)
+    qpos = [context - 1, context - 9, 16 * 2048 - 1, 16 * 2048 - 17, 100]
+    announce(f"matrix-core threshold edge context={context}")
+    m = lib()
+    wl = synth.workload("decode_1m", context=context, batch=1)
+    gc = m.Cache(1, context, idx_heads=8, idx_k_dtype="fp8")
+    oc = O.OracleCache(1, context, idx_heads=8, idx_k_dtype="fp8", lazy=True)
+    data = synth.gen_batch(wl)
+    seq, pos = np.zeros(context, np.int32), np.arange(context, dtype=np.int32)
+    m.csa2_kv_append(gc, dev_u16(data.k[0]), dev_u16(data.v[0]), dev_u16(data.ik[0]),
+                     dev_i32(seq), dev_i32(pos))
+    oc.append(data.k[0], data.v[0], data.ik[0], seq, pos)
+    del data
+    rng = np.random.default_rng(context + 1)
+    qi = synth.f32_to_bf16_bits(rng.standard_normal((len(qpos), 8, 64)).astype(np.float32))
+    top_k = 2048
+    tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qi), dev_i32([0] * len(qpos)), dev_i32(qpos),
+                              top_k, q_dtype="fp8")
+    torch.cuda.synchronize()
+    got = host(tk)
+    swaps = 0
+    for i, p in enumerate(qpos):
+        swaps += _relaxed_query(oc, 0, p, O.query_index_values(qi[i], "fp8"), got[i], top_k)
+    assert list(got[4, :101]) == list(range(101)) and np.all(got[4, 101:] == -1)
+    announce(f"  swaps at the K-th score: {swaps}")
+
+
 def test_matrix_core_topk_is_deterministic():
     # run twice on the same inputs: identical bytes (the block maxima, the
     # threshold and the candidate compaction use atomics and cross-workgroup
