@@ -211,6 +211,45 @@ def test_filter_path_bit_exact(context, batch, qpos):
                 assert np.array_equal(host(pool)[i], p), (top_k, i)
 
 
+@pytest.mark.parametrize("context,q_dtype", [(60000, "bf16"), (70000, "bf16"), (70000, "fp8")])
+def test_largest_top_k(context, q_dtype):
+    # K = 65536, the largest the calls take: over 60000 rows (the ranked
+    # records: every candidate selected, then padding) and over 70000 rows
+    # (the histogram stream with a real cut of 4464 candidates; and the
+    # matrix-core scorer)
+    announce(f"top_k 65536 context={context} q={q_dtype}")
+    m = lib()
+    batch = 2
+    wl = synth.workload("decode_1m", context=context, batch=batch)
+    gc = m.Cache(batch, context, idx_heads=8, idx_k_dtype="fp8")
+    oc = O.OracleCache(batch, context, idx_heads=8, idx_k_dtype="fp8", lazy=True)
+    data = synth.gen_batch(wl)
+    for b in range(batch):
+        seq, pos = np.full(context, b, np.int32), np.arange(context, dtype=np.int32)
+        m.csa2_kv_append(gc, dev_u16(data.k[b]), dev_u16(data.v[b]), dev_u16(data.ik[b]),
+                         dev_i32(seq), dev_i32(pos))
+        oc.append(data.k[b], data.v[b], data.ik[b], seq, pos)
+    del data
+    top_k = 65536
+    qpos = [context - 1, context - 1, 40000]
+    qseq = [0, 1, 1]
+    rng = np.random.default_rng(context + 3)
+    qi = synth.f32_to_bf16_bits(rng.standard_normal((len(qpos), 8, 64)).astype(np.float32))
+    tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qi), dev_i32(qseq), dev_i32(qpos), top_k,
+                              q_dtype=q_dtype)
+    torch.cuda.synchronize()
+    got = host(tk)
+    for i, p in enumerate(qpos):
+        n = min(p + 1, top_k)
+        assert np.all(got[i, n:] == -1)
+        if q_dtype == "fp8":
+            _relaxed_query(oc, qseq[i], p, O.query_index_values(qi[i], "fp8"), got[i], top_k)
+        else:
+            want, _, _, _ = O.index_topk("full", oc, qseq[i], p, O.query_index_values(qi[i], "bf16"),
+                                         top_k)
+            assert np.array_equal(got[i], want), i
+
+
 # ---------------------------------------------------------------------------
 # matrix-core scorer (E4M3 index query, E4M3 keys, every visible position)
 # ---------------------------------------------------------------------------
