@@ -105,12 +105,14 @@ def test_attention_deterministic():
 
 
 @pytest.mark.parametrize("nq,top_k,heads", [(32, 2048, 64), (32, 1500, 64), (16, 1000, 48),
-                                            (256, 300, 16), (64, 2048, 32), (8, 2048, 64)])
+                                            (256, 300, 16), (64, 2048, 32), (8, 2048, 64),
+                                            (4, 65536, 16)])
 def test_attention_batch_shapes(nq, top_k, heads):
     # Batch shapes whose splits hold several 64-row sub-chunks (an odd count:
     # 1500 rows give 3 per split), one split per query (256 queries: the final
-    # output written directly, no combine) and 16 splits of two sub-chunks (8
-    # queries of 2048 rows).  Holes, an empty list, duplicates; determinism.
+    # output written directly, no combine), 16 splits of two sub-chunks (8
+    # queries of 2048 rows) and the largest K (65536 rows: splits of the
+    # most rows a split takes).  Holes, an empty list, duplicates; determinism.
     announce(f"attn batch shape nq={nq} k={top_k} heads={heads}")
     m = lib()
     wl, gc, oc = _setup(heads)

@@ -250,6 +250,39 @@ def test_largest_top_k(context, q_dtype):
             assert np.array_equal(got[i], want), i
 
 
+def test_large_pool_and_reindex():
+    # a pool of 8192 blocks (65536 positions) over 70000 rows, then a Reindex
+    # layer over it: pools past the ranked records' size (the pool scorer and
+    # the histogram stream)
+    announce("pool of 8192 blocks, Reindex over it")
+    m = lib()
+    context, batch = 70000, 1
+    wl = synth.workload("decode_1m", context=context, batch=batch)
+    gc = m.Cache(batch, context, idx_heads=8, idx_k_dtype="fp8")
+    oc = O.OracleCache(batch, context, idx_heads=8, idx_k_dtype="fp8", lazy=True)
+    data = synth.gen_batch(wl)
+    seq, pos = np.zeros(context, np.int32), np.arange(context, dtype=np.int32)
+    m.csa2_kv_append(gc, dev_u16(data.k[0]), dev_u16(data.v[0]), dev_u16(data.ik[0]),
+                     dev_i32(seq), dev_i32(pos))
+    oc.append(data.k[0], data.v[0], data.ik[0], seq, pos)
+    del data
+    qpos = [context - 1, 60000]
+    rng = np.random.default_rng(8192)
+    qi = synth.f32_to_bf16_bits(rng.standard_normal((2, 2, 8, 64)).astype(np.float32))
+    tk, pool = m.csa2_index_topk(gc, "full", dev_u16(qi[0]), dev_i32([0, 0]), dev_i32(qpos), 2048,
+                                 pool_blocks=8192)
+    tk2, _ = m.csa2_index_topk(gc, "reindex", dev_u16(qi[1]), dev_i32([0, 0]), dev_i32(qpos), 2048,
+                               pool_in=pool)
+    torch.cuda.synchronize()
+    for i, p in enumerate(qpos):
+        t, pl, _, _ = O.index_topk("full", oc, 0, p, O.query_index_values(qi[0, i], "bf16"), 2048,
+                                   pool_blocks=8192)
+        assert np.array_equal(host(tk)[i], t) and np.array_equal(host(pool)[i], pl), i
+        t2, _, _, _ = O.index_topk("reindex", oc, 0, p, O.query_index_values(qi[1, i], "bf16"),
+                                   2048, pool_in=pl)
+        assert np.array_equal(host(tk2)[i], t2), i
+
+
 # ---------------------------------------------------------------------------
 # matrix-core scorer (E4M3 index query, E4M3 keys, every visible position)
 # ---------------------------------------------------------------------------
