@@ -3,7 +3,8 @@ quantize-and-append) against the oracle's project_and_append.
 
 Bit-exact on hidden states and weights drawn from a coarse grid (x in
 {-1, -3/4, .., 1}, w in {-1/2, -3/8, .., 1/2}): every product and partial sum
-is a multiple of 2^-5 below 2^12, exact in fp32 in any order, so the matrix
+is a multiple of 2^-5 of magnitude at most d_model / 2 <= 2^15 (20
+significant bits), exact in fp32 in any order, so the matrix
 cores' sums equal the oracle's exact ones and the bf16 rounding, codes, scales
 and index keys agree byte for byte.  On random normal inputs the fp32
 accumulation order differs from the exact sum, so a value that lands next to
@@ -53,7 +54,8 @@ def _run(heads, dtype, n, d_model, grid=True, seed=0, capacity=512):
 
 @pytest.mark.parametrize("heads,dtype", [(8, "fp8"), (4, "bf16")])
 @pytest.mark.parametrize("n,d_model", [(1, 32), (100, 512), (200, 1056), (64, 4096), (257, 96),
-                                       (300, 512), (1000, 1056), (600, 96), (1024, 4096)])
+                                       (300, 512), (1000, 1056), (600, 96), (1024, 4096),
+                                       (1, 65536), (520, 65536)])
 def test_proj_append_bit_exact_on_exact_sums(heads, dtype, n, d_model):
     announce(f"proj append heads={heads} idx={dtype} n={n} d={d_model}")
     got, want = _run(heads, dtype, n, d_model, seed=n + d_model)
