@@ -1671,6 +1671,8 @@ TopkWorkspace topk_workspace_layout(const csa2_cache &c, csa2_mode mode, int32_t
 
 bool append_fusable(const IndexArgs &a) {
   if (a.ap.n <= 0 || a.ap.n > kFuseMaxRows || a.mode == CSA2_REUSE) return false;
+  // the rows take up to kFuseMaxRows / 4 extra grid rows past the queries'
+  if (a.nq + kFuseMaxRows / 4 > 65535) return false;
   if (a.q_fp8 && gemm_eligible(*a.cache, a.mode, a.pool_len, a.pool_blocks)) return false;
   const bool pool = a.mode == CSA2_FULL && a.pool_blocks > 0;
   const bool reindex_pool = a.mode == CSA2_REINDEX && a.pool_in != nullptr;
