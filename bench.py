@@ -568,6 +568,35 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n}), flush=True)
 
 
+def copy_reference(hip, gib=1, reps=20):
+    """A plain 1 GiB device-to-device copy (torch's copy kernel) timed with HIP
+    events in the same run: the practical read+write rate the roofline's 8 TB/s
+    peak is measured against."""
+    import torch
+    n = gib << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < MIN_WARMUP_S:
+        b.copy_(a)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(reps):
+        b.copy_(a)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(e0, e1) / reps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    del a, b
+    torch.cuda.empty_cache()
+    gbps = 2 * n / (ms * 1e-3) / 1e9
+    return {"bytes_copied": n, "avg_ms": ms, "read_plus_write_gbps": gbps,
+            "frac_of_peak": gbps / HBM_PEAK_GBPS}
+
+
 def main():
     args = _args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -601,6 +630,7 @@ def main():
     }
     if "attention_roofline" in res:
         line["attention_roofline"] = res["attention_roofline"]
+    line["copy_reference"] = copy_reference(hip)
     if not args.no_extra:
         line["extra"] = {}
         for name in ("decode_1m", "chain8_256k_b8", "prefill_4k_on_128k", "released_256k_b8",
