@@ -28,6 +28,21 @@
 //                       (ties to the lower position, ascending output), with
 //                       the radix passes of the streaming path.
 // With continuous scores about K plus a few percent candidates survive.
+//
+// Long rows take a cheaper first pass.  gemm_score_kernel<3> computes the
+// block maxima of every eighth group of 16 blocks only (a stratified sample,
+// an eighth of the product), and gemm_kth_wave_kernel<1> sets t' to the m-th
+// largest sampled maximum, m chosen above the sample's expected share of the
+// K largest blocks by five standard deviations, so that t' lies below t for
+// every query but rare ones.  Pass 2 then emits every position scoring at
+// least t'.  Whatever t' is, the result stays exact: when a query gets at
+// least min(K, visible) candidates, its K-th largest score is at least t' and
+// every position of the Top-K (ties included) is among them.  The launches
+// after pass 2 check exactly that: gemm_score_kernel<1> in its fallback form
+// counts every query's candidates, and for the query groups holding a query
+// short of them it computes all block maxima, the threshold kernel gives
+// those queries the exact t, and pass 2 emits their candidates again; for the
+// other groups the three launches return at once.
 #include <algorithm>
 
 #include "csa2_select.h"
@@ -65,13 +80,17 @@ __device__ __forceinline__ const uint16_t *bmax_at(const uint16_t *bmax, int32_t
 constexpr int kDmaPerTile = 2;          // next-stage pieces a thread loads per row tile
 constexpr int kKthThreads = 256;
 // Candidates a gemm_resolve_kernel keeps in LDS: ~K(1 + 10 %) with continuous
-// scores for K = 2048 (blocks holding two candidates, the threshold's 16-bit
-// granularity); under 40 KB of LDS per workgroup four share a CU (thousands
-// of queries per call).  More candidates take the streamed path.
-constexpr int kGemmResolveCap = 2560;
+// scores for K = 2048 and the exact threshold (blocks holding two candidates,
+// the threshold's 16-bit granularity), ~1.5 K with the sampled one; at 45 KB
+// of LDS per workgroup three share a CU (thousands of queries per call).
+// More candidates take the streamed path.
+constexpr int kGemmResolveCap = 3584;
 constexpr int kGemmResolveThreads = 256;
 constexpr int kGemmEarlySlots = 16;     // candidate slots per resolve thread read before the counts
 constexpr int kKthRegMax = 32768;       // block maxima a gemm_kth_kernel keeps in registers
+constexpr int kSampleEvery = 8;         // the sampled first pass: one block group in kSampleEvery
+constexpr float kSampleSigma = 5.0f;    // its margin, in standard deviations of the sample count
+constexpr uint32_t kThrNone = 0xFF800000u;   // threshold key of +inf: no finite score reaches it
 
 __device__ __forceinline__ uint32_t e4m3_code(float f) {
   return e4m3_from_f32_nonneg(fabsf(f)) | ((__float_as_uint(f) >> 24) & 0x80u);
@@ -146,14 +165,22 @@ __device__ __forceinline__ void emit_lowest(uint2 *c, uint32_t &off, uint32_t &m
 // The output tile's lane l holds rows (positions) 4(l/16)..4(l/16)+3 of
 // column (query) l % 16.
 // ---------------------------------------------------------------------------
-template <int H, int kPass>
+// kPass 1: block maxima of every block; 3: of the sampled block groups only,
+// stored compacted (sampled group g / kSampleEvery); 2: emission.
+// kFallback (passes 1 and 2): the checking launches after a sampled threshold.
+// Pass 1 then first counts each of its queries' candidates (workgroups of
+// range 0 store fail[q] and the group's gflag) and returns unless a query of
+// the group is short of min(K, visible); pass 2 returns for groups without
+// such a query and emits for those queries only.
+template <int H, int kPass, bool kFallback>
 __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const uint8_t *__restrict__ idx_k, int64_t capacity, const uint8_t *__restrict__ q8,
     const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos, int32_t nq,
     const uint32_t *__restrict__ plan, uint16_t *__restrict__ bmax,
     const uint32_t *__restrict__ thr, uint2 *__restrict__ cand, int64_t cand_stride,
-    uint32_t *__restrict__ cnt, int32_t nranges) {
-  constexpr int kGemmStage = kPass == 1 ? CSA2_GEMM_STAGE1 : CSA2_GEMM_STAGE2;
+    uint32_t *__restrict__ cnt, int32_t nranges, uint32_t *__restrict__ fail,
+    uint32_t *__restrict__ gflag, int32_t top_k) {
+  constexpr int kGemmStage = kPass == 2 ? CSA2_GEMM_STAGE2 : CSA2_GEMM_STAGE1;
   constexpr int kPB = H * 64;                          // key bytes per position
   constexpr int kSteps = kPB / 128;                    // MFMA k-steps
   constexpr int kTileBytes = kBlk * kPB;               // one 16-row tile
@@ -179,6 +206,30 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
   const int r = blockIdx.x;
   const int qbase = blockIdx.y * kGemmQ;
   const int p_begin = r * sub;   // positions fit int32 (capacity is an int32)
+
+  static_assert(kGemmQ == kGemmThreads, "the check: one thread per query of the group");
+  if (kFallback) {
+    if (kPass == 1) {
+      // thread tid checks query qbase + tid
+      const int q = qbase + tid;
+      uint32_t f = 0u;
+      if (q < nq) {
+        const int64_t nvis = (int64_t)q_pos[q] + 1;
+        const int64_t nreg = min((int64_t)nranges, (nvis + sub - 1) / sub);
+        int64_t c = 0;
+        for (int64_t i = 0; i < nreg; ++i) c += min((int64_t)cnt[(int64_t)q * nranges + i], (int64_t)sub);
+        f = c < min((int64_t)top_k, nvis) ? 1u : 0u;
+      }
+      const int any = __syncthreads_or((int)f);
+      if (r == 0) {
+        if (q < nq) fail[q] = f;
+        if (tid == 0) gflag[blockIdx.y] = any ? 1u : 0u;
+      }
+      if (!any) return;   // uniform
+    } else if (gflag[blockIdx.y] == 0u) {
+      return;   // uniform
+    }
+  }
 
   // the group's sequences and furthest visible position
   const int qt = qbase + tid;
@@ -213,7 +264,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const int qc = in ? q : nq - 1;
     cbase[j] = cand + (int64_t)qc * cand_stride + (int64_t)r * sub;
     qp[j] = in ? q_pos[q] : -1;
-    qs[j] = in ? q_seq[q] : -1;
+    // (a fallback emission leaves the queries that had enough candidates alone)
+    qs[j] = (in && (kPass != 2 || !kFallback || fail[q] != 0u)) ? q_seq[q] : -1;
     tq[j] = (kPass == 2 && in) ? thr[q] : 0u;
     run[j] = 0;
     const uint8_t *qrow = q8 + (int64_t)qc * kPB;
@@ -295,7 +347,26 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     for (int d = 32; d >= 1; d >>= 1) min_qp = min(min_qp, __shfl_xor(min_qp, d, kWave));
     const bool wave_act = min_qp != INT32_MAX;
     const uint8_t *kb = idx_k + (int64_t)sigma * capacity * kPB;
-    const int n_st = (p_end - p_begin + kGemmStage - 1) / kGemmStage;
+    // the stages: contiguous from p_begin, or (pass 3) the two of every
+    // sampled block group (groups g with g % kSampleEvery == 0)
+    int s_first = p_begin, n_st;
+    if constexpr (kPass == 3) {
+      const int g0 = p_begin / kRangeAlign;
+      s_first = (g0 + kSampleEvery - 1) / kSampleEvery * kSampleEvery * kRangeAlign;
+      if (s_first >= p_end) {
+        n_st = 0;
+      } else {
+        const int ng = (p_end - 1 - s_first) / (kSampleEvery * kRangeAlign) + 1;
+        const int last = s_first + (ng - 1) * kSampleEvery * kRangeAlign;
+        n_st = 2 * ng - (last + kGemmStage >= p_end ? 1 : 0);
+      }
+    } else {
+      n_st = (p_end - p_begin + kGemmStage - 1) / kGemmStage;
+    }
+    auto stage_p0 = [&](int it) -> int {
+      if (kPass != 3) return p_begin + it * kGemmStage;
+      return s_first + (it >> 1) * (kSampleEvery * kRangeAlign) + (it & 1) * kGemmStage;
+    };
     uint32_t sreg[kBlkGroup / 2];   // pass 1: this lane's query's block maxima, oldest lowest
     // A operand of (row tile rt, k-step s) from a staged buffer
     auto lds_a = [&](const uint8_t *cur, int rt, int s) -> v8i {
@@ -356,11 +427,12 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     // goes into `nxt`, kDmaPerTile pieces per row tile, so that no wave stalls
     // on a burst of loads.  Pass 2 emits a tile's candidates after issuing
     // the next tile's products, so that the matrix cores work meanwhile.
-    auto compute = [&](const uint8_t *cur, int p0, uint8_t *nxt, bool more, int half) {
+    auto compute = [&](const uint8_t *cur, int p0, uint8_t *nxt, bool more, int pn_s, int half) {
+      const int pn = kPass == 3 ? pn_s : p0 + kGemmStage;   // the next stage's first position
       if (!wave_act) {
         if (more) {
 #pragma unroll
-          for (int k = 0; k < kPieces; ++k) dma_piece(kb, nxt, p0 + kGemmStage, k);
+          for (int k = 0; k < kPieces; ++k) dma_piece(kb, nxt, pn, k);
         }
         return;
       }
@@ -373,7 +445,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
         if (more) {
 #pragma unroll
           for (int k = rt * kDmaPerTile; k < (rt + 1) * kDmaPerTile; ++k)
-            if (k < kPieces) dma_piece(kb, nxt, p0 + kGemmStage, k);
+            if (k < kPieces) dma_piece(kb, nxt, pn, k);
         }
         if (pt >= p_end) break;
         v4f acc[4];
@@ -445,7 +517,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
           const int q = qbase + wave * 64 + lane;     // column tile grp, column col
           const bool own_act = grp == 0 ? act[0] : grp == 1 ? act[1] : grp == 2 ? act[2] : act[3];
           if (q < nq && own_act) {
-            const int64_t g = (pt / kBlk) / kBlkGroup;   // the group's index
+            // the group's index (pass 3: among the sampled groups)
+            const int64_t g = (pt / kBlk) / kBlkGroup / (kPass == 3 ? kSampleEvery : 1);
             uint4 *dst = reinterpret_cast<uint4 *>(bmax + (g * nq + q) * kBlkGroup);
             dst[0] = make_uint4(sreg[0], sreg[1], sreg[2], sreg[3]);
             dst[1] = make_uint4(sreg[4], sreg[5], sreg[6], sreg[7]);
@@ -454,21 +527,37 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
       }
       if (kPass == 2) emit(accp, ptl);   // the stage's last tile
     };
+    if constexpr (kPass == 3) {
+      if (n_st > 0) {   // uniform (no load is left in flight when there is no stage)
 #pragma unroll
-    for (int k = 0; k < kPieces; ++k) dma_piece(kb, stageA, p_begin, k);
-    for (int it = 0; it < n_st; ++it) {
-      const int p0 = p_begin + it * kGemmStage;
-      __syncthreads();   // this stage's loads done; the other buffer no longer read
-      const bool more = it + 1 < n_st;
-      if ((it & 1) == 0) compute(stageA, p0, stageB, more, 0);
-      else compute(stageB, p0, stageA, more, 1);
+        for (int k = 0; k < kPieces; ++k) dma_piece(kb, stageA, stage_p0(0), k);
+      }
+      for (int it = 0; it < n_st; ++it) {
+        const int p0 = stage_p0(it);
+        __syncthreads();   // this stage's loads done; the other buffer no longer read
+        const bool more = it + 1 < n_st;
+        const int pn = stage_p0(it + 1);
+        if ((it & 1) == 0) compute(stageA, p0, stageB, more, pn, 0);
+        else compute(stageB, p0, stageA, more, pn, 1);
+      }
+    } else {
+      // (n_st >= 1: p_end > p_begin)
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) dma_piece(kb, stageA, p_begin, k);
+      for (int it = 0; it < n_st; ++it) {
+        const int p0 = p_begin + it * kGemmStage;
+        __syncthreads();   // this stage's loads done; the other buffer no longer read
+        const bool more = it + 1 < n_st;
+        if ((it & 1) == 0) compute(stageA, p0, stageB, more, 0, 0);
+        else compute(stageB, p0, stageA, more, 0, 1);
+      }
     }
     __syncthreads();   // the next sequence's first stage reuses stage A
   }
   if (kPass == 2) {
     const int q = qbase + wave * 64 + lane;
     const uint32_t own = grp == 0 ? run[0] : grp == 1 ? run[1] : grp == 2 ? run[2] : run[3];
-    if (q < nq) cnt[(int64_t)q * nranges + r] = own;
+    if (q < nq && (!kFallback || fail[q] != 0u)) cnt[(int64_t)q * nranges + r] = own;
   }
 }
 
@@ -499,12 +588,14 @@ __device__ __forceinline__ uint32_t kth_block_sum(uint32_t c, uint32_t (*part)[k
   return total;
 }
 
+// fail: nullptr, or only the queries with fail[q] != 0 (the checking launch).
 __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
     const uint16_t *__restrict__ bmax, int32_t nq, const int32_t *__restrict__ q_pos,
-    int32_t top_k, uint32_t *__restrict__ thr) {
+    int32_t top_k, uint32_t *__restrict__ thr, const uint32_t *__restrict__ fail) {
   __shared__ uint32_t part[2][kKthThreads / kWave];
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
+  if (fail != nullptr && fail[q] == 0u) return;   // uniform
   const int64_t nblk = ((int64_t)q_pos[q] + 1 + kBlk - 1) / kBlk;
   if (nblk < top_k) {
     if (tid == 0) thr[q] = 0u;
@@ -586,21 +677,43 @@ __device__ __forceinline__ uint32_t pk_count_ge(uint32_t acc, uint32_t w, uint32
 // the row's end: 0), and a bit costs three packed operations per word (two
 // values) and a wave sum -- no barrier anywhere. Bits that the row's largest
 // and smallest values share are taken from them without a pass.
+// kSampled: the rows are the sampled block maxima of gemm_score_kernel<3>
+// (the query's visible ones are a prefix of its row: n_s of them), and the
+// threshold is their m-th largest, m from the expected number of the K
+// largest blocks in the sample plus kSampleSigma standard deviations; a
+// sample too short for that gets kThrNone (no candidates: the checking
+// launches compute the query exactly).  fail: as in gemm_kth_kernel.
 constexpr int kKthWaveGroups = 20;
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 constexpr int64_t kKthWaveMax = 8 * kWave * kKthWaveGroups;   // 10240 blocks: 163840 positions
 
+template <bool kSampled>
 __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
     const uint16_t *__restrict__ bmax, const int32_t *__restrict__ q_pos, int32_t nq,
-    int32_t top_k, uint32_t *__restrict__ thr) {
+    int32_t top_k, uint32_t *__restrict__ thr, const uint32_t *__restrict__ fail) {
   const int lane = threadIdx.x & (kWave - 1);
   const int q = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
   if (q >= nq) return;   // uniform per wave
-  // at most kKthWaveMax: the host launches this kernel only for such rows
-  const int nblk = (q_pos[q] + kBlk) / kBlk;
-  if (nblk < top_k) {
+  if (fail != nullptr && fail[q] == 0u) return;
+  // the host launches this kernel only for rows of at most kKthWaveMax values
+  const int vis = (q_pos[q] + kBlk) / kBlk;   // visible blocks
+  if (vis < top_k) {
     if (lane == 0) thr[q] = 0u;
     return;
+  }
+  int nblk = vis;   // values in the row
+  uint32_t kk = (uint32_t)top_k;   // the rank looked for
+  if (kSampled) {
+    constexpr int kSpan = kSampleEvery * kBlkGroup;   // blocks per sampled group's stride
+    nblk = kBlkGroup * (vis / kSpan) + min(kBlkGroup, vis % kSpan);
+    const float mu = (float)top_k * (float)nblk / (float)vis;
+    const float sd = sqrtf(mu * (1.0f - (float)top_k / (float)vis));
+    const int m = (int)ceilf(mu + kSampleSigma * sd) + 1;
+    if (m > nblk) {
+      if (lane == 0) thr[q] = kThrNone;
+      return;
+    }
+    kk = (uint32_t)m;
   }
   const int ngroups = (nblk + 8 * kWave - 1) / (8 * kWave);   // uniform
   const int last8 = (nblk - 1) / 8 * 8;                       // the row's last group of 8
@@ -632,7 +745,7 @@ __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
   const uint32_t diff = (uint32_t)(hi_v ^ lo_v);
   const int top = diff ? 31 - __builtin_clz(diff) : -1;
   uint32_t prefix = (uint32_t)hi_v & ~(diff ? (2u << top) - 1u : 0u);
-  const uint32_t k = (uint32_t)top_k;
+  const uint32_t k = kk;
   const uint32_t one = 0x00010001u;
   for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = prefix | (1u << bit);
@@ -738,8 +851,11 @@ int32_t gemm_ranges(int32_t nq, int32_t capacity) {
   return std::min(r, (capacity + kRangeAlign - 1) / kRangeAlign);
 }
 
+// pass 1, 2 or 3 (the sampled block maxima, into L.bmax_s); fallback: the
+// checking form of passes 1 and 2
 template <int H>
-void launch_gemm_scores(const IndexArgs &a, const GemmWorkspace &L, int pass, hipStream_t s) {
+void launch_gemm_scores(const IndexArgs &a, const GemmWorkspace &L, int pass, bool fallback,
+                        hipStream_t s) {
   const csa2_cache &c = *a.cache;
   uint8_t *w = a.ws;
   const dim3 grid((unsigned)L.nranges, (unsigned)((a.nq + kGemmQ - 1) / kGemmQ));
@@ -748,16 +864,31 @@ void launch_gemm_scores(const IndexArgs &a, const GemmWorkspace &L, int pass, hi
                        static_cast<const uint8_t *>(c.idx_k), (int64_t)c.capacity,
                        reinterpret_cast<const uint8_t *>(w + L.q8), a.q_seq, a.q_pos, a.nq,
                        reinterpret_cast<const uint32_t *>(w + L.plan),
-                       reinterpret_cast<uint16_t *>(w + L.bmax),
+                       reinterpret_cast<uint16_t *>(w + (pass == 3 ? L.bmax_s : L.bmax)),
                        reinterpret_cast<const uint32_t *>(w + L.thr),
                        reinterpret_cast<uint2 *>(w + L.cand), L.cand_stride,
-                       reinterpret_cast<uint32_t *>(w + L.cnt), L.nranges);
+                       reinterpret_cast<uint32_t *>(w + L.cnt), L.nranges,
+                       reinterpret_cast<uint32_t *>(w + L.fail),
+                       reinterpret_cast<uint32_t *>(w + L.gflag), a.top_k);
   };
-  if (pass == 1) args(gemm_score_kernel<H, 1>);
-  else args(gemm_score_kernel<H, 2>);
+  if (pass == 1 && fallback) args(gemm_score_kernel<H, 1, true>);
+  else if (pass == 1) args(gemm_score_kernel<H, 1, false>);
+  else if (pass == 2 && fallback) args(gemm_score_kernel<H, 2, true>);
+  else if (pass == 2) args(gemm_score_kernel<H, 2, false>);
+  else args(gemm_score_kernel<H, 3, false>);
 }
 
+
 }  // namespace
+
+// The sampled first pass: rows long enough for the sample to pay (at least
+// twice K blocks), and sampled rows that fit one wave's threshold registers.
+static bool gemm_sampled(const csa2_cache &c, int32_t top_k) {
+  const int64_t blocks = ((int64_t)c.capacity + kBlk - 1) / kBlk;
+  const int64_t groups = ((int64_t)c.capacity + kRangeAlign - 1) / kRangeAlign;
+  const int64_t sampled = (groups + kSampleEvery - 1) / kSampleEvery * kBlkGroup;
+  return blocks >= 2 * (int64_t)top_k && sampled <= kKthWaveMax;
+}
 
 bool gemm_eligible(const csa2_cache &c, csa2_mode mode, int32_t pool_len, int32_t pool_blocks) {
   if (c.idx_k_dtype != CSA2_FP8_E4M3) return false;
@@ -771,6 +902,9 @@ GemmWorkspace gemm_workspace_layout(const csa2_cache &c, int32_t nq) {
       (((int64_t)c.capacity + w.nranges - 1) / w.nranges + kRangeAlign - 1) / kRangeAlign * kRangeAlign;
   // one row of block maxima per query, whole 16-block groups
   w.bmax_row = ((int64_t)c.capacity + kRangeAlign - 1) / kRangeAlign * kBlkGroup;
+  const int64_t groups = w.bmax_row / kBlkGroup;
+  w.bmax_s_row = (groups + kSampleEvery - 1) / kSampleEvery * kBlkGroup;
+  const int64_t qgroups = std::max<int64_t>(1, ((int64_t)nq + kGemmQ - 1) / kGemmQ);
   w.cand_stride = sub_max * w.nranges;
   size_t off = 0;
   w.q8 = off;
@@ -781,6 +915,12 @@ GemmWorkspace gemm_workspace_layout(const csa2_cache &c, int32_t nq) {
   off = align256(off + (size_t)nq * 4);
   w.bmax = off;
   off = align256(off + (size_t)w.bmax_row * nq * 2);
+  w.bmax_s = off;
+  off = align256(off + (size_t)w.bmax_s_row * nq * 2);
+  w.fail = off;
+  off = align256(off + (size_t)nq * 4);
+  w.gflag = off;
+  off = align256(off + (size_t)qgroups * 4);
   w.cnt = off;
   off = align256(off + (size_t)nq * w.nranges * 4);
   w.cand = off;
@@ -799,19 +939,37 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
                      dim3(256), 0, s, a.q_idx, n_elems, w + L.q8, a.q_pos, a.nq, L.nranges,
                      reinterpret_cast<uint32_t *>(w + L.plan));
   if (before != nullptr) (void)hipEventRecord(before, s);
-  if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 1, s);
-  else launch_gemm_scores<4>(a, L, 1, s);
-  if ((c.capacity + kBlk - 1) / kBlk <= kKthWaveMax)   // every row fits one wave's registers
-    hipLaunchKernelGGL(gemm_kth_wave_kernel, dim3((unsigned)((a.nq + 3) / 4)), dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t *>(w + L.bmax), a.q_pos, a.nq, a.top_k,
-                       reinterpret_cast<uint32_t *>(w + L.thr));
-  else
-    hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
-                       reinterpret_cast<const uint16_t *>(w + L.bmax), a.nq, a.q_pos, a.top_k,
-                       reinterpret_cast<uint32_t *>(w + L.thr));
-  if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, 2, s);
-  else launch_gemm_scores<4>(a, L, 2, s);
-  // the profiling events cover both product passes and the threshold between them
+  auto pass = [&](int p, bool fallback) {
+    if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, p, fallback, s);
+    else launch_gemm_scores<4>(a, L, p, fallback, s);
+  };
+  // exact thresholds (t) from every block maximum; fail: only those queries
+  auto exact_kth = [&](const uint32_t *fail) {
+    if ((c.capacity + kBlk - 1) / kBlk <= kKthWaveMax)   // every row fits one wave's registers
+      hipLaunchKernelGGL(gemm_kth_wave_kernel<false>, dim3((unsigned)((a.nq + 3) / 4)), dim3(256),
+                         0, s, reinterpret_cast<const uint16_t *>(w + L.bmax), a.q_pos, a.nq,
+                         a.top_k, reinterpret_cast<uint32_t *>(w + L.thr), fail);
+    else
+      hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
+                         reinterpret_cast<const uint16_t *>(w + L.bmax), a.nq, a.q_pos, a.top_k,
+                         reinterpret_cast<uint32_t *>(w + L.thr), fail);
+  };
+  if (gemm_sampled(c, a.top_k)) {
+    pass(3, false);
+    hipLaunchKernelGGL(gemm_kth_wave_kernel<true>, dim3((unsigned)((a.nq + 3) / 4)), dim3(256), 0,
+                       s, reinterpret_cast<const uint16_t *>(w + L.bmax_s), a.q_pos, a.nq,
+                       a.top_k, reinterpret_cast<uint32_t *>(w + L.thr), nullptr);
+    pass(2, false);
+    // the check, and the exact passes for the query groups that need them
+    pass(1, true);
+    exact_kth(reinterpret_cast<const uint32_t *>(w + L.fail));
+    pass(2, true);
+  } else {
+    pass(1, false);
+    exact_kth(nullptr);
+    pass(2, false);
+  }
+  // the profiling events cover the product passes and the thresholds between them
   if (after != nullptr) (void)hipEventRecord(after, s);
   hipLaunchKernelGGL(gemm_resolve_kernel, dim3((unsigned)a.nq), dim3(kGemmResolveThreads), 0, s,
                      a.q_pos, a.top_k, reinterpret_cast<const uint32_t *>(w + L.plan),
