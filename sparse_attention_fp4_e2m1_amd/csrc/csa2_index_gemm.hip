@@ -32,10 +32,10 @@
 // Long rows take a cheaper first pass.  gemm_score_kernel<3> computes the
 // block maxima of every eighth group of 16 blocks only (a stratified sample,
 // an eighth of the product), and gemm_kth_wave_kernel<1> sets t' to the m-th
-// largest sampled maximum, m chosen above the sample's expected share of the
-// K largest blocks by five standard deviations, so that t' lies below t for
-// every query but rare ones.  Pass 2 then emits every position scoring at
-// least t'.  Whatever t' is, the result stays exact: when a query gets at
+// largest sampled maximum, m chosen five standard deviations above the
+// expected number of sampled blocks that hold one of the K largest scores,
+// so that t' lies below the K-th largest score for every query but rare
+// ones.  Pass 2 then emits every position scoring at least t'.  Whatever t' is, the result stays exact: when a query gets at
 // least min(K, visible) candidates, its K-th largest score is at least t' and
 // every position of the Top-K (ties included) is among them.  The launches
 // after pass 2 check exactly that: gemm_score_kernel<1> in its fallback form
@@ -85,12 +85,11 @@ constexpr int kKthThreads = 256;
 // of LDS per workgroup three share a CU (thousands of queries per call).
 // More candidates take the streamed path.
 constexpr int kGemmResolveCap = 3584;
-constexpr int kGemmResolveThreads = 256;
-constexpr int kGemmEarlySlots = 16;     // candidate slots per resolve thread read before the counts
+constexpr int kGemmResolveThreads = 512;
+constexpr int kGemmEarlySlots = 8;      // candidate slots per resolve thread read before the counts
 constexpr int kKthRegMax = 32768;       // block maxima a gemm_kth_kernel keeps in registers
 constexpr int kSampleEvery = 8;         // the sampled first pass: one block group in kSampleEvery
 constexpr float kSampleSigma = 5.0f;    // its margin, in standard deviations of the sample count
-constexpr uint32_t kThrNone = 0xFF800000u;   // threshold key of +inf: no finite score reaches it
 
 __device__ __forceinline__ uint32_t e4m3_code(float f) {
   return e4m3_from_f32_nonneg(fabsf(f)) | ((__float_as_uint(f) >> 24) & 0x80u);
@@ -99,9 +98,11 @@ __device__ __forceinline__ uint32_t e4m3_code(float f) {
 // E4M3 copy of q_idx (n_elems bf16 values), and plan[0] = the position-range
 // length: ceil(L / nranges) rounded up to a multiple of kRangeAlign, with
 // L = 1 + max q_pos.
+// Also clears tot, the per-query candidate totals pass 2 adds up.
 __global__ void __launch_bounds__(256) gemm_prep_kernel(
     const uint16_t *__restrict__ q_idx, int64_t n_elems, uint8_t *__restrict__ q8,
-    const int32_t *__restrict__ q_pos, int32_t nq, int32_t nranges, uint32_t *__restrict__ plan) {
+    const int32_t *__restrict__ q_pos, int32_t nq, int32_t nranges, uint32_t *__restrict__ plan,
+    uint32_t *__restrict__ tot) {
   if (blockIdx.x == 0) {
     __shared__ int32_t red[256 / kWave];
     int32_t m = -1;
@@ -117,13 +118,27 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(
       plan[0] = (uint32_t)max(sub, (int64_t)kRangeAlign);
     }
   }
-  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < nq) tot[t] = 0u;   // (the grid has n_elems / 8 >= nq threads)
+  const int64_t i0 = t * 8;
   if (i0 >= n_elems) return;
+  // eight bf16 values: one 16-byte load where the array allows it
+  uint32_t v[4];
+  if ((reinterpret_cast<uintptr_t>(q_idx) & 15u) == 0u) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(q_idx + i0);
+    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (uint32_t)q_idx[i0 + 2 * e] | ((uint32_t)q_idx[i0 + 2 * e + 1] << 16);
+  }
   uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) lo |= e4m3_code(bf16_to_f32(q_idx[i0 + e])) << (8 * e);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) hi |= e4m3_code(bf16_to_f32(q_idx[i0 + 4 + e])) << (8 * e);
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h = (uint32_t)(v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    lo |= e4m3_code(bf16_to_f32(h)) << (8 * e);
+    const uint32_t h2 = (uint32_t)(v[2 + (e >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
+    hi |= e4m3_code(bf16_to_f32(h2)) << (8 * e);
+  }
   *reinterpret_cast<uint2 *>(q8 + i0) = make_uint2(lo, hi);
 }
 
@@ -168,10 +183,10 @@ __device__ __forceinline__ void emit_lowest(uint2 *c, uint32_t &off, uint32_t &m
 // kPass 1: block maxima of every block; 3: of the sampled block groups only,
 // stored compacted (sampled group g / kSampleEvery); 2: emission.
 // kFallback (passes 1 and 2): the checking launches after a sampled threshold.
-// Pass 1 then first counts each of its queries' candidates (workgroups of
-// range 0 store fail[q] and the group's gflag) and returns unless a query of
-// the group is short of min(K, visible); pass 2 returns for groups without
-// such a query and emits for those queries only.
+// Pass 1 then first reads each of its queries' candidate total (tot[q], which
+// pass 2 adds up; workgroups of range 0 store fail[q] and the group's gflag)
+// and returns unless a query of the group is short of min(K, visible); pass
+// 2 returns for groups without such a query and emits for those queries only.
 template <int H, int kPass, bool kFallback>
 __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const uint8_t *__restrict__ idx_k, int64_t capacity, const uint8_t *__restrict__ q8,
@@ -179,7 +194,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const uint32_t *__restrict__ plan, uint16_t *__restrict__ bmax,
     const uint32_t *__restrict__ thr, uint2 *__restrict__ cand, int64_t cand_stride,
     uint32_t *__restrict__ cnt, int32_t nranges, uint32_t *__restrict__ fail,
-    uint32_t *__restrict__ gflag, int32_t top_k) {
+    uint32_t *__restrict__ gflag, uint32_t *__restrict__ tot, int32_t top_k) {
   constexpr int kGemmStage = kPass == 2 ? CSA2_GEMM_STAGE2 : CSA2_GEMM_STAGE1;
   constexpr int kPB = H * 64;                          // key bytes per position
   constexpr int kSteps = kPB / 128;                    // MFMA k-steps
@@ -215,10 +230,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
       uint32_t f = 0u;
       if (q < nq) {
         const int64_t nvis = (int64_t)q_pos[q] + 1;
-        const int64_t nreg = min((int64_t)nranges, (nvis + sub - 1) / sub);
-        int64_t c = 0;
-        for (int64_t i = 0; i < nreg; ++i) c += min((int64_t)cnt[(int64_t)q * nranges + i], (int64_t)sub);
-        f = c < min((int64_t)top_k, nvis) ? 1u : 0u;
+        f = (int64_t)tot[q] < min((int64_t)top_k, nvis) ? 1u : 0u;
       }
       const int any = __syncthreads_or((int)f);
       if (r == 0) {
@@ -558,6 +570,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const int q = qbase + wave * 64 + lane;
     const uint32_t own = grp == 0 ? run[0] : grp == 1 ? run[1] : grp == 2 ? run[2] : run[3];
     if (q < nq && (!kFallback || fail[q] != 0u)) cnt[(int64_t)q * nranges + r] = own;
+    if (!kFallback && q < nq && own != 0u) atomicAdd(&tot[q], own);
   }
 }
 
@@ -679,10 +692,11 @@ __device__ __forceinline__ uint32_t pk_count_ge(uint32_t acc, uint32_t w, uint32
 // and smallest values share are taken from them without a pass.
 // kSampled: the rows are the sampled block maxima of gemm_score_kernel<3>
 // (the query's visible ones are a prefix of its row: n_s of them), and the
-// threshold is their m-th largest, m from the expected number of the K
-// largest blocks in the sample plus kSampleSigma standard deviations; a
-// sample too short for that gets kThrNone (no candidates: the checking
-// launches compute the query exactly).  fail: as in gemm_kth_kernel.
+// threshold is their m-th largest, m the expected number of sampled blocks
+// holding one of the query's K largest scores plus kSampleSigma standard
+// deviations; a sample too short for that makes every visible position a
+// candidate (t' = 0).  Only the groups holding the row's values are loaded.
+// fail: as in gemm_kth_kernel.
 constexpr int kKthWaveGroups = 20;
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 constexpr int64_t kKthWaveMax = 8 * kWave * kKthWaveGroups;   // 10240 blocks: 163840 positions
@@ -706,11 +720,21 @@ __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
   if (kSampled) {
     constexpr int kSpan = kSampleEvery * kBlkGroup;   // blocks per sampled group's stride
     nblk = kBlkGroup * (vis / kSpan) + min(kBlkGroup, vis % kSpan);
-    const float mu = (float)top_k * (float)nblk / (float)vis;
-    const float sd = sqrtf(mu * (1.0f - (float)top_k / (float)vis));
+    // a block holds one of the K largest of n scores with probability
+    // 1 - (1 - K/n)^16 when they lie anywhere alike; the sample's count of such
+    // blocks is about binomial
+    const float p = (float)top_k / (float)(q_pos[q] + 1);
+    float r = 1.0f - p;
+    r *= r;
+    r *= r;
+    r *= r;
+    r *= r;
+    const float fb = 1.0f - r;
+    const float mu = (float)nblk * fb;
+    const float sd = sqrtf(mu * r);
     const int m = (int)ceilf(mu + kSampleSigma * sd) + 1;
-    if (m > nblk) {
-      if (lane == 0) thr[q] = kThrNone;
+    if (m > nblk) {   // every visible position a candidate (exact; the sample cannot help)
+      if (lane == 0) thr[q] = 0u;
       return;
     }
     kk = (uint32_t)m;
@@ -723,7 +747,9 @@ __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
   for (int u = 0; u < kKthWaveGroups; ++u) {
     // branch-free: groups past the row read its last group and are masked
     const int i = 8 * (u * kWave + lane);
-    const uint4 w = *reinterpret_cast<const uint4 *>(bmax_at(bmax, nq, q, min(i, last8)));
+    const uint4 w = (!kSampled || u < ngroups)
+                        ? *reinterpret_cast<const uint4 *>(bmax_at(bmax, nq, q, min(i, last8)))
+                        : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -869,7 +895,8 @@ void launch_gemm_scores(const IndexArgs &a, const GemmWorkspace &L, int pass, bo
                        reinterpret_cast<uint2 *>(w + L.cand), L.cand_stride,
                        reinterpret_cast<uint32_t *>(w + L.cnt), L.nranges,
                        reinterpret_cast<uint32_t *>(w + L.fail),
-                       reinterpret_cast<uint32_t *>(w + L.gflag), a.top_k);
+                       reinterpret_cast<uint32_t *>(w + L.gflag),
+                       reinterpret_cast<uint32_t *>(w + L.tot), a.top_k);
   };
   if (pass == 1 && fallback) args(gemm_score_kernel<H, 1, true>);
   else if (pass == 1) args(gemm_score_kernel<H, 1, false>);
@@ -921,6 +948,8 @@ GemmWorkspace gemm_workspace_layout(const csa2_cache &c, int32_t nq) {
   off = align256(off + (size_t)nq * 4);
   w.gflag = off;
   off = align256(off + (size_t)qgroups * 4);
+  w.tot = off;
+  off = align256(off + (size_t)nq * 4);
   w.cnt = off;
   off = align256(off + (size_t)nq * w.nranges * 4);
   w.cand = off;
@@ -937,7 +966,7 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
   const int64_t n_elems = (int64_t)a.nq * c.idx_heads * 64;
   hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)std::max<int64_t>(1, (n_elems / 8 + 255) / 256)),
                      dim3(256), 0, s, a.q_idx, n_elems, w + L.q8, a.q_pos, a.nq, L.nranges,
-                     reinterpret_cast<uint32_t *>(w + L.plan));
+                     reinterpret_cast<uint32_t *>(w + L.plan), reinterpret_cast<uint32_t *>(w + L.tot));
   if (before != nullptr) (void)hipEventRecord(before, s);
   auto pass = [&](int p, bool fallback) {
     if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, p, fallback, s);

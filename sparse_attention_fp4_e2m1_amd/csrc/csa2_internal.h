@@ -61,6 +61,7 @@ struct GemmWorkspace {
   size_t bmax_s = 0;       // uint16 [bmax_s_row / 16][nq][16]  the sampled block groups' maxima, compacted
   size_t fail = 0;         // uint32 [nq]  the query had fewer candidates than it needs (sampled threshold)
   size_t gflag = 0;        // uint32 [ceil(nq / 512)]  its query group holds such a query
+  size_t tot = 0;          // uint32 [nq]  candidates pass 2 emitted for the query (all ranges)
   size_t cnt = 0;          // uint32 [nq][nranges]  candidates per (query, range)
   size_t cand = 0;         // uint2  [nq][cand_stride]  (score key, position)
   int64_t bmax_row = 0;
