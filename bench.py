@@ -327,13 +327,14 @@ def measure(name, steps, warmup, hip, use_graph):
     res["warmup_steps_run"] = run.warmup_steps
     if scan_ms is not None and matrix_core_scan(wl):
         # the matrix-core scorer: the method's index product (every query
-        # against every visible position) counted once, over the time of both
-        # product passes and the threshold kernel between them
+        # against every visible position) counted once, over the time of its
+        # product passes and the threshold and checking launches between them
         flops = run.scan_flops()
         ach = flops / (scan_ms * 1e-3) / 1e12
         res["roofline"] = {"bound": "mfma",
-                           "kernel": "gemm_score_kernel passes 1 and 2 + the threshold kernel "
-                                     "between them (fp8 index product, counted once)",
+                           "kernel": "gemm_score_kernel sampled pass + emitting pass, with the "
+                                     "threshold and checking launches between them (fp8 index "
+                                     "product, counted once)",
                            "achieved": ach, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": ach / FP8_PEAK_TFLOPS, "traffic": None,
                            "flops_per_launch": flops, "avg_launch_ms": scan_ms}

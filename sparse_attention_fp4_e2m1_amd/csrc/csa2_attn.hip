@@ -33,7 +33,15 @@ namespace csa2 {
 namespace {
 
 constexpr int kSub = 64;                      // rows per sub-chunk
-constexpr int kVtPitch = kSub + 4;            // fp16 elements per LDS row of V^T
+constexpr int kVtPitch = kSub + 8;            // fp16 elements per LDS row of V^T (16-B aligned rows)
+
+// Where row r (0..63) of a sub-chunk sits in an LDS row of V^T: in each half
+// of 32 rows, the rows one lane group of the PV product reads (4g..4g+3 and
+// 16+4g..16+4g+3) are adjacent, so that its operand is one 16-byte read.
+// Rows 2p and 2p + 1 stay adjacent.
+__device__ __forceinline__ int vt_col(int r) {
+  return (r & 32) + 8 * ((r >> 2) & 3) + 4 * ((r >> 4) & 1) + (r & 3);
+}
 constexpr int kMaxRowsPerSplit = 2048;
 constexpr int kTargetGroups = 256;            // workgroups aimed for (one per CU)
 constexpr int kTwoSubMinGroups = 128;         // see rows_per_split
@@ -130,7 +138,7 @@ __device__ __forceinline__ void dequant(const Gathered<kThreads> &gd, uint4 *kq,
       const f16x2 sab = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gd.vs[it], 1.0f, false);
       const _Float16 sa = sab[0], sb = sab[1];
       const f16x2 s2a = {sa, sa}, s2b = {sb, sb};
-      uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + 2 * pr);
+      uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + vt_col(2 * pr));
 #pragma unroll
       for (int hw = 0; hw < 2; ++hw) {
         const uint32_t wa = hw ? gd.vc[it][0].y : gd.vc[it][0].x;
@@ -278,10 +286,9 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
                           __builtin_bit_cast(uint32_t, p2[4 * sg + 3])));
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const _Float16 *vrow = vbuf + (dt * 16 + l16) * kVtPitch + 32 * sg + 4 * g;
-      const uint2 a = *reinterpret_cast<const uint2 *>(vrow);
-      const uint2 b = *reinterpret_cast<const uint2 *>(vrow + 16);
-      const f16x8 vb = __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+      // rows 32sg + 4g + 0..3 and 32sg + 16 + 4g + 0..3 (adjacent, see vt_col)
+      const _Float16 *vrow = vbuf + (dt * 16 + l16) * kVtPitch + 32 * sg + 8 * g;
+      const f16x8 vb = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4 *>(vrow));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb, pa, o[dt], 0, 0, 0);
     }
   }
@@ -380,7 +387,7 @@ __device__ __forceinline__ void stage_local(const uint8_t *__restrict__ lk,
     const uint4 wa = *reinterpret_cast<const uint4 *>(lv + (sbase + sa) * 128 + 16 * b);
     const uint4 wb = *reinterpret_cast<const uint4 *>(lv + (sbase + sb) * 128 + 16 * b);
     const uint32_t xa[4] = {wa.x, wa.y, wa.z, wa.w}, xb[4] = {wb.x, wb.y, wb.z, wb.w};
-    uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + 2 * pr);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + vt_col(2 * pr));
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t a[2] = {
@@ -427,7 +434,7 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
   constexpr int kThreads = kWaves * 64;
   __shared__ int32_t rows[kMaxRowsPerSplit + 2 * kSub];
   __shared__ uint4 kq[4 * 4 * 64];
-  __shared__ _Float16 vt[128 * kVtPitch];
+  __shared__ __attribute__((aligned(16))) _Float16 vt[128 * kVtPitch];
 
   const int split = blockIdx.x;
   const int q = blockIdx.y;
@@ -621,7 +628,7 @@ __global__ void __launch_bounds__(kWaves * 64) local_attn_kernel(
   constexpr int kThreads = kWaves * 64;
   __shared__ int32_t rows[kMaxLocalWindow + kSub];   // slot of each row, -1: no row
   __shared__ uint4 kq[4 * 4 * 64];
-  __shared__ _Float16 vt[128 * kVtPitch];
+  __shared__ __attribute__((aligned(16))) _Float16 vt[128 * kVtPitch];
 
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
