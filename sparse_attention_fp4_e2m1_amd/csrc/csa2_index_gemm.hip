@@ -31,18 +31,18 @@
 //
 // Long rows take a cheaper first pass.  gemm_score_kernel<3> computes the
 // block maxima of every eighth group of 16 blocks only (a stratified sample,
-// an eighth of the product), and gemm_kth_wave_kernel<1> sets t' to the m-th
-// largest sampled maximum, m chosen five standard deviations above the
+// an eighth of the product), and gemm_kth_wave_kernel<true> sets t' to the
+// m-th largest sampled maximum, m chosen five standard deviations above the
 // expected number of sampled blocks that hold one of the K largest scores,
 // so that t' lies below the K-th largest score for every query but rare
-// ones.  Pass 2 then emits every position scoring at least t'.  Whatever t' is, the result stays exact: when a query gets at
-// least min(K, visible) candidates, its K-th largest score is at least t' and
-// every position of the Top-K (ties included) is among them.  The launches
-// after pass 2 check exactly that: gemm_score_kernel<1> in its fallback form
-// counts every query's candidates, and for the query groups holding a query
-// short of them it computes all block maxima, the threshold kernel gives
-// those queries the exact t, and pass 2 emits their candidates again; for the
-// other groups the three launches return at once.
+// ones.  Pass 2 then emits every position scoring at least t'.  Whatever t'
+// is, the result stays exact: when a query gets at least min(K, visible)
+// candidates, its K-th largest score is at least t' and every position of
+// the Top-K (ties included) is among them.  The launch after pass 2 checks
+// exactly that: gemm_score_kernel<2> in its checking form reads every
+// query's candidate total and, for the query groups holding a query short of
+// them, emits every visible position of those queries (t = 0: the resolve
+// then streams them, exact); for the other groups it returns at once.
 #include <algorithm>
 
 #include "csa2_select.h"
@@ -181,20 +181,18 @@ __device__ __forceinline__ void emit_lowest(uint2 *c, uint32_t &off, uint32_t &m
 // column (query) l % 16.
 // ---------------------------------------------------------------------------
 // kPass 1: block maxima of every block; 3: of the sampled block groups only,
-// stored compacted (sampled group g / kSampleEvery); 2: emission.
-// kFallback (passes 1 and 2): the checking launches after a sampled threshold.
-// Pass 1 then first reads each of its queries' candidate total (tot[q], which
-// pass 2 adds up; workgroups of range 0 store fail[q] and the group's gflag)
-// and returns unless a query of the group is short of min(K, visible); pass
-// 2 returns for groups without such a query and emits for those queries only.
+// stored compacted (sampled group g / kSampleEvery); 2: emission, every
+// query's candidate total added into tot[q].
+// kFallback (pass 2): the checking launch after a sampled threshold.  It
+// returns unless a query of the group has fewer than min(K, visible)
+// candidates in tot, and emits every visible position of those queries only.
 template <int H, int kPass, bool kFallback>
 __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const uint8_t *__restrict__ idx_k, int64_t capacity, const uint8_t *__restrict__ q8,
     const int32_t *__restrict__ q_seq, const int32_t *__restrict__ q_pos, int32_t nq,
     const uint32_t *__restrict__ plan, uint16_t *__restrict__ bmax,
     const uint32_t *__restrict__ thr, uint2 *__restrict__ cand, int64_t cand_stride,
-    uint32_t *__restrict__ cnt, int32_t nranges, uint32_t *__restrict__ fail,
-    uint32_t *__restrict__ gflag, uint32_t *__restrict__ tot, int32_t top_k) {
+    uint32_t *__restrict__ cnt, int32_t nranges, uint32_t *__restrict__ tot, int32_t top_k) {
   constexpr int kGemmStage = kPass == 2 ? CSA2_GEMM_STAGE2 : CSA2_GEMM_STAGE1;
   constexpr int kPB = H * 64;                          // key bytes per position
   constexpr int kSteps = kPB / 128;                    // MFMA k-steps
@@ -222,25 +220,15 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
   const int qbase = blockIdx.y * kGemmQ;
   const int p_begin = r * sub;   // positions fit int32 (capacity is an int32)
 
+  static_assert(kPass == 2 || !kFallback, "the checking form is an emission");
   static_assert(kGemmQ == kGemmThreads, "the check: one thread per query of the group");
+  // a query short of candidates after the sampled threshold (the checking launch)
+  auto short_of = [&](int q) -> bool {
+    return (int64_t)tot[q] < min((int64_t)top_k, (int64_t)q_pos[q] + 1);
+  };
   if (kFallback) {
-    if (kPass == 1) {
-      // thread tid checks query qbase + tid
-      const int q = qbase + tid;
-      uint32_t f = 0u;
-      if (q < nq) {
-        const int64_t nvis = (int64_t)q_pos[q] + 1;
-        f = (int64_t)tot[q] < min((int64_t)top_k, nvis) ? 1u : 0u;
-      }
-      const int any = __syncthreads_or((int)f);
-      if (r == 0) {
-        if (q < nq) fail[q] = f;
-        if (tid == 0) gflag[blockIdx.y] = any ? 1u : 0u;
-      }
-      if (!any) return;   // uniform
-    } else if (gflag[blockIdx.y] == 0u) {
-      return;   // uniform
-    }
+    const int q = qbase + tid;
+    if (!__syncthreads_or(q < nq && short_of(q) ? 1 : 0)) return;   // uniform
   }
 
   // the group's sequences and furthest visible position
@@ -276,9 +264,11 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     const int qc = in ? q : nq - 1;
     cbase[j] = cand + (int64_t)qc * cand_stride + (int64_t)r * sub;
     qp[j] = in ? q_pos[q] : -1;
-    // (a fallback emission leaves the queries that had enough candidates alone)
-    qs[j] = (in && (kPass != 2 || !kFallback || fail[q] != 0u)) ? q_seq[q] : -1;
-    tq[j] = (kPass == 2 && in) ? thr[q] : 0u;
+    // (the checking emission leaves the queries that had enough candidates
+    // alone, and takes every visible position of the others)
+    const bool mine = in && (!kFallback || short_of(q));
+    qs[j] = mine ? q_seq[q] : -1;
+    tq[j] = (kPass == 2 && in && !kFallback) ? thr[q] : 0u;
     run[j] = 0;
     const uint8_t *qrow = q8 + (int64_t)qc * kPB;
 #pragma unroll
@@ -569,7 +559,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
   if (kPass == 2) {
     const int q = qbase + wave * 64 + lane;
     const uint32_t own = grp == 0 ? run[0] : grp == 1 ? run[1] : grp == 2 ? run[2] : run[3];
-    if (q < nq && (!kFallback || fail[q] != 0u)) cnt[(int64_t)q * nranges + r] = own;
+    if (q < nq && (!kFallback || short_of(q))) cnt[(int64_t)q * nranges + r] = own;
     if (!kFallback && q < nq && own != 0u) atomicAdd(&tot[q], own);
   }
 }
@@ -601,14 +591,12 @@ __device__ __forceinline__ uint32_t kth_block_sum(uint32_t c, uint32_t (*part)[k
   return total;
 }
 
-// fail: nullptr, or only the queries with fail[q] != 0 (the checking launch).
 __global__ void __launch_bounds__(kKthThreads) gemm_kth_kernel(
     const uint16_t *__restrict__ bmax, int32_t nq, const int32_t *__restrict__ q_pos,
-    int32_t top_k, uint32_t *__restrict__ thr, const uint32_t *__restrict__ fail) {
+    int32_t top_k, uint32_t *__restrict__ thr) {
   __shared__ uint32_t part[2][kKthThreads / kWave];
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
-  if (fail != nullptr && fail[q] == 0u) return;   // uniform
   const int64_t nblk = ((int64_t)q_pos[q] + 1 + kBlk - 1) / kBlk;
   if (nblk < top_k) {
     if (tid == 0) thr[q] = 0u;
@@ -696,7 +684,6 @@ __device__ __forceinline__ uint32_t pk_count_ge(uint32_t acc, uint32_t w, uint32
 // holding one of the query's K largest scores plus kSampleSigma standard
 // deviations; a sample too short for that makes every visible position a
 // candidate (t' = 0).  Only the groups holding the row's values are loaded.
-// fail: as in gemm_kth_kernel.
 constexpr int kKthWaveGroups = 20;
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 constexpr int64_t kKthWaveMax = 8 * kWave * kKthWaveGroups;   // 10240 blocks: 163840 positions
@@ -704,11 +691,10 @@ constexpr int64_t kKthWaveMax = 8 * kWave * kKthWaveGroups;   // 10240 blocks: 1
 template <bool kSampled>
 __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
     const uint16_t *__restrict__ bmax, const int32_t *__restrict__ q_pos, int32_t nq,
-    int32_t top_k, uint32_t *__restrict__ thr, const uint32_t *__restrict__ fail) {
+    int32_t top_k, uint32_t *__restrict__ thr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int q = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
   if (q >= nq) return;   // uniform per wave
-  if (fail != nullptr && fail[q] == 0u) return;
   // the host launches this kernel only for rows of at most kKthWaveMax values
   const int vis = (q_pos[q] + kBlk) / kBlk;   // visible blocks
   if (vis < top_k) {
@@ -878,7 +864,7 @@ int32_t gemm_ranges(int32_t nq, int32_t capacity) {
 }
 
 // pass 1, 2 or 3 (the sampled block maxima, into L.bmax_s); fallback: the
-// checking form of passes 1 and 2
+// checking form of pass 2
 template <int H>
 void launch_gemm_scores(const IndexArgs &a, const GemmWorkspace &L, int pass, bool fallback,
                         hipStream_t s) {
@@ -894,12 +880,9 @@ void launch_gemm_scores(const IndexArgs &a, const GemmWorkspace &L, int pass, bo
                        reinterpret_cast<const uint32_t *>(w + L.thr),
                        reinterpret_cast<uint2 *>(w + L.cand), L.cand_stride,
                        reinterpret_cast<uint32_t *>(w + L.cnt), L.nranges,
-                       reinterpret_cast<uint32_t *>(w + L.fail),
-                       reinterpret_cast<uint32_t *>(w + L.gflag),
                        reinterpret_cast<uint32_t *>(w + L.tot), a.top_k);
   };
-  if (pass == 1 && fallback) args(gemm_score_kernel<H, 1, true>);
-  else if (pass == 1) args(gemm_score_kernel<H, 1, false>);
+  if (pass == 1) args(gemm_score_kernel<H, 1, false>);
   else if (pass == 2 && fallback) args(gemm_score_kernel<H, 2, true>);
   else if (pass == 2) args(gemm_score_kernel<H, 2, false>);
   else args(gemm_score_kernel<H, 3, false>);
@@ -931,7 +914,6 @@ GemmWorkspace gemm_workspace_layout(const csa2_cache &c, int32_t nq) {
   w.bmax_row = ((int64_t)c.capacity + kRangeAlign - 1) / kRangeAlign * kBlkGroup;
   const int64_t groups = w.bmax_row / kBlkGroup;
   w.bmax_s_row = (groups + kSampleEvery - 1) / kSampleEvery * kBlkGroup;
-  const int64_t qgroups = std::max<int64_t>(1, ((int64_t)nq + kGemmQ - 1) / kGemmQ);
   w.cand_stride = sub_max * w.nranges;
   size_t off = 0;
   w.q8 = off;
@@ -944,10 +926,6 @@ GemmWorkspace gemm_workspace_layout(const csa2_cache &c, int32_t nq) {
   off = align256(off + (size_t)w.bmax_row * nq * 2);
   w.bmax_s = off;
   off = align256(off + (size_t)w.bmax_s_row * nq * 2);
-  w.fail = off;
-  off = align256(off + (size_t)nq * 4);
-  w.gflag = off;
-  off = align256(off + (size_t)qgroups * 4);
   w.tot = off;
   off = align256(off + (size_t)nq * 4);
   w.cnt = off;
@@ -972,30 +950,23 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
     if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, p, fallback, s);
     else launch_gemm_scores<4>(a, L, p, fallback, s);
   };
-  // exact thresholds (t) from every block maximum; fail: only those queries
-  auto exact_kth = [&](const uint32_t *fail) {
-    if ((c.capacity + kBlk - 1) / kBlk <= kKthWaveMax)   // every row fits one wave's registers
-      hipLaunchKernelGGL(gemm_kth_wave_kernel<false>, dim3((unsigned)((a.nq + 3) / 4)), dim3(256),
-                         0, s, reinterpret_cast<const uint16_t *>(w + L.bmax), a.q_pos, a.nq,
-                         a.top_k, reinterpret_cast<uint32_t *>(w + L.thr), fail);
-    else
-      hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
-                         reinterpret_cast<const uint16_t *>(w + L.bmax), a.nq, a.q_pos, a.top_k,
-                         reinterpret_cast<uint32_t *>(w + L.thr), fail);
-  };
   if (gemm_sampled(c, a.top_k)) {
     pass(3, false);
     hipLaunchKernelGGL(gemm_kth_wave_kernel<true>, dim3((unsigned)((a.nq + 3) / 4)), dim3(256), 0,
                        s, reinterpret_cast<const uint16_t *>(w + L.bmax_s), a.q_pos, a.nq,
-                       a.top_k, reinterpret_cast<uint32_t *>(w + L.thr), nullptr);
+                       a.top_k, reinterpret_cast<uint32_t *>(w + L.thr));
     pass(2, false);
-    // the check, and the exact passes for the query groups that need them
-    pass(1, true);
-    exact_kth(reinterpret_cast<const uint32_t *>(w + L.fail));
-    pass(2, true);
+    pass(2, true);   // the check, and the emission again for queries short of candidates
   } else {
     pass(1, false);
-    exact_kth(nullptr);
+    if ((c.capacity + kBlk - 1) / kBlk <= kKthWaveMax)   // every row fits one wave's registers
+      hipLaunchKernelGGL(gemm_kth_wave_kernel<false>, dim3((unsigned)((a.nq + 3) / 4)), dim3(256),
+                         0, s, reinterpret_cast<const uint16_t *>(w + L.bmax), a.q_pos, a.nq,
+                         a.top_k, reinterpret_cast<uint32_t *>(w + L.thr));
+    else
+      hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
+                         reinterpret_cast<const uint16_t *>(w + L.bmax), a.nq, a.q_pos, a.top_k,
+                         reinterpret_cast<uint32_t *>(w + L.thr));
     pass(2, false);
   }
   // the profiling events cover the product passes and the thresholds between them

@@ -59,8 +59,6 @@ struct GemmWorkspace {
   size_t thr = 0;          // uint32 [nq] candidate threshold key
   size_t bmax = 0;         // uint16 [bmax_row / 16][nq][16]  block maxima of 16 positions (top 16 key bits), group-major
   size_t bmax_s = 0;       // uint16 [bmax_s_row / 16][nq][16]  the sampled block groups' maxima, compacted
-  size_t fail = 0;         // uint32 [nq]  the query had fewer candidates than it needs (sampled threshold)
-  size_t gflag = 0;        // uint32 [ceil(nq / 512)]  its query group holds such a query
   size_t tot = 0;          // uint32 [nq]  candidates pass 2 emitted for the query (all ranges)
   size_t cnt = 0;          // uint32 [nq][nranges]  candidates per (query, range)
   size_t cand = 0;         // uint2  [nq][cand_stride]  (score key, position)
