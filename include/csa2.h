@@ -430,8 +430,8 @@ csa2_status csa2_local_clear(const csa2_local_cache *cache, int32_t seq, void *s
  * events (two hipEvent_t), every csa2_index_topk call made later from the same
  * host thread records `before` and `after` on its stream around its scoring:
  * the streaming scorer's one kernel that reads the index keys, or the
- * matrix-core scorer's two product passes together with the threshold kernel
- * between them.  csa2_profile_index_scan(NULL, NULL) turns the hook off.  The
+ * matrix-core scorer's product passes (the sampled and the emitting pass, or
+ * the block-maximum and the emitting pass) with the launches between them.  csa2_profile_index_scan(NULL, NULL) turns the hook off.  The
  * events are caller-owned; the library only records them.
  */
 void csa2_profile_index_scan(void *before, void *after);
