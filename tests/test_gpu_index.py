@@ -436,9 +436,11 @@ def test_matrix_core_threshold_register_edge(context):
 
 def test_matrix_core_topk_is_deterministic():
     # run twice on the same inputs: identical bytes (the block maxima, the
-    # threshold and the candidate compaction use atomics and cross-workgroup
-    # ordering, which must not leak into the result); a 700-query chunk of one
-    # sequence plus six queries of six sequences
+    # threshold, the candidate totals and the candidate compaction use atomics
+    # and cross-workgroup ordering, which must not leak into the result); a
+    # 700-query chunk of one sequence (K 2048: the exact two-pass threshold;
+    # K 128: rows of at least 2K blocks, the sampled one) plus six queries of
+    # six sequences
     announce("matrix-core determinism")
     m = lib()
     wl, gc, oc = _setup(8, "fp8")
@@ -447,6 +449,7 @@ def test_matrix_core_topk_is_deterministic():
     qpos = np.arange(CAP - nq, CAP)
     qidx = synth.f32_to_bf16_bits(rng.standard_normal((nq, 8, 64)).astype(np.float32) * 2)
     cases = [(dev_u16(qidx), dev_i32(np.full(nq, 3)), dev_i32(qpos), 2048),
+             (dev_u16(qidx), dev_i32(np.full(nq, 3)), dev_i32(qpos), 128),
              (dev_u16(synth.gen_queries(wl, 0).q_idx), dev_i32(np.arange(len(QPOS))),
               dev_i32(QPOS), 256)]
     for q_idx, q_seq, q_pos, top_k in cases:
