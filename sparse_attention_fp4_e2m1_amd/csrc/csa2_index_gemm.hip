@@ -684,11 +684,14 @@ __device__ __forceinline__ uint32_t pk_count_ge(uint32_t acc, uint32_t w, uint32
 // holding one of the query's K largest scores plus kSampleSigma standard
 // deviations; a sample too short for that makes every visible position a
 // candidate (t' = 0).  Only the groups holding the row's values are loaded.
+// kGroups: register groups per lane (the row's length bound: 512 kGroups
+// values); the search's work per bit grows with it.
 constexpr int kKthWaveGroups = 20;
+constexpr int kKthShortGroups = 4;   // sampled rows of up to 2048 values
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 constexpr int64_t kKthWaveMax = 8 * kWave * kKthWaveGroups;   // 10240 blocks: 163840 positions
 
-template <bool kSampled>
+template <bool kSampled, int kGroups = kKthWaveGroups>
 __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
     const uint16_t *__restrict__ bmax, const int32_t *__restrict__ q_pos, int32_t nq,
     int32_t top_k, uint32_t *__restrict__ thr) {
@@ -727,10 +730,10 @@ __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
   }
   const int ngroups = (nblk + 8 * kWave - 1) / (8 * kWave);   // uniform
   const int last8 = (nblk - 1) / 8 * 8;                       // the row's last group of 8
-  uint32_t v[4 * kKthWaveGroups];
+  uint32_t v[4 * kGroups];
   u16x2 vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};   // over the row's values only
 #pragma unroll
-  for (int u = 0; u < kKthWaveGroups; ++u) {
+  for (int u = 0; u < kGroups; ++u) {
     // branch-free: groups past the row read its last group and are masked
     const int i = 8 * (u * kWave + lane);
     const uint4 w = (!kSampled || u < ngroups)
@@ -766,7 +769,7 @@ __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
     const uint32_t cm1 = (cand - 1u) * 0x00010001u;
     uint32_t acc = 0u;
 #pragma unroll
-    for (int u = 0; u < kKthWaveGroups; ++u) {
+    for (int u = 0; u < kGroups; ++u) {
       if (u < ngroups) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -952,9 +955,15 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
   };
   if (gemm_sampled(c, a.top_k)) {
     pass(3, false);
-    hipLaunchKernelGGL(gemm_kth_wave_kernel<true>, dim3((unsigned)((a.nq + 3) / 4)), dim3(256), 0,
-                       s, reinterpret_cast<const uint16_t *>(w + L.bmax_s), a.q_pos, a.nq,
-                       a.top_k, reinterpret_cast<uint32_t *>(w + L.thr));
+    if (L.bmax_s_row <= 8 * kWave * kKthShortGroups)   // short sampled rows: fewer registers
+      hipLaunchKernelGGL((gemm_kth_wave_kernel<true, kKthShortGroups>),
+                         dim3((unsigned)((a.nq + 3) / 4)), dim3(256), 0, s,
+                         reinterpret_cast<const uint16_t *>(w + L.bmax_s), a.q_pos, a.nq, a.top_k,
+                         reinterpret_cast<uint32_t *>(w + L.thr));
+    else
+      hipLaunchKernelGGL(gemm_kth_wave_kernel<true>, dim3((unsigned)((a.nq + 3) / 4)), dim3(256),
+                         0, s, reinterpret_cast<const uint16_t *>(w + L.bmax_s), a.q_pos, a.nq,
+                         a.top_k, reinterpret_cast<uint32_t *>(w + L.thr));
     pass(2, false);
     pass(2, true);   // the check, and the emission again for queries short of candidates
   } else {
