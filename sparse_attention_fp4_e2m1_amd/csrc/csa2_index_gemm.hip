@@ -30,8 +30,10 @@
 // With continuous scores about K plus a few percent candidates survive.
 //
 // Long rows take a cheaper first pass.  gemm_score_kernel<3> computes the
-// block maxima of every eighth group of 16 blocks only (a stratified sample,
-// an eighth of the product), and gemm_kth_wave_kernel<true> sets t' to the
+// block maxima of the first eighth of every position range's groups of 16
+// blocks only (a sample stratified over the ranges, about an eighth of the
+// product, run like pass 1 over shorter ranges), and
+// gemm_kth_wave_kernel<true> sets t' to the
 // m-th largest sampled maximum, m chosen five standard deviations above the
 // expected number of sampled blocks that hold one of the K largest scores,
 // so that t' lies below the K-th largest score for every query but rare
@@ -89,6 +91,11 @@ constexpr int kGemmResolveThreads = 512;
 constexpr int kGemmEarlySlots = 8;      // candidate slots per resolve thread read before the counts
 constexpr int kKthRegMax = 32768;       // block maxima a gemm_kth_kernel keeps in registers
 constexpr int kSampleEvery = 8;         // the sampled first pass: one block group in kSampleEvery
+
+// Block groups a range of `sub` positions samples (its first ones).
+__host__ __device__ constexpr int sampled_groups(int64_t sub) {
+  return (int)(sub / kRangeAlign / kSampleEvery > 1 ? sub / kRangeAlign / kSampleEvery : 1);
+}
 constexpr float kSampleSigma = 5.0f;    // its margin, in standard deviations of the sample count
 
 __device__ __forceinline__ uint32_t e4m3_code(float f) {
@@ -181,7 +188,8 @@ __device__ __forceinline__ void emit_lowest(uint2 *c, uint32_t &off, uint32_t &m
 // column (query) l % 16.
 // ---------------------------------------------------------------------------
 // kPass 1: block maxima of every block; 3: of the sampled block groups only,
-// stored compacted (sampled group g / kSampleEvery); 2: emission, every
+// stored compacted (range r's sampled group j at r * sampled_groups(sub) + j);
+// 2: emission, every
 // query's candidate total added into tot[q].
 // kFallback (pass 2): the checking launch after a sampled threshold.  It
 // returns unless a query of the group has fewer than min(K, visible)
@@ -242,7 +250,9 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
   int32_t maxqp = s_red[0];
   for (int w = 1; w < kGemmWaves; ++w) maxqp = max(maxqp, s_red[w]);
   if (p_begin > maxqp) return;   // uniform: no query of the group sees this range
-  const int p_end = min(p_begin + sub, maxqp + 1);
+  // (pass 3: the range's first sampled_groups(sub) block groups only)
+  const int p_end = min(kPass == 3 ? p_begin + sampled_groups(sub) * kRangeAlign : p_begin + sub,
+                        maxqp + 1);
 
   bool first = qt < nq;
   for (int j = tid - 1; first && j >= 0; --j)
@@ -349,26 +359,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     for (int d = 32; d >= 1; d >>= 1) min_qp = min(min_qp, __shfl_xor(min_qp, d, kWave));
     const bool wave_act = min_qp != INT32_MAX;
     const uint8_t *kb = idx_k + (int64_t)sigma * capacity * kPB;
-    // the stages: contiguous from p_begin, or (pass 3) the two of every
-    // sampled block group (groups g with g % kSampleEvery == 0)
-    int s_first = p_begin, n_st;
-    if constexpr (kPass == 3) {
-      const int g0 = p_begin / kRangeAlign;
-      s_first = (g0 + kSampleEvery - 1) / kSampleEvery * kSampleEvery * kRangeAlign;
-      if (s_first >= p_end) {
-        n_st = 0;
-      } else {
-        const int ng = (p_end - 1 - s_first) / (kSampleEvery * kRangeAlign) + 1;
-        const int last = s_first + (ng - 1) * kSampleEvery * kRangeAlign;
-        n_st = 2 * ng - (last + kGemmStage >= p_end ? 1 : 0);
-      }
-    } else {
-      n_st = (p_end - p_begin + kGemmStage - 1) / kGemmStage;
-    }
-    auto stage_p0 = [&](int it) -> int {
-      if (kPass != 3) return p_begin + it * kGemmStage;
-      return s_first + (it >> 1) * (kSampleEvery * kRangeAlign) + (it & 1) * kGemmStage;
-    };
+    const int n_st = (p_end - p_begin + kGemmStage - 1) / kGemmStage;   // >= 1
     uint32_t sreg[kBlkGroup / 2];   // pass 1: this lane's query's block maxima, oldest lowest
     // A operand of (row tile rt, k-step s) from a staged buffer
     auto lds_a = [&](const uint8_t *cur, int rt, int s) -> v8i {
@@ -429,8 +420,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
     // goes into `nxt`, kDmaPerTile pieces per row tile, so that no wave stalls
     // on a burst of loads.  Pass 2 emits a tile's candidates after issuing
     // the next tile's products, so that the matrix cores work meanwhile.
-    auto compute = [&](const uint8_t *cur, int p0, uint8_t *nxt, bool more, int pn_s, int half) {
-      const int pn = kPass == 3 ? pn_s : p0 + kGemmStage;   // the next stage's first position
+    auto compute = [&](const uint8_t *cur, int p0, uint8_t *nxt, bool more, int half) {
+      const int pn = p0 + kGemmStage;   // the next stage's first position
       if (!wave_act) {
         if (more) {
 #pragma unroll
@@ -520,7 +511,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
           const bool own_act = grp == 0 ? act[0] : grp == 1 ? act[1] : grp == 2 ? act[2] : act[3];
           if (q < nq && own_act) {
             // the group's index (pass 3: among the sampled groups)
-            const int64_t g = (pt / kBlk) / kBlkGroup / (kPass == 3 ? kSampleEvery : 1);
+            const int64_t g = kPass == 3 ? (int64_t)r * sampled_groups(sub) + (pt - p_begin) / kRangeAlign
+                                         : (int64_t)(pt / kBlk) / kBlkGroup;
             uint4 *dst = reinterpret_cast<uint4 *>(bmax + (g * nq + q) * kBlkGroup);
             dst[0] = make_uint4(sreg[0], sreg[1], sreg[2], sreg[3]);
             dst[1] = make_uint4(sreg[4], sreg[5], sreg[6], sreg[7]);
@@ -529,20 +521,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
       }
       if (kPass == 2) emit(accp, ptl);   // the stage's last tile
     };
-    if constexpr (kPass == 3) {
-      if (n_st > 0) {   // uniform (no load is left in flight when there is no stage)
-#pragma unroll
-        for (int k = 0; k < kPieces; ++k) dma_piece(kb, stageA, stage_p0(0), k);
-      }
-      for (int it = 0; it < n_st; ++it) {
-        const int p0 = stage_p0(it);
-        __syncthreads();   // this stage's loads done; the other buffer no longer read
-        const bool more = it + 1 < n_st;
-        const int pn = stage_p0(it + 1);
-        if ((it & 1) == 0) compute(stageA, p0, stageB, more, pn, 0);
-        else compute(stageB, p0, stageA, more, pn, 1);
-      }
-    } else {
+    {
       // (n_st >= 1: p_end > p_begin)
 #pragma unroll
       for (int k = 0; k < kPieces; ++k) dma_piece(kb, stageA, p_begin, k);
@@ -550,8 +529,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
         const int p0 = p_begin + it * kGemmStage;
         __syncthreads();   // this stage's loads done; the other buffer no longer read
         const bool more = it + 1 < n_st;
-        if ((it & 1) == 0) compute(stageA, p0, stageB, more, 0, 0);
-        else compute(stageB, p0, stageA, more, 0, 1);
+        if ((it & 1) == 0) compute(stageA, p0, stageB, more, 0);
+        else compute(stageB, p0, stageA, more, 1);
       }
     }
     __syncthreads();   // the next sequence's first stage reuses stage A
@@ -694,7 +673,7 @@ constexpr int64_t kKthWaveMax = 8 * kWave * kKthWaveGroups;   // 10240 blocks: 1
 template <bool kSampled, int kGroups = kKthWaveGroups>
 __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
     const uint16_t *__restrict__ bmax, const int32_t *__restrict__ q_pos, int32_t nq,
-    int32_t top_k, uint32_t *__restrict__ thr) {
+    int32_t top_k, uint32_t *__restrict__ thr, const uint32_t *__restrict__ plan) {
   const int lane = threadIdx.x & (kWave - 1);
   const int q = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
   if (q >= nq) return;   // uniform per wave
@@ -707,8 +686,13 @@ __global__ void __launch_bounds__(256) gemm_kth_wave_kernel(
   int nblk = vis;   // values in the row
   uint32_t kk = (uint32_t)top_k;   // the rank looked for
   if (kSampled) {
-    constexpr int kSpan = kSampleEvery * kBlkGroup;   // blocks per sampled group's stride
-    nblk = kBlkGroup * (vis / kSpan) + min(kBlkGroup, vis % kSpan);
+    // the visible sampled blocks: every range before the query's whole, then
+    // the start of its own (a prefix of the compacted row)
+    const int sub = (int)plan[0];
+    const int len = sampled_groups(sub) * kRangeAlign;   // sampled positions per range
+    const int nvis = q_pos[q] + 1;
+    const int a = nvis / sub;
+    nblk = a * (len / kBlk) + (min(nvis - a * sub, len) + kBlk - 1) / kBlk;
     // a block holds one of the K largest of n scores with probability
     // 1 - (1 - K/n)^16 when they lie anywhere alike; the sample's count of such
     // blocks is about binomial
@@ -895,12 +879,13 @@ void launch_gemm_scores(const IndexArgs &a, const GemmWorkspace &L, int pass, bo
 }  // namespace
 
 // The sampled first pass: rows long enough for the sample to pay (at least
-// twice K blocks), and sampled rows that fit one wave's threshold registers.
-static bool gemm_sampled(const csa2_cache &c, int32_t top_k) {
+// twice K blocks, ranges of at least kSampleEvery block groups), and sampled
+// rows that fit one wave's threshold registers.
+static bool gemm_sampled(const csa2_cache &c, int32_t top_k, const GemmWorkspace &L) {
   const int64_t blocks = ((int64_t)c.capacity + kBlk - 1) / kBlk;
-  const int64_t groups = ((int64_t)c.capacity + kRangeAlign - 1) / kRangeAlign;
-  const int64_t sampled = (groups + kSampleEvery - 1) / kSampleEvery * kBlkGroup;
-  return blocks >= 2 * (int64_t)top_k && sampled <= kKthWaveMax;
+  const int64_t sub_max = L.cand_stride / L.nranges;
+  return blocks >= 2 * (int64_t)top_k && sub_max >= (int64_t)kSampleEvery * kRangeAlign &&
+         L.bmax_s_row <= kKthWaveMax;
 }
 
 bool gemm_eligible(const csa2_cache &c, csa2_mode mode, int32_t pool_len, int32_t pool_blocks) {
@@ -915,8 +900,8 @@ GemmWorkspace gemm_workspace_layout(const csa2_cache &c, int32_t nq) {
       (((int64_t)c.capacity + w.nranges - 1) / w.nranges + kRangeAlign - 1) / kRangeAlign * kRangeAlign;
   // one row of block maxima per query, whole 16-block groups
   w.bmax_row = ((int64_t)c.capacity + kRangeAlign - 1) / kRangeAlign * kBlkGroup;
-  const int64_t groups = w.bmax_row / kBlkGroup;
-  w.bmax_s_row = (groups + kSampleEvery - 1) / kSampleEvery * kBlkGroup;
+  // the sampled block groups of every range (a range of sub <= sub_max positions)
+  w.bmax_s_row = (int64_t)w.nranges * sampled_groups(sub_max) * kBlkGroup;
   w.cand_stride = sub_max * w.nranges;
   size_t off = 0;
   w.q8 = off;
@@ -953,17 +938,19 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
     if (c.idx_heads == 8) launch_gemm_scores<8>(a, L, p, fallback, s);
     else launch_gemm_scores<4>(a, L, p, fallback, s);
   };
-  if (gemm_sampled(c, a.top_k)) {
+  if (gemm_sampled(c, a.top_k, L)) {
     pass(3, false);
     if (L.bmax_s_row <= 8 * kWave * kKthShortGroups)   // short sampled rows: fewer registers
       hipLaunchKernelGGL((gemm_kth_wave_kernel<true, kKthShortGroups>),
                          dim3((unsigned)((a.nq + 3) / 4)), dim3(256), 0, s,
                          reinterpret_cast<const uint16_t *>(w + L.bmax_s), a.q_pos, a.nq, a.top_k,
-                         reinterpret_cast<uint32_t *>(w + L.thr));
+                         reinterpret_cast<uint32_t *>(w + L.thr),
+                         reinterpret_cast<const uint32_t *>(w + L.plan));
     else
       hipLaunchKernelGGL(gemm_kth_wave_kernel<true>, dim3((unsigned)((a.nq + 3) / 4)), dim3(256),
                          0, s, reinterpret_cast<const uint16_t *>(w + L.bmax_s), a.q_pos, a.nq,
-                         a.top_k, reinterpret_cast<uint32_t *>(w + L.thr));
+                         a.top_k, reinterpret_cast<uint32_t *>(w + L.thr),
+                         reinterpret_cast<const uint32_t *>(w + L.plan));
     pass(2, false);
     pass(2, true);   // the check, and the emission again for queries short of candidates
   } else {
@@ -971,7 +958,8 @@ hipError_t launch_index_topk_gemm(const IndexArgs &a, hipEvent_t before, hipEven
     if ((c.capacity + kBlk - 1) / kBlk <= kKthWaveMax)   // every row fits one wave's registers
       hipLaunchKernelGGL(gemm_kth_wave_kernel<false>, dim3((unsigned)((a.nq + 3) / 4)), dim3(256),
                          0, s, reinterpret_cast<const uint16_t *>(w + L.bmax), a.q_pos, a.nq,
-                         a.top_k, reinterpret_cast<uint32_t *>(w + L.thr));
+                         a.top_k, reinterpret_cast<uint32_t *>(w + L.thr),
+                         reinterpret_cast<const uint32_t *>(w + L.plan));
     else
       hipLaunchKernelGGL(gemm_kth_kernel, dim3((unsigned)a.nq), dim3(kKthThreads), 0, s,
                          reinterpret_cast<const uint16_t *>(w + L.bmax), a.nq, a.q_pos, a.top_k,

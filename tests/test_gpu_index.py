@@ -438,9 +438,9 @@ def test_matrix_core_topk_is_deterministic():
     # run twice on the same inputs: identical bytes (the block maxima, the
     # threshold, the candidate totals and the candidate compaction use atomics
     # and cross-workgroup ordering, which must not leak into the result); a
-    # 700-query chunk of one sequence (K 2048: the exact two-pass threshold;
-    # K 128: rows of at least 2K blocks, the sampled one) plus six queries of
-    # six sequences
+    # 700-query chunk of one sequence (K 2048 and 128) plus six queries of six
+    # sequences (the sampled threshold's run-twice check is in
+    # test_matrix_core_sampled_threshold_matches_exact)
     announce("matrix-core determinism")
     m = lib()
     wl, gc, oc = _setup(8, "fp8")
@@ -604,21 +604,25 @@ def test_ranked_poisoned_workspace_reused():
 
 
 def test_matrix_core_sampled_threshold_matches_exact():
-    # Rows of at least 2K blocks take the sampled first pass (block maxima of
-    # every eighth group of 256 positions); a cache of more than 1310720
-    # positions takes the exact two-pass path.  The same keys in both give the
-    # same scores (same instructions per position), so every Top-K must be the
-    # same bytes.  Query 5 is built so that the sample misleads it: the keys
-    # of the sampled groups point along its own direction, so its sampled
-    # threshold admits fewer than K positions and the checking launches
-    # compute its query group exactly.
-    cap_a, cap_b, top_k, nq = 24576, 1331200, 512, 600
+    # Rows of at least 2K blocks, with position ranges of at least 8 groups of
+    # 256 positions, take the sampled first pass: the block maxima of each
+    # range's first eighth of groups.  600 queries make 128 ranges, so the
+    # 262144-position cache has ranges of 2048 positions, sampled in their
+    # first 256; a 1572864-position cache has more sampled block maxima than
+    # one wave's threshold registers hold and takes the exact two-pass path.
+    # The same keys in both give the same scores (same instructions per
+    # position), so every Top-K must be the same bytes.  Query 5 is built so
+    # that the sample misleads it: the keys of the sampled positions point
+    # along its own direction, so its sampled threshold admits fewer than K
+    # positions and the checking launch gives it every visible position.  The
+    # sampled path runs twice (identical bytes: determinism).
+    cap_a, cap_b, top_k, nq = 262144, 1572864, 512, 600
     announce(f"matrix-core sampled threshold vs exact cap={cap_a} k={top_k} nq={nq}")
     m = lib()
     rng = np.random.default_rng(77)
     u = rng.standard_normal((8, 64)).astype(np.float32)
     ik = rng.standard_normal((cap_a, 8, 64)).astype(np.float32)
-    sampled = (np.arange(cap_a) // 256) % 8 == 0
+    sampled = (np.arange(cap_a) % 2048) < 256
     ik[sampled] = 2 * u + 0.3 * ik[sampled]
     ik = synth.f32_to_bf16_bits(ik)
     kv = synth.f32_to_bf16_bits(rng.standard_normal((cap_a, 128)).astype(np.float32))
@@ -629,7 +633,7 @@ def test_matrix_core_sampled_threshold_matches_exact():
     qpos[5] = cap_a - 1
     seq, pos = np.zeros(cap_a, np.int32), np.arange(cap_a, dtype=np.int32)
     got = []
-    for cap in (cap_a, cap_b):
+    for cap in (cap_a, cap_a, cap_b):
         gc = m.Cache(1, cap, idx_heads=8, idx_k_dtype="fp8")
         m.csa2_kv_append(gc, dev_u16(kv), dev_u16(kv), dev_u16(ik), dev_i32(seq), dev_i32(pos))
         tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qidx), dev_i32(np.zeros(nq)), dev_i32(qpos),
@@ -639,10 +643,11 @@ def test_matrix_core_sampled_threshold_matches_exact():
         del gc, tk
         torch.cuda.empty_cache()
     assert np.array_equal(got[0], got[1])
-    oc = O.OracleCache(1, cap_a, idx_heads=8, idx_k_dtype="fp8")
+    assert np.array_equal(got[0], got[2])
+    oc = O.OracleCache(1, cap_a, idx_heads=8, idx_k_dtype="fp8", lazy=True)
     oc.append(kv, kv, ik, seq, pos)
     swaps = 0
-    for i in [5, 0, 511, 512, nq - 1]:
+    for i in [5, 0, 511, nq - 1]:
         qi = O.query_index_values(qidx[i], "fp8")
         swaps += _relaxed_query(oc, 0, int(qpos[i]), qi, got[0][i], top_k)
     announce(f"  swaps at the K-th score: {swaps}")
