@@ -113,7 +113,17 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(
   if (blockIdx.x == 0) {
     __shared__ int32_t red[256 / kWave];
     int32_t m = -1;
-    for (int i = threadIdx.x; i < nq; i += 256) m = max(m, q_pos[i]);
+    // sixteen loads in flight per thread per round (4096 queries in one round)
+    for (int i0 = 0; i0 < nq; i0 += 16 * 256) {
+      int32_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = i0 + u * 256 + (int)threadIdx.x;
+        v[u] = i < nq ? q_pos[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) m = max(m, v[u]);
+    }
     for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, kWave));
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
     __syncthreads();
