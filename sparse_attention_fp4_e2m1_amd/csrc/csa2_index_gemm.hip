@@ -160,7 +160,10 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(
 }
 
 // The lowest remaining candidate row of mask m (rows of a, m != 0) into slot
-// off of c, then off + 1 and m without that row.
+// off of c, then off + 1 and m without that row.  c is the column tile's base
+// (the same in every lane) and off a slot index from it whose byte offset fits
+// 32 bits, so the store takes its address from scalar registers plus one
+// 32-bit offset.
 __device__ __forceinline__ void emit_lowest(uint2 *c, uint32_t &off, uint32_t &m, const v4f &a,
                                             int prow) {
   const uint32_t i = (uint32_t)__builtin_ctz(m);
@@ -168,7 +171,8 @@ __device__ __forceinline__ void emit_lowest(uint2 *c, uint32_t &off, uint32_t &m
   v = (m & 4u) ? a[2] : v;
   v = (m & 2u) ? a[1] : v;
   v = (m & 1u) ? a[0] : v;
-  c[off] = make_uint2(score_key(v), (uint32_t)prow + i);
+  *reinterpret_cast<uint2 *>(reinterpret_cast<char *>(c) + (off << 3)) =
+      make_uint2(score_key(v), (uint32_t)prow + i);
   ++off;
   m &= m - 1u;
 }
@@ -275,14 +279,20 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
   // this lane's four queries (one per column tile)
   int32_t qp[4], qs[4];
   uint32_t tq[4], run[4];
-  uint2 *cbase[4];   // pass 2: the query's slot region of this range
+  // pass 2: each column tile's slot base (query qbase + 64 wave + 16 j, this
+  // range) and the lane's slot region from it (col rows of cand_stride slots:
+  // under 16 * 2^23 slots, whose byte offsets fit 32 bits)
+  const uint32_t cofs = (uint32_t)(col * cand_stride);   // (a column past nq never emits)
+  uint2 *tbase[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    tbase[j] = cand + (int64_t)(qbase + wave * 64 + 16 * j) * cand_stride + (int64_t)r * sub;
   v8i qb[4][kSteps];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int q = qbase + wave * 64 + 16 * j + col;
     const bool in = q < nq;
     const int qc = in ? q : nq - 1;
-    cbase[j] = cand + (int64_t)qc * cand_stride + (int64_t)r * sub;
     qp[j] = in ? q_pos[q] : -1;
     // (the checking emission leaves the queries that had enough candidates
     // alone, and takes every visible position of the others)
@@ -410,16 +420,16 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
       const uint32_t pre = ((grp & 1) ? r16[0] : 0u) + ((grp & 2) ? r32[0] : 0u);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t off = run[j] + ((pre >> (8 * j)) & 0xFFu);
+        uint32_t off = cofs + run[j] + ((pre >> (8 * j)) & 0xFFu);
         run[j] += (tot >> (8 * j)) & 0xFFu;
         uint32_t m = selm[j];
         if (m != 0u) {
-          emit_lowest(cbase[j], off, m, acc[j], prow);
+          emit_lowest(tbase[j], off, m, acc[j], prow);
           if (m != 0u) {
-            emit_lowest(cbase[j], off, m, acc[j], prow);
+            emit_lowest(tbase[j], off, m, acc[j], prow);
             if (m != 0u) {
-              emit_lowest(cbase[j], off, m, acc[j], prow);
-              if (m != 0u) emit_lowest(cbase[j], off, m, acc[j], prow);
+              emit_lowest(tbase[j], off, m, acc[j], prow);
+              if (m != 0u) emit_lowest(tbase[j], off, m, acc[j], prow);
             }
           }
         }
