@@ -651,3 +651,35 @@ def test_matrix_core_sampled_threshold_matches_exact():
         qi = O.query_index_values(qidx[i], "fp8")
         swaps += _relaxed_query(oc, 0, int(qpos[i]), qi, got[0][i], top_k)
     announce(f"  swaps at the K-th score: {swaps}")
+
+
+@pytest.mark.parametrize("distinct", [1, 3])
+def test_matrix_core_sampled_threshold_tie_heavy(distinct):
+    # 4096 queries of one sequence on 65536 positions: 32 position ranges of
+    # 2048, so the sampled first pass runs.  Few distinct index keys give few
+    # distinct scores: the sampled threshold equals a tied value, every
+    # position of that value is a candidate (the resolve streams them) and the
+    # ties go to the lower positions.
+    cap, nq, top_k = 65536, 4096, 256
+    announce(f"matrix-core sampled threshold, ties distinct={distinct}")
+    m = lib()
+    rng = np.random.default_rng(100 + distinct)
+    base = synth.f32_to_bf16_bits(rng.standard_normal((distinct, 8, 64)).astype(np.float32))
+    ik = base[rng.integers(0, distinct, cap)]
+    kv = synth.f32_to_bf16_bits(rng.standard_normal((cap, 128)).astype(np.float32))
+    gc = m.Cache(1, cap, idx_heads=8, idx_k_dtype="fp8")
+    oc = O.OracleCache(1, cap, idx_heads=8, idx_k_dtype="fp8", lazy=True)
+    seq, pos = np.zeros(cap, np.int32), np.arange(cap, dtype=np.int32)
+    m.csa2_kv_append(gc, dev_u16(kv), dev_u16(kv), dev_u16(ik), dev_i32(seq), dev_i32(pos))
+    oc.append(kv, kv, ik, seq, pos)
+    qi = synth.f32_to_bf16_bits(rng.standard_normal((nq, 8, 64)).astype(np.float32))
+    qpos = np.arange(cap - nq, cap, dtype=np.int32)
+    tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qi), dev_i32(np.zeros(nq)), dev_i32(qpos), top_k,
+                              q_dtype="fp8")
+    torch.cuda.synchronize()
+    got = host(tk)
+    assert np.all(np.diff(got, axis=1) > 0)
+    for i in [0, 1, 2047, nq - 1]:
+        _relaxed_query(oc, 0, int(qpos[i]), O.query_index_values(qi[i], "fp8"), got[i], top_k)
+    if distinct == 1:   # identical keys give identical sums: ties to the lower position
+        assert np.array_equal(got, np.broadcast_to(np.arange(top_k), got.shape))
