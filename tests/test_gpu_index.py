@@ -683,3 +683,41 @@ def test_matrix_core_sampled_threshold_tie_heavy(distinct):
         _relaxed_query(oc, 0, int(qpos[i]), O.query_index_values(qi[i], "fp8"), got[i], top_k)
     if distinct == 1:   # identical keys give identical sums: ties to the lower position
         assert np.array_equal(got, np.broadcast_to(np.arange(top_k), got.shape))
+
+
+def test_matrix_core_sampled_threshold_two_sequences():
+    # The sampled path with two sequences in one 512-query group (one pass per
+    # sequence) and a ragged second group: 700 queries (300 of sequence 0, 400
+    # of sequence 1, at scattered positions), against the exact two-pass path
+    # on a cache too long for the sample (same keys, same score bits).
+    cap_a, cap_b, top_k, nq = 262144, 1572864, 384, 700
+    announce(f"matrix-core sampled threshold, two sequences, nq={nq}")
+    m = lib()
+    rng = np.random.default_rng(91)
+    ik = [synth.f32_to_bf16_bits(rng.standard_normal((cap_a, 8, 64)).astype(np.float32))
+          for _ in range(2)]
+    kv = synth.f32_to_bf16_bits(rng.standard_normal((cap_a, 128)).astype(np.float32))
+    qidx = synth.f32_to_bf16_bits(rng.standard_normal((nq, 8, 64)).astype(np.float32))
+    qseq = np.array([0] * 300 + [1] * 400, np.int32)
+    qpos = rng.integers(cap_a // 2, cap_a, nq).astype(np.int32)
+    qpos[0] = qpos[300] = cap_a - 1
+    pos = np.arange(cap_a, dtype=np.int32)
+    got = []
+    for cap in (cap_a, cap_b):
+        gc = m.Cache(2, cap, idx_heads=8, idx_k_dtype="fp8")
+        for b in range(2):
+            m.csa2_kv_append(gc, dev_u16(kv), dev_u16(kv), dev_u16(ik[b]),
+                             dev_i32(np.full(cap_a, b)), dev_i32(pos))
+        tk, _ = m.csa2_index_topk(gc, "full", dev_u16(qidx), dev_i32(qseq), dev_i32(qpos), top_k,
+                                  q_dtype="fp8")
+        torch.cuda.synchronize()
+        got.append(host(tk))
+        del gc, tk
+        torch.cuda.empty_cache()
+    assert np.array_equal(got[0], got[1])
+    oc = O.OracleCache(2, cap_a, idx_heads=8, idx_k_dtype="fp8", lazy=True)
+    for b in range(2):
+        oc.append(kv, kv, ik[b], np.full(cap_a, b), pos)
+    for i in [0, 299, 300, 511, 512, nq - 1]:
+        _relaxed_query(oc, int(qseq[i]), int(qpos[i]), O.query_index_values(qidx[i], "fp8"),
+                       got[0][i], top_k)
