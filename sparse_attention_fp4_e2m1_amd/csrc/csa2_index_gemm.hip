@@ -32,12 +32,11 @@
 // Long rows take a cheaper first pass.  gemm_score_kernel<3> computes the
 // block maxima of the first eighth of every position range's groups of 16
 // blocks only (a sample stratified over the ranges, about an eighth of the
-// product, run like pass 1 over shorter ranges), and
-// gemm_kth_wave_kernel<true> sets t' to the
-// m-th largest sampled maximum, m chosen five standard deviations above the
-// expected number of sampled blocks that hold one of the K largest scores,
-// so that t' lies below the K-th largest score for every query but rare
-// ones.  Pass 2 then emits every position scoring at least t'.  Whatever t'
+// product, run like pass 1 over shorter ranges), and gemm_kth_wave_kernel<true>
+// sets t' to the m-th largest sampled maximum, m chosen five standard
+// deviations above the expected number of sampled blocks that hold one of
+// the K largest scores, so that t' lies below the K-th largest score for
+// every query but rare ones.  Pass 2 then emits every position scoring at least t'.  Whatever t'
 // is, the result stays exact: when a query gets at least min(K, visible)
 // candidates, its K-th largest score is at least t' and every position of
 // the Top-K (ties included) is among them.  The launch after pass 2 checks
@@ -83,7 +82,7 @@ constexpr int kDmaPerTile = 2;          // next-stage pieces a thread loads per 
 constexpr int kKthThreads = 256;
 // Candidates a gemm_resolve_kernel keeps in LDS: ~K(1 + 10 %) with continuous
 // scores for K = 2048 and the exact threshold (blocks holding two candidates,
-// the threshold's 16-bit granularity), ~1.5 K with the sampled one; at 45 KB
+// the threshold's 16-bit granularity), ~1.35 K with the sampled one; at 47 KB
 // of LDS per workgroup three share a CU (thousands of queries per call).
 // More candidates take the streamed path.
 constexpr int kGemmResolveCap = 3584;
@@ -203,8 +202,7 @@ __device__ __forceinline__ void emit_lowest(uint2 *c, uint32_t &off, uint32_t &m
 // ---------------------------------------------------------------------------
 // kPass 1: block maxima of every block; 3: of the sampled block groups only,
 // stored compacted (range r's sampled group j at r * sampled_groups(sub) + j);
-// 2: emission, every
-// query's candidate total added into tot[q].
+// 2: emission, every query's candidate total added into tot[q].
 // kFallback (pass 2): the checking launch after a sampled threshold.  It
 // returns unless a query of the group has fewer than min(K, visible)
 // candidates in tot, and emits every visible position of those queries only.
@@ -541,17 +539,14 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_score_kernel(
       }
       if (kPass == 2) emit(accp, ptl);   // the stage's last tile
     };
-    {
-      // (n_st >= 1: p_end > p_begin)
 #pragma unroll
-      for (int k = 0; k < kPieces; ++k) dma_piece(kb, stageA, p_begin, k);
-      for (int it = 0; it < n_st; ++it) {
-        const int p0 = p_begin + it * kGemmStage;
-        __syncthreads();   // this stage's loads done; the other buffer no longer read
-        const bool more = it + 1 < n_st;
-        if ((it & 1) == 0) compute(stageA, p0, stageB, more, 0);
-        else compute(stageB, p0, stageA, more, 1);
-      }
+    for (int k = 0; k < kPieces; ++k) dma_piece(kb, stageA, p_begin, k);
+    for (int it = 0; it < n_st; ++it) {
+      const int p0 = p_begin + it * kGemmStage;
+      __syncthreads();   // this stage's loads done; the other buffer no longer read
+      const bool more = it + 1 < n_st;
+      if ((it & 1) == 0) compute(stageA, p0, stageB, more, 0);
+      else compute(stageB, p0, stageA, more, 1);
     }
     __syncthreads();   // the next sequence's first stage reuses stage A
   }
