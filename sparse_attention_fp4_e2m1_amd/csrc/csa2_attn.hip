@@ -297,7 +297,7 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
 // One workgroup per (query, split of the selected rows), one wave per 16
 // heads.  Per sub-chunk of 64 rows the workgroup gathers the codes (two
 // sub-chunks ahead, in registers), dequantizes K^ and V^ once into LDS and
-// every wave runs its heads over them.  One LDS stage (42 KB per workgroup)
+// every wave runs its heads over them.  One LDS stage (43 KB per workgroup)
 // and at most 168 VGPRs let three workgroups share a CU, which hides the
 // dequantization and softmax phases of one behind the others'.  With a
 // single split the results are final (normalized output and lse); otherwise
