@@ -45,6 +45,7 @@ __device__ __forceinline__ int vt_col(int r) {
 constexpr int kMaxRowsPerSplit = 2048;
 constexpr int kTargetGroups = 256;            // workgroups aimed for (one per CU)
 constexpr int kTwoSubMinGroups = 128;         // see rows_per_split
+constexpr int64_t kDenseMinGroups = 768;      // 64 heads: the four-per-CU form from this many workgroups
 constexpr int kMaxSplits = 256;               // splits of one query, at most
 constexpr int kCombineBatch = 32;
 constexpr int kLocalRowsPerSplit = 128;       // window rows per split of the fused call             // split outputs per round of combine loads
@@ -421,8 +422,14 @@ __device__ __forceinline__ void store_partial(float *__restrict__ part_acc,
 
 // kWithLocal: the launch also holds the window splits (csa2_sparse_local_attn); the
 // sparse-only instantiation carries none of their code.
-template <int kWaves, bool kWithLocal>
-__global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial_kernel(
+// kDense (64 heads, grids of thousands of workgroups, sparse rows only): four
+// workgroups per CU instead of three -- the split's row list passes through a
+// ring of four sub-chunks in LDS (each sub-chunk's indices loaded two
+// iterations ahead, through a register) instead of staying whole, and the
+// codes are gathered one sub-chunk ahead, so that the stage and the registers
+// fit four.
+template <int kWaves, bool kWithLocal, bool kDense = false>
+__global__ void __launch_bounds__(kWaves * 64, kDense ? 4 : (kWaves >= 4 ? 3 : 1)) attn_partial_kernel(
     const uint8_t *__restrict__ kv_codes, const uint8_t *__restrict__ kv_scales,
     int64_t capacity, const uint16_t *__restrict__ qg, int32_t n_heads,
     const int32_t *__restrict__ q_seq, const int32_t *__restrict__ topk, int32_t top_k,
@@ -432,7 +439,8 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
     const uint8_t *__restrict__ lv, const int32_t *__restrict__ lpos, int32_t window,
     const int32_t *__restrict__ q_pos) {
   constexpr int kThreads = kWaves * 64;
-  __shared__ int32_t rows[kMaxRowsPerSplit + 2 * kSub];
+  static_assert(!kDense || (kWaves == 4 && !kWithLocal), "the dense form: 64 heads, sparse rows");
+  __shared__ int32_t rows[kDense ? 4 * kSub : kMaxRowsPerSplit + 2 * kSub];
   __shared__ uint4 kq[4 * 4 * 64];
   __shared__ __attribute__((aligned(16))) _Float16 vt[128 * kVtPitch];
 
@@ -479,17 +487,24 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
   // the query's rows of Q first (their loads overlap the row list's)
   uint4 qraw[4];
   load_q_raw(qg, q, n_heads, wave, l16, g, qraw);
-  // the split's row list (and -1 for two sub-chunks past its end, which the
-  // look-ahead gathers read), eight entries per thread per batch of loads:
-  // branch-free (an index clamped into the split), so that a batch is in
-  // flight together
-  {
-    const int32_t *src = topk + (int64_t)q * top_k + row0;
+  const int32_t *srow = topk + (int64_t)q * top_k + row0;
+  // (kDense) entry r of the split's row list, -1 past its end
+  auto row_at = [&](int r) -> int32_t { return r < nrows ? srow[r] : -1; };
+  int32_t pend = -1;   // (kDense) thread tid < kSub: its entry of the next sub-chunk for the ring
+  if constexpr (kDense) {
+    // sub-chunks 0 and 1 into ring slots 0 and 1; sub-chunk 2's entry pending
+    if (tid < 2 * kSub) rows[tid] = row_at(tid);
+    if (tid < kSub) pend = row_at(2 * kSub + tid);
+  } else {
+    // the split's row list (and -1 for two sub-chunks past its end, which the
+    // look-ahead gathers read), eight entries per thread per batch of loads:
+    // branch-free (an index clamped into the split), so that a batch is in
+    // flight together
     const int nslots = (nsub + 2) * kSub;
     for (int r0 = 0; r0 < nslots; r0 += 8 * kThreads) {
       int32_t v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = src[min(r0 + u * kThreads + tid, nrows - 1)];
+      for (int u = 0; u < 8; ++u) v[u] = srow[min(r0 + u * kThreads + tid, nrows - 1)];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int r = r0 + u * kThreads + tid;
@@ -507,25 +522,44 @@ __global__ void __launch_bounds__(kWaves * 64, kWaves >= 4 ? 3 : 1) attn_partial
   float m_run = -INFINITY;   // for head 16*wave + l16 (same in all four lane groups)
   float l_run = 0.0f;
 
-  // The codes of sub-chunk c are gathered two sub-chunks ahead, into register
-  // set c & 1 (the loop is unrolled by two so that each set is a fixed
-  // register array): no branch around a gather and no copy between sets, so
-  // the compiler waits only for the set being dequantized.
-  Gathered<kThreads> ga, gb;
-  gather(ga, rows, 0, codes, scales, tid);
-  gather(gb, rows, kSub, codes, scales, tid);
-  for (int c = 0; c < nsub; c += 2) {
-    __syncthreads();   // the previous sub-chunk's readers are done with the stage
-    dequant(ga, kq, vt, tid);
-    gather(ga, rows, (c + 2) * kSub, codes, scales, tid);
-    __syncthreads();
-    attend_sub(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
-    if (c + 1 >= nsub) break;
-    __syncthreads();
-    dequant(gb, kq, vt, tid);
-    gather(gb, rows, (c + 3) * kSub, codes, scales, tid);
-    __syncthreads();
-    attend_sub(kq, vt, rows, (c + 1) * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+  if constexpr (kDense) {
+    // ring slot s & 3 holds sub-chunk s; at iteration c slot (c + 2) & 3 (last
+    // read for sub-chunk c - 2) takes sub-chunk c + 2, read first by the
+    // gather of iteration c + 1
+    Gathered<kThreads> ga;
+    gather(ga, rows, 0, codes, scales, tid);
+    for (int c = 0; c < nsub; ++c) {
+      __syncthreads();   // the previous sub-chunk's readers are done with the stage
+      if (tid < kSub) {
+        rows[((c + 2) & 3) * kSub + tid] = pend;
+        pend = row_at((c + 3) * kSub + tid);
+      }
+      dequant(ga, kq, vt, tid);
+      gather(ga, rows + ((c + 1) & 3) * kSub, 0, codes, scales, tid);
+      __syncthreads();
+      attend_sub(kq, vt, rows + (c & 3) * kSub, 0, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+    }
+  } else {
+    // The codes of sub-chunk c are gathered two sub-chunks ahead, into register
+    // set c & 1 (the loop is unrolled by two so that each set is a fixed
+    // register array): no branch around a gather and no copy between sets, so
+    // the compiler waits only for the set being dequantized.
+    Gathered<kThreads> ga, gb;
+    gather(ga, rows, 0, codes, scales, tid);
+    gather(gb, rows, kSub, codes, scales, tid);
+    for (int c = 0; c < nsub; c += 2) {
+      __syncthreads();   // the previous sub-chunk's readers are done with the stage
+      dequant(ga, kq, vt, tid);
+      gather(ga, rows, (c + 2) * kSub, codes, scales, tid);
+      __syncthreads();
+      attend_sub(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+      if (c + 1 >= nsub) break;
+      __syncthreads();
+      dequant(gb, kq, vt, tid);
+      gather(gb, rows, (c + 3) * kSub, codes, scales, tid);
+      __syncthreads();
+      attend_sub(kq, vt, rows, (c + 1) * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+    }
   }
 
   // O^T tile dt: this lane's head 16*wave + l16, channels 16 dt + 4g + 0..3
@@ -759,6 +793,16 @@ hipError_t launch_sparse_attn(const csa2_cache &c, const uint16_t *q, int32_t n_
   const int32_t window = lc ? lc->window : 0;
   dim3 grid((unsigned)total, (unsigned)nq);
   const int waves = n_heads / 16;
+  if (waves == 4 && L.local_splits == 0 && (int64_t)nq * total >= kDenseMinGroups) {
+    hipLaunchKernelGGL((attn_partial_kernel<4, false, true>), grid, dim3(4 * 64), 0, s,
+                       c.kv_codes, c.kv_scales, (int64_t)c.capacity, q, n_heads, q_seq, topk,
+                       top_k, rps, scale_log2, q_negate, acc, ml, total, out, lse, L.splits, lk,
+                       lv, lpos, window, q_pos);
+    if (total == 1) return hipGetLastError();
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(n_heads / 4), (unsigned)nq), dim3(512),
+                       0, s, acc, ml, n_heads, total, out, lse);
+    return hipGetLastError();
+  }
 #define CSA2_ATTN_CASE(W)                                                                        \
   case W:                                                                                        \
     if (L.local_splits > 0)                                                                      \

@@ -136,3 +136,37 @@ def test_attention_batch_shapes(nq, top_k, heads):
     out2, lse2 = m.csa2_sparse_attn(gc, dev_u16(q), dev_i32(q_seq), dev_i32(topk))
     torch.cuda.synchronize()
     assert np.array_equal(host(out2), out) and np.array_equal(host(lse2), lse)
+
+
+@pytest.mark.parametrize("nq,top_k", [(800, 2048), (1600, 1000), (3200, 300)])
+def test_attention_large_grids_match_small(nq, top_k):
+    # Calls of at least 768 workgroups with 64 heads take the four-per-CU form
+    # (the row list through an LDS ring, the gathers one sub-chunk ahead); the
+    # same queries in calls of fewer workgroups take the three-per-CU form.
+    # Both run the same sub-chunk updates in the same order: identical bytes.
+    # Holes, an empty list, duplicates; and the oracle on a few queries.
+    announce(f"attn large grid nq={nq} k={top_k}")
+    m = lib()
+    wl, gc, oc = _setup(64)
+    rng = np.random.default_rng(nq * 7 + top_k)
+    q = synth.f32_to_bf16_bits(rng.standard_normal((nq, 64, 128)).astype(np.float32))
+    topk = rng.integers(0, 3000, (nq, top_k)).astype(np.int32)
+    topk[1, rng.random(top_k) < 0.3] = -1
+    topk[2] = -1
+    topk[3, : top_k // 2] = topk[3, 0]
+    q_seq = np.arange(nq) % gc.batch
+    out, lse = m.csa2_sparse_attn(gc, dev_u16(q), dev_i32(q_seq), dev_i32(topk))
+    torch.cuda.synchronize()
+    out, lse = host(out), host(lse)
+    # pieces of 400 queries: still one split per query (256 workgroups or
+    # more), but grids of fewer than 768
+    for s0 in range(0, nq, 400):
+        sl = slice(s0, s0 + 400)
+        o2, l2 = m.csa2_sparse_attn(gc, dev_u16(q[sl]), dev_i32(q_seq[sl]), dev_i32(topk[sl]))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(o2), out[sl]) and np.array_equal(host(l2), lse[sl]), s0
+    for i in [0, 1, 3, nq - 1]:
+        ro, rl = O.sparse_attention(q[i], oc, int(q_seq[i]), topk[i])
+        rel, dl = attn_errors(out[i], lse[i], ro, rl)
+        assert rel.max() <= ATTN_TOL and dl.max() <= ATTN_TOL, (i, rel.max(), dl.max())
+    assert np.all(out[2] == 0.0) and np.all(np.isneginf(lse[2]))
