@@ -47,8 +47,8 @@ constexpr int kTargetGroups = 256;            // workgroups aimed for (one per C
 constexpr int kTwoSubMinGroups = 128;         // see rows_per_split
 constexpr int64_t kDenseMinGroups = 768;      // 64 heads: the four-per-CU form from this many workgroups
 constexpr int kMaxSplits = 256;               // splits of one query, at most
-constexpr int kCombineBatch = 32;
-constexpr int kLocalRowsPerSplit = 128;       // window rows per split of the fused call             // split outputs per round of combine loads
+constexpr int kCombineBatch = 32;            // split outputs per round of combine loads
+constexpr int kLocalRowsPerSplit = 128;       // window rows per split of the fused call
 static_assert(kTargetGroups <= kMaxSplits && (65536 + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit <= kMaxSplits,
               "every accepted top_k fits the combine's split table");
 constexpr float kLog2e = 1.4426950408889634f;
