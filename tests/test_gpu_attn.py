@@ -138,7 +138,8 @@ def test_attention_batch_shapes(nq, top_k, heads):
     assert np.array_equal(host(out2), out) and np.array_equal(host(lse2), lse)
 
 
-@pytest.mark.parametrize("nq,top_k", [(800, 2048), (1600, 1000), (3200, 300)])
+@pytest.mark.parametrize("nq,top_k", [(800, 2048), (1600, 1000), (3200, 300), (800, 100), (800, 64),
+                                      (800, 1)])
 def test_attention_large_grids_match_small(nq, top_k):
     # Calls of at least 768 workgroups with 64 heads take the four-per-CU form
     # (the row list through an LDS ring, the gathers one sub-chunk ahead); the
@@ -153,7 +154,7 @@ def test_attention_large_grids_match_small(nq, top_k):
     topk = rng.integers(0, 3000, (nq, top_k)).astype(np.int32)
     topk[1, rng.random(top_k) < 0.3] = -1
     topk[2] = -1
-    topk[3, : top_k // 2] = topk[3, 0]
+    topk[3, : max(top_k // 2, 1)] = topk[3, 0]
     q_seq = np.arange(nq) % gc.batch
     out, lse = m.csa2_sparse_attn(gc, dev_u16(q), dev_i32(q_seq), dev_i32(topk))
     torch.cuda.synchronize()
