@@ -10,8 +10,9 @@
 // attn_partial_kernel: one workgroup per (query, split of the selected rows),
 // one wave per 16 query heads; the split is walked in sub-chunks of 64 rows
 // with an online softmax.
-//   * The workgroup gathers a sub-chunk's codes one sub-chunk ahead and
-//     dequantizes them once into LDS, shared by every head wave: K^ in fp16 as
+//   * The workgroup gathers a sub-chunk's codes two sub-chunks ahead (one in
+//     the four-per-CU form that large 64-head grids take) and dequantizes
+//     them once into LDS, shared by every head wave: K^ in fp16 as
 //     MFMA A fragments (the contraction index permuted, k-slice s and lane
 //     group g <-> channels 32g + 8s .. +7, identically for Q), V^ in fp16
 //     transposed [channel][row].  E2M1 codes go through the hardware FP4
