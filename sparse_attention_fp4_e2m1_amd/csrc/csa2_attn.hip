@@ -112,7 +112,7 @@ __device__ __forceinline__ void gather(Gathered<kThreads> &gd, const int32_t *ro
 // Dequantizes one gathered sub-chunk into LDS: K^ as fp16 MFMA A fragments
 // kq[tile][k-step][lane] (16 B each: k-step s of lane group g is channels
 // 32g + 8s .. +7), V^ transposed as fp16 vt[channel][row].
-template <int kThreads>
+template <int kThreads, int kPitch>
 __device__ __forceinline__ void dequant(const Gathered<kThreads> &gd, uint4 *kq, _Float16 *vt,
                                         int tid) {
 #pragma unroll
@@ -140,7 +140,7 @@ __device__ __forceinline__ void dequant(const Gathered<kThreads> &gd, uint4 *kq,
       const f16x2 sab = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(gd.vs[it], 1.0f, false);
       const _Float16 sa = sab[0], sb = sab[1];
       const f16x2 s2a = {sa, sa}, s2b = {sb, sb};
-      uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kVtPitch + vt_col(2 * pr));
+      uint32_t *dst = reinterpret_cast<uint32_t *>(vt + (16 * b) * kPitch + vt_col(2 * pr));
 #pragma unroll
       for (int hw = 0; hw < 2; ++hw) {
         const uint32_t wa = hw ? gd.vc[it][0].y : gd.vc[it][0].x;
@@ -155,8 +155,8 @@ __device__ __forceinline__ void dequant(const Gathered<kThreads> &gd, uint4 *kq,
           const uint32_t a = __builtin_bit_cast(uint32_t, ra[e]);
           const uint32_t c = __builtin_bit_cast(uint32_t, rb[e]);
           // channel 8hw + 2e: (row 2pr, row 2pr+1); channel 8hw + 2e + 1 likewise
-          dst[((8 * hw + 2 * e) * kVtPitch) / 2] = __builtin_amdgcn_perm(c, a, 0x05040100u);
-          dst[((8 * hw + 2 * e + 1) * kVtPitch) / 2] = __builtin_amdgcn_perm(c, a, 0x07060302u);
+          dst[((8 * hw + 2 * e) * kPitch) / 2] = __builtin_amdgcn_perm(c, a, 0x05040100u);
+          dst[((8 * hw + 2 * e + 1) * kPitch) / 2] = __builtin_amdgcn_perm(c, a, 0x07060302u);
         }
       }
     }
@@ -189,6 +189,7 @@ __device__ __forceinline__ float lane_pair_sum32(float x) {
 // O^T += V^T P^T.  scale_log2 = |softmax scale| * log2(e) (a negative scale was
 // folded into Q), so the running maximum of the scaled scores is the scaled
 // maximum of the raw ones.
+template <int kPitch>
 __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf,
                                            const int32_t *rows, int base, const f16x8 (&qf)[4],
                                            float scale_log2, int g, int l16, int lane,
@@ -289,7 +290,7 @@ __device__ __forceinline__ void attend_sub(const uint4 *kq, const _Float16 *vbuf
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       // rows 32sg + 4g + 0..3 and 32sg + 16 + 4g + 0..3 (adjacent, see vt_col)
-      const _Float16 *vrow = vbuf + (dt * 16 + l16) * kVtPitch + 32 * sg + 8 * g;
+      const _Float16 *vrow = vbuf + (dt * 16 + l16) * kPitch + 32 * sg + 8 * g;
       const f16x8 vb = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4 *>(vrow));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vb, pa, o[dt], 0, 0, 0);
     }
@@ -441,9 +442,13 @@ __global__ void __launch_bounds__(kWaves * 64, kDense ? 4 : (kWaves >= 4 ? 3 : 1
     const int32_t *__restrict__ q_pos) {
   constexpr int kThreads = kWaves * 64;
   static_assert(!kDense || (kWaves == 4 && !kWithLocal), "the dense form: 64 heads, sparse rows");
+  // V^T row pitch: 80 in the dense form, where the LDS bank-conflict counter
+  // then reads zero (with 72 the PV fragment reads conflict, ~13% of the
+  // launch's cycles); 72 measured faster in the three-per-CU form
+  constexpr int kPitch = kDense ? kSub + 16 : kVtPitch;
   __shared__ int32_t rows[kDense ? 4 * kSub : kMaxRowsPerSplit + 2 * kSub];
   __shared__ uint4 kq[4 * 4 * 64];
-  __shared__ __attribute__((aligned(16))) _Float16 vt[128 * kVtPitch];
+  __shared__ __attribute__((aligned(16))) _Float16 vt[128 * kPitch];
 
   const int split = blockIdx.x;
   const int q = blockIdx.y;
@@ -472,7 +477,7 @@ __global__ void __launch_bounds__(kWaves * 64, kDense ? 4 : (kWaves >= 4 ? 3 : 1
     for (int c = 0; c < nsub; ++c) {
       stage_local<kThreads>(lk, lv, sbase, rows, c * kSub, kq, vt, tid);
       __syncthreads();
-      attend_sub(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+      attend_sub<kPitch>(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
       __syncthreads();
     }
     store_partial(part_acc, part_ml, q, splits, split, n_heads, wave * 16 + l16, g, o, m_run, l_run);
@@ -535,10 +540,10 @@ __global__ void __launch_bounds__(kWaves * 64, kDense ? 4 : (kWaves >= 4 ? 3 : 1
         rows[((c + 2) & 3) * kSub + tid] = pend;
         pend = row_at((c + 3) * kSub + tid);
       }
-      dequant(ga, kq, vt, tid);
+      dequant<kThreads, kPitch>(ga, kq, vt, tid);
       gather(ga, rows + ((c + 1) & 3) * kSub, 0, codes, scales, tid);
       __syncthreads();
-      attend_sub(kq, vt, rows + (c & 3) * kSub, 0, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+      attend_sub<kPitch>(kq, vt, rows + (c & 3) * kSub, 0, qf, scale_log2, g, l16, lane, m_run, l_run, o);
     }
   } else {
     // The codes of sub-chunk c are gathered two sub-chunks ahead, into register
@@ -550,16 +555,16 @@ __global__ void __launch_bounds__(kWaves * 64, kDense ? 4 : (kWaves >= 4 ? 3 : 1
     gather(gb, rows, kSub, codes, scales, tid);
     for (int c = 0; c < nsub; c += 2) {
       __syncthreads();   // the previous sub-chunk's readers are done with the stage
-      dequant(ga, kq, vt, tid);
+      dequant<kThreads, kPitch>(ga, kq, vt, tid);
       gather(ga, rows, (c + 2) * kSub, codes, scales, tid);
       __syncthreads();
-      attend_sub(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+      attend_sub<kPitch>(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
       if (c + 1 >= nsub) break;
       __syncthreads();
-      dequant(gb, kq, vt, tid);
+      dequant<kThreads, kPitch>(gb, kq, vt, tid);
       gather(gb, rows, (c + 3) * kSub, codes, scales, tid);
       __syncthreads();
-      attend_sub(kq, vt, rows, (c + 1) * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+      attend_sub<kPitch>(kq, vt, rows, (c + 1) * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
     }
   }
 
@@ -663,7 +668,8 @@ __global__ void __launch_bounds__(kWaves * 64) local_attn_kernel(
   constexpr int kThreads = kWaves * 64;
   __shared__ int32_t rows[kMaxLocalWindow + kSub];   // slot of each row, -1: no row
   __shared__ uint4 kq[4 * 4 * 64];
-  __shared__ __attribute__((aligned(16))) _Float16 vt[128 * kVtPitch];
+  constexpr int kPitch = kVtPitch;
+  __shared__ __attribute__((aligned(16))) _Float16 vt[128 * kPitch];
 
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
@@ -687,7 +693,7 @@ __global__ void __launch_bounds__(kWaves * 64) local_attn_kernel(
   for (int c = 0; c < nsub; ++c) {
     stage_local<kThreads>(lk, lv, sbase, rows, c * kSub, kq, vt, tid);
     __syncthreads();
-    attend_sub(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
+    attend_sub<kPitch>(kq, vt, rows, c * kSub, qf, scale_log2, g, l16, lane, m_run, l_run, o);
     __syncthreads();   // the stage is rewritten next
   }
 
